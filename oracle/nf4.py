@@ -1,0 +1,251 @@
+"""Oracle: NF4 blockwise quantization with double quantization (DQ).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Plain numpy; every
+floating-point step that decides an integer is done in IEEE binary32 exactly as
+stated below, everything else in float64.
+
+What is computed, in the pages' order
+-------------------------------------
+1. Block-wise first level [rkmt §1.2, §2.1; zky "three parts"]: the flat
+   row-major weight is cut into fixed 64-element blocks; each block gets its own
+   scale, its absolute maximum ``absmax_b`` (an fp32 value; exact, since the
+   weights are bf16).
+2. NF4 encode [zky "NF4"; lqnn §2.1]: each element is normalized by its block's
+   absmax into [-1, 1] (binary32 division, correctly rounded) and mapped to the
+   nearest of the 16 NF4 levels.  Ties go to the lower code.  An all-zero block
+   (absmax 0) encodes every element as the level 0.
+3. Packing [rkmt §4.2: 4-bit data packed in uint8 storage]: two codes per
+   byte.  Reading (the pages fix no nibble order): within each 4-byte word that
+   holds elements 8w .. 8w+7, byte j (j = 0..3) holds code(8w+j) in bits 0-3 and
+   code(8w+j+4) in bits 4-7.
+4. Double quantization [rkmt §1.3, §2.2, §2.3; zky "double quantization"]:
+   the block absmax values are quantized again to 8 bits in groups of 256
+   consecutive blocks, each group keeping one fp32 second-level constant.
+   Reading: unsigned, scale only (the scales are non-negative, so the range
+   [0, c2] has zero-point 0): ``step_g = fp32(c2 / 255)`` with ``c2`` the group's
+   largest absmax, ``qscale_b = min(255, rint_even(fp32(absmax_b / step_g)))``
+   (0 when step_g is 0).  The first-level zero-point is not stored: NF4 is
+   absmax-symmetric and has an exact zero level.
+5. Dequantization [lqnn §3.3; zky "a counter-intuitive combination"]:
+   ``s'_b = fp32(qscale_b * step_g)``, ``w = bf16_rne(fp32(level[code] * s'_b))``.
+
+The codebook [zky "NF4": levels placed by the normal distribution so that each
+level receives about the same share of weights; kwkr §2.1: zero must be exactly
+representable].  Reading: 8 positive levels Phi^-1(p_j) for p_j equally spaced
+in (0.5, 1 - 1/32], 7 negative levels -Phi^-1(q_j) for q_j equally spaced in
+(0.5, 1 - 1/30], an exact 0, each side divided by its largest magnitude so the
+table spans [-1, 1]; computed in float64 and rounded to fp32.  Midpoint k is the
+largest fp32 not above the exact mean of levels k and k+1, so that
+``code = #{k : v > mid[k]}`` is exactly "nearest level, ties to the lower code"
+for every fp32 v.
+
+Parity unpinned: the level values themselves rest on the construction rule
+(the pages print no table); the 8-bit second-level format is pinned by the
+closed-form storage sizes only.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import ndtri
+
+BLOCK = 64      # elements per first-level block [rkmt §1.2]
+GROUP = 256     # first-level scales per second-level group [rkmt §2.2]
+
+
+# --------------------------------------------------------------------------
+# bf16 <-> fp32, written from the definition of the formats
+# --------------------------------------------------------------------------
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 is the upper half of an fp32 bit pattern: widening is exact."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16, nearest with ties to even; NaN stays NaN (quiet)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    rounded = ((u + 0x7FFF + lsb) >> 16).astype(np.uint32)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    quiet = ((u >> 16) | 0x40).astype(np.uint32)
+    return np.where(nan, quiet, rounded).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# codebook
+# --------------------------------------------------------------------------
+def codebook() -> tuple[np.ndarray, np.ndarray]:
+    """Returns (levels float32[16] ascending, mids float32[15])."""
+    p = np.linspace(0.5, 1.0 - 1.0 / 32.0, 9)[1:]        # 8 positive quantiles
+    q = np.linspace(0.5, 1.0 - 1.0 / 30.0, 8)[1:]        # 7 negative quantiles
+    pos = ndtri(p) / ndtri(1.0 - 1.0 / 32.0)
+    neg = -ndtri(q) / ndtri(1.0 - 1.0 / 30.0)
+    levels64 = np.concatenate([neg[::-1], [0.0], pos])
+    levels = levels64.astype(np.float32)
+    mids = np.empty(15, dtype=np.float32)
+    for k in range(15):
+        exact = (float(levels[k]) + float(levels[k + 1])) / 2.0   # exact in float64
+        m = np.float32(exact)
+        if float(m) > exact:                                       # round toward -inf
+            m = np.nextafter(m, np.float32(-np.inf))
+        mids[k] = m
+    return levels, mids
+
+
+# --------------------------------------------------------------------------
+# storage sizes [rkmt §1.3, §2.3]
+# --------------------------------------------------------------------------
+def nf4_bytes(n: int, k: int) -> tuple[int, int, int]:
+    """(code bytes, u8 scale bytes, fp32 second-level bytes) of an n x k weight."""
+    numel = n * k
+    if numel % BLOCK:
+        raise ValueError("numel must be a multiple of 64")
+    nblocks = numel // BLOCK
+    ngroups = -(-nblocks // GROUP)
+    return numel // 2, nblocks, 4 * ngroups
+
+
+# --------------------------------------------------------------------------
+# quantize / dequantize
+# --------------------------------------------------------------------------
+def encode(v: np.ndarray, mids: np.ndarray) -> np.ndarray:
+    """Nearest NF4 level of normalized fp32 values, ties to the lower code."""
+    v = np.asarray(v, dtype=np.float32)
+    code = np.zeros(v.shape, dtype=np.uint8)
+    for k in range(15):
+        code += (v > mids[k]).astype(np.uint8)
+    return code
+
+
+def pack(code: np.ndarray) -> np.ndarray:
+    """Codes (one per element, flat) -> bytes, in the word layout of step 3."""
+    c = np.asarray(code, dtype=np.uint8).reshape(-1, 8)
+    lo = c[:, 0:4]
+    hi = c[:, 4:8]
+    return (lo | (hi << 4)).astype(np.uint8).reshape(-1)
+
+
+def unpack(codes: np.ndarray) -> np.ndarray:
+    b = np.asarray(codes, dtype=np.uint8).reshape(-1, 4)
+    out = np.empty((b.shape[0], 8), dtype=np.uint8)
+    out[:, 0:4] = b & 0x0F
+    out[:, 4:8] = b >> 4
+    return out.reshape(-1)
+
+
+def block_absmax(w_bits: np.ndarray) -> np.ndarray:
+    x = bf16_to_f32(np.asarray(w_bits).reshape(-1)).reshape(-1, BLOCK)
+    return np.max(np.abs(x), axis=1).astype(np.float32)
+
+
+def quantize(w_bits: np.ndarray, mids: np.ndarray):
+    """bf16 weight bits (any shape, numel % 64 == 0) ->
+    (codes uint8[numel/2], qscale uint8[numel/64], step float32[ngroups])."""
+    flat = np.asarray(w_bits, dtype=np.uint16).reshape(-1)
+    if flat.size % BLOCK:
+        raise ValueError("numel must be a multiple of 64")
+    x = bf16_to_f32(flat).reshape(-1, BLOCK)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite weights are outside the contract")
+    # step 1: first-level scale per 64-block
+    absmax = np.max(np.abs(x), axis=1).astype(np.float32)
+    # step 2: normalize (binary32 division) and encode
+    safe = np.where(absmax == 0, np.float32(1), absmax).astype(np.float32)
+    v = np.divide(x, safe[:, None], dtype=np.float32)
+    v = np.where((absmax == 0)[:, None], np.float32(0), v).astype(np.float32)
+    code = encode(v, mids)
+    # step 3: pack two codes per byte
+    codes = pack(code.reshape(-1))
+    # step 4: second level over groups of 256 block scales
+    nblocks = absmax.size
+    ngroups = -(-nblocks // GROUP)
+    qscale = np.empty(nblocks, dtype=np.uint8)
+    step = np.empty(ngroups, dtype=np.float32)
+    for g in range(ngroups):
+        a = absmax[g * GROUP:(g + 1) * GROUP]
+        c2 = np.max(a)
+        st = np.float32(c2) / np.float32(255.0)
+        step[g] = st
+        if st == 0:
+            qscale[g * GROUP:(g + 1) * GROUP] = 0
+        else:
+            qv = np.rint(np.divide(a, st, dtype=np.float32))
+            qscale[g * GROUP:(g + 1) * GROUP] = np.minimum(qv, 255).astype(np.uint8)
+    return codes, qscale, step
+
+
+def block_scale(qscale: np.ndarray, step: np.ndarray) -> np.ndarray:
+    """s'_b = fp32(qscale_b * step_g)."""
+    q = np.asarray(qscale, dtype=np.uint8).astype(np.float32)
+    g = np.arange(q.size) // GROUP
+    return (q * np.asarray(step, dtype=np.float32)[g]).astype(np.float32)
+
+
+def dequantize(codes, qscale, step, levels) -> np.ndarray:
+    """-> bf16 bits (flat): bf16_rne(fp32(level[code] * s'_b))."""
+    code = unpack(codes)
+    s = block_scale(qscale, step)
+    s_el = np.repeat(s, BLOCK)
+    prod = (np.asarray(levels, dtype=np.float32)[code] * s_el).astype(np.float32)
+    return f32_to_bf16_rne(prod)
+
+
+def dequantize_f32(codes, qscale, step, levels) -> np.ndarray:
+    return bf16_to_f32(dequantize(codes, qscale, step, levels))
+
+
+def dequant_error_bound(w_bits: np.ndarray, levels: np.ndarray) -> np.ndarray:
+    """Per-element bound on |w - deq(q(w))| (float64), derived from the steps,
+    independent of how ``quantize`` is written:
+
+    * encode: the normalized value lies in a codebook interval [L_i, L_i+1] and
+      the nearest level is at most half that gap away, plus the rounding of the
+      binary32 quotient (2^-24 relative)            -> absmax * (gap/2 + 2^-23)
+    * double quantization: qscale * step is within half a step of absmax, plus
+      the binary32 roundings of c2/255, absmax/step and qscale*step
+                                                     -> 0.5*step + 2^-15*step + 2^-22*absmax
+      (multiplied by |level| <= 1)
+    * the binary32 product level*s' and the final bf16 rounding
+                                                     -> 2^-23 |w| + half a bf16 ulp of |w|
+    """
+    flat = np.asarray(w_bits, dtype=np.uint16).reshape(-1)
+    x = bf16_to_f32(flat).astype(np.float64).reshape(-1, BLOCK)
+    absmax = np.max(np.abs(x), axis=1)
+    nblocks = absmax.size
+    ngroups = -(-nblocks // GROUP)
+    c2 = np.array([absmax[g * GROUP:(g + 1) * GROUP].max() for g in range(ngroups)])
+    step = (c2 / 255.0)[np.arange(nblocks) // GROUP]
+    lv = np.asarray(levels, dtype=np.float64)
+    v = np.where(absmax[:, None] > 0,
+                 x / np.where(absmax > 0, absmax, 1.0)[:, None], 0.0)
+    idx = np.clip(np.searchsorted(lv, v, side="right") - 1, 0, 14)
+    gap = lv[idx + 1] - lv[idx]
+    enc = absmax[:, None] * (0.5 * gap + 2.0 ** -23)
+    dq = (0.5 * step + 2.0 ** -15 * step + 2.0 ** -22 * absmax)[:, None]
+    wmax = np.abs(x) + enc + dq
+    _, e = np.frexp(np.maximum(wmax, np.finfo(np.float64).tiny))
+    half_ulp_bf16 = np.ldexp(1.0, e - 9)
+    bound = enc + dq + 2.0 ** -23 * wmax + half_ulp_bf16
+    return bound.reshape(-1)
+
+
+def bits_per_param(block: int = BLOCK, group: int = GROUP, double_quant: bool = True,
+                   scale_bytes: int = 4, zero_point_bytes: int = 0) -> float:
+    """Storage per weight in bits: 4-bit code plus the constants' share."""
+    if double_quant:
+        return 4.0 + 8.0 / block + 8.0 * 4 / (block * group)
+    return 4.0 + 8.0 * (scale_bytes + zero_point_bytes) / block
+
+
+def model_bytes(params: float, double_quant: bool = True,
+                zero_point_bytes: int = 0) -> dict:
+    """Byte totals for a model of ``params`` weights, as in [rkmt §2.3]."""
+    nblocks = params / BLOCK
+    codes = params * 4 / 8
+    if double_quant:
+        consts = nblocks * 1 + math.ceil(nblocks / GROUP) * 4
+    else:
+        consts = nblocks * (4 + zero_point_bytes)
+    return {"blocks": nblocks, "codes": codes, "constants": consts,
+            "total": codes + consts}
