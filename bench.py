@@ -1,0 +1,245 @@
+"""Benchmark: QLoRA NF4 linear forward + backward on one MI355X.
+
+Workload (the 7B-style decoder layer linears): q, k, v, o 4096x4096, gate and
+up 11008x4096, down 4096x11008, weights N(0, 0.02) quantized to NF4 with
+double quantization; M = 2048 tokens (batch 1 x sequence 2048) of bf16
+activations N(0, 1); LoRA r = 8, alpha = 16 (s = 2) on q, k, v, o; upstream
+gradients N(0, 1).  One step = for every projection: the forward (Y, T) and
+the backward (dX, dA, dB).  Outputs Y and dX are bf16, T/dA/dB fp32.  Inputs
+are resident in HBM before the timed region; no allocation inside it.
+
+Prints one JSON line.  Throughput is algorithmic: forward 2MNK + 2Mr(K+N),
+backward 2MNK + 2Mr(2K+2N) flops; bytes = packed weight once per pass plus
+every activation, gradient and adapter tensor at its dtype.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+M_TOKENS = 2048
+RANK, ALPHA = 8, 16
+PROJ = [  # name, N (out), K (in), LoRA rank
+    ("q", 4096, 4096, RANK), ("k", 4096, 4096, RANK), ("v", 4096, 4096, RANK),
+    ("o", 4096, 4096, RANK), ("gate", 11008, 4096, 0), ("up", 11008, 4096, 0),
+    ("down", 4096, 11008, 0),
+]
+WORKLOAD = ("7B-style decoder layer linears (q,k,v,o 4096x4096; gate,up 11008x4096; "
+            "down 4096x11008), M=2048 tokens, LoRA r=8 alpha=16 on q,k,v,o, fwd+bwd")
+METRIC = "QLoRA linear fwd+bwd TFLOP/s & effective GB/s (% roofline) on 1 MI355X"
+
+
+def flops_fwd(M, N, K, r):
+    return 2 * M * N * K + 2 * M * r * (K + N)
+
+
+def flops_bwd(M, N, K, r):
+    return 2 * M * N * K + 2 * M * r * (2 * K + 2 * N)
+
+
+def packed_bytes(N, K):
+    return N * K // 2 + N * K // 64 + 4 * ((N * K // 64 + 255) // 256)
+
+
+def step_bytes(M, N, K, r):
+    w = packed_bytes(N, K)
+    fwd = w + 2 * M * K + 2 * M * N + (2 * r * K + 2 * N * r + 4 * M * r if r else 0)
+    bwd = w + 2 * M * N + 2 * M * K + (2 * M * K + 2 * r * K + 2 * N * r + 4 * M * r
+                                       + 4 * r * K + 4 * N * r if r else 0)
+    return fwd + bwd
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "qlora_fine_tuning_nf4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel, src_files):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash(src_files):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(sample_tokens: int):
+    """The oracle, as it stands, on a bounded sample of the same workload: all
+    seven projections with the first `sample_tokens` tokens: dequantize each
+    weight, forward, backward (float64 numpy)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import synth
+    from oracle import linear as olin
+    from oracle import nf4 as onf4
+
+    lv, mid = onf4.codebook()
+    M = sample_tokens
+    total_flops = 0
+    elapsed = 0.0
+    for i, (name, N, K, r) in enumerate(PROJ):
+        W = synth.normal_bf16((N, K), 0.02, synth.tensor_seed(2, 10 * i))
+        codes, qs, st = onf4.quantize(W, mid)          # storage, not part of the step
+        X = synth.normal_bf16((M, K), 1.0, synth.tensor_seed(2, 10 * i + 1))
+        dY = synth.normal_bf16((M, N), 1.0, synth.tensor_seed(2, 10 * i + 2))
+        A = synth.normal_bf16((r, K), 0.01, synth.tensor_seed(2, 10 * i + 3)) if r else None
+        B = synth.normal_bf16((N, r), 0.01, synth.tensor_seed(2, 10 * i + 4)) if r else None
+        t0 = time.perf_counter()
+        Wd = onf4.dequantize(codes, qs, st, lv).reshape(N, K)
+        olin.forward(Wd, X, A, B, ALPHA / RANK)
+        Wd = onf4.dequantize(codes, qs, st, lv).reshape(N, K)
+        olin.backward(Wd, X, dY, A, B, ALPHA / RANK)
+        elapsed += time.perf_counter() - t0
+        total_flops += flops_fwd(M, N, K, r) + flops_bwd(M, N, K, r)
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    return {"value": round(total_flops / elapsed / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"all 7 projections at M={M} of the {M_TOKENS} tokens: dequantize + fwd + bwd "
+                      f"in float64 numpy ({elapsed:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only; --gpus must be 1 "
+              "(the multi-GPU sharding is a design, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from qlora_fine_tuning_nf4_amd import binding as QB
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cb = QB.device_codebook(dev)
+    M = M_TOKENS
+    s = ALPHA / RANK
+    layers = []
+    for i, (name, N, K, r) in enumerate(PROJ):
+        W = synth.device_normal_bf16((N, K), 0.02, synth.tensor_seed(2, 10 * i), device=dev)
+        q = QB.qlora_quantize(W, cb)
+        del W
+        L = dict(name=name, N=N, K=K, r=r, q=q)
+        L["X"] = synth.device_normal_bf16((M, K), 1.0, synth.tensor_seed(2, 10 * i + 1), device=dev)
+        L["dY"] = synth.device_normal_bf16((M, N), 1.0, synth.tensor_seed(2, 10 * i + 2), device=dev)
+        L["A"] = synth.device_normal_bf16((r, K), 0.01, synth.tensor_seed(2, 10 * i + 3), device=dev) if r else None
+        L["B"] = synth.device_normal_bf16((N, r), 0.01, synth.tensor_seed(2, 10 * i + 4), device=dev) if r else None
+        L["Y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        L["T"] = torch.empty((M, r), dtype=torch.float32, device=dev) if r else None
+        L["dX"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        L["dA"] = torch.empty((r, K), dtype=torch.float32, device=dev) if r else None
+        L["dB"] = torch.empty((N, r), dtype=torch.float32, device=dev) if r else None
+        nws = max(QB.qlora_workspace_bytes(0, M, N, K, r), QB.qlora_workspace_bytes(1, M, N, K, r), 16)
+        L["ws"] = torch.empty(nws, dtype=torch.uint8, device=dev)
+        layers.append(L)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev_fwd, ev_dx = [], []
+
+    def step(record):
+        for L in layers:
+            single = record and L["r"] == 0      # r = 0: the call is one GEMM launch
+            if single:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            QB.qlora_linear_fwd(L["q"], cb, L["X"], L["A"], L["B"], s, out=L["Y"], T_out=L["T"],
+                                workspace=L["ws"])
+            if single:
+                e1.record(stream)
+                ev_fwd.append((e0, e1, L))
+                e2 = torch.cuda.Event(enable_timing=True)
+                e3 = torch.cuda.Event(enable_timing=True)
+                e2.record(stream)
+            QB.qlora_linear_bwd(L["q"], cb, L["X"], L["dY"], L["A"], L["B"], s, T=L["T"],
+                                dX_out=L["dX"], dA_out=L["dA"], dB_out=L["dB"], workspace=L["ws"])
+            if single:
+                e3.record(stream)
+                ev_dx.append((e2, e3, L))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    g0.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = g0.elapsed_time(g1)
+    ms_per_step = wall * 1e3 / args.steps
+
+    total_flops = sum(flops_fwd(M, L["N"], L["K"], L["r"]) + flops_bwd(M, L["N"], L["K"], L["r"])
+                      for L in layers)
+    total_bytes = sum(step_bytes(M, L["N"], L["K"], L["r"]) for L in layers)
+    tflops = total_flops / (ms_per_step * 1e-3) / 1e12
+    gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
+
+    def kstats(evs):
+        durs = [a.elapsed_time(b) * 1e-3 for a, b, _ in evs]
+        flops = [2 * M * L["N"] * L["K"] for _, _, L in evs]
+        return sum(durs), sum(flops), len(durs)
+
+    tf, ff, nf = kstats(ev_fwd)
+    td, fd, nd = kstats(ev_dx)
+    if td >= tf:
+        kname, t_tot, f_tot, n_l, srcs = "k_gemm_dx", td, fd, nd, ["gemm_dx.hip", "common.h"]
+    else:
+        kname, t_tot, f_tot, n_l, srcs = "k_gemm_fwd", tf, ff, nf, ["gemm_fwd.hip", "common.h"]
+    achieved = (f_tot / n_l) / (t_tot / n_l) / 1e12
+    roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "avg_launch_us": round(t_tot / n_l * 1e6, 2),
+                "traffic": traffic_from_profile(kname, srcs),
+                "other_gemm": {"k_gemm_fwd": round(ff / tf / 1e12, 1) if tf else None,
+                               "k_gemm_dx": round(fd / td / 1e12, 1) if td else None}}
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights quantized to NF4+DQ, N(0,1) activations)",
+        "config": {"workload": WORKLOAD, "M": M, "r": RANK, "alpha": ALPHA,
+                   "projections": [[p[0], p[1], p[2], p[3]] for p in PROJ], "y_dtype": "bf16",
+                   "dx_dtype": "bf16", "parallelism": "none (1 GPU)"},
+        "effective_GBps": round(gbs, 1),
+        "frac_of_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

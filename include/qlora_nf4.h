@@ -1,0 +1,178 @@
+/*
+ * qlora_nf4.h -- C ABI of the QLoRA NF4 quantized-linear library (gfx950 / MI355X).
+ *
+ * The frozen base weight W [n x k] (out_features x in_features) is stored as
+ * block-wise 4-bit NF4 with double quantization of the block scales; the
+ * forward and backward of the LoRA-augmented linear layer dequantize it to
+ * bf16 inside the kernels.
+ *
+ * Pages cited (address and section):
+ *   news.rkmt.cn/news/4821   (QLoRA double / block-wise quantization)
+ *   zky001.github.io/llm-training-guide/docs/post-training/qlora (section 5.8)
+ *   kwkr.cn/news/627310      (quantized vs. non-quantized)
+ *   www.lqnn.cn/news/228537  (course notes: quantization + LoRA)
+ *   www.cf-1.com/news/5705389 (LoRA training on a quantized base)
+ *
+ * Conventions for every entry point
+ *   - Device pointers are owned by the caller; the library never allocates,
+ *     frees or synchronizes.  Work is enqueued on `stream` (a hipStream_t, or
+ *     NULL for the null stream) and is ordered with other work on it.
+ *   - Matrices are row-major and contiguous.  bf16 tensors are passed as raw
+ *     16-bit patterns (uint16_t).
+ *   - codes, X, Y, dY and dX must be 16-byte aligned; every other device
+ *     pointer 4-byte aligned.
+ *   - k % 64 == 0; m >= 1 and n >= 1 are arbitrary (ragged tails are masked).
+ *   - r == 0 switches the LoRA branch off: A, B, T_save, T_saved, dA and dB
+ *     are then ignored and may be NULL.
+ *   - All arguments are validated before any HIP call; on error nothing is
+ *     enqueued and a positive status is returned.  A failed launch returns
+ *     QLORA_ERR_HIP.  Asynchronous faults surface at the caller's next
+ *     synchronization.  Non-finite weights are outside the contract (no check).
+ *   - The library keeps no state between calls: calls are re-entrant and
+ *     thread-safe; two calls that write the same buffers race.
+ *   - Results are deterministic: the same inputs give the same bits.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = 1,      /* a required pointer is NULL */
+  QLORA_ERR_SHAPE = 2,     /* m, n or k <= 0, k % 64 != 0, or descriptor sizes mismatch */
+  QLORA_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
+  QLORA_ERR_DTYPE = 4,     /* unknown dtype enum */
+  QLORA_ERR_RANK = 5,      /* LoRA rank r < 0 or r > QLORA_MAX_RANK */
+  QLORA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than qlora_workspace_bytes() */
+  QLORA_ERR_HIP = 7,       /* a HIP launch failed */
+  QLORA_ERR_ARG = 8        /* another argument is out of range (path, op) */
+};
+
+/* output dtypes */
+enum { QLORA_F32 = 0, QLORA_BF16 = 1 };
+
+/* path selection for qlora_linear_fwd / qlora_linear_bwd */
+enum {
+  QLORA_PATH_AUTO = 0, /* by m: split-K streaming path for small m, MFMA GEMM otherwise */
+  QLORA_PATH_GEMV = 1, /* force the small-m streaming path (m <= QLORA_GEMV_MAX_M) */
+  QLORA_PATH_GEMM = 2  /* force the tiled MFMA GEMM path */
+};
+
+#define QLORA_BLOCK 64        /* weights per first-level block   (news.rkmt.cn/news/4821 §1.2) */
+#define QLORA_GROUP 256       /* block scales per second-level group (news.rkmt.cn/news/4821 §2.2) */
+#define QLORA_MAX_RANK 128    /* largest supported LoRA rank */
+#define QLORA_GEMV_MAX_M 64   /* largest m the streaming path accepts */
+#define QLORA_CODEBOOK_LEN 31 /* 16 NF4 levels then 15 decision midpoints */
+
+/*
+ * Packed NF4 + double-quantized weight (device buffers owned by the caller).
+ * Flat block b covers elements [64b, 64b+64) of the row-major weight; group g
+ * covers blocks [256g, 256g+256).  Sizes come from qlora_nf4_bytes().
+ *   codes : n*k/2 bytes.  The 4-byte word w holds elements 8w..8w+7: byte j
+ *           (j = 0..3) is code(8w+j) | code(8w+j+4) << 4.
+ *   qscale: n*k/64 bytes, the block absmax quantized to 8 bits.
+ *   step  : ceil(n*k/16384) floats, the fp32 second-level constant per group.
+ * Dequantized weight: w = bf16_rne(level[code] * fp32(qscale_b * step_g)).
+ * (news.rkmt.cn/news/4821 §1.3, §2.2, §2.3; zky001 section 5.8 "double quantization")
+ */
+typedef struct {
+  int64_t n;       /* out_features */
+  int64_t k;       /* in_features, k % 64 == 0 */
+  uint8_t *codes;
+  uint8_t *qscale;
+  float *step;
+} qlora_nf4;
+
+/*
+ * Host.  Writes the NF4 table to out[0..30]: 16 ascending levels in [-1, 1]
+ * (level 0 at index 7, exactly 0), then the 15 decision midpoints, midpoint i
+ * being the largest fp32 not above (level[i] + level[i+1]) / 2.  Levels are
+ * standard-normal quantiles normalised to [-1, 1], 8 positive and 7 negative
+ * plus an exact zero (zky001 section 5.8 "NF4"; kwkr.cn/news/627310 §2.1 on
+ * the exact zero).  Copy it to the device and pass it as `codebook` below.
+ * Returns QLORA_ERR_NULL if out is NULL.
+ */
+int qlora_nf4_codebook(float *out);
+
+/*
+ * Host.  Byte sizes of the three arrays of an n x k packed weight
+ * (news.rkmt.cn/news/4821 §2.3: 4-bit codes + 8-bit scale per 64 + fp32 per
+ * 256 scales).  Any output pointer may be NULL.  QLORA_ERR_SHAPE unless
+ * n >= 1, k >= 64 and k % 64 == 0.
+ */
+int qlora_nf4_bytes(int64_t n, int64_t k, size_t *codes, size_t *qscale, size_t *step);
+
+/*
+ * Host.  Workspace bytes needed by qlora_linear_fwd (op = 0) or
+ * qlora_linear_bwd (op = 1) for these sizes, for any path.  0 on bad input.
+ */
+size_t qlora_workspace_bytes(int op, int64_t m, int64_t n, int64_t k, int r);
+
+/*
+ * Quantize a bf16 weight W [n x k] (device) into `out` (device arrays sized by
+ * qlora_nf4_bytes, out->n and out->k set).  Block-wise absmax scaling over 64
+ * elements, nearest NF4 level of the binary32 quotient w / absmax (ties to the
+ * lower level; an all-zero block gives level 0), then double quantization:
+ * step_g = fp32(c2 / 255) with c2 the largest absmax of the group and
+ * qscale_b = min(255, rint_even(fp32(absmax_b / step_g))), 0 when step_g is 0
+ * (news.rkmt.cn/news/4821 §1.2, §2.1, §2.2; zky001 section 5.8).
+ * `codebook` is the device copy of qlora_nf4_codebook().
+ */
+int qlora_quantize(const uint16_t *W, const float *codebook, const qlora_nf4 *out, void *stream);
+
+/*
+ * Dequantize `W` into a dense bf16 [n x k] device array `out`, with the same
+ * arithmetic the linear kernels use internally.  For checking and for merging
+ * an adapter into the base (www.lqnn.cn/news/228537 §3.3), not for the linear
+ * layer itself, which never materializes the bf16 weight.
+ */
+int qlora_dequantize(const qlora_nf4 *W, const float *codebook, uint16_t *out, void *stream);
+
+/*
+ * Forward of the LoRA-augmented quantized linear (www.cf-1.com/news/5705389
+ * §2.1, §3.2; www.lqnn.cn/news/228537 §3.2-§3.3):
+ *     T = X A^T            [m x r], fp32 (written to T_save if not NULL)
+ *     Y = X deq(W)^T + scaling * T B^T      [m x n]
+ * X [m x k] bf16, A [r x k] bf16, B [n x r] bf16, scaling = alpha / r.
+ * The product runs on bf16 operands with fp32 accumulation; T stays fp32.
+ * Y is fp32 (y_dtype QLORA_F32) or bf16 rounded to nearest even (QLORA_BF16).
+ * ws: device workspace of at least qlora_workspace_bytes(0, m, n, k, r) bytes
+ * (may be NULL only if that size is 0).  path: QLORA_PATH_*.
+ */
+int qlora_linear_fwd(const qlora_nf4 *W, const float *codebook, const uint16_t *X, int64_t m,
+                     const uint16_t *A, const uint16_t *B, int r, float scaling,
+                     void *Y, int y_dtype, float *T_save,
+                     void *ws, size_t ws_bytes, int path, void *stream);
+
+/*
+ * Backward of the same layer (www.cf-1.com/news/5705389 §2.1: dL/dx = dL/dy W0^T
+ * through the quantized matrix; www.lqnn.cn/news/228537 §3.3 and zky001
+ * section 5.8: the frozen base gets no gradient, only A and B):
+ *     U  = dY B                          [m x r] fp32
+ *     dX = dY deq(W) + scaling * U A     [m x k]  (fp32 or bf16 per dx_dtype)
+ *     dA = scaling * U^T X               [r x k]  fp32, overwritten
+ *     dB = scaling * dY^T T              [n x r]  fp32, overwritten
+ * T = X A^T is taken from T_saved ([m x r] fp32, as written by the forward) or
+ * recomputed when T_saved is NULL.  dX may be NULL to skip the input gradient;
+ * dA/dB are required when r > 0.
+ */
+int qlora_linear_bwd(const qlora_nf4 *W, const float *codebook, const uint16_t *X,
+                     const uint16_t *dY, int64_t m, const uint16_t *A, const uint16_t *B,
+                     int r, float scaling, const float *T_saved,
+                     void *dX, int dx_dtype, float *dA, float *dB,
+                     void *ws, size_t ws_bytes, int path, void *stream);
+
+/* Host.  Static message for a status code (never NULL). */
+const char *qlora_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QLORA_NF4_H */

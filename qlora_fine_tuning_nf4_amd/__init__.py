@@ -1,0 +1,11 @@
+"""MI355X-native QLoRA NF4 quantized-linear hot path.
+
+The product is the C-ABI HIP library ``libqlora_nf4.so`` (declared in
+``include/qlora_nf4.h``); ``binding`` is its thin ctypes binding, with the same
+entry-point names.  Build in-tree with ``python -m qlora_fine_tuning_nf4_amd.build``.
+"""
+from .binding import (  # noqa: F401
+    NF4Weight, QLoRAError, device_codebook, lib, qlora_dequantize, qlora_linear_bwd,
+    qlora_linear_fwd, qlora_nf4_bytes, qlora_nf4_codebook, qlora_quantize, qlora_strerror,
+    qlora_workspace_bytes,
+)

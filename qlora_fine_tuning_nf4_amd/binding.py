@@ -1,0 +1,213 @@
+"""Thin ctypes binding of the C ABI in ``include/qlora_nf4.h``.
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.  The
+function names are those of the C entry points.  Loading fails loudly when the
+built library is missing: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
+
+QLORA_F32, QLORA_BF16 = 0, 1
+PATHS = {"auto": 0, "gemv": 1, "gemm": 2}
+CODEBOOK_LEN = 31
+GEMV_MAX_M = 64
+MAX_RANK = 128
+
+
+class QLoRAError(RuntimeError):
+    pass
+
+
+class _Nf4Desc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("qscale", ctypes.c_void_p), ("step", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise QLoRAError(f"HIP library not built: {LIB_PATH} is missing "
+                             "(run python -m qlora_fine_tuning_nf4_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float,
+                                 ctypes.c_size_t)
+        P = ctypes.POINTER
+        L.qlora_strerror.restype = ctypes.c_char_p
+        L.qlora_strerror.argtypes = [i32]
+        L.qlora_nf4_codebook.restype = i32
+        L.qlora_nf4_codebook.argtypes = [P(ctypes.c_float)]
+        L.qlora_nf4_bytes.restype = i32
+        L.qlora_nf4_bytes.argtypes = [i64, i64, P(sz), P(sz), P(sz)]
+        L.qlora_workspace_bytes.restype = sz
+        L.qlora_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
+        L.qlora_quantize.restype = i32
+        L.qlora_quantize.argtypes = [vp, vp, P(_Nf4Desc), vp]
+        L.qlora_dequantize.restype = i32
+        L.qlora_dequantize.argtypes = [P(_Nf4Desc), vp, vp, vp]
+        L.qlora_linear_fwd.restype = i32
+        L.qlora_linear_fwd.argtypes = [P(_Nf4Desc), vp, vp, i64, vp, vp, i32, f32, vp, i32, vp,
+                                       vp, sz, i32, vp]
+        L.qlora_linear_bwd.restype = i32
+        L.qlora_linear_bwd.argtypes = [P(_Nf4Desc), vp, vp, vp, i64, vp, vp, i32, f32, vp, vp,
+                                       i32, vp, vp, vp, sz, i32, vp]
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().qlora_strerror(status).decode()
+        raise QLoRAError(f"{what}: status {status} ({msg})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def qlora_strerror(status: int) -> str:
+    return lib().qlora_strerror(status).decode()
+
+
+def qlora_nf4_codebook() -> np.ndarray:
+    """Host: float32[31] = 16 NF4 levels then 15 midpoints, from the library."""
+    out = (ctypes.c_float * CODEBOOK_LEN)()
+    _check(lib().qlora_nf4_codebook(out), "qlora_nf4_codebook")
+    return np.frombuffer(out, dtype=np.float32).copy()
+
+
+def qlora_nf4_bytes(n: int, k: int):
+    c, q, s = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().qlora_nf4_bytes(n, k, ctypes.byref(c), ctypes.byref(q), ctypes.byref(s)),
+           "qlora_nf4_bytes")
+    return c.value, q.value, s.value
+
+
+def qlora_workspace_bytes(op: int, m: int, n: int, k: int, r: int) -> int:
+    return int(lib().qlora_workspace_bytes(op, m, n, k, r))
+
+
+@dataclass
+class NF4Weight:
+    """Packed NF4 + double-quantized weight (device tensors)."""
+    n: int
+    k: int
+    codes: torch.Tensor    # uint8 [n*k/2]
+    qscale: torch.Tensor   # uint8 [n*k/64]
+    step: torch.Tensor     # float32 [ceil(n*k/16384)]
+
+    def desc(self) -> _Nf4Desc:
+        return _Nf4Desc(self.n, self.k, self.codes.data_ptr(), self.qscale.data_ptr(),
+                        self.step.data_ptr())
+
+    @staticmethod
+    def empty(n: int, k: int, device="cuda") -> "NF4Weight":
+        c, q, s = qlora_nf4_bytes(n, k)
+        return NF4Weight(n, k, torch.empty(c, dtype=torch.uint8, device=device),
+                         torch.empty(q, dtype=torch.uint8, device=device),
+                         torch.empty(s // 4, dtype=torch.float32, device=device))
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.qscale.numel() + 4 * self.step.numel()
+
+
+def device_codebook(device="cuda") -> torch.Tensor:
+    return torch.from_numpy(qlora_nf4_codebook()).to(device)
+
+
+def _bf16(t, name):
+    if t.dtype != torch.bfloat16 or not t.is_contiguous():
+        raise QLoRAError(f"{name} must be a contiguous bfloat16 tensor")
+    return t
+
+
+def qlora_quantize(W: torch.Tensor, codebook: torch.Tensor, out: NF4Weight | None = None) -> NF4Weight:
+    _bf16(W, "W")
+    n, k = W.shape
+    out = out if out is not None else NF4Weight.empty(n, k, W.device)
+    d = out.desc()
+    _check(lib().qlora_quantize(_ptr(W), _ptr(codebook), ctypes.byref(d), _stream()),
+           "qlora_quantize")
+    return out
+
+
+def qlora_dequantize(w: NF4Weight, codebook: torch.Tensor) -> torch.Tensor:
+    out = torch.empty((w.n, w.k), dtype=torch.bfloat16, device=w.codes.device)
+    d = w.desc()
+    _check(lib().qlora_dequantize(ctypes.byref(d), _ptr(codebook), _ptr(out), _stream()),
+           "qlora_dequantize")
+    return out
+
+
+def qlora_linear_fwd(w: NF4Weight, codebook: torch.Tensor, X: torch.Tensor, A=None, B=None,
+                     scaling: float = 0.0, y_dtype=torch.float32, save_T: bool = True,
+                     path: str = "auto", out=None, T_out=None, workspace=None):
+    """-> (Y [m x n], T [m x r] fp32 or None)."""
+    _bf16(X, "X")
+    m = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if r:
+        _bf16(A, "A")
+        _bf16(B, "B")
+    dev = X.device
+    Y = out if out is not None else torch.empty((m, w.n), dtype=y_dtype, device=dev)
+    T = T_out if T_out is not None else (
+        torch.empty((m, r), dtype=torch.float32, device=dev) if (r and save_T) else None)
+    nws = qlora_workspace_bytes(0, m, w.n, w.k, r)
+    ws = workspace if workspace is not None else (
+        torch.empty(max(nws, 16), dtype=torch.uint8, device=dev))
+    d = w.desc()
+    _check(lib().qlora_linear_fwd(
+        ctypes.byref(d), _ptr(codebook), _ptr(X), m, _ptr(A) if r else None,
+        _ptr(B) if r else None, r, float(scaling), _ptr(Y),
+        QLORA_BF16 if Y.dtype == torch.bfloat16 else QLORA_F32, _ptr(T), _ptr(ws),
+        ws.numel(), PATHS[path], _stream()), "qlora_linear_fwd")
+    return Y, T
+
+
+def qlora_linear_bwd(w: NF4Weight, codebook: torch.Tensor, X, dY, A=None, B=None,
+                     scaling: float = 0.0, T=None, dx_dtype=torch.float32, need_dX: bool = True,
+                     path: str = "auto", dX_out=None, dA_out=None, dB_out=None, workspace=None):
+    """-> (dX [m x k] or None, dA [r x k] fp32 or None, dB [n x r] fp32 or None)."""
+    _bf16(dY, "dY")
+    m = dY.shape[0]
+    r = 0 if A is None else A.shape[0]
+    dev = dY.device
+    if r:
+        _bf16(X, "X")
+        _bf16(A, "A")
+        _bf16(B, "B")
+    dX = dX_out if dX_out is not None else (
+        torch.empty((m, w.k), dtype=dx_dtype, device=dev) if need_dX else None)
+    dA = dA_out if dA_out is not None else (
+        torch.empty((r, w.k), dtype=torch.float32, device=dev) if r else None)
+    dB = dB_out if dB_out is not None else (
+        torch.empty((w.n, r), dtype=torch.float32, device=dev) if r else None)
+    nws = qlora_workspace_bytes(1, m, w.n, w.k, r)
+    ws = workspace if workspace is not None else (
+        torch.empty(max(nws, 16), dtype=torch.uint8, device=dev))
+    d = w.desc()
+    _check(lib().qlora_linear_bwd(
+        ctypes.byref(d), _ptr(codebook), _ptr(X) if X is not None else None, _ptr(dY), m,
+        _ptr(A) if r else None, _ptr(B) if r else None, r, float(scaling), _ptr(T),
+        _ptr(dX), QLORA_BF16 if (dX is not None and dX.dtype == torch.bfloat16) else QLORA_F32,
+        _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), PATHS[path], _stream()), "qlora_linear_bwd")
+    return dX, dA, dB

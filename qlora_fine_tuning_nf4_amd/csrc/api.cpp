@@ -1,0 +1,318 @@
+// C ABI: argument validation, path and split choice, launches.  Everything is
+// checked before the first HIP call; on error nothing is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/qlora_nf4.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kB = QLORA_BLOCK;
+constexpr int64_t kG = QLORA_GROUP;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+size_t up16(size_t b) { return (b + 15) & ~size_t(15); }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- inverse standard-normal CDF: rational first guess refined by Halley's
+// method on Phi(x) = erfc(-x / sqrt 2) / 2, which converges to full double
+// precision in two steps.
+double norm_cdf(double x) { return 0.5 * std::erfc(-x / std::sqrt(2.0)); }
+
+double norm_ppf(double p) {
+  // first guess: tail/central rational approximation (Acklam's coefficients)
+  static const double a[] = {-3.969683028665376e+01, 2.209460984245205e+02, -2.759285104469687e+02,
+                             1.383577518672690e+02,  -3.066479806614716e+01, 2.506628277459239e+00};
+  static const double b[] = {-5.447609879822406e+01, 1.615858368580409e+02, -1.556989798598866e+02,
+                             6.680131188771972e+01,  -1.328068155288572e+01};
+  static const double c[] = {-7.784894002430293e-03, -3.223964580411365e-01, -2.400758277161838e+00,
+                             -2.549732539343734e+00, 4.374664141464968e+00,  2.938163982698783e+00};
+  static const double d[] = {7.784695709041462e-03, 3.224671290700398e-01, 2.445134137142996e+00,
+                             3.754408661907416e+00};
+  double x;
+  if (p < 0.02425) {
+    const double q = std::sqrt(-2 * std::log(p));
+    x = (((((c[0] * q + c[1]) * q + c[2]) * q + c[3]) * q + c[4]) * q + c[5]) /
+        ((((d[0] * q + d[1]) * q + d[2]) * q + d[3]) * q + 1);
+  } else if (p > 1 - 0.02425) {
+    const double q = std::sqrt(-2 * std::log(1 - p));
+    x = -(((((c[0] * q + c[1]) * q + c[2]) * q + c[3]) * q + c[4]) * q + c[5]) /
+        ((((d[0] * q + d[1]) * q + d[2]) * q + d[3]) * q + 1);
+  } else {
+    const double q = p - 0.5, t = q * q;
+    x = (((((a[0] * t + a[1]) * t + a[2]) * t + a[3]) * t + a[4]) * t + a[5]) * q /
+        (((((b[0] * t + b[1]) * t + b[2]) * t + b[3]) * t + b[4]) * t + 1);
+  }
+  for (int it = 0; it < 3; ++it) {
+    const double e = norm_cdf(x) - p;
+    const double u = e * std::sqrt(2 * M_PI) * std::exp(x * x / 2);
+    x = x - u / (1 + x * u / 2);
+  }
+  return x;
+}
+
+// j-th of `num` points equally spaced over [start, stop], stop hit exactly.
+double spaced(double start, double stop, int num, int j) {
+  if (j == num - 1) return stop;
+  const double step = (stop - start) / (num - 1);
+  return j * step + start;
+}
+
+struct FwdPlan {
+  bool gemv;
+  int ksplit;
+};
+
+FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int path) {
+  FwdPlan p;
+  p.gemv = path == QLORA_PATH_GEMV || (path == QLORA_PATH_AUTO && m <= 32);
+  if (p.gemv) {
+    const int64_t ntiles = cdiv(n, 16), nquads = cdiv(k / kB, 4);
+    const int64_t cap = std::max<int64_t>(1, nquads / 4);
+    p.ksplit = (int)std::min<int64_t>(cap, std::max<int64_t>(1, cdiv(1024, ntiles)));
+  } else {
+    const int64_t tiles = cdiv(m, 128) * cdiv(n, 128), nsteps = cdiv(k, 128);
+    const int64_t cap = std::max<int64_t>(1, nsteps / 2);
+    p.ksplit = tiles >= 256 ? 1 : (int)std::min<int64_t>(cap, cdiv(512, tiles));
+  }
+  return p;
+}
+
+int plan_dx_split(int64_t m, int64_t n, int64_t k) {
+  const int64_t tiles = cdiv(m, 128) * cdiv(k, 128), nsteps = cdiv(n, 128);
+  const int64_t cap = std::max<int64_t>(1, nsteps / 2);
+  return tiles >= 256 ? 1 : (int)std::min<int64_t>(cap, cdiv(512, tiles));
+}
+
+int plan_wgrad_split(int64_t m, int64_t c, int r) {
+  const int64_t wgs = cdiv(c, 512) * cdiv(r, 8);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(m, 16), cdiv(256, wgs)));
+}
+
+struct FwdWs {
+  size_t t_off, part_off, total;
+};
+FwdWs fwd_ws(int64_t m, int64_t n, int64_t k, int r, int path) {
+  const FwdPlan p = plan_fwd(m, n, k, path);
+  FwdWs w;
+  w.t_off = 0;
+  w.part_off = up16(sizeof(float) * (size_t)(m * r));
+  w.total = w.part_off + (p.ksplit > 1 ? sizeof(float) * (size_t)p.ksplit * m * n : 0);
+  return w;
+}
+
+struct BwdWs {
+  size_t u_off, t_off, bt_off, dx_off, wg_off, total;
+};
+BwdWs bwd_ws(int64_t m, int64_t n, int64_t k, int r) {
+  BwdWs w;
+  w.u_off = 0;
+  w.t_off = w.u_off + up16(sizeof(float) * (size_t)(m * r));
+  w.bt_off = w.t_off + up16(sizeof(float) * (size_t)(m * r));
+  w.dx_off = w.bt_off + up16(sizeof(uint16_t) * (size_t)(r * n));
+  const int ns = plan_dx_split(m, n, k);
+  w.wg_off = w.dx_off + up16(ns > 1 ? sizeof(float) * (size_t)ns * m * k : 0);
+  size_t wg = 0;
+  if (r > 0) {
+    const int s1 = plan_wgrad_split(m, k, r), s2 = plan_wgrad_split(m, n, r);
+    wg = sizeof(float) * std::max((size_t)s1 * r * k * (s1 > 1), (size_t)s2 * r * n * (s2 > 1));
+  }
+  w.total = w.wg_off + up16(wg);
+  return w;
+}
+
+int check_desc(const qlora_nf4* W) {
+  if (!W || !W->codes || !W->qscale || !W->step) return QLORA_ERR_NULL;
+  if (W->n < 1 || W->k < kB || W->k % kB) return QLORA_ERR_SHAPE;
+  if (!aligned(W->codes, 16) || !aligned(W->step, 4)) return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+ql::Nf4View view(const qlora_nf4* W) { return ql::Nf4View{W->codes, W->qscale, W->step, W->n, W->k}; }
+
+}  // namespace
+
+extern "C" {
+
+const char* qlora_strerror(int s) {
+  switch (s) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL: return "a required pointer is NULL";
+    case QLORA_ERR_SHAPE: return "bad shape (m, n, k must be >= 1 and k a multiple of 64)";
+    case QLORA_ERR_ALIGN: return "pointer not aligned as required";
+    case QLORA_ERR_DTYPE: return "unknown dtype";
+    case QLORA_ERR_RANK: return "LoRA rank out of range [0, 128]";
+    case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QLORA_ERR_HIP: return "HIP launch failed";
+    case QLORA_ERR_ARG: return "argument out of range";
+    default: return "unknown status";
+  }
+}
+
+int qlora_nf4_codebook(float* out) {
+  if (!out) return QLORA_ERR_NULL;
+  const double cp = norm_ppf(1.0 - 1.0 / 32.0), cn = norm_ppf(1.0 - 1.0 / 30.0);
+  double lv[16];
+  for (int j = 1; j <= 8; ++j) lv[7 + j] = norm_ppf(spaced(0.5, 1.0 - 1.0 / 32.0, 9, j)) / cp;
+  for (int j = 1; j <= 7; ++j) lv[7 - j] = -norm_ppf(spaced(0.5, 1.0 - 1.0 / 30.0, 8, j)) / cn;
+  lv[7] = 0.0;
+  for (int i = 0; i < 16; ++i) out[i] = (float)lv[i];
+  for (int i = 0; i < 15; ++i) {
+    const double exact = ((double)out[i] + (double)out[i + 1]) / 2.0;
+    float mid = (float)exact;
+    if ((double)mid > exact) mid = std::nextafter(mid, -INFINITY);
+    out[16 + i] = mid;
+  }
+  return QLORA_OK;
+}
+
+int qlora_nf4_bytes(int64_t n, int64_t k, size_t* codes, size_t* qscale, size_t* step) {
+  if (n < 1 || k < kB || k % kB) return QLORA_ERR_SHAPE;
+  const int64_t nb = n * (k / kB);
+  if (codes) *codes = (size_t)(n * k / 2);
+  if (qscale) *qscale = (size_t)nb;
+  if (step) *step = sizeof(float) * (size_t)cdiv(nb, kG);
+  return QLORA_OK;
+}
+
+size_t qlora_workspace_bytes(int op, int64_t m, int64_t n, int64_t k, int r) {
+  if (m < 1 || n < 1 || k < kB || k % kB || r < 0 || r > QLORA_MAX_RANK) return 0;
+  if (op == 0) {
+    size_t b = 0;
+    for (int path : {QLORA_PATH_AUTO, QLORA_PATH_GEMV, QLORA_PATH_GEMM}) {
+      if (path == QLORA_PATH_GEMV && m > QLORA_GEMV_MAX_M) continue;
+      b = std::max(b, fwd_ws(m, n, k, r, path).total);
+    }
+    return b;
+  }
+  if (op == 1) return bwd_ws(m, n, k, r).total;
+  return 0;
+}
+
+int qlora_quantize(const uint16_t* W, const float* codebook, const qlora_nf4* out, void* stream) {
+  if (!W || !codebook) return QLORA_ERR_NULL;
+  if (int e = check_desc(out)) return e;
+  if (!aligned(W, 16) || !aligned(codebook, 4)) return QLORA_ERR_ALIGN;
+  const int64_t nblocks = out->n * (out->k / kB);
+  if (ql::launch_quantize(W, codebook, out->codes, out->qscale, out->step, nblocks,
+                          (hipStream_t)stream) != hipSuccess)
+    return QLORA_ERR_HIP;
+  return QLORA_OK;
+}
+
+int qlora_dequantize(const qlora_nf4* W, const float* codebook, uint16_t* out, void* stream) {
+  if (!codebook || !out) return QLORA_ERR_NULL;
+  if (int e = check_desc(W)) return e;
+  if (!aligned(out, 16) || !aligned(codebook, 4)) return QLORA_ERR_ALIGN;
+  if (ql::launch_dequant(W->codes, W->qscale, W->step, codebook, out, W->n * (W->k / kB),
+                         (hipStream_t)stream) != hipSuccess)
+    return QLORA_ERR_HIP;
+  return QLORA_OK;
+}
+
+int qlora_linear_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* X, int64_t m,
+                     const uint16_t* A, const uint16_t* B, int r, float scaling, void* Y,
+                     int y_dtype, float* T_save, void* ws, size_t ws_bytes, int path,
+                     void* stream) {
+  if (!codebook || !X || !Y) return QLORA_ERR_NULL;
+  if (int e = check_desc(W)) return e;
+  if (m < 1) return QLORA_ERR_SHAPE;
+  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
+  if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
+  if (y_dtype != QLORA_F32 && y_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
+  if (path < QLORA_PATH_AUTO || path > QLORA_PATH_GEMM) return QLORA_ERR_ARG;
+  if (path == QLORA_PATH_GEMV && m > QLORA_GEMV_MAX_M) return QLORA_ERR_ARG;
+  if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(codebook, 4)) return QLORA_ERR_ALIGN;
+  if (r > 0 && (!aligned(A, 16) || !aligned(B, 2) || (T_save && !aligned(T_save, 4))))
+    return QLORA_ERR_ALIGN;
+  const int64_t n = W->n, k = W->k;
+  const FwdWs L = fwd_ws(m, n, k, r, path);
+  const bool need_ws = L.total > L.part_off || (r > 0 && !T_save);
+  if (need_ws && (!ws || ws_bytes < L.total)) return QLORA_ERR_WORKSPACE;
+  if (ws && !aligned(ws, 16)) return QLORA_ERR_ALIGN;
+
+  hipStream_t s = (hipStream_t)stream;
+  const FwdPlan p = plan_fwd(m, n, k, path);
+  char* wsb = (char*)ws;
+  float* T = nullptr;
+  if (r > 0) {
+    T = T_save ? T_save : (float*)(wsb + L.t_off);
+    if (ql::launch_rowdot(X, A, m, k, r, T, s) != hipSuccess) return QLORA_ERR_HIP;
+  }
+  ql::LoraTerm lora{T, B, (int64_t)r, 1, r, scaling};
+  float* part = p.ksplit > 1 ? (float*)(wsb + L.part_off) : nullptr;
+  const ql::Nf4View v = view(W);
+  const bool bf = y_dtype == QLORA_BF16;
+  hipError_t e = p.gemv ? ql::launch_gemv_fwd(v, codebook, X, m, lora, Y, bf, part, p.ksplit, s)
+                        : ql::launch_gemm_fwd(v, codebook, X, m, lora, Y, bf, part, p.ksplit, s);
+  if (e != hipSuccess) return QLORA_ERR_HIP;
+  if (p.ksplit > 1 && ql::launch_reduce(part, p.ksplit, m, n, lora, Y, bf, s) != hipSuccess)
+    return QLORA_ERR_HIP;
+  return QLORA_OK;
+}
+
+int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* X,
+                     const uint16_t* dY, int64_t m, const uint16_t* A, const uint16_t* B, int r,
+                     float scaling, const float* T_saved, void* dX, int dx_dtype, float* dA,
+                     float* dB, void* ws, size_t ws_bytes, int path, void* stream) {
+  if (!codebook || !dY) return QLORA_ERR_NULL;
+  if (int e = check_desc(W)) return e;
+  if (m < 1) return QLORA_ERR_SHAPE;
+  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
+  if (r > 0 && (!A || !B || !dA || !dB || !X)) return QLORA_ERR_NULL;
+  if (dx_dtype != QLORA_F32 && dx_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
+  if (path < QLORA_PATH_AUTO || path > QLORA_PATH_GEMM) return QLORA_ERR_ARG;
+  if (!aligned(dY, 16) || !aligned(codebook, 4) || (dX && !aligned(dX, 16)) ||
+      (X && !aligned(X, 16)))
+    return QLORA_ERR_ALIGN;
+  if (r > 0 && (!aligned(A, 16) || !aligned(B, 2) || !aligned(dA, 4) || !aligned(dB, 4) ||
+                (T_saved && !aligned(T_saved, 4))))
+    return QLORA_ERR_ALIGN;
+  const int64_t n = W->n, k = W->k;
+  const BwdWs L = bwd_ws(m, n, k, r);
+  if (L.total > 0 && (!ws || ws_bytes < L.total)) return QLORA_ERR_WORKSPACE;
+  if (ws && !aligned(ws, 16)) return QLORA_ERR_ALIGN;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  float* U = nullptr;
+  const float* T = T_saved;
+  if (r > 0) {
+    U = (float*)(wsb + L.u_off);
+    uint16_t* Bt = (uint16_t*)(wsb + L.bt_off);
+    if (ql::launch_transpose_bf16(B, n, r, Bt, s) != hipSuccess) return QLORA_ERR_HIP;
+    if (ql::launch_rowdot(dY, Bt, m, n, r, U, s) != hipSuccess) return QLORA_ERR_HIP;
+    if (!T) {
+      float* Tw = (float*)(wsb + L.t_off);
+      if (ql::launch_rowdot(X, A, m, k, r, Tw, s) != hipSuccess) return QLORA_ERR_HIP;
+      T = Tw;
+    }
+  }
+  if (dX) {
+    const int ns = plan_dx_split(m, n, k);
+    ql::LoraTerm lora{U, A, 1, k, r, scaling};
+    float* part = ns > 1 ? (float*)(wsb + L.dx_off) : nullptr;
+    const bool bf = dx_dtype == QLORA_BF16;
+    if (ql::launch_gemm_dx(view(W), codebook, dY, m, lora, dX, bf, part, ns, s) != hipSuccess)
+      return QLORA_ERR_HIP;
+    if (ns > 1 && ql::launch_reduce(part, ns, m, k, lora, dX, bf, s) != hipSuccess)
+      return QLORA_ERR_HIP;
+  }
+  if (r > 0) {
+    float* part = (float*)(wsb + L.wg_off);
+    if (ql::launch_wgrad(X, U, m, k, r, scaling, dA, false, part, plan_wgrad_split(m, k, r), s) !=
+        hipSuccess)
+      return QLORA_ERR_HIP;
+    if (ql::launch_wgrad(dY, T, m, n, r, scaling, dB, true, part, plan_wgrad_split(m, n, r), s) !=
+        hipSuccess)
+      return QLORA_ERR_HIP;
+  }
+  return QLORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Shared device helpers of the HIP path (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define QL_DEV __device__ __forceinline__
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+namespace ql {
+
+constexpr int kBlock = 64;    // weights per first-level block
+constexpr int kGroup = 256;   // block scales per second-level group
+constexpr int kWave = 64;
+
+// D[16x16] += A[16x32] * B[32x16], bf16 operands, fp32 accumulate.
+// Lane l holds A[l%16][8(l/16) .. +7], B[8(l/16) .. +7][l%16] and
+// D[4(l/16) .. +3][l%16] (layout measured on gfx950).
+QL_DEV f32x4_t mfma16x16x32(const u32x4_t a, const u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+QL_DEV uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+QL_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+QL_DEV uint16_t to_bf16(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+QL_DEV float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+QL_DEV float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xFFFF0000u); }
+
+// Per-block lookup table of the 16 dequantized bf16 values, kept as byte
+// planes so that a 4-bit code selects its byte with v_perm_b32:
+//   lo[i] byte b = low byte of E[4i+b], hi[i] byte b = high byte of E[4i+b],
+//   E[c] = bf16_rne(level[c] * s)   (s = qscale * step of the block).
+struct Lut {
+  uint32_t lo[4], hi[4];
+};
+
+QL_DEV Lut make_lut(const float* lv, float s) {
+  uint32_t d[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) d[i] = pack_bf16x2(lv[2 * i] * s, lv[2 * i + 1] * s);
+  Lut t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t.lo[i] = perm(d[2 * i + 1], d[2 * i], 0x06040200u);
+    t.hi[i] = perm(d[2 * i + 1], d[2 * i], 0x07050301u);
+  }
+  return t;
+}
+
+// Decode one packed word (elements 8w .. 8w+7: byte j = code j | code j+4 << 4)
+// into 8 bf16 values in element order, as 4 packed pairs.
+QL_DEV u32x4_t decode8(const Lut& t, uint32_t x) {
+  const uint32_t sa = x & 0x07070707u;          // codes 0..3, low three bits
+  const uint32_t sb = (x >> 4) & 0x07070707u;   // codes 4..7
+  const uint32_t ma = ((x >> 3) & 0x01010101u) * 0xFFu;   // 0xFF where code >= 8
+  const uint32_t mb = ((x >> 7) & 0x01010101u) * 0xFFu;
+  const uint32_t loa = (ma & perm(t.lo[3], t.lo[2], sa)) | (~ma & perm(t.lo[1], t.lo[0], sa));
+  const uint32_t hia = (ma & perm(t.hi[3], t.hi[2], sa)) | (~ma & perm(t.hi[1], t.hi[0], sa));
+  const uint32_t lob = (mb & perm(t.lo[3], t.lo[2], sb)) | (~mb & perm(t.lo[1], t.lo[0], sb));
+  const uint32_t hib = (mb & perm(t.hi[3], t.hi[2], sb)) | (~mb & perm(t.hi[1], t.hi[0], sb));
+  u32x4_t o;
+  o[0] = perm(hia, loa, 0x05010400u);
+  o[1] = perm(hia, loa, 0x07030602u);
+  o[2] = perm(hib, lob, 0x05010400u);
+  o[3] = perm(hib, lob, 0x07030602u);
+  return o;
+}
+
+// Block scale s' = fp32(qscale * step): one rounding, as the format defines.
+QL_DEV float block_scale(const uint8_t* qscale, const float* step, int64_t b) {
+  return (float)qscale[b] * step[b / kGroup];
+}
+
+QL_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+QL_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace ql

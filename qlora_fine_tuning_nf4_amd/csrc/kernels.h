@@ -1,0 +1,60 @@
+// Host-side launchers of the HIP kernels (one per kernel family).  Shapes are
+// validated by the caller (api.cpp) before any of these runs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ql {
+
+// LoRA term added by epilogues:  out[m][c] += scaling * sum_j L[m*r + j] * R[c*rs_c + j*rs_j]
+struct LoraTerm {
+  const float* L;      // [M x r] fp32 (T in the forward, U in the backward), or nullptr
+  const uint16_t* R;   // bf16 (B [N x r] in the forward, A [r x K] in the backward)
+  int64_t rs_c, rs_j;  // strides of R
+  int r;
+  float scaling;
+};
+
+struct Nf4View {
+  const uint8_t* codes;
+  const uint8_t* qscale;
+  const float* step;
+  int64_t n, k;
+};
+
+hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* codes,
+                           uint8_t* qscale, float* step, int64_t nblocks, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
+                          const float* codebook, uint16_t* out, int64_t nblocks, hipStream_t s);
+
+// Forward base product Y = X deq(W)^T (+ LoRA term), tiled MFMA GEMM.
+// ksplit > 1 writes fp32 partials part[ksplit][M][N] and leaves the epilogue
+// to launch_reduce.
+hipError_t launch_gemm_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,
+                           const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
+                           hipStream_t s);
+// Forward for small M (<= 64): streaming split-K over the packed weight.
+hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,
+                           const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
+                           hipStream_t s);
+// dX = dY deq(W) (+ LoRA term), contraction over n; nsplit > 1 -> partials.
+hipError_t launch_gemm_dx(const Nf4View& w, const float* codebook, const uint16_t* dY, int64_t M,
+                          const LoraTerm& lora, void* dX, bool dx_bf16, float* part, int nsplit,
+                          hipStream_t s);
+// out[m][c] = sum_s part[s][m][c] + LoRA term, for C columns.
+hipError_t launch_reduce(const float* part, int nsplit, int64_t M, int64_t C,
+                         const LoraTerm& lora, void* out, bool out_bf16, hipStream_t s);
+
+// out[m][j] = sum_c P[m][c] * Q[j][c]   (P bf16 [M x C], Q bf16 [r x C], out fp32 [M x r])
+hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
+                         float* out, hipStream_t s);
+// Qt[j][n] = Q[n][j] for a bf16 [N x r] matrix.
+hipError_t launch_transpose_bf16(const uint16_t* Q, int64_t N, int r, uint16_t* Qt, hipStream_t s);
+// Weight gradients of the adapter: out = scaling * sum_m Q[m][j] * P[m][c]
+// (P bf16 [M x C], Q fp32 [M x r]); written as out[j][c] (transpose_out false,
+// [r x C]) or out[c][j] (true, [C x r]).  msplit partials go through `part`.
+hipError_t launch_wgrad(const uint16_t* P, const float* Q, int64_t M, int64_t C, int r,
+                        float scaling, float* out, bool transpose_out, float* part, int msplit,
+                        hipStream_t s);
+
+}  // namespace ql

@@ -1,0 +1,122 @@
+// Block-wise NF4 quantization with double quantization of the block scales,
+// and the dense dequantization used for checking and adapter merging.
+//
+// Format (news.rkmt.cn/news/4821 §1.2, §1.3, §2.2, §2.3; zky001 section 5.8
+// "NF4" and "double quantization"): 64-element blocks scaled by their absmax,
+// 4-bit NF4 codes, block absmax quantized to 8 bits in groups of 256 blocks
+// with one fp32 constant per group.
+#include "common.h"
+#include "kernels.h"
+
+namespace ql {
+
+// One workgroup per group of 256 blocks (16384 weights, 32 KiB of bf16).
+// Each wave handles 8 blocks per iteration: lane l reads 16 bytes (8 weights)
+// of block l/8, so one wave load is 1 KiB contiguous.  The block absmax is a
+// max over the 8 lanes of the block; encoding needs only the block's own
+// absmax, so codes are written in the same pass and the group max is taken
+// afterwards from LDS.
+__global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict__ W,
+                                                      const float* __restrict__ codebook,
+                                                      uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ qscale,
+                                                      float* __restrict__ step, int64_t nblocks) {
+  __shared__ float s_absmax[kGroup];
+  __shared__ float s_red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t blk0 = (int64_t)blockIdx.x * kGroup;
+  const int nb = (int)min<int64_t>(kGroup, nblocks - blk0);
+
+  float mid[15];
+#pragma unroll
+  for (int i = 0; i < 15; ++i) mid[i] = codebook[16 + i];
+
+#pragma unroll 2
+  for (int it = 0; it < kGroup / 32; ++it) {
+    const int lb = it * 32 + wave * 8 + (lane >> 3);   // local block index
+    const bool valid = lb < nb;
+    u32x4_t raw = {0u, 0u, 0u, 0u};
+    if (valid)
+      raw = *reinterpret_cast<const u32x4_t*>(W + (blk0 + lb) * kBlock + (lane & 7) * 8);
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_lo(raw[j]);
+      x[2 * j + 1] = bf16_hi(raw[j]);
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+    am = fmaxf(am, __shfl_xor(am, 1));
+    am = fmaxf(am, __shfl_xor(am, 2));
+    am = fmaxf(am, __shfl_xor(am, 4));
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // binary32 quotient, correctly rounded (no reciprocal); zero block -> 0
+      const float v = am == 0.f ? 0.f : x[j] / am;
+      uint32_t c = 0;
+#pragma unroll
+      for (int i = 0; i < 15; ++i) c += v > mid[i] ? 1u : 0u;
+      word |= c << (j < 4 ? 8 * j : 8 * (j - 4) + 4);
+    }
+    if (valid) {
+      reinterpret_cast<uint32_t*>(codes)[(blk0 + lb) * 8 + (lane & 7)] = word;
+      if ((lane & 7) == 0) s_absmax[lb] = am;
+    }
+  }
+  __syncthreads();
+  const float a = tid < nb ? s_absmax[tid] : 0.f;
+  const float wm = wave_max(a);
+  if (lane == 0) s_red[wave] = wm;
+  __syncthreads();
+  const float c2 = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  const float st = c2 / 255.0f;
+  if (tid < nb) {
+    const float q = st == 0.f ? 0.f : fminf(rintf(a / st), 255.f);
+    qscale[blk0 + tid] = (uint8_t)q;
+  }
+  if (tid == 0) step[blockIdx.x] = st;
+}
+
+// Dense dequantization: one thread per 64-block, 8 x 16-byte stores.
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
+                                                 const uint8_t* __restrict__ qscale,
+                                                 const float* __restrict__ step,
+                                                 const float* __restrict__ codebook,
+                                                 uint16_t* __restrict__ out, int64_t nblocks) {
+  __shared__ float s_lv[16];
+  if (threadIdx.x < 16) s_lv[threadIdx.x] = codebook[threadIdx.x];
+  __syncthreads();
+  float lv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lv[i] = s_lv[i];
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const Lut t = make_lut(lv, block_scale(qscale, step, b));
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(codes + b * 32);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + b * kBlock);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const u32x4_t w = src[h];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[h * 4 + j] = decode8(t, w[j]);
+  }
+}
+
+hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* codes,
+                           uint8_t* qscale, float* step, int64_t nblocks, hipStream_t s) {
+  const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
+  hipLaunchKernelGGL(k_quant_nf4_dq, dim3((unsigned)ngroups), dim3(256), 0, s, W, codebook, codes,
+                     qscale, step, nblocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
+                          const float* codebook, uint16_t* out, int64_t nblocks, hipStream_t s) {
+  hipLaunchKernelGGL(k_dequant, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, s, codes,
+                     qscale, step, codebook, out, nblocks);
+  return hipGetLastError();
+}
+
+}  // namespace ql

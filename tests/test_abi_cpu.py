@@ -1,0 +1,138 @@
+"""Host-side checks of the C-ABI library: it loads, exports every entry point
+the header declares, its host functions agree with the oracle, and every
+argument error returns its status before any HIP call (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import nf4
+from qlora_fine_tuning_nf4_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"qlora_quantize", "qlora_linear_fwd", "qlora_linear_bwd"} <= set(names)
+    L = B.lib()
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_codebook_matches_oracle_bitwise():
+    lib_cb = B.qlora_nf4_codebook()
+    lv, mid = nf4.codebook()
+    assert np.array_equal(lib_cb[:16].view(np.uint32), lv.view(np.uint32))
+    assert np.array_equal(lib_cb[16:].view(np.uint32), mid.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,k", [(1, 64), (3, 128), (4096, 4096), (11008, 4096), (4096, 11008),
+                                 (28672, 8192), (257, 320)])
+def test_nf4_bytes_matches_oracle(n, k):
+    assert B.qlora_nf4_bytes(n, k) == nf4.nf4_bytes(n, k)
+
+
+def test_nf4_bytes_errors():
+    L = B.lib()
+    z = ctypes.c_size_t()
+    for n, k in [(0, 64), (1, 0), (1, 63), (1, 100), (-1, 64)]:
+        assert L.qlora_nf4_bytes(n, k, ctypes.byref(z), None, None) == 2
+
+
+def test_workspace_bytes_bad_input_and_monotone():
+    L = B.lib()
+    assert L.qlora_workspace_bytes(0, 0, 64, 64, 0) == 0
+    assert L.qlora_workspace_bytes(0, 4, 64, 65, 0) == 0
+    assert L.qlora_workspace_bytes(0, 4, 64, 64, 129) == 0
+    assert L.qlora_workspace_bytes(2, 4, 64, 64, 0) == 0
+    assert L.qlora_workspace_bytes(0, 16, 4096, 4096, 8) >= 16 * 8 * 4
+    assert L.qlora_workspace_bytes(1, 2048, 4096, 4096, 8) >= 2 * 2048 * 8 * 4
+
+
+def test_strerror_covers_codes():
+    for s in range(0, 9):
+        assert B.qlora_strerror(s) != "unknown status"
+    assert B.qlora_strerror(99) == "unknown status"
+
+
+FAKE = 0x100000   # never dereferenced: every call below fails validation first
+
+
+def _desc(n=64, k=128, codes=FAKE, qs=FAKE, st=FAKE):
+    return B._Nf4Desc(n, k, codes, qs, st)
+
+
+def test_quantize_argument_errors():
+    L = B.lib()
+    d = _desc()
+    assert L.qlora_quantize(None, FAKE, ctypes.byref(d), None) == 1
+    assert L.qlora_quantize(FAKE, None, ctypes.byref(d), None) == 1
+    assert L.qlora_quantize(FAKE, FAKE, None, None) == 1
+    assert L.qlora_quantize(FAKE, FAKE, ctypes.byref(_desc(codes=0)), None) == 1
+    assert L.qlora_quantize(FAKE, FAKE, ctypes.byref(_desc(k=100)), None) == 2
+    assert L.qlora_quantize(FAKE, FAKE, ctypes.byref(_desc(n=0)), None) == 2
+    assert L.qlora_quantize(FAKE + 2, FAKE, ctypes.byref(d), None) == 3
+    assert L.qlora_quantize(FAKE, FAKE, ctypes.byref(_desc(codes=FAKE + 8)), None) == 3
+
+
+def _fwd(L, d, X=FAKE, m=16, A=FAKE, Bp=FAKE, r=8, Y=FAKE, ydt=0, T=FAKE, ws=FAKE, wsb=1 << 30,
+         path=0, cb=FAKE):
+    return L.qlora_linear_fwd(ctypes.byref(d) if d is not None else None, cb, X, m, A, Bp, r,
+                              2.0, Y, ydt, T, ws, wsb, path, None)
+
+
+def test_fwd_argument_errors():
+    L = B.lib()
+    d = _desc()
+    assert _fwd(L, None) == 1
+    assert _fwd(L, d, X=None) == 1
+    assert _fwd(L, d, Y=None) == 1
+    assert _fwd(L, d, cb=None) == 1
+    assert _fwd(L, d, A=None) == 1
+    assert _fwd(L, d, m=0) == 2
+    assert _fwd(L, _desc(k=96)) == 2
+    assert _fwd(L, d, r=-1) == 5
+    assert _fwd(L, d, r=129) == 5
+    assert _fwd(L, d, ydt=7) == 4
+    assert _fwd(L, d, path=3) == 8
+    assert _fwd(L, d, path=1, m=65) == 8
+    assert _fwd(L, d, X=FAKE + 2) == 3
+    assert _fwd(L, d, Y=FAKE + 4) == 3
+    assert _fwd(L, d, m=16, wsb=0, T=None) == 6
+    assert _fwd(L, d, m=16, ws=None, T=None) == 6
+
+
+def test_bwd_argument_errors():
+    L = B.lib()
+    d = _desc()
+
+    def bwd(**kw):
+        a = dict(W=ctypes.byref(d), cb=FAKE, X=FAKE, dY=FAKE, m=16, A=FAKE, Bp=FAKE, r=8,
+                 T=FAKE, dX=FAKE, dt=0, dA=FAKE, dB=FAKE, ws=FAKE, wsb=1 << 30, path=0)
+        a.update(kw)
+        return L.qlora_linear_bwd(a["W"], a["cb"], a["X"], a["dY"], a["m"], a["A"], a["Bp"],
+                                  a["r"], 1.0, a["T"], a["dX"], a["dt"], a["dA"], a["dB"],
+                                  a["ws"], a["wsb"], a["path"], None)
+    assert bwd(W=None) == 1
+    assert bwd(dY=None) == 1
+    assert bwd(dA=None) == 1
+    assert bwd(dB=None) == 1
+    assert bwd(X=None) == 1
+    assert bwd(m=0) == 2
+    assert bwd(r=200) == 5
+    assert bwd(dt=5) == 4
+    assert bwd(path=-1) == 8
+    assert bwd(dY=FAKE + 2) == 3
+    assert bwd(dX=FAKE + 4) == 3
+    assert bwd(wsb=16) == 6
+    assert bwd(ws=None) == 6

@@ -1,0 +1,342 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Quantization and dequantization must be bit-exact.  Linear outputs are
+compared in fp32 by relative Frobenius error, bound 2e-3; the measured error
+is far below (fp32 accumulation of exact bf16 products vs. float64).  The LoRA
+branch is about 3 % of Y, so it is also checked alone (W = 0).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import linear as olin
+from oracle import nf4 as onf4
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 2e-3
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from qlora_fine_tuning_nf4_amd import binding
+    binding.lib()
+    return binding
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _t(bits, dev="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def _bits(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _rel(a, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.linalg.norm(np.asarray(a, dtype=np.float64) - ref)
+    den = np.linalg.norm(ref)
+    return num / den if den > 0 else num
+
+
+_LV, _MID = onf4.codebook()
+
+
+def _oracle_q(w_bits):
+    return onf4.quantize(w_bits, _MID)
+
+
+def _oracle_wd(w_bits):
+    c, q, s = _oracle_q(w_bits)
+    return onf4.dequantize(c, q, s, _LV).reshape(w_bits.shape)
+
+
+def _cb(B):
+    return B.device_codebook()
+
+
+# --------------------------------------------------------------------------- quantize
+def _special_weight(n, k, seed):
+    w = synth.normal_bf16((n, k), 0.02, seed)
+    flat = w.reshape(-1)
+    nb = flat.size // 64
+    flat[0:64] = 0                                          # zero block
+    if nb > 2:
+        flat[64:128] = 0x3E80                               # all equal: 0.25
+    if nb > 3:
+        flat[128:192] = 0xBF00                              # all -0.5
+    if nb > 5:
+        flat[5 * 64] = 0xC2C8                               # -100: negative outlier absmax
+    return w
+
+
+@pytest.mark.parametrize("n,k,dist", [
+    (1, 64, "normal"), (3, 128, "special"), (17, 192, "normal"), (300, 64, "special"),
+    (256, 11008, "outlier"), (4096, 4096, "normal"), (1000, 8192, "outlier"),
+    (256, 256, "zero"),
+])
+def test_quantize_bitexact(n, k, dist):
+    B = _dev()
+    _say("quantize", n, k, dist)
+    if dist == "normal":
+        w = synth.normal_bf16((n, k), 0.02, n * 7 + k)
+    elif dist == "outlier":
+        w = synth.normal_bf16((n, k), 0.015, n * 7 + k, outlier_rate=0.001, outlier_scale=20)
+    elif dist == "zero":
+        w = np.zeros((n, k), dtype=np.uint16)
+    else:
+        w = _special_weight(n, k, n + k)
+    q = B.qlora_quantize(_t(w), _cb(B))
+    torch.cuda.synchronize()
+    c, qs, st = _oracle_q(w)
+    assert np.array_equal(q.codes.cpu().numpy(), c)
+    assert np.array_equal(q.qscale.cpu().numpy(), qs)
+    assert np.array_equal(q.step.cpu().numpy().view(np.uint32), st.view(np.uint32))
+
+
+def test_quantize_full_size_sampled():
+    """A 28672 x 8192 projection (70B-style MLP), drawn on the device; sampled
+    groups (two weight rows each) checked against the oracle."""
+    B = _dev()
+    n, k = 28672, 8192
+    _say("quantize full", n, k)
+    W = synth.device_normal_bf16((n, k), 0.015, seed=4001, outlier_rate=0.001, outlier_scale=20)
+    q = B.qlora_quantize(W, _cb(B))
+    torch.cuda.synchronize()
+    rows_per_group = 16384 // k
+    g = synth.rng(5)
+    groups = sorted(set([0, n // rows_per_group - 1] + list(g.integers(0, n // rows_per_group, 24))))
+    codes = q.codes.cpu().numpy()
+    qs = q.qscale.cpu().numpy()
+    st = q.step.cpu().numpy()
+    for gi in groups:
+        r0 = gi * rows_per_group
+        wb = _bits(W[r0:r0 + rows_per_group])
+        c, qq, s = _oracle_q(wb)
+        assert np.array_equal(codes[gi * 8192:(gi + 1) * 8192], c)
+        assert np.array_equal(qs[gi * 256:(gi + 1) * 256], qq)
+        assert st[gi].view(np.uint32) == s[0].view(np.uint32)
+
+
+def test_dequantize_bitexact():
+    B = _dev()
+    n, k = 513, 1024
+    w = synth.normal_bf16((n, k), 0.015, 77, outlier_rate=0.002, outlier_scale=20)
+    q = B.qlora_quantize(_t(w), _cb(B))
+    d = B.qlora_dequantize(q, _cb(B))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(d).reshape(-1), _oracle_wd(w).reshape(-1))
+
+
+# --------------------------------------------------------------------------- fused dequant
+@pytest.mark.parametrize("path", ["gemm", "gemv"])
+def test_fused_dequant_identity_fwd(path):
+    """X = identity rows: each Y element is exactly one product w * 1, so Y
+    must equal the dequantized weight bit for bit (pins the in-kernel decode)."""
+    B = _dev()
+    n, k = 200, 512
+    w = synth.normal_bf16((n, k), 0.02, 91, outlier_rate=0.01, outlier_scale=20)
+    q = B.qlora_quantize(_t(w), _cb(B))
+    wd = onf4.bf16_to_f32(_oracle_wd(w))
+    rows = range(0, k, 64) if path == "gemv" else [range(k)]
+    for r0 in (rows if path == "gemv" else [0]):
+        m = 64 if path == "gemv" else k
+        eye = np.zeros((m, k), dtype=np.float32)
+        eye[np.arange(m), r0 + np.arange(m)] = 1.0
+        X = torch.from_numpy(eye).to(torch.bfloat16).cuda()
+        Y, _ = B.qlora_linear_fwd(q, _cb(B), X, path=path)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy(), wd[:, r0:r0 + m].T), (path, r0)
+
+
+def test_fused_dequant_identity_dx():
+    """dY = identity rows: dX = deq(W) exactly (transposed decode path)."""
+    B = _dev()
+    n, k = 300, 384
+    w = synth.normal_bf16((n, k), 0.02, 92)
+    q = B.qlora_quantize(_t(w), _cb(B))
+    wd = onf4.bf16_to_f32(_oracle_wd(w))
+    dY = torch.eye(n, dtype=torch.float32).to(torch.bfloat16).cuda()
+    dX, _, _ = B.qlora_linear_bwd(q, _cb(B), None, dY)
+    torch.cuda.synchronize()
+    assert np.array_equal(dX.cpu().numpy(), wd)
+
+
+# --------------------------------------------------------------------------- linear parity
+def _inputs(M, N, K, r, seed, wsig=0.02):
+    X = synth.normal_bf16((M, K), 1.0, seed)
+    W = synth.normal_bf16((N, K), wsig, seed + 1)
+    A = synth.normal_bf16((r, K), 0.01, seed + 2)
+    Bm = synth.normal_bf16((N, r), 0.01, seed + 3)
+    dY = synth.normal_bf16((M, N), 1.0, seed + 4)
+    return X, W, A, Bm, dY
+
+
+FWD_CASES = [
+    (1, 64, 64, 0, "gemv"), (1, 4096, 4096, 8, "gemv"), (4, 1000, 1024, 8, "gemv"),
+    (16, 4096, 4096, 8, "gemv"), (33, 257, 320, 16, "gemv"), (64, 300, 512, 8, "gemv"),
+    (5, 100, 192, 4, "gemm"), (16, 4096, 4096, 8, "gemm"), (130, 300, 512, 16, "gemm"),
+    (257, 513, 640, 64, "gemm"), (512, 1024, 1024, 8, "auto"), (96, 2048, 11008, 8, "auto"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,r,path", FWD_CASES)
+def test_forward_parity(M, N, K, r, path):
+    B = _dev()
+    _say("fwd", M, N, K, r, path)
+    s = 2.0
+    X, W, A, Bm, _ = _inputs(M, N, K, r, seed=M * 31 + N * 7 + K + r)
+    q = B.qlora_quantize(_t(W), _cb(B))
+    Yg, Tg = B.qlora_linear_fwd(q, _cb(B), _t(X), _t(A) if r else None, _t(Bm) if r else None,
+                                s, path=path)
+    torch.cuda.synchronize()
+    Wd = _oracle_wd(W)
+    Yo, To = olin.forward(Wd, X, A if r else None, Bm if r else None, s)
+    err = _rel(Yg.cpu().numpy(), Yo)
+    _say(f"  rel_fro(Y) = {err:.3e}")
+    assert err <= REL_TOL
+    if r:
+        errT = _rel(Tg.cpu().numpy(), To)
+        assert errT <= REL_TOL, errT
+
+
+@pytest.mark.parametrize("M,N,K,r,path", [(16, 512, 1024, 8, "gemv"), (200, 384, 512, 16, "gemm")])
+def test_forward_lora_only(M, N, K, r, path):
+    """W = 0 isolates the LoRA branch, which is only ~3 % of Y otherwise."""
+    B = _dev()
+    s = 2.0
+    X, _, A, Bm, _ = _inputs(M, N, K, r, seed=5)
+    W = np.zeros((N, K), dtype=np.uint16)
+    q = B.qlora_quantize(_t(W), _cb(B))
+    Yg, _ = B.qlora_linear_fwd(q, _cb(B), _t(X), _t(A), _t(Bm), s, path=path)
+    torch.cuda.synchronize()
+    Yo, _ = olin.forward(_oracle_wd(W), X, A, Bm, s)
+    err = _rel(Yg.cpu().numpy(), Yo)
+    _say(f"  lora-only rel_fro = {err:.3e}")
+    assert err <= REL_TOL
+
+
+def test_forward_bf16_output_within_one_ulp():
+    B = _dev()
+    M, N, K, r = 64, 512, 1024, 8
+    X, W, A, Bm, _ = _inputs(M, N, K, r, seed=9)
+    q = B.qlora_quantize(_t(W), _cb(B))
+    for path in ("gemv", "gemm"):
+        Yg, _ = B.qlora_linear_fwd(q, _cb(B), _t(X), _t(A), _t(Bm), 2.0, y_dtype=torch.bfloat16,
+                                   path=path)
+        torch.cuda.synchronize()
+        Yo, _ = olin.forward(_oracle_wd(W), X, A, Bm, 2.0)
+        yo = onf4.bf16_to_f32(onf4.f32_to_bf16_rne(Yo.astype(np.float32)))
+        yg = Yg.float().cpu().numpy()
+        ulp = np.spacing(np.abs(yo).astype(np.float32)) * 65536.0
+        assert np.all(np.abs(yg - yo) <= ulp + 1e-30), path
+
+
+BWD_CASES = [(1, 64, 64, 2), (16, 4096, 4096, 8), (5, 100, 192, 4), (130, 300, 512, 16),
+             (257, 513, 640, 64), (512, 1024, 1024, 8), (33, 11008, 256, 8)]
+
+
+@pytest.mark.parametrize("M,N,K,r", BWD_CASES)
+def test_backward_parity(M, N, K, r):
+    B = _dev()
+    _say("bwd", M, N, K, r)
+    s = 2.0
+    X, W, A, Bm, dY = _inputs(M, N, K, r, seed=M * 13 + N + K * 3 + r)
+    q = B.qlora_quantize(_t(W), _cb(B))
+    Xd, Ad, Bd, dYd = _t(X), _t(A), _t(Bm), _t(dY)
+    _, T = B.qlora_linear_fwd(q, _cb(B), Xd, Ad, Bd, s)
+    dXg, dAg, dBg = B.qlora_linear_bwd(q, _cb(B), Xd, dYd, Ad, Bd, s, T=T)
+    dXr, dAr, dBr = B.qlora_linear_bwd(q, _cb(B), Xd, dYd, Ad, Bd, s, T=None)   # recompute T
+    torch.cuda.synchronize()
+    dXo, dAo, dBo = olin.backward(_oracle_wd(W), X, dY, A, Bm, s)
+    e = (_rel(dXg.cpu().numpy(), dXo), _rel(dAg.cpu().numpy(), dAo), _rel(dBg.cpu().numpy(), dBo))
+    _say(f"  rel_fro dX {e[0]:.3e} dA {e[1]:.3e} dB {e[2]:.3e}")
+    assert max(e) <= REL_TOL
+    assert torch.equal(dXg, dXr) and torch.equal(dAg, dAr) and torch.equal(dBg, dBr)
+
+
+def test_backward_lora_only_and_r0():
+    B = _dev()
+    M, N, K, r = 40, 320, 512, 8
+    X, W, A, Bm, dY = _inputs(M, N, K, r, seed=17)
+    Z = np.zeros_like(W)
+    q = B.qlora_quantize(_t(Z), _cb(B))
+    dXg, _, _ = B.qlora_linear_bwd(q, _cb(B), _t(X), _t(dY), _t(A), _t(Bm), 0.5)
+    q2 = B.qlora_quantize(_t(W), _cb(B))
+    dX0, dA0, dB0 = B.qlora_linear_bwd(q2, _cb(B), None, _t(dY))
+    torch.cuda.synchronize()
+    dXo, _, _ = olin.backward(_oracle_wd(Z), X, dY, A, Bm, 0.5)
+    assert _rel(dXg.cpu().numpy(), dXo) <= REL_TOL
+    dXo0, _, _ = olin.backward(_oracle_wd(W), X, dY)
+    assert dA0 is None and dB0 is None
+    assert _rel(dX0.cpu().numpy(), dXo0) <= REL_TOL
+
+
+# --------------------------------------------------------------------------- full sizes (sampled)
+@pytest.mark.parametrize("N,K", [(4096, 4096), (11008, 4096), (4096, 11008)])
+def test_full_size_layer_sampled(N, K):
+    """7B-style projection at M = 2048 tokens (the launch configuration the
+    bench times): full GPU fwd + bwd, oracle on sampled rows and columns."""
+    B = _dev()
+    M, r, s = 2048, 8, 2.0
+    _say("full", M, N, K)
+    X, W, A, Bm, dY = _inputs(M, N, K, r, seed=N + K)
+    q = B.qlora_quantize(_t(W), _cb(B))
+    Xd, Ad, Bd, dYd = _t(X), _t(A), _t(Bm), _t(dY)
+    Y, T = B.qlora_linear_fwd(q, _cb(B), Xd, Ad, Bd, s)
+    dX, dA, dB = B.qlora_linear_bwd(q, _cb(B), Xd, dYd, Ad, Bd, s, T=T)
+    torch.cuda.synchronize()
+    g = synth.rng(N * 3 + K)
+    ms = np.sort(g.choice(M, 24, replace=False))
+    ns = np.sort(g.choice(N, 48, replace=False))
+    Wd = _oracle_wd(W)
+    Yo, _ = olin.forward(Wd[ns], X[ms], A, Bm[ns], s)
+    assert _rel(Y.cpu().numpy()[np.ix_(ms, ns)], Yo) <= REL_TOL
+    dXo = olin.backward(Wd, X[ms], dY[ms], A, Bm, s)[0]
+    assert _rel(dX.cpu().numpy()[ms], dXo) <= REL_TOL
+    # adapter gradients reduce over all M: full oracle for dA rows, sampled dB rows
+    dXf, dAo, dBo_full = None, None, None
+    xf, dyf = onf4.bf16_to_f32(X).astype(np.float64), onf4.bf16_to_f32(dY).astype(np.float64)
+    af, bf = onf4.bf16_to_f32(A).astype(np.float64), onf4.bf16_to_f32(Bm).astype(np.float64)
+    U = dyf @ bf
+    dAo = s * U.T @ xf
+    dBo = s * dyf[:, ns].T @ (xf @ af.T)
+    assert _rel(dA.cpu().numpy(), dAo) <= REL_TOL
+    assert _rel(dB.cpu().numpy()[ns], dBo) <= REL_TOL
+
+
+# --------------------------------------------------------------------------- robustness
+def test_deterministic_and_nan_poisoned_outputs():
+    B = _dev()
+    M, N, K, r = 130, 700, 1024, 8
+    X, W, A, Bm, dY = _inputs(M, N, K, r, seed=23)
+    q = B.qlora_quantize(_t(W), _cb(B))
+    Xd, Ad, Bd, dYd = _t(X), _t(A), _t(Bm), _t(dY)
+    outs = []
+    for rep in range(2):
+        Y = torch.full((M, N), float("nan"), device="cuda")
+        dX = torch.full((M, K), float("nan"), device="cuda")
+        dA = torch.full((r, K), float("nan"), device="cuda")
+        dB = torch.full((N, r), float("nan"), device="cuda")
+        _, T = B.qlora_linear_fwd(q, _cb(B), Xd, Ad, Bd, 2.0, out=Y)
+        B.qlora_linear_bwd(q, _cb(B), Xd, dYd, Ad, Bd, 2.0, T=T, dX_out=dX, dA_out=dA, dB_out=dB)
+        torch.cuda.synchronize()
+        for t in (Y, dX, dA, dB):
+            assert not torch.isnan(t).any()
+        outs.append([t.clone() for t in (Y, dX, dA, dB)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    for M2 in (1, 16, 48):
+        Ys = [B.qlora_linear_fwd(q, _cb(B), Xd[:M2].contiguous(), Ad, Bd, 2.0, path="gemv")[0]
+              for _ in range(2)]
+        torch.cuda.synchronize()
+        assert torch.equal(Ys[0], Ys[1])
