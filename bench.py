@@ -211,9 +211,9 @@ def main():
     tf, ff, nf = kstats(ev_fwd)
     td, fd, nd = kstats(ev_dx)
     if td >= tf:
-        kname, t_tot, f_tot, n_l, srcs = "k_gemm_dx", td, fd, nd, ["gemm_dx.hip", "common.h"]
+        kname, t_tot, f_tot, n_l, srcs = "k_gemm_dx", td, fd, nd, ["gemm.hip", "common.h"]
     else:
-        kname, t_tot, f_tot, n_l, srcs = "k_gemm_fwd", tf, ff, nf, ["gemm_fwd.hip", "common.h"]
+        kname, t_tot, f_tot, n_l, srcs = "k_gemm_fwd", tf, ff, nf, ["gemm.hip", "common.h"]
     achieved = (f_tot / n_l) / (t_tot / n_l) / 1e12
     roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -76,17 +76,19 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int path) {
     const int64_t cap = std::max<int64_t>(1, nquads / 4);
     p.ksplit = (int)std::min<int64_t>(cap, std::max<int64_t>(1, cdiv(1024, ntiles)));
   } else {
-    const int64_t tiles = cdiv(m, 128) * cdiv(n, 128), nsteps = cdiv(k, 128);
-    const int64_t cap = std::max<int64_t>(1, nsteps / 2);
-    p.ksplit = tiles >= 256 ? 1 : (int)std::min<int64_t>(cap, cdiv(512, tiles));
+    // 256 x 128 output tiles, 64-deep steps; split the contraction only when
+    // the tiles cannot fill the 256 CUs
+    const int64_t tiles = cdiv(m, 256) * cdiv(n, 128), nsteps = cdiv(k, 64);
+    const int64_t cap = std::max<int64_t>(1, nsteps / 4);
+    p.ksplit = tiles >= 192 ? 1 : (int)std::min<int64_t>(cap, cdiv(256, tiles));
   }
   return p;
 }
 
 int plan_dx_split(int64_t m, int64_t n, int64_t k) {
-  const int64_t tiles = cdiv(m, 128) * cdiv(k, 128), nsteps = cdiv(n, 128);
-  const int64_t cap = std::max<int64_t>(1, nsteps / 2);
-  return tiles >= 256 ? 1 : (int)std::min<int64_t>(cap, cdiv(512, tiles));
+  const int64_t tiles = cdiv(m, 256) * cdiv(k, 128), nsteps = cdiv(n, 64);
+  const int64_t cap = std::max<int64_t>(1, nsteps / 4);
+  return tiles >= 192 ? 1 : (int)std::min<int64_t>(cap, cdiv(256, tiles));
 }
 
 int plan_wgrad_split(int64_t m, int64_t c, int r) {

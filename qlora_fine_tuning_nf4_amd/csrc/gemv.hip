@@ -5,10 +5,7 @@
 // www.lqnn.cn/news/228537 §3.3 and zky001 section 5.8: dequantize to 16 bits
 // for the product, then discard).
 //
-// Two kernels:
-//  * k_gemm_fwd  -- large M: 128x128 output tiles, K-steps of 128 (two quant
-//    blocks per weight row), bf16 MFMA 16x16x32 with fp32 accumulation.  Each
-//    thread decodes one 64-block per K-step into the LDS tile.
+// Small-M forward (the large-M GEMMs are in gemm.hip) and the split-K reduce.
 //  * k_gemv_fwd  -- small M (<= 64): a wave owns 16 weight rows and streams
 //    their packed bytes; each lane decodes a whole 64-block (one lookup table
 //    per block) and feeds eight MFMAs whose 32-wide contraction spans four
@@ -17,8 +14,6 @@
 #include "kernels.h"
 
 namespace ql {
-
-constexpr int FBM = 128, FBN = 128, FBK = 128, FLD = FBK + 8;
 
 QL_DEV float lora_dot(const LoraTerm& L, int64_t m, int64_t c) {
   float acc = 0.f;
@@ -33,116 +28,6 @@ QL_DEV void store_out(void* out, bool bf16, int64_t idx, float v) {
     reinterpret_cast<uint16_t*>(out)[idx] = to_bf16(v);
   else
     reinterpret_cast<float*>(out)[idx] = v;
-}
-
-__global__ __launch_bounds__(256) void k_gemm_fwd(const uint16_t* __restrict__ X, Nf4View w,
-                                                  const float* __restrict__ codebook, int64_t M,
-                                                  LoraTerm lora, void* __restrict__ Y, int y_bf16,
-                                                  float* __restrict__ part, int ksplit,
-                                                  int steps_per_split) {
-  __shared__ __attribute__((aligned(16))) uint16_t sX[FBM * FLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[FBN * FLD];
-  __shared__ float s_lv[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t N = w.n, K = w.k, nkb = K / kBlock;
-  const int64_t n0 = (int64_t)blockIdx.x * FBN, m0 = (int64_t)blockIdx.y * FBM;
-  const int split = blockIdx.z;
-  const int nsteps = (int)((K + FBK - 1) / FBK);
-  const int s_begin = split * steps_per_split;
-  const int s_end = min(nsteps, s_begin + steps_per_split);
-  if (tid < 16) s_lv[tid] = codebook[tid];
-  __syncthreads();
-  float lv[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) lv[i] = s_lv[i];
-
-  u32x4_t xr[8];
-  u32x4_t wc0, wc1;
-  float wsc;
-  const int wrow = tid >> 1, whalf = tid & 1;
-  auto load = [&](int st) {
-    const int64_t k0 = (int64_t)st * FBK;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i, row = c >> 4, col = (c & 15) * 8;
-      const int64_t m = m0 + row, k = k0 + col;
-      xr[i] = (m < M && k < K) ? *reinterpret_cast<const u32x4_t*>(X + m * K + k)
-                               : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    const int64_t n = n0 + wrow, kb = k0 / kBlock + whalf;
-    if (n < N && kb < nkb) {
-      const int64_t b = n * nkb + kb;
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w.codes + b * 32);
-      wc0 = src[0];
-      wc1 = src[1];
-      wsc = block_scale(w.qscale, w.step, b);
-    } else {
-      wc0 = u32x4_t{0u, 0u, 0u, 0u};
-      wc1 = wc0;
-      wsc = 0.f;
-    }
-  };
-
-  f32x4_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int wm = wave & 1, wn = wave >> 1;
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  if (s_begin < s_end) load(s_begin);
-  for (int st = s_begin; st < s_end; ++st) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i, row = c >> 4, col = (c & 15) * 8;
-      *reinterpret_cast<u32x4_t*>(sX + row * FLD + col) = xr[i];
-    }
-    {
-      const Lut t = make_lut(lv, wsc);
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(sW + wrow * FLD + whalf * 64);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[j] = decode8(t, wc0[j]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[4 + j] = decode8(t, wc1[j]);
-    }
-    __syncthreads();
-    if (st + 1 < s_end) load(st + 1);
-#pragma unroll
-    for (int kk = 0; kk < FBK / 32; ++kk) {
-      u32x4_t a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const u32x4_t*>(sX + (wm * 64 + i * 16 + fr) * FLD + kk * 32 + fk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const u32x4_t*>(sW + (wn * 64 + j * 16 + fr) * FLD + kk * 32 + fk);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
-        const int64_t n = n0 + wn * 64 + j * 16 + fr;
-        if (m < M && n < N) {
-          float v = acc[i][j][e];
-          if (ksplit > 1) {
-            part[((int64_t)split * M + m) * N + n] = v;
-          } else {
-            if (lora.r > 0) v += lora.scaling * lora_dot(lora, m, n);
-            store_out(Y, y_bf16, m * N + n, v);
-          }
-        }
-      }
 }
 
 template <int MT>
@@ -230,17 +115,6 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, 
   for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * M * C + idx];
   if (lora.r > 0) v += lora.scaling * lora_dot(lora, idx / C, idx % C);
   store_out(out, out_bf16, idx, v);
-}
-
-hipError_t launch_gemm_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,
-                           const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
-                           hipStream_t s) {
-  const int nsteps = (int)((w.k + FBK - 1) / FBK);
-  const int per = (nsteps + ksplit - 1) / ksplit;
-  dim3 grid((unsigned)((w.n + FBN - 1) / FBN), (unsigned)((M + FBM - 1) / FBM), (unsigned)ksplit);
-  hipLaunchKernelGGL(k_gemm_fwd, grid, dim3(256), 0, s, X, w, codebook, M, lora, Y, (int)y_bf16,
-                     part, ksplit, per);
-  return hipGetLastError();
 }
 
 hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,
