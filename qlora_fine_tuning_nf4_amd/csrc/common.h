@@ -29,10 +29,14 @@ QL_DEV uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
   return __builtin_amdgcn_perm(s0, s1, sel);
 }
 
-// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair, round to nearest even, in one
+// v_cvt_pk_bf16_f32.
 QL_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const bf16x2_t v = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 QL_DEV uint16_t to_bf16(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
@@ -61,16 +65,19 @@ QL_DEV Lut make_lut(const float* lv, float s) {
 }
 
 // Decode one packed word (elements 8w .. 8w+7: byte j = code j | code j+4 << 4)
-// into 8 bf16 values in element order, as 4 packed pairs.
+// into 8 bf16 values in element order, as 4 packed pairs.  Each byte plane is
+// looked up twice (entries 0-7 and 8-15, selected by the low three code
+// bits), then a third v_perm picks, per byte, the lookup that matches code
+// bit 3 (selector j or j+4).
 QL_DEV u32x4_t decode8(const Lut& t, uint32_t x) {
-  const uint32_t sa = x & 0x07070707u;          // codes 0..3, low three bits
-  const uint32_t sb = (x >> 4) & 0x07070707u;   // codes 4..7
-  const uint32_t ma = ((x >> 3) & 0x01010101u) * 0xFFu;   // 0xFF where code >= 8
-  const uint32_t mb = ((x >> 7) & 0x01010101u) * 0xFFu;
-  const uint32_t loa = (ma & perm(t.lo[3], t.lo[2], sa)) | (~ma & perm(t.lo[1], t.lo[0], sa));
-  const uint32_t hia = (ma & perm(t.hi[3], t.hi[2], sa)) | (~ma & perm(t.hi[1], t.hi[0], sa));
-  const uint32_t lob = (mb & perm(t.lo[3], t.lo[2], sb)) | (~mb & perm(t.lo[1], t.lo[0], sb));
-  const uint32_t hib = (mb & perm(t.hi[3], t.hi[2], sb)) | (~mb & perm(t.hi[1], t.hi[0], sb));
+  const uint32_t sa = x & 0x07070707u;                            // codes 0..3, low bits
+  const uint32_t sb = (x >> 4) & 0x07070707u;                     // codes 4..7
+  const uint32_t ka = ((x >> 1) & 0x04040404u) | 0x03020100u;     // bit 3 of codes 0..3
+  const uint32_t kb = ((x >> 5) & 0x04040404u) | 0x03020100u;     // bit 3 of codes 4..7
+  const uint32_t loa = perm(perm(t.lo[3], t.lo[2], sa), perm(t.lo[1], t.lo[0], sa), ka);
+  const uint32_t hia = perm(perm(t.hi[3], t.hi[2], sa), perm(t.hi[1], t.hi[0], sa), ka);
+  const uint32_t lob = perm(perm(t.lo[3], t.lo[2], sb), perm(t.lo[1], t.lo[0], sb), kb);
+  const uint32_t hib = perm(perm(t.hi[3], t.hi[2], sb), perm(t.hi[1], t.hi[0], sb), kb);
   u32x4_t o;
   o[0] = perm(hia, loa, 0x05010400u);
   o[1] = perm(hia, loa, 0x07030602u);

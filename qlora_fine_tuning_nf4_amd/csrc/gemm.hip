@@ -8,15 +8,20 @@
 // discard).
 //
 // gfx950 design:
-//  * 256 x 128 output tile per workgroup, 4 waves; wave w owns rows
-//    [64w, 64w+64) and all 128 columns: 2 x 4 MFMA 32x32x16 bf16 tiles with
-//    fp32 accumulators (128 per lane).
-//  * The activation operand (X or dY) streams global -> registers directly in
-//    the MFMA A layout, one K-step ahead; it never touches LDS.
+//  * 256 x 128 output tile per workgroup, 8 waves (two per SIMD, so one
+//    wave's LDS/barrier latency and decode work overlap the other's MFMAs);
+//    wave w owns the 64 x 64 sub-tile (w%4, w/4): 2 x 2 MFMA 32x32x16 bf16
+//    tiles with fp32 accumulators.
+//  * The activation operand (X or dY) goes global -> LDS with the gfx950
+//    global_load_lds b128 DMA (no registers, each wave load covers 8 whole
+//    128-byte row pieces) into a 3-stage ring, two K-steps ahead.  16-byte
+//    chunks are XOR-swizzled by row so the MFMA fragment reads are free of
+//    bank conflicts.
 //  * The weight tile of each K-step (128 x 64 weights = 128 NF4 blocks) is
-//    decoded by all 256 threads, half a block each, into a double-buffered LDS
-//    stage; the decode of step s+1 overlaps the MFMAs of step s, one barrier
-//    per step.  Decoding is amortized over 256 output rows.
+//    decoded by the 256 threads of waves 0-3 (one per SIMD), half a block
+//    each, into a double-buffered LDS stage; the decode of step s+1 is
+//    interleaved with the MFMAs of step s, one barrier per step.  Decoding is
+//    amortized over 256 output rows.
 //  * Forward reads B fragments with ds_read_b128 from the [n][k] stage; the
 //    backward contracts over n and reads them with the transposing
 //    ds_read_b64_tr_b16 from a [n][k] stage.
@@ -78,18 +83,47 @@ QL_DEV int64_t logical_tile(int64_t id, int64_t total) {
   return xcd * base + (xcd < rem ? xcd : rem) + slot;
 }
 
-template <bool DX>
-__global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ act, Nf4View w,
-                                              const float* __restrict__ codebook, int64_t M,
-                                              LoraTerm lora, void* __restrict__ out, int out_bf16,
-                                              float* __restrict__ part, int ksplit,
-                                              int steps_per_split, int64_t mtiles, int64_t otiles) {
+constexpr int NA = 3;                 // activation stages in the DMA ring
+constexpr int A_STAGE = GBM * GBK;     // bf16 elements per activation stage (32 KiB)
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8).
+#define QL_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | 0x0F70)
+#define QL_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+// Workgroup barrier for the K loop.  __syncthreads() would add a release
+// fence, and with LDS DMA in flight that fence waits for every outstanding
+// vector load (vmcnt 0), draining the prefetch pipeline at each step.  Here
+// the caller states the vmcnt it needs; this waits for the wave's own LDS
+// traffic and the empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+QL_DEV void k_barrier() {
+  QL_LGKMCNT0();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Physical 16-byte chunk of logical chunk c in activation row r of a stage.
+QL_DEV int a_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+template <bool DX, bool VEC>
+__global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ act, Nf4View w,
+                                                 const float* __restrict__ codebook, int64_t M,
+                                                 LoraTerm lora, void* __restrict__ out, int out_bf16,
+                                                 float* __restrict__ part, int ksplit,
+                                                 int steps_per_split, int64_t mtiles, int64_t otiles) {
   using G = Geo<DX>;
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][G::stage];
+  extern __shared__ __attribute__((aligned(16))) uint16_t sA[];   // [NA][GBM rows][GBK], swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2 * G::stage];   // decoded weight stages
   __shared__ float s_lv[16];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index in an SGPR, so role branches below are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;                  // 64-row block, 64-column half
   const int lr = lane & 31, lg = lane >> 5;
+  const bool decoder = wave < 4;                             // one decoding wave per SIMD
   const int64_t N = w.n, K = w.k, nkb = K / kBlock;
   const int64_t C = DX ? N : K;       // contraction length
   const int64_t O = DX ? K : N;       // output columns
@@ -108,110 +142,194 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ act, 
 
   if (tid < 16) s_lv[tid] = codebook[tid];
 
-  // ---- per-thread roles
-  const bool vec = DX ? (N % 8) == 0 : true;
-  const int64_t arow0 = m0 + wave * 64 + lr;                // + 32*mt
-  // weight decode role: half a 64-block
-  const int half = tid & 1;
-  const int wr = DX ? (tid >> 2) : (tid >> 1);              // stage row
-  const int wcb = DX ? ((tid >> 1) & 1) : 0;                // block within the stage row (dx)
+  // decode role of threads 0..255: half a 64-block each
+  const int dt = tid & 255;
+  const int half = dt & 1;
+  const int wr = DX ? (dt >> 2) : (dt >> 1);                // stage row
+  const int wcb = DX ? ((dt >> 1) & 1) : 0;                 // block within the stage row (dx)
 
-  auto load_a = [&](int st, u32x4_t (&a)[4][2]) {
+  // Activation tile of step st into ring stage `stage`: wave w fills rows
+  // [32w, 32w+32) with 4 DMA loads of 8 rows; lane l lands at byte 16l of its
+  // load's 1 KiB, i.e. row l/8, physical chunk l%8.  Rows past M and columns
+  // past the contraction are clamped (products discarded or against zero
+  // weights).
+  // per-lane source of each of the 4 DMA loads: row base and the largest
+  // step offset that keeps the 8-element piece inside the row
+  const uint16_t* a_src[4];
+  int64_t a_cmax[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = wave * 32 + i * 8 + (lane >> 3);
+    const int lc = a_chunk(rl, lane & 7);
+    a_src[i] = act + min(m0 + rl, M - 1) * C + lc * 8;
+    a_cmax[i] = C - 8 - lc * 8;
+  }
+  auto fill_a = [&](int st, int stage) {
     const int64_t c0 = (int64_t)st * GBK;
+    uint16_t* base = sA + stage * A_STAGE;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int64_t row = arow0 + 32 * mt, c = c0 + 16 * kk + 8 * lg;
-        a[kk][mt] = (row < M && c < C) ? load_act8(act + row * C, c, C, vec && c + 8 <= C)
-                                       : u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 4; ++i) {
+      uint16_t* dst = base + (wave * 32 + i * 8) * GBK;
+      if (VEC) {
+        __builtin_amdgcn_global_load_lds(a_src[i] + min(c0, a_cmax[i]),
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      } else {
+        const int rl = wave * 32 + i * 8 + (lane >> 3);
+        const int64_t row = min(m0 + rl, M - 1);
+        const int64_t c = c0 + a_chunk(rl, lane & 7) * 8;
+        const u32x4_t v = c < C ? load_act8(act + row * C, c, C, false) : u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(dst + lane * 8) = v;
       }
+    }
   };
-  auto load_w = [&](int st, u32x4_t& codes, float& sc) {
-    int64_t n, kb;
-    if (DX) {
-      n = (int64_t)st * GBK + wr;
-      kb = o0 / kBlock + wcb;
-    } else {
-      n = o0 + wr;
-      kb = st;
-    }
-    if (n < N && kb < nkb) {
-      const int64_t b = n * nkb + kb;
-      codes = *reinterpret_cast<const u32x4_t*>(w.codes + b * 32 + half * 16);
-      sc = block_scale(w.qscale, w.step, b);
-    } else {
-      codes = u32x4_t{0u, 0u, 0u, 0u};
-      sc = 0.f;
-    }
+
+  struct WRaw {
+    u32x4_t codes;
+    uint32_t qword;   // the aligned dword holding the block's 8-bit scale
+    uint32_t qshift;  // its bit offset in qword
+    float step;
+    bool ok;
+  };
+  // block index of this thread's half-block at step st: b0 + st * bstride
+  // (forward: along the row; backward: down the rows)
+  const int64_t b0 = DX ? (int64_t)wr * nkb + o0 / kBlock + wcb : (o0 + wr) * nkb;
+  const int64_t bstride = DX ? GBK * nkb : 1;
+  const bool w_ok_fixed = DX ? (o0 / kBlock + wcb) < nkb : (o0 + wr) < N;
+  auto load_w = [&](int st, WRaw& r) {
+    r.ok = w_ok_fixed && (!DX || (int64_t)st * GBK + wr < N);
+    const int64_t b = r.ok ? b0 + st * bstride : 0;
+    r.codes = *reinterpret_cast<const u32x4_t*>(w.codes + b * 32 + half * 16);
+    r.qword = *reinterpret_cast<const uint32_t*>(w.qscale + (b & ~int64_t(3)));
+    r.qshift = (uint32_t)(b & 3) * 8;
+    r.step = w.step[b >> 8];
   };
   __syncthreads();
   float lv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) lv[i] = s_lv[i];
-  auto decode_w = [&](int stage, const u32x4_t codes, float sc) {
-    const Lut t = make_lut(lv, sc);
-    uint16_t* base = &sW[stage][wr * G::ld + wcb * 64 + half * 32];
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(base);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dst[j] = decode8(t, codes[j]);
-  };
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[2][2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
 
+  auto read_a = [&](const uint16_t* sa, int kk, u32x4_t (&a)[2]) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int r = wm * 64 + 32 * mt + lr;
+      a[mt] = *reinterpret_cast<const u32x4_t*>(sa + r * GBK + a_chunk(r, 2 * kk + lg) * 8);
+    }
+  };
+  auto read_b = [&](const uint16_t* sw, int kk, u32x4_t (&b)[2]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      if (DX) {
+        const int G16 = lane >> 4, i16 = lane & 15;
+        const int row = 16 * kk + 8 * (G16 >> 1) + (i16 >> 2);
+        const int col = wn * 64 + 32 * nt + 16 * (G16 & 1) + 4 * (i16 & 3);
+        const u32x2_t lo = ds_tr16(sw + row * G::ld + col);
+        const u32x2_t hi = ds_tr16(sw + (row + 4) * G::ld + col);
+        b[nt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      } else {
+        b[nt] = *reinterpret_cast<const u32x4_t*>(sw + (wn * 64 + 32 * nt + lr) * G::ld + 16 * kk + 8 * lg);
+      }
+    }
+  };
+
   if (s_begin < s_end) {
-    u32x4_t acur[4][2], anext[4][2];
-    u32x4_t wc, wc_next = {0u, 0u, 0u, 0u};
-    float ws, ws_next = 0.f;
-    load_w(s_begin, wc, ws);
-    load_a(s_begin, acur);
-    decode_w(0, wc, ws);
-    if (s_begin + 1 < s_end) load_w(s_begin + 1, wc, ws);
+    const int last = s_end - 1;
+    // prologue: activation stages of steps s_begin, s_begin+1; decoded weight
+    // stage 0 of s_begin; codes of s_begin+1 (w0) and s_begin+2 (w1)
+    WRaw w0, w1;
+    fill_a(s_begin, 0);
+    fill_a(min(s_begin + 1, last), 1);
+    if (decoder) {
+      WRaw wf;
+      load_w(s_begin, wf);
+      load_w(min(s_begin + 1, last), w0);
+      load_w(min(s_begin + 2, last), w1);
+      const Lut t = make_lut(lv, wf.ok ? (float)((wf.qword >> wf.qshift) & 0xFFu) * wf.step : 0.f);
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(sW + wr * G::ld + wcb * 64 + half * 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[j] = decode8(t, wf.codes[j]);
+    }
+    QL_VMCNT(0);
     __syncthreads();
 
-    for (int st = s_begin; st < s_end; ++st) {
-      const int stage = (st - s_begin) & 1;
-      const bool more = st + 1 < s_end;
-      if (more) load_a(st + 1, anext);
-      if (st + 2 < s_end) load_w(st + 2, wc_next, ws_next);
-      const uint16_t* sw = sW[stage];
+    // One K-step t: MFMAs on activation stage t%3 and weight stage (t-s)&1;
+    // the DMA of step t+2 is issued first; decoding waves also decode the
+    // codes of step t+1 (`wd`) into the other weight stage between their
+    // MFMAs and then refill `wd` with the codes of step t+3 (consumed two
+    // steps later).  Loads are unconditional (clamped step index).
+    auto kstep = [&](int st, WRaw& wd, bool dec) {
+      const int rel = st - s_begin;
+      const int wstage = rel & 1;
+      Lut t;
+      if (dec) {
+        // `wd` was loaded at the end of step t-2; issued since: DMA of t+1 (4)
+        // and the codes of t+2 (3)
+        if (VEC) QL_VMCNT(7); else QL_VMCNT(0);
+        t = make_lut(lv, wd.ok ? (float)((wd.qword >> wd.qshift) & 0xFFu) * wd.step : 0.f);
+      }
+      fill_a(min(st + 2, last), (rel + 2) % NA);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t* sa = sA + (rel % NA) * A_STAGE;
+      const uint16_t* sw = sW + wstage * G::stage;
+      u32x4_t* dst =
+          reinterpret_cast<u32x4_t*>(sW + (wstage ^ 1) * G::stage + wr * G::ld + wcb * 64 + half * 32);
+      u32x4_t ac[2], an[2], bc[2], bn[2];
+      read_a(sa, 0, ac);
+      read_b(sw, 0, bc);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        u32x4_t b[4];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          if (DX) {
-            const int G16 = lane >> 4, i16 = lane & 15;
-            const int row = 16 * kk + 8 * (G16 >> 1) + (i16 >> 2);
-            const int col = 32 * nt + 16 * (G16 & 1) + 4 * (i16 & 3);
-            const u32x2_t lo = ds_tr16(sw + row * G::ld + col);
-            const u32x2_t hi = ds_tr16(sw + (row + 4) * G::ld + col);
-            b[nt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-          } else {
-            b[nt] = *reinterpret_cast<const u32x4_t*>(sw + (32 * nt + lr) * G::ld + 16 * kk + 8 * lg);
-          }
+        if (kk < 3) {
+          read_a(sa, kk + 1, an);
+          read_b(sw, kk + 1, bn);
         }
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma32(acur[kk][mt], b[nt], acc[mt][nt]);
-      }
-      if (more) decode_w(stage ^ 1, wc, ws);
-      __syncthreads();
-      if (more) {
+          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(ac[mt], bc[nt], acc[mt][nt]);
+        if (dec) {
+          dst[kk] = decode8(t, wd.codes[kk]);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) acur[kk][mt] = anext[kk][mt];
-        wc = wc_next;
-        ws = ws_next;
+          for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // then up to eight VALU
+          }
+        }
+        if (kk < 3) {
+          ac[0] = an[0];
+          ac[1] = an[1];
+          bc[0] = bn[0];
+          bc[1] = bn[1];
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (dec) {
+        load_w(min(st + 3, last), wd);
+        // DMA of t+1 was issued a step ago; issued after it: codes of t+2 (3),
+        // DMA of t+2 (4), codes of t+3 (3)
+        if (VEC) QL_VMCNT(10); else QL_VMCNT(0);
+      } else {
+        // issued after the DMA of t+1: the DMA of t+2 (4)
+        if (VEC) QL_VMCNT(4); else QL_VMCNT(0);
+      }
+      k_barrier();
+    };
+
+    if (decoder) {
+      int st = s_begin;
+      for (; st + 1 < s_end; st += 2) {
+        kstep(st, w0, true);
+        kstep(st + 1, w1, true);
+      }
+      if (st < s_end) kstep(st, w0, true);
+    } else {
+      for (int st = s_begin; st < s_end; ++st) kstep(st, w0, false);
     }
   }
 
@@ -219,11 +337,11 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ act, 
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int64_t m = m0 + wave * 64 + 32 * mt + 8 * (i >> 2) + 4 * lg + (i & 3);
-        const int64_t o = o0 + 32 * nt + lr;
+        const int64_t m = m0 + wm * 64 + 32 * mt + 8 * (i >> 2) + 4 * lg + (i & 3);
+        const int64_t o = o0 + wn * 64 + 32 * nt + lr;
         if (m < M && o < O) {
           float v = acc[mt][nt][i];
           if (ksplit > 1) {
@@ -240,6 +358,29 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ act, 
 }
 
 template <bool DX>
+static constexpr size_t smem_bytes() {
+  return sizeof(uint16_t) * NA * A_STAGE;   // dynamic part: the activation ring
+}
+
+template <bool DX, bool VEC>
+static hipError_t launch_one(dim3 grid, hipStream_t s, const uint16_t* act, const Nf4View& w,
+                             const float* codebook, int64_t M, const LoraTerm& lora, void* out,
+                             bool bf16, float* part, int ksplit, int per, int64_t mtiles,
+                             int64_t otiles) {
+  static bool attr_set = false;   // idempotent: the same value every time
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<DX, VEC>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)smem_bytes<DX>());
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((k_gemm<DX, VEC>), grid, dim3(512), smem_bytes<DX>(), s, act, w, codebook, M,
+                     lora, out, (int)bf16, part, ksplit, per, mtiles, otiles);
+  return hipGetLastError();
+}
+
+template <bool DX>
 static hipError_t launch(const Nf4View& w, const float* codebook, const uint16_t* act, int64_t M,
                          const LoraTerm& lora, void* out, bool bf16, float* part, int ksplit,
                          hipStream_t s) {
@@ -247,10 +388,12 @@ static hipError_t launch(const Nf4View& w, const float* codebook, const uint16_t
   const int nsteps = (int)((C + GBK - 1) / GBK);
   const int per = (nsteps + ksplit - 1) / ksplit;
   const int64_t mtiles = (M + GBM - 1) / GBM, otiles = (O + GBN - 1) / GBN;
-  const int64_t total = mtiles * otiles * ksplit;
-  hipLaunchKernelGGL(k_gemm<DX>, dim3((unsigned)total), dim3(256), 0, s, act, w, codebook, M, lora,
-                     out, (int)bf16, part, ksplit, per, mtiles, otiles);
-  return hipGetLastError();
+  const dim3 grid((unsigned)(mtiles * otiles * ksplit));
+  if (!DX || C % 8 == 0)
+    return launch_one<DX, true>(grid, s, act, w, codebook, M, lora, out, bf16, part, ksplit, per,
+                                mtiles, otiles);
+  return launch_one<DX, false>(grid, s, act, w, codebook, M, lora, out, bf16, part, ksplit, per,
+                               mtiles, otiles);
 }
 
 hipError_t launch_gemm_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,

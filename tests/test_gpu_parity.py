@@ -246,7 +246,7 @@ def test_forward_bf16_output_within_one_ulp():
         assert np.all(np.abs(yg - Yo) <= ulp + gamma), path
 
 
-BWD_CASES = [(1, 64, 64, 2), (16, 4096, 4096, 8), (5, 100, 192, 4), (130, 300, 512, 16),
+BWD_CASES = [(1, 64, 64, 2), (16, 4096, 4096, 8), (5, 100, 192, 4), (130, 300, 512, 16), (300, 200, 256, 8),
              (257, 513, 640, 64), (512, 1024, 1024, 8), (33, 11008, 256, 8)]
 
 
