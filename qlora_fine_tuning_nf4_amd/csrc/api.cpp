@@ -91,10 +91,8 @@ int plan_dx_split(int64_t m, int64_t n, int64_t k) {
   return tiles >= 192 ? 1 : (int)std::min<int64_t>(cap, cdiv(256, tiles));
 }
 
-int plan_wgrad_split(int64_t m, int64_t c, int r) {
-  const int64_t wgs = cdiv(c, 512) * cdiv(r, 8);
-  return (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(m, 16), cdiv(256, wgs)));
-}
+// the adapter-gradient kernel reduces 128 rows per workgroup
+int plan_wgrad_split(int64_t m, int64_t c, int r) { return (int)cdiv(m, 128); }
 
 struct FwdWs {
   size_t t_off, part_off, total;

@@ -64,6 +64,32 @@ QL_DEV Lut make_lut(const float* lv, float s) {
   return t;
 }
 
+// Lookup table built by the four lanes of a DPP quad that share one block:
+// lane q (= lane & 3) computes entries 4q..4q+3 and the planes lo[q], hi[q];
+// quad broadcasts hand every lane all four planes.
+QL_DEV uint32_t quad_bcast(uint32_t v, int j) {
+  switch (j) {   // dpp quad_perm [j, j, j, j]
+    case 0: return __builtin_amdgcn_mov_dpp(v, 0x00, 0xF, 0xF, false);
+    case 1: return __builtin_amdgcn_mov_dpp(v, 0x55, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_mov_dpp(v, 0xAA, 0xF, 0xF, false);
+    default: return __builtin_amdgcn_mov_dpp(v, 0xFF, 0xF, 0xF, false);
+  }
+}
+
+// lvq[i] = level[4q + i] for this lane's quad position q.
+QL_DEV Lut make_lut_quad(const float* lvq, float s) {
+  const uint32_t d0 = pack_bf16x2(lvq[0] * s, lvq[1] * s);
+  const uint32_t d1 = pack_bf16x2(lvq[2] * s, lvq[3] * s);
+  const uint32_t lo = perm(d1, d0, 0x06040200u), hi = perm(d1, d0, 0x07050301u);
+  Lut t;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    t.lo[j] = quad_bcast(lo, j);
+    t.hi[j] = quad_bcast(hi, j);
+  }
+  return t;
+}
+
 // Decode one packed word (elements 8w .. 8w+7: byte j = code j | code j+4 << 4)
 // into 8 bf16 values in element order, as 4 packed pairs.  Each byte plane is
 // looked up twice (entries 0-7 and 8-15, selected by the low three code

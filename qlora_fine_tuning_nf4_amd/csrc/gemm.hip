@@ -18,10 +18,11 @@
 //    chunks are XOR-swizzled by row so the MFMA fragment reads are free of
 //    bank conflicts.
 //  * The weight tile of each K-step (128 x 64 weights = 128 NF4 blocks) is
-//    decoded by the 256 threads of waves 0-3 (one per SIMD), half a block
-//    each, into a double-buffered LDS stage; the decode of step s+1 is
-//    interleaved with the MFMAs of step s, one barrier per step.  Decoding is
-//    amortized over 256 output rows.
+//    decoded by all 512 threads into a double-buffered LDS stage: the four
+//    lanes of a DPP quad share a block, build its 16-entry table together
+//    (broadcast with quad_perm) and decode 16 weights each.  The decode of
+//    step s+1 is interleaved with the MFMAs of step s, one barrier per step;
+//    it is amortized over 256 output rows.
 //  * Forward reads B fragments with ds_read_b128 from the [n][k] stage; the
 //    backward contracts over n and reads them with the transposing
 //    ds_read_b64_tr_b16 from a [n][k] stage.
@@ -83,7 +84,10 @@ QL_DEV int64_t logical_tile(int64_t id, int64_t total) {
   return xcd * base + (xcd < rem ? xcd : rem) + slot;
 }
 
-constexpr int NA = 3;                 // activation stages in the DMA ring
+#ifndef QL_A_DMA
+#define QL_A_DMA 1                     // activation tiles by LDS DMA (1) or through registers (0)
+#endif
+constexpr int NA = 3;                 // activation stages in the ring
 constexpr int A_STAGE = GBM * GBK;     // bf16 elements per activation stage (32 KiB)
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
@@ -119,11 +123,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
   __shared__ float s_lv[16];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  // wave index in an SGPR, so role branches below are scalar branches
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 3, wn = wave >> 2;                  // 64-row block, 64-column half
   const int lr = lane & 31, lg = lane >> 5;
-  const bool decoder = wave < 4;                             // one decoding wave per SIMD
   const int64_t N = w.n, K = w.k, nkb = K / kBlock;
   const int64_t C = DX ? N : K;       // contraction length
   const int64_t O = DX ? K : N;       // output columns
@@ -142,17 +144,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
 
   if (tid < 16) s_lv[tid] = codebook[tid];
 
-  // decode role of threads 0..255: half a 64-block each
-  const int dt = tid & 255;
-  const int half = dt & 1;
-  const int wr = DX ? (dt >> 2) : (dt >> 1);                // stage row
-  const int wcb = DX ? ((dt >> 1) & 1) : 0;                 // block within the stage row (dx)
+  // Decode role (all 512 threads): a quad of lanes shares one of the step's
+  // 128 blocks, lane q = tid & 3 decodes its elements [16q, 16q+16).
+  const int q = tid & 3;
+  const int blk = tid >> 2;
+  const int wr = DX ? (blk >> 1) : blk;                     // stage row
+  const int wcb = DX ? (blk & 1) : 0;                       // block within the stage row (dx)
 
-  // Activation tile of step st into ring stage `stage`: wave w fills rows
-  // [32w, 32w+32) with 4 DMA loads of 8 rows; lane l lands at byte 16l of its
-  // load's 1 KiB, i.e. row l/8, physical chunk l%8.  Rows past M and columns
-  // past the contraction are clamped (products discarded or against zero
-  // weights).
   // per-lane source of each of the 4 DMA loads: row base and the largest
   // step offset that keeps the 8-element piece inside the row
   const uint16_t* a_src[4];
@@ -164,6 +162,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     a_src[i] = act + min(m0 + rl, M - 1) * C + lc * 8;
     a_cmax[i] = C - 8 - lc * 8;
   }
+  // Activation tile of step st into ring stage `stage`: wave w fills rows
+  // [32w, 32w+32) with 4 DMA loads of 8 rows; lane l lands at byte 16l of its
+  // load's 1 KiB, i.e. row l/8, physical chunk l%8.  Rows past M and columns
+  // past the contraction are clamped (products discarded or against zero
+  // weights).
   auto fill_a = [&](int st, int stage) {
     const int64_t c0 = (int64_t)st * GBK;
     uint16_t* base = sA + stage * A_STAGE;
@@ -182,31 +185,55 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       }
     }
   };
+  // register-staged alternative: load (coalesced, same lane mapping) now,
+  // store to the ring stage later
+  auto load_a_regs = [&](int st, u32x4_t (&r)[4]) {
+    const int64_t c0 = (int64_t)st * GBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (VEC) {
+        r[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + min(c0, a_cmax[i]));
+      } else {
+        const int rl = wave * 32 + i * 8 + (lane >> 3);
+        const int64_t row = min(m0 + rl, M - 1);
+        const int64_t c = c0 + a_chunk(rl, lane & 7) * 8;
+        r[i] = c < C ? load_act8(act + row * C, c, C, false) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_a_regs = [&](int stage, const u32x4_t (&r)[4]) {
+    uint16_t* base = sA + stage * A_STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4_t*>(base + (wave * 32 + i * 8) * GBK + lane * 8) = r[i];
+  };
 
   struct WRaw {
-    u32x4_t codes;
+    u32x2_t codes;    // this lane's two packed words
     uint32_t qword;   // the aligned dword holding the block's 8-bit scale
     uint32_t qshift;  // its bit offset in qword
     float step;
     bool ok;
   };
-  // block index of this thread's half-block at step st: b0 + st * bstride
-  // (forward: along the row; backward: down the rows)
+  // block index of this lane's block at step st: b0 + st * bstride
   const int64_t b0 = DX ? (int64_t)wr * nkb + o0 / kBlock + wcb : (o0 + wr) * nkb;
   const int64_t bstride = DX ? GBK * nkb : 1;
   const bool w_ok_fixed = DX ? (o0 / kBlock + wcb) < nkb : (o0 + wr) < N;
   auto load_w = [&](int st, WRaw& r) {
     r.ok = w_ok_fixed && (!DX || (int64_t)st * GBK + wr < N);
     const int64_t b = r.ok ? b0 + st * bstride : 0;
-    r.codes = *reinterpret_cast<const u32x4_t*>(w.codes + b * 32 + half * 16);
+    r.codes = *reinterpret_cast<const u32x2_t*>(w.codes + b * 32 + q * 8);
     r.qword = *reinterpret_cast<const uint32_t*>(w.qscale + (b & ~int64_t(3)));
     r.qshift = (uint32_t)(b & 3) * 8;
     r.step = w.step[b >> 8];
   };
+  auto scale_of = [](const WRaw& r) {
+    return r.ok ? (float)((r.qword >> r.qshift) & 0xFFu) * r.step : 0.f;
+  };
   __syncthreads();
-  float lv[16];
+  float lvq[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) lv[i] = s_lv[i];
+  for (int i = 0; i < 4; ++i) lvq[i] = s_lv[4 * q + i];
 
   f32x16_t acc[2][2];
 #pragma unroll
@@ -238,102 +265,149 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       }
     }
   };
+  auto wdst = [&](int stage) {
+    return reinterpret_cast<u32x4_t*>(sW + stage * G::stage + wr * G::ld + wcb * 64 + q * 16);
+  };
 
   if (s_begin < s_end) {
     const int last = s_end - 1;
     // prologue: activation stages of steps s_begin, s_begin+1; decoded weight
     // stage 0 of s_begin; codes of s_begin+1 (w0) and s_begin+2 (w1)
     WRaw w0, w1;
-    fill_a(s_begin, 0);
-    fill_a(min(s_begin + 1, last), 1);
-    if (decoder) {
+    u32x4_t ra0[4], ra1[4];    // register-staged activations (QL_A_DMA == 0)
+    {
       WRaw wf;
       load_w(s_begin, wf);
+      if (QL_A_DMA) {
+        fill_a(s_begin, 0);
+        fill_a(min(s_begin + 1, last), 1);
+      } else {
+        load_a_regs(s_begin, ra0);
+        load_a_regs(min(s_begin + 1, last), ra1);
+      }
       load_w(min(s_begin + 1, last), w0);
       load_w(min(s_begin + 2, last), w1);
-      const Lut t = make_lut(lv, wf.ok ? (float)((wf.qword >> wf.qshift) & 0xFFu) * wf.step : 0.f);
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(sW + wr * G::ld + wcb * 64 + half * 32);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[j] = decode8(t, wf.codes[j]);
+      QL_VMCNT(0);
+      if (!QL_A_DMA) {
+        store_a_regs(0, ra0);
+        store_a_regs(1, ra1);
+        load_a_regs(min(s_begin + 2, last), ra0);
+      }
+      const Lut t = make_lut_quad(lvq, scale_of(wf));
+      u32x4_t* dst = wdst(0);
+      dst[0] = decode8(t, wf.codes[0]);
+      dst[1] = decode8(t, wf.codes[1]);
+      __syncthreads();
     }
-    QL_VMCNT(0);
-    __syncthreads();
 
-    // One K-step t: MFMAs on activation stage t%3 and weight stage (t-s)&1;
-    // the DMA of step t+2 is issued first; decoding waves also decode the
-    // codes of step t+1 (`wd`) into the other weight stage between their
-    // MFMAs and then refill `wd` with the codes of step t+3 (consumed two
-    // steps later).  Loads are unconditional (clamped step index).
-    auto kstep = [&](int st, WRaw& wd, bool dec) {
+    // One K-step t: MFMAs on activation stage t%3 and weight stage (t-s)&1.
+    // First the activation tile of step t+2 is started (DMA), or, with
+    // register staging, the tile of t+2 (loaded a step ago) is stored and the
+    // tile of t+3 loaded; then all fragment reads of the step are issued; the
+    // decode of the codes of step t+1 (`wd`) into the other weight stage runs
+    // between the MFMAs; then `wd` is refilled with the codes of step t+3
+    // (consumed two steps later).  Every wave issues the same loads, so the
+    // vmcnt values below are exact.
+    auto kstep = [&](int st, WRaw& wd, u32x4_t (&ra)[4]) {
       const int rel = st - s_begin;
       const int wstage = rel & 1;
-      Lut t;
-      if (dec) {
-        // `wd` was loaded at the end of step t-2; issued since: DMA of t+1 (4)
-        // and the codes of t+2 (3)
-        if (VEC) QL_VMCNT(7); else QL_VMCNT(0);
-        t = make_lut(lv, wd.ok ? (float)((wd.qword >> wd.qshift) & 0xFFu) * wd.step : 0.f);
+      // `wd` was loaded at the end of step t-2; issued since: the activation
+      // loads of step t-1 (4) and the codes of t+2 (3)
+      if (VEC) QL_VMCNT(7); else QL_VMCNT(0);
+      const float sc = scale_of(wd);
+      if (QL_A_DMA) {
+        fill_a(min(st + 2, last), (rel + 2) % NA);
+      } else {
+        store_a_regs((rel + 2) % NA, ra);       // tile of t+2, loaded during step t-1
+        load_a_regs(min(st + 3, last), ra);     // tile of t+3
       }
-      fill_a(min(st + 2, last), (rel + 2) % NA);
       __builtin_amdgcn_sched_barrier(0);
       const uint16_t* sa = sA + (rel % NA) * A_STAGE;
       const uint16_t* sw = sW + wstage * G::stage;
-      u32x4_t* dst =
-          reinterpret_cast<u32x4_t*>(sW + (wstage ^ 1) * G::stage + wr * G::ld + wcb * 64 + half * 32);
-      u32x4_t ac[2], an[2], bc[2], bn[2];
-      read_a(sa, 0, ac);
-      read_b(sw, 0, bc);
+      u32x4_t a[4][2], b[4][2];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        if (kk < 3) {
-          read_a(sa, kk + 1, an);
-          read_b(sw, kk + 1, bn);
-        }
+        read_a(sa, kk, a[kk]);
+        read_b(sw, kk, b[kk]);
+      }
+      const Lut t = make_lut_quad(lvq, sc);
+      u32x4_t* dst = wdst(wstage ^ 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(ac[mt], bc[nt], acc[mt][nt]);
-        if (dec) {
-          dst[kk] = decode8(t, wd.codes[kk]);
+          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(a[kk][mt], b[kk][nt], acc[mt][nt]);
+        if (kk == 1) dst[0] = decode8(t, wd.codes[0]);
+        if (kk == 2) dst[1] = decode8(t, wd.codes[1]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // then up to eight VALU
-          }
-        }
-        if (kk < 3) {
-          ac[0] = an[0];
-          ac[1] = an[1];
-          bc[0] = bn[0];
-          bc[1] = bn[1];
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // then up to six VALU
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (dec) {
-        load_w(min(st + 3, last), wd);
-        // DMA of t+1 was issued a step ago; issued after it: codes of t+2 (3),
-        // DMA of t+2 (4), codes of t+3 (3)
-        if (VEC) QL_VMCNT(10); else QL_VMCNT(0);
-      } else {
-        // issued after the DMA of t+1: the DMA of t+2 (4)
-        if (VEC) QL_VMCNT(4); else QL_VMCNT(0);
-      }
+      load_w(min(st + 3, last), wd);
+      // the activation loads of step t+1 were issued a step ago; issued after
+      // them: codes of t+2 (3), activation loads of this step (4), codes of
+      // t+3 (3).  (Register staging: the loads of t+3 issued this step are
+      // stored next step, also waited for here.)
+      if (VEC) QL_VMCNT(10); else QL_VMCNT(0);
       k_barrier();
     };
 
-    if (decoder) {
-      int st = s_begin;
-      for (; st + 1 < s_end; st += 2) {
-        kstep(st, w0, true);
-        kstep(st + 1, w1, true);
-      }
-      if (st < s_end) kstep(st, w0, true);
-    } else {
-      for (int st = s_begin; st < s_end; ++st) kstep(st, w0, false);
+    int st = s_begin;
+    for (; st + 1 < s_end; st += 2) {
+      kstep(st, w0, ra0);
+      kstep(st + 1, w1, ra0);
     }
+    if (st < s_end) kstep(st, w0, ra0);
   }
 
-  // ---- epilogue
+  // ---- epilogue.  LoRA term (ksplit == 1): out += (scaling * L) R^T on the
+  // matrix cores, 16 ranks per MFMA step; the fp32 factor scaling * L is
+  // split into bf16 hi + lo parts so the product keeps fp32 accuracy.
+  if (ksplit == 1 && lora.r > 0) {
+    for (int j0 = 0; j0 < lora.r; j0 += 16) {
+      // B fragments: R[o][j0 + 8*lg + e] (the rank index is the contraction)
+      u32x4_t rb[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int64_t o = min(o0 + wn * 64 + 32 * nt + lr, O - 1);
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + 8 * lg + e;
+          h[e] = j < lora.r ? lora.R[o * lora.rs_c + (int64_t)j * lora.rs_j] : 0u;
+        }
+        rb[nt] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+      }
+      // A fragments: s * L[m][j], split into bf16 hi + lo (exact to 2^-16)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int64_t m = min(m0 + wm * 64 + 32 * mt + lr, M - 1);
+        float tv[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + 8 * lg + e;
+          tv[e] = j < lora.r ? lora.scaling * lora.L[m * lora.r + j] : 0.f;
+        }
+        u32x4_t ahi, alo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ahi[e] = pack_bf16x2(tv[2 * e], tv[2 * e + 1]);
+          lo[2 * e] = tv[2 * e] - bf16_lo(ahi[e]);
+          lo[2 * e + 1] = tv[2 * e + 1] - bf16_hi(ahi[e]);
+          alo[e] = pack_bf16x2(lo[2 * e], lo[2 * e + 1]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          acc[mt][nt] = mfma32(ahi, rb[nt], acc[mt][nt]);
+          acc[mt][nt] = mfma32(alo, rb[nt], acc[mt][nt]);
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -343,16 +417,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
         const int64_t m = m0 + wm * 64 + 32 * mt + 8 * (i >> 2) + 4 * lg + (i & 3);
         const int64_t o = o0 + wn * 64 + 32 * nt + lr;
         if (m < M && o < O) {
-          float v = acc[mt][nt][i];
-          if (ksplit > 1) {
+          const float v = acc[mt][nt][i];
+          if (ksplit > 1)
             part[((int64_t)split * M + m) * O + o] = v;
-          } else {
-            if (lora.r > 0) v += lora.scaling * lora_dot_g(lora, m, o);
-            if (out_bf16)
-              reinterpret_cast<uint16_t*>(out)[m * O + o] = to_bf16(v);
-            else
-              reinterpret_cast<float*>(out)[m * O + o] = v;
-          }
+          else if (out_bf16)
+            reinterpret_cast<uint16_t*>(out)[m * O + o] = to_bf16(v);
+          else
+            reinterpret_cast<float*>(out)[m * O + o] = v;
         }
       }
 }
