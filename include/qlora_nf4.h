@@ -169,6 +169,56 @@ int qlora_linear_bwd(const qlora_nf4 *W, const float *codebook, const uint16_t *
                      void *dX, int dx_dtype, float *dA, float *dB,
                      void *ws, size_t ws_bytes, int path, void *stream);
 
+/*
+ * Grouped forward for small m (decode): one launch streams the packed weights
+ * of many independent projections, so that each projection does not pay a
+ * kernel launch of its own.  Same arithmetic as qlora_linear_fwd on the
+ * streaming path, except that the contraction is never split (the per-row
+ * sums run in one pass).
+ *
+ * One job per projection (host struct; the buffers it points to are device
+ * memory owned by the caller, with the sizes and alignments of
+ * qlora_linear_fwd).  T is required (written) when r > 0.
+ */
+typedef struct {
+  qlora_nf4 w;
+  const uint16_t *X; /* [m x w.k] bf16 */
+  const uint16_t *A; /* [r x w.k] bf16, NULL when r == 0 */
+  const uint16_t *B; /* [w.n x r] bf16, NULL when r == 0 */
+  int r;
+  float scaling;
+  void *Y;           /* [m x w.n], the group's y_dtype */
+  float *T;          /* [m x r] fp32 */
+} qlora_fwd_job;
+
+/* Plain-data handle filled by qlora_group_init; `table` is the caller's device buffer. */
+typedef struct {
+  void *table;
+  int count, lora_count, max_r, y_dtype;
+  int64_t m, row_groups, max_quads;
+} qlora_group;
+
+/* Host.  Device bytes of the job table for `count` jobs (0 if count < 1). */
+size_t qlora_group_table_bytes(int count);
+
+/*
+ * Host, setup time.  Validates every job (QLORA_ERR_* as qlora_linear_fwd,
+ * QLORA_ERR_ARG if m > QLORA_GEMV_MAX_M or count < 1) and writes the device
+ * job table into `table` (16-byte aligned, >= qlora_group_table_bytes(count)
+ * bytes) with a blocking host-to-device copy: unlike every other call this
+ * one synchronizes.  The buffers named by the jobs must stay valid while the
+ * group is used.
+ */
+int qlora_group_init(qlora_group *g, const qlora_fwd_job *jobs, int count, int64_t m,
+                     int y_dtype, void *table, size_t table_bytes);
+
+/*
+ * Enqueue the forward of every job of `g` on `stream`: T = X A^T for the jobs
+ * with r > 0 (one launch), then Y = X deq(W)^T + scaling T B^T for all jobs
+ * (one launch).  No workspace.  Jobs must not write overlapping outputs.
+ */
+int qlora_linear_fwd_grouped(const qlora_group *g, const float *codebook, void *stream);
+
 /* Host.  Static message for a status code (never NULL). */
 const char *qlora_strerror(int status);
 

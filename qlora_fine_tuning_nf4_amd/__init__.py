@@ -5,7 +5,7 @@ The product is the C-ABI HIP library ``libqlora_nf4.so`` (declared in
 entry-point names.  Build in-tree with ``python -m qlora_fine_tuning_nf4_amd.build``.
 """
 from .binding import (  # noqa: F401
-    NF4Weight, QLoRAError, device_codebook, lib, qlora_dequantize, qlora_linear_bwd,
-    qlora_linear_fwd, qlora_nf4_bytes, qlora_nf4_codebook, qlora_quantize, qlora_strerror,
-    qlora_workspace_bytes,
+    FwdGroup, NF4Weight, QLoRAError, device_codebook, lib, qlora_dequantize, qlora_group_init,
+    qlora_group_table_bytes, qlora_linear_bwd, qlora_linear_fwd, qlora_linear_fwd_grouped,
+    qlora_nf4_bytes, qlora_nf4_codebook, qlora_quantize, qlora_strerror, qlora_workspace_bytes,
 )

@@ -33,6 +33,18 @@ class _Nf4Desc(ctypes.Structure):
                 ("qscale", ctypes.c_void_p), ("step", ctypes.c_void_p)]
 
 
+class _FwdJob(ctypes.Structure):
+    _fields_ = [("w", _Nf4Desc), ("X", ctypes.c_void_p), ("A", ctypes.c_void_p),
+                ("B", ctypes.c_void_p), ("r", ctypes.c_int), ("scaling", ctypes.c_float),
+                ("Y", ctypes.c_void_p), ("T", ctypes.c_void_p)]
+
+
+class _Group(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_void_p), ("count", ctypes.c_int), ("lora_count", ctypes.c_int),
+                ("max_r", ctypes.c_int), ("y_dtype", ctypes.c_int), ("m", ctypes.c_int64),
+                ("row_groups", ctypes.c_int64), ("max_quads", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -65,6 +77,12 @@ def lib():
         L.qlora_linear_bwd.restype = i32
         L.qlora_linear_bwd.argtypes = [P(_Nf4Desc), vp, vp, vp, i64, vp, vp, i32, f32, vp, vp,
                                        i32, vp, vp, vp, sz, i32, vp]
+        L.qlora_group_table_bytes.restype = sz
+        L.qlora_group_table_bytes.argtypes = [i32]
+        L.qlora_group_init.restype = i32
+        L.qlora_group_init.argtypes = [P(_Group), P(_FwdJob), i32, i64, i32, vp, sz]
+        L.qlora_linear_fwd_grouped.restype = i32
+        L.qlora_linear_fwd_grouped.argtypes = [P(_Group), vp, vp]
         _lib = L
     return _lib
 
@@ -211,3 +229,42 @@ def qlora_linear_bwd(w: NF4Weight, codebook: torch.Tensor, X, dY, A=None, B=None
         _ptr(dX), QLORA_BF16 if (dX is not None and dX.dtype == torch.bfloat16) else QLORA_F32,
         _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), PATHS[path], _stream()), "qlora_linear_bwd")
     return dX, dA, dB
+
+
+class FwdGroup:
+    """A grouped small-m forward: the job table lives in a device tensor owned
+    by this object, which also keeps the jobs' tensors alive."""
+
+    def __init__(self, handle: _Group, table: torch.Tensor, keep: list):
+        self.handle, self.table, self._keep = handle, table, keep
+
+
+def qlora_group_table_bytes(count: int) -> int:
+    return int(lib().qlora_group_table_bytes(count))
+
+
+def qlora_group_init(jobs, m: int, y_dtype=torch.bfloat16, device="cuda") -> FwdGroup:
+    """jobs: list of dicts with keys w (NF4Weight), X, Y, and optionally A, B,
+    scaling, T (required when A/B are given)."""
+    arr = (_FwdJob * len(jobs))()
+    keep = []
+    for i, j in enumerate(jobs):
+        w = j["w"]
+        A, B = j.get("A"), j.get("B")
+        r = 0 if A is None else A.shape[0]
+        arr[i] = _FwdJob(w.desc(), j["X"].data_ptr(), A.data_ptr() if r else None,
+                         B.data_ptr() if r else None, r, float(j.get("scaling", 0.0)),
+                         j["Y"].data_ptr(), j["T"].data_ptr() if r else None)
+        keep.append(j)
+    nbytes = qlora_group_table_bytes(len(jobs))
+    table = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    g = _Group()
+    yd = QLORA_BF16 if y_dtype == torch.bfloat16 else QLORA_F32
+    _check(lib().qlora_group_init(ctypes.byref(g), arr, len(jobs), m, yd, _ptr(table), nbytes),
+           "qlora_group_init")
+    return FwdGroup(g, table, keep)
+
+
+def qlora_linear_fwd_grouped(group: FwdGroup, codebook: torch.Tensor):
+    _check(lib().qlora_linear_fwd_grouped(ctypes.byref(group.handle), _ptr(codebook), _stream()),
+           "qlora_linear_fwd_grouped")

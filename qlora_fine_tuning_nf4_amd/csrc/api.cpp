@@ -256,6 +256,78 @@ int qlora_linear_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
   return QLORA_OK;
 }
 
+size_t qlora_group_table_bytes(int count) {
+  if (count < 1) return 0;
+  return up16(sizeof(ql::GemvJob) * (size_t)count) + up16(sizeof(ql::RowdotJob) * (size_t)count);
+}
+
+int qlora_group_init(qlora_group* g, const qlora_fwd_job* jobs, int count, int64_t m, int y_dtype,
+                     void* table, size_t table_bytes) {
+  if (!g || !jobs || !table) return QLORA_ERR_NULL;
+  if (count < 1 || m > QLORA_GEMV_MAX_M) return QLORA_ERR_ARG;
+  if (m < 1) return QLORA_ERR_SHAPE;
+  if (y_dtype != QLORA_F32 && y_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
+  if (!aligned(table, 16)) return QLORA_ERR_ALIGN;
+  if (table_bytes < qlora_group_table_bytes(count)) return QLORA_ERR_WORKSPACE;
+  const size_t rd_off = up16(sizeof(ql::GemvJob) * (size_t)count);
+  ql::GemvJob* gj = new ql::GemvJob[count];
+  ql::RowdotJob* rj = new ql::RowdotJob[count];
+  int nl = 0, max_r = 0;
+  int64_t rgs = 0, maxq = 0;
+  int st = QLORA_OK;
+  for (int i = 0; i < count && st == QLORA_OK; ++i) {
+    const qlora_fwd_job& J = jobs[i];
+    if ((st = check_desc(&J.w))) break;
+    if (!J.X || !J.Y) { st = QLORA_ERR_NULL; break; }
+    if (J.r < 0 || J.r > QLORA_MAX_RANK) { st = QLORA_ERR_RANK; break; }
+    if (J.r > 0 && (!J.A || !J.B || !J.T)) { st = QLORA_ERR_NULL; break; }
+    if (!aligned(J.X, 16) || !aligned(J.Y, 16) ||
+        (J.r > 0 && (!aligned(J.A, 16) || !aligned(J.B, 2) || !aligned(J.T, 4)))) {
+      st = QLORA_ERR_ALIGN;
+      break;
+    }
+    const int64_t n = J.w.n, k = J.w.k;
+    ql::LoraTerm lora{J.r > 0 ? J.T : nullptr, J.B, (int64_t)J.r, 1, J.r, J.scaling};
+    gj[i] = ql::GemvJob{J.X, view(&J.w), lora, J.Y, nullptr, m, y_dtype == QLORA_BF16, rgs};
+    rgs += cdiv(n, 16);
+    maxq = std::max(maxq, cdiv(k / kB, 4));
+    if (J.r > 0) {
+      rj[nl++] = ql::RowdotJob{J.X, J.A, J.T, k, J.r};
+      max_r = std::max(max_r, J.r);
+    }
+  }
+  if (st == QLORA_OK) {
+    if (hipMemcpy(table, gj, sizeof(ql::GemvJob) * (size_t)count, hipMemcpyHostToDevice) != hipSuccess ||
+        (nl > 0 && hipMemcpy((char*)table + rd_off, rj, sizeof(ql::RowdotJob) * (size_t)nl,
+                             hipMemcpyHostToDevice) != hipSuccess))
+      st = QLORA_ERR_HIP;
+  }
+  delete[] gj;
+  delete[] rj;
+  if (st != QLORA_OK) return st;
+  *g = qlora_group{table, count, nl, max_r, y_dtype, m, rgs, maxq};
+  return QLORA_OK;
+}
+
+int qlora_linear_fwd_grouped(const qlora_group* g, const float* codebook, void* stream) {
+  if (!g || !g->table || !codebook) return QLORA_ERR_NULL;
+  if (g->count < 1 || g->m < 1 || g->m > QLORA_GEMV_MAX_M || g->lora_count < 0 ||
+      g->lora_count > g->count || g->row_groups < 1)
+    return QLORA_ERR_ARG;
+  if (!aligned(codebook, 4)) return QLORA_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const char* tb = (const char*)g->table;
+  const size_t rd_off = up16(sizeof(ql::GemvJob) * (size_t)g->count);
+  if (g->lora_count > 0 &&
+      ql::launch_rowdot_grouped((const ql::RowdotJob*)(tb + rd_off), g->lora_count, g->m, g->max_r,
+                                s) != hipSuccess)
+    return QLORA_ERR_HIP;
+  if (ql::launch_gemv_grouped((const ql::GemvJob*)tb, g->count, g->row_groups, g->m, codebook,
+                              g->max_quads, s) != hipSuccess)
+    return QLORA_ERR_HIP;
+  return QLORA_OK;
+}
+
 int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* X,
                      const uint16_t* dY, int64_t m, const uint16_t* A, const uint16_t* B, int r,
                      float scaling, const float* T_saved, void* dX, int dx_dtype, float* dA,

@@ -117,6 +117,10 @@ QL_DEV float block_scale(const uint8_t* qscale, const float* step, int64_t b) {
   return (float)qscale[b] * step[b / kGroup];
 }
 
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8).
+#define QL_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | 0x0F70)
+
 QL_DEV float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -90,9 +90,6 @@ QL_DEV int64_t logical_tile(int64_t id, int64_t total) {
 constexpr int NA = 3;                 // activation stages in the ring
 constexpr int A_STAGE = GBM * GBK;     // bf16 elements per activation stage (32 KiB)
 
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4, lgkmcnt 11:8).
-#define QL_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | 0x0F70)
 #define QL_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 // Workgroup barrier for the K loop.  __syncthreads() would add a release
@@ -210,8 +207,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
 
   struct WRaw {
     u32x2_t codes;    // this lane's two packed words
-    uint32_t qword;   // the aligned dword holding the block's 8-bit scale
-    uint32_t qshift;  // its bit offset in qword
+    uint32_t qbyte;   // the block's 8-bit scale
     float step;
     bool ok;
   };
@@ -223,12 +219,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     r.ok = w_ok_fixed && (!DX || (int64_t)st * GBK + wr < N);
     const int64_t b = r.ok ? b0 + st * bstride : 0;
     r.codes = *reinterpret_cast<const u32x2_t*>(w.codes + b * 32 + q * 8);
-    r.qword = *reinterpret_cast<const uint32_t*>(w.qscale + (b & ~int64_t(3)));
-    r.qshift = (uint32_t)(b & 3) * 8;
+    r.qbyte = w.qscale[b];
     r.step = w.step[b >> 8];
   };
   auto scale_of = [](const WRaw& r) {
-    return r.ok ? (float)((r.qword >> r.qshift) & 0xFFu) * r.step : 0.f;
+    return r.ok ? (float)r.qbyte * r.step : 0.f;
   };
   __syncthreads();
   float lvq[4];
@@ -330,6 +325,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
         read_a(sa, kk, a[kk]);
         read_b(sw, kk, b[kk]);
       }
+      // forward: all fragment reads of the step are issued before the first
+      // MFMA (the scheduler would otherwise sink each read next to its use and
+      // expose the LDS latency at every MFMA pair); measured slower for the
+      // transposing reads of the backward, which keep the default order
+      if (!DX) __builtin_amdgcn_sched_barrier(0);
       const Lut t = make_lut_quad(lvq, sc);
       u32x4_t* dst = wdst(wstage ^ 1);
 #pragma unroll

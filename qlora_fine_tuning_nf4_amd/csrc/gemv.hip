@@ -9,7 +9,9 @@
 //  * k_gemv_fwd  -- small M (<= 64): a wave owns 16 weight rows and streams
 //    their packed bytes; each lane decodes a whole 64-block (one lookup table
 //    per block) and feeds eight MFMAs whose 32-wide contraction spans four
-//    different blocks; the activation fragments are read straight from L2.
+//    different blocks.  The next block's codes, scale and activation
+//    fragments are loaded while the current one is decoded.  One launch can
+//    cover a list of independent projections (grouped form).
 #include "common.h"
 #include "kernels.h"
 
@@ -30,76 +32,158 @@ QL_DEV void store_out(void* out, bool bf16, int64_t idx, float v) {
     reinterpret_cast<float*>(out)[idx] = v;
 }
 
-template <int MT>
-__global__ __launch_bounds__(256) void k_gemv_fwd(const uint16_t* __restrict__ X, Nf4View w,
-                                                  const float* __restrict__ codebook, int64_t M,
-                                                  LoraTerm lora, void* __restrict__ Y, int y_bf16,
-                                                  float* __restrict__ part, int ksplit,
-                                                  int quads_per_split) {
-  __shared__ float s_lv[16];
+// Per-lane work unit of the streaming forward: lane (n = l % 16, g = l / 16)
+// of a wave owns the 64-block (n, 4q + g) of quad q: its 32 code bytes, its
+// scale, and the activation fragments X[m][64(4q + g) + 8i .. +8], i = 0..7,
+// for the 16-row groups of M.  The eight MFMA 16x16x32 steps of a quad
+// contract, for each i, word i of the four blocks of the quad.
+template <int MT, bool PREX>
+struct GemvUnit {
+  u32x4_t c0, c1;          // packed words 0-3 and 4-7 of the block
+  uint32_t qbyte;
+  float step;
+  bool ok;
+  u32x4_t x[PREX ? MT : 1][8];
+};
+
+template <int MT, bool GROUPED>
+__global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* __restrict__ jobs,
+                                                  int njobs, const float* __restrict__ codebook,
+                                                  int ksplit, int quads_per_split) {
+  constexpr bool PREX = MT <= 2;   // activation fragments prefetched with the codes
   __shared__ f32x4_t s_red[3][MT][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t N = w.n, K = w.k, nkb = K / kBlock, nquads = (nkb + 3) / 4;
-  const int64_t n = (int64_t)blockIdx.x * 16 + (lane & 15);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int64_t rg = blockIdx.x;
+  GemvJob J;
+  if constexpr (GROUPED) {
+    // the job whose row-group range holds this workgroup (uniform search)
+    int lo = 0, hi = njobs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (jobs[mid].rg_begin <= rg) lo = mid; else hi = mid - 1;
+    }
+    J = jobs[lo];
+    rg -= J.rg_begin;
+  } else {
+    J = job1;
+  }
+  const Nf4View& w = J.w;
+  const int64_t N = w.n, K = w.k, M = J.M;
+  const int nkb = (int)(K / kBlock), nquads = (nkb + 3) / 4;   // loop indices stay 32-bit (SALU)
+  const int64_t n = rg * 16 + (lane & 15);
+  const bool nok = n < N;
+  const int64_t nn = nok ? n : N - 1;
   const int g = lane >> 4;
   const int split = blockIdx.y;
-  const int64_t q0 = (int64_t)split * quads_per_split;
-  const int64_t q1 = min(nquads, q0 + quads_per_split);
-  if (tid < 16) s_lv[tid] = codebook[tid];
-  __syncthreads();
+  const int q0 = split * quads_per_split;
+  const int q1 = min(nquads, q0 + quads_per_split);
+
   float lv[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) lv[i] = s_lv[i];
+  for (int i = 0; i < 16; ++i) lv[i] = codebook[i];
 
-  f32x4_t acc[MT];
+  // rows of M past the end are loaded from row M-1 (their outputs are dropped)
+  const uint16_t* xrow[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt) xrow[mt] = J.X + min((int64_t)(mt * 16 + (lane & 15)), M - 1) * K;
 
-  for (int64_t q = q0 + wave; q < q1; q += 4) {
-    const int64_t kb = 4 * q + g;
-    u32x4_t c0 = {0u, 0u, 0u, 0u}, c1 = {0u, 0u, 0u, 0u};
-    float sc = 0.f;
-    if (n < N && kb < nkb) {
-      const int64_t b = n * nkb + kb;
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w.codes + b * 32);
-      c0 = src[0];
-      c1 = src[1];
-      sc = block_scale(w.qscale, w.step, b);
+  using U = GemvUnit<MT, PREX>;
+  auto load = [&](int q, U& u) {
+    const int kb = 4 * q + g;
+    u.ok = nok && kb < nkb;
+    const int kbc = min(kb, nkb - 1);
+    const int64_t b = nn * nkb + kbc;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w.codes + b * 32);
+    u.c0 = src[0];
+    u.c1 = src[1];
+    u.qbyte = w.qscale[b];
+    u.step = w.step[b >> 8];
+    if constexpr (PREX) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          u.x[mt][i] = *reinterpret_cast<const u32x4_t*>(xrow[mt] + (int64_t)kbc * kBlock + i * 8);
     }
+  };
+
+  f32x4_t acc[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int q, const U& u) {
+    const float sc = u.ok ? (float)u.qbyte * u.step : 0.f;
     const Lut t = make_lut(lv, sc);
+    const int kbc = min(4 * q + g, nkb - 1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const u32x4_t bf = decode8(t, i < 4 ? c0[i] : c1[i - 4]);
+      const u32x4_t bf = decode8(t, i < 4 ? u.c0[i] : u.c1[i - 4]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int64_t m = mt * 16 + (lane & 15);
-        u32x4_t af = {0u, 0u, 0u, 0u};
-        if (m < M && kb < nkb) af = *reinterpret_cast<const u32x4_t*>(X + m * K + kb * kBlock + i * 8);
-        acc[mt] = mfma16x16x32(af, bf, acc[mt]);
+        u32x4_t af;
+        if constexpr (PREX)
+          af = u.x[mt][i];
+        else
+          af = *reinterpret_cast<const u32x4_t*>(xrow[mt] + (int64_t)kbc * kBlock + i * 8);
+        acc[mt][i & 1] = mfma16x16x32(af, bf, acc[mt][i & 1]);
       }
     }
+  };
+
+  // quads q0 + wave + 4j of this split, one unit ahead: the loads of the
+  // next unit are issued (and kept, by the scheduling fences) before the
+  // current unit is decoded, whose own loads are then the only ones waited for
+  constexpr int NLOAD = 4 + (PREX ? 8 * MT : 0);   // vector loads per unit
+  const int qlast = q1 - 1;
+  int q = q0 + wave;
+  if (q < q1) {
+    U u0, u1;
+    load(q, u0);
+    for (;;) {
+      load(min(q + 4, qlast), u1);
+      __builtin_amdgcn_sched_barrier(0);
+      QL_VMCNT(NLOAD);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(q, u0);
+      __builtin_amdgcn_sched_barrier(0);
+      q += 4;
+      if (q >= q1) break;
+      load(min(q + 4, qlast), u0);
+      __builtin_amdgcn_sched_barrier(0);
+      QL_VMCNT(NLOAD);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(q, u1);
+      __builtin_amdgcn_sched_barrier(0);
+      q += 4;
+      if (q >= q1) break;
+    }
   }
+
+  f32x4_t tot[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) tot[mt] = acc[mt][0] + acc[mt][1];
   if (wave > 0)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) s_red[wave - 1][mt][lane] = acc[mt];
+    for (int mt = 0; mt < MT; ++mt) s_red[wave - 1][mt][lane] = tot[mt];
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    f32x4_t v = acc[mt];
+    f32x4_t v = tot[mt];
     v += s_red[0][mt][lane];
     v += s_red[1][mt][lane];
     v += s_red[2][mt][lane];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t m = mt * 16 + g * 4 + e;
-      if (m < M && n < N) {
+      if (m < M && nok) {
         float y = v[e];
         if (ksplit > 1) {
-          part[((int64_t)split * M + m) * N + n] = y;
+          J.part[((int64_t)split * M + m) * N + n] = y;
         } else {
-          if (lora.r > 0) y += lora.scaling * lora_dot(lora, m, n);
-          store_out(Y, y_bf16, m * N + n, y);
+          if (J.lora.r > 0) y += J.lora.scaling * lora_dot(J.lora, m, n);
+          store_out(J.Y, J.y_bf16, m * N + n, y);
         }
       }
     }
@@ -122,11 +206,30 @@ hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16
                            hipStream_t s) {
   const int64_t nquads = (w.k / kBlock + 3) / 4;
   const int per = (int)((nquads + ksplit - 1) / ksplit);
+  const GemvJob job{X, w, lora, Y, part, M, (int)y_bf16, 0};
   dim3 grid((unsigned)((w.n + 15) / 16), (unsigned)ksplit);
   const int mt = (int)((M + 15) / 16);
 #define QL_GEMV(MT)                                                                             \
-  hipLaunchKernelGGL(k_gemv_fwd<MT>, grid, dim3(256), 0, s, X, w, codebook, M, lora, Y,        \
-                     (int)y_bf16, part, ksplit, per)
+  hipLaunchKernelGGL((k_gemv_fwd<MT, false>), grid, dim3(256), 0, s, job, nullptr, 0, codebook, \
+                     ksplit, per)
+  switch (mt) {
+    case 1: QL_GEMV(1); break;
+    case 2: QL_GEMV(2); break;
+    case 3: QL_GEMV(3); break;
+    default: QL_GEMV(4); break;
+  }
+#undef QL_GEMV
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_grouped(const GemvJob* jobs, int njobs, int64_t row_groups, int64_t M,
+                               const float* codebook, int64_t max_quads, hipStream_t s) {
+  dim3 grid((unsigned)row_groups, 1);
+  const int mt = (int)((M + 15) / 16);
+  const GemvJob none{};
+#define QL_GEMV(MT)                                                                           \
+  hipLaunchKernelGGL((k_gemv_fwd<MT, true>), grid, dim3(256), 0, s, none, jobs, njobs,        \
+                     codebook, 1, (int)max_quads)
   switch (mt) {
     case 1: QL_GEMV(1); break;
     case 2: QL_GEMV(2); break;

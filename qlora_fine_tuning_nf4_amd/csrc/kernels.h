@@ -33,10 +33,28 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const flo
 hipError_t launch_gemm_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,
                            const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
                            hipStream_t s);
+// One projection of the small-M forward.  rg_begin: first 16-row group of
+// this job in a grouped launch (ascending over the job list).
+struct GemvJob {
+  const uint16_t* X;
+  Nf4View w;
+  LoraTerm lora;
+  void* Y;
+  float* part;
+  int64_t M;
+  int y_bf16;
+  int64_t rg_begin;
+};
+
 // Forward for small M (<= 64): streaming split-K over the packed weight.
 hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,
                            const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
                            hipStream_t s);
+// Grouped small-M forward: one launch over `njobs` device-resident jobs that
+// share M, covering `row_groups` 16-row groups in total; no split of the
+// contraction.  max_quads: the largest k/256 (rounded up) over the jobs.
+hipError_t launch_gemv_grouped(const GemvJob* jobs, int njobs, int64_t row_groups, int64_t M,
+                               const float* codebook, int64_t max_quads, hipStream_t s);
 // dX = dY deq(W) (+ LoRA term), contraction over n; nsplit > 1 -> partials.
 hipError_t launch_gemm_dx(const Nf4View& w, const float* codebook, const uint16_t* dY, int64_t M,
                           const LoraTerm& lora, void* dX, bool dx_bf16, float* part, int nsplit,
@@ -48,6 +66,17 @@ hipError_t launch_reduce(const float* part, int nsplit, int64_t M, int64_t C,
 // out[m][j] = sum_c P[m][c] * Q[j][c]   (P bf16 [M x C], Q bf16 [r x C], out fp32 [M x r])
 hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
                          float* out, hipStream_t s);
+// One product of the grouped rowdot: out[m][j] = sum_c P[m][c] Q[j][c].
+struct RowdotJob {
+  const uint16_t* P;
+  const uint16_t* Q;
+  float* out;
+  int64_t C;
+  int r;
+};
+// All jobs share M; max_r is the largest r among them.
+hipError_t launch_rowdot_grouped(const RowdotJob* jobs, int njobs, int64_t M, int max_r,
+                                 hipStream_t s);
 // Qt[j][n] = Q[n][j] for a bf16 [N x r] matrix.
 hipError_t launch_transpose_bf16(const uint16_t* Q, int64_t N, int r, uint16_t* Qt, hipStream_t s);
 // Weight gradients of the adapter: out = scaling * sum_m Q[m][j] * P[m][c]

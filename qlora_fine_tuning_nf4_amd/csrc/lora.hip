@@ -21,9 +21,20 @@ QL_DEV u32x4_t load8_guard(const uint16_t* row, int64_t c, int64_t C, bool vec) 
 // are summed in a fixed order through LDS.  bf16 products are exact, sums
 // fp32.
 constexpr int RD_WAVES = 16;
+template <bool GROUPED>
 __global__ __launch_bounds__(1024) void k_rowdot(const uint16_t* __restrict__ P,
                                                  const uint16_t* __restrict__ Q, int64_t M,
-                                                 int64_t C, int r, float* __restrict__ out) {
+                                                 int64_t C, int r, float* __restrict__ out,
+                                                 const RowdotJob* __restrict__ jobs) {
+  if constexpr (GROUPED) {
+    const RowdotJob& J = jobs[blockIdx.z];
+    P = J.P;
+    Q = J.Q;
+    out = J.out;
+    C = J.C;
+    r = J.r;
+    if ((int)blockIdx.y * 16 >= r) return;
+  }
   __shared__ f32x4_t s_red[RD_WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t m = (int64_t)blockIdx.x * 16 + (lane & 15);
@@ -177,7 +188,16 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ 
 hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
                          float* out, hipStream_t s) {
   dim3 grid((unsigned)((M + 15) / 16), (unsigned)((r + 15) / 16));
-  hipLaunchKernelGGL(k_rowdot, grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out);
+  hipLaunchKernelGGL(k_rowdot<false>, grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out,
+                     nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowdot_grouped(const RowdotJob* jobs, int njobs, int64_t M, int max_r,
+                                 hipStream_t s) {
+  dim3 grid((unsigned)((M + 15) / 16), (unsigned)((max_r + 15) / 16), (unsigned)njobs);
+  hipLaunchKernelGGL(k_rowdot<true>, grid, dim3(64 * RD_WAVES), 0, s, nullptr, nullptr, M,
+                     int64_t(0), 0, nullptr, jobs);
   return hipGetLastError();
 }
 

@@ -136,3 +136,55 @@ def test_bwd_argument_errors():
     assert bwd(dX=FAKE + 4) == 3
     assert bwd(wsb=16) == 6
     assert bwd(ws=None) == 6
+
+
+def _job(n=64, k=128, X=FAKE, A=FAKE, Bp=FAKE, r=8, Y=FAKE, T=FAKE, codes=FAKE):
+    return B._FwdJob(_desc(n, k, codes=codes), X, A, Bp, r, 2.0, Y, T)
+
+
+def test_group_table_bytes():
+    L = B.lib()
+    assert L.qlora_group_table_bytes(0) == 0
+    assert L.qlora_group_table_bytes(-3) == 0
+    assert L.qlora_group_table_bytes(1) > 0
+    assert L.qlora_group_table_bytes(224) >= 224 * L.qlora_group_table_bytes(1) // 2
+
+
+def test_group_init_argument_errors():
+    L = B.lib()
+    g = B._Group()
+    tb = L.qlora_group_table_bytes(2)
+
+    def init(jobs, m=1, ydt=1, table=FAKE, nbytes=tb, count=None, handle=True):
+        arr = (B._FwdJob * max(len(jobs), 1))(*jobs)
+        return L.qlora_group_init(ctypes.byref(g) if handle else None, arr,
+                                  len(jobs) if count is None else count, m, ydt, table, nbytes)
+    ok = _job()
+    assert init([ok, ok], handle=False) == 1
+    assert init([ok, ok], table=None) == 1
+    assert init([ok, ok], count=0) == 8
+    assert init([ok, ok], m=65) == 8
+    assert init([ok, ok], m=0) == 2
+    assert init([ok, ok], ydt=3) == 4
+    assert init([ok, ok], table=FAKE + 4) == 3
+    assert init([ok, ok], nbytes=tb - 1) == 6
+    assert init([ok, _job(codes=0)]) == 1
+    assert init([ok, _job(k=100)]) == 2
+    assert init([ok, _job(X=None)]) == 1
+    assert init([ok, _job(T=None)]) == 1
+    assert init([ok, _job(r=129)]) == 5
+    assert init([ok, _job(X=FAKE + 2)]) == 3
+    assert init([ok, _job(Y=FAKE + 8)]) == 3
+
+
+def test_grouped_fwd_argument_errors():
+    L = B.lib()
+    assert L.qlora_linear_fwd_grouped(None, FAKE, None) == 1
+    g = B._Group(FAKE, 2, 0, 0, 1, 1, 8, 1)
+    assert L.qlora_linear_fwd_grouped(ctypes.byref(g), None, None) == 1
+    bad = B._Group(FAKE, 0, 0, 0, 1, 1, 8, 1)
+    assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
+    bad = B._Group(FAKE, 2, 0, 0, 1, 65, 8, 1)
+    assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
+    bad = B._Group(FAKE, 2, 3, 0, 1, 1, 8, 1)
+    assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
