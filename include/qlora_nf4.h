@@ -73,12 +73,21 @@ enum {
 
 /*
  * Packed NF4 + double-quantized weight (device buffers owned by the caller).
- * Flat block b covers elements [64b, 64b+64) of the row-major weight; group g
- * covers blocks [256g, 256g+256).  Sizes come from qlora_nf4_bytes().
- *   codes : n*k/2 bytes.  The 4-byte word w holds elements 8w..8w+7: byte j
- *           (j = 0..3) is code(8w+j) | code(8w+j+4) << 4.
+ * Flat block b = row * (k/64) + kb covers elements [64b, 64b+64) of the
+ * row-major weight; group g covers flat blocks [256g, 256g+256).  Sizes come
+ * from qlora_nf4_bytes().
+ *   codes : n*k/2 bytes, 32 per block.  Inside a block, the 4-byte word w
+ *           holds elements 8w..8w+7: byte j (j = 0..3) is
+ *           code(8w+j) | code(8w+j+4) << 4.
  *   qscale: n*k/64 bytes, the block absmax quantized to 8 bits.
- *   step  : ceil(n*k/16384) floats, the fp32 second-level constant per group.
+ *   step  : ceil(n*k/16384) floats, the fp32 second-level constant per group,
+ *           indexed by flat group.
+ * Storage order of the blocks in codes and qscale: rows are taken in groups
+ * of 16 (the last group holds R = n mod 16 rows if that is not 0, else 16);
+ * inside a group the blocks are ordered by kb, then by row, so block
+ * (row, kb) sits at position g0*(k/64) + kb*R + (row - g0), g0 = 16*(row/16).
+ * The 16 rows of a group are contiguous at every kb, which lets the kernels
+ * read a group's codes as one coalesced run.
  * Dequantized weight: w = bf16_rne(level[code] * fp32(qscale_b * step_g)).
  * (news.rkmt.cn/news/4821 §1.3, §2.2, §2.3; zky001 section 5.8 "double quantization")
  */

@@ -28,6 +28,12 @@ What is computed, in the pages' order
    absmax-symmetric and has an exact zero level.
 5. Dequantization [lqnn §3.3; zky "a counter-intuitive combination"]:
    ``s'_b = fp32(qscale_b * step_g)``, ``w = bf16_rne(fp32(level[code] * s'_b))``.
+6. Storage order (a layout choice of this implementation; the pages fix only
+   that the 4-bit codes live in uint8 storage, rkmt §4.2): the 32 code bytes
+   and the 8-bit scale of each block are stored with the rows taken in groups
+   of 16 and, inside a group, the blocks ordered by k-block, then by row.  The
+   fp32 second-level constants stay indexed by the flat block.  ``quantize``
+   returns the flat (logical) order; ``to_storage`` / ``from_storage`` convert.
 
 The codebook [zky "NF4": levels placed by the normal distribution so that each
 level receives about the same share of weights; kwkr §2.1: zero must be exactly
@@ -132,6 +138,35 @@ def unpack(codes: np.ndarray) -> np.ndarray:
     out[:, 0:4] = b & 0x0F
     out[:, 4:8] = b >> 4
     return out.reshape(-1)
+
+
+def storage_positions(n: int, k: int) -> np.ndarray:
+    """Storage position of every flat block b = row * (k/64) + kb (step 6):
+    group start g0 = 16 * (row // 16), R = min(16, n - g0) rows in the group,
+    position g0 * (k/64) + kb * R + (row - g0)."""
+    nkb = k // BLOCK
+    row = np.arange(n, dtype=np.int64)[:, None]
+    kb = np.arange(nkb, dtype=np.int64)[None, :]
+    g0 = (row // 16) * 16
+    rows_in_group = np.minimum(16, n - g0)
+    return (g0 * nkb + kb * rows_in_group + (row - g0)).reshape(-1)
+
+
+def to_storage(codes: np.ndarray, qscale: np.ndarray, n: int, k: int):
+    """Flat-order (codes, qscale) of an n x k weight -> storage order."""
+    pos = storage_positions(n, k)
+    cs = np.empty((pos.size, 32), dtype=np.uint8)
+    cs[pos] = np.asarray(codes, dtype=np.uint8).reshape(-1, 32)
+    qs = np.empty(pos.size, dtype=np.uint8)
+    qs[pos] = np.asarray(qscale, dtype=np.uint8)
+    return cs.reshape(-1), qs
+
+
+def from_storage(codes: np.ndarray, qscale: np.ndarray, n: int, k: int):
+    """Storage-order (codes, qscale) -> flat order."""
+    pos = storage_positions(n, k)
+    cs = np.asarray(codes, dtype=np.uint8).reshape(-1, 32)[pos]
+    return cs.reshape(-1), np.asarray(qscale, dtype=np.uint8)[pos]
 
 
 def block_absmax(w_bits: np.ndarray) -> np.ndarray:

@@ -198,8 +198,7 @@ int qlora_quantize(const uint16_t* W, const float* codebook, const qlora_nf4* ou
   if (!W || !codebook) return QLORA_ERR_NULL;
   if (int e = check_desc(out)) return e;
   if (!aligned(W, 16) || !aligned(codebook, 4)) return QLORA_ERR_ALIGN;
-  const int64_t nblocks = out->n * (out->k / kB);
-  if (ql::launch_quantize(W, codebook, out->codes, out->qscale, out->step, nblocks,
+  if (ql::launch_quantize(W, codebook, out->codes, out->qscale, out->step, out->n, out->k,
                           (hipStream_t)stream) != hipSuccess)
     return QLORA_ERR_HIP;
   return QLORA_OK;
@@ -209,7 +208,7 @@ int qlora_dequantize(const qlora_nf4* W, const float* codebook, uint16_t* out, v
   if (!codebook || !out) return QLORA_ERR_NULL;
   if (int e = check_desc(W)) return e;
   if (!aligned(out, 16) || !aligned(codebook, 4)) return QLORA_ERR_ALIGN;
-  if (ql::launch_dequant(W->codes, W->qscale, W->step, codebook, out, W->n * (W->k / kB),
+  if (ql::launch_dequant(W->codes, W->qscale, W->step, codebook, out, W->n, W->k,
                          (hipStream_t)stream) != hipSuccess)
     return QLORA_ERR_HIP;
   return QLORA_OK;

@@ -112,9 +112,22 @@ QL_DEV u32x4_t decode8(const Lut& t, uint32_t x) {
   return o;
 }
 
+// Storage position of the 64-block (n, kb) of an N-row weight with nkb blocks
+// per row: rows are taken in groups of 16 and inside a group the blocks are
+// ordered by k-block, then by row, so the blocks that 16 consecutive rows
+// hold at one k-block are contiguous (512 code bytes, 16 scale bytes).  Both
+// the codes (32 bytes per block) and the 8-bit scales use this order; the
+// fp32 second-level constants are indexed by the flat block n * nkb + kb.
+QL_DEV int64_t blk_pos(int64_t n, int64_t kb, int64_t N, int64_t nkb) {
+  const int64_t g0 = n & ~int64_t(15);
+  const int64_t R = min(int64_t(16), N - g0);
+  return g0 * nkb + kb * R + (n - g0);
+}
+
 // Block scale s' = fp32(qscale * step): one rounding, as the format defines.
-QL_DEV float block_scale(const uint8_t* qscale, const float* step, int64_t b) {
-  return (float)qscale[b] * step[b / kGroup];
+// b is the flat block index, p its storage position.
+QL_DEV float block_scale(const uint8_t* qscale, const float* step, int64_t b, int64_t p) {
+  return (float)qscale[p] * step[b / kGroup];
 }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and

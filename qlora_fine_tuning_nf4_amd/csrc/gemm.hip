@@ -211,15 +211,29 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     float step;
     bool ok;
   };
-  // block index of this lane's block at step st: b0 + st * bstride
-  const int64_t b0 = DX ? (int64_t)wr * nkb + o0 / kBlock + wcb : (o0 + wr) * nkb;
+  // flat index of this lane's block at step st: b0 + st * bstride; its
+  // storage position (rows in groups of 16, k-block-major inside a group):
+  // forward p0 + st * R (the row is fixed), backward recomputed per step
+  const int64_t kb_dx = o0 / kBlock + wcb;
+  const int64_t b0 = DX ? (int64_t)wr * nkb + kb_dx : (o0 + wr) * nkb;
   const int64_t bstride = DX ? GBK * nkb : 1;
-  const bool w_ok_fixed = DX ? (o0 / kBlock + wcb) < nkb : (o0 + wr) < N;
+  const bool w_ok_fixed = DX ? kb_dx < nkb : (o0 + wr) < N;
+  const int64_t fg0 = (o0 + wr) & ~int64_t(15);
+  const int64_t fR = min(int64_t(16), N - fg0);
+  const int64_t fp0 = fg0 * nkb + (o0 + wr - fg0);
   auto load_w = [&](int st, WRaw& r) {
     r.ok = w_ok_fixed && (!DX || (int64_t)st * GBK + wr < N);
-    const int64_t b = r.ok ? b0 + st * bstride : 0;
-    r.codes = *reinterpret_cast<const u32x2_t*>(w.codes + b * 32 + q * 8);
-    r.qbyte = w.qscale[b];
+    int64_t b = 0, p = 0;
+    if (DX) {
+      const int64_t n = (int64_t)st * GBK + wr, g0 = n & ~int64_t(15);
+      b = r.ok ? b0 + st * bstride : 0;
+      p = r.ok ? g0 * nkb + kb_dx * min(int64_t(16), N - g0) + (n - g0) : 0;
+    } else {
+      b = r.ok ? b0 + st : 0;
+      p = r.ok ? fp0 + st * fR : 0;
+    }
+    r.codes = *reinterpret_cast<const u32x2_t*>(w.codes + p * 32 + q * 8);
+    r.qbyte = w.qscale[p];
     r.step = w.step[b >> 8];
   };
   auto scale_of = [](const WRaw& r) {

@@ -89,15 +89,22 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
   for (int mt = 0; mt < MT; ++mt) xrow[mt] = J.X + min((int64_t)(mt * 16 + (lane & 15)), M - 1) * K;
 
   using U = GemvUnit<MT, PREX>;
+  // storage position of (nn, kb): the 16 rows of this row group are
+  // contiguous at each k-block, so lane l of a unit reads bytes [32l, 32l+32)
+  // of a 2 KiB run (full row group)
+  const int64_t g0 = nn & ~int64_t(15);
+  const int64_t R = min(int64_t(16), N - g0);
+  const int64_t p0 = g0 * nkb + (nn - g0);
   auto load = [&](int q, U& u) {
     const int kb = 4 * q + g;
     u.ok = nok && kb < nkb;
     const int kbc = min(kb, nkb - 1);
     const int64_t b = nn * nkb + kbc;
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w.codes + b * 32);
+    const int64_t p = p0 + kbc * R;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w.codes + p * 32);
     u.c0 = src[0];
     u.c1 = src[1];
-    u.qbyte = w.qscale[b];
+    u.qbyte = w.qscale[p];
     u.step = w.step[b >> 8];
     if constexpr (PREX) {
 #pragma unroll

@@ -23,9 +23,9 @@ struct Nf4View {
 };
 
 hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* codes,
-                           uint8_t* qscale, float* step, int64_t nblocks, hipStream_t s);
+                           uint8_t* qscale, float* step, int64_t n, int64_t k, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          const float* codebook, uint16_t* out, int64_t nblocks, hipStream_t s);
+                          const float* codebook, uint16_t* out, int64_t n, int64_t k, hipStream_t s);
 
 // Forward base product Y = X deq(W)^T (+ LoRA term), tiled MFMA GEMM.
 // ksplit > 1 writes fp32 partials part[ksplit][M][N] and leaves the epilogue

@@ -20,8 +20,10 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
                                                       const float* __restrict__ codebook,
                                                       uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ qscale,
-                                                      float* __restrict__ step, int64_t nblocks) {
+                                                      float* __restrict__ step, int64_t N,
+                                                      int64_t nkb) {
   __shared__ float s_absmax[kGroup];
+  const int64_t nblocks = N * nkb;
   __shared__ float s_red[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t blk0 = (int64_t)blockIdx.x * kGroup;
@@ -61,7 +63,9 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
       word |= c << (j < 4 ? 8 * j : 8 * (j - 4) + 4);
     }
     if (valid) {
-      reinterpret_cast<uint32_t*>(codes)[(blk0 + lb) * 8 + (lane & 7)] = word;
+      const int64_t b = blk0 + lb;
+      const int64_t p = blk_pos(b / nkb, b % nkb, N, nkb);
+      reinterpret_cast<uint32_t*>(codes)[p * 8 + (lane & 7)] = word;
       if ((lane & 7) == 0) s_absmax[lb] = am;
     }
   }
@@ -74,7 +78,8 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
   const float st = c2 / 255.0f;
   if (tid < nb) {
     const float q = st == 0.f ? 0.f : fminf(rintf(a / st), 255.f);
-    qscale[blk0 + tid] = (uint8_t)q;
+    const int64_t b = blk0 + tid;
+    qscale[blk_pos(b / nkb, b % nkb, N, nkb)] = (uint8_t)q;
   }
   if (tid == 0) step[blockIdx.x] = st;
 }
@@ -84,7 +89,9 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
                                                  const uint8_t* __restrict__ qscale,
                                                  const float* __restrict__ step,
                                                  const float* __restrict__ codebook,
-                                                 uint16_t* __restrict__ out, int64_t nblocks) {
+                                                 uint16_t* __restrict__ out, int64_t N,
+                                                 int64_t nkb) {
+  const int64_t nblocks = N * nkb;
   __shared__ float s_lv[16];
   if (threadIdx.x < 16) s_lv[threadIdx.x] = codebook[threadIdx.x];
   __syncthreads();
@@ -93,8 +100,9 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
   for (int i = 0; i < 16; ++i) lv[i] = s_lv[i];
   const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= nblocks) return;
-  const Lut t = make_lut(lv, block_scale(qscale, step, b));
-  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(codes + b * 32);
+  const int64_t p = blk_pos(b / nkb, b % nkb, N, nkb);
+  const Lut t = make_lut(lv, block_scale(qscale, step, b, p));
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(codes + p * 32);
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + b * kBlock);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -105,17 +113,18 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
 }
 
 hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* codes,
-                           uint8_t* qscale, float* step, int64_t nblocks, hipStream_t s) {
-  const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
+                           uint8_t* qscale, float* step, int64_t n, int64_t k, hipStream_t s) {
+  const int64_t nkb = k / kBlock, ngroups = (n * nkb + kGroup - 1) / kGroup;
   hipLaunchKernelGGL(k_quant_nf4_dq, dim3((unsigned)ngroups), dim3(256), 0, s, W, codebook, codes,
-                     qscale, step, nblocks);
+                     qscale, step, n, nkb);
   return hipGetLastError();
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          const float* codebook, uint16_t* out, int64_t nblocks, hipStream_t s) {
+                          const float* codebook, uint16_t* out, int64_t n, int64_t k, hipStream_t s) {
+  const int64_t nkb = k / kBlock, nblocks = n * nkb;
   hipLaunchKernelGGL(k_dequant, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, s, codes,
-                     qscale, step, codebook, out, nblocks);
+                     qscale, step, codebook, out, n, nkb);
   return hipGetLastError();
 }
 

@@ -98,6 +98,7 @@ def test_quantize_bitexact(n, k, dist):
     q = B.qlora_quantize(_t(w), _cb(B))
     torch.cuda.synchronize()
     c, qs, st = _oracle_q(w)
+    c, qs = onf4.to_storage(c, qs, n, k)
     assert np.array_equal(q.codes.cpu().numpy(), c)
     assert np.array_equal(q.qscale.cpu().numpy(), qs)
     assert np.array_equal(q.step.cpu().numpy().view(np.uint32), st.view(np.uint32))
@@ -115,8 +116,7 @@ def test_quantize_full_size_sampled():
     rows_per_group = 16384 // k
     g = synth.rng(5)
     groups = sorted(set([0, n // rows_per_group - 1] + list(g.integers(0, n // rows_per_group, 24))))
-    codes = q.codes.cpu().numpy()
-    qs = q.qscale.cpu().numpy()
+    codes, qs = onf4.from_storage(q.codes.cpu().numpy(), q.qscale.cpu().numpy(), n, k)
     st = q.step.cpu().numpy()
     for gi in groups:
         r0 = gi * rows_per_group

@@ -337,3 +337,42 @@ def test_full_path_small():
     bound = nf4.dequant_error_bound(W, lv).reshape(W.shape)
     err_max = np.abs(_f(X)) @ bound.T
     assert np.all(np.abs(Yq - Yf) <= err_max + 1e-12)
+
+
+# --------------------------------------------------------------------------- storage order
+def test_storage_positions_small_cases_by_hand():
+    # 3 rows (one partial group of R = 3), 2 blocks per row: k-block-major, then row
+    assert nf4.storage_positions(3, 128).tolist() == [0, 3, 1, 4, 2, 5]
+    # 17 rows: a full group (R = 16) then a group of one row (R = 1)
+    pos = nf4.storage_positions(17, 128).reshape(17, 2)
+    assert pos[0].tolist() == [0, 16]
+    assert pos[15].tolist() == [15, 31]
+    assert pos[16].tolist() == [32, 33]
+
+
+@pytest.mark.parametrize("n,k", [(1, 64), (16, 256), (17, 320), (100, 11008), (4096, 128)])
+def test_storage_positions_are_a_permutation_with_contiguous_row_runs(n, k):
+    pos = nf4.storage_positions(n, k)
+    nkb = k // 64
+    assert np.array_equal(np.sort(pos), np.arange(n * nkb))
+    grid = pos.reshape(n, nkb)
+    for g0 in range(0, n, 16):
+        rows = grid[g0:g0 + 16]
+        # the rows of a group hold one contiguous, row-ordered run at each k-block
+        assert np.all(np.diff(rows, axis=0) == 1)
+        assert np.all(np.diff(rows[0]) == rows.shape[0])
+
+
+def test_storage_round_trip():
+    g = np.random.default_rng(3)
+    n, k = 37, 192
+    codes = g.integers(0, 256, n * k // 2, dtype=np.uint8)
+    qs = g.integers(0, 256, n * k // 64, dtype=np.uint8)
+    cst, qst = nf4.to_storage(codes, qs, n, k)
+    c2, q2 = nf4.from_storage(cst, qst, n, k)
+    assert np.array_equal(c2, codes) and np.array_equal(q2, qs)
+    # a block keeps its 32 bytes together
+    b = 5 * 3 + 2
+    p = nf4.storage_positions(n, k)[b]
+    assert np.array_equal(cst[32 * p:32 * p + 32], codes[32 * b:32 * b + 32])
+    assert qst[p] == qs[b]
