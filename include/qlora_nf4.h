@@ -68,7 +68,7 @@ enum {
 #define QLORA_BLOCK 64        /* weights per first-level block   (news.rkmt.cn/news/4821 §1.2) */
 #define QLORA_GROUP 256       /* block scales per second-level group (news.rkmt.cn/news/4821 §2.2) */
 #define QLORA_MAX_RANK 128    /* largest supported LoRA rank */
-#define QLORA_GEMV_MAX_M 64   /* largest m the streaming path accepts */
+#define QLORA_GEMV_MAX_M 32   /* largest m the streaming path accepts */
 #define QLORA_CODEBOOK_LEN 31 /* 16 NF4 levels then 15 decision midpoints */
 
 /*

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
 QLORA_F32, QLORA_BF16 = 0, 1
 PATHS = {"auto": 0, "gemv": 1, "gemm": 2}
 CODEBOOK_LEN = 31
-GEMV_MAX_M = 64
+GEMV_MAX_M = 32
 MAX_RANK = 128
 
 

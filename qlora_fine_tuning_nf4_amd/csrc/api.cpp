@@ -72,9 +72,11 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int path) {
   FwdPlan p;
   p.gemv = path == QLORA_PATH_GEMV || (path == QLORA_PATH_AUTO && m <= 32);
   if (p.gemv) {
-    const int64_t ntiles = cdiv(n, 16), nquads = cdiv(k / kB, 4);
+    // 64-row workgroups; split the contraction until there are ~512 of them,
+    // keeping at least 4 quads (1024 k) per split
+    const int64_t ntiles = cdiv(n, 64), nquads = cdiv(k / kB, 4);
     const int64_t cap = std::max<int64_t>(1, nquads / 4);
-    p.ksplit = (int)std::min<int64_t>(cap, std::max<int64_t>(1, cdiv(1024, ntiles)));
+    p.ksplit = (int)std::min<int64_t>(cap, std::max<int64_t>(1, cdiv(512, ntiles)));
   } else {
     // 256 x 128 output tiles, 64-deep steps; split the contraction only when
     // the tiles cannot fill the 256 CUs
@@ -288,7 +290,7 @@ int qlora_group_init(qlora_group* g, const qlora_fwd_job* jobs, int count, int64
     const int64_t n = J.w.n, k = J.w.k;
     ql::LoraTerm lora{J.r > 0 ? J.T : nullptr, J.B, (int64_t)J.r, 1, J.r, J.scaling};
     gj[i] = ql::GemvJob{J.X, view(&J.w), lora, J.Y, nullptr, m, y_dtype == QLORA_BF16, rgs};
-    rgs += cdiv(n, 16);
+    rgs += cdiv(n, 64);
     maxq = std::max(maxq, cdiv(k / kB, 4));
     if (J.r > 0) {
       rj[nl++] = ql::RowdotJob{J.X, J.A, J.T, k, J.r};

@@ -25,6 +25,20 @@ QL_DEV f32x4_t mfma16x16x32(const u32x4_t a, const u32x4_t b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Global-memory view of a generic pointer.  Pointers loaded from memory
+// (job tables) are generic to the compiler, which then emits flat loads; flat
+// loads count in both the vector-memory and the LDS wait counters, so an LDS
+// wait would also wait for them.
+#define QL_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+QL_DEV const QL_GLOBAL T* gptr(const T* p) {
+  return (const QL_GLOBAL T*)p;
+}
+template <typename T>
+QL_DEV QL_GLOBAL T* gptr_w(T* p) {
+  return (QL_GLOBAL T*)p;
+}
+
 QL_DEV uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
   return __builtin_amdgcn_perm(s0, s1, sel);
 }
@@ -133,6 +147,7 @@ QL_DEV float block_scale(const uint8_t* qscale, const float* step, int64_t b, in
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4, lgkmcnt 11:8).
 #define QL_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | 0x0F70)
+#define QL_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 QL_DEV float wave_max(float v) {
 #pragma unroll

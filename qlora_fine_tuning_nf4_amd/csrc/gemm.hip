@@ -90,7 +90,6 @@ QL_DEV int64_t logical_tile(int64_t id, int64_t total) {
 constexpr int NA = 3;                 // activation stages in the ring
 constexpr int A_STAGE = GBM * GBK;     // bf16 elements per activation stage (32 KiB)
 
-#define QL_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 // Workgroup barrier for the K loop.  __syncthreads() would add a release
 // fence, and with LDS DMA in flight that fence waits for every outstanding

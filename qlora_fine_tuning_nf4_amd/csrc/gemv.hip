@@ -6,7 +6,7 @@
 // for the product, then discard).
 //
 // Small-M forward (the large-M GEMMs are in gemm.hip) and the split-K reduce.
-//  * k_gemv_fwd  -- small M (<= 64): a wave owns 16 weight rows and streams
+//  * k_gemv_fwd  -- small M (<= 32): a wave owns 16 weight rows and streams
 //    their packed bytes; each lane decodes a whole 64-block (one lookup table
 //    per block) and feeds eight MFMAs whose 32-wide contraction spans four
 //    different blocks.  The next block's codes, scale and activation
@@ -14,6 +14,8 @@
 //    cover a list of independent projections (grouped form).
 #include "common.h"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace ql {
 
@@ -27,53 +29,94 @@ QL_DEV float lora_dot(const LoraTerm& L, int64_t m, int64_t c) {
 
 QL_DEV void store_out(void* out, bool bf16, int64_t idx, float v) {
   if (bf16)
-    reinterpret_cast<uint16_t*>(out)[idx] = to_bf16(v);
+    gptr_w(reinterpret_cast<uint16_t*>(out))[idx] = to_bf16(v);
   else
-    reinterpret_cast<float*>(out)[idx] = v;
+    gptr_w(reinterpret_cast<float*>(out))[idx] = v;
 }
 
-// Per-lane work unit of the streaming forward: lane (n = l % 16, g = l / 16)
-// of a wave owns the 64-block (n, 4q + g) of quad q: its 32 code bytes, its
-// scale, and the activation fragments X[m][64(4q + g) + 8i .. +8], i = 0..7,
-// for the 16-row groups of M.  The eight MFMA 16x16x32 steps of a quad
-// contract, for each i, word i of the four blocks of the quad.
-template <int MT, bool PREX>
-struct GemvUnit {
-  u32x4_t c0, c1;          // packed words 0-3 and 4-7 of the block
+// LoRA term of one output: scaling * sum_j L[m][j] R[c][j], with 16-byte loads
+// when the rank and the pointers allow it.
+QL_DEV float lora_dot_v(const LoraTerm& L, int64_t m, int64_t c, bool vec) {
+  const QL_GLOBAL float* lr = gptr(L.L + m * L.r);
+  const QL_GLOBAL uint16_t* rr = gptr(L.R + c * L.rs_c);
+  float acc = 0.f;
+  int j = 0;
+  if (vec) {
+    for (; j + 8 <= L.r; j += 8) {
+      const u32x4_t bv = *reinterpret_cast<const QL_GLOBAL u32x4_t*>(rr + j);
+      const f32x4_t t0 = *reinterpret_cast<const QL_GLOBAL f32x4_t*>(lr + j);
+      const f32x4_t t1 = *reinterpret_cast<const QL_GLOBAL f32x4_t*>(lr + j + 4);
+      acc += t0[0] * bf16_lo(bv[0]) + t0[1] * bf16_hi(bv[0]) + t0[2] * bf16_lo(bv[1]) +
+             t0[3] * bf16_hi(bv[1]) + t1[0] * bf16_lo(bv[2]) + t1[1] * bf16_hi(bv[2]) +
+             t1[2] * bf16_lo(bv[3]) + t1[3] * bf16_hi(bv[3]);
+    }
+  }
+  for (; j < L.r; ++j) acc += lr[j] * __builtin_bit_cast(float, (uint32_t)rr[j] << 16);
+  return acc;
+}
+
+// Streaming forward, small M.  A workgroup of 4 waves owns 64 weight rows
+// (wave w: the 16-row group 4 * blockIdx.x + w) and walks the quads (4
+// blocks = 256 k) of its split in step.  Per quad, lane l (n = l % 16,
+// g = l / 16) decodes the 64-block (n, 4q + g): 32 code bytes read as part of
+// one coalesced 2 KiB run (tiled storage order), one lookup table, eight
+// decoded words; MFMA 16x16x32 step i contracts word i of the four blocks.
+// The activation chunk X[0..M)[256q, 256q + 256) goes global -> LDS once per
+// workgroup with the LDS DMA (rows XOR-swizzled in 16-byte units so the
+// fragment reads of 16 different rows hit 16 different bank groups) and is
+// read from there by all four waves.  Three-deep rings (LDS chunks, code
+// registers) keep the loads of quad q+2 in flight while quad q is computed;
+// one barrier per quad.
+template <int MT>
+struct GemvRaw {
+  u32x4_t c0, c1;   // packed words 0-3 and 4-7 of the lane's block
   uint32_t qbyte;
   float step;
-  bool ok;
-  u32x4_t x[PREX ? MT : 1][8];
 };
 
-template <int MT, bool GROUPED>
+constexpr int GV_CHUNK_BYTES = 512;   // one row of an activation chunk: 256 bf16
+
+// XPW: activation-chunk DMA instructions per wave and quad (8 * XPW chunk
+// rows: XPW = 1 for M <= 8, 2 for M <= 16, 4 for M <= 32).
+template <int MT, int XPW, bool GROUPED>
 __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* __restrict__ jobs,
                                                   int njobs, const float* __restrict__ codebook,
                                                   int ksplit, int quads_per_split) {
-  constexpr bool PREX = MT <= 2;   // activation fragments prefetched with the codes
-  __shared__ f32x4_t s_red[3][MT][64];
+  constexpr int XROWS = 8 * XPW;                           // rows of a chunk stage
+  constexpr int XSTAGE = XROWS * GV_CHUNK_BYTES / 2;       // bf16 elements per stage
+  // three separate chunk stages: distinct LDS objects let the compiler see
+  // that the DMA into one stage does not feed the reads of another
+  __shared__ __attribute__((aligned(16))) uint16_t sX0[XSTAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t sX1[XSTAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t sX2[XSTAGE];
+  auto stage_ptr = [&](int st) { return st == 0 ? sX0 : (st == 1 ? sX1 : sX2); };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int64_t rg = blockIdx.x;
+  int64_t wg = blockIdx.x;
   GemvJob J;
   if constexpr (GROUPED) {
-    // the job whose row-group range holds this workgroup (uniform search)
+    // the job whose workgroup range holds this workgroup (uniform search)
     int lo = 0, hi = njobs - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (jobs[mid].rg_begin <= rg) lo = mid; else hi = mid - 1;
+      if (jobs[mid].rg_begin <= wg) lo = mid; else hi = mid - 1;
     }
     J = jobs[lo];
-    rg -= J.rg_begin;
+    wg -= J.rg_begin;
   } else {
     J = job1;
   }
   const Nf4View& w = J.w;
   const int64_t N = w.n, K = w.k, M = J.M;
-  const int nkb = (int)(K / kBlock), nquads = (nkb + 3) / 4;   // loop indices stay 32-bit (SALU)
-  const int64_t n = rg * 16 + (lane & 15);
+  const int nkb = (int)(K / kBlock), nquads = (nkb + 3) / 4;
+  const int64_t g0 = (wg * 4 + wave) * 16;                 // this wave's row group
+  const int64_t n = g0 + (lane & 15);
   const bool nok = n < N;
-  const int64_t nn = nok ? n : N - 1;
+  // rows past N read (and discard) the last row; its group gives the layout
+  const int64_t nn = min(n, N - 1);
+  const int64_t gg = nn & ~int64_t(15);
+  const int64_t R = min(int64_t(16), N - gg);
+  const int64_t p0 = gg * nkb + (nn - gg);
   const int g = lane >> 4;
   const int split = blockIdx.y;
   const int q0 = split * quads_per_split;
@@ -81,115 +124,123 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
 
   float lv[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) lv[i] = codebook[i];
+  for (int i = 0; i < 16; ++i) lv[i] = gptr(codebook)[i];
 
-  // rows of M past the end are loaded from row M-1 (their outputs are dropped)
-  const uint16_t* xrow[MT];
+  // DMA of an activation chunk: instruction j covers chunk rows 2j, 2j+1;
+  // instruction j is issued by wave j % 4.  Lane l writes LDS bytes
+  // [16l, 16l + 16) of the instruction's 1 KiB: row 2j + l / 32, physical
+  // 16-byte column l % 32, which holds logical column (l % 32) ^ (row % 16).
+  // Every wave issues XPW DMA instructions per chunk (a compile-time count,
+  // so the waits below are exact): instruction j = wave + 4t covers chunk
+  // rows 2j, 2j+1; rows past M re-read row M-1 (their products are dropped).
+  auto load_x = [&](int q, int stage) {
+    const int kq = min(q, nquads - 1) * 256;                // first k of the quad
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) xrow[mt] = J.X + min((int64_t)(mt * 16 + (lane & 15)), M - 1) * K;
-
-  using U = GemvUnit<MT, PREX>;
-  // storage position of (nn, kb): the 16 rows of this row group are
-  // contiguous at each k-block, so lane l of a unit reads bytes [32l, 32l+32)
-  // of a 2 KiB run (full row group)
-  const int64_t g0 = nn & ~int64_t(15);
-  const int64_t R = min(int64_t(16), N - g0);
-  const int64_t p0 = g0 * nkb + (nn - g0);
-  auto load = [&](int q, U& u) {
-    const int kb = 4 * q + g;
-    u.ok = nok && kb < nkb;
-    const int kbc = min(kb, nkb - 1);
+    for (int t = 0; t < XPW; ++t) {
+      const int j = wave + 4 * t;
+      const int row = 2 * j + (lane >> 5);
+      const int col = (lane & 31) ^ (row & 15);
+      const int64_t m = min((int64_t)row, M - 1);
+      // k past the row end (last quad of a ragged k) reads the clamped
+      // column; those products meet zero weights
+      const int64_t kk = min((int64_t)(kq + 8 * col), K - 8);
+      __builtin_amdgcn_global_load_lds(gptr(J.X + m * K + kk),
+                                       (__attribute__((address_space(3))) void*)(stage_ptr(stage) + j * 512),
+                                       16, 0, 0);
+    }
+  };
+  auto load_w = [&](int q, GemvRaw<MT>& u) {
+    const int kbc = min(4 * min(q, nquads - 1) + g, nkb - 1);
     const int64_t b = nn * nkb + kbc;
     const int64_t p = p0 + kbc * R;
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w.codes + p * 32);
+    const QL_GLOBAL u32x4_t* src = gptr(reinterpret_cast<const u32x4_t*>(w.codes + p * 32));
     u.c0 = src[0];
     u.c1 = src[1];
-    u.qbyte = w.qscale[p];
-    u.step = w.step[b >> 8];
-    if constexpr (PREX) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          u.x[mt][i] = *reinterpret_cast<const u32x4_t*>(xrow[mt] + (int64_t)kbc * kBlock + i * 8);
-    }
+    u.qbyte = gptr(w.qscale)[p];
+    u.step = gptr(w.step)[b >> 8];
   };
 
   f32x4_t acc[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int q, const U& u) {
-    const float sc = u.ok ? (float)u.qbyte * u.step : 0.f;
+  auto compute = [&](int q, int stage, const GemvRaw<MT>& u) {
+    const bool ok = nok && 4 * q + g < nkb;
+    const float scr = (float)u.qbyte * u.step;
+    const float sc = ok ? scr : 0.f;
     const Lut t = make_lut(lv, sc);
-    const int kbc = min(4 * q + g, nkb - 1);
+    const uint16_t* sx = stage_ptr(stage);
+    u32x4_t af[MT][8];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = (int)min((int64_t)(16 * mt + (lane & 15)), M - 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        af[mt][i] = *reinterpret_cast<const u32x4_t*>(sx + row * 256 + ((8 * g + i) ^ (row & 15)) * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // the fragment reads go out before the decode
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const u32x4_t bf = decode8(t, i < 4 ? u.c0[i] : u.c1[i - 4]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        u32x4_t af;
-        if constexpr (PREX)
-          af = u.x[mt][i];
-        else
-          af = *reinterpret_cast<const u32x4_t*>(xrow[mt] + (int64_t)kbc * kBlock + i * 8);
-        acc[mt][i & 1] = mfma16x16x32(af, bf, acc[mt][i & 1]);
-      }
+      for (int mt = 0; mt < MT; ++mt) acc[mt][i & 1] = mfma16x16x32(af[mt][i], bf, acc[mt][i & 1]);
     }
   };
 
-  // quads q0 + wave + 4j of this split, one unit ahead: the loads of the
-  // next unit are issued (and kept, by the scheduling fences) before the
-  // current unit is decoded, whose own loads are then the only ones waited for
-  constexpr int NLOAD = 4 + (PREX ? 8 * MT : 0);   // vector loads per unit
-  const int qlast = q1 - 1;
-  int q = q0 + wave;
-  if (q < q1) {
-    U u0, u1;
-    load(q, u0);
-    for (;;) {
-      load(min(q + 4, qlast), u1);
+  // wait for this wave's loads of quad q (everything but the loads issued in
+  // the following iteration: 4 code loads + XPW chunk loads), then barrier
+  auto wait_q = [&]() {
+    QL_VMCNT(4 + XPW);
+    QL_LGKMCNT0();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  if (q0 < q1) {
+    GemvRaw<MT> rw[3];
+    load_w(q0, rw[0]);
+    load_x(q0, 0);
+    load_w(q0 + 1, rw[1]);
+    load_x(q0 + 1, 1);
+    auto step = [&](int q, auto PHc) {
+      constexpr int PH = decltype(PHc)::value;
+      wait_q();
       __builtin_amdgcn_sched_barrier(0);
-      QL_VMCNT(NLOAD);
+      load_w(q + 2, rw[(PH + 2) % 3]);
+      load_x(q + 2, (PH + 2) % 3);
       __builtin_amdgcn_sched_barrier(0);
-      compute(q, u0);
+      compute(q, PH, rw[PH]);
       __builtin_amdgcn_sched_barrier(0);
-      q += 4;
-      if (q >= q1) break;
-      load(min(q + 4, qlast), u0);
-      __builtin_amdgcn_sched_barrier(0);
-      QL_VMCNT(NLOAD);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(q, u1);
-      __builtin_amdgcn_sched_barrier(0);
-      q += 4;
-      if (q >= q1) break;
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    int q = q0;
+    for (; q + 2 < q1; q += 3) {
+      step(q, P0{});
+      step(q + 1, P1{});
+      step(q + 2, P2{});
     }
+    if (q < q1) step(q, P0{});
+    if (q + 1 < q1) step(q + 1, P1{});
   }
 
-  f32x4_t tot[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) tot[mt] = acc[mt][0] + acc[mt][1];
-  if (wave > 0)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) s_red[wave - 1][mt][lane] = tot[mt];
-  __syncthreads();
-  if (wave != 0) return;
+  const bool lvec = J.lora.r % 8 == 0 && (reinterpret_cast<uintptr_t>(J.lora.R) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(J.lora.L) & 15) == 0 && J.lora.rs_j == 1 &&
+                    J.lora.rs_c == J.lora.r;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    f32x4_t v = tot[mt];
-    v += s_red[0][mt][lane];
-    v += s_red[1][mt][lane];
-    v += s_red[2][mt][lane];
+    const f32x4_t v = acc[mt][0] + acc[mt][1];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t m = mt * 16 + g * 4 + e;
       if (m < M && nok) {
         float y = v[e];
         if (ksplit > 1) {
-          J.part[((int64_t)split * M + m) * N + n] = y;
+          gptr_w(J.part)[((int64_t)split * M + m) * N + n] = y;
         } else {
-          if (J.lora.r > 0) y += J.lora.scaling * lora_dot(J.lora, m, n);
+          if (J.lora.r > 0) y += J.lora.scaling * lora_dot_v(J.lora, m, n, lvec);
           store_out(J.Y, J.y_bf16, m * N + n, y);
         }
       }
@@ -214,17 +265,14 @@ hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16
   const int64_t nquads = (w.k / kBlock + 3) / 4;
   const int per = (int)((nquads + ksplit - 1) / ksplit);
   const GemvJob job{X, w, lora, Y, part, M, (int)y_bf16, 0};
-  dim3 grid((unsigned)((w.n + 15) / 16), (unsigned)ksplit);
-  const int mt = (int)((M + 15) / 16);
-#define QL_GEMV(MT)                                                                             \
-  hipLaunchKernelGGL((k_gemv_fwd<MT, false>), grid, dim3(256), 0, s, job, nullptr, 0, codebook, \
-                     ksplit, per)
-  switch (mt) {
-    case 1: QL_GEMV(1); break;
-    case 2: QL_GEMV(2); break;
-    case 3: QL_GEMV(3); break;
-    default: QL_GEMV(4); break;
-  }
+  dim3 grid((unsigned)((w.n + 63) / 64), (unsigned)ksplit);
+#define QL_GEMV(MT, XPW)                                                                    \
+  hipLaunchKernelGGL((k_gemv_fwd<MT, XPW, false>), grid, dim3(256), 0, s, job, nullptr, 0, \
+                     codebook, ksplit, per)
+  // M <= 32, checked by the caller
+  if (M <= 8) QL_GEMV(1, 1);
+  else if (M <= 16) QL_GEMV(1, 2);
+  else QL_GEMV(2, 4);
 #undef QL_GEMV
   return hipGetLastError();
 }
@@ -232,17 +280,13 @@ hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16
 hipError_t launch_gemv_grouped(const GemvJob* jobs, int njobs, int64_t row_groups, int64_t M,
                                const float* codebook, int64_t max_quads, hipStream_t s) {
   dim3 grid((unsigned)row_groups, 1);
-  const int mt = (int)((M + 15) / 16);
   const GemvJob none{};
-#define QL_GEMV(MT)                                                                           \
-  hipLaunchKernelGGL((k_gemv_fwd<MT, true>), grid, dim3(256), 0, s, none, jobs, njobs,        \
+#define QL_GEMV(MT, XPW)                                                                     \
+  hipLaunchKernelGGL((k_gemv_fwd<MT, XPW, true>), grid, dim3(256), 0, s, none, jobs, njobs, \
                      codebook, 1, (int)max_quads)
-  switch (mt) {
-    case 1: QL_GEMV(1); break;
-    case 2: QL_GEMV(2); break;
-    case 3: QL_GEMV(3); break;
-    default: QL_GEMV(4); break;
-  }
+  if (M <= 8) QL_GEMV(1, 1);
+  else if (M <= 16) QL_GEMV(1, 2);
+  else QL_GEMV(2, 4);
 #undef QL_GEMV
   return hipGetLastError();
 }

@@ -33,7 +33,7 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const flo
 hipError_t launch_gemm_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,
                            const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
                            hipStream_t s);
-// One projection of the small-M forward.  rg_begin: first 16-row group of
+// One projection of the small-M forward.  rg_begin: first 64-row workgroup of
 // this job in a grouped launch (ascending over the job list).
 struct GemvJob {
   const uint16_t* X;
@@ -51,7 +51,7 @@ hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16
                            const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
                            hipStream_t s);
 // Grouped small-M forward: one launch over `njobs` device-resident jobs that
-// share M, covering `row_groups` 16-row groups in total; no split of the
+// share M, covering `row_groups` 64-row workgroups in total; no split of the
 // contraction.  max_quads: the largest k/256 (rounded up) over the jobs.
 hipError_t launch_gemv_grouped(const GemvJob* jobs, int njobs, int64_t row_groups, int64_t M,
                                const float* codebook, int64_t max_quads, hipStream_t s);

@@ -105,7 +105,7 @@ def test_fwd_argument_errors():
     assert _fwd(L, d, r=129) == 5
     assert _fwd(L, d, ydt=7) == 4
     assert _fwd(L, d, path=3) == 8
-    assert _fwd(L, d, path=1, m=65) == 8
+    assert _fwd(L, d, path=1, m=33) == 8
     assert _fwd(L, d, X=FAKE + 2) == 3
     assert _fwd(L, d, Y=FAKE + 4) == 3
     assert _fwd(L, d, m=16, wsb=0, T=None) == 6
@@ -163,7 +163,7 @@ def test_group_init_argument_errors():
     assert init([ok, ok], handle=False) == 1
     assert init([ok, ok], table=None) == 1
     assert init([ok, ok], count=0) == 8
-    assert init([ok, ok], m=65) == 8
+    assert init([ok, ok], m=33) == 8
     assert init([ok, ok], m=0) == 2
     assert init([ok, ok], ydt=3) == 4
     assert init([ok, ok], table=FAKE + 4) == 3
@@ -184,7 +184,7 @@ def test_grouped_fwd_argument_errors():
     assert L.qlora_linear_fwd_grouped(ctypes.byref(g), None, None) == 1
     bad = B._Group(FAKE, 0, 0, 0, 1, 1, 8, 1)
     assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
-    bad = B._Group(FAKE, 2, 0, 0, 1, 65, 8, 1)
+    bad = B._Group(FAKE, 2, 0, 0, 1, 33, 8, 1)
     assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
     bad = B._Group(FAKE, 2, 3, 0, 1, 1, 8, 1)
     assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
