@@ -11,6 +11,17 @@ are resident in HBM before the timed region; no allocation inside it.
 Prints one JSON line.  Throughput is algorithmic: forward 2MNK + 2Mr(K+N),
 backward 2MNK + 2Mr(2K+2N) flops; bytes = packed weight once per pass plus
 every activation, gradient and adapter tensor at its dtype.
+
+Other workloads (--workload), each printing its own line of the same form:
+  decode      the seven projections stacked for 32 layers (6.48e9 NF4 params,
+              3.35 GB packed), forward only at M = 1 (also 4 and 16 in
+              "per_m"), LoRA r = 8, alpha = 16 on q, k, v, o; one grouped
+              launch per sweep; effective GB/s against HBM peak.
+  quantize70b quantize + double-quantize a 70B-style layer (q, k, v, o
+              8192x8192; gate, up 28672x8192; down 8192x28672; N(0, 0.015)
+              with 0.1 % of the weights scaled x20); GB/s against HBM peak.
+  layer70b    the same layer, fwd + bwd at M = 4096 with LoRA r = 16,
+              alpha = 32 on all seven; TFLOP/s against bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -36,6 +47,10 @@ PROJ = [  # name, N (out), K (in), LoRA rank
 WORKLOAD = ("7B-style decoder layer linears (q,k,v,o 4096x4096; gate,up 11008x4096; "
             "down 4096x11008), M=2048 tokens, LoRA r=8 alpha=16 on q,k,v,o, fwd+bwd")
 METRIC = "QLoRA linear fwd+bwd TFLOP/s & effective GB/s (% roofline) on 1 MI355X"
+PROJ70 = [("q", 8192, 8192), ("k", 8192, 8192), ("v", 8192, 8192), ("o", 8192, 8192),
+          ("gate", 28672, 8192), ("up", 28672, 8192), ("down", 8192, 28672)]
+DECODE_LAYERS = 32
+CPU_DECODE_LAYERS = 5
 
 
 def flops_fwd(M, N, K, r):
@@ -115,19 +130,7 @@ def cpu_baseline(sample_tokens: int):
                       f"in float64 numpy ({elapsed:.1f} s)"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=768)
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only; --gpus must be 1 "
-              "(the multi-GPU sharding is a design, not built)", file=sys.stderr)
-        sys.exit(2)
-
+def run_layer7b(args):
     import torch
 
     import synth
@@ -238,6 +241,281 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
+    return out
+
+
+
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def _timed(fn, steps, warmup):
+    """Run fn warmup times, then time `steps` runs with HIP events on the
+    current stream: (wall seconds per run, GPU seconds per run)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = _events()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    return wall, e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def _traffic(kernel, srcs):
+    return traffic_from_profile(kernel, srcs)
+
+
+def run_decode(args):
+    """Forward-only sweep over 32 layers x 7 projections at small M, one grouped
+    launch (plus one for the LoRA T products) per sweep."""
+    import torch
+
+    import synth
+    from qlora_fine_tuning_nf4_amd import binding as QB
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cb = QB.device_codebook(dev)
+    weights = []
+    for layer in range(DECODE_LAYERS):
+        for i, (name, N, K, r) in enumerate(PROJ):
+            W = synth.device_normal_bf16((N, K), 0.02, synth.tensor_seed(3, 100 * layer + 10 * i),
+                                         device=dev)
+            weights.append((QB.qlora_quantize(W, cb), N, K, r))
+            del W
+    torch.cuda.synchronize()
+    per_m = {}
+    kern = None
+    for M in (1, 4, 16):
+        jobs, jobs0 = [], []
+        nbytes = nbytes0 = 0
+        for idx, (q, N, K, r) in enumerate(weights):
+            X = synth.device_normal_bf16((M, K), 1.0, synth.tensor_seed(3, 20000 + idx), device=dev)
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            j = dict(w=q, X=X, Y=Y)
+            b0 = q.nbytes() + 2 * M * K + 2 * M * N
+            nbytes0 += b0
+            nbytes += b0
+            if r:
+                j.update(A=synth.device_normal_bf16((r, K), 0.01, synth.tensor_seed(3, 40000 + idx),
+                                                    device=dev),
+                         B=synth.device_normal_bf16((N, r), 0.01, synth.tensor_seed(3, 60000 + idx),
+                                                    device=dev),
+                         scaling=ALPHA / RANK, T=torch.empty((M, r), dtype=torch.float32, device=dev))
+                nbytes += 2 * r * K + 2 * N * r + 4 * M * r
+            jobs.append(j)
+            jobs0.append(dict(w=q, X=X, Y=Y))
+        g = QB.qlora_group_init(jobs, M, y_dtype=torch.bfloat16)
+        g0 = QB.qlora_group_init(jobs0, M, y_dtype=torch.bfloat16)
+        wall, gpu = _timed(lambda: QB.qlora_linear_fwd_grouped(g, cb), args.steps, args.warmup)
+        # the streaming kernel alone: the same sweep without LoRA is one launch
+        wall0, gpu0 = _timed(lambda: QB.qlora_linear_fwd_grouped(g0, cb), args.steps, args.warmup)
+        per_m[str(M)] = {"ms_per_sweep": round(wall * 1e3, 4), "GBps": round(nbytes / wall / 1e9, 1),
+                         "frac_of_hbm_peak": round(nbytes / wall / 1e9 / PEAK_HBM_GBS, 4),
+                         "kernel_us": round(gpu0 * 1e6, 1),
+                         "kernel_GBps": round(nbytes0 / gpu0 / 1e9, 1)}
+        if M == 1:
+            kern = (nbytes0, gpu0, wall, nbytes)
+        del g, g0, jobs, jobs0
+    nbytes0, gpu0, wall, nbytes = kern
+    achieved = nbytes0 / gpu0 / 1e9
+    out = {
+        "metric": "QLoRA NF4 decode-sweep forward effective GB/s (% HBM roofline) on 1 MI355X",
+        "value": round(nbytes / wall / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights quantized to NF4+DQ, N(0,1) activations)",
+        "config": {"workload": f"decode sweep: {DECODE_LAYERS} layers x (q,k,v,o 4096x4096; gate,up "
+                               "11008x4096; down 4096x11008), M=1, LoRA r=8 alpha=16 on q,k,v,o, "
+                               "forward only, one grouped launch per sweep",
+                   "M": 1, "layers": DECODE_LAYERS, "params": sum(N * K for _, N, K, _ in weights),
+                   "packed_bytes": sum(q.nbytes() for q, *_ in weights), "parallelism": "none (1 GPU)"},
+        "per_m": per_m,
+        "roofline": {"bound": "hbm", "kernel": "k_gemv_fwd", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "avg_launch_us": round(gpu0 * 1e6, 1),
+                     "traffic": _traffic("k_gemv_fwd", ["gemv.hip", "common.h"])},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode()
+    return out
+
+
+def cpu_baseline_decode():
+    """The oracle on a bounded sample of the decode sweep: dequantize + forward
+    of the seven projections of the first CPU_DECODE_LAYERS layers at M = 1
+    (float64 numpy)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import synth
+    from oracle import linear as olin
+    from oracle import nf4 as onf4
+
+    lv, mid = onf4.codebook()
+    nbytes, elapsed = 0, 0.0
+    for layer in range(CPU_DECODE_LAYERS):
+        for i, (name, N, K, r) in enumerate(PROJ):
+            idx = 7 * layer + i
+            W = synth.normal_bf16((N, K), 0.02, synth.tensor_seed(3, 100 * layer + 10 * i))
+            codes, qs, st = onf4.quantize(W, mid)
+            X = synth.normal_bf16((1, K), 1.0, synth.tensor_seed(3, 20000 + idx))
+            A = synth.normal_bf16((r, K), 0.01, synth.tensor_seed(3, 40000 + idx)) if r else None
+            B = synth.normal_bf16((N, r), 0.01, synth.tensor_seed(3, 60000 + idx)) if r else None
+            t0 = time.perf_counter()
+            Wd = onf4.dequantize(codes, qs, st, lv).reshape(N, K)
+            olin.forward(Wd, X, A, B, ALPHA / RANK)
+            elapsed += time.perf_counter() - t0
+            nbytes += packed_bytes(N, K) + 2 * K + 2 * N
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{CPU_DECODE_LAYERS} of the {DECODE_LAYERS} layers (7 projections each) at "
+                      f"M=1: dequantize + forward in float64 numpy ({elapsed:.1f} s)"}
+
+
+def _weights70(dev):
+    import synth
+    out = []
+    for i, (name, N, K) in enumerate(PROJ70):
+        out.append(synth.device_normal_bf16((N, K), 0.015, synth.tensor_seed(4, 10 * i), device=dev,
+                                            outlier_rate=0.001, outlier_scale=20))
+    return out
+
+
+def run_quantize70b(args):
+    import torch
+
+    from qlora_fine_tuning_nf4_amd import binding as QB
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cb = QB.device_codebook(dev)
+    Ws = _weights70(dev)
+    outs = [QB.NF4Weight.empty(N, K, dev) for _, N, K in PROJ70]
+    params = sum(N * K for _, N, K in PROJ70)
+    nbytes = sum(2 * N * K + packed_bytes(N, K) for _, N, K in PROJ70)
+
+    def step():
+        for W, o in zip(Ws, outs):
+            QB.qlora_quantize(W, cb, out=o)
+    wall, gpu = _timed(step, args.steps, args.warmup)
+    # largest projection alone (one launch) for the kernel roofline
+    big = 4
+    kb = 2 * PROJ70[big][1] * PROJ70[big][2] + packed_bytes(PROJ70[big][1], PROJ70[big][2])
+    _, gk = _timed(lambda: QB.qlora_quantize(Ws[big], cb, out=outs[big]), args.steps, args.warmup)
+    ach = kb / gk / 1e9
+    out = {
+        "metric": "NF4 + double-quant quantization GB/s (% HBM roofline) on 1 MI355X",
+        "value": round(nbytes / wall / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16->u8",
+        "data": "synthetic (seeded N(0,0.015) bf16 weights, 0.1% outliers x20)",
+        "config": {"workload": "quantize a 70B-style layer: q,k,v,o 8192x8192; gate,up 28672x8192; "
+                               "down 8192x28672 (973,078,528 params)", "params": params,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "k_quant_nf4_dq", "achieved": round(ach, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                     "avg_launch_us": round(gk * 1e6, 1),
+                     "traffic": _traffic("k_quant_nf4_dq", ["quantize.hip", "common.h"])},
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from threadpoolctl import threadpool_info
+
+        import synth
+        from oracle import nf4 as onf4
+        _, mid = onf4.codebook()
+        rows = 16384
+        W = synth.normal_bf16((rows, 8192), 0.015, 77, outlier_rate=0.001, outlier_scale=20)
+        t0 = time.perf_counter()
+        onf4.quantize(W, mid)
+        el = time.perf_counter() - t0
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+        out["cpu_baseline"] = {"value": round((2 * rows * 8192 + packed_bytes(rows, 8192)) / el / 1e9, 4),
+                               "unit": "GB/s", "cores": threads, "kind": "oracle",
+                               "sample": f"{rows} x 8192 rows of the q projection ({el:.1f} s)"}
+    return out
+
+
+def run_layer70b(args):
+    import torch
+
+    import synth
+    from qlora_fine_tuning_nf4_amd import binding as QB
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cb = QB.device_codebook(dev)
+    M, r, alpha = 4096, 16, 32
+    s = alpha / r
+    layers = []
+    for i, (W, (name, N, K)) in enumerate(zip(_weights70(dev), PROJ70)):
+        q = QB.qlora_quantize(W, cb)
+        del W
+        L = dict(N=N, K=K, q=q)
+        L["X"] = synth.device_normal_bf16((M, K), 1.0, synth.tensor_seed(4, 10 * i + 1), device=dev)
+        L["dY"] = synth.device_normal_bf16((M, N), 1.0, synth.tensor_seed(4, 10 * i + 2), device=dev)
+        L["A"] = synth.device_normal_bf16((r, K), 0.01, synth.tensor_seed(4, 10 * i + 3), device=dev)
+        L["B"] = synth.device_normal_bf16((N, r), 0.01, synth.tensor_seed(4, 10 * i + 4), device=dev)
+        L["Y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        L["T"] = torch.empty((M, r), dtype=torch.float32, device=dev)
+        L["dX"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        L["dA"] = torch.empty((r, K), dtype=torch.float32, device=dev)
+        L["dB"] = torch.empty((N, r), dtype=torch.float32, device=dev)
+        nws = max(QB.qlora_workspace_bytes(0, M, N, K, r), QB.qlora_workspace_bytes(1, M, N, K, r), 16)
+        L["ws"] = torch.empty(nws, dtype=torch.uint8, device=dev)
+        layers.append(L)
+    torch.cuda.synchronize()
+
+    def step():
+        for L in layers:
+            QB.qlora_linear_fwd(L["q"], cb, L["X"], L["A"], L["B"], s, out=L["Y"], T_out=L["T"],
+                                workspace=L["ws"])
+            QB.qlora_linear_bwd(L["q"], cb, L["X"], L["dY"], L["A"], L["B"], s, T=L["T"],
+                                dX_out=L["dX"], dA_out=L["dA"], dB_out=L["dB"], workspace=L["ws"])
+    wall, gpu = _timed(step, args.steps, args.warmup)
+    flops = sum(flops_fwd(M, L["N"], L["K"], r) + flops_bwd(M, L["N"], L["K"], r) for L in layers)
+    tf = flops / wall / 1e12
+    out = {
+        "metric": METRIC, "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4),
+        "gpu_event_ms_per_step": round(gpu * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.015) weights with 0.1% outliers x20, NF4+DQ; N(0,1) activations)",
+        "config": {"workload": "70B-style layer linears (q,k,v,o 8192x8192; gate,up 28672x8192; down "
+                               "8192x28672), M=4096 tokens, LoRA r=16 alpha=32 on all seven, fwd+bwd",
+                   "M": M, "r": r, "alpha": alpha, "parallelism": "none (1 GPU)"},
+        "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+    }
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=768)
+    ap.add_argument("--workload", default="layer7b",
+                    choices=["layer7b", "decode", "quantize70b", "layer70b"])
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only; --gpus must be 1 "
+              "(the multi-GPU sharding is a design, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    run = {"layer7b": run_layer7b, "decode": run_decode, "quantize70b": run_quantize70b,
+           "layer70b": run_layer70b}[args.workload]
+    out = run(args)
     print(json.dumps(out), flush=True)
 
 
