@@ -10,12 +10,41 @@
 
 namespace ql {
 
+// Encode table: v in [-1, 1] falls in bin floor(256 v + 256) (clamped to
+// 511); bin i covers [-1 + i/256, -1 + (i+1)/256).  Widened by 2^-10 on both
+// sides, each bin holds at most one decision midpoint (they are more than
+// 0.05 apart), so code = #{k : v > mid_k} = base_i + (v > m_i), with base_i
+// the number of midpoints below the widened bin and m_i the midpoint inside
+// it (+inf if none).  The widening covers the rounding of the bin index.
+constexpr int kEncBins = 512;
+
+QL_DEV void build_encode_table(const float* mid, float2* tab, int tid, int nthreads) {
+  for (int i = tid; i < kEncBins; i += nthreads) {
+    const float lo = -1.0f + (float)i * (1.0f / 256.0f) - (1.0f / 1024.0f);
+    const float hi = -1.0f + (float)(i + 1) * (1.0f / 256.0f) + (1.0f / 1024.0f);
+    int base = 0;
+    float m = __builtin_huge_valf();
+    for (int k = 0; k < 15; ++k) {
+      if (mid[k] < lo) ++base;
+      else if (mid[k] <= hi) m = mid[k];
+    }
+    tab[i] = make_float2(m, __builtin_bit_cast(float, base));
+  }
+}
+
 // One workgroup per group of 256 blocks (16384 weights, 32 KiB of bf16).
 // Each wave handles 8 blocks per iteration: lane l reads 16 bytes (8 weights)
 // of block l/8, so one wave load is 1 KiB contiguous.  The block absmax is a
 // max over the 8 lanes of the block; encoding needs only the block's own
 // absmax, so codes are written in the same pass and the group max is taken
 // afterwards from LDS.
+//
+// Quotient: v = fp32(w / absmax) is formed as fp32(w * r) in binary64 with r
+// = 1/absmax refined to binary64 accuracy.  For bf16 w and absmax (8-bit
+// significands) the exact quotient is either a short dyadic (no fp32 rounding
+// tie possible) or at least 2^-33 (relative) away from every fp32 rounding
+// boundary, far more than the binary64 error, so this equals the correctly
+// rounded binary32 division bit for bit.
 __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict__ W,
                                                       const float* __restrict__ codebook,
                                                       uint8_t* __restrict__ codes,
@@ -23,19 +52,29 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
                                                       float* __restrict__ step, int64_t N,
                                                       int64_t nkb) {
   __shared__ float s_absmax[kGroup];
-  const int64_t nblocks = N * nkb;
   __shared__ float s_red[4];
+  __shared__ float2 s_tab[kEncBins];
+  const int64_t nblocks = N * nkb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t blk0 = (int64_t)blockIdx.x * kGroup;
   const int nb = (int)min<int64_t>(kGroup, nblocks - blk0);
 
-  float mid[15];
+  {
+    float mid[15];
 #pragma unroll
-  for (int i = 0; i < 15; ++i) mid[i] = codebook[16 + i];
+    for (int i = 0; i < 15; ++i) mid[i] = codebook[16 + i];
+    build_encode_table(mid, s_tab, tid, 256);
+  }
+  __syncthreads();
 
+  // (row, k-block) of this lane's block, advanced by 32 blocks per iteration
+  // without a division
+  const int lb0 = wave * 8 + (lane >> 3);
+  int64_t row = (blk0 + lb0) / nkb;
+  int64_t kb = (blk0 + lb0) - row * nkb;
 #pragma unroll 2
   for (int it = 0; it < kGroup / 32; ++it) {
-    const int lb = it * 32 + wave * 8 + (lane >> 3);   // local block index
+    const int lb = it * 32 + lb0;                      // local block index
     const bool valid = lb < nb;
     u32x4_t raw = {0u, 0u, 0u, 0u};
     if (valid)
@@ -52,21 +91,32 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
     am = fmaxf(am, __shfl_xor(am, 1));
     am = fmaxf(am, __shfl_xor(am, 2));
     am = fmaxf(am, __shfl_xor(am, 4));
+    // 1/absmax in binary64: hardware reciprocal plus one Newton step (0 for
+    // an all-zero block, which then encodes as the zero level)
+    double r = 0.0;
+    if (am > 0.f) {
+      const double a = (double)am;
+      r = __builtin_amdgcn_rcp(a);
+      r = __builtin_fma(r, __builtin_fma(-a, r, 1.0), r);
+    }
     uint32_t word = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      // binary32 quotient, correctly rounded (no reciprocal); zero block -> 0
-      const float v = am == 0.f ? 0.f : x[j] / am;
-      uint32_t c = 0;
-#pragma unroll
-      for (int i = 0; i < 15; ++i) c += v > mid[i] ? 1u : 0u;
+      const float v = (float)((double)x[j] * r);
+      const int bin = min((int)__builtin_fmaf(v, 256.0f, 256.0f), kEncBins - 1);
+      const float2 e = s_tab[bin];
+      const uint32_t c = (uint32_t)__builtin_bit_cast(int, e.y) + (v > e.x ? 1u : 0u);
       word |= c << (j < 4 ? 8 * j : 8 * (j - 4) + 4);
     }
     if (valid) {
-      const int64_t b = blk0 + lb;
-      const int64_t p = blk_pos(b / nkb, b % nkb, N, nkb);
+      const int64_t p = blk_pos(row, kb, N, nkb);
       reinterpret_cast<uint32_t*>(codes)[p * 8 + (lane & 7)] = word;
       if ((lane & 7) == 0) s_absmax[lb] = am;
+    }
+    kb += 32;
+    while (kb >= nkb) {
+      kb -= nkb;
+      ++row;
     }
   }
   __syncthreads();

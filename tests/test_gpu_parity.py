@@ -417,3 +417,39 @@ def test_grouped_forward_graph_replays_match_eager():
         now = [j["Y"] for j in jobs] + [j["T"] for j in jobs if "T" in j]
         for a, b in zip(now, eager):
             assert torch.equal(a, b), f"replay {rep}"
+
+
+def test_quantize_quotients_near_decision_midpoints():
+    """Blocks whose elements sit a few bf16 ulps around absmax * midpoint for
+    every midpoint, over absmax values spread across the exponent range: the
+    kernel's quotient must round exactly as binary32 division does."""
+    B = _dev()
+    g = np.random.default_rng(2024)
+    nblk = 32768
+    # absmax: random bf16 magnitudes over a wide exponent range (normal numbers)
+    exps = g.integers(90, 170, nblk)
+    mants = g.integers(0, 128, nblk)
+    a_bits = ((exps << 7) | mants).astype(np.uint16)
+    a = onf4.bf16_to_f32(a_bits).astype(np.float64)
+    mids = _MID.astype(np.float64)
+    blocks = np.empty((nblk, 64), dtype=np.uint16)
+    blocks[:, 0] = a_bits
+    for j in range(1, 64):
+        k = (j - 1) % 15
+        off = (j - 1) // 15 - 2                      # -2 .. 2 bf16 ulps around the target
+        tgt = onf4.f32_to_bf16_rne((a * mids[k]).astype(np.float32))
+        sgn = tgt & 0x8000
+        mag = (tgt & 0x7FFF).astype(np.int32) + off
+        mag = np.clip(mag, 0, 0x7F7F)
+        blocks[:, j] = (sgn | mag).astype(np.uint16)
+    # keep |x| <= absmax so the block's absmax is element 0
+    xf = np.abs(onf4.bf16_to_f32(blocks).astype(np.float64))
+    over = xf > a[:, None]
+    blocks[over] = (blocks[over] & 0x8000) | np.repeat(a_bits[:, None], 64, axis=1)[over]
+    w = blocks.reshape(2048, 1024)
+    q = B.qlora_quantize(_t(w), _cb(B))
+    torch.cuda.synchronize()
+    c, qs, st = _oracle_q(w)
+    c, qs = onf4.to_storage(c, qs, 2048, 1024)
+    assert np.array_equal(q.codes.cpu().numpy(), c)
+    assert np.array_equal(q.qscale.cpu().numpy(), qs)
