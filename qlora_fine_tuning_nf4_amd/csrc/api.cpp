@@ -128,9 +128,14 @@ BwdWs bwd_ws(int64_t m, int64_t n, int64_t k, int r) {
   return w;
 }
 
+// block counts are kept below 2^32 (n * k < 2^38 weights per matrix)
+bool shape_ok(int64_t n, int64_t k) {
+  return n >= 1 && k >= kB && k % kB == 0 && n <= ((int64_t(1) << 38) - 1) / k;
+}
+
 int check_desc(const qlora_nf4* W) {
   if (!W || !W->codes || !W->qscale || !W->step) return QLORA_ERR_NULL;
-  if (W->n < 1 || W->k < kB || W->k % kB) return QLORA_ERR_SHAPE;
+  if (!shape_ok(W->n, W->k)) return QLORA_ERR_SHAPE;
   if (!aligned(W->codes, 16) || !aligned(W->step, 4)) return QLORA_ERR_ALIGN;
   return QLORA_OK;
 }
@@ -174,7 +179,7 @@ int qlora_nf4_codebook(float* out) {
 }
 
 int qlora_nf4_bytes(int64_t n, int64_t k, size_t* codes, size_t* qscale, size_t* step) {
-  if (n < 1 || k < kB || k % kB) return QLORA_ERR_SHAPE;
+  if (!shape_ok(n, k)) return QLORA_ERR_SHAPE;
   const int64_t nb = n * (k / kB);
   if (codes) *codes = (size_t)(n * k / 2);
   if (qscale) *qscale = (size_t)nb;

@@ -8,20 +8,24 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace ql {
 
-// Encode table: v in [-1, 1] falls in bin floor(256 v + 256) (clamped to
-// 511); bin i covers [-1 + i/256, -1 + (i+1)/256).  Widened by 2^-10 on both
-// sides, each bin holds at most one decision midpoint (they are more than
-// 0.05 apart), so code = #{k : v > mid_k} = base_i + (v > m_i), with base_i
-// the number of midpoints below the widened bin and m_i the midpoint inside
-// it (+inf if none).  The widening covers the rounding of the bin index.
-constexpr int kEncBins = 512;
+// Encode table: v in [-1, 1] goes to bin n = rint(32 v + 32) in [0, 64];
+// bin n covers [(n - 32.5) / 32, (n - 31.5) / 32].  Widened by 2^-10 on both
+// sides, a bin holds at most one decision midpoint (they are more than 0.07
+// apart), so code = #{k : v > mid_k} = base_n + (v > m_n), with base_n the
+// number of midpoints below the widened bin and m_n the midpoint inside it
+// (+inf if none).  The widening covers the rounding of the bin index.  Few
+// bins keep the lookups mostly broadcast reads (weights crowd the centre).
+constexpr int kEncBins = 65;
+constexpr float kEncMagic = 12582912.0f;           // 1.5 * 2^23: rounds to integers in the mantissa
 
 QL_DEV void build_encode_table(const float* mid, float2* tab, int tid, int nthreads) {
   for (int i = tid; i < kEncBins; i += nthreads) {
-    const float lo = -1.0f + (float)i * (1.0f / 256.0f) - (1.0f / 1024.0f);
-    const float hi = -1.0f + (float)(i + 1) * (1.0f / 256.0f) + (1.0f / 1024.0f);
+    const float lo = ((float)i - 32.5f) * (1.0f / 32.0f) - (1.0f / 1024.0f);
+    const float hi = ((float)i - 31.5f) * (1.0f / 32.0f) + (1.0f / 1024.0f);
     int base = 0;
     float m = __builtin_huge_valf();
     for (int k = 0; k < 15; ++k) {
@@ -32,19 +36,42 @@ QL_DEV void build_encode_table(const float* mid, float2* tab, int tid, int nthre
   }
 }
 
-// One workgroup per group of 256 blocks (16384 weights, 32 KiB of bf16).
-// Each wave handles 8 blocks per iteration: lane l reads 16 bytes (8 weights)
-// of block l/8, so one wave load is 1 KiB contiguous.  The block absmax is a
-// max over the 8 lanes of the block; encoding needs only the block's own
-// absmax, so codes are written in the same pass and the group max is taken
-// afterwards from LDS.
-//
-// Quotient: v = fp32(w / absmax) is formed as fp32(w * r) in binary64 with r
-// = 1/absmax refined to binary64 accuracy.  For bf16 w and absmax (8-bit
-// significands) the exact quotient is either a short dyadic (no fp32 rounding
-// tie possible) or at least 2^-33 (relative) away from every fp32 rounding
-// boundary, far more than the binary64 error, so this equals the correctly
-// rounded binary32 division bit for bit.
+// 8 weights (one 16-byte piece of a block) -> one packed word, given the
+// block absmax am.  The quotient v = fp32(w / am) is formed as
+// q0 = fp32(w * r), e = w - q0 * am (exact, fma), v = fp32(q0 + e * r) with r
+// ~ 1/am: for bf16 w and am (8-bit significands) the exact quotient is a short
+// dyadic or at least 2^-33 (relative) away from every binary32 rounding
+// boundary, while q0 + e * r is within ~2^-46 of it, so v equals the
+// correctly rounded binary32 division bit for bit.  Absmax values below 2^-100
+// are scaled by 2^100 first (exact) so 1/am stays finite.
+QL_DEV uint32_t encode8(const float (&xin)[8], float am, const float2* tab) {
+  const bool tiny = am < 0x1p-100f;
+  const float sc = tiny ? 0x1p100f : 1.0f;
+  const float a = am * sc;
+  const float r = am > 0.f ? __builtin_amdgcn_rcpf(a) : 0.f;
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float x = xin[j] * sc;
+    const float q0 = x * r;
+    const float e = __builtin_fmaf(-q0, a, x);
+    const float v = __builtin_fmaf(e, r, q0);
+    const int n = __builtin_bit_cast(int, __builtin_fmaf(v, 32.0f, kEncMagic + 32.0f)) -
+                  __builtin_bit_cast(int, kEncMagic);
+    const float2 t = tab[n];
+    const uint32_t c = (uint32_t)__builtin_bit_cast(int, t.y) + (v > t.x ? 1u : 0u);
+    word |= c << (j < 4 ? 8 * j : 8 * (j - 4) + 4);
+  }
+  return word;
+}
+
+// One workgroup per group of 256 blocks (16384 weights, 32 KiB of bf16) at a
+// time, walking groups with the grid as stride; the next group's loads are
+// issued before the current one is encoded.  Each wave handles 8 blocks per
+// step: lane l reads 16 bytes (8 weights) of block l/8, so one wave load is
+// 1 KiB contiguous.  The block absmax is a max over the 8 lanes of the block;
+// encoding needs only the block's own absmax, so codes are written in the
+// same pass and the group max is taken afterwards from LDS.
 __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict__ W,
                                                       const float* __restrict__ codebook,
                                                       uint8_t* __restrict__ codes,
@@ -54,10 +81,12 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
   __shared__ float s_absmax[kGroup];
   __shared__ float s_red[4];
   __shared__ float2 s_tab[kEncBins];
-  const int64_t nblocks = N * nkb;
+  // block counts fit 32 bits (n * k / 64 < 2^32 for any weight the ABI
+  // accepts), so block coordinates use 32-bit division
+  const uint32_t nblocks = (uint32_t)(N * nkb), ukb = (uint32_t)nkb;
+  const uint32_t ngroups = (nblocks + kGroup - 1) / kGroup;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t blk0 = (int64_t)blockIdx.x * kGroup;
-  const int nb = (int)min<int64_t>(kGroup, nblocks - blk0);
+  const int lb0 = wave * 8 + (lane >> 3);
 
   {
     float mid[15];
@@ -65,73 +94,88 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
     for (int i = 0; i < 15; ++i) mid[i] = codebook[16 + i];
     build_encode_table(mid, s_tab, tid, 256);
   }
-  __syncthreads();
 
-  // (row, k-block) of this lane's block, advanced by 32 blocks per iteration
-  // without a division
-  const int lb0 = wave * 8 + (lane >> 3);
-  int64_t row = (blk0 + lb0) / nkb;
-  int64_t kb = (blk0 + lb0) - row * nkb;
-#pragma unroll 2
-  for (int it = 0; it < kGroup / 32; ++it) {
-    const int lb = it * 32 + lb0;                      // local block index
-    const bool valid = lb < nb;
-    u32x4_t raw = {0u, 0u, 0u, 0u};
-    if (valid)
-      raw = *reinterpret_cast<const u32x4_t*>(W + (blk0 + lb) * kBlock + (lane & 7) * 8);
-    float x[8];
+  // the eight 16-byte loads of this lane for group grp (a short last group
+  // re-reads its last block; those lanes are not stored)
+  auto load_group = [&](uint32_t grp, u32x4_t (&r)[kGroup / 32]) {
+    const uint32_t blk0 = grp * kGroup;
+    const int nb = (int)min(kGroup, nblocks - blk0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = bf16_lo(raw[j]);
-      x[2 * j + 1] = bf16_hi(raw[j]);
+    for (int it = 0; it < kGroup / 32; ++it) {
+      const int lb = min(it * 32 + lb0, nb - 1);
+      r[it] = *reinterpret_cast<const u32x4_t*>(W + ((int64_t)blk0 + lb) * kBlock + (lane & 7) * 8);
     }
-    float am = 0.f;
+  };
+
+  auto do_group = [&](uint32_t grp, const u32x4_t (&cur)[kGroup / 32]) {
+    const uint32_t blk0 = grp * kGroup;
+    const int nb = (int)min(kGroup, nblocks - blk0);
+    // (row, k-block) of this lane's block, advanced by 32 blocks per step
+    uint32_t row = (blk0 + lb0) / ukb;
+    uint32_t kb = (blk0 + lb0) - row * ukb;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
-    am = fmaxf(am, __shfl_xor(am, 1));
-    am = fmaxf(am, __shfl_xor(am, 2));
-    am = fmaxf(am, __shfl_xor(am, 4));
-    // 1/absmax in binary64: hardware reciprocal plus one Newton step (0 for
-    // an all-zero block, which then encodes as the zero level)
-    double r = 0.0;
-    if (am > 0.f) {
-      const double a = (double)am;
-      r = __builtin_amdgcn_rcp(a);
-      r = __builtin_fma(r, __builtin_fma(-a, r, 1.0), r);
-    }
-    uint32_t word = 0;
+    for (int it = 0; it < kGroup / 32; ++it) {
+      const int lb = it * 32 + lb0;                    // local block index
+      float x[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float v = (float)((double)x[j] * r);
-      const int bin = min((int)__builtin_fmaf(v, 256.0f, 256.0f), kEncBins - 1);
-      const float2 e = s_tab[bin];
-      const uint32_t c = (uint32_t)__builtin_bit_cast(int, e.y) + (v > e.x ? 1u : 0u);
-      word |= c << (j < 4 ? 8 * j : 8 * (j - 4) + 4);
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = bf16_lo(cur[it][j]);
+        x[2 * j + 1] = bf16_hi(cur[it][j]);
+      }
+      float am = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+      am = fmaxf(am, __shfl_xor(am, 1));
+      am = fmaxf(am, __shfl_xor(am, 2));
+      am = fmaxf(am, __shfl_xor(am, 4));
+      const uint32_t word = encode8(x, am, s_tab);
+      if (lb < nb) {
+        const int64_t p = blk_pos(row, kb, N, nkb);
+        reinterpret_cast<uint32_t*>(codes)[p * 8 + (lane & 7)] = word;
+        if ((lane & 7) == 0) s_absmax[lb] = am;
+      }
+      kb += 32;
+      while (kb >= ukb) {
+        kb -= ukb;
+        ++row;
+      }
     }
-    if (valid) {
-      const int64_t p = blk_pos(row, kb, N, nkb);
-      reinterpret_cast<uint32_t*>(codes)[p * 8 + (lane & 7)] = word;
-      if ((lane & 7) == 0) s_absmax[lb] = am;
+    __syncthreads();
+    const float a = tid < nb ? s_absmax[tid] : 0.f;
+    const float wm = wave_max(a);
+    if (lane == 0) s_red[wave] = wm;
+    __syncthreads();
+    const float c2 = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float st = c2 / 255.0f;
+    if (tid < nb) {
+      const float q = st == 0.f ? 0.f : fminf(rintf(a / st), 255.f);
+      const uint32_t b = blk0 + tid, br = b / ukb;
+      qscale[blk_pos(br, b - br * ukb, N, nkb)] = (uint8_t)q;
     }
-    kb += 32;
-    while (kb >= nkb) {
-      kb -= nkb;
-      ++row;
-    }
+    if (tid == 0) step[grp] = st;
+    __syncthreads();   // s_absmax and s_red are reused by the next group
+  };
+
+  // Workgroup ids are dealt to the 8 XCDs round robin; renumber them so that
+  // consecutive groups run on one XCD: the rows of a 16-row storage group are
+  // then written through one L2, which merges the 32-byte block writes of
+  // neighbouring rows into whole lines.  (The grid is a multiple of 8.)
+  const uint32_t per_xcd = gridDim.x / 8;
+  const uint32_t lwg = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  // ping-pong between two register sets (no copies of in-flight loads)
+  u32x4_t ra[kGroup / 32], rb[kGroup / 32];
+  uint32_t grp = lwg;
+  if (grp < ngroups) load_group(grp, ra);
+  __syncthreads();   // encode table ready
+  while (grp < ngroups) {
+    if (grp + gridDim.x < ngroups) load_group(grp + gridDim.x, rb);
+    do_group(grp, ra);
+    grp += gridDim.x;
+    if (grp >= ngroups) break;
+    if (grp + gridDim.x < ngroups) load_group(grp + gridDim.x, ra);
+    do_group(grp, rb);
+    grp += gridDim.x;
   }
-  __syncthreads();
-  const float a = tid < nb ? s_absmax[tid] : 0.f;
-  const float wm = wave_max(a);
-  if (lane == 0) s_red[wave] = wm;
-  __syncthreads();
-  const float c2 = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  const float st = c2 / 255.0f;
-  if (tid < nb) {
-    const float q = st == 0.f ? 0.f : fminf(rintf(a / st), 255.f);
-    const int64_t b = blk0 + tid;
-    qscale[blk_pos(b / nkb, b % nkb, N, nkb)] = (uint8_t)q;
-  }
-  if (tid == 0) step[blockIdx.x] = st;
 }
 
 // Dense dequantization: one thread per 64-block, 8 x 16-byte stores.
@@ -165,7 +209,10 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
 hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* codes,
                            uint8_t* qscale, float* step, int64_t n, int64_t k, hipStream_t s) {
   const int64_t nkb = k / kBlock, ngroups = (n * nkb + kGroup - 1) / kGroup;
-  hipLaunchKernelGGL(k_quant_nf4_dq, dim3((unsigned)ngroups), dim3(256), 0, s, W, codebook, codes,
+  // persistent workgroups (each walks groups with a stride of the grid), a
+  // few per CU so loads of the next group overlap the current one
+  const int64_t grid = std::min<int64_t>((ngroups + 7) / 8 * 8, 256 * 8);   // multiple of 8
+  hipLaunchKernelGGL(k_quant_nf4_dq, dim3((unsigned)grid), dim3(256), 0, s, W, codebook, codes,
                      qscale, step, n, nkb);
   return hipGetLastError();
 }

@@ -188,3 +188,10 @@ def test_grouped_fwd_argument_errors():
     assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
     bad = B._Group(FAKE, 2, 3, 0, 1, 1, 8, 1)
     assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
+
+
+def test_nf4_bytes_rejects_oversized_weights():
+    L = B.lib()
+    z = ctypes.c_size_t()
+    assert L.qlora_nf4_bytes(1 << 26, 4096, ctypes.byref(z), None, None) == 2   # 2^38 elements
+    assert L.qlora_nf4_bytes((1 << 26) - 1, 4096, ctypes.byref(z), None, None) == 0
