@@ -47,10 +47,14 @@ constexpr int GBM = 256, GBN = 128, GBK = 64;
 
 template <bool DX>
 struct Geo {
-  // LDS stage of one K-step of the weight, bf16, [rows][cols + 8]
+  // LDS stage of one K-step of the weight, bf16, [rows][ld].  Forward:
+  // 144-byte rows put the 16 rows of a ds_read_b128 quarter-wave on 16
+  // different bank groups.  Backward: 320-byte rows (16 banks apart) keep the
+  // 4-row x 32-byte footprints of the two 16-lane groups of a tr16 half-wave
+  // read on disjoint banks.
   static constexpr int rows = DX ? GBK : GBN;    // n (dx: contraction) or n (fwd: output)
   static constexpr int cols = DX ? GBN : GBK;    // k
-  static constexpr int ld = cols + 8;
+  static constexpr int ld = DX ? cols + 32 : cols + 8;
   static constexpr int stage = rows * ld;
 };
 
