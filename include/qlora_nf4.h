@@ -22,7 +22,8 @@
  *   - codes, X, Y, dY and dX must be 16-byte aligned; every other device
  *     pointer 4-byte aligned.
  *   - k % 64 == 0; m >= 1 and n >= 1 are arbitrary (ragged tails are masked);
- *     a packed weight holds fewer than 2^38 elements (n * k / 64 < 2^32 blocks).
+ *     n < 2^22, k < 2^22 and a packed weight holds fewer than 2^38 elements
+ *     (n * k / 64 < 2^32 blocks).
  *   - r == 0 switches the LoRA branch off: A, B, T_save, T_saved, dA and dB
  *     are then ignored and may be NULL.
  *   - All arguments are validated before any HIP call; on error nothing is
@@ -115,7 +116,7 @@ int qlora_nf4_codebook(float *out);
  * Host.  Byte sizes of the three arrays of an n x k packed weight
  * (news.rkmt.cn/news/4821 §2.3: 4-bit codes + 8-bit scale per 64 + fp32 per
  * 256 scales).  Any output pointer may be NULL.  QLORA_ERR_SHAPE unless
- * n >= 1, k >= 64, k % 64 == 0 and n * k < 2^38.
+ * n >= 1, k >= 64, k % 64 == 0, n < 2^22, k < 2^22 and n * k < 2^38.
  */
 int qlora_nf4_bytes(int64_t n, int64_t k, size_t *codes, size_t *qscale, size_t *step);
 

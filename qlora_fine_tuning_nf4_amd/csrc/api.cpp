@@ -129,8 +129,11 @@ BwdWs bwd_ws(int64_t m, int64_t n, int64_t k, int r) {
 }
 
 // block counts are kept below 2^32 (n * k < 2^38 weights per matrix)
+// n and k stay below 2^22 so that the kernels' per-tile byte offsets fit in
+// 32 bits; the element count below 2^38 keeps block indices in 32 bits.
 bool shape_ok(int64_t n, int64_t k) {
-  return n >= 1 && k >= kB && k % kB == 0 && n <= ((int64_t(1) << 38) - 1) / k;
+  return n >= 1 && k >= kB && k % kB == 0 && n < (int64_t(1) << 22) && k < (int64_t(1) << 22) &&
+         n <= ((int64_t(1) << 38) - 1) / k;
 }
 
 int check_desc(const qlora_nf4* W) {

@@ -30,6 +30,14 @@ QL_DEV f32x4_t mfma16x16x32(const u32x4_t a, const u32x4_t b, f32x4_t c) {
 // loads count in both the vector-memory and the LDS wait counters, so an LDS
 // wait would also wait for them.
 #define QL_GLOBAL __attribute__((address_space(1)))
+#define QL_LDS __attribute__((address_space(3)))
+
+// Raw buffer resource over `bytes` bytes from `base` (stride 0; loads past
+// the end return zeros).  Built in scalar registers when `base` is uniform.
+QL_DEV __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes = 0x7FFFFFFFu) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                          0x00020000);
+}
 template <typename T>
 QL_DEV const QL_GLOBAL T* gptr(const T* p) {
   return (const QL_GLOBAL T*)p;

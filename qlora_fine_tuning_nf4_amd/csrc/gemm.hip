@@ -32,6 +32,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace ql {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -108,6 +110,14 @@ QL_DEV void k_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier that waits for nothing: the caller has already waited for
+// what it needs.
+QL_DEV void k_barrier_issue() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Physical 16-byte chunk of logical chunk c in activation row r of a stage.
 QL_DEV int a_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
@@ -124,7 +134,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 3, wn = wave >> 2;                  // 64-row block, 64-column half
+  // wave w: rows [64 (w % 4), +64) of the tile, all 128 columns, the half
+  // kk in {2g, 2g+1} of every K-step, g = w / 4 (its group)
+  const int wm = wave & 3, grp = wave >> 2;
   const int lr = lane & 31, lg = lane >> 5;
   const int64_t N = w.n, K = w.k, nkb = K / kBlock;
   const int64_t C = DX ? N : K;       // contraction length
@@ -144,242 +156,317 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
 
   if (tid < 16) s_lv[tid] = codebook[tid];
 
-  // Decode role (all 512 threads): a quad of lanes shares one of the step's
-  // 128 blocks, lane q = tid & 3 decodes its elements [16q, 16q+16).
+  // Decode role: group g decodes blocks [64g, 64g+64) of each step's 128; a
+  // quad of lanes shares one block, lane q = tid & 3 decodes its elements
+  // [16q, 16q+16).
   const int q = tid & 3;
-  const int blk = tid >> 2;
+  const int blk = 64 * grp + ((tid & 255) >> 2);
   const int wr = DX ? (blk >> 1) : blk;                     // stage row
   const int wcb = DX ? (blk & 1) : 0;                       // block within the stage row (dx)
 
-  // per-lane source of each of the 4 DMA loads: row base and the largest
-  // step offset that keeps the 8-element piece inside the row
-  const uint16_t* a_src[4];
-  int64_t a_cmax[4];
+  // Activation tile of step st into ring stage `stage`: wave w fills rows
+  // [32w, 32w+32) with 4 DMA loads of 8 rows; lane l lands at byte 16l of its
+  // load's 1 KiB, i.e. row l/8, physical chunk l%8.  Rows past M are clamped
+  // to row M-1 (their products are discarded).  With 16-byte rows (VEC) the
+  // loads are buffer loads from a per-step base held in scalar registers and
+  // a fixed per-lane offset, so they cost no vector ALU work; a ragged last
+  // step clamps each piece into its row instead (columns past the
+  // contraction meet zero weights).  Without 16-byte rows the loads go
+  // through registers with zero fill and complete before the stores.
+  uint32_t a_vo[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rl = wave * 32 + i * 8 + (lane >> 3);
-    const int lc = a_chunk(rl, lane & 7);
-    a_src[i] = act + min(m0 + rl, M - 1) * C + lc * 8;
-    a_cmax[i] = C - 8 - lc * 8;
+    a_vo[i] = (uint32_t)(((min(m0 + rl, M - 1) - m0) * C + a_chunk(rl, lane & 7) * 8) * 2);
   }
-  // Activation tile of step st into ring stage `stage`: wave w fills rows
-  // [32w, 32w+32) with 4 DMA loads of 8 rows; lane l lands at byte 16l of its
-  // load's 1 KiB, i.e. row l/8, physical chunk l%8.  Rows past M and columns
-  // past the contraction are clamped (products discarded or against zero
-  // weights).
+  const uint16_t* a_tile = act + m0 * C;
+  // steps whose 64 columns all lie inside the contraction (the forward's
+  // contraction is a whole number of 64-blocks)
+  const int full_steps = (int)(C / GBK);
+  auto fill_a_one = [&](int64_t c0, uint16_t* base, int i, auto FULLc) {
+    uint16_t* dst = base + (wave * 32 + i * 8) * GBK;
+    const int rl = wave * 32 + i * 8 + (lane >> 3);
+    const int lc = a_chunk(rl, lane & 7);
+    if (VEC) {
+      if (decltype(FULLc)::value) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(a_tile + c0), (QL_LDS void*)dst, 16,
+                                                 a_vo[i], 0, 0, 0);
+      } else {
+        const int64_t row = min(m0 + rl, M - 1);
+        __builtin_amdgcn_global_load_lds(act + row * C + min(c0 + lc * 8, C - 8), (QL_LDS void*)dst,
+                                         16, 0, 0);
+      }
+    } else {
+      const int64_t row = min(m0 + rl, M - 1);
+      const int64_t c = c0 + lc * 8;
+      const u32x4_t v = c < C ? load_act8(act + row * C, c, C, false) : u32x4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(dst + lane * 8) = v;
+    }
+  };
   auto fill_a = [&](int st, int stage) {
-    const int64_t c0 = (int64_t)st * GBK;
-    uint16_t* base = sA + stage * A_STAGE;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint16_t* dst = base + (wave * 32 + i * 8) * GBK;
-      if (VEC) {
-        __builtin_amdgcn_global_load_lds(a_src[i] + min(c0, a_cmax[i]),
-                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-      } else {
-        const int rl = wave * 32 + i * 8 + (lane >> 3);
-        const int64_t row = min(m0 + rl, M - 1);
-        const int64_t c = c0 + a_chunk(rl, lane & 7) * 8;
-        const u32x4_t v = c < C ? load_act8(act + row * C, c, C, false) : u32x4_t{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4_t*>(dst + lane * 8) = v;
-      }
+      if (!DX || st < full_steps)
+        fill_a_one((int64_t)st * GBK, sA + stage * A_STAGE, i, std::true_type{});
+      else
+        fill_a_one((int64_t)st * GBK, sA + stage * A_STAGE, i, std::false_type{});
     }
-  };
-  // register-staged alternative: load (coalesced, same lane mapping) now,
-  // store to the ring stage later
-  auto load_a_regs = [&](int st, u32x4_t (&r)[4]) {
-    const int64_t c0 = (int64_t)st * GBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (VEC) {
-        r[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + min(c0, a_cmax[i]));
-      } else {
-        const int rl = wave * 32 + i * 8 + (lane >> 3);
-        const int64_t row = min(m0 + rl, M - 1);
-        const int64_t c = c0 + a_chunk(rl, lane & 7) * 8;
-        r[i] = c < C ? load_act8(act + row * C, c, C, false) : u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_a_regs = [&](int stage, const u32x4_t (&r)[4]) {
-    uint16_t* base = sA + stage * A_STAGE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4_t*>(base + (wave * 32 + i * 8) * GBK + lane * 8) = r[i];
   };
 
   struct WRaw {
     u32x2_t codes;    // this lane's two packed words
     uint32_t qbyte;   // the block's 8-bit scale
     float step;
-    bool ok;
   };
-  // flat index of this lane's block at step st: b0 + st * bstride; its
-  // storage position (rows in groups of 16, k-block-major inside a group):
-  // forward p0 + st * R (the row is fixed), backward recomputed per step
+  // This lane's block at step st.  Storage position (rows in groups of 16,
+  // k-block-major inside a group): forward fp0 + st * fR (fixed row; fR = 16
+  // except in a partial last group), backward st * 64 * nkb plus a fixed part
+  // whenever all 64 rows of the step are present.  Positions are taken
+  // relative to a per-step base in scalar registers; blocks outside the
+  // weight get an offset past the buffer end, so the hardware returns zeros
+  // (scale 0, hence decoded zeros).  The fp32 constant of flat block b is
+  // step[b / 256].
+  constexpr uint32_t kOut = 0x80000000u;
   const int64_t kb_dx = o0 / kBlock + wcb;
-  const int64_t b0 = DX ? (int64_t)wr * nkb + kb_dx : (o0 + wr) * nkb;
-  const int64_t bstride = DX ? GBK * nkb : 1;
-  const bool w_ok_fixed = DX ? kb_dx < nkb : (o0 + wr) < N;
   const int64_t fg0 = (o0 + wr) & ~int64_t(15);
-  const int64_t fR = min(int64_t(16), N - fg0);
-  const int64_t fp0 = fg0 * nkb + (o0 + wr - fg0);
+  const bool f_ok = (o0 + wr) < N;
+  const uint32_t fR = f_ok ? (uint32_t)min(int64_t(16), N - fg0) : 16u;
+  const uint32_t f_prel = (uint32_t)((fg0 - o0) * nkb + (o0 + wr - fg0));   // fp0 - o0 * nkb
+  const bool d_kok = kb_dx < nkb;
+  const uint32_t d_prel = (uint32_t)((wr & ~15) * nkb + kb_dx * 16 + (wr & 15));
+  const uint32_t c_vo0 = DX ? (d_kok ? d_prel * 32 + q * 8 : kOut) : (f_ok ? f_prel * 32 + q * 8 : kOut);
+  const uint32_t q_vo0 = DX ? (d_kok ? d_prel : kOut) : (f_ok ? f_prel : kOut);
+  const uint32_t b_lane = (uint32_t)(DX ? wr * nkb + kb_dx : (o0 + wr) * nkb);
+  const auto step_rsrc = buf_rsrc(w.step, (uint32_t)(((N * nkb + kGroup - 1) / kGroup) * 4));
   auto load_w = [&](int st, WRaw& r) {
-    r.ok = w_ok_fixed && (!DX || (int64_t)st * GBK + wr < N);
-    int64_t b = 0, p = 0;
+    uint32_t cvo, qvo, bidx;
+    const uint8_t *cbase, *qbase;
     if (DX) {
-      const int64_t n = (int64_t)st * GBK + wr, g0 = n & ~int64_t(15);
-      b = r.ok ? b0 + st * bstride : 0;
-      p = r.ok ? g0 * nkb + kb_dx * min(int64_t(16), N - g0) + (n - g0) : 0;
+      const int64_t n0 = (int64_t)st * GBK;
+      cbase = w.codes + n0 * nkb * 32;
+      qbase = w.qscale + n0 * nkb;
+      bidx = b_lane + (uint32_t)(n0 * nkb);
+      if (st < full_steps) {
+        cvo = c_vo0;
+        qvo = q_vo0;
+      } else {   // ragged last step: partial group and rows past N
+        const int64_t g0 = (wr & ~15), R = min(int64_t(16), N - n0 - g0);
+        const bool ok = d_kok && n0 + wr < N;
+        const uint32_t prel = (uint32_t)(g0 * nkb + kb_dx * R + (wr & 15));
+        cvo = ok ? prel * 32 + q * 8 : kOut;
+        qvo = ok ? prel : kOut;
+      }
     } else {
-      b = r.ok ? b0 + st : 0;
-      p = r.ok ? fp0 + st * fR : 0;
+      cbase = w.codes + o0 * nkb * 32;
+      qbase = w.qscale + o0 * nkb;
+      cvo = c_vo0 + (uint32_t)st * fR * 32;
+      qvo = q_vo0 + (uint32_t)st * fR;
+      bidx = b_lane + (uint32_t)st;
     }
-    r.codes = *reinterpret_cast<const u32x2_t*>(w.codes + p * 32 + q * 8);
-    r.qbyte = w.qscale[p];
-    r.step = w.step[b >> 8];
+    r.codes = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(buf_rsrc(cbase), cvo, 0, 0));
+    r.qbyte = __builtin_amdgcn_raw_buffer_load_b8(buf_rsrc(qbase), qvo, 0, 0);
+    r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(step_rsrc, (bidx >> 8) * 4, 0, 0));
   };
-  auto scale_of = [](const WRaw& r) {
-    return r.ok ? (float)r.qbyte * r.step : 0.f;
+  auto scale_of = [](const WRaw& r) { return (float)r.qbyte * r.step; };
+  auto wdst = [&](int stage) {
+    return reinterpret_cast<u32x4_t*>(sW + stage * G::stage + wr * G::ld + wcb * 64 + q * 16);
   };
+  // MFMA fragments of this wave for one step: A rows 64 wm + 32 mt, B
+  // columns 32 nt, contraction kk = 2g + h (16 wide each)
+  auto read_frags = [&](const uint16_t* sa, const uint16_t* sw, u32x4_t (&a)[2][2],
+                        u32x4_t (&b)[2][4]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kk = 2 * grp + h;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int r = wm * 64 + 32 * mt + lr;
+        a[h][mt] = *reinterpret_cast<const u32x4_t*>(sa + r * GBK + a_chunk(r, 2 * kk + lg) * 8);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        if (DX) {
+          const int G16 = lane >> 4, i16 = lane & 15;
+          const int row = 16 * kk + 8 * (G16 >> 1) + (i16 >> 2);
+          const int col = 32 * nt + 16 * (G16 & 1) + 4 * (i16 & 3);
+          const u32x2_t lo = ds_tr16(sw + row * G::ld + col);
+          const u32x2_t hi = ds_tr16(sw + (row + 4) * G::ld + col);
+          b[h][nt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          b[h][nt] = *reinterpret_cast<const u32x4_t*>(sw + (32 * nt + lr) * G::ld + 16 * kk + 8 * lg);
+        }
+      }
+    }
+  };
+
   __syncthreads();
   float lvq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) lvq[i] = s_lv[4 * q + i];
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[2][4];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
 
-  auto read_a = [&](const uint16_t* sa, int kk, u32x4_t (&a)[2]) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int r = wm * 64 + 32 * mt + lr;
-      a[mt] = *reinterpret_cast<const u32x4_t*>(sa + r * GBK + a_chunk(r, 2 * kk + lg) * 8);
-    }
-  };
-  auto read_b = [&](const uint16_t* sw, int kk, u32x4_t (&b)[2]) {
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      if (DX) {
-        const int G16 = lane >> 4, i16 = lane & 15;
-        const int row = 16 * kk + 8 * (G16 >> 1) + (i16 >> 2);
-        const int col = wn * 64 + 32 * nt + 16 * (G16 & 1) + 4 * (i16 & 3);
-        const u32x2_t lo = ds_tr16(sw + row * G::ld + col);
-        const u32x2_t hi = ds_tr16(sw + (row + 4) * G::ld + col);
-        b[nt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-      } else {
-        b[nt] = *reinterpret_cast<const u32x4_t*>(sw + (wn * 64 + 32 * nt + lr) * G::ld + 16 * kk + 8 * lg);
-      }
-    }
-  };
-  auto wdst = [&](int stage) {
-    return reinterpret_cast<u32x4_t*>(sW + stage * G::stage + wr * G::ld + wcb * 64 + q * 16);
-  };
+  // Loads issued by a wave in one memory phase: 4 activation DMA loads (with
+  // 16-byte rows) and 3 code loads.
+  constexpr int NLOAD = VEC ? 7 : 3;
 
   if (s_begin < s_end) {
     const int last = s_end - 1;
-    // prologue: activation stages of steps s_begin, s_begin+1; decoded weight
-    // stage 0 of s_begin; codes of s_begin+1 (w0) and s_begin+2 (w1)
-    WRaw w0, w1;
-    u32x4_t ra0[4], ra1[4];    // register-staged activations (QL_A_DMA == 0)
+    // prologue: decoded weight of s_begin (stage 0), activation tiles of
+    // s_begin and s_begin+1, codes of s_begin+1 and s_begin+2
+    WRaw rw[3];   // codes of step t in rw[(t - s_begin) % 3]
     {
       WRaw wf;
       load_w(s_begin, wf);
-      if (QL_A_DMA) {
-        fill_a(s_begin, 0);
-        fill_a(min(s_begin + 1, last), 1);
-      } else {
-        load_a_regs(s_begin, ra0);
-        load_a_regs(min(s_begin + 1, last), ra1);
-      }
-      load_w(min(s_begin + 1, last), w0);
-      load_w(min(s_begin + 2, last), w1);
-      QL_VMCNT(0);
-      if (!QL_A_DMA) {
-        store_a_regs(0, ra0);
-        store_a_regs(1, ra1);
-        load_a_regs(min(s_begin + 2, last), ra0);
-      }
+      fill_a(s_begin, 0);
+      fill_a(min(s_begin + 1, last), 1);
+      load_w(min(s_begin + 1, last), rw[1]);
+      load_w(min(s_begin + 2, last), rw[2]);
+      __builtin_amdgcn_s_waitcnt(0);       // (prologue only)
       const Lut t = make_lut_quad(lvq, scale_of(wf));
       u32x4_t* dst = wdst(0);
       dst[0] = decode8(t, wf.codes[0]);
       dst[1] = decode8(t, wf.codes[1]);
       __syncthreads();
     }
+    u32x4_t fa[2][2], fb[2][4];
 
-    // One K-step t: MFMAs on activation stage t%3 and weight stage (t-s)&1.
-    // First the activation tile of step t+2 is started (DMA), or, with
-    // register staging, the tile of t+2 (loaded a step ago) is stored and the
-    // tile of t+3 loaded; then all fragment reads of the step are issued; the
-    // decode of the codes of step t+1 (`wd`) into the other weight stage runs
-    // between the MFMAs; then `wd` is refilled with the codes of step t+3
-    // (consumed two steps later).  Every wave issues the same loads, so the
-    // vmcnt values below are exact.
-    auto kstep = [&](int st, WRaw& wd, u32x4_t (&ra)[4]) {
+    // Ping-pong schedule.  Every step t has a memory phase MEM(t) and a
+    // matrix phase MMA(t) per wave; group 0 runs MEM(t) while group 1 runs
+    // MMA(t-1), then group 0 runs MMA(t) while group 1 runs MEM(t), with a
+    // workgroup barrier between phases, so each SIMD (one wave of each group)
+    // alternates the matrix cores between its two waves.
+    //   MEM(t): read this wave's fragments of step t (A ring stage t%3, W
+    //   stage t&1), decode the group's half of W(t+1) into stage (t+1)&1 and
+    //   wait for its LDS traffic.
+    //   MMA(t): 16 MFMAs (2 K halves x 2 x 4 tiles) from those fragments,
+    //   with the DMA of A(t+2) and the codes of W(t+3) issued between them so
+    //   that the address and data paths stay busy under the matrix work.
+    // A(t+2) is first read by group 0 in MEM(t+2), two phases after group 1
+    // issued its rows in MMA(t): every wave waits for all its loads at the
+    // end of its next MEM phase.
+    auto mem = [&](int st, auto PHc) {
+      constexpr int PH = decltype(PHc)::value;   // (st - s_begin) % 3
       const int rel = st - s_begin;
-      const int wstage = rel & 1;
-      // `wd` was loaded at the end of step t-2; issued since: the activation
-      // loads of step t-1 (4) and the codes of t+2 (3)
-      if (VEC) QL_VMCNT(7); else QL_VMCNT(0);
-      const float sc = scale_of(wd);
-      if (QL_A_DMA) {
-        fill_a(min(st + 2, last), (rel + 2) % NA);
-      } else {
-        store_a_regs((rel + 2) % NA, ra);       // tile of t+2, loaded during step t-1
-        load_a_regs(min(st + 3, last), ra);     // tile of t+3
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      const uint16_t* sa = sA + (rel % NA) * A_STAGE;
-      const uint16_t* sw = sW + wstage * G::stage;
-      u32x4_t a[4][2], b[4][2];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        read_a(sa, kk, a[kk]);
-        read_b(sw, kk, b[kk]);
-      }
-      // forward: all fragment reads of the step are issued before the first
-      // MFMA (the scheduler would otherwise sink each read next to its use and
-      // expose the LDS latency at every MFMA pair); measured slower for the
-      // transposing reads of the backward, which keep the default order
-      if (!DX) __builtin_amdgcn_sched_barrier(0);
+      const float sc = scale_of(rw[(PH + 1) % 3]);
+      read_frags(sA + (rel % NA) * A_STAGE, sW + (rel & 1) * G::stage, fa, fb);
       const Lut t = make_lut_quad(lvq, sc);
-      u32x4_t* dst = wdst(wstage ^ 1);
+      u32x4_t* dst = wdst((rel + 1) & 1);
+      dst[0] = decode8(t, rw[(PH + 1) % 3].codes[0]);
+      dst[1] = decode8(t, rw[(PH + 1) % 3].codes[1]);
+      QL_LGKMCNT0();
+      QL_VMCNT(0);
+      __builtin_amdgcn_sched_barrier(0);
+      k_barrier_issue();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto mma = [&](int st, auto PHc) {
+      constexpr int PH = decltype(PHc)::value;
+      const int rel = st - s_begin;
+      const int sa = min(st + 2, last);
+      const int64_t c0 = (int64_t)sa * GBK;
+      uint16_t* abase = sA + ((rel + 2) % NA) * A_STAGE;
+      const bool full = !DX || sa < full_steps;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(a[kk][mt], b[kk][nt], acc[mt][nt]);
-        if (kk == 1) dst[0] = decode8(t, wd.codes[0]);
-        if (kk == 2) dst[1] = decode8(t, wd.codes[1]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // then up to six VALU
-        }
-      }
+          for (int nt = 0; nt < 4; ++nt) {
+            acc[mt][nt] = mfma32(fa[h][mt], fb[h][nt], acc[mt][nt]);
+            const int i = (h * 2 + mt) * 4 + nt;
+            if (i % 4 == 0) {
+              __builtin_amdgcn_sched_barrier(0);
+              if (full)
+                fill_a_one(c0, abase, i / 4, std::true_type{});
+              else
+                fill_a_one(c0, abase, i / 4, std::false_type{});
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            if (i == 6) {
+              load_w(min(st + 3, last), rw[PH % 3]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
       __builtin_amdgcn_sched_barrier(0);
-      load_w(min(st + 3, last), wd);
-      // the activation loads of step t+1 were issued a step ago; issued after
-      // them: codes of t+2 (3), activation loads of this step (4), codes of
-      // t+3 (3).  (Register staging: the loads of t+3 issued this step are
-      // stored next step, also waited for here.)
-      if (VEC) QL_VMCNT(10); else QL_VMCNT(0);
-      k_barrier();
+      k_barrier_issue();
+      __builtin_amdgcn_sched_barrier(0);
     };
-
+    // group 1 starts one phase late
+    if (grp == 1) k_barrier_issue();
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
     int st = s_begin;
-    for (; st + 1 < s_end; st += 2) {
-      kstep(st, w0, ra0);
-      kstep(st + 1, w1, ra0);
+    for (; st + 2 < s_end; st += 3) {
+      mem(st, P0{});
+      mma(st, P0{});
+      mem(st + 1, P1{});
+      mma(st + 1, P1{});
+      mem(st + 2, P2{});
+      mma(st + 2, P2{});
     }
-    if (st < s_end) kstep(st, w0, ra0);
+    if (st < s_end) {
+      mem(st, P0{});
+      mma(st, P0{});
+    }
+    if (st + 1 < s_end) {
+      mem(st + 1, P1{});
+      mma(st + 1, P1{});
+    }
+    // group 0 matches group 1's extra barrier
+    if (grp == 0) k_barrier_issue();
   }
+
+  // ---- the two groups hold partial sums over complementary K halves of the
+  // same 64 x 128 tiles: group 0 finishes columns [0, 64), group 1 columns
+  // [64, 128).  Each wave hands the other group's half to its partner wave
+  // (same rows) through 16 KiB of LDS: waves 0-5 in the activation ring,
+  // waves 6-7 in the weight stages.  The clamped prefetches of the last steps
+  // may still be landing in the ring, hence the full wait first.
+  QL_VMCNT(0);
+  __syncthreads();
+  f32x16_t fin[2][2];   // this wave's finished 64 x 64 output tile
+  {
+    auto region = [&](int v) {
+      return v < 6 ? reinterpret_cast<f32x4_t*>(sA) + (size_t)v * 1024
+                   : reinterpret_cast<f32x4_t*>(sW) + (size_t)(v - 6) * 1024;
+    };
+    static_assert(2 * G::stage * sizeof(uint16_t) >= 2 * 16384, "exchange needs 32 KiB of stages");
+    static_assert(NA * A_STAGE * sizeof(uint16_t) >= 6 * 16384, "exchange needs 96 KiB of ring");
+    // (the accumulators are selected, never indexed by the group, so they
+    // stay in registers)
+    f32x4_t* mine = region(wave);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const f32x16_t v = grp == 0 ? acc[mt][2 + j] : acc[mt][j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          mine[((mt * 2 + j) * 4 + e) * 64 + lane] = f32x4_t{v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]};
+        fin[mt][j] = grp == 0 ? acc[mt][j] : acc[mt][2 + j];
+      }
+    __syncthreads();
+    const f32x4_t* theirs = region(wave ^ 4);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x4_t v = theirs[((mt * 2 + j) * 4 + e) * 64 + lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) fin[mt][j][4 * e + i] += v[i];
+        }
+  }
+  const int nt0 = grp == 0 ? 0 : 2;   // this wave's output columns: nt0, nt0 + 1
 
   // ---- epilogue.  LoRA term (ksplit == 1): out += (scaling * L) R^T on the
   // matrix cores, 16 ranks per MFMA step; the fp32 factor scaling * L is
@@ -389,15 +476,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       // B fragments: R[o][j0 + 8*lg + e] (the rank index is the contraction)
       u32x4_t rb[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int64_t o = min(o0 + wn * 64 + 32 * nt + lr, O - 1);
+      for (int j = 0; j < 2; ++j) {
+        const int64_t o = min(o0 + 32 * (nt0 + j) + lr, O - 1);
         uint32_t h[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int j = j0 + 8 * lg + e;
-          h[e] = j < lora.r ? lora.R[o * lora.rs_c + (int64_t)j * lora.rs_j] : 0u;
+          const int jj = j0 + 8 * lg + e;
+          h[e] = jj < lora.r ? lora.R[o * lora.rs_c + (int64_t)jj * lora.rs_j] : 0u;
         }
-        rb[nt] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+        rb[j] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
       }
       // A fragments: s * L[m][j], split into bf16 hi + lo (exact to 2^-16)
 #pragma unroll
@@ -406,8 +493,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
         float tv[8], lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int j = j0 + 8 * lg + e;
-          tv[e] = j < lora.r ? lora.scaling * lora.L[m * lora.r + j] : 0.f;
+          const int jj = j0 + 8 * lg + e;
+          tv[e] = jj < lora.r ? lora.scaling * lora.L[m * lora.r + jj] : 0.f;
         }
         u32x4_t ahi, alo;
 #pragma unroll
@@ -418,9 +505,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
           alo[e] = pack_bf16x2(lo[2 * e], lo[2 * e + 1]);
         }
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          acc[mt][nt] = mfma32(ahi, rb[nt], acc[mt][nt]);
-          acc[mt][nt] = mfma32(alo, rb[nt], acc[mt][nt]);
+        for (int j = 0; j < 2; ++j) {
+          fin[mt][j] = mfma32(ahi, rb[j], fin[mt][j]);
+          fin[mt][j] = mfma32(alo, rb[j], fin[mt][j]);
         }
       }
     }
@@ -428,13 +515,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int64_t m = m0 + wm * 64 + 32 * mt + 8 * (i >> 2) + 4 * lg + (i & 3);
-        const int64_t o = o0 + wn * 64 + 32 * nt + lr;
+        const int64_t o = o0 + 32 * (nt0 + j) + lr;
         if (m < M && o < O) {
-          const float v = acc[mt][nt][i];
+          const float v = fin[mt][j][i];
           if (ksplit > 1)
             part[((int64_t)split * M + m) * O + o] = v;
           else if (out_bf16)

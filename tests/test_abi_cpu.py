@@ -193,5 +193,9 @@ def test_grouped_fwd_argument_errors():
 def test_nf4_bytes_rejects_oversized_weights():
     L = B.lib()
     z = ctypes.c_size_t()
-    assert L.qlora_nf4_bytes(1 << 26, 4096, ctypes.byref(z), None, None) == 2   # 2^38 elements
-    assert L.qlora_nf4_bytes((1 << 26) - 1, 4096, ctypes.byref(z), None, None) == 0
+    assert L.qlora_nf4_bytes(1 << 21, 1 << 17, ctypes.byref(z), None, None) == 2   # 2^38 elements
+    assert L.qlora_nf4_bytes((1 << 21) - 1, 1 << 17, ctypes.byref(z), None, None) == 0
+    assert L.qlora_nf4_bytes(1 << 22, 64, ctypes.byref(z), None, None) == 2        # n = 2^22
+    assert L.qlora_nf4_bytes((1 << 22) - 1, 64, ctypes.byref(z), None, None) == 0
+    assert L.qlora_nf4_bytes(1, 1 << 22, ctypes.byref(z), None, None) == 2         # k = 2^22
+    assert L.qlora_nf4_bytes(1, (1 << 22) - 64, ctypes.byref(z), None, None) == 0

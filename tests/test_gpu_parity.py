@@ -158,10 +158,12 @@ def test_fused_dequant_identity_fwd(path):
         assert np.array_equal(Y.cpu().numpy(), wd[:, r0:r0 + m].T), (path, r0)
 
 
-def test_fused_dequant_identity_dx():
-    """dY = identity rows: dX = deq(W) exactly (transposed decode path)."""
+@pytest.mark.parametrize("n,k", [(300, 384), (200, 384)])
+def test_fused_dequant_identity_dx(n, k):
+    """dY = identity rows: dX = deq(W) exactly (transposed decode path).  n = 300
+    takes the unaligned-row path; n = 200 the 16-byte-row path with a ragged
+    last step and a partial 16-row group."""
     B = _dev()
-    n, k = 300, 384
     w = synth.normal_bf16((n, k), 0.02, 92)
     q = B.qlora_quantize(_t(w), _cb(B))
     wd = onf4.bf16_to_f32(_oracle_wd(w))
