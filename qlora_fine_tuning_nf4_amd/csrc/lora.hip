@@ -15,17 +15,18 @@ QL_DEV u32x4_t load8_guard(const uint16_t* row, int64_t c, int64_t C, bool vec) 
   return u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
 }
 
-// out[m][j] = sum_c P[m][c] Q[j][c]: a 16 x 16 output tile per workgroup of
-// 16 waves; wave w takes the 32-wide contraction slices w, w+16, ... and keeps
-// four independent accumulators (four loads in flight); the 16 partial tiles
-// are summed in a fixed order through LDS.  bf16 products are exact, sums
-// fp32.
+// out[m][j] = sum_c P[m][c] Q[j][c]: an output tile of `rows` (16, or 8 so
+// that a few thousand rows still spread over every compute unit) x 16 ranks
+// per workgroup of 16 waves; wave w takes the 32-wide contraction slices w,
+// w+16, ... and keeps four independent accumulators (four loads in flight);
+// the 16 partial tiles are summed in a fixed order through LDS.  bf16
+// products are exact, sums fp32.
 constexpr int RD_WAVES = 16;
 template <bool GROUPED>
 __global__ __launch_bounds__(1024) void k_rowdot(const uint16_t* __restrict__ P,
                                                  const uint16_t* __restrict__ Q, int64_t M,
                                                  int64_t C, int r, float* __restrict__ out,
-                                                 const RowdotJob* __restrict__ jobs) {
+                                                 const RowdotJob* __restrict__ jobs, int rows) {
   if constexpr (GROUPED) {
     const RowdotJob& J = jobs[blockIdx.z];
     P = J.P;
@@ -37,11 +38,11 @@ __global__ __launch_bounds__(1024) void k_rowdot(const uint16_t* __restrict__ P,
   }
   __shared__ f32x4_t s_red[RD_WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t m = (int64_t)blockIdx.x * 16 + (lane & 15);
+  const int64_t m = (int64_t)blockIdx.x * rows + (lane & 15);
   const int64_t j = (int64_t)blockIdx.y * 16 + (lane & 15);
   const int g = lane >> 4;
   const bool vec = (C % 8) == 0;
-  const bool mok = m < M, jok = j < r;
+  const bool mok = (lane & 15) < rows && m < M, jok = j < r;
   f32x4_t acc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -64,17 +65,17 @@ __global__ __launch_bounds__(1024) void k_rowdot(const uint16_t* __restrict__ P,
   for (int w = 1; w < RD_WAVES; ++w) v += s_red[w][lane];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int64_t mm = (int64_t)blockIdx.x * 16 + g * 4 + e;
-    if (mm < M && jok) out[mm * r + j] = v[e];
+    const int64_t mm = (int64_t)blockIdx.x * rows + g * 4 + e;
+    if (g * 4 + e < rows && mm < M && jok) out[mm * r + j] = v[e];
   }
 }
 
-__global__ void k_transpose_bf16(const uint16_t* __restrict__ Q, int64_t N, int r,
+// Qt[j][n] = Q[n][j]; thread (j, n) with n fastest, so the writes coalesce
+// (N * r < 2^31).
+__global__ void k_transpose_bf16(const uint16_t* __restrict__ Q, int N, int r,
                                  uint16_t* __restrict__ Qt) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= N * r) return;
-  const int64_t n = idx / r, j = idx % r;
-  Qt[j * N + n] = Q[idx];
+  const int n = (int)blockIdx.x * 256 + (int)threadIdx.x, j = (int)blockIdx.y;
+  if (n < N) Qt[(int64_t)j * N + n] = Q[(int64_t)n * r + j];
 }
 
 // Partial weight gradient over a slice of WG_ROWS rows m:
@@ -176,8 +177,18 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ 
                                                       float* __restrict__ out, int transpose_out) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // = j * C + c
   if (idx >= (int64_t)r * C) return;
+  // partials added in split order; eight loads in flight at a time
+  const int64_t stride = (int64_t)r * C;
   float v = 0.f;
-  for (int s = 0; s < msplit; ++s) v += part[(int64_t)s * r * C + idx];
+  int s = 0;
+  for (; s + 8 <= msplit; s += 8) {
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = part[(int64_t)(s + u) * stride + idx];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v += t[u];
+  }
+  for (; s < msplit; ++s) v += part[(int64_t)s * stride + idx];
   const int64_t j = idx / C, c = idx % C;
   if (transpose_out)
     out[c * r + j] = scaling * v;
@@ -187,9 +198,11 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ 
 
 hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
                          float* out, hipStream_t s) {
-  dim3 grid((unsigned)((M + 15) / 16), (unsigned)((r + 15) / 16));
+  // 8-row tiles when 16-row tiles would leave compute units idle
+  const int rows = ((M + 15) / 16) * ((r + 15) / 16) < 512 ? 8 : 16;
+  dim3 grid((unsigned)((M + rows - 1) / rows), (unsigned)((r + 15) / 16));
   hipLaunchKernelGGL(k_rowdot<false>, grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out,
-                     nullptr);
+                     nullptr, rows);
   return hipGetLastError();
 }
 
@@ -197,14 +210,13 @@ hipError_t launch_rowdot_grouped(const RowdotJob* jobs, int njobs, int64_t M, in
                                  hipStream_t s) {
   dim3 grid((unsigned)((M + 15) / 16), (unsigned)((max_r + 15) / 16), (unsigned)njobs);
   hipLaunchKernelGGL(k_rowdot<true>, grid, dim3(64 * RD_WAVES), 0, s, nullptr, nullptr, M,
-                     int64_t(0), 0, nullptr, jobs);
+                     int64_t(0), 0, nullptr, jobs, 16);
   return hipGetLastError();
 }
 
 hipError_t launch_transpose_bf16(const uint16_t* Q, int64_t N, int r, uint16_t* Qt, hipStream_t s) {
-  const int64_t total = N * r;
-  hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, Q, N,
-                     r, Qt);
+  hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)((N + 255) / 256), (unsigned)r), dim3(256), 0,
+                     s, Q, (int)N, r, Qt);
   return hipGetLastError();
 }
 
