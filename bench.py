@@ -26,6 +26,7 @@ Other workloads (--workload), each printing its own line of the same form:
 from __future__ import annotations
 
 import argparse
+import statistics
 import hashlib
 import json
 import os
@@ -188,16 +189,17 @@ def run_layer7b(args):
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
+    # one event per step boundary: per-step GPU times for the median and spread
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    g0.record(stream)
-    for _ in range(args.steps):
+    bounds[0].record(stream)
+    for i in range(args.steps):
         step(True)
-    g1.record(stream)
+        bounds[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = g0.elapsed_time(g1)
+    gpu_ms = bounds[0].elapsed_time(bounds[-1])
+    step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]
     ms_per_step = wall * 1e3 / args.steps
 
     total_flops = sum(flops_fwd(M, L["N"], L["K"], L["r"]) + flops_bwd(M, L["N"], L["K"], L["r"])
@@ -230,6 +232,7 @@ def run_layer7b(args):
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4),
+        "gpu_step_ms": _spread(step_ms),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.02) weights quantized to NF4+DQ, N(0,1) activations)",
         "config": {"workload": WORKLOAD, "M": M, "r": RANK, "alpha": ALPHA,
@@ -250,22 +253,31 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
+def _spread(ms):
+    """Median and spread of per-step GPU times (ms)."""
+    v = sorted(ms)
+    return {"median": round(statistics.median(v), 4), "min": round(v[0], 4), "max": round(v[-1], 4),
+            "n": len(v)}
+
+
 def _timed(fn, steps, warmup):
     """Run fn warmup times, then time `steps` runs with HIP events on the
-    current stream: (wall seconds per run, GPU seconds per run)."""
+    current stream (one event per run boundary): (wall seconds per run, GPU
+    seconds per run, per-run GPU milliseconds)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    e0, e1 = _events()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         fn()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    return wall, e0.elapsed_time(e1) * 1e-3 / steps
+    return wall, ev[0].elapsed_time(ev[-1]) * 1e-3 / steps, [ev[i].elapsed_time(ev[i + 1])
+                                                             for i in range(steps)]
 
 
 def _traffic(kernel, srcs):
@@ -314,13 +326,14 @@ def run_decode(args):
             jobs0.append(dict(w=q, X=X, Y=Y))
         g = QB.qlora_group_init(jobs, M, y_dtype=torch.bfloat16)
         g0 = QB.qlora_group_init(jobs0, M, y_dtype=torch.bfloat16)
-        wall, gpu = _timed(lambda: QB.qlora_linear_fwd_grouped(g, cb), args.steps, args.warmup)
+        wall, gpu, sweeps = _timed(lambda: QB.qlora_linear_fwd_grouped(g, cb), args.steps, args.warmup)
         # the streaming kernel alone: the same sweep without LoRA is one launch
-        wall0, gpu0 = _timed(lambda: QB.qlora_linear_fwd_grouped(g0, cb), args.steps, args.warmup)
+        wall0, gpu0, _ = _timed(lambda: QB.qlora_linear_fwd_grouped(g0, cb), args.steps, args.warmup)
         per_m[str(M)] = {"ms_per_sweep": round(wall * 1e3, 4), "GBps": round(nbytes / wall / 1e9, 1),
                          "frac_of_hbm_peak": round(nbytes / wall / 1e9 / PEAK_HBM_GBS, 4),
                          "kernel_us": round(gpu0 * 1e6, 1),
-                         "kernel_GBps": round(nbytes0 / gpu0 / 1e9, 1)}
+                         "kernel_GBps": round(nbytes0 / gpu0 / 1e9, 1),
+                         "gpu_sweep_ms": _spread(sweeps)}
         if M == 1:
             kern = (nbytes0, gpu0, wall, nbytes)
         del g, g0, jobs, jobs0
@@ -406,16 +419,17 @@ def run_quantize70b(args):
     def step():
         for W, o in zip(Ws, outs):
             QB.qlora_quantize(W, cb, out=o)
-    wall, gpu = _timed(step, args.steps, args.warmup)
+    wall, gpu, steps_ms = _timed(step, args.steps, args.warmup)
     # largest projection alone (one launch) for the kernel roofline
     big = 4
     kb = 2 * PROJ70[big][1] * PROJ70[big][2] + packed_bytes(PROJ70[big][1], PROJ70[big][2])
-    _, gk = _timed(lambda: QB.qlora_quantize(Ws[big], cb, out=outs[big]), args.steps, args.warmup)
+    _, gk, _ = _timed(lambda: QB.qlora_quantize(Ws[big], cb, out=outs[big]), args.steps, args.warmup)
     ach = kb / gk / 1e9
     out = {
         "metric": "NF4 + double-quant quantization GB/s (% HBM roofline) on 1 MI355X",
         "value": round(nbytes / wall / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "gpu_step_ms": _spread(steps_ms),
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16->u8",
         "data": "synthetic (seeded N(0,0.015) bf16 weights, 0.1% outliers x20)",
         "config": {"workload": "quantize a 70B-style layer: q,k,v,o 8192x8192; gate,up 28672x8192; "
@@ -481,13 +495,14 @@ def run_layer70b(args):
                                 workspace=L["ws"])
             QB.qlora_linear_bwd(L["q"], cb, L["X"], L["dY"], L["A"], L["B"], s, T=L["T"],
                                 dX_out=L["dX"], dA_out=L["dA"], dB_out=L["dB"], workspace=L["ws"])
-    wall, gpu = _timed(step, args.steps, args.warmup)
+    wall, gpu, steps_ms = _timed(step, args.steps, args.warmup)
     flops = sum(flops_fwd(M, L["N"], L["K"], r) + flops_bwd(M, L["N"], L["K"], r) for L in layers)
     tf = flops / wall / 1e12
     out = {
         "metric": METRIC, "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4),
-        "gpu_event_ms_per_step": round(gpu * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "gpu_event_ms_per_step": round(gpu * 1e3, 4), "gpu_step_ms": _spread(steps_ms),
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.015) weights with 0.1% outliers x20, NF4+DQ; N(0,1) activations)",
         "config": {"workload": "70B-style layer linears (q,k,v,o 8192x8192; gate,up 28672x8192; down "
