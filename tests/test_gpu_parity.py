@@ -322,6 +322,85 @@ def test_full_size_layer_sampled(N, K):
     assert _rel(dB.cpu().numpy()[ns], dBo) <= REL_TOL
 
 
+def test_full_size_70b_projection_sampled():
+    """70B-style gate projection 28672 x 8192 (0.1 % outliers x 20) at M = 4096
+    tokens with LoRA r = 16, s = 2: the launch configuration of the 70B layer
+    workload.  Inputs drawn on the device; full GPU fwd + bwd, oracle on
+    sampled rows and columns (dA in full)."""
+    B = _dev()
+    N, K, M, r, s = 28672, 8192, 4096, 16, 2.0
+    _say("full 70b", M, N, K, r)
+    W = synth.device_normal_bf16((N, K), 0.015, 4101, outlier_rate=0.001, outlier_scale=20)
+    X = synth.device_normal_bf16((M, K), 1.0, 4102)
+    dY = synth.device_normal_bf16((M, N), 1.0, 4103)
+    A = synth.device_normal_bf16((r, K), 0.01, 4104)
+    Bm = synth.device_normal_bf16((N, r), 0.01, 4105)
+    q = B.qlora_quantize(W, _cb(B))
+    Y, T = B.qlora_linear_fwd(q, _cb(B), X, A, Bm, s)
+    dX, dA, dB = B.qlora_linear_bwd(q, _cb(B), X, dY, A, Bm, s, T=T)
+    torch.cuda.synchronize()
+    g = synth.rng(4106)
+    ms = np.sort(g.choice(M, 16, replace=False))
+    ns = np.sort(np.concatenate([[0, N - 1], g.choice(np.arange(1, N - 1), 30, replace=False)]))
+    Wb, Xb, dYb, Ab, Bb = _bits(W), _bits(X), _bits(dY), _bits(A), _bits(Bm)
+    del W
+    Wd = _oracle_wd(Wb)
+    Yo, _ = olin.forward(Wd[ns], Xb[ms], Ab, Bb[ns], s)
+    assert _rel(Y.cpu().numpy()[np.ix_(ms, ns)], Yo) <= REL_TOL
+    dXo = olin.backward(Wd, Xb[ms], dYb[ms], Ab, Bb, s)[0]
+    assert _rel(dX.cpu().numpy()[ms], dXo) <= REL_TOL
+    del Wd
+    xf, dyf = onf4.bf16_to_f32(Xb).astype(np.float64), onf4.bf16_to_f32(dYb).astype(np.float64)
+    af, bf = onf4.bf16_to_f32(Ab).astype(np.float64), onf4.bf16_to_f32(Bb).astype(np.float64)
+    dAo = s * (dyf @ bf).T @ xf
+    dBo = s * dyf[:, ns].T @ (xf @ af.T)
+    assert _rel(dA.cpu().numpy(), dAo) <= REL_TOL
+    assert _rel(dB.cpu().numpy()[ns], dBo) <= REL_TOL
+
+
+@pytest.mark.parametrize("N,K", [(64, (1 << 22) - 64), ((1 << 22) - 1, 64)])
+def test_largest_dimensions(N, K):
+    """n or k at its largest accepted value (just under 2^22): quantize
+    bit-exact, GEMM forward and backward against the oracle on sampled
+    outputs.  The kernels' 32-bit per-tile offsets reach their extremes;
+    n = 2^22 - 1 also ends in a partial 16-row group and gives dY rows that are
+    not 16-byte aligned; r = 4 takes the unaligned LoRA loads."""
+    B = _dev()
+    M, r, s = 40, 4, 2.0
+    _say("largest", M, N, K, r)
+    W = synth.device_normal_bf16((N, K), 0.02, 4201)
+    X = synth.device_normal_bf16((M, K), 1.0, 4202)
+    dY = synth.device_normal_bf16((M, N), 1.0, 4203)
+    A = synth.device_normal_bf16((r, K), 0.01, 4204)
+    Bm = synth.device_normal_bf16((N, r), 0.01, 4205)
+    q = B.qlora_quantize(W, _cb(B))
+    Y, T = B.qlora_linear_fwd(q, _cb(B), X, A, Bm, s, path="gemm")
+    dX, dA, dB = B.qlora_linear_bwd(q, _cb(B), X, dY, A, Bm, s, T=T)
+    torch.cuda.synchronize()
+    Wb, Xb, dYb, Ab, Bb = _bits(W), _bits(X), _bits(dY), _bits(A), _bits(Bm)
+    del W
+    c, qs, st = _oracle_q(Wb)
+    cs, qss = onf4.to_storage(c, qs, N, K)
+    assert np.array_equal(q.codes.cpu().numpy(), cs)
+    assert np.array_equal(q.qscale.cpu().numpy(), qss)
+    assert np.array_equal(q.step.cpu().numpy().view(np.uint32), st.view(np.uint32))
+    del cs, qss
+    Wd = onf4.dequantize(c, qs, st, _LV).reshape(N, K)
+    g = synth.rng(4206)
+    ns = np.sort(np.concatenate([[0, N - 1], g.choice(np.arange(1, N - 1), min(N - 2, 62), replace=False)]))
+    ks = np.sort(np.concatenate([[0, K - 1], g.choice(np.arange(1, K - 1), min(K - 2, 62), replace=False)]))
+    Yo, _ = olin.forward(Wd[ns], Xb, Ab, Bb[ns], s)
+    assert _rel(Y.cpu().numpy()[:, ns], Yo) <= REL_TOL
+    dXo = olin.backward(Wd[:, ks], Xb[:, ks], dYb, Ab[:, ks], Bb, s)[0]
+    assert _rel(dX.cpu().numpy()[:, ks], dXo) <= REL_TOL
+    xf, dyf = onf4.bf16_to_f32(Xb).astype(np.float64), onf4.bf16_to_f32(dYb).astype(np.float64)
+    af, bf = onf4.bf16_to_f32(Ab).astype(np.float64), onf4.bf16_to_f32(Bb).astype(np.float64)
+    dAo = s * (dyf @ bf).T @ xf[:, ks]
+    dBo = s * dyf[:, ns].T @ (xf @ af.T)
+    assert _rel(dA.cpu().numpy()[:, ks], dAo) <= REL_TOL
+    assert _rel(dB.cpu().numpy()[ns], dBo) <= REL_TOL
+
+
 # --------------------------------------------------------------------------- robustness
 def test_deterministic_and_nan_poisoned_outputs():
     B = _dev()
