@@ -114,9 +114,8 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
   const bool nok = n < N;
   // rows past N read (and discard) the last row; its group gives the layout
   const int64_t nn = min(n, N - 1);
-  const int64_t gg = nn & ~int64_t(15);
-  const int64_t R = min(int64_t(16), N - gg);
-  const int64_t p0 = gg * nkb + (nn - gg);
+  const int64_t gg = min(g0, (N - 1) & ~int64_t(15));      // = nn & ~15, uniform
+  const int64_t R = min(int64_t(16), N - gg);              // rows of the group
   const int g = lane >> 4;
   const int split = blockIdx.y;
   const int q0 = split * quads_per_split;
@@ -133,31 +132,46 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
   // Every wave issues XPW DMA instructions per chunk (a compile-time count,
   // so the waits below are exact): instruction j = wave + 4t covers chunk
   // rows 2j, 2j+1; rows past M re-read row M-1 (their products are dropped).
+  // All loads are buffer loads from a per-quad base in scalar registers with
+  // a fixed per-lane offset.  A ragged last quad (k % 256 != 0) reads, past
+  // the row end, the next row or zeros past the end of the buffer; those
+  // values meet blocks whose scale is forced to zero.
+  // XPW <= 4; a fixed-size array (one sized by the template parameter, used as
+  // a buffer-load offset, made the host pass drop the kernel stubs)
+  uint32_t x_vo[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int t = 0; t < XPW; ++t) {
+    const int j = wave + 4 * t;
+    const int row = 2 * j + (lane >> 5);
+    const int col = (lane & 31) ^ (row & 15);
+    x_vo[t] = (uint32_t)((min((int64_t)row, M - 1) * K + 8 * col) * 2);
+  }
+  const uint32_t x_bytes = (uint32_t)(M * K * 2);
   auto load_x = [&](int q, int stage) {
-    const int kq = min(q, nquads - 1) * 256;                // first k of the quad
+    const uint32_t off = (uint32_t)min(q, nquads - 1) * 512u;   // first k of the quad, bytes
+    const auto rs = buf_rsrc(reinterpret_cast<const uint8_t*>(J.X) + off, x_bytes - off);
 #pragma unroll
     for (int t = 0; t < XPW; ++t) {
       const int j = wave + 4 * t;
-      const int row = 2 * j + (lane >> 5);
-      const int col = (lane & 31) ^ (row & 15);
-      const int64_t m = min((int64_t)row, M - 1);
-      // k past the row end (last quad of a ragged k) reads the clamped
-      // column; those products meet zero weights
-      const int64_t kk = min((int64_t)(kq + 8 * col), K - 8);
-      __builtin_amdgcn_global_load_lds(gptr(J.X + m * K + kk),
-                                       (__attribute__((address_space(3))) void*)(stage_ptr(stage) + j * 512),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (QL_LDS void*)(stage_ptr(stage) + j * 512), 16,
+                                               x_vo[t], 0, 0, 0);
     }
   };
+  // block (nn, 4q + g) sits at storage position gg * nkb + 4q * R + (g * R + nn - gg)
+  const uint32_t w_lane = (uint32_t)(g * R + (nn - gg));
+  const uint32_t b_lane = (uint32_t)(nn * nkb + g);          // flat block index at q = 0
+  const int64_t nblk = N * nkb;
+  const auto step_rsrc = buf_rsrc(w.step, (uint32_t)(((nblk + kGroup - 1) / kGroup) * 4));
   auto load_w = [&](int q, GemvRaw<MT>& u) {
-    const int kbc = min(4 * min(q, nquads - 1) + g, nkb - 1);
-    const int64_t b = nn * nkb + kbc;
-    const int64_t p = p0 + kbc * R;
-    const QL_GLOBAL u32x4_t* src = gptr(reinterpret_cast<const u32x4_t*>(w.codes + p * 32));
-    u.c0 = src[0];
-    u.c1 = src[1];
-    u.qbyte = gptr(w.qscale)[p];
-    u.step = gptr(w.step)[b >> 8];
+    const int qc = min(q, nquads - 1);
+    const int64_t ub = gg * nkb + (int64_t)4 * qc * R;
+    const auto rc = buf_rsrc(w.codes + ub * 32, (uint32_t)((nblk - ub) * 32));
+    const auto rq = buf_rsrc(w.qscale + ub, (uint32_t)(nblk - ub));
+    u.c0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, w_lane * 32, 0, 0));
+    u.c1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, w_lane * 32 + 16, 0, 0));
+    u.qbyte = __builtin_amdgcn_raw_buffer_load_b8(rq, w_lane, 0, 0);
+    u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           step_rsrc, ((b_lane + 4 * (uint32_t)qc) >> 8) * 4, 0, 0));
   };
 
   f32x4_t acc[MT][2];
