@@ -35,6 +35,13 @@ What is computed, in the pages' order
    fp32 second-level constants stay indexed by the flat block.  ``quantize``
    returns the flat (logical) order; ``to_storage`` / ``from_storage`` convert.
 
+Without double quantization [rkmt §1.2, §2.3: one fp32 scale per 64-block,
+0.5 bit per parameter; zky "double quantization" names the saving]: steps 1-3
+only; the block keeps its fp32 absmax as the scale (``quantize_nodq``), and
+``w = bf16_rne(fp32(level[code] * absmax_b))`` (``dequantize_nodq``).  The
+absmax array uses the same storage order as the 8-bit scales
+(``blocks_to_storage``).
+
 The codebook [zky "NF4": levels placed by the normal distribution so that each
 level receives about the same share of weights; kwkr §2.1: zero must be exactly
 representable].  Reading: 8 positive levels Phi^-1(p_j) for p_j equally spaced
@@ -174,9 +181,9 @@ def block_absmax(w_bits: np.ndarray) -> np.ndarray:
     return np.max(np.abs(x), axis=1).astype(np.float32)
 
 
-def quantize(w_bits: np.ndarray, mids: np.ndarray):
-    """bf16 weight bits (any shape, numel % 64 == 0) ->
-    (codes uint8[numel/2], qscale uint8[numel/64], step float32[ngroups])."""
+def quantize_nodq(w_bits: np.ndarray, mids: np.ndarray):
+    """Steps 1-3 only: bf16 weight bits (numel % 64 == 0) ->
+    (codes uint8[numel/2], absmax float32[numel/64]), flat order."""
     flat = np.asarray(w_bits, dtype=np.uint16).reshape(-1)
     if flat.size % BLOCK:
         raise ValueError("numel must be a multiple of 64")
@@ -191,7 +198,30 @@ def quantize(w_bits: np.ndarray, mids: np.ndarray):
     v = np.where((absmax == 0)[:, None], np.float32(0), v).astype(np.float32)
     code = encode(v, mids)
     # step 3: pack two codes per byte
-    codes = pack(code.reshape(-1))
+    return pack(code.reshape(-1)), absmax
+
+
+def dequantize_nodq(codes, absmax, levels) -> np.ndarray:
+    """-> bf16 bits (flat): bf16_rne(fp32(level[code] * absmax_b))."""
+    code = unpack(codes)
+    s_el = np.repeat(np.asarray(absmax, dtype=np.float32), BLOCK)
+    prod = (np.asarray(levels, dtype=np.float32)[code] * s_el).astype(np.float32)
+    return f32_to_bf16_rne(prod)
+
+
+def blocks_to_storage(per_block: np.ndarray, n: int, k: int) -> np.ndarray:
+    """Flat-order per-block array (any dtype) -> storage order (step 6)."""
+    pos = storage_positions(n, k)
+    a = np.asarray(per_block)
+    out = np.empty_like(a)
+    out[pos] = a
+    return out
+
+
+def quantize(w_bits: np.ndarray, mids: np.ndarray):
+    """bf16 weight bits (any shape, numel % 64 == 0) ->
+    (codes uint8[numel/2], qscale uint8[numel/64], step float32[ngroups])."""
+    codes, absmax = quantize_nodq(w_bits, mids)
     # step 4: second level over groups of 256 block scales
     nblocks = absmax.size
     ngroups = -(-nblocks // GROUP)
@@ -230,7 +260,8 @@ def dequantize_f32(codes, qscale, step, levels) -> np.ndarray:
     return bf16_to_f32(dequantize(codes, qscale, step, levels))
 
 
-def dequant_error_bound(w_bits: np.ndarray, levels: np.ndarray) -> np.ndarray:
+def dequant_error_bound(w_bits: np.ndarray, levels: np.ndarray,
+                        double_quant: bool = True) -> np.ndarray:
     """Per-element bound on |w - deq(q(w))| (float64), derived from the steps,
     independent of how ``quantize`` is written:
 
@@ -258,6 +289,8 @@ def dequant_error_bound(w_bits: np.ndarray, levels: np.ndarray) -> np.ndarray:
     gap = lv[idx + 1] - lv[idx]
     enc = absmax[:, None] * (0.5 * gap + 2.0 ** -23)
     dq = (0.5 * step + 2.0 ** -15 * step + 2.0 ** -22 * absmax)[:, None]
+    if not double_quant:   # the block keeps its exact absmax
+        dq = np.zeros_like(dq)
     wmax = np.abs(x) + enc + dq
     _, e = np.frexp(np.maximum(wmax, np.finfo(np.float64).tiny))
     half_ulp_bf16 = np.ldexp(1.0, e - 9)

@@ -253,6 +253,65 @@ def test_dequant_error_within_derived_bound(sigma, outliers):
     assert np.all(bound <= 0.16 * am + 0.6 * step_el + 1e-30)
 
 
+# ------------------------------------------ without double quantization (rkmt §1.2, §2.3)
+def test_nodq_special_blocks_and_hand_values():
+    """fp32 absmax kept per block: the extremes dequantize to +-absmax exactly,
+    zero blocks to zeros, and level 0 to exact zeros."""
+    lv, mid = nf4.codebook()
+    w = np.zeros((3, 64), dtype=np.uint16)
+    w[1] = _bits([0.25] * 64)
+    row = np.linspace(-3.0, 1.0, 64).astype(np.float32)
+    w[2] = _bits(row)
+    codes, am = nf4.quantize_nodq(w, mid)
+    assert am.dtype == np.float32 and am.tolist() == [0.0, 0.25, 3.0]
+    c = nf4.unpack(codes).reshape(3, 64)
+    assert np.all(c[0] == 7) and np.all(c[1] == 15) and c[2][0] == 0
+    d = nf4.bf16_to_f32(nf4.dequantize_nodq(codes, am, lv)).reshape(3, 64)
+    assert np.all(d[0] == 0.0) and np.all(d[1] == 0.25) and d[2][0] == -3.0
+    # hand case: absmax 0.75 (exact in bf16): levels +-1 -> +-0.75, level 0 -> 0
+    hand = nf4.pack(np.array([15, 0, 7, 15, 0, 7, 15, 0] * 8, dtype=np.uint8))
+    dh = nf4.bf16_to_f32(nf4.dequantize_nodq(hand, np.array([0.75], np.float32), lv))
+    assert list(dh[:8]) == [0.75, -0.75, 0.0, 0.75, -0.75, 0.0, 0.75, -0.75]
+
+
+def test_nodq_absmax_by_python_loops_and_codes_match_double_quant():
+    """absmax is the block maximum of |w| (python loops over a small weight);
+    the first level does not depend on the second, so the codes equal those
+    of the double-quantized format."""
+    _, mid = nf4.codebook()
+    w = synth.normal_bf16((7, 192), 0.02, seed=31, outlier_rate=0.02, outlier_scale=20)
+    codes, am = nf4.quantize_nodq(w, mid)
+    x = nf4.bf16_to_f32(w.reshape(-1))
+    for b in range(am.size):
+        assert am[b] == max(abs(float(v)) for v in x[64 * b:64 * b + 64])
+    codes_dq, _, _ = nf4.quantize(w, mid)
+    assert np.array_equal(codes, codes_dq)
+
+
+@pytest.mark.parametrize("sigma,outliers", [(0.02, 0.0), (1.0, 0.05)])
+def test_nodq_error_within_derived_bound(sigma, outliers):
+    lv, mid = nf4.codebook()
+    w = synth.normal_bf16((128, 1024), sigma, seed=23, outlier_rate=outliers, outlier_scale=20)
+    codes, am = nf4.quantize_nodq(w, mid)
+    d = nf4.bf16_to_f32(nf4.dequantize_nodq(codes, am, lv)).astype(np.float64)
+    x = nf4.bf16_to_f32(w.reshape(-1)).astype(np.float64)
+    bound = nf4.dequant_error_bound(w, lv, double_quant=False)
+    assert np.all(np.abs(d - x) <= bound)
+    amb = np.repeat(am.astype(np.float64), 64)
+    assert np.all(bound <= 0.16 * amb + 1e-30)
+
+
+def test_blocks_to_storage_uses_the_scale_positions():
+    g = np.random.default_rng(4)
+    n, k = 37, 192
+    qs = g.integers(0, 256, n * k // 64, dtype=np.uint8)
+    am = g.random(n * k // 64).astype(np.float32)
+    _, qst = nf4.to_storage(np.zeros(n * k // 2, np.uint8), qs, n, k)
+    assert np.array_equal(nf4.blocks_to_storage(qs, n, k), qst)
+    pos = nf4.storage_positions(n, k)
+    assert np.array_equal(nf4.blocks_to_storage(am, n, k)[pos], am)
+
+
 # ---------------------------------------------------------------- linear algebra
 def _tiny(seed, M=3, N=5, K=64, r=2):
     X = synth.normal_bf16((M, K), 1.0, seed)
