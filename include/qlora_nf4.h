@@ -92,6 +92,13 @@ enum {
  * read a group's codes as one coalesced run.
  * Dequantized weight: w = bf16_rne(level[code] * fp32(qscale_b * step_g)).
  * (news.rkmt.cn/news/4821 §1.3, §2.2, §2.3; zky001 section 5.8 "double quantization")
+ *
+ * Single-level format (no double quantization; news.rkmt.cn/news/4821 §1.2,
+ * §2.3: one fp32 scale per 64-block, 0.5 bit per weight): qscale = NULL and
+ * step holds n*k/64 floats, the fp32 absmax of each block at the block's
+ * storage position (the order above); w = bf16_rne(level[code] * absmax_b).
+ * Every entry point accepts either format; a grouped forward needs one format
+ * for all its jobs.
  */
 typedef struct {
   int64_t n;       /* out_features */
@@ -121,6 +128,13 @@ int qlora_nf4_codebook(float *out);
 int qlora_nf4_bytes(int64_t n, int64_t k, size_t *codes, size_t *qscale, size_t *step);
 
 /*
+ * Host.  Byte sizes of the two arrays of an n x k weight in the single-level
+ * format: codes n*k/2, absmax (passed as `step`) 4*n*k/64.  Errors as
+ * qlora_nf4_bytes.
+ */
+int qlora_nf4_single_bytes(int64_t n, int64_t k, size_t *codes, size_t *absmax);
+
+/*
  * Host.  Workspace bytes needed by qlora_linear_fwd (op = 0) or
  * qlora_linear_bwd (op = 1) for these sizes, for any path.  0 on bad input.
  */
@@ -134,6 +148,9 @@ size_t qlora_workspace_bytes(int op, int64_t m, int64_t n, int64_t k, int r);
  * step_g = fp32(c2 / 255) with c2 the largest absmax of the group and
  * qscale_b = min(255, rint_even(fp32(absmax_b / step_g))), 0 when step_g is 0
  * (news.rkmt.cn/news/4821 §1.2, §2.1, §2.2; zky001 section 5.8).
+ * With out->qscale == NULL the second level is skipped: the single-level
+ * format, the fp32 absmax of each block written to out->step (sized by
+ * qlora_nf4_single_bytes).
  * `codebook` is the device copy of qlora_nf4_codebook().
  */
 int qlora_quantize(const uint16_t *W, const float *codebook, const qlora_nf4 *out, void *stream);
@@ -205,7 +222,7 @@ typedef struct {
 /* Plain-data handle filled by qlora_group_init; `table` is the caller's device buffer. */
 typedef struct {
   void *table;
-  int count, lora_count, max_r, y_dtype;
+  int count, lora_count, max_r, y_dtype, dq;
   int64_t m, row_groups, max_quads;
 } qlora_group;
 
@@ -214,7 +231,8 @@ size_t qlora_group_table_bytes(int count);
 
 /*
  * Host, setup time.  Validates every job (QLORA_ERR_* as qlora_linear_fwd,
- * QLORA_ERR_ARG if m > QLORA_GEMV_MAX_M or count < 1) and writes the device
+ * QLORA_ERR_ARG if m > QLORA_GEMV_MAX_M, count < 1 or the jobs' weights mix
+ * the two formats) and writes the device
  * job table into `table` (16-byte aligned, >= qlora_group_table_bytes(count)
  * bytes) with a blocking host-to-device copy: unlike every other call this
  * one synchronizes.  The buffers named by the jobs must stay valid while the

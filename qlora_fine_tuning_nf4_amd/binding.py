@@ -41,7 +41,8 @@ class _FwdJob(ctypes.Structure):
 
 class _Group(ctypes.Structure):
     _fields_ = [("table", ctypes.c_void_p), ("count", ctypes.c_int), ("lora_count", ctypes.c_int),
-                ("max_r", ctypes.c_int), ("y_dtype", ctypes.c_int), ("m", ctypes.c_int64),
+                ("max_r", ctypes.c_int), ("y_dtype", ctypes.c_int), ("dq", ctypes.c_int),
+                ("m", ctypes.c_int64),
                 ("row_groups", ctypes.c_int64), ("max_quads", ctypes.c_int64)]
 
 
@@ -65,6 +66,8 @@ def lib():
         L.qlora_nf4_codebook.argtypes = [P(ctypes.c_float)]
         L.qlora_nf4_bytes.restype = i32
         L.qlora_nf4_bytes.argtypes = [i64, i64, P(sz), P(sz), P(sz)]
+        L.qlora_nf4_single_bytes.restype = i32
+        L.qlora_nf4_single_bytes.argtypes = [i64, i64, P(sz), P(sz)]
         L.qlora_workspace_bytes.restype = sz
         L.qlora_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
         L.qlora_quantize.restype = i32
@@ -119,32 +122,51 @@ def qlora_nf4_bytes(n: int, k: int):
     return c.value, q.value, s.value
 
 
+def qlora_nf4_single_bytes(n: int, k: int):
+    c, a = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().qlora_nf4_single_bytes(n, k, ctypes.byref(c), ctypes.byref(a)),
+           "qlora_nf4_single_bytes")
+    return c.value, a.value
+
+
 def qlora_workspace_bytes(op: int, m: int, n: int, k: int, r: int) -> int:
     return int(lib().qlora_workspace_bytes(op, m, n, k, r))
 
 
 @dataclass
 class NF4Weight:
-    """Packed NF4 + double-quantized weight (device tensors)."""
+    """Packed NF4 weight (device tensors).  Double-quantized: qscale uint8
+    [n*k/64] and step float32 [ceil(n*k/16384)].  Single level: qscale None and
+    step float32 [n*k/64], the fp32 absmax of every block."""
     n: int
     k: int
-    codes: torch.Tensor    # uint8 [n*k/2]
-    qscale: torch.Tensor   # uint8 [n*k/64]
-    step: torch.Tensor     # float32 [ceil(n*k/16384)]
+    codes: torch.Tensor               # uint8 [n*k/2]
+    qscale: torch.Tensor | None
+    step: torch.Tensor
+
+    @property
+    def double_quant(self) -> bool:
+        return self.qscale is not None
 
     def desc(self) -> _Nf4Desc:
-        return _Nf4Desc(self.n, self.k, self.codes.data_ptr(), self.qscale.data_ptr(),
+        return _Nf4Desc(self.n, self.k, self.codes.data_ptr(),
+                        self.qscale.data_ptr() if self.qscale is not None else None,
                         self.step.data_ptr())
 
     @staticmethod
-    def empty(n: int, k: int, device="cuda") -> "NF4Weight":
+    def empty(n: int, k: int, device="cuda", double_quant: bool = True) -> "NF4Weight":
+        if not double_quant:
+            c, a = qlora_nf4_single_bytes(n, k)
+            return NF4Weight(n, k, torch.empty(c, dtype=torch.uint8, device=device), None,
+                             torch.empty(a // 4, dtype=torch.float32, device=device))
         c, q, s = qlora_nf4_bytes(n, k)
         return NF4Weight(n, k, torch.empty(c, dtype=torch.uint8, device=device),
                          torch.empty(q, dtype=torch.uint8, device=device),
                          torch.empty(s // 4, dtype=torch.float32, device=device))
 
     def nbytes(self) -> int:
-        return self.codes.numel() + self.qscale.numel() + 4 * self.step.numel()
+        q = self.qscale.numel() if self.qscale is not None else 0
+        return self.codes.numel() + q + 4 * self.step.numel()
 
 
 def device_codebook(device="cuda") -> torch.Tensor:
@@ -157,10 +179,12 @@ def _bf16(t, name):
     return t
 
 
-def qlora_quantize(W: torch.Tensor, codebook: torch.Tensor, out: NF4Weight | None = None) -> NF4Weight:
+def qlora_quantize(W: torch.Tensor, codebook: torch.Tensor, out: NF4Weight | None = None,
+                   double_quant: bool = True) -> NF4Weight:
+    """Quantize W; the format follows `out` when given, else `double_quant`."""
     _bf16(W, "W")
     n, k = W.shape
-    out = out if out is not None else NF4Weight.empty(n, k, W.device)
+    out = out if out is not None else NF4Weight.empty(n, k, W.device, double_quant)
     d = out.desc()
     _check(lib().qlora_quantize(_ptr(W), _ptr(codebook), ctypes.byref(d), _stream()),
            "qlora_quantize")

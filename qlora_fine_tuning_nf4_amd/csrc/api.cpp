@@ -136,8 +136,9 @@ bool shape_ok(int64_t n, int64_t k) {
          n <= ((int64_t(1) << 38) - 1) / k;
 }
 
+// qscale may be NULL: the single-level format (fp32 absmax per block in step)
 int check_desc(const qlora_nf4* W) {
-  if (!W || !W->codes || !W->qscale || !W->step) return QLORA_ERR_NULL;
+  if (!W || !W->codes || !W->step) return QLORA_ERR_NULL;
   if (!shape_ok(W->n, W->k)) return QLORA_ERR_SHAPE;
   if (!aligned(W->codes, 16) || !aligned(W->step, 4)) return QLORA_ERR_ALIGN;
   return QLORA_OK;
@@ -187,6 +188,13 @@ int qlora_nf4_bytes(int64_t n, int64_t k, size_t* codes, size_t* qscale, size_t*
   if (codes) *codes = (size_t)(n * k / 2);
   if (qscale) *qscale = (size_t)nb;
   if (step) *step = sizeof(float) * (size_t)cdiv(nb, kG);
+  return QLORA_OK;
+}
+
+int qlora_nf4_single_bytes(int64_t n, int64_t k, size_t* codes, size_t* absmax) {
+  if (!shape_ok(n, k)) return QLORA_ERR_SHAPE;
+  if (codes) *codes = (size_t)(n * k / 2);
+  if (absmax) *absmax = sizeof(float) * (size_t)(n * (k / kB));
   return QLORA_OK;
 }
 
@@ -284,9 +292,11 @@ int qlora_group_init(qlora_group* g, const qlora_fwd_job* jobs, int count, int64
   int nl = 0, max_r = 0;
   int64_t rgs = 0, maxq = 0;
   int st = QLORA_OK;
+  const bool dq = jobs[0].w.qscale != nullptr;
   for (int i = 0; i < count && st == QLORA_OK; ++i) {
     const qlora_fwd_job& J = jobs[i];
     if ((st = check_desc(&J.w))) break;
+    if ((J.w.qscale != nullptr) != dq) { st = QLORA_ERR_ARG; break; }   // one format per group
     if (!J.X || !J.Y) { st = QLORA_ERR_NULL; break; }
     if (J.r < 0 || J.r > QLORA_MAX_RANK) { st = QLORA_ERR_RANK; break; }
     if (J.r > 0 && (!J.A || !J.B || !J.T)) { st = QLORA_ERR_NULL; break; }
@@ -314,7 +324,7 @@ int qlora_group_init(qlora_group* g, const qlora_fwd_job* jobs, int count, int64
   delete[] gj;
   delete[] rj;
   if (st != QLORA_OK) return st;
-  *g = qlora_group{table, count, nl, max_r, y_dtype, m, rgs, maxq};
+  *g = qlora_group{table, count, nl, max_r, y_dtype, dq ? 1 : 0, m, rgs, maxq};
   return QLORA_OK;
 }
 
@@ -332,7 +342,7 @@ int qlora_linear_fwd_grouped(const qlora_group* g, const float* codebook, void* 
                                 s) != hipSuccess)
     return QLORA_ERR_HIP;
   if (ql::launch_gemv_grouped((const ql::GemvJob*)tb, g->count, g->row_groups, g->m, codebook,
-                              g->max_quads, s) != hipSuccess)
+                              g->max_quads, g->dq != 0, s) != hipSuccess)
     return QLORA_ERR_HIP;
   return QLORA_OK;
 }

@@ -121,7 +121,7 @@ QL_DEV void k_barrier_issue() {
 // Physical 16-byte chunk of logical chunk c in activation row r of a stage.
 QL_DEV int a_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <bool DX, bool VEC>
+template <bool DX, bool VEC, bool DQ>
 __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ act, Nf4View w,
                                                  const float* __restrict__ codebook, int64_t M,
                                                  LoraTerm lora, void* __restrict__ out, int out_bf16,
@@ -224,8 +224,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
   // whenever all 64 rows of the step are present.  Positions are taken
   // relative to a per-step base in scalar registers; blocks outside the
   // weight get an offset past the buffer end, so the hardware returns zeros
-  // (scale 0, hence decoded zeros).  The fp32 constant of flat block b is
-  // step[b / 256].
+  // (scale 0, hence decoded zeros).  Double-quantized (DQ): 8-bit scale at
+  // the storage position, fp32 constant of flat block b at step[b / 256].
+  // Single level: the fp32 absmax at the storage position in `step`.
   constexpr uint32_t kOut = 0x80000000u;
   const int64_t kb_dx = o0 / kBlock + wcb;
   const int64_t fg0 = (o0 + wr) & ~int64_t(15);
@@ -236,36 +237,44 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
   const uint32_t d_prel = (uint32_t)((wr & ~15) * nkb + kb_dx * 16 + (wr & 15));
   const uint32_t c_vo0 = DX ? (d_kok ? d_prel * 32 + q * 8 : kOut) : (f_ok ? f_prel * 32 + q * 8 : kOut);
   const uint32_t q_vo0 = DX ? (d_kok ? d_prel : kOut) : (f_ok ? f_prel : kOut);
+  // single-level format: the fp32 scale at the block's storage position
+  const uint32_t s_vo0 = DX ? (d_kok ? d_prel * 4 : kOut) : (f_ok ? f_prel * 4 : kOut);
   const uint32_t b_lane = (uint32_t)(DX ? wr * nkb + kb_dx : (o0 + wr) * nkb);
   const auto step_rsrc = buf_rsrc(w.step, (uint32_t)(((N * nkb + kGroup - 1) / kGroup) * 4));
   auto load_w = [&](int st, WRaw& r) {
-    uint32_t cvo, qvo, bidx;
-    const uint8_t *cbase, *qbase;
+    uint32_t cvo, qvo, svo, bidx;
+    int64_t pbase;   // storage position of the per-step (backward) or per-tile (forward) base
     if (DX) {
       const int64_t n0 = (int64_t)st * GBK;
-      cbase = w.codes + n0 * nkb * 32;
-      qbase = w.qscale + n0 * nkb;
+      pbase = n0 * nkb;
       bidx = b_lane + (uint32_t)(n0 * nkb);
       if (st < full_steps) {
         cvo = c_vo0;
         qvo = q_vo0;
+        svo = s_vo0;
       } else {   // ragged last step: partial group and rows past N
         const int64_t g0 = (wr & ~15), R = min(int64_t(16), N - n0 - g0);
         const bool ok = d_kok && n0 + wr < N;
         const uint32_t prel = (uint32_t)(g0 * nkb + kb_dx * R + (wr & 15));
         cvo = ok ? prel * 32 + q * 8 : kOut;
         qvo = ok ? prel : kOut;
+        svo = ok ? prel * 4 : kOut;
       }
     } else {
-      cbase = w.codes + o0 * nkb * 32;
-      qbase = w.qscale + o0 * nkb;
+      pbase = o0 * nkb;
       cvo = c_vo0 + (uint32_t)st * fR * 32;
       qvo = q_vo0 + (uint32_t)st * fR;
+      svo = s_vo0 + (uint32_t)st * fR * 4;
       bidx = b_lane + (uint32_t)st;
     }
-    r.codes = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(buf_rsrc(cbase), cvo, 0, 0));
-    r.qbyte = __builtin_amdgcn_raw_buffer_load_b8(buf_rsrc(qbase), qvo, 0, 0);
-    r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(step_rsrc, (bidx >> 8) * 4, 0, 0));
+    r.codes = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(buf_rsrc(w.codes + pbase * 32), cvo, 0, 0));
+    if (DQ) {
+      r.qbyte = __builtin_amdgcn_raw_buffer_load_b8(buf_rsrc(w.qscale + pbase), qvo, 0, 0);
+      r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(step_rsrc, (bidx >> 8) * 4, 0, 0));
+    } else {
+      r.qbyte = 1u;   // scale = 1 * absmax, exact
+      r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(w.step + pbase), svo, 0, 0));
+    }
   };
   auto scale_of = [](const WRaw& r) { return (float)r.qbyte * r.step; };
   auto wdst = [&](int stage) {
@@ -311,10 +320,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
-
-  // Loads issued by a wave in one memory phase: 4 activation DMA loads (with
-  // 16-byte rows) and 3 code loads.
-  constexpr int NLOAD = VEC ? 7 : 3;
 
   if (s_begin < s_end) {
     const int last = s_end - 1;
@@ -537,20 +542,20 @@ static constexpr size_t smem_bytes() {
   return sizeof(uint16_t) * NA * A_STAGE;   // dynamic part: the activation ring
 }
 
-template <bool DX, bool VEC>
+template <bool DX, bool VEC, bool DQ>
 static hipError_t launch_one(dim3 grid, hipStream_t s, const uint16_t* act, const Nf4View& w,
                              const float* codebook, int64_t M, const LoraTerm& lora, void* out,
                              bool bf16, float* part, int ksplit, int per, int64_t mtiles,
                              int64_t otiles) {
   static bool attr_set = false;   // idempotent: the same value every time
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<DX, VEC>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<DX, VEC, DQ>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)smem_bytes<DX>());
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemm<DX, VEC>), grid, dim3(512), smem_bytes<DX>(), s, act, w, codebook, M,
+  hipLaunchKernelGGL((k_gemm<DX, VEC, DQ>), grid, dim3(512), smem_bytes<DX>(), s, act, w, codebook, M,
                      lora, out, (int)bf16, part, ksplit, per, mtiles, otiles);
   return hipGetLastError();
 }
@@ -564,11 +569,18 @@ static hipError_t launch(const Nf4View& w, const float* codebook, const uint16_t
   const int per = (nsteps + ksplit - 1) / ksplit;
   const int64_t mtiles = (M + GBM - 1) / GBM, otiles = (O + GBN - 1) / GBN;
   const dim3 grid((unsigned)(mtiles * otiles * ksplit));
+  // the weight format (with or without double quantization) and 16-byte
+  // activation rows select the instantiation
+  const bool dq = w.qscale != nullptr;
   if (!DX || C % 8 == 0)
-    return launch_one<DX, true>(grid, s, act, w, codebook, M, lora, out, bf16, part, ksplit, per,
-                                mtiles, otiles);
-  return launch_one<DX, false>(grid, s, act, w, codebook, M, lora, out, bf16, part, ksplit, per,
-                               mtiles, otiles);
+    return dq ? launch_one<DX, true, true>(grid, s, act, w, codebook, M, lora, out, bf16, part,
+                                           ksplit, per, mtiles, otiles)
+              : launch_one<DX, true, false>(grid, s, act, w, codebook, M, lora, out, bf16, part,
+                                            ksplit, per, mtiles, otiles);
+  return dq ? launch_one<DX, false, true>(grid, s, act, w, codebook, M, lora, out, bf16, part,
+                                          ksplit, per, mtiles, otiles)
+            : launch_one<DX, false, false>(grid, s, act, w, codebook, M, lora, out, bf16, part,
+                                           ksplit, per, mtiles, otiles);
 }
 
 hipError_t launch_gemm_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,

@@ -78,7 +78,7 @@ constexpr int GV_CHUNK_BYTES = 512;   // one row of an activation chunk: 256 bf1
 
 // XPW: activation-chunk DMA instructions per wave and quad (8 * XPW chunk
 // rows: XPW = 1 for M <= 8, 2 for M <= 16, 4 for M <= 32).
-template <int MT, int XPW, bool GROUPED>
+template <int MT, int XPW, bool GROUPED, bool DQ>
 __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* __restrict__ jobs,
                                                   int njobs, const float* __restrict__ codebook,
                                                   int ksplit, int quads_per_split) {
@@ -166,12 +166,18 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
     const int qc = min(q, nquads - 1);
     const int64_t ub = gg * nkb + (int64_t)4 * qc * R;
     const auto rc = buf_rsrc(w.codes + ub * 32, (uint32_t)((nblk - ub) * 32));
-    const auto rq = buf_rsrc(w.qscale + ub, (uint32_t)(nblk - ub));
     u.c0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, w_lane * 32, 0, 0));
     u.c1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, w_lane * 32 + 16, 0, 0));
-    u.qbyte = __builtin_amdgcn_raw_buffer_load_b8(rq, w_lane, 0, 0);
-    u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           step_rsrc, ((b_lane + 4 * (uint32_t)qc) >> 8) * 4, 0, 0));
+    if (DQ) {
+      const auto rq = buf_rsrc(w.qscale + ub, (uint32_t)(nblk - ub));
+      u.qbyte = __builtin_amdgcn_raw_buffer_load_b8(rq, w_lane, 0, 0);
+      u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             step_rsrc, ((b_lane + 4 * (uint32_t)qc) >> 8) * 4, 0, 0));
+    } else {   // single level: the fp32 absmax at the storage position
+      u.qbyte = 1u;
+      u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             buf_rsrc(w.step + ub, (uint32_t)((nblk - ub) * 4)), w_lane * 4, 0, 0));
+    }
   };
 
   f32x4_t acc[MT][2];
@@ -202,9 +208,10 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
   };
 
   // wait for this wave's loads of quad q (everything but the loads issued in
-  // the following iteration: 4 code loads + XPW chunk loads), then barrier
+  // the following iteration: 4 code loads (3 without double quantization) +
+  // XPW chunk loads), then barrier
   auto wait_q = [&]() {
-    QL_VMCNT(4 + XPW);
+    QL_VMCNT((DQ ? 4 : 3) + XPW);
     QL_LGKMCNT0();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -280,9 +287,15 @@ hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16
   const int per = (int)((nquads + ksplit - 1) / ksplit);
   const GemvJob job{X, w, lora, Y, part, M, (int)y_bf16, 0};
   dim3 grid((unsigned)((w.n + 63) / 64), (unsigned)ksplit);
-#define QL_GEMV(MT, XPW)                                                                    \
-  hipLaunchKernelGGL((k_gemv_fwd<MT, XPW, false>), grid, dim3(256), 0, s, job, nullptr, 0, \
-                     codebook, ksplit, per)
+#define QL_GEMV(MT, XPW)                                                                     \
+  do {                                                                                       \
+    if (w.qscale)                                                                            \
+      hipLaunchKernelGGL((k_gemv_fwd<MT, XPW, false, true>), grid, dim3(256), 0, s, job,   \
+                         nullptr, 0, codebook, ksplit, per);                                 \
+    else                                                                                     \
+      hipLaunchKernelGGL((k_gemv_fwd<MT, XPW, false, false>), grid, dim3(256), 0, s, job,  \
+                         nullptr, 0, codebook, ksplit, per);                                 \
+  } while (0)
   // M <= 32, checked by the caller
   if (M <= 8) QL_GEMV(1, 1);
   else if (M <= 16) QL_GEMV(1, 2);
@@ -292,12 +305,18 @@ hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16
 }
 
 hipError_t launch_gemv_grouped(const GemvJob* jobs, int njobs, int64_t row_groups, int64_t M,
-                               const float* codebook, int64_t max_quads, hipStream_t s) {
+                               const float* codebook, int64_t max_quads, bool dq, hipStream_t s) {
   dim3 grid((unsigned)row_groups, 1);
   const GemvJob none{};
 #define QL_GEMV(MT, XPW)                                                                     \
-  hipLaunchKernelGGL((k_gemv_fwd<MT, XPW, true>), grid, dim3(256), 0, s, none, jobs, njobs, \
-                     codebook, 1, (int)max_quads)
+  do {                                                                                       \
+    if (dq)                                                                                  \
+      hipLaunchKernelGGL((k_gemv_fwd<MT, XPW, true, true>), grid, dim3(256), 0, s, none,    \
+                         jobs, njobs, codebook, 1, (int)max_quads);                          \
+    else                                                                                     \
+      hipLaunchKernelGGL((k_gemv_fwd<MT, XPW, true, false>), grid, dim3(256), 0, s, none,   \
+                         jobs, njobs, codebook, 1, (int)max_quads);                          \
+  } while (0)
   if (M <= 8) QL_GEMV(1, 1);
   else if (M <= 16) QL_GEMV(1, 2);
   else QL_GEMV(2, 4);

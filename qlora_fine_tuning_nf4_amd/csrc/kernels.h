@@ -15,6 +15,8 @@ struct LoraTerm {
   float scaling;
 };
 
+// Packed weight.  qscale == nullptr: single-level format, `step` then holds
+// the fp32 absmax of every block at its storage position.
 struct Nf4View {
   const uint8_t* codes;
   const uint8_t* qscale;
@@ -51,10 +53,11 @@ hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16
                            const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
                            hipStream_t s);
 // Grouped small-M forward: one launch over `njobs` device-resident jobs that
-// share M, covering `row_groups` 64-row workgroups in total; no split of the
-// contraction.  max_quads: the largest k/256 (rounded up) over the jobs.
+// share M and the weight format (dq: double-quantized scales), covering
+// `row_groups` 64-row workgroups in total; no split of the contraction.
+// max_quads: the largest k/256 (rounded up) over the jobs.
 hipError_t launch_gemv_grouped(const GemvJob* jobs, int njobs, int64_t row_groups, int64_t M,
-                               const float* codebook, int64_t max_quads, hipStream_t s);
+                               const float* codebook, int64_t max_quads, bool dq, hipStream_t s);
 // dX = dY deq(W) (+ LoRA term), contraction over n; nsplit > 1 -> partials.
 hipError_t launch_gemm_dx(const Nf4View& w, const float* codebook, const uint16_t* dY, int64_t M,
                           const LoraTerm& lora, void* dX, bool dx_bf16, float* part, int nsplit,

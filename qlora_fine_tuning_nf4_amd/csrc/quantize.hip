@@ -71,7 +71,10 @@ QL_DEV uint32_t encode8(const float (&xin)[8], float am, const float2* tab) {
 // step: lane l reads 16 bytes (8 weights) of block l/8, so one wave load is
 // 1 KiB contiguous.  The block absmax is a max over the 8 lanes of the block;
 // encoding needs only the block's own absmax, so codes are written in the
-// same pass and the group max is taken afterwards from LDS.
+// same pass and the group max is taken afterwards from LDS.  Without double
+// quantization (DQ false) the block absmax itself is stored, fp32, at the
+// block's storage position in `step`, and `qscale` is unused.
+template <bool DQ>
 __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict__ W,
                                                       const float* __restrict__ codebook,
                                                       uint8_t* __restrict__ codes,
@@ -132,7 +135,12 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
       if (lb < nb) {
         const int64_t p = blk_pos(row, kb, N, nkb);
         reinterpret_cast<uint32_t*>(codes)[p * 8 + (lane & 7)] = word;
-        if ((lane & 7) == 0) s_absmax[lb] = am;
+        if ((lane & 7) == 0) {
+          if (DQ)
+            s_absmax[lb] = am;
+          else
+            step[p] = am;
+        }
       }
       kb += 32;
       while (kb >= ukb) {
@@ -140,6 +148,7 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
         ++row;
       }
     }
+    if (!DQ) return;
     __syncthreads();
     const float a = tid < nb ? s_absmax[tid] : 0.f;
     const float wm = wave_max(a);
@@ -178,7 +187,8 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
   }
 }
 
-// Dense dequantization: one thread per 64-block, 8 x 16-byte stores.
+// Dense dequantization: one thread per 64-block, 8 x 16-byte stores.  Without
+// double quantization (qscale NULL) the scale is the stored fp32 absmax.
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
                                                  const uint8_t* __restrict__ qscale,
                                                  const float* __restrict__ step,
@@ -195,7 +205,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
   const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= nblocks) return;
   const int64_t p = blk_pos(b / nkb, b % nkb, N, nkb);
-  const Lut t = make_lut(lv, block_scale(qscale, step, b, p));
+  const Lut t = make_lut(lv, qscale ? block_scale(qscale, step, b, p) : step[p]);
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(codes + p * 32);
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + b * kBlock);
 #pragma unroll
@@ -212,8 +222,12 @@ hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* co
   // persistent workgroups (each walks groups with a stride of the grid), a
   // few per CU so loads of the next group overlap the current one
   const int64_t grid = std::min<int64_t>((ngroups + 7) / 8 * 8, 256 * 8);   // multiple of 8
-  hipLaunchKernelGGL(k_quant_nf4_dq, dim3((unsigned)grid), dim3(256), 0, s, W, codebook, codes,
-                     qscale, step, n, nkb);
+  if (qscale)
+    hipLaunchKernelGGL(k_quant_nf4_dq<true>, dim3((unsigned)grid), dim3(256), 0, s, W, codebook,
+                       codes, qscale, step, n, nkb);
+  else
+    hipLaunchKernelGGL(k_quant_nf4_dq<false>, dim3((unsigned)grid), dim3(256), 0, s, W, codebook,
+                       codes, qscale, step, n, nkb);
   return hipGetLastError();
 }
 

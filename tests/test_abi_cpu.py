@@ -42,6 +42,17 @@ def test_nf4_bytes_matches_oracle(n, k):
     assert B.qlora_nf4_bytes(n, k) == nf4.nf4_bytes(n, k)
 
 
+@pytest.mark.parametrize("n,k", [(1, 64), (3, 128), (4096, 11008), (257, 320)])
+def test_nf4_single_bytes_matches_oracle(n, k):
+    """Single-level format: codes as before, one fp32 absmax per 64-block."""
+    codes, absmax = nf4.quantize_nodq(np.zeros((n, k), np.uint16), nf4.codebook()[1])
+    assert B.qlora_nf4_single_bytes(n, k) == (codes.nbytes, absmax.nbytes)
+    L = B.lib()
+    z = ctypes.c_size_t()
+    for bad_n, bad_k in [(0, 64), (1, 63), (1 << 22, 64)]:
+        assert L.qlora_nf4_single_bytes(bad_n, bad_k, ctypes.byref(z), None) == 2
+
+
 def test_nf4_bytes_errors():
     L = B.lib()
     z = ctypes.c_size_t()
@@ -79,6 +90,9 @@ def test_quantize_argument_errors():
     assert L.qlora_quantize(FAKE, None, ctypes.byref(d), None) == 1
     assert L.qlora_quantize(FAKE, FAKE, None, None) == 1
     assert L.qlora_quantize(FAKE, FAKE, ctypes.byref(_desc(codes=0)), None) == 1
+    # qscale NULL selects the single-level format; step is still required
+    assert L.qlora_quantize(FAKE, FAKE, ctypes.byref(_desc(qs=0, st=0)), None) == 1
+    assert L.qlora_quantize(FAKE, FAKE, ctypes.byref(_desc(qs=0, k=100)), None) == 2
     assert L.qlora_quantize(FAKE, FAKE, ctypes.byref(_desc(k=100)), None) == 2
     assert L.qlora_quantize(FAKE, FAKE, ctypes.byref(_desc(n=0)), None) == 2
     assert L.qlora_quantize(FAKE + 2, FAKE, ctypes.byref(d), None) == 3
@@ -138,8 +152,8 @@ def test_bwd_argument_errors():
     assert bwd(ws=None) == 6
 
 
-def _job(n=64, k=128, X=FAKE, A=FAKE, Bp=FAKE, r=8, Y=FAKE, T=FAKE, codes=FAKE):
-    return B._FwdJob(_desc(n, k, codes=codes), X, A, Bp, r, 2.0, Y, T)
+def _job(n=64, k=128, X=FAKE, A=FAKE, Bp=FAKE, r=8, Y=FAKE, T=FAKE, codes=FAKE, qs=FAKE):
+    return B._FwdJob(_desc(n, k, codes=codes, qs=qs), X, A, Bp, r, 2.0, Y, T)
 
 
 def test_group_table_bytes():
@@ -175,18 +189,23 @@ def test_group_init_argument_errors():
     assert init([ok, _job(r=129)]) == 5
     assert init([ok, _job(X=FAKE + 2)]) == 3
     assert init([ok, _job(Y=FAKE + 8)]) == 3
+    assert init([ok, _job(qs=0)]) == 8            # one weight format per group
+    assert init([_job(qs=0), ok]) == 8
 
 
 def test_grouped_fwd_argument_errors():
     L = B.lib()
     assert L.qlora_linear_fwd_grouped(None, FAKE, None) == 1
-    g = B._Group(FAKE, 2, 0, 0, 1, 1, 8, 1)
+    def grp(count=2, lora_count=0, m=1):
+        return B._Group(table=FAKE, count=count, lora_count=lora_count, max_r=0, y_dtype=1, dq=1,
+                        m=m, row_groups=8, max_quads=1)
+    g = grp()
     assert L.qlora_linear_fwd_grouped(ctypes.byref(g), None, None) == 1
-    bad = B._Group(FAKE, 0, 0, 0, 1, 1, 8, 1)
+    bad = grp(count=0)
     assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
-    bad = B._Group(FAKE, 2, 0, 0, 1, 33, 8, 1)
+    bad = grp(m=33)
     assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
-    bad = B._Group(FAKE, 2, 3, 0, 1, 1, 8, 1)
+    bad = grp(lora_count=3)
     assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
 
 

@@ -401,6 +401,116 @@ def test_largest_dimensions(N, K):
     assert _rel(dB.cpu().numpy()[ns], dBo) <= REL_TOL
 
 
+# --------------------------------------------------------------------------- single-level format
+def _oracle_wd_single(w_bits):
+    codes, am = onf4.quantize_nodq(w_bits, _MID)
+    return onf4.dequantize_nodq(codes, am, _LV).reshape(w_bits.shape)
+
+
+@pytest.mark.parametrize("n,k,dist", [(1, 64, "normal"), (3, 128, "special"), (300, 64, "special"),
+                                      (257, 11008, "outlier"), (1000, 4096, "normal")])
+def test_quantize_single_level_bitexact(n, k, dist):
+    """Without double quantization: codes and the fp32 block absmax (storage
+    order) bit for bit."""
+    B = _dev()
+    _say("quantize single", n, k, dist)
+    if dist == "normal":
+        w = synth.normal_bf16((n, k), 0.02, n * 5 + k)
+    elif dist == "outlier":
+        w = synth.normal_bf16((n, k), 0.015, n * 5 + k, outlier_rate=0.001, outlier_scale=20)
+    else:
+        w = _special_weight(n, k, n + 2 * k)
+    q = B.qlora_quantize(_t(w), _cb(B), double_quant=False)
+    torch.cuda.synchronize()
+    assert q.qscale is None and q.step.numel() == n * k // 64
+    c, am = onf4.quantize_nodq(w, _MID)
+    cs, _ = onf4.to_storage(c, np.zeros(n * k // 64, np.uint8), n, k)
+    assert np.array_equal(q.codes.cpu().numpy(), cs)
+    assert np.array_equal(q.step.cpu().numpy().view(np.uint32),
+                          onf4.blocks_to_storage(am, n, k).view(np.uint32))
+    d = B.qlora_dequantize(q, _cb(B))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(d).reshape(-1), _oracle_wd_single(w).reshape(-1))
+
+
+@pytest.mark.parametrize("path", ["gemm", "gemv"])
+def test_single_level_fused_identity_fwd(path):
+    B = _dev()
+    n, k = 200, 512
+    w = synth.normal_bf16((n, k), 0.02, 93, outlier_rate=0.01, outlier_scale=20)
+    q = B.qlora_quantize(_t(w), _cb(B), double_quant=False)
+    wd = onf4.bf16_to_f32(_oracle_wd_single(w))
+    for r0 in (range(0, k, 32) if path == "gemv" else [0]):
+        m = 32 if path == "gemv" else k
+        eye = np.zeros((m, k), dtype=np.float32)
+        eye[np.arange(m), r0 + np.arange(m)] = 1.0
+        X = torch.from_numpy(eye).to(torch.bfloat16).cuda()
+        Y, _ = B.qlora_linear_fwd(q, _cb(B), X, path=path)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy(), wd[:, r0:r0 + m].T), (path, r0)
+
+
+@pytest.mark.parametrize("n,k", [(300, 384), (200, 384)])
+def test_single_level_fused_identity_dx(n, k):
+    B = _dev()
+    w = synth.normal_bf16((n, k), 0.02, 94)
+    q = B.qlora_quantize(_t(w), _cb(B), double_quant=False)
+    wd = onf4.bf16_to_f32(_oracle_wd_single(w))
+    dY = torch.eye(n, dtype=torch.float32).to(torch.bfloat16).cuda()
+    dX, _, _ = B.qlora_linear_bwd(q, _cb(B), None, dY)
+    torch.cuda.synchronize()
+    assert np.array_equal(dX.cpu().numpy(), wd)
+
+
+@pytest.mark.parametrize("M,N,K,r", [(130, 300, 512, 16), (257, 513, 640, 8), (2048, 4096, 4096, 8)])
+def test_single_level_linear_parity(M, N, K, r):
+    """Forward (GEMM and, for small M, GEMV) and backward on the single-level
+    format against the oracle (full outputs; sampled rows at 4096)."""
+    B = _dev()
+    _say("single linear", M, N, K, r)
+    s = 2.0
+    X, W, A, Bm, dY = _inputs(M, N, K, r, seed=M + N * 3 + K)
+    q = B.qlora_quantize(_t(W), _cb(B), double_quant=False)
+    Xd, Ad, Bd, dYd = _t(X), _t(A), _t(Bm), _t(dY)
+    Y, T = B.qlora_linear_fwd(q, _cb(B), Xd, Ad, Bd, s)
+    dX, dA, dB = B.qlora_linear_bwd(q, _cb(B), Xd, dYd, Ad, Bd, s, T=T)
+    Yv, _ = B.qlora_linear_fwd(q, _cb(B), Xd[:32], Ad, Bd, s, path="gemv")
+    torch.cuda.synchronize()
+    Wd = _oracle_wd_single(W)
+    ms = np.arange(M) if M <= 512 else np.sort(synth.rng(7).choice(M, 32, replace=False))
+    Yo, _ = olin.forward(Wd, X[ms], A, Bm, s)
+    assert _rel(Y.cpu().numpy()[ms], Yo) <= REL_TOL
+    Yvo, _ = olin.forward(Wd, X[:32], A, Bm, s)
+    assert _rel(Yv.cpu().numpy(), Yvo) <= REL_TOL
+    dXo = olin.backward(Wd, X[ms], dY[ms], A, Bm, s)[0]
+    assert _rel(dX.cpu().numpy()[ms], dXo) <= REL_TOL
+    xf, dyf = onf4.bf16_to_f32(X).astype(np.float64), onf4.bf16_to_f32(dY).astype(np.float64)
+    af, bf = onf4.bf16_to_f32(A).astype(np.float64), onf4.bf16_to_f32(Bm).astype(np.float64)
+    dAo = s * (dyf @ bf).T @ xf
+    dBo = s * dyf.T @ (xf @ af.T)
+    assert _rel(dA.cpu().numpy(), dAo) <= REL_TOL and _rel(dB.cpu().numpy(), dBo) <= REL_TOL
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_single_level_grouped_forward(M):
+    B = _dev()
+    jobs, ref = [], []
+    for i, (N, K, r) in enumerate(GROUP_SHAPES):
+        X, W, A, Bm, _ = _inputs(M, N, K, r, seed=300 + M + 17 * i)
+        q = B.qlora_quantize(_t(W), _cb(B), double_quant=False)
+        j = dict(w=q, X=_t(X), Y=torch.full((M, N), float("nan"), device="cuda"))
+        if r:
+            j.update(A=_t(A), B=_t(Bm), scaling=2.0, T=torch.full((M, r), float("nan"), device="cuda"))
+        jobs.append(j)
+        ref.append((W, X, A if r else None, Bm if r else None))
+    g = B.qlora_group_init(jobs, M, y_dtype=torch.float32)
+    B.qlora_linear_fwd_grouped(g, _cb(B))
+    torch.cuda.synchronize()
+    for j, (W, X, A, Bm) in zip(jobs, ref):
+        Yo, _ = olin.forward(_oracle_wd_single(W), X, A, Bm, 2.0)
+        assert _rel(j["Y"].cpu().numpy(), Yo) <= REL_TOL
+
+
 # --------------------------------------------------------------------------- robustness
 def test_deterministic_and_nan_poisoned_outputs():
     B = _dev()
