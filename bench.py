@@ -62,7 +62,14 @@ def flops_bwd(M, N, K, r):
     return 2 * M * N * K + 2 * M * r * (2 * K + 2 * N)
 
 
+# weight format: double-quantized scales (default) or one fp32 absmax per
+# block (--single-level)
+DQ = True
+
+
 def packed_bytes(N, K):
+    if not DQ:
+        return N * K // 2 + 4 * (N * K // 64)
     return N * K // 2 + N * K // 64 + 4 * ((N * K // 64 + 255) // 256)
 
 
@@ -145,7 +152,7 @@ def run_layer7b(args):
     layers = []
     for i, (name, N, K, r) in enumerate(PROJ):
         W = synth.device_normal_bf16((N, K), 0.02, synth.tensor_seed(2, 10 * i), device=dev)
-        q = QB.qlora_quantize(W, cb)
+        q = QB.qlora_quantize(W, cb, double_quant=DQ)
         del W
         L = dict(name=name, N=N, K=K, r=r, q=q)
         L["X"] = synth.device_normal_bf16((M, K), 1.0, synth.tensor_seed(2, 10 * i + 1), device=dev)
@@ -235,7 +242,7 @@ def run_layer7b(args):
         "gpu_step_ms": _spread(step_ms),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.02) weights quantized to NF4+DQ, N(0,1) activations)",
-        "config": {"workload": WORKLOAD, "M": M, "r": RANK, "alpha": ALPHA,
+        "config": {"workload": WORKLOAD, "M": M, "r": RANK, "alpha": ALPHA, "double_quant": DQ,
                    "projections": [[p[0], p[1], p[2], p[3]] for p in PROJ], "y_dtype": "bf16",
                    "dx_dtype": "bf16", "parallelism": "none (1 GPU)"},
         "effective_GBps": round(gbs, 1),
@@ -300,7 +307,7 @@ def run_decode(args):
         for i, (name, N, K, r) in enumerate(PROJ):
             W = synth.device_normal_bf16((N, K), 0.02, synth.tensor_seed(3, 100 * layer + 10 * i),
                                          device=dev)
-            weights.append((QB.qlora_quantize(W, cb), N, K, r))
+            weights.append((QB.qlora_quantize(W, cb, double_quant=DQ), N, K, r))
             del W
     torch.cuda.synchronize()
     per_m = {}
@@ -348,7 +355,7 @@ def run_decode(args):
         "config": {"workload": f"decode sweep: {DECODE_LAYERS} layers x (q,k,v,o 4096x4096; gate,up "
                                "11008x4096; down 4096x11008), M=1, LoRA r=8 alpha=16 on q,k,v,o, "
                                "forward only, one grouped launch per sweep",
-                   "M": 1, "layers": DECODE_LAYERS, "params": sum(N * K for _, N, K, _ in weights),
+                   "M": 1, "layers": DECODE_LAYERS, "double_quant": DQ, "params": sum(N * K for _, N, K, _ in weights),
                    "packed_bytes": sum(q.nbytes() for q, *_ in weights), "parallelism": "none (1 GPU)"},
         "per_m": per_m,
         "roofline": {"bound": "hbm", "kernel": "k_gemv_fwd", "achieved": round(achieved, 1),
@@ -412,7 +419,7 @@ def run_quantize70b(args):
     torch.cuda.set_device(dev)
     cb = QB.device_codebook(dev)
     Ws = _weights70(dev)
-    outs = [QB.NF4Weight.empty(N, K, dev) for _, N, K in PROJ70]
+    outs = [QB.NF4Weight.empty(N, K, dev, double_quant=DQ) for _, N, K in PROJ70]
     params = sum(N * K for _, N, K in PROJ70)
     nbytes = sum(2 * N * K + packed_bytes(N, K) for _, N, K in PROJ70)
 
@@ -434,6 +441,7 @@ def run_quantize70b(args):
         "data": "synthetic (seeded N(0,0.015) bf16 weights, 0.1% outliers x20)",
         "config": {"workload": "quantize a 70B-style layer: q,k,v,o 8192x8192; gate,up 28672x8192; "
                                "down 8192x28672 (973,078,528 params)", "params": params,
+                   "double_quant": DQ,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "k_quant_nf4_dq", "achieved": round(ach, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
@@ -472,7 +480,7 @@ def run_layer70b(args):
     s = alpha / r
     layers = []
     for i, (W, (name, N, K)) in enumerate(zip(_weights70(dev), PROJ70)):
-        q = QB.qlora_quantize(W, cb)
+        q = QB.qlora_quantize(W, cb, double_quant=DQ)
         del W
         L = dict(N=N, K=K, q=q)
         L["X"] = synth.device_normal_bf16((M, K), 1.0, synth.tensor_seed(4, 10 * i + 1), device=dev)
@@ -507,7 +515,7 @@ def run_layer70b(args):
         "data": "synthetic (seeded N(0,0.015) weights with 0.1% outliers x20, NF4+DQ; N(0,1) activations)",
         "config": {"workload": "70B-style layer linears (q,k,v,o 8192x8192; gate,up 28672x8192; down "
                                "8192x28672), M=4096 tokens, LoRA r=16 alpha=32 on all seven, fwd+bwd",
-                   "M": M, "r": r, "alpha": alpha, "parallelism": "none (1 GPU)"},
+                   "M": M, "r": r, "alpha": alpha, "double_quant": DQ, "parallelism": "none (1 GPU)"},
         "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
     }
     return out
@@ -519,14 +527,21 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single-level", action="store_true",
+                    help="weights without double quantization (fp32 absmax per block); "
+                         "no CPU baseline (the oracle baselines time the double-quantized format)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=768)
     ap.add_argument("--workload", default="layer7b",
                     choices=["layer7b", "decode", "quantize70b", "layer70b"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only; --gpus must be 1 "
-              "(the multi-GPU sharding is a design, not built)", file=sys.stderr)
+        print("bench.py measures one GPU only; --gpus must be 1 "
+              "(sharding over several GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
+    if args.single_level:
+        global DQ
+        DQ = False
+        args.no_cpu_baseline = True
 
     run = {"layer7b": run_layer7b, "decode": run_decode, "quantize70b": run_quantize70b,
            "layer70b": run_layer70b}[args.workload]
