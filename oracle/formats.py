@@ -68,34 +68,24 @@ def _blocks(w_bits: np.ndarray, size: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # asymmetric uint4
 # --------------------------------------------------------------------------
-def u4_params(x_block: np.ndarray):
-    """Steps 1-3 for one block of fp32 values -> (scale fp32, zp fp32)."""
-    lo = np.float32(min(float(np.min(x_block)), 0.0))
-    hi = np.float32(max(float(np.max(x_block)), 0.0))
-    span = np.float32(hi - lo)                    # binary32 subtraction
-    scale = np.float32(span / np.float32(15.0))
-    if scale == 0:
-        return np.float32(0.0), np.float32(0.0)
-    z = np.rint(np.float32(-lo / scale))          # binary32 quotient, ties to even
-    return scale, np.float32(min(max(z, 0.0), 15.0))
-
-
 def u4_quantize(w_bits: np.ndarray):
     """bf16 weight bits (numel % 64 == 0) -> (codes uint8[numel/2] packed as
     NF4, scale float32[nb], zp float32[nb]), flat block order."""
     x = _blocks(w_bits, U4_BLOCK)
-    nb = x.shape[0]
-    scale = np.empty(nb, dtype=np.float32)
-    zp = np.empty(nb, dtype=np.float32)
-    code = np.zeros(x.shape, dtype=np.uint8)
-    for b in range(nb):
-        s, z = u4_params(x[b])
-        scale[b], zp[b] = s, z
-        if s == 0:
-            continue
-        qv = np.rint(np.divide(x[b], s, dtype=np.float32)).astype(np.int64) + int(z)
-        code[b] = np.clip(qv, 0, 15).astype(np.uint8)
-    return pack(code.reshape(-1)), scale, zp
+    # step 1: the block range, widened to hold 0
+    lo = np.minimum(np.min(x, axis=1), np.float32(0)).astype(np.float32)
+    hi = np.maximum(np.max(x, axis=1), np.float32(0)).astype(np.float32)
+    # step 2: binary32 subtraction and division
+    scale = np.divide((hi - lo).astype(np.float32), np.float32(15.0), dtype=np.float32)
+    live = scale > 0
+    safe = np.where(live, scale, np.float32(1)).astype(np.float32)
+    # step 3: zero-point, an integer value in [0, 15] (0 for an all-zero block)
+    z = np.rint(np.divide(-lo, safe, dtype=np.float32))
+    zp = np.where(live, np.clip(z, 0, 15), 0).astype(np.int64)
+    # step 4: codes
+    qv = np.rint(np.divide(x, safe[:, None], dtype=np.float32)).astype(np.int64) + zp[:, None]
+    code = np.where(live[:, None], np.clip(qv, 0, 15), 0).astype(np.uint8)
+    return pack(code.reshape(-1)), np.where(live, scale, 0).astype(np.float32), zp.astype(np.float32)
 
 
 def u4_dequantize(codes, scale, zp) -> np.ndarray:

@@ -50,9 +50,12 @@ def test_u4_one_sign_block_widened_to_zero():
     # scale is a little above 1/15 (0x3D888889): 0.5 / scale = 7.4999996 -> 7
     assert q.max() == 15 and q.min() == 7
     assert f(F.u4_dequantize(codes, s, z))[63] == 1.0
-    # all negative: hi widened to 0, zero-point 15
+    # all negative: hi widened to 0 (the same scale), zero-point 15, -1 on
+    # code 0 and -0.5 on rint(-7.4999996) + 15 = 8
     codes, s, z = F.u4_quantize(bf(-x))
-    assert z[0] == 15.0 and u4_codes(codes).min() == 0
+    assert s[0] == np.float32(0.0666666701436042) and z[0] == 15.0
+    q = u4_codes(codes)
+    assert q[63] == 0 and q[0] == 8
 
 
 def test_u4_zero_block_and_exact_zero():
