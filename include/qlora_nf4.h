@@ -2,9 +2,9 @@
  * qlora_nf4.h -- C ABI of the QLoRA NF4 quantized-linear library (gfx950 / MI355X).
  *
  * The frozen base weight W [n x k] (out_features x in_features) is stored as
- * block-wise 4-bit NF4 with double quantization of the block scales; the
- * forward and backward of the LoRA-augmented linear layer dequantize it to
- * bf16 inside the kernels.
+ * block-wise 4-bit NF4 with double quantization of the block scales (or in
+ * one of the alternate block formats below); the forward and backward of the
+ * LoRA-augmented linear layer dequantize it to bf16 inside the kernels.
  *
  * Pages cited (address and section):
  *   news.rkmt.cn/news/4821   (QLoRA double / block-wise quantization)
@@ -67,6 +67,13 @@ enum {
   QLORA_PATH_GEMM = 2  /* force the tiled MFMA GEMM path */
 };
 
+/* weight formats (qlora_nf4.format; 0, the NF4 format, when zero-initialized) */
+enum {
+  QLORA_FMT_NF4 = 0,     /* NF4 codes, double-quantized or single-level scales */
+  QLORA_FMT_U4_ASYM = 1, /* asymmetric 4-bit min/max blocks of 64, fp32 scale + zero-point */
+  QLORA_FMT_Q8_0 = 2     /* int8 blocks of 32 with an fp16 scale */
+};
+
 #define QLORA_BLOCK 64        /* weights per first-level block   (news.rkmt.cn/news/4821 §1.2) */
 #define QLORA_GROUP 256       /* block scales per second-level group (news.rkmt.cn/news/4821 §2.2) */
 #define QLORA_MAX_RANK 128    /* largest supported LoRA rank */
@@ -97,8 +104,29 @@ enum {
  * §2.3: one fp32 scale per 64-block, 0.5 bit per weight): qscale = NULL and
  * step holds n*k/64 floats, the fp32 absmax of each block at the block's
  * storage position (the order above); w = bf16_rne(level[code] * absmax_b).
- * Every entry point accepts either format; a grouped forward needs one format
- * for all its jobs.
+ *
+ * Alternate formats.  The weight is cut into 64-weight units (one row, 64
+ * consecutive k: the NF4 block) stored in the order above, unit (row, kb) at
+ * position p.
+ *   QLORA_FMT_U4_ASYM (news.rkmt.cn/news/4821 §1.3, §2.1; kwkr.cn/news/627310
+ *     §2.1): per 64-block lo = min(min, 0), hi = max(max, 0),
+ *     scale = fp32(fp32(hi - lo) / 15), zp = clamp(rint_even(fp32(-lo / scale)),
+ *     0, 15), q = clamp(rint_even(fp32(x / scale)) + zp, 0, 15) (all 0 when
+ *     scale is 0); w = bf16_rne(fp32(scale * (q - zp))).  codes: n*k/2 bytes,
+ *     q packed as the NF4 codes; step: 2*n*k/64 floats, step[2p] = scale,
+ *     step[2p+1] = zp (an integer value); qscale must be NULL.  8-byte aligned
+ *     step.
+ *   QLORA_FMT_Q8_0 (www.cf-1.com/news/5705389 §1.1, §2.2; symmetric scale of
+ *     kwkr.cn/news/627310 §2.1): per 32-block d16 = fp16_rne(fp32(absmax / 127)),
+ *     q = clamp(rint_even(fp32(x / d16)), -127, 127) (0 when d16 is 0);
+ *     w = bf16_rne(d16 * q).  codes: n*k bytes, 64 per unit, byte e of unit p
+ *     the int8 q of its element e; qscale: 4*n*k/64 bytes, the fp16 scales
+ *     (little-endian binary16) of the unit's elements 0-31 at bytes [4p, 4p+2)
+ *     and 32-63 at [4p+2, 4p+4); step is unused (may be NULL).  Blocks with
+ *     absmax above 127 * 65504 are outside the contract.
+ * The codebook argument of every entry point is used by (and required for)
+ * the NF4 format only.  Every entry point accepts every format; a grouped
+ * forward needs one format (and for NF4 one scale level) for all its jobs.
  */
 typedef struct {
   int64_t n;       /* out_features */
@@ -106,6 +134,7 @@ typedef struct {
   uint8_t *codes;
   uint8_t *qscale;
   float *step;
+  int32_t format;  /* QLORA_FMT_* */
 } qlora_nf4;
 
 /*
@@ -135,6 +164,15 @@ int qlora_nf4_bytes(int64_t n, int64_t k, size_t *codes, size_t *qscale, size_t 
 int qlora_nf4_single_bytes(int64_t n, int64_t k, size_t *codes, size_t *absmax);
 
 /*
+ * Host.  Byte sizes of the three arrays of an n x k weight in `format`
+ * (QLORA_FMT_NF4: the double-quantized sizes of qlora_nf4_bytes); arrays the
+ * format does not use get 0.  Errors as qlora_nf4_bytes, QLORA_ERR_ARG for an
+ * unknown format.
+ */
+int qlora_weight_bytes(int format, int64_t n, int64_t k, size_t *codes, size_t *qscale,
+                       size_t *step);
+
+/*
  * Host.  Workspace bytes needed by qlora_linear_fwd (op = 0) or
  * qlora_linear_bwd (op = 1) for these sizes, for any path.  0 on bad input.
  */
@@ -150,7 +188,8 @@ size_t qlora_workspace_bytes(int op, int64_t m, int64_t n, int64_t k, int r);
  * (news.rkmt.cn/news/4821 §1.2, §2.1, §2.2; zky001 section 5.8).
  * With out->qscale == NULL the second level is skipped: the single-level
  * format, the fp32 absmax of each block written to out->step (sized by
- * qlora_nf4_single_bytes).
+ * qlora_nf4_single_bytes).  With out->format an alternate format, the
+ * weight is encoded in that format (codebook unused, may be NULL).
  * `codebook` is the device copy of qlora_nf4_codebook().
  */
 int qlora_quantize(const uint16_t *W, const float *codebook, const qlora_nf4 *out, void *stream);
@@ -222,7 +261,7 @@ typedef struct {
 /* Plain-data handle filled by qlora_group_init; `table` is the caller's device buffer. */
 typedef struct {
   void *table;
-  int count, lora_count, max_r, y_dtype, dq;
+  int count, lora_count, max_r, y_dtype, variant;   /* variant: the jobs' weight format (internal) */
   int64_t m, row_groups, max_quads;
 } qlora_group;
 
@@ -232,7 +271,7 @@ size_t qlora_group_table_bytes(int count);
 /*
  * Host, setup time.  Validates every job (QLORA_ERR_* as qlora_linear_fwd,
  * QLORA_ERR_ARG if m > QLORA_GEMV_MAX_M, count < 1 or the jobs' weights mix
- * the two formats) and writes the device
+ * formats or NF4 scale levels) and writes the device
  * job table into `table` (16-byte aligned, >= qlora_group_table_bytes(count)
  * bytes) with a blocking host-to-device copy: unlike every other call this
  * one synchronizes.  The buffers named by the jobs must stay valid while the

@@ -18,6 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
 
 QLORA_F32, QLORA_BF16 = 0, 1
+QLORA_FMT_NF4, QLORA_FMT_U4_ASYM, QLORA_FMT_Q8_0 = 0, 1, 2
+FORMATS = {"nf4": QLORA_FMT_NF4, "u4_asym": QLORA_FMT_U4_ASYM, "q8_0": QLORA_FMT_Q8_0}
 PATHS = {"auto": 0, "gemv": 1, "gemm": 2}
 CODEBOOK_LEN = 31
 GEMV_MAX_M = 32
@@ -30,7 +32,7 @@ class QLoRAError(RuntimeError):
 
 class _Nf4Desc(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("codes", ctypes.c_void_p),
-                ("qscale", ctypes.c_void_p), ("step", ctypes.c_void_p)]
+                ("qscale", ctypes.c_void_p), ("step", ctypes.c_void_p), ("format", ctypes.c_int32)]
 
 
 class _FwdJob(ctypes.Structure):
@@ -41,7 +43,7 @@ class _FwdJob(ctypes.Structure):
 
 class _Group(ctypes.Structure):
     _fields_ = [("table", ctypes.c_void_p), ("count", ctypes.c_int), ("lora_count", ctypes.c_int),
-                ("max_r", ctypes.c_int), ("y_dtype", ctypes.c_int), ("dq", ctypes.c_int),
+                ("max_r", ctypes.c_int), ("y_dtype", ctypes.c_int), ("variant", ctypes.c_int),
                 ("m", ctypes.c_int64),
                 ("row_groups", ctypes.c_int64), ("max_quads", ctypes.c_int64)]
 
@@ -68,6 +70,8 @@ def lib():
         L.qlora_nf4_bytes.argtypes = [i64, i64, P(sz), P(sz), P(sz)]
         L.qlora_nf4_single_bytes.restype = i32
         L.qlora_nf4_single_bytes.argtypes = [i64, i64, P(sz), P(sz)]
+        L.qlora_weight_bytes.restype = i32
+        L.qlora_weight_bytes.argtypes = [i32, i64, i64, P(sz), P(sz), P(sz)]
         L.qlora_workspace_bytes.restype = sz
         L.qlora_workspace_bytes.argtypes = [i32, i64, i64, i64, i32]
         L.qlora_quantize.restype = i32
@@ -129,44 +133,66 @@ def qlora_nf4_single_bytes(n: int, k: int):
     return c.value, a.value
 
 
+def qlora_weight_bytes(fmt: int, n: int, k: int):
+    c, q, s = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().qlora_weight_bytes(fmt, n, k, ctypes.byref(c), ctypes.byref(q), ctypes.byref(s)),
+           "qlora_weight_bytes")
+    return c.value, q.value, s.value
+
+
 def qlora_workspace_bytes(op: int, m: int, n: int, k: int, r: int) -> int:
     return int(lib().qlora_workspace_bytes(op, m, n, k, r))
 
 
 @dataclass
 class NF4Weight:
-    """Packed NF4 weight (device tensors).  Double-quantized: qscale uint8
-    [n*k/64] and step float32 [ceil(n*k/16384)].  Single level: qscale None and
-    step float32 [n*k/64], the fp32 absmax of every block."""
+    """Packed weight (device tensors), in the format `fmt` (QLORA_FMT_*).
+    NF4 double-quantized: qscale uint8 [n*k/64], step float32
+    [ceil(n*k/16384)].  NF4 single level: qscale None, step float32 [n*k/64]
+    (the fp32 absmax of every block).  Asymmetric uint4: qscale None, step
+    float32 [2*n*k/64] (scale, zero-point per block).  Q8_0: codes [n*k] int8
+    bytes, qscale uint8 [4*n*k/64] (two fp16 scales per 64 weights), step None."""
     n: int
     k: int
-    codes: torch.Tensor               # uint8 [n*k/2]
+    codes: torch.Tensor               # uint8
     qscale: torch.Tensor | None
-    step: torch.Tensor
+    step: torch.Tensor | None
+    fmt: int = QLORA_FMT_NF4
 
     @property
     def double_quant(self) -> bool:
-        return self.qscale is not None
+        return self.fmt == QLORA_FMT_NF4 and self.qscale is not None
 
     def desc(self) -> _Nf4Desc:
         return _Nf4Desc(self.n, self.k, self.codes.data_ptr(),
                         self.qscale.data_ptr() if self.qscale is not None else None,
-                        self.step.data_ptr())
+                        self.step.data_ptr() if self.step is not None else None, self.fmt)
 
     @staticmethod
-    def empty(n: int, k: int, device="cuda", double_quant: bool = True) -> "NF4Weight":
+    def empty(n: int, k: int, device="cuda", double_quant: bool = True,
+              fmt: int = QLORA_FMT_NF4) -> "NF4Weight":
+        def u8(b):
+            return torch.empty(b, dtype=torch.uint8, device=device)
+
+        def f32(b):
+            return torch.empty(b // 4, dtype=torch.float32, device=device)
+
+        if fmt == QLORA_FMT_U4_ASYM:
+            c, _, s = qlora_weight_bytes(fmt, n, k)
+            return NF4Weight(n, k, u8(c), None, f32(s), fmt)
+        if fmt == QLORA_FMT_Q8_0:
+            c, q, _ = qlora_weight_bytes(fmt, n, k)
+            return NF4Weight(n, k, u8(c), u8(q), None, fmt)
         if not double_quant:
             c, a = qlora_nf4_single_bytes(n, k)
-            return NF4Weight(n, k, torch.empty(c, dtype=torch.uint8, device=device), None,
-                             torch.empty(a // 4, dtype=torch.float32, device=device))
+            return NF4Weight(n, k, u8(c), None, f32(a), fmt)
         c, q, s = qlora_nf4_bytes(n, k)
-        return NF4Weight(n, k, torch.empty(c, dtype=torch.uint8, device=device),
-                         torch.empty(q, dtype=torch.uint8, device=device),
-                         torch.empty(s // 4, dtype=torch.float32, device=device))
+        return NF4Weight(n, k, u8(c), u8(q), f32(s), fmt)
 
     def nbytes(self) -> int:
         q = self.qscale.numel() if self.qscale is not None else 0
-        return self.codes.numel() + q + 4 * self.step.numel()
+        s = 4 * self.step.numel() if self.step is not None else 0
+        return self.codes.numel() + q + s
 
 
 def device_codebook(device="cuda") -> torch.Tensor:
@@ -179,12 +205,13 @@ def _bf16(t, name):
     return t
 
 
-def qlora_quantize(W: torch.Tensor, codebook: torch.Tensor, out: NF4Weight | None = None,
-                   double_quant: bool = True) -> NF4Weight:
-    """Quantize W; the format follows `out` when given, else `double_quant`."""
+def qlora_quantize(W: torch.Tensor, codebook: torch.Tensor | None, out: NF4Weight | None = None,
+                   double_quant: bool = True, fmt: int = QLORA_FMT_NF4) -> NF4Weight:
+    """Quantize W; the format follows `out` when given, else `fmt` and (NF4)
+    `double_quant`.  The codebook is used by NF4 only (None otherwise)."""
     _bf16(W, "W")
     n, k = W.shape
-    out = out if out is not None else NF4Weight.empty(n, k, W.device, double_quant)
+    out = out if out is not None else NF4Weight.empty(n, k, W.device, double_quant, fmt)
     d = out.desc()
     _check(lib().qlora_quantize(_ptr(W), _ptr(codebook), ctypes.byref(d), _stream()),
            "qlora_quantize")

@@ -136,15 +136,50 @@ bool shape_ok(int64_t n, int64_t k) {
          n <= ((int64_t(1) << 38) - 1) / k;
 }
 
-// qscale may be NULL: the single-level format (fp32 absmax per block in step)
+// The arrays each format uses (NF4: qscale NULL selects the single-level
+// scales), their alignment, the shape.
 int check_desc(const qlora_nf4* W) {
-  if (!W || !W->codes || !W->step) return QLORA_ERR_NULL;
+  if (!W) return QLORA_ERR_NULL;
+  switch (W->format) {
+    case QLORA_FMT_NF4:
+      if (!W->codes || !W->step) return QLORA_ERR_NULL;
+      break;
+    case QLORA_FMT_U4_ASYM:
+      if (!W->codes || !W->step) return QLORA_ERR_NULL;
+      if (W->qscale) return QLORA_ERR_ARG;
+      break;
+    case QLORA_FMT_Q8_0:
+      if (!W->codes || !W->qscale) return QLORA_ERR_NULL;
+      break;
+    default:
+      return QLORA_ERR_ARG;
+  }
   if (!shape_ok(W->n, W->k)) return QLORA_ERR_SHAPE;
-  if (!aligned(W->codes, 16) || !aligned(W->step, 4)) return QLORA_ERR_ALIGN;
+  if (!aligned(W->codes, 16)) return QLORA_ERR_ALIGN;
+  if (W->format == QLORA_FMT_NF4 && !aligned(W->step, 4)) return QLORA_ERR_ALIGN;
+  if (W->format == QLORA_FMT_U4_ASYM && !aligned(W->step, 8)) return QLORA_ERR_ALIGN;
+  if (W->format == QLORA_FMT_Q8_0 && !aligned(W->qscale, 4)) return QLORA_ERR_ALIGN;
   return QLORA_OK;
 }
 
-ql::Nf4View view(const qlora_nf4* W) { return ql::Nf4View{W->codes, W->qscale, W->step, W->n, W->k}; }
+// The codebook: required (and 4-byte aligned) for NF4 only.
+int check_codebook(const qlora_nf4* W, const float* codebook) {
+  if (W->format != QLORA_FMT_NF4) return QLORA_OK;
+  if (!codebook) return QLORA_ERR_NULL;
+  return aligned(codebook, 4) ? QLORA_OK : QLORA_ERR_ALIGN;
+}
+
+int kernel_fmt(const qlora_nf4* W) {
+  switch (W->format) {
+    case QLORA_FMT_U4_ASYM: return ql::kFmtU4;
+    case QLORA_FMT_Q8_0: return ql::kFmtQ8;
+    default: return W->qscale ? ql::kFmtNf4Dq : ql::kFmtNf4;
+  }
+}
+
+ql::Nf4View view(const qlora_nf4* W) {
+  return ql::Nf4View{W->codes, W->qscale, W->step, W->n, W->k, kernel_fmt(W)};
+}
 
 }  // namespace
 
@@ -198,6 +233,19 @@ int qlora_nf4_single_bytes(int64_t n, int64_t k, size_t* codes, size_t* absmax) 
   return QLORA_OK;
 }
 
+int qlora_weight_bytes(int format, int64_t n, int64_t k, size_t* codes, size_t* qscale,
+                       size_t* step) {
+  if (format < QLORA_FMT_NF4 || format > QLORA_FMT_Q8_0) return QLORA_ERR_ARG;
+  if (!shape_ok(n, k)) return QLORA_ERR_SHAPE;
+  if (format == QLORA_FMT_NF4) return qlora_nf4_bytes(n, k, codes, qscale, step);
+  const size_t units = (size_t)(n * (k / kB));
+  const bool u4 = format == QLORA_FMT_U4_ASYM;
+  if (codes) *codes = u4 ? (size_t)(n * k / 2) : (size_t)(n * k);
+  if (qscale) *qscale = u4 ? 0 : 4 * units;
+  if (step) *step = u4 ? 8 * units : 0;
+  return QLORA_OK;
+}
+
 size_t qlora_workspace_bytes(int op, int64_t m, int64_t n, int64_t k, int r) {
   if (m < 1 || n < 1 || k < kB || k % kB || r < 0 || r > QLORA_MAX_RANK) return 0;
   if (op == 0) {
@@ -213,21 +261,22 @@ size_t qlora_workspace_bytes(int op, int64_t m, int64_t n, int64_t k, int r) {
 }
 
 int qlora_quantize(const uint16_t* W, const float* codebook, const qlora_nf4* out, void* stream) {
-  if (!W || !codebook) return QLORA_ERR_NULL;
+  if (!W) return QLORA_ERR_NULL;
   if (int e = check_desc(out)) return e;
-  if (!aligned(W, 16) || !aligned(codebook, 4)) return QLORA_ERR_ALIGN;
+  if (int e = check_codebook(out, codebook)) return e;
+  if (!aligned(W, 16)) return QLORA_ERR_ALIGN;
   if (ql::launch_quantize(W, codebook, out->codes, out->qscale, out->step, out->n, out->k,
-                          (hipStream_t)stream) != hipSuccess)
+                          kernel_fmt(out), (hipStream_t)stream) != hipSuccess)
     return QLORA_ERR_HIP;
   return QLORA_OK;
 }
 
 int qlora_dequantize(const qlora_nf4* W, const float* codebook, uint16_t* out, void* stream) {
-  if (!codebook || !out) return QLORA_ERR_NULL;
+  if (!out) return QLORA_ERR_NULL;
   if (int e = check_desc(W)) return e;
-  if (!aligned(out, 16) || !aligned(codebook, 4)) return QLORA_ERR_ALIGN;
-  if (ql::launch_dequant(W->codes, W->qscale, W->step, codebook, out, W->n, W->k,
-                         (hipStream_t)stream) != hipSuccess)
+  if (int e = check_codebook(W, codebook)) return e;
+  if (!aligned(out, 16)) return QLORA_ERR_ALIGN;
+  if (ql::launch_dequant(view(W), codebook, out, (hipStream_t)stream) != hipSuccess)
     return QLORA_ERR_HIP;
   return QLORA_OK;
 }
@@ -236,15 +285,16 @@ int qlora_linear_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
                      const uint16_t* A, const uint16_t* B, int r, float scaling, void* Y,
                      int y_dtype, float* T_save, void* ws, size_t ws_bytes, int path,
                      void* stream) {
-  if (!codebook || !X || !Y) return QLORA_ERR_NULL;
+  if (!X || !Y) return QLORA_ERR_NULL;
   if (int e = check_desc(W)) return e;
+  if (int e = check_codebook(W, codebook)) return e;
   if (m < 1) return QLORA_ERR_SHAPE;
   if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
   if (y_dtype != QLORA_F32 && y_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
   if (path < QLORA_PATH_AUTO || path > QLORA_PATH_GEMM) return QLORA_ERR_ARG;
   if (path == QLORA_PATH_GEMV && m > QLORA_GEMV_MAX_M) return QLORA_ERR_ARG;
-  if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(codebook, 4)) return QLORA_ERR_ALIGN;
+  if (!aligned(X, 16) || !aligned(Y, 16)) return QLORA_ERR_ALIGN;
   if (r > 0 && (!aligned(A, 16) || !aligned(B, 2) || (T_save && !aligned(T_save, 4))))
     return QLORA_ERR_ALIGN;
   const int64_t n = W->n, k = W->k;
@@ -292,11 +342,12 @@ int qlora_group_init(qlora_group* g, const qlora_fwd_job* jobs, int count, int64
   int nl = 0, max_r = 0;
   int64_t rgs = 0, maxq = 0;
   int st = QLORA_OK;
-  const bool dq = jobs[0].w.qscale != nullptr;
+  int fmt = -1;
   for (int i = 0; i < count && st == QLORA_OK; ++i) {
     const qlora_fwd_job& J = jobs[i];
     if ((st = check_desc(&J.w))) break;
-    if ((J.w.qscale != nullptr) != dq) { st = QLORA_ERR_ARG; break; }   // one format per group
+    if (i == 0) fmt = kernel_fmt(&J.w);
+    if (kernel_fmt(&J.w) != fmt) { st = QLORA_ERR_ARG; break; }   // one format per group
     if (!J.X || !J.Y) { st = QLORA_ERR_NULL; break; }
     if (J.r < 0 || J.r > QLORA_MAX_RANK) { st = QLORA_ERR_RANK; break; }
     if (J.r > 0 && (!J.A || !J.B || !J.T)) { st = QLORA_ERR_NULL; break; }
@@ -324,16 +375,19 @@ int qlora_group_init(qlora_group* g, const qlora_fwd_job* jobs, int count, int64
   delete[] gj;
   delete[] rj;
   if (st != QLORA_OK) return st;
-  *g = qlora_group{table, count, nl, max_r, y_dtype, dq ? 1 : 0, m, rgs, maxq};
+  *g = qlora_group{table, count, nl, max_r, y_dtype, fmt, m, rgs, maxq};
   return QLORA_OK;
 }
 
 int qlora_linear_fwd_grouped(const qlora_group* g, const float* codebook, void* stream) {
-  if (!g || !g->table || !codebook) return QLORA_ERR_NULL;
+  if (!g || !g->table) return QLORA_ERR_NULL;
   if (g->count < 1 || g->m < 1 || g->m > QLORA_GEMV_MAX_M || g->lora_count < 0 ||
-      g->lora_count > g->count || g->row_groups < 1)
+      g->lora_count > g->count || g->row_groups < 1 || g->variant < ql::kFmtNf4Dq ||
+      g->variant > ql::kFmtQ8)
     return QLORA_ERR_ARG;
-  if (!aligned(codebook, 4)) return QLORA_ERR_ALIGN;
+  const bool nf4 = g->variant == ql::kFmtNf4Dq || g->variant == ql::kFmtNf4;
+  if (nf4 && !codebook) return QLORA_ERR_NULL;
+  if (nf4 && !aligned(codebook, 4)) return QLORA_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   const char* tb = (const char*)g->table;
   const size_t rd_off = up16(sizeof(ql::GemvJob) * (size_t)g->count);
@@ -342,7 +396,7 @@ int qlora_linear_fwd_grouped(const qlora_group* g, const float* codebook, void* 
                                 s) != hipSuccess)
     return QLORA_ERR_HIP;
   if (ql::launch_gemv_grouped((const ql::GemvJob*)tb, g->count, g->row_groups, g->m, codebook,
-                              g->max_quads, g->dq != 0, s) != hipSuccess)
+                              g->max_quads, g->variant, s) != hipSuccess)
     return QLORA_ERR_HIP;
   return QLORA_OK;
 }
@@ -351,15 +405,15 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
                      const uint16_t* dY, int64_t m, const uint16_t* A, const uint16_t* B, int r,
                      float scaling, const float* T_saved, void* dX, int dx_dtype, float* dA,
                      float* dB, void* ws, size_t ws_bytes, int path, void* stream) {
-  if (!codebook || !dY) return QLORA_ERR_NULL;
+  if (!dY) return QLORA_ERR_NULL;
   if (int e = check_desc(W)) return e;
+  if (int e = check_codebook(W, codebook)) return e;
   if (m < 1) return QLORA_ERR_SHAPE;
   if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
   if (r > 0 && (!A || !B || !dA || !dB || !X)) return QLORA_ERR_NULL;
   if (dx_dtype != QLORA_F32 && dx_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
   if (path < QLORA_PATH_AUTO || path > QLORA_PATH_GEMM) return QLORA_ERR_ARG;
-  if (!aligned(dY, 16) || !aligned(codebook, 4) || (dX && !aligned(dX, 16)) ||
-      (X && !aligned(X, 16)))
+  if (!aligned(dY, 16) || (dX && !aligned(dX, 16)) || (X && !aligned(X, 16)))
     return QLORA_ERR_ALIGN;
   if (r > 0 && (!aligned(A, 16) || !aligned(B, 2) || !aligned(dA, 4) || !aligned(dB, 4) ||
                 (T_saved && !aligned(T_saved, 4))))

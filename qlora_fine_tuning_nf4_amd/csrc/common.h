@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 #define QL_DEV __device__ __forceinline__
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -13,9 +15,23 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 namespace ql {
 
-constexpr int kBlock = 64;    // weights per first-level block
+constexpr int kBlock = 64;    // weights per first-level block (and per storage unit)
 constexpr int kGroup = 256;   // block scales per second-level group
 constexpr int kWave = 64;
+
+// Per-unit storage of each weight format (WFmt, kernels.h): each 64-weight
+// unit (one row, 64 consecutive k) is stored at the NF4 block position
+// (blk_pos); per unit:
+//   kFmtNf4Dq  32 code bytes, an 8-bit scale; an fp32 constant per 256 units
+//   kFmtNf4    32 code bytes, the fp32 absmax
+//   kFmtU4     32 code bytes (uint4, NF4 packing), fp32 scale and zero-point
+//   kFmtQ8     64 int8 bytes, two fp16 scales (elements 0-31, 32-63)
+template <int FMT>
+struct FmtInfo {
+  static constexpr bool nf4 = FMT == kFmtNf4Dq || FMT == kFmtNf4;     // decodes through the codebook
+  static constexpr int code_bytes = FMT == kFmtQ8 ? 64 : 32;         // per unit
+  static constexpr int param_bytes = FMT == kFmtNf4Dq ? 1 : (FMT == kFmtU4 ? 8 : 4);
+};
 
 // D[16x16] += A[16x32] * B[32x16], bf16 operands, fp32 accumulate.
 // Lane l holds A[l%16][8(l/16) .. +7], B[8(l/16) .. +7][l%16] and
@@ -38,6 +54,9 @@ QL_DEV __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes = 0x7FFF
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                           0x00020000);
 }
+// Byte count of a buffer resource, clamped to the 31-bit range that every
+// buffer offset here stays in.
+QL_DEV uint32_t rsrc_bytes(int64_t b) { return (uint32_t)(b < 0x7FFFFFFF ? b : 0x7FFFFFFF); }
 template <typename T>
 QL_DEV const QL_GLOBAL T* gptr(const T* p) {
   return (const QL_GLOBAL T*)p;
@@ -132,6 +151,33 @@ QL_DEV u32x4_t decode8(const Lut& t, uint32_t x) {
   o[2] = perm(hib, lob, 0x05010400u);
   o[3] = perm(hib, lob, 0x07030602u);
   return o;
+}
+
+// Q8_0: four int8 values (one packed word, element order) times the block
+// scale d, as two packed bf16 pairs.  Each byte is biased to unsigned
+// (q + 128, converted exactly by v_cvt_f32_ubyte) and fma(q + 128, d, -128 d)
+// forms q * d exactly (11 + 8 significant bits fit binary32), then one
+// rounding to bf16.
+QL_DEV u32x2_t decode_q8x4(uint32_t x, float d) {
+  const uint32_t u = x ^ 0x80808080u;
+  const float nb = -128.0f * d;
+  const float f0 = __builtin_fmaf((float)(u & 0xFFu), d, nb);
+  const float f1 = __builtin_fmaf((float)((u >> 8) & 0xFFu), d, nb);
+  const float f2 = __builtin_fmaf((float)((u >> 16) & 0xFFu), d, nb);
+  const float f3 = __builtin_fmaf((float)(u >> 24), d, nb);
+  return u32x2_t{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3)};
+}
+
+// 8 consecutive Q8_0 elements (two packed words) -> 4 packed bf16 pairs, in
+// the element order decode8 produces.
+QL_DEV u32x4_t decode_q8x8(uint32_t w0, uint32_t w1, float d) {
+  const u32x2_t a = decode_q8x4(w0, d), b = decode_q8x4(w1, d);
+  return u32x4_t{a[0], a[1], b[0], b[1]};
+}
+
+// fp16 bits -> fp32 (exact)
+QL_DEV float half_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
 // Storage position of the 64-block (n, kb) of an N-row weight with nkb blocks

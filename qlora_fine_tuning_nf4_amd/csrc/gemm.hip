@@ -1,9 +1,10 @@
 // Fused-dequant MFMA GEMMs of the quantized linear (large-M regime):
 //   forward   Y  = X  deq(W)^T (+ LoRA term)    contraction over k
 //   backward  dX = dY deq(W)   (+ LoRA term)    contraction over n
-// The 4-bit weight is decoded to bf16 inside the kernel and lives only in
-// registers and LDS (www.cf-1.com/news/5705389 §2.2, §4.2: block dequant in
-// the GEMM's outer loop, results kept in registers / shared memory;
+// The packed weight (NF4, asymmetric uint4 or Q8_0) is decoded to bf16 inside
+// the kernel and lives only in registers and LDS (www.cf-1.com/news/5705389
+// §2.2, §4.2: block dequant in the GEMM's outer loop, results kept in
+// registers / shared memory;
 // www.lqnn.cn/news/228537 §3.3: dequantize to 16 bits for the product, then
 // discard).
 //
@@ -17,10 +18,11 @@
 //    128-byte row pieces) into a 3-stage ring, two K-steps ahead.  16-byte
 //    chunks are XOR-swizzled by row so the MFMA fragment reads are free of
 //    bank conflicts.
-//  * The weight tile of each K-step (128 x 64 weights = 128 NF4 blocks) is
+//  * The weight tile of each K-step (128 x 64 weights = 128 storage units) is
 //    decoded by all 512 threads into a double-buffered LDS stage: the four
-//    lanes of a DPP quad share a block, build its 16-entry table together
-//    (broadcast with quad_perm) and decode 16 weights each.  The decode of
+//    lanes of a DPP quad share a unit and decode 16 weights each; for the
+//    4-bit formats they build its 16-entry table together (broadcast with
+//    quad_perm), Q8_0 bytes are scaled directly.  The decode of
 //    step s+1 is interleaved with the MFMAs of step s, one barrier per step;
 //    it is amortized over 256 output rows.
 //  * Forward reads B fragments with ds_read_b128 from the [n][k] stage; the
@@ -121,7 +123,7 @@ QL_DEV void k_barrier_issue() {
 // Physical 16-byte chunk of logical chunk c in activation row r of a stage.
 QL_DEV int a_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <bool DX, bool VEC, bool DQ>
+template <bool DX, bool VEC, int FMT>
 __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ act, Nf4View w,
                                                  const float* __restrict__ codebook, int64_t M,
                                                  LoraTerm lora, void* __restrict__ out, int out_bf16,
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
   const int s_begin = split * steps_per_split;
   const int s_end = min(nsteps, s_begin + steps_per_split);
 
-  if (tid < 16) s_lv[tid] = codebook[tid];
+  if (FmtInfo<FMT>::nf4 && tid < 16) s_lv[tid] = codebook[tid];
 
   // Decode role: group g decodes blocks [64g, 64g+64) of each step's 128; a
   // quad of lanes shares one block, lane q = tid & 3 decodes its elements
@@ -214,19 +216,23 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
   };
 
   struct WRaw {
-    u32x2_t codes;    // this lane's two packed words
-    uint32_t qbyte;   // the block's 8-bit scale
-    float step;
+    u32x4_t codes;    // this lane's 16 weights: words 0-1 (4-bit formats) or 0-3 (Q8_0)
+    uint32_t qbyte;   // NF4 with double quantization: the 8-bit scale; Q8_0: the two fp16 scales
+    float step;       // NF4: the group's fp32 constant, or the block absmax; uint4: the scale
+    float zp;         // uint4: the zero-point
   };
-  // This lane's block at step st.  Storage position (rows in groups of 16,
+  // This lane's unit at step st.  Storage position (rows in groups of 16,
   // k-block-major inside a group): forward fp0 + st * fR (fixed row; fR = 16
   // except in a partial last group), backward st * 64 * nkb plus a fixed part
   // whenever all 64 rows of the step are present.  Positions are taken
-  // relative to a per-step base in scalar registers; blocks outside the
+  // relative to a per-step base in scalar registers; units outside the
   // weight get an offset past the buffer end, so the hardware returns zeros
-  // (scale 0, hence decoded zeros).  Double-quantized (DQ): 8-bit scale at
-  // the storage position, fp32 constant of flat block b at step[b / 256].
-  // Single level: the fp32 absmax at the storage position in `step`.
+  // (scale 0, hence decoded zeros).  Per-unit data at the storage position:
+  // CB code bytes and PB parameter bytes (the 8-bit scale with double
+  // quantization, whose fp32 constant of flat block b sits at step[b / 256];
+  // the fp32 absmax; the uint4 scale and zero-point; the two Q8_0 scales).
+  using FI = FmtInfo<FMT>;
+  constexpr uint32_t CB = FI::code_bytes, PB = FI::param_bytes;
   constexpr uint32_t kOut = 0x80000000u;
   const int64_t kb_dx = o0 / kBlock + wcb;
   const int64_t fg0 = (o0 + wr) & ~int64_t(15);
@@ -235,14 +241,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
   const uint32_t f_prel = (uint32_t)((fg0 - o0) * nkb + (o0 + wr - fg0));   // fp0 - o0 * nkb
   const bool d_kok = kb_dx < nkb;
   const uint32_t d_prel = (uint32_t)((wr & ~15) * nkb + kb_dx * 16 + (wr & 15));
-  const uint32_t c_vo0 = DX ? (d_kok ? d_prel * 32 + q * 8 : kOut) : (f_ok ? f_prel * 32 + q * 8 : kOut);
-  const uint32_t q_vo0 = DX ? (d_kok ? d_prel : kOut) : (f_ok ? f_prel : kOut);
-  // single-level format: the fp32 scale at the block's storage position
-  const uint32_t s_vo0 = DX ? (d_kok ? d_prel * 4 : kOut) : (f_ok ? f_prel * 4 : kOut);
+  const uint32_t c_vo0 =
+      DX ? (d_kok ? d_prel * CB + q * (CB / 4) : kOut) : (f_ok ? f_prel * CB + q * (CB / 4) : kOut);
+  const uint32_t p_vo0 = DX ? (d_kok ? d_prel * PB : kOut) : (f_ok ? f_prel * PB : kOut);
   const uint32_t b_lane = (uint32_t)(DX ? wr * nkb + kb_dx : (o0 + wr) * nkb);
   const auto step_rsrc = buf_rsrc(w.step, (uint32_t)(((N * nkb + kGroup - 1) / kGroup) * 4));
   auto load_w = [&](int st, WRaw& r) {
-    uint32_t cvo, qvo, svo, bidx;
+    uint32_t cvo, pvo, bidx;
     int64_t pbase;   // storage position of the per-step (backward) or per-tile (forward) base
     if (DX) {
       const int64_t n0 = (int64_t)st * GBK;
@@ -250,33 +255,71 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       bidx = b_lane + (uint32_t)(n0 * nkb);
       if (st < full_steps) {
         cvo = c_vo0;
-        qvo = q_vo0;
-        svo = s_vo0;
+        pvo = p_vo0;
       } else {   // ragged last step: partial group and rows past N
         const int64_t g0 = (wr & ~15), R = min(int64_t(16), N - n0 - g0);
         const bool ok = d_kok && n0 + wr < N;
         const uint32_t prel = (uint32_t)(g0 * nkb + kb_dx * R + (wr & 15));
-        cvo = ok ? prel * 32 + q * 8 : kOut;
-        qvo = ok ? prel : kOut;
-        svo = ok ? prel * 4 : kOut;
+        cvo = ok ? prel * CB + q * (CB / 4) : kOut;
+        pvo = ok ? prel * PB : kOut;
       }
     } else {
       pbase = o0 * nkb;
-      cvo = c_vo0 + (uint32_t)st * fR * 32;
-      qvo = q_vo0 + (uint32_t)st * fR;
-      svo = s_vo0 + (uint32_t)st * fR * 4;
+      cvo = c_vo0 + (uint32_t)st * fR * CB;
+      pvo = p_vo0 + (uint32_t)st * fR * PB;
       bidx = b_lane + (uint32_t)st;
     }
-    r.codes = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(buf_rsrc(w.codes + pbase * 32), cvo, 0, 0));
-    if (DQ) {
-      r.qbyte = __builtin_amdgcn_raw_buffer_load_b8(buf_rsrc(w.qscale + pbase), qvo, 0, 0);
-      r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(step_rsrc, (bidx >> 8) * 4, 0, 0));
+    const auto crs = buf_rsrc(w.codes + pbase * CB);
+    if constexpr (FMT == kFmtQ8) {
+      r.codes = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, cvo, 0, 0));
+      r.qbyte = __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(w.qscale + pbase * 4), pvo, 0, 0);
     } else {
-      r.qbyte = 1u;   // scale = 1 * absmax, exact
-      r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(w.step + pbase), svo, 0, 0));
+      const u32x2_t c = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(crs, cvo, 0, 0));
+      r.codes = u32x4_t{c[0], c[1], 0u, 0u};
+      if constexpr (FMT == kFmtNf4Dq) {
+        r.qbyte = __builtin_amdgcn_raw_buffer_load_b8(buf_rsrc(w.qscale + pbase), pvo, 0, 0);
+        r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(step_rsrc, (bidx >> 8) * 4, 0, 0));
+      } else if constexpr (FMT == kFmtNf4) {
+        r.qbyte = 1u;   // scale = 1 * absmax, exact
+        r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(w.step + pbase), pvo, 0, 0));
+      } else {
+        // two dword loads (the backend merges them): a 64-bit buffer load
+        // whose halves are bit-cast to float is shrunk to one dword by this
+        // compiler, both halves then holding the scale
+        const auto prs = buf_rsrc(w.step + 2 * pbase);
+        r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, pvo, 0, 0));
+        r.zp = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, pvo + 4, 0, 0));
+      }
     }
   };
-  auto scale_of = [](const WRaw& r) { return (float)r.qbyte * r.step; };
+  float lvq[4] = {0.f, 0.f, 0.f, 0.f};   // NF4: level[4q + i] (set once the codebook is in LDS)
+  // Decode this lane's 16 weights into the stage: the 4-bit formats through a
+  // per-block table built by the quad (entries level[c] * s for NF4,
+  // (c - zp) * scale for uint4); Q8_0 bytes times the fp16 scale of the
+  // lane's 32-element half.
+  auto decode_to = [&](const WRaw& r, u32x4_t* dst) {
+    if constexpr (FMT == kFmtQ8) {
+      const float d = half_bits_to_float(q >= 2 ? r.qbyte >> 16 : r.qbyte & 0xFFFFu);
+      dst[0] = decode_q8x8(r.codes[0], r.codes[1], d);
+      dst[1] = decode_q8x8(r.codes[2], r.codes[3], d);
+    } else {
+      float lvr[4];
+      float sc;
+      if constexpr (FMT == kFmtU4) {
+        const int zp = (int)r.zp;   // c - zp formed as an integer: +0 at c == zp
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lvr[i] = (float)(4 * q + i - zp);
+        sc = r.step;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lvr[i] = lvq[i];
+        sc = (float)r.qbyte * r.step;
+      }
+      const Lut t = make_lut_quad(lvr, sc);
+      dst[0] = decode8(t, r.codes[0]);
+      dst[1] = decode8(t, r.codes[1]);
+    }
+  };
   auto wdst = [&](int stage) {
     return reinterpret_cast<u32x4_t*>(sW + stage * G::stage + wr * G::ld + wcb * 64 + q * 16);
   };
@@ -309,9 +352,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
   };
 
   __syncthreads();
-  float lvq[4];
+  if constexpr (FmtInfo<FMT>::nf4) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lvq[i] = s_lv[4 * q + i];
+    for (int i = 0; i < 4; ++i) lvq[i] = s_lv[4 * q + i];
+  }
 
   f32x16_t acc[2][4];
 #pragma unroll
@@ -334,10 +378,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       load_w(min(s_begin + 1, last), rw[1]);
       load_w(min(s_begin + 2, last), rw[2]);
       __builtin_amdgcn_s_waitcnt(0);       // (prologue only)
-      const Lut t = make_lut_quad(lvq, scale_of(wf));
-      u32x4_t* dst = wdst(0);
-      dst[0] = decode8(t, wf.codes[0]);
-      dst[1] = decode8(t, wf.codes[1]);
+      decode_to(wf, wdst(0));
       __syncthreads();
     }
     u32x4_t fa[2][2], fb[2][4];
@@ -359,12 +400,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     auto mem = [&](int st, auto PHc) {
       constexpr int PH = decltype(PHc)::value;   // (st - s_begin) % 3
       const int rel = st - s_begin;
-      const float sc = scale_of(rw[(PH + 1) % 3]);
       read_frags(sA + (rel % NA) * A_STAGE, sW + (rel & 1) * G::stage, fa, fb);
-      const Lut t = make_lut_quad(lvq, sc);
-      u32x4_t* dst = wdst((rel + 1) & 1);
-      dst[0] = decode8(t, rw[(PH + 1) % 3].codes[0]);
-      dst[1] = decode8(t, rw[(PH + 1) % 3].codes[1]);
+      decode_to(rw[(PH + 1) % 3], wdst((rel + 1) & 1));
       QL_LGKMCNT0();
       QL_VMCNT(0);
       __builtin_amdgcn_sched_barrier(0);
@@ -542,22 +579,38 @@ static constexpr size_t smem_bytes() {
   return sizeof(uint16_t) * NA * A_STAGE;   // dynamic part: the activation ring
 }
 
-template <bool DX, bool VEC, bool DQ>
+template <bool DX, bool VEC, int FMT>
 static hipError_t launch_one(dim3 grid, hipStream_t s, const uint16_t* act, const Nf4View& w,
                              const float* codebook, int64_t M, const LoraTerm& lora, void* out,
                              bool bf16, float* part, int ksplit, int per, int64_t mtiles,
                              int64_t otiles) {
   static bool attr_set = false;   // idempotent: the same value every time
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<DX, VEC, DQ>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<DX, VEC, FMT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)smem_bytes<DX>());
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemm<DX, VEC, DQ>), grid, dim3(512), smem_bytes<DX>(), s, act, w, codebook, M,
-                     lora, out, (int)bf16, part, ksplit, per, mtiles, otiles);
+  hipLaunchKernelGGL((k_gemm<DX, VEC, FMT>), grid, dim3(512), smem_bytes<DX>(), s, act, w, codebook,
+                     M, lora, out, (int)bf16, part, ksplit, per, mtiles, otiles);
   return hipGetLastError();
+}
+
+template <bool DX, bool VEC>
+static hipError_t launch_fmt(dim3 grid, hipStream_t s, const uint16_t* act, const Nf4View& w,
+                             const float* codebook, int64_t M, const LoraTerm& lora, void* out,
+                             bool bf16, float* part, int ksplit, int per, int64_t mtiles,
+                             int64_t otiles) {
+#define QL_ONE(F) \
+  launch_one<DX, VEC, F>(grid, s, act, w, codebook, M, lora, out, bf16, part, ksplit, per, mtiles, otiles)
+  switch (w.fmt) {
+    case kFmtNf4Dq: return QL_ONE(kFmtNf4Dq);
+    case kFmtNf4: return QL_ONE(kFmtNf4);
+    case kFmtU4: return QL_ONE(kFmtU4);
+    default: return QL_ONE(kFmtQ8);
+  }
+#undef QL_ONE
 }
 
 template <bool DX>
@@ -569,18 +622,15 @@ static hipError_t launch(const Nf4View& w, const float* codebook, const uint16_t
   const int per = (nsteps + ksplit - 1) / ksplit;
   const int64_t mtiles = (M + GBM - 1) / GBM, otiles = (O + GBN - 1) / GBN;
   const dim3 grid((unsigned)(mtiles * otiles * ksplit));
-  // the weight format (with or without double quantization) and 16-byte
-  // activation rows select the instantiation
-  const bool dq = w.qscale != nullptr;
-  if (!DX || C % 8 == 0)
-    return dq ? launch_one<DX, true, true>(grid, s, act, w, codebook, M, lora, out, bf16, part,
-                                           ksplit, per, mtiles, otiles)
-              : launch_one<DX, true, false>(grid, s, act, w, codebook, M, lora, out, bf16, part,
-                                            ksplit, per, mtiles, otiles);
-  return dq ? launch_one<DX, false, true>(grid, s, act, w, codebook, M, lora, out, bf16, part,
-                                          ksplit, per, mtiles, otiles)
-            : launch_one<DX, false, false>(grid, s, act, w, codebook, M, lora, out, bf16, part,
-                                           ksplit, per, mtiles, otiles);
+  // the weight format and 16-byte activation rows select the instantiation
+  // (the forward's contraction is a whole number of 64-blocks)
+  if constexpr (DX) {
+    if (C % 8 != 0)
+      return launch_fmt<DX, false>(grid, s, act, w, codebook, M, lora, out, bf16, part, ksplit,
+                                   per, mtiles, otiles);
+  }
+  return launch_fmt<DX, true>(grid, s, act, w, codebook, M, lora, out, bf16, part, ksplit, per,
+                              mtiles, otiles);
 }
 
 hipError_t launch_gemm_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,

@@ -1,5 +1,5 @@
 // Forward base product of the quantized linear, Y = X deq(W)^T (+ LoRA term),
-// with the 4-bit weight dequantized to bf16 inside the kernels and never
+// with the packed weight dequantized to bf16 inside the kernels and never
 // written to global memory (www.cf-1.com/news/5705389 §2.2 and §4.2: block
 // dequantization inside the GEMM, results kept in registers / shared memory;
 // www.lqnn.cn/news/228537 §3.3 and zky001 section 5.8: dequantize to 16 bits
@@ -7,9 +7,9 @@
 //
 // Small-M forward (the large-M GEMMs are in gemm.hip) and the split-K reduce.
 //  * k_gemv_fwd  -- small M (<= 32): a wave owns 16 weight rows and streams
-//    their packed bytes; each lane decodes a whole 64-block (one lookup table
-//    per block) and feeds eight MFMAs whose 32-wide contraction spans four
-//    different blocks.  The next block's codes, scale and activation
+//    their packed bytes; each lane decodes a whole 64-weight unit (one lookup
+//    table per 4-bit block; Q8_0 bytes times their fp16 scale) and feeds
+//    eight MFMAs whose 32-wide contraction spans four different units.  The next block's codes, scale and activation
 //    fragments are loaded while the current one is decoded.  One launch can
 //    cover a list of independent projections (grouped form).
 #include "common.h"
@@ -67,18 +67,19 @@ QL_DEV float lora_dot_v(const LoraTerm& L, int64_t m, int64_t c, bool vec) {
 // read from there by all four waves.  Three-deep rings (LDS chunks, code
 // registers) keep the loads of quad q+2 in flight while quad q is computed;
 // one barrier per quad.
-template <int MT>
+template <int FMT>
 struct GemvRaw {
-  u32x4_t c0, c1;   // packed words 0-3 and 4-7 of the lane's block
-  uint32_t qbyte;
-  float step;
+  u32x4_t c[FMT == kFmtQ8 ? 4 : 2];   // the lane's unit: 32 code bytes, or 64 int8 values
+  uint32_t qbyte;   // NF4 with double quantization: the 8-bit scale; Q8_0: the two fp16 scales
+  float step;       // NF4: the group's fp32 constant, or the block absmax; uint4: the scale
+  float zp;         // uint4: the zero-point
 };
 
 constexpr int GV_CHUNK_BYTES = 512;   // one row of an activation chunk: 256 bf16
 
 // XPW: activation-chunk DMA instructions per wave and quad (8 * XPW chunk
 // rows: XPW = 1 for M <= 8, 2 for M <= 16, 4 for M <= 32).
-template <int MT, int XPW, bool GROUPED, bool DQ>
+template <int MT, int XPW, bool GROUPED, int FMT>
 __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* __restrict__ jobs,
                                                   int njobs, const float* __restrict__ codebook,
                                                   int ksplit, int quads_per_split) {
@@ -121,9 +122,11 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
   const int q0 = split * quads_per_split;
   const int q1 = min(nquads, q0 + quads_per_split);
 
+  using FI = FmtInfo<FMT>;
+  constexpr int CB = FI::code_bytes, NC = CB / 16;   // code bytes per unit, 16-byte loads
   float lv[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) lv[i] = gptr(codebook)[i];
+  for (int i = 0; i < 16; ++i) lv[i] = FI::nf4 ? gptr(codebook)[i] : 0.f;
 
   // DMA of an activation chunk: instruction j covers chunk rows 2j, 2j+1;
   // instruction j is issued by wave j % 4.  Lane l writes LDS bytes
@@ -162,21 +165,36 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
   const uint32_t b_lane = (uint32_t)(nn * nkb + g);          // flat block index at q = 0
   const int64_t nblk = N * nkb;
   const auto step_rsrc = buf_rsrc(w.step, (uint32_t)(((nblk + kGroup - 1) / kGroup) * 4));
-  auto load_w = [&](int q, GemvRaw<MT>& u) {
+  // per-unit data at the storage position: CB code bytes, then the 8-bit
+  // scale (double quantization; the fp32 constant of flat block b at
+  // step[b / 256]), the fp32 absmax, the uint4 scale and zero-point, or the
+  // two Q8_0 scales
+  auto load_w = [&](int q, GemvRaw<FMT>& u) {
     const int qc = min(q, nquads - 1);
     const int64_t ub = gg * nkb + (int64_t)4 * qc * R;
-    const auto rc = buf_rsrc(w.codes + ub * 32, (uint32_t)((nblk - ub) * 32));
-    u.c0 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, w_lane * 32, 0, 0));
-    u.c1 = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, w_lane * 32 + 16, 0, 0));
-    if (DQ) {
-      const auto rq = buf_rsrc(w.qscale + ub, (uint32_t)(nblk - ub));
+    const auto rc = buf_rsrc(w.codes + ub * CB, rsrc_bytes((nblk - ub) * CB));
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+      u.c[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, w_lane * CB + 16 * j, 0, 0));
+    if constexpr (FMT == kFmtNf4Dq) {
+      const auto rq = buf_rsrc(w.qscale + ub, rsrc_bytes(nblk - ub));
       u.qbyte = __builtin_amdgcn_raw_buffer_load_b8(rq, w_lane, 0, 0);
       u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                              step_rsrc, ((b_lane + 4 * (uint32_t)qc) >> 8) * 4, 0, 0));
-    } else {   // single level: the fp32 absmax at the storage position
+    } else if constexpr (FMT == kFmtNf4) {
       u.qbyte = 1u;
       u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                             buf_rsrc(w.step + ub, (uint32_t)((nblk - ub) * 4)), w_lane * 4, 0, 0));
+                                             buf_rsrc(w.step + ub, rsrc_bytes((nblk - ub) * 4)), w_lane * 4, 0, 0));
+    } else if constexpr (FMT == kFmtU4) {
+      // two dword loads: a 64-bit buffer load whose halves are bit-cast to
+      // float is shrunk to one dword by this compiler, both halves then
+      // holding the scale
+      const auto prs = buf_rsrc(w.step + 2 * ub, rsrc_bytes((nblk - ub) * 8));
+      u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, w_lane * 8, 0, 0));
+      u.zp = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, w_lane * 8 + 4, 0, 0));
+    } else {
+      u.qbyte = __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(w.qscale + 4 * ub, rsrc_bytes((nblk - ub) * 4)),
+                                                     w_lane * 4, 0, 0);
     }
   };
 
@@ -184,11 +202,8 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int q, int stage, const GemvRaw<MT>& u) {
+  auto compute = [&](int q, int stage, const GemvRaw<FMT>& u) {
     const bool ok = nok && 4 * q + g < nkb;
-    const float scr = (float)u.qbyte * u.step;
-    const float sc = ok ? scr : 0.f;
-    const Lut t = make_lut(lv, sc);
     const uint16_t* sx = stage_ptr(stage);
     u32x4_t af[MT][8];
 #pragma unroll
@@ -199,19 +214,47 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
         af[mt][i] = *reinterpret_cast<const u32x4_t*>(sx + row * 256 + ((8 * g + i) ^ (row & 15)) * 8);
     }
     __builtin_amdgcn_sched_barrier(0);   // the fragment reads go out before the decode
+    if constexpr (FMT == kFmtQ8) {
+      // elements 8i .. 8i+7 are bytes 8i .. 8i+7: words 2i, 2i+1 of the unit
+      const float d0 = ok ? half_bits_to_float(u.qbyte & 0xFFFFu) : 0.f;
+      const float d1 = ok ? half_bits_to_float(u.qbyte >> 16) : 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4_t bf = decode8(t, i < 4 ? u.c0[i] : u.c1[i - 4]);
+      for (int i = 0; i < 8; ++i) {
+        const u32x4_t& cw = u.c[i >> 1];
+        const u32x4_t bf = decode_q8x8(cw[2 * (i & 1)], cw[2 * (i & 1) + 1], i < 4 ? d0 : d1);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt][i & 1] = mfma16x16x32(af[mt][i], bf, acc[mt][i & 1]);
+        for (int mt = 0; mt < MT; ++mt) acc[mt][i & 1] = mfma16x16x32(af[mt][i], bf, acc[mt][i & 1]);
+      }
+    } else {
+      float lvu[16];   // table levels: NF4 levels, or c - zp for uint4
+      float scr;
+      if constexpr (FMT == kFmtU4) {
+        const int zp = (int)u.zp;   // c - zp formed as an integer: +0 at c == zp
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lvu[i] = (float)(i - zp);
+        scr = u.step;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lvu[i] = lv[i];
+        scr = (float)u.qbyte * u.step;
+      }
+      const Lut t = make_lut(lvu, ok ? scr : 0.f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const u32x4_t bf = decode8(t, u.c[i >> 2][i & 3]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt][i & 1] = mfma16x16x32(af[mt][i], bf, acc[mt][i & 1]);
+      }
     }
   };
 
   // wait for this wave's loads of quad q (everything but the loads issued in
-  // the following iteration: 4 code loads (3 without double quantization) +
-  // XPW chunk loads), then barrier
+  // the following iteration: NC code loads, one or two parameter loads and
+  // XPW chunk loads), then barrier.  The uint4 pair counts as one load: the
+  // backend may merge its two dword loads, and where it does not, the count
+  // only waits for one load of the next quad as well.
   auto wait_q = [&]() {
-    QL_VMCNT((DQ ? 4 : 3) + XPW);
+    QL_VMCNT(NC + (FMT == kFmtNf4Dq ? 2 : 1) + XPW);
     QL_LGKMCNT0();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -219,7 +262,7 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
   };
 
   if (q0 < q1) {
-    GemvRaw<MT> rw[3];
+    GemvRaw<FMT> rw[3];
     load_w(q0, rw[0]);
     load_x(q0, 0);
     load_w(q0 + 1, rw[1]);
@@ -280,47 +323,46 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, 
   store_out(out, out_bf16, idx, v);
 }
 
+template <int MT, int XPW, bool GROUPED>
+static void gemv_launch(int fmt, dim3 grid, hipStream_t s, const GemvJob& job1, const GemvJob* jobs,
+                        int njobs, const float* codebook, int ksplit, int per) {
+#define QL_GEMV(F)                                                                              \
+  hipLaunchKernelGGL((k_gemv_fwd<MT, XPW, GROUPED, F>), grid, dim3(256), 0, s, job1, jobs, njobs, \
+                     codebook, ksplit, per)
+  switch (fmt) {
+    case kFmtNf4Dq: QL_GEMV(kFmtNf4Dq); break;
+    case kFmtNf4: QL_GEMV(kFmtNf4); break;
+    case kFmtU4: QL_GEMV(kFmtU4); break;
+    default: QL_GEMV(kFmtQ8); break;
+  }
+#undef QL_GEMV
+}
+
+template <bool GROUPED>
+static void gemv_launch_m(int64_t M, int fmt, dim3 grid, hipStream_t s, const GemvJob& job1,
+                          const GemvJob* jobs, int njobs, const float* codebook, int ksplit, int per) {
+  // M <= 32, checked by the caller
+  if (M <= 8) gemv_launch<1, 1, GROUPED>(fmt, grid, s, job1, jobs, njobs, codebook, ksplit, per);
+  else if (M <= 16) gemv_launch<1, 2, GROUPED>(fmt, grid, s, job1, jobs, njobs, codebook, ksplit, per);
+  else gemv_launch<2, 4, GROUPED>(fmt, grid, s, job1, jobs, njobs, codebook, ksplit, per);
+}
+
 hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,
                            const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
                            hipStream_t s) {
   const int64_t nquads = (w.k / kBlock + 3) / 4;
   const int per = (int)((nquads + ksplit - 1) / ksplit);
   const GemvJob job{X, w, lora, Y, part, M, (int)y_bf16, 0};
-  dim3 grid((unsigned)((w.n + 63) / 64), (unsigned)ksplit);
-#define QL_GEMV(MT, XPW)                                                                     \
-  do {                                                                                       \
-    if (w.qscale)                                                                            \
-      hipLaunchKernelGGL((k_gemv_fwd<MT, XPW, false, true>), grid, dim3(256), 0, s, job,   \
-                         nullptr, 0, codebook, ksplit, per);                                 \
-    else                                                                                     \
-      hipLaunchKernelGGL((k_gemv_fwd<MT, XPW, false, false>), grid, dim3(256), 0, s, job,  \
-                         nullptr, 0, codebook, ksplit, per);                                 \
-  } while (0)
-  // M <= 32, checked by the caller
-  if (M <= 8) QL_GEMV(1, 1);
-  else if (M <= 16) QL_GEMV(1, 2);
-  else QL_GEMV(2, 4);
-#undef QL_GEMV
+  const dim3 grid((unsigned)((w.n + 63) / 64), (unsigned)ksplit);
+  gemv_launch_m<false>(M, w.fmt, grid, s, job, nullptr, 0, codebook, ksplit, per);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_grouped(const GemvJob* jobs, int njobs, int64_t row_groups, int64_t M,
-                               const float* codebook, int64_t max_quads, bool dq, hipStream_t s) {
-  dim3 grid((unsigned)row_groups, 1);
+                               const float* codebook, int64_t max_quads, int fmt, hipStream_t s) {
+  const dim3 grid((unsigned)row_groups, 1);
   const GemvJob none{};
-#define QL_GEMV(MT, XPW)                                                                     \
-  do {                                                                                       \
-    if (dq)                                                                                  \
-      hipLaunchKernelGGL((k_gemv_fwd<MT, XPW, true, true>), grid, dim3(256), 0, s, none,    \
-                         jobs, njobs, codebook, 1, (int)max_quads);                          \
-    else                                                                                     \
-      hipLaunchKernelGGL((k_gemv_fwd<MT, XPW, true, false>), grid, dim3(256), 0, s, none,   \
-                         jobs, njobs, codebook, 1, (int)max_quads);                          \
-  } while (0)
-  if (M <= 8) QL_GEMV(1, 1);
-  else if (M <= 16) QL_GEMV(1, 2);
-  else QL_GEMV(2, 4);
-#undef QL_GEMV
+  gemv_launch_m<true>(M, fmt, grid, s, none, jobs, njobs, codebook, 1, (int)max_quads);
   return hipGetLastError();
 }
 

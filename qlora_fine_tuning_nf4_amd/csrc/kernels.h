@@ -6,6 +6,9 @@
 
 namespace ql {
 
+// Weight formats as the kernels see them (a template parameter of each kernel).
+enum WFmt : int { kFmtNf4Dq = 0, kFmtNf4 = 1, kFmtU4 = 2, kFmtQ8 = 3 };
+
 // LoRA term added by epilogues:  out[m][c] += scaling * sum_j L[m*r + j] * R[c*rs_c + j*rs_j]
 struct LoraTerm {
   const float* L;      // [M x r] fp32 (T in the forward, U in the backward), or nullptr
@@ -15,19 +18,23 @@ struct LoraTerm {
   float scaling;
 };
 
-// Packed weight.  qscale == nullptr: single-level format, `step` then holds
-// the fp32 absmax of every block at its storage position.
+// Packed weight; fmt is a WFmt (common.h) and says what the arrays hold:
+//   kFmtNf4Dq  codes, qscale (8-bit), step (fp32 per 256 units)
+//   kFmtNf4    codes, step (fp32 absmax per unit); qscale unused
+//   kFmtU4     codes, step (fp32 scale, zero-point per unit); qscale unused
+//   kFmtQ8     codes (int8), qscale (two fp16 per unit); step unused
 struct Nf4View {
   const uint8_t* codes;
   const uint8_t* qscale;
   const float* step;
   int64_t n, k;
+  int fmt;
 };
 
 hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* codes,
-                           uint8_t* qscale, float* step, int64_t n, int64_t k, hipStream_t s);
-hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          const float* codebook, uint16_t* out, int64_t n, int64_t k, hipStream_t s);
+                           uint8_t* qscale, float* step, int64_t n, int64_t k, int fmt,
+                           hipStream_t s);
+hipError_t launch_dequant(const Nf4View& w, const float* codebook, uint16_t* out, hipStream_t s);
 
 // Forward base product Y = X deq(W)^T (+ LoRA term), tiled MFMA GEMM.
 // ksplit > 1 writes fp32 partials part[ksplit][M][N] and leaves the epilogue
@@ -53,11 +60,11 @@ hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16
                            const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
                            hipStream_t s);
 // Grouped small-M forward: one launch over `njobs` device-resident jobs that
-// share M and the weight format (dq: double-quantized scales), covering
-// `row_groups` 64-row workgroups in total; no split of the contraction.
-// max_quads: the largest k/256 (rounded up) over the jobs.
+// share M and the weight format `fmt` (a WFmt), covering `row_groups` 64-row
+// workgroups in total; no split of the contraction.  max_quads: the largest
+// k/256 (rounded up) over the jobs.
 hipError_t launch_gemv_grouped(const GemvJob* jobs, int njobs, int64_t row_groups, int64_t M,
-                               const float* codebook, int64_t max_quads, bool dq, hipStream_t s);
+                               const float* codebook, int64_t max_quads, int fmt, hipStream_t s);
 // dX = dY deq(W) (+ LoRA term), contraction over n; nsplit > 1 -> partials.
 hipError_t launch_gemm_dx(const Nf4View& w, const float* codebook, const uint16_t* dY, int64_t M,
                           const LoraTerm& lora, void* dX, bool dx_bf16, float* part, int nsplit,

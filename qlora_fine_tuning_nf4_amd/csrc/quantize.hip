@@ -1,5 +1,6 @@
 // Block-wise NF4 quantization with double quantization of the block scales,
-// and the dense dequantization used for checking and adapter merging.
+// the alternate block formats (asymmetric uint4, Q8_0), and the dense
+// dequantization used for checking and adapter merging.
 //
 // Format (news.rkmt.cn/news/4821 §1.2, §1.3, §2.2, §2.3; zky001 section 5.8
 // "NF4" and "double quantization"): 64-element blocks scaled by their absmax,
@@ -187,55 +188,180 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
   }
 }
 
-// Dense dequantization: one thread per 64-block, 8 x 16-byte stores.  Without
-// double quantization (qscale NULL) the scale is the stored fp32 absmax.
-__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
-                                                 const uint8_t* __restrict__ qscale,
-                                                 const float* __restrict__ step,
-                                                 const float* __restrict__ codebook,
-                                                 uint16_t* __restrict__ out, int64_t N,
-                                                 int64_t nkb) {
-  const int64_t nblocks = N * nkb;
-  __shared__ float s_lv[16];
-  if (threadIdx.x < 16) s_lv[threadIdx.x] = codebook[threadIdx.x];
-  __syncthreads();
-  float lv[16];
+// Asymmetric uint4 (news.rkmt.cn/news/4821 §1.3, §2.1; kwkr.cn/news/627310
+// §2.1): per 64-block, the range widened to hold 0, scale = (hi - lo) / 15,
+// zero-point = rint(-lo / scale) in [0, 15] (an fp32 integer value, never
+// -0), q = clamp(rint(x / scale) + zp, 0, 15); an all-zero block gets scale
+// 0, zp 0 and codes 0.  Every division is the correctly rounded binary32 one.
+// Eight lanes per 64-weight unit (16-byte loads, eight weights each), one
+// unit per lane group; codes packed as the NF4 codes, (scale, zp) at the
+// unit's storage position.
+__global__ __launch_bounds__(256) void k_quant_u4(const uint16_t* __restrict__ W,
+                                                  uint8_t* __restrict__ codes,
+                                                  float* __restrict__ params, int64_t N,
+                                                  int64_t nkb) {
+  const uint32_t nunits = (uint32_t)(N * nkb), ukb = (uint32_t)nkb;
+  const int lane8 = threadIdx.x & 7;
+  const uint32_t u = blockIdx.x * 32u + (threadIdx.x >> 3);
+  if (u >= nunits) return;   // whole lane groups leave together
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + (int64_t)u * kBlock + lane8 * 8);
+  float x[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) lv[i] = s_lv[i];
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = bf16_lo(v[j]);
+    x[2 * j + 1] = bf16_hi(v[j]);
+  }
+  float lo = 0.f, hi = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    lo = fminf(lo, x[j]);
+    hi = fmaxf(hi, x[j]);
+  }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o));
+    hi = fmaxf(hi, __shfl_xor(hi, o));
+  }
+  const float sc = (hi - lo) / 15.0f;
+  const bool live = sc > 0.f;
+  const int zp = live ? (int)fminf(fmaxf(rintf(-lo / sc), 0.f), 15.f) : 0;
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = live ? min(max((int)rintf(x[j] / sc) + zp, 0), 15) : 0;
+    word |= (uint32_t)q << (j < 4 ? 8 * j : 8 * (j - 4) + 4);
+  }
+  const uint32_t row = u / ukb;
+  const int64_t p = blk_pos(row, u - row * ukb, N, nkb);
+  reinterpret_cast<uint32_t*>(codes)[p * 8 + lane8] = word;
+  if (lane8 == 0) reinterpret_cast<float2*>(params)[p] = make_float2(live ? sc : 0.f, (float)zp);
+}
+
+// Q8_0 (www.cf-1.com/news/5705389 §1.1, §2.2; kwkr.cn/news/627310 §2.1): per
+// 32-block, d16 = fp16_rne(fp32(absmax / 127)), q = clamp(rint(x / d16), -127,
+// 127), 0 when d16 is 0.  Eight lanes per 64-weight unit, four per block;
+// 64 int8 codes and the two fp16 scales at the unit's storage position.
+__global__ __launch_bounds__(256) void k_quant_q8(const uint16_t* __restrict__ W,
+                                                  uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ scales, int64_t N,
+                                                  int64_t nkb) {
+  const uint32_t nunits = (uint32_t)(N * nkb), ukb = (uint32_t)nkb;
+  const int lane8 = threadIdx.x & 7;
+  const uint32_t u = blockIdx.x * 32u + (threadIdx.x >> 3);
+  if (u >= nunits) return;
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + (int64_t)u * kBlock + lane8 * 8);
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = bf16_lo(v[j]);
+    x[2 * j + 1] = bf16_hi(v[j]);
+  }
+  float am = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, __shfl_xor(am, 2));
+  const _Float16 h = (_Float16)(am / 127.0f);
+  const float d = (float)h;
+  uint32_t b[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = d != 0.f ? min(max((int)rintf(x[j] / d), -127), 127) : 0;
+    b[j >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (j & 3));
+  }
+  const uint32_t row = u / ukb;
+  const int64_t p = blk_pos(row, u - row * ukb, N, nkb);
+  *reinterpret_cast<u32x2_t*>(codes + p * 64 + lane8 * 8) = u32x2_t{b[0], b[1]};
+  if ((lane8 & 3) == 0)
+    reinterpret_cast<uint16_t*>(scales)[p * 2 + (lane8 >> 2)] = __builtin_bit_cast(uint16_t, h);
+}
+
+// Dense dequantization: one thread per 64-weight unit, 8 x 16-byte stores.
+// The 4-bit formats go through a per-block table (NF4: level[c] times the
+// block scale; uint4: (c - zp) times the scale), Q8_0 bytes are scaled
+// directly.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_dequant(Nf4View w, const float* __restrict__ codebook,
+                                                 uint16_t* __restrict__ out) {
+  const int64_t N = w.n, nkb = w.k / kBlock, nblocks = N * nkb;
+  __shared__ float s_lv[16];
+  if (FmtInfo<FMT>::nf4 && threadIdx.x < 16) s_lv[threadIdx.x] = codebook[threadIdx.x];
+  __syncthreads();
   const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= nblocks) return;
   const int64_t p = blk_pos(b / nkb, b % nkb, N, nkb);
-  const Lut t = make_lut(lv, qscale ? block_scale(qscale, step, b, p) : step[p]);
-  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(codes + p * 32);
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + b * kBlock);
+  if constexpr (FMT == kFmtQ8) {
+    const uint16_t* sc = reinterpret_cast<const uint16_t*>(w.qscale) + p * 2;
+    const float d0 = half_bits_to_float(sc[0]), d1 = half_bits_to_float(sc[1]);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w.codes + p * 64);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const u32x4_t w = src[h];
+    for (int h = 0; h < 4; ++h) {
+      const u32x4_t c = src[h];
+      dst[2 * h] = decode_q8x8(c[0], c[1], h < 2 ? d0 : d1);
+      dst[2 * h + 1] = decode_q8x8(c[2], c[3], h < 2 ? d0 : d1);
+    }
+  } else {
+    float lv[16];
+    float s;
+    if constexpr (FMT == kFmtU4) {
+      const float2 sz = reinterpret_cast<const float2*>(w.step)[p];
+      const int zp = (int)sz.y;   // c - zp is formed exactly as an integer (c == zp gives +0)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dst[h * 4 + j] = decode8(t, w[j]);
+      for (int i = 0; i < 16; ++i) lv[i] = (float)(i - zp);
+      s = sz.x;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lv[i] = s_lv[i];
+      s = FMT == kFmtNf4Dq ? block_scale(w.qscale, w.step, b, p) : w.step[p];
+    }
+    const Lut t = make_lut(lv, s);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w.codes + p * 32);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4_t c = src[h];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[h * 4 + j] = decode8(t, c[j]);
+    }
   }
 }
 
 hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* codes,
-                           uint8_t* qscale, float* step, int64_t n, int64_t k, hipStream_t s) {
-  const int64_t nkb = k / kBlock, ngroups = (n * nkb + kGroup - 1) / kGroup;
-  // persistent workgroups (each walks groups with a stride of the grid), a
-  // few per CU so loads of the next group overlap the current one
+                           uint8_t* qscale, float* step, int64_t n, int64_t k, int fmt,
+                           hipStream_t s) {
+  const int64_t nkb = k / kBlock, nunits = n * nkb, ngroups = (nunits + kGroup - 1) / kGroup;
+  // NF4: persistent workgroups (each walks groups with a stride of the grid),
+  // a few per CU so loads of the next group overlap the current one
   const int64_t grid = std::min<int64_t>((ngroups + 7) / 8 * 8, 256 * 8);   // multiple of 8
-  if (qscale)
-    hipLaunchKernelGGL(k_quant_nf4_dq<true>, dim3((unsigned)grid), dim3(256), 0, s, W, codebook,
-                       codes, qscale, step, n, nkb);
-  else
-    hipLaunchKernelGGL(k_quant_nf4_dq<false>, dim3((unsigned)grid), dim3(256), 0, s, W, codebook,
-                       codes, qscale, step, n, nkb);
+  const dim3 ugrid((unsigned)((nunits + 31) / 32));                         // 32 units per workgroup
+  switch (fmt) {
+    case kFmtNf4Dq:
+      hipLaunchKernelGGL(k_quant_nf4_dq<true>, dim3((unsigned)grid), dim3(256), 0, s, W, codebook,
+                         codes, qscale, step, n, nkb);
+      break;
+    case kFmtNf4:
+      hipLaunchKernelGGL(k_quant_nf4_dq<false>, dim3((unsigned)grid), dim3(256), 0, s, W, codebook,
+                         codes, qscale, step, n, nkb);
+      break;
+    case kFmtU4:
+      hipLaunchKernelGGL(k_quant_u4, ugrid, dim3(256), 0, s, W, codes, step, n, nkb);
+      break;
+    default:
+      hipLaunchKernelGGL(k_quant_q8, ugrid, dim3(256), 0, s, W, codes, qscale, n, nkb);
+      break;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          const float* codebook, uint16_t* out, int64_t n, int64_t k, hipStream_t s) {
-  const int64_t nkb = k / kBlock, nblocks = n * nkb;
-  hipLaunchKernelGGL(k_dequant, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, s, codes,
-                     qscale, step, codebook, out, n, nkb);
+hipError_t launch_dequant(const Nf4View& w, const float* codebook, uint16_t* out, hipStream_t s) {
+  const int64_t nblocks = w.n * (w.k / kBlock);
+  const dim3 grid((unsigned)((nblocks + 255) / 256));
+  switch (w.fmt) {
+    case kFmtNf4Dq: hipLaunchKernelGGL(k_dequant<kFmtNf4Dq>, grid, dim3(256), 0, s, w, codebook, out); break;
+    case kFmtNf4: hipLaunchKernelGGL(k_dequant<kFmtNf4>, grid, dim3(256), 0, s, w, codebook, out); break;
+    case kFmtU4: hipLaunchKernelGGL(k_dequant<kFmtU4>, grid, dim3(256), 0, s, w, codebook, out); break;
+    default: hipLaunchKernelGGL(k_dequant<kFmtQ8>, grid, dim3(256), 0, s, w, codebook, out); break;
+  }
   return hipGetLastError();
 }
 

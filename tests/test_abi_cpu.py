@@ -8,7 +8,7 @@ import re
 import numpy as np
 import pytest
 
-from oracle import nf4
+from oracle import formats, nf4
 from qlora_fine_tuning_nf4_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -79,8 +79,49 @@ def test_strerror_covers_codes():
 FAKE = 0x100000   # never dereferenced: every call below fails validation first
 
 
-def _desc(n=64, k=128, codes=FAKE, qs=FAKE, st=FAKE):
-    return B._Nf4Desc(n, k, codes, qs, st)
+def _desc(n=64, k=128, codes=FAKE, qs=FAKE, st=FAKE, fmt=0):
+    return B._Nf4Desc(n, k, codes, qs, st, fmt)
+
+
+@pytest.mark.parametrize("n,k", [(1, 64), (3, 128), (3072, 8192), (8192, 3072), (257, 320)])
+def test_weight_bytes_match_oracle_formats(n, k):
+    assert B.qlora_weight_bytes(B.QLORA_FMT_NF4, n, k) == nf4.nf4_bytes(n, k)
+    c, p = formats.u4_bytes(n, k)
+    assert B.qlora_weight_bytes(B.QLORA_FMT_U4_ASYM, n, k) == (c, 0, p)
+    c, s = formats.q8_bytes(n, k)
+    assert B.qlora_weight_bytes(B.QLORA_FMT_Q8_0, n, k) == (c, s, 0)
+    L = B.lib()
+    z = ctypes.c_size_t()
+    assert L.qlora_weight_bytes(3, n, k, ctypes.byref(z), None, None) == 8
+    assert L.qlora_weight_bytes(-1, n, k, ctypes.byref(z), None, None) == 8
+    assert L.qlora_weight_bytes(1, n, 100, ctypes.byref(z), None, None) == 2
+
+
+def test_format_argument_errors():
+    """Per-format arrays, alignments and the codebook (NF4 only), all checked
+    before any HIP call."""
+    L = B.lib()
+    U4, Q8 = B.QLORA_FMT_U4_ASYM, B.QLORA_FMT_Q8_0
+
+    def q(d, W=FAKE, cb=FAKE):
+        return L.qlora_quantize(W, cb, ctypes.byref(d), None)
+    assert q(_desc(fmt=3)) == 8
+    assert q(_desc(fmt=-1)) == 8
+    assert q(_desc(fmt=U4)) == 8                        # uint4 takes no qscale
+    assert q(_desc(fmt=U4, qs=0, st=0)) == 1
+    assert q(_desc(fmt=U4, qs=0, st=FAKE + 4)) == 3     # (scale, zp) pairs: 8-byte aligned
+    assert q(_desc(fmt=U4, qs=0, k=96)) == 2
+    assert q(_desc(fmt=U4, qs=0), cb=None, W=FAKE + 2) == 3   # no codebook needed
+    assert q(_desc(fmt=Q8, qs=0)) == 1
+    assert q(_desc(fmt=Q8, qs=FAKE + 2)) == 3           # fp16 pairs: 4-byte aligned
+    assert q(_desc(fmt=Q8, st=0), cb=None, W=FAKE + 2) == 3   # step unused, no codebook
+    assert q(_desc(fmt=0), cb=None) == 1                 # NF4 needs the codebook
+    assert q(_desc(fmt=0), cb=FAKE + 2) == 3
+    assert L.qlora_dequantize(ctypes.byref(_desc(fmt=Q8, st=0)), None, FAKE + 8, None) == 3
+    assert L.qlora_dequantize(ctypes.byref(_desc(fmt=0)), None, FAKE, None) == 1
+    assert _fwd(L, _desc(fmt=U4, qs=0), cb=None, X=FAKE + 2) == 3
+    assert _fwd(L, _desc(fmt=U4), cb=None) == 8
+    assert _fwd(L, _desc(fmt=0), cb=None) == 1
 
 
 def test_quantize_argument_errors():
@@ -152,8 +193,8 @@ def test_bwd_argument_errors():
     assert bwd(ws=None) == 6
 
 
-def _job(n=64, k=128, X=FAKE, A=FAKE, Bp=FAKE, r=8, Y=FAKE, T=FAKE, codes=FAKE, qs=FAKE):
-    return B._FwdJob(_desc(n, k, codes=codes, qs=qs), X, A, Bp, r, 2.0, Y, T)
+def _job(n=64, k=128, X=FAKE, A=FAKE, Bp=FAKE, r=8, Y=FAKE, T=FAKE, codes=FAKE, qs=FAKE, fmt=0):
+    return B._FwdJob(_desc(n, k, codes=codes, qs=qs, fmt=fmt), X, A, Bp, r, 2.0, Y, T)
 
 
 def test_group_table_bytes():
@@ -191,16 +232,23 @@ def test_group_init_argument_errors():
     assert init([ok, _job(Y=FAKE + 8)]) == 3
     assert init([ok, _job(qs=0)]) == 8            # one weight format per group
     assert init([_job(qs=0), ok]) == 8
+    assert init([ok, _job(fmt=B.QLORA_FMT_Q8_0)]) == 8
+    assert init([_job(fmt=B.QLORA_FMT_U4_ASYM, qs=0), _job(fmt=B.QLORA_FMT_Q8_0)]) == 8
+    assert init([ok, _job(fmt=7)]) == 8
 
 
 def test_grouped_fwd_argument_errors():
     L = B.lib()
     assert L.qlora_linear_fwd_grouped(None, FAKE, None) == 1
-    def grp(count=2, lora_count=0, m=1):
-        return B._Group(table=FAKE, count=count, lora_count=lora_count, max_r=0, y_dtype=1, dq=1,
-                        m=m, row_groups=8, max_quads=1)
+    def grp(count=2, lora_count=0, m=1, variant=0):
+        return B._Group(table=FAKE, count=count, lora_count=lora_count, max_r=0, y_dtype=1,
+                        variant=variant, m=m, row_groups=8, max_quads=1)
     g = grp()
     assert L.qlora_linear_fwd_grouped(ctypes.byref(g), None, None) == 1
+    bad = grp(variant=4)
+    assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
+    bad = grp(variant=-1)
+    assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
     bad = grp(count=0)
     assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
     bad = grp(m=33)
