@@ -22,6 +22,11 @@ Other workloads (--workload), each printing its own line of the same form:
               with 0.1 % of the weights scaled x20); GB/s against HBM peak.
   layer70b    the same layer, fwd + bwd at M = 4096 with LoRA r = 16,
               alpha = 32 on all seven; TFLOP/s against bf16 MFMA peak.
+  layer3.8b   3.8B-style layer linears (hidden 3072, intermediate 8192: q, k,
+              v, o 3072x3072; gate, up 8192x3072; down 3072x8192), fwd + bwd
+              at M = 4096 (seq 4096) with LoRA r = 64, alpha = 128 on all
+              seven, weights in the --format block format (q8_0, u4_asym or
+              nf4); TFLOP/s against bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -521,6 +526,147 @@ def run_layer70b(args):
     return out
 
 
+PROJ38 = [("q", 3072, 3072), ("k", 3072, 3072), ("v", 3072, 3072), ("o", 3072, 3072),
+          ("gate", 8192, 3072), ("up", 8192, 3072), ("down", 3072, 8192)]
+FORMAT_NAMES = {"q8_0": "Q8_0 (32 int8 + fp16 scale per 32)",
+                "u4_asym": "asymmetric uint4 (fp32 scale + zero-point per 64)",
+                "nf4": "NF4 + double quantization"}
+
+
+def format_bytes(fmt, N, K):
+    """Packed bytes of an N x K weight in block format `fmt`."""
+    if fmt == "q8_0":
+        return N * K + 2 * (N * K // 32)
+    if fmt == "u4_asym":
+        return N * K // 2 + 8 * (N * K // 64)
+    return packed_bytes(N, K)
+
+
+def cpu_baseline_layer38(fmt, sample_tokens):
+    """The oracle on a bounded sample of the 3.8B-style layer: all seven
+    projections at the first `sample_tokens` tokens, dequantize + forward +
+    backward in float64 numpy (quantization outside the timed part)."""
+    from threadpoolctl import threadpool_info
+
+    import synth
+    from oracle import formats as ofmt
+    from oracle import linear as olin
+    from oracle import nf4 as onf4
+
+    lv, mid = onf4.codebook()
+    M, r, s = sample_tokens, 64, 128 / 64
+    total_flops, elapsed = 0, 0.0
+    for i, (name, N, K) in enumerate(PROJ38):
+        W = synth.normal_bf16((N, K), 0.02, synth.tensor_seed(5, 10 * i))
+        X = synth.normal_bf16((M, K), 1.0, synth.tensor_seed(5, 10 * i + 1))
+        dY = synth.normal_bf16((M, N), 1.0, synth.tensor_seed(5, 10 * i + 2))
+        A = synth.normal_bf16((r, K), 0.01, synth.tensor_seed(5, 10 * i + 3))
+        B = synth.normal_bf16((N, r), 0.01, synth.tensor_seed(5, 10 * i + 4))
+        if fmt == "q8_0":
+            qv, d16 = ofmt.q8_quantize(W)
+            deq = lambda: ofmt.q8_dequantize(qv, d16).reshape(N, K)   # noqa: E731
+        elif fmt == "u4_asym":
+            c, sc, zp = ofmt.u4_quantize(W)
+            deq = lambda: ofmt.u4_dequantize(c, sc, zp).reshape(N, K)   # noqa: E731
+        else:
+            c, qs, st = onf4.quantize(W, mid)
+            deq = lambda: onf4.dequantize(c, qs, st, lv).reshape(N, K)   # noqa: E731
+        t0 = time.perf_counter()
+        olin.forward(deq(), X, A, B, s)
+        olin.backward(deq(), X, dY, A, B, s)
+        elapsed += time.perf_counter() - t0
+        total_flops += flops_fwd(M, N, K, r) + flops_bwd(M, N, K, r)
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    return {"value": round(total_flops / elapsed / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"all 7 projections at M={M} of the 4096 tokens: dequantize + fwd + bwd "
+                      f"in float64 numpy ({elapsed:.1f} s)"}
+
+
+def run_layer38(args):
+    import torch
+
+    import synth
+    from qlora_fine_tuning_nf4_amd import binding as QB
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fmt = args.format
+    fcode = QB.FORMATS[fmt]
+    cb = QB.device_codebook(dev) if fmt == "nf4" else None
+    M, r, alpha = 4096, 64, 128
+    s = alpha / r
+    layers = []
+    for i, (name, N, K) in enumerate(PROJ38):
+        W = synth.device_normal_bf16((N, K), 0.02, synth.tensor_seed(5, 10 * i), device=dev)
+        q = QB.qlora_quantize(W, cb, double_quant=DQ, fmt=fcode)
+        del W
+        L = dict(N=N, K=K, q=q)
+        L["X"] = synth.device_normal_bf16((M, K), 1.0, synth.tensor_seed(5, 10 * i + 1), device=dev)
+        L["dY"] = synth.device_normal_bf16((M, N), 1.0, synth.tensor_seed(5, 10 * i + 2), device=dev)
+        L["A"] = synth.device_normal_bf16((r, K), 0.01, synth.tensor_seed(5, 10 * i + 3), device=dev)
+        L["B"] = synth.device_normal_bf16((N, r), 0.01, synth.tensor_seed(5, 10 * i + 4), device=dev)
+        L["Y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        L["T"] = torch.empty((M, r), dtype=torch.float32, device=dev)
+        L["dX"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        L["dA"] = torch.empty((r, K), dtype=torch.float32, device=dev)
+        L["dB"] = torch.empty((N, r), dtype=torch.float32, device=dev)
+        nws = max(QB.qlora_workspace_bytes(0, M, N, K, r), QB.qlora_workspace_bytes(1, M, N, K, r), 16)
+        L["ws"] = torch.empty(nws, dtype=torch.uint8, device=dev)
+        layers.append(L)
+    torch.cuda.synchronize()
+
+    def step():
+        for L in layers:
+            QB.qlora_linear_fwd(L["q"], cb, L["X"], L["A"], L["B"], s, out=L["Y"], T_out=L["T"],
+                                workspace=L["ws"])
+            QB.qlora_linear_bwd(L["q"], cb, L["X"], L["dY"], L["A"], L["B"], s, T=L["T"],
+                                dX_out=L["dX"], dA_out=L["dA"], dB_out=L["dB"], workspace=L["ws"])
+    wall, gpu, steps_ms = _timed(step, args.steps, args.warmup)
+    flops = sum(flops_fwd(M, L["N"], L["K"], r) + flops_bwd(M, L["N"], L["K"], r) for L in layers)
+    tf = flops / wall / 1e12
+
+    # the fused-dequant GEMMs alone (LoRA off: one launch per call), timed with
+    # HIP events on the stream they run on
+    def gemm_only(dx):
+        def f():
+            for L in layers:
+                if dx:
+                    QB.qlora_linear_bwd(L["q"], cb, None, L["dY"], dX_out=L["dX"], workspace=L["ws"])
+                else:
+                    QB.qlora_linear_fwd(L["q"], cb, L["X"], out=L["Y"], workspace=L["ws"])
+        return f
+    kf = 2 * M * sum(L["N"] * L["K"] for L in layers)
+    _, gf, _ = _timed(gemm_only(False), args.steps, args.warmup)
+    _, gd, _ = _timed(gemm_only(True), args.steps, args.warmup)
+    tf_f, tf_d = kf / gf / 1e12, kf / gd / 1e12
+    kname, ach, t_k = ("k_gemm_dx", tf_d, gd) if gd >= gf else ("k_gemm_fwd", tf_f, gf)
+    out = {
+        "metric": METRIC, "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4),
+        "gpu_event_ms_per_step": round(gpu * 1e3, 4), "gpu_step_ms": _spread(steps_ms),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": f"synthetic (seeded N(0,0.02) weights in {FORMAT_NAMES[fmt]}; N(0,1) activations)",
+        "config": {"workload": "3.8B-style layer linears (q,k,v,o 3072x3072; gate,up 8192x3072; down "
+                               "3072x8192), M=4096 tokens (seq 4096), LoRA r=64 alpha=128 on all "
+                               f"seven, fwd+bwd, weights {FORMAT_NAMES[fmt]}",
+                   "M": M, "r": r, "alpha": alpha, "format": fmt,
+                   "double_quant": DQ if fmt == "nf4" else None,
+                   "packed_bytes": sum(L["q"].nbytes() for L in layers),
+                   "parallelism": "none (1 GPU)"},
+        "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(ach, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "avg_launch_us": round(t_k / len(layers) * 1e6, 2),
+                     "traffic": None,
+                     "other_gemm": {"k_gemm_fwd": round(tf_f, 1), "k_gemm_dx": round(tf_d, 1)}},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_layer38(fmt, args.cpu_sample_tokens // 6)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -532,7 +678,9 @@ def main():
                          "no CPU baseline (the oracle baselines time the double-quantized format)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=768)
     ap.add_argument("--workload", default="layer7b",
-                    choices=["layer7b", "decode", "quantize70b", "layer70b"])
+                    choices=["layer7b", "decode", "quantize70b", "layer70b", "layer3.8b"])
+    ap.add_argument("--format", default="q8_0", choices=["q8_0", "u4_asym", "nf4"],
+                    help="weight block format of the layer3.8b workload")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only; --gpus must be 1 "
@@ -544,7 +692,7 @@ def main():
         args.no_cpu_baseline = True
 
     run = {"layer7b": run_layer7b, "decode": run_decode, "quantize70b": run_quantize70b,
-           "layer70b": run_layer70b}[args.workload]
+           "layer70b": run_layer70b, "layer3.8b": run_layer38}[args.workload]
     out = run(args)
     print(json.dumps(out), flush=True)
 
