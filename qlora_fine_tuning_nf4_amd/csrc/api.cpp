@@ -93,8 +93,14 @@ int plan_dx_split(int64_t m, int64_t n, int64_t k) {
   return tiles >= 192 ? 1 : (int)std::min<int64_t>(cap, cdiv(256, tiles));
 }
 
-// the adapter-gradient kernel reduces 128 rows per workgroup
-int plan_wgrad_split(int64_t m, int64_t c, int r) { return (int)cdiv(m, 128); }
+// adapter-gradient splits over the rows: enough workgroups (tiles of 128
+// columns x 32 or 64 ranks, times the splits) to fill the chip twice over,
+// each split at least one 64-row chunk
+int plan_wgrad_split(int64_t m, int64_t c, int r) {
+  const int64_t jw = r <= 32 ? 32 : 64;
+  const int64_t tiles = cdiv(c, 128) * cdiv(std::max(r, 1), jw);
+  return (int)std::min<int64_t>(std::max<int64_t>(1, cdiv(512, tiles)), cdiv(m, 64));
+}
 
 struct FwdWs {
   size_t t_off, part_off, total;

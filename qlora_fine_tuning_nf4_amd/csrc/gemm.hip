@@ -512,32 +512,72 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
 
   // ---- epilogue.  LoRA term (ksplit == 1): out += (scaling * L) R^T on the
   // matrix cores, 16 ranks per MFMA step; the fp32 factor scaling * L is
-  // split into bf16 hi + lo parts so the product keeps fp32 accuracy.
+  // split into bf16 hi + lo parts so the product keeps fp32 accuracy.  The
+  // operands of each 16-rank chunk are fetched without branches (indices
+  // clamped into the matrices, values past the rank masked to zero), as
+  // 16-byte loads where the layout allows, and the next chunk's fetch is
+  // issued before the current chunk's MFMAs.
   if (ksplit == 1 && lora.r > 0) {
-    for (int j0 = 0; j0 < lora.r; j0 += 16) {
-      // B fragments: R[o][j0 + 8*lg + e] (the rank index is the contraction)
+    const int r = lora.r;
+    int64_t orow[2], mrow[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) orow[j] = min(o0 + 32 * (nt0 + j) + lr, O - 1);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) mrow[mt] = min(m0 + wm * 64 + 32 * mt + lr, M - 1);
+    const bool rvec = lora.rs_j == 1 && r % 8 == 0 && (lora.rs_c % 8) == 0 &&
+                      (reinterpret_cast<uintptr_t>(lora.R) & 15) == 0;
+    const bool lvec = r % 8 == 0 && (reinterpret_cast<uintptr_t>(lora.L) & 15) == 0;
+    struct Ops {
+      u32x4_t rb[2];      // R[o][jb .. jb+7], bf16 pairs
+      f32x4_t lv[2][2];   // L[m][jb .. jb+7]
+    };
+    // this lane's ranks of the chunk at j0: jb .. jb+7, jb = j0 + 8 lg
+    auto fetch = [&](int j0, Ops& op) {
+      const int jb = j0 + 8 * lg;
+      const int jc = min(jb, r - 8 > 0 ? r - 8 : 0);   // vector start kept inside the row
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (rvec) {
+          op.rb[j] = *reinterpret_cast<const u32x4_t*>(lora.R + orow[j] * lora.rs_c + jc);
+        } else {
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            h[e] = lora.R[orow[j] * lora.rs_c + (int64_t)min(jb + e, r - 1) * lora.rs_j];
+          op.rb[j] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const float* lp = lora.L + mrow[mt] * r;
+        if (lvec) {
+          op.lv[mt][0] = *reinterpret_cast<const f32x4_t*>(lp + jc);
+          op.lv[mt][1] = *reinterpret_cast<const f32x4_t*>(lp + jc + 4);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) op.lv[mt][e >> 2][e & 3] = lp[min(jb + e, r - 1)];
+        }
+      }
+    };
+    auto apply = [&](int j0, const Ops& op) {
+      const int jb = j0 + 8 * lg;
+      // ranks past r read a clamped element: zero both factors' share
       u32x4_t rb[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int64_t o = min(o0 + 32 * (nt0 + j) + lr, O - 1);
-        uint32_t h[8];
+        rb[j] = op.rb[j];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int jj = j0 + 8 * lg + e;
-          h[e] = jj < lora.r ? lora.R[o * lora.rs_c + (int64_t)jj * lora.rs_j] : 0u;
+        for (int e = 0; e < 4; ++e) {
+          const bool k0 = jb + 2 * e < r, k1 = jb + 2 * e + 1 < r;
+          rb[j][e] = (k0 ? rb[j][e] & 0xFFFFu : 0u) | (k1 ? rb[j][e] & 0xFFFF0000u : 0u);
         }
-        rb[j] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
       }
-      // A fragments: s * L[m][j], split into bf16 hi + lo (exact to 2^-16)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const int64_t m = min(m0 + wm * 64 + 32 * mt + lr, M - 1);
         float tv[8], lo[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int jj = j0 + 8 * lg + e;
-          tv[e] = jj < lora.r ? lora.scaling * lora.L[m * lora.r + jj] : 0.f;
-        }
+        for (int e = 0; e < 8; ++e)
+          tv[e] = jb + e < r ? lora.scaling * op.lv[mt][e >> 2][e & 3] : 0.f;
         u32x4_t ahi, alo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -551,6 +591,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
           fin[mt][j] = mfma32(ahi, rb[j], fin[mt][j]);
           fin[mt][j] = mfma32(alo, rb[j], fin[mt][j]);
         }
+      }
+    };
+    // two operand sets in turn (a copy of a set still in flight would wait)
+    Ops opa, opb;
+    fetch(0, opa);
+    for (int j0 = 0; j0 < r; j0 += 32) {
+      const bool two = j0 + 16 < r;
+      if (two) fetch(j0 + 16, opb);
+      apply(j0, opa);
+      if (two) {
+        if (j0 + 32 < r) fetch(j0 + 32, opa);
+        apply(j0 + 16, opb);
       }
     }
   }

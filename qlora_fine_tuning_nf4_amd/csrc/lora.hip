@@ -15,18 +15,21 @@ QL_DEV u32x4_t load8_guard(const uint16_t* row, int64_t c, int64_t C, bool vec) 
   return u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
 }
 
-// out[m][j] = sum_c P[m][c] Q[j][c]: an output tile of `rows` (16, or 8 so
-// that a few thousand rows still spread over every compute unit) x 16 ranks
-// per workgroup of 16 waves; wave w takes the 32-wide contraction slices w,
-// w+16, ... and keeps four independent accumulators (four loads in flight);
-// the 16 partial tiles are summed in a fixed order through LDS.  bf16
-// products are exact, sums fp32.
-constexpr int RD_WAVES = 16;
-template <bool GROUPED>
-__global__ __launch_bounds__(1024) void k_rowdot(const uint16_t* __restrict__ P,
-                                                 const uint16_t* __restrict__ Q, int64_t M,
-                                                 int64_t C, int r, float* __restrict__ out,
-                                                 const RowdotJob* __restrict__ jobs, int rows) {
+// out[m][j] = sum_c P[m][c] Q[j][c]: a workgroup of 8 waves owns `rows`
+// rows (16, or 8 so that a few thousand rows still spread over every compute
+// unit) and all r ranks, in RT tiles of 16.  Wave w takes the 32-wide
+// contraction slices w, w+8, ..., U at a time (all U slices' loads are issued
+// before their MFMAs, so many loads are in flight per wave); per slice it
+// loads the rows' fragment once and one fragment per rank tile, and feeds RT
+// MFMAs 16x16x32, so P is read once whatever the rank.  The 8 partial tiles
+// are summed in a fixed order through LDS.  bf16 products are exact, sums
+// fp32.
+constexpr int RD_WAVES = 8;
+template <int RT, bool GROUPED>
+__global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
+                                                const uint16_t* __restrict__ Q, int64_t M,
+                                                int64_t C, int r, float* __restrict__ out,
+                                                const RowdotJob* __restrict__ jobs, int rows) {
   if constexpr (GROUPED) {
     const RowdotJob& J = jobs[blockIdx.z];
     P = J.P;
@@ -34,39 +37,53 @@ __global__ __launch_bounds__(1024) void k_rowdot(const uint16_t* __restrict__ P,
     out = J.out;
     C = J.C;
     r = J.r;
-    if ((int)blockIdx.y * 16 >= r) return;
   }
-  __shared__ f32x4_t s_red[RD_WAVES][64];
+  __shared__ f32x4_t s_red[RD_WAVES - 1][RT][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t m = (int64_t)blockIdx.x * rows + (lane & 15);
-  const int64_t j = (int64_t)blockIdx.y * 16 + (lane & 15);
-  const int g = lane >> 4;
+  const int li = lane & 15, g = lane >> 4;
+  const int64_t m = (int64_t)blockIdx.x * rows + li;
+  const bool mok = li < rows && m < M;
   const bool vec = (C % 8) == 0;
-  const bool mok = (lane & 15) < rows && m < M, jok = j < r;
-  f32x4_t acc[4];
+  const uint16_t* prow = P + (mok ? m : 0) * C;
+  f32x4_t acc[RT];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int64_t stride = 32 * RD_WAVES;
-  for (int64_t c0 = wave * 32; c0 < C; c0 += 4 * stride) {
-    u32x4_t a[4], b[4];
+  for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  constexpr int U = RT <= 2 ? 6 : (RT == 4 ? 4 : 2);   // slices per round (register budget)
+  constexpr int64_t stride = 32 * RD_WAVES;
+  for (int64_t c0 = wave * 32; c0 < C; c0 += U * stride) {
+    u32x4_t a[U], b[U][RT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int64_t c = c0 + u * stride + g * 8;
-      a[u] = mok ? load8_guard(P + m * C, c, C, vec) : u32x4_t{0u, 0u, 0u, 0u};
-      b[u] = jok ? load8_guard(Q + j * C, c, C, vec) : u32x4_t{0u, 0u, 0u, 0u};
+      a[u] = mok ? load8_guard(prow, c, C, vec) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int j = 16 * t + li;
+        b[u][t] = j < r ? load8_guard(Q + (int64_t)j * C, c, C, vec) : u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = mfma16x16x32(a[u], b[u], acc[u]);
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[t] = mfma16x16x32(a[u], b[u][t], acc[t]);
   }
-  s_red[wave][lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) s_red[wave - 1][t][lane] = acc[t];
+  }
   __syncthreads();
   if (wave != 0) return;
-  f32x4_t v = s_red[0][lane];
-  for (int w = 1; w < RD_WAVES; ++w) v += s_red[w][lane];
+  for (int w = 0; w < RD_WAVES - 1; ++w)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int64_t mm = (int64_t)blockIdx.x * rows + g * 4 + e;
-    if (g * 4 + e < rows && mm < M && jok) out[mm * r + j] = v[e];
+    for (int t = 0; t < RT; ++t) acc[t] += s_red[w][t][lane];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int j = 16 * t + li;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t mm = (int64_t)blockIdx.x * rows + g * 4 + e;
+      if (g * 4 + e < rows && mm < M && j < r) out[mm * r + j] = acc[t][e];
+    }
   }
 }
 
@@ -78,98 +95,152 @@ __global__ void k_transpose_bf16(const uint16_t* __restrict__ Q, int N, int r,
   if (n < N) Qt[(int64_t)j * N + n] = Q[(int64_t)n * r + j];
 }
 
-// Partial weight gradient over a slice of WG_ROWS rows m:
-//   part[split][j][c] = sum_{m in slice} Q[m][j] * P[m][c]
-// A workgroup owns 128 columns (two per lane) and eight ranks j (blockIdx.z);
-// the slice's Q values (128 rows x 8 ranks) are staged in LDS and read back as
-// broadcasts; wave w takes rows [32w, 32w+32) with all 32 P loads issued
-// before the FMAs, and the four wave partials are summed through LDS in a
-// fixed order.
-constexpr int WG_ROWS = 128;
+QL_DEV u32x2_t ds_tr16(const uint16_t* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Weight gradient of the adapter on the matrix cores:
+//   out = scaling * sum_m Q[m][j] P[m][c]   (P bf16 [M x C], Q fp32 [M x r])
+// written as out[j][c] ([r x C]) or, transposed, out[c][j] ([C x r]); with
+// msplit > 1 split s writes its unscaled sum over rows
+// [s * rows_per_split, +rows_per_split) to part[s][j][c] for k_wgrad_reduce.
+// A workgroup of 4 waves owns 32*JT ranks x 128 columns and walks its rows
+// in chunks of 64.  Each chunk of P (64 x 128 bf16) and of Q (64 x 32*JT
+// fp32, split into bf16 parts hi = bf16(q) and lo = bf16(q - hi), which
+// carry q to about 2^-16) is staged in LDS; the contraction m runs down the
+// stage rows, so wave w reads its 32 columns of P and every rank tile of Q
+// with the transposing ds_read_b64_tr_b16 and accumulates the hi and lo
+// products with MFMA 32x32x16 (bf16 products exact, sums fp32).  The next
+// chunk's global loads are issued before the current chunk's MFMAs.  320- and
+// 192-byte stage rows keep the 4-row footprints of a transposing read on
+// disjoint banks.
+constexpr int WG_CHUNK = 64;
+template <int JT>
 __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ P,
                                                const float* __restrict__ Q, int64_t M, int64_t C,
                                                int r, float scaling, float* __restrict__ out,
                                                int transpose_out, float* __restrict__ part,
                                                int msplit, int rows_per_split) {
-  __shared__ float s_red[3][8][128];
-  __shared__ __attribute__((aligned(16))) float sQ[WG_ROWS][8];
+  constexpr int JW = 32 * JT;              // ranks per workgroup tile
+  constexpr int LDP = 128 + 32;            // stage pitches (bf16 elements)
+  constexpr int LDQ = JW + 32;
+  constexpr int QV = JW / 4;               // float4 pieces per Q chunk row
+  constexpr int QPASS = WG_CHUNK * QV / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t sP[WG_CHUNK * LDP];
+  __shared__ __attribute__((aligned(16))) uint16_t sQh[WG_CHUNK * LDQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sQl[WG_CHUNK * LDQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cl = lane * 2;                                  // local column pair
-  const int64_t c = (int64_t)blockIdx.x * 128 + cl;
+  const int64_t c0 = (int64_t)blockIdx.x * 128;
   const int split = blockIdx.y;
-  const int j0 = blockIdx.z * 8;
-  const int64_t mb = (int64_t)split * rows_per_split + wave * 32;
-  {
-    // 1024 values, 4 per thread: row tid/2, ranks 4*(tid&1) .. +3
-    const int row = tid >> 1, jq = (tid & 1) * 4;
-    const int64_t m = (int64_t)split * rows_per_split + row;
+  const int j0 = blockIdx.z * JW;
+  const int64_t m_begin = (int64_t)split * rows_per_split;
+  const int64_t m_end = min(M, m_begin + rows_per_split);
+  const bool pvec = (C % 8) == 0;
+  const bool qvec = (r % 4) == 0 && (reinterpret_cast<uintptr_t>(Q) & 15) == 0;
+
+  // this thread's pieces of a chunk: P rows (tid >> 4) + 16 i, columns
+  // 8 (tid & 15); Q rows (tid / QV) + (256 / QV) i, ranks 4 (tid % QV)
+  const int p_row = tid >> 4, p_col = 8 * (tid & 15);
+  const int q_row = tid / QV, q_j = 4 * (tid % QV);
+  u32x4_t pr[4];
+  f32x4_t qr[QPASS];
+  auto load = [&](int64_t mb) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      sQ[row][jq + e] = (m < M && j0 + jq + e < r) ? Q[m * r + j0 + jq + e] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = mb + p_row + 16 * i;
+      pr[i] = m < m_end ? load8_guard(P + m * C, c0 + p_col, C, pvec) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < QPASS; ++i) {
+      const int64_t m = mb + q_row + (256 / QV) * i;
+      const int j = j0 + q_j;
+      f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (m < m_end) {
+        const float* qp = Q + m * r + j;
+        if (qvec && j + 4 <= r) {
+          v = *reinterpret_cast<const f32x4_t*>(qp);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = j + e < r ? qp[e] : 0.f;
+        }
+      }
+      qr[i] = v;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4_t*>(sP + (p_row + 16 * i) * LDP + p_col) = pr[i];
+#pragma unroll
+    for (int i = 0; i < QPASS; ++i) {
+      const f32x4_t v = qr[i];
+      const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
+      const uint32_t l01 = pack_bf16x2(v[0] - bf16_lo(h01), v[1] - bf16_hi(h01));
+      const uint32_t l23 = pack_bf16x2(v[2] - bf16_lo(h23), v[3] - bf16_hi(h23));
+      const int o = (q_row + (256 / QV) * i) * LDQ + q_j;
+      *reinterpret_cast<u32x2_t*>(sQh + o) = u32x2_t{h01, h23};
+      *reinterpret_cast<u32x2_t*>(sQl + o) = u32x2_t{l01, l23};
+    }
+  };
+
+  f32x16_t acc[JT];
+#pragma unroll
+  for (int t = 0; t < JT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+
+  // transposing fragment read: contraction rows 16 kk .. +15, 32 columns
+  // from `col`
+  const int G16 = lane >> 4, i16 = lane & 15;
+  auto frag = [&](const uint16_t* st, int ld, int kk, int col) {
+    const int row = 16 * kk + 8 * (G16 >> 1) + (i16 >> 2);
+    const int cc = col + 16 * (G16 & 1) + 4 * (i16 & 3);
+    const u32x2_t lo = ds_tr16(st + row * ld + cc);
+    const u32x2_t hi = ds_tr16(st + (row + 4) * ld + cc);
+    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  };
+
+  if (m_begin < m_end) load(m_begin);
+  for (int64_t mb = m_begin; mb < m_end; mb += WG_CHUNK) {
+    store();
+    __syncthreads();
+    if (mb + WG_CHUNK < m_end) load(mb + WG_CHUNK);
+#pragma unroll
+    for (int kk = 0; kk < WG_CHUNK / 16; ++kk) {
+      const u32x4_t b = frag(sP, LDP, kk, 32 * wave);
+#pragma unroll
+      for (int t = 0; t < JT; ++t) {
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, frag(sQh, LDQ, kk, 32 * t)), __builtin_bit_cast(bf16x8_t, b),
+            acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, frag(sQl, LDQ, kk, 32 * t)), __builtin_bit_cast(bf16x8_t, b),
+            acc[t], 0, 0, 0);
+      }
+    }
+    __syncthreads();
   }
-  const bool pair = (C % 2) == 0 && c + 1 < C;
-  float acc0[8], acc1[8];
+
+  // D[8(i/4) + 4(l/32) + i%4][l%32]: rank rows, column lanes
+  const int64_t c = c0 + 32 * wave + (lane & 31);
 #pragma unroll
-  for (int t = 0; t < 8; ++t) acc0[t] = acc1[t] = 0.f;
-  uint32_t pv[32];
+  for (int t = 0; t < JT; ++t)
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int64_t m = mb + i;
-    uint32_t v = 0;
-    if (m < M && c < C) {
-      if (pair)
-        v = *reinterpret_cast<const uint32_t*>(P + m * C + c);
+    for (int i = 0; i < 16; ++i) {
+      const int j = j0 + 32 * t + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (j >= r || c >= C) continue;
+      const float v = acc[t][i];
+      if (msplit > 1)
+        part[((int64_t)split * r + j) * C + c] = v;
+      else if (transpose_out)
+        out[c * r + j] = scaling * v;
       else
-        v = (uint32_t)P[m * C + c] | (c + 1 < C ? (uint32_t)P[m * C + c + 1] << 16 : 0u);
+        out[(int64_t)j * C + c] = scaling * v;
     }
-    pv[i] = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float p0 = bf16_lo(pv[i]), p1 = bf16_hi(pv[i]);
-    const f32x4_t qa = *reinterpret_cast<const f32x4_t*>(&sQ[wave * 32 + i][0]);
-    const f32x4_t qb = *reinterpret_cast<const f32x4_t*>(&sQ[wave * 32 + i][4]);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      acc0[t] += qa[t] * p0;
-      acc1[t] += qa[t] * p1;
-      acc0[4 + t] += qb[t] * p0;
-      acc1[4 + t] += qb[t] * p1;
-    }
-  }
-  if (wave > 0) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      s_red[wave - 1][t][cl] = acc0[t];
-      s_red[wave - 1][t][cl + 1] = acc1[t];
-    }
-  }
-  __syncthreads();
-  if (wave != 0 || c >= C) return;
-#pragma unroll
-  for (int w = 0; w < 3; ++w)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      acc0[t] += s_red[w][t][cl];
-      acc1[t] += s_red[w][t][cl + 1];
-    }
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int j = j0 + t;
-    if (j >= r) break;
-    if (msplit > 1) {
-      float* dst = part + ((int64_t)split * r + j) * C + c;
-      dst[0] = acc0[t];
-      if (c + 1 < C) dst[1] = acc1[t];
-    } else if (transpose_out) {
-      out[c * r + j] = scaling * acc0[t];
-      if (c + 1 < C) out[(c + 1) * r + j] = scaling * acc1[t];
-    } else {
-      out[(int64_t)j * C + c] = scaling * acc0[t];
-      if (c + 1 < C) out[(int64_t)j * C + c + 1] = scaling * acc1[t];
-    }
-  }
 }
 
 __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ part, int msplit,
@@ -196,21 +267,30 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ 
     out[idx] = scaling * v;
 }
 
+template <bool GROUPED>
+static void rowdot_launch(int max_r, dim3 grid, hipStream_t s, const uint16_t* P, const uint16_t* Q,
+                          int64_t M, int64_t C, int r, float* out, const RowdotJob* jobs, int rows) {
+#define QL_RD(RT) \
+  hipLaunchKernelGGL((k_rowdot<RT, GROUPED>), grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out, jobs, rows)
+  if (max_r <= 16) QL_RD(1);
+  else if (max_r <= 32) QL_RD(2);
+  else if (max_r <= 64) QL_RD(4);
+  else QL_RD(8);
+#undef QL_RD
+}
+
 hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
                          float* out, hipStream_t s) {
   // 8-row tiles when 16-row tiles would leave compute units idle
-  const int rows = ((M + 15) / 16) * ((r + 15) / 16) < 512 ? 8 : 16;
-  dim3 grid((unsigned)((M + rows - 1) / rows), (unsigned)((r + 15) / 16));
-  hipLaunchKernelGGL(k_rowdot<false>, grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out,
-                     nullptr, rows);
+  const int rows = (M + 15) / 16 < 256 ? 8 : 16;
+  rowdot_launch<false>(r, dim3((unsigned)((M + rows - 1) / rows)), s, P, Q, M, C, r, out, nullptr, rows);
   return hipGetLastError();
 }
 
 hipError_t launch_rowdot_grouped(const RowdotJob* jobs, int njobs, int64_t M, int max_r,
                                  hipStream_t s) {
-  dim3 grid((unsigned)((M + 15) / 16), (unsigned)((max_r + 15) / 16), (unsigned)njobs);
-  hipLaunchKernelGGL(k_rowdot<true>, grid, dim3(64 * RD_WAVES), 0, s, nullptr, nullptr, M,
-                     int64_t(0), 0, nullptr, jobs, 16);
+  rowdot_launch<true>(max_r, dim3((unsigned)((M + 15) / 16), 1, (unsigned)njobs), s, nullptr, nullptr,
+                      M, int64_t(0), 0, nullptr, jobs, 16);
   return hipGetLastError();
 }
 
@@ -220,13 +300,24 @@ hipError_t launch_transpose_bf16(const uint16_t* Q, int64_t N, int r, uint16_t* 
   return hipGetLastError();
 }
 
+int wgrad_rows_per_split(int64_t M, int msplit) {
+  const int64_t per = (M + msplit - 1) / msplit;
+  return (int)((per + WG_CHUNK - 1) / WG_CHUNK * WG_CHUNK);
+}
+
 hipError_t launch_wgrad(const uint16_t* P, const float* Q, int64_t M, int64_t C, int r,
                         float scaling, float* out, bool transpose_out, float* part, int msplit,
                         hipStream_t s) {
-  const int rows = WG_ROWS;   // msplit == ceil(M / WG_ROWS), chosen by the caller
-  dim3 grid((unsigned)((C + 127) / 128), (unsigned)msplit, (unsigned)((r + 7) / 8));
-  hipLaunchKernelGGL(k_wgrad, grid, dim3(256), 0, s, P, Q, M, C, r, scaling, out,
-                     (int)transpose_out, part, msplit, rows);
+  // splits of whole 64-row chunks; a split past the rows writes a zero partial
+  const int rows = wgrad_rows_per_split(M, msplit);
+  const int jt = r <= 32 ? 1 : 2;
+  dim3 grid((unsigned)((C + 127) / 128), (unsigned)msplit, (unsigned)((r + 32 * jt - 1) / (32 * jt)));
+  if (jt == 1)
+    hipLaunchKernelGGL(k_wgrad<1>, grid, dim3(256), 0, s, P, Q, M, C, r, scaling, out,
+                       (int)transpose_out, part, msplit, rows);
+  else
+    hipLaunchKernelGGL(k_wgrad<2>, grid, dim3(256), 0, s, P, Q, M, C, r, scaling, out,
+                       (int)transpose_out, part, msplit, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || msplit == 1) return e;
   const int64_t total = (int64_t)r * C;
