@@ -110,7 +110,12 @@ FwdWs fwd_ws(int64_t m, int64_t n, int64_t k, int r, int path) {
   FwdWs w;
   w.t_off = 0;
   w.part_off = up16(sizeof(float) * (size_t)(m * r));
-  w.total = w.part_off + (p.ksplit > 1 ? sizeof(float) * (size_t)p.ksplit * m * n : 0);
+  // the region after T holds the GEMM's split partials, and before the GEMM
+  // runs the rank projection's split partials
+  const int rs = r > 0 ? ql::rowdot_splits(m, k, r) : 1;
+  const size_t gemm_part = p.ksplit > 1 ? sizeof(float) * (size_t)p.ksplit * m * n : 0;
+  const size_t rd_part = rs > 1 ? sizeof(float) * (size_t)rs * m * r : 0;
+  w.total = w.part_off + std::max(gemm_part, rd_part);
   return w;
 }
 
@@ -125,10 +130,14 @@ BwdWs bwd_ws(int64_t m, int64_t n, int64_t k, int r) {
   w.dx_off = w.bt_off + up16(sizeof(uint16_t) * (size_t)(r * n));
   const int ns = plan_dx_split(m, n, k);
   w.wg_off = w.dx_off + up16(ns > 1 ? sizeof(float) * (size_t)ns * m * k : 0);
+  // the last region holds the adapter-gradient split partials, and before
+  // those run the rank projections' split partials (U over n, T over k)
   size_t wg = 0;
   if (r > 0) {
     const int s1 = plan_wgrad_split(m, k, r), s2 = plan_wgrad_split(m, n, r);
     wg = sizeof(float) * std::max((size_t)s1 * r * k * (s1 > 1), (size_t)s2 * r * n * (s2 > 1));
+    const int ru = ql::rowdot_splits(m, n, r), rt = ql::rowdot_splits(m, k, r);
+    wg = std::max(wg, sizeof(float) * (size_t)std::max(ru * (ru > 1), rt * (rt > 1)) * m * r);
   }
   w.total = w.wg_off + up16(wg);
   return w;
@@ -315,7 +324,9 @@ int qlora_linear_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
   float* T = nullptr;
   if (r > 0) {
     T = T_save ? T_save : (float*)(wsb + L.t_off);
-    if (ql::launch_rowdot(X, A, m, k, r, T, s) != hipSuccess) return QLORA_ERR_HIP;
+    float* rpart = ws ? (float*)(wsb + L.part_off) : nullptr;   // needed only with splits
+    if (ql::launch_rowdot(X, A, m, k, r, T, rpart, s) != hipSuccess)
+      return QLORA_ERR_HIP;
   }
   ql::LoraTerm lora{T, B, (int64_t)r, 1, r, scaling};
   float* part = p.ksplit > 1 ? (float*)(wsb + L.part_off) : nullptr;
@@ -437,10 +448,11 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
     U = (float*)(wsb + L.u_off);
     uint16_t* Bt = (uint16_t*)(wsb + L.bt_off);
     if (ql::launch_transpose_bf16(B, n, r, Bt, s) != hipSuccess) return QLORA_ERR_HIP;
-    if (ql::launch_rowdot(dY, Bt, m, n, r, U, s) != hipSuccess) return QLORA_ERR_HIP;
+    float* rpart = (float*)(wsb + L.wg_off);
+    if (ql::launch_rowdot(dY, Bt, m, n, r, U, rpart, s) != hipSuccess) return QLORA_ERR_HIP;
     if (!T) {
       float* Tw = (float*)(wsb + L.t_off);
-      if (ql::launch_rowdot(X, A, m, k, r, Tw, s) != hipSuccess) return QLORA_ERR_HIP;
+      if (ql::launch_rowdot(X, A, m, k, r, Tw, rpart, s) != hipSuccess) return QLORA_ERR_HIP;
       T = Tw;
     }
   }

@@ -73,9 +73,27 @@ hipError_t launch_gemm_dx(const Nf4View& w, const float* codebook, const uint16_
 hipError_t launch_reduce(const float* part, int nsplit, int64_t M, int64_t C,
                          const LoraTerm& lora, void* out, bool out_bf16, hipStream_t s);
 
-// out[m][j] = sum_c P[m][c] * Q[j][c]   (P bf16 [M x C], Q bf16 [r x C], out fp32 [M x r])
+// Rank projection plan.  For M >= 512 and 16 < r <= 64 (and 16-byte rows)
+// the projection runs on 128-row tiles with the contraction split so that
+// about 256 workgroups run; rowdot_splits() is the number of splits (each
+// needing M * r floats of partials when > 1; the launcher and the workspace
+// sizing both use it).  At r <= 16 the rank factor is small enough that the
+// single-pass kernel, which needs no partials, is faster.
+inline bool rowdot_uses_split_path(int64_t M, int r) { return M >= 512 && r > 16 && r <= 64; }
+inline int rowdot_splits(int64_t M, int64_t C, int r) {
+  if (!rowdot_uses_split_path(M, r)) return 1;
+  const int64_t ch = r <= 32 ? 256 : 128;
+  const int64_t tiles = (M + 127) / 128, chunks = (C + ch - 1) / ch;
+  int64_t want = (256 + tiles - 1) / tiles;
+  if (want > chunks) want = chunks;
+  if (want < 1) want = 1;
+  const int64_t per = (chunks + want - 1) / want;
+  return (int)((chunks + per - 1) / per);
+}
+// out[m][j] = sum_c P[m][c] * Q[j][c]   (P bf16 [M x C], Q bf16 [r x C], out fp32 [M x r]);
+// `part` holds rowdot_splits(M, C, r) * M * r floats when that is above 1.
 hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
-                         float* out, hipStream_t s);
+                         float* out, float* part, hipStream_t s);
 // One product of the grouped rowdot: out[m][j] = sum_c P[m][c] Q[j][c].
 struct RowdotJob {
   const uint16_t* P;

@@ -18,14 +18,16 @@ QL_DEV u32x4_t load8_guard(const uint16_t* row, int64_t c, int64_t C, bool vec) 
 // out[m][j] = sum_c P[m][c] Q[j][c]: a workgroup of 8 waves owns `rows`
 // rows (16, or 8 so that a few thousand rows still spread over every compute
 // unit) and all r ranks, in RT tiles of 16.  Wave w takes the 32-wide
-// contraction slices w, w+8, ..., U at a time (all U slices' loads are issued
-// before their MFMAs, so many loads are in flight per wave); per slice it
-// loads the rows' fragment once and one fragment per rank tile, and feeds RT
-// MFMAs 16x16x32, so P is read once whatever the rank.  The 8 partial tiles
-// are summed in a fixed order through LDS.  bf16 products are exact, sums
-// fp32.
+// contraction slices w, w+8, ..., U at a time; per slice it loads the rows'
+// fragment once and one fragment per rank tile and feeds RT MFMAs 16x16x32,
+// so P is read once whatever the rank.  With 16-byte rows (VEC) the loads
+// are buffer loads whose masked lanes (rows past M, ranks past r, slices
+// past the contraction) point past the buffer and read zeros, so there are
+// no branches, and two register sets alternate: the next U slices load while
+// the current ones are multiplied.  The 8 partial tiles are summed in a
+// fixed order through LDS.  bf16 products are exact, sums fp32.
 constexpr int RD_WAVES = 8;
-template <int RT, bool GROUPED>
+template <int RT, bool GROUPED, bool VEC>
 __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
                                                 const uint16_t* __restrict__ Q, int64_t M,
                                                 int64_t C, int r, float* __restrict__ out,
@@ -41,31 +43,69 @@ __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
   __shared__ f32x4_t s_red[RD_WAVES - 1][RT][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, g = lane >> 4;
-  const int64_t m = (int64_t)blockIdx.x * rows + li;
-  const bool mok = li < rows && m < M;
-  const bool vec = (C % 8) == 0;
-  const uint16_t* prow = P + (mok ? m : 0) * C;
+  const int64_t m0 = (int64_t)blockIdx.x * rows;
   f32x4_t acc[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   constexpr int U = RT <= 2 ? 6 : (RT == 4 ? 4 : 2);   // slices per round (register budget)
-  constexpr int64_t stride = 32 * RD_WAVES;
-  for (int64_t c0 = wave * 32; c0 < C; c0 += U * stride) {
-    u32x4_t a[U], b[U][RT];
+  constexpr int64_t stride = 32 * RD_WAVES;            // elements between a wave's slices
+  if constexpr (VEC) {
+    constexpr uint32_t kOut = 0x80000000u;
+    const int nr = (int)min((int64_t)rows, M - m0);
+    const auto prs = buf_rsrc(P + m0 * C, rsrc_bytes((int64_t)nr * C * 2));
+    const auto qrs = buf_rsrc(Q, rsrc_bytes((int64_t)r * C * 2));
+    const uint32_t pbase = li < nr ? (uint32_t)(li * C * 2) : kOut;
+    uint32_t qbase[RT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + u * stride + g * 8;
-      a[u] = mok ? load8_guard(prow, c, C, vec) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int t = 0; t < RT; ++t) qbase[t] = 16 * t + li < r ? (uint32_t)((16 * t + li) * C * 2) : kOut;
+    auto ld_round = [&](int64_t c0, u32x4_t (&a)[U], u32x4_t (&b)[U][RT]) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const int j = 16 * t + li;
-        b[u][t] = j < r ? load8_guard(Q + (int64_t)j * C, c, C, vec) : u32x4_t{0u, 0u, 0u, 0u};
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * stride + 8 * g;
+        const bool cok = c < C;
+        const uint32_t co = (uint32_t)(c * 2);
+        a[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs, cok ? pbase + co : kOut, 0, 0));
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          b[u][t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(qrs, cok ? qbase[t] + co : kOut, 0, 0));
       }
+    };
+    auto mma_round = [&](const u32x4_t (&a)[U], const u32x4_t (&b)[U][RT]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[t] = mfma16x16x32(a[u], b[u][t], acc[t]);
+    };
+    u32x4_t a0[U], b0[U][RT], a1[U], b1[U][RT];
+    int64_t c0 = wave * 32;
+    ld_round(c0, a0, b0);
+    for (; c0 < C; c0 += 2 * U * stride) {
+      ld_round(c0 + U * stride, a1, b1);
+      mma_round(a0, b0);
+      ld_round(c0 + 2 * U * stride, a0, b0);
+      mma_round(a1, b1);
     }
+  } else {
+    const int64_t m = m0 + li;
+    const bool mok = li < rows && m < M;
+    const uint16_t* prow = P + (mok ? m : 0) * C;
+    for (int64_t c0 = wave * 32; c0 < C; c0 += U * stride) {
+      u32x4_t a[U], b[U][RT];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * stride + g * 8;
+        a[u] = mok ? load8_guard(prow, c, C, false) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int t = 0; t < RT; ++t) acc[t] = mfma16x16x32(a[u], b[u][t], acc[t]);
+        for (int t = 0; t < RT; ++t) {
+          const int j = 16 * t + li;
+          b[u][t] = j < r ? load8_guard(Q + (int64_t)j * C, c, C, false) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[t] = mfma16x16x32(a[u], b[u][t], acc[t]);
+    }
   }
   if (wave > 0) {
 #pragma unroll
@@ -81,9 +121,169 @@ __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
     const int j = 16 * t + li;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int64_t mm = (int64_t)blockIdx.x * rows + g * 4 + e;
+      const int64_t mm = m0 + g * 4 + e;
       if (g * 4 + e < rows && mm < M && j < r) out[mm * r + j] = acc[t][e];
     }
+  }
+}
+
+// Large-M rank projection, out[m][j] = sum_c P[m][c] Q[j][c], for 16-byte
+// rows (C % 8 == 0, aligned bases) and 16 < r <= 64.  Every row tile reads all of
+// Q, so Q is shared through LDS: a workgroup of 8 waves owns 128 rows (wave
+// w: rows 16w .. 16w+15) and the contraction range of its split, walked in
+// chunks of CH columns.  Each chunk of Q (16 RT ranks x CH bf16, rows padded
+// by 16 bytes so that the 16 rows of a fragment read fall on distinct bank
+// groups) is staged once and read by the 8 waves, which load their own rows
+// of P as buffer loads (masked lanes read zeros past the buffer).  The next
+// chunk's loads are issued before the current chunk's MFMAs 16x16x32, with
+// one barrier per chunk (two LDS buffers).  With several splits each one
+// writes its sums to part[split][m][j] and k_rowdot_reduce adds them in
+// split order; with one split the sums go to out.
+constexpr int RS_ROWS = 128;
+template <int RT>
+struct RsGeo {
+  static constexpr int CH = RT <= 2 ? 256 : 128;      // columns per chunk
+  static constexpr int PITCH = CH + 8;                // LDS row pitch (bf16)
+  static constexpr int QL = RT * CH / 256;            // 16-byte Q pieces per thread and chunk
+  static constexpr int XS = CH / 32;                  // slices per wave and chunk
+};
+
+template <int RT>
+__global__ __launch_bounds__(512) void k_rowdot_sk(const uint16_t* __restrict__ P,
+                                                   const uint16_t* __restrict__ Q, int64_t M,
+                                                   int64_t C, int r, float* __restrict__ out,
+                                                   float* __restrict__ part, int nsplit,
+                                                   int chunks_per_split) {
+  using G = RsGeo<RT>;
+  constexpr int CH = G::CH, PITCH = G::PITCH, QL = G::QL, XS = G::XS;
+  constexpr uint32_t kOut = 0x80000000u;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ0[16 * RT * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ1[16 * RT * PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.x * RS_ROWS;
+  const int split = blockIdx.y;
+  const int64_t c_begin = (int64_t)split * chunks_per_split * CH;
+  const int64_t c_end = min(C, c_begin + (int64_t)chunks_per_split * CH);
+  const int nch = c_begin < c_end ? (int)((c_end - c_begin + CH - 1) / CH) : 0;
+
+  const int nr = (int)min((int64_t)RS_ROWS, M - m0);
+  const auto prs = buf_rsrc(P + m0 * C, rsrc_bytes((int64_t)nr * C * 2));
+  const auto qrs = buf_rsrc(Q, rsrc_bytes((int64_t)r * C * 2));
+  const int prow = 16 * wave + li;
+  const uint32_t pbase = prow < nr ? (uint32_t)(prow * C * 2) : kOut;
+
+  // Q pieces of this thread: piece i covers chunk row q / (CH/8), 8 columns
+  // from 8 (q % (CH/8)), q = tid + 512 i
+  auto load_q = [&](int64_t cb, u32x4_t (&v)[QL]) {
+#pragma unroll
+    for (int i = 0; i < QL; ++i) {
+      const int q = tid + 512 * i;
+      const int j = q / (CH / 8);
+      const int64_t c = cb + 8 * (q % (CH / 8));
+      const bool ok = j < r && c < c_end;
+      v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                            qrs, ok ? (uint32_t)((j * C + c) * 2) : kOut, 0, 0));
+    }
+  };
+  auto store_q = [&](const u32x4_t (&v)[QL], uint16_t* sq) {
+#pragma unroll
+    for (int i = 0; i < QL; ++i) {
+      const int q = tid + 512 * i;
+      *reinterpret_cast<u32x4_t*>(sq + (q / (CH / 8)) * PITCH + 8 * (q % (CH / 8))) = v[i];
+    }
+  };
+  auto load_x = [&](int64_t cb, u32x4_t (&x)[XS]) {
+#pragma unroll
+    for (int k = 0; k < XS; ++k) {
+      const int64_t c = cb + 32 * k + 8 * g;
+      x[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                            prs, c < c_end ? pbase + (uint32_t)(c * 2) : kOut, 0, 0));
+    }
+  };
+  f32x4_t acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const uint16_t* sq, const u32x4_t (&x)[XS]) {
+#pragma unroll
+    for (int k = 0; k < XS; ++k)
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(sq + (16 * t + li) * PITCH + 32 * k + 8 * g);
+        acc[t] = mfma16x16x32(x[k], b, acc[t]);
+      }
+  };
+
+  u32x4_t qa[QL], qb[QL], xa[XS], xb[XS];
+  int64_t cb = c_begin;
+  if (nch > 0) {
+    load_q(cb, qa);
+    load_x(cb, xa);
+  }
+  for (int ch = 0; ch < nch; ch += 2) {
+    store_q(qa, sQ0);
+    __syncthreads();
+    if (ch + 1 < nch) {
+      load_q(cb + CH, qb);
+      load_x(cb + CH, xb);
+    }
+    compute(sQ0, xa);
+    if (ch + 1 < nch) {
+      store_q(qb, sQ1);
+      __syncthreads();
+      if (ch + 2 < nch) {
+        load_q(cb + 2 * CH, qa);
+        load_x(cb + 2 * CH, xa);
+      }
+      compute(sQ1, xb);
+    }
+    cb += 2 * CH;
+  }
+
+  // D[4g + e][li]: rows m0 + 16 wave + 4g + e, rank 16t + li
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int j = 16 * t + li;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t m = m0 + 16 * wave + 4 * g + e;
+      if (m < M && j < r) {
+        if (nsplit > 1)
+          part[((int64_t)split * M + m) * r + j] = acc[t][e];
+        else
+          out[m * r + j] = acc[t][e];
+      }
+    }
+  }
+}
+
+// out[i] = sum_s part[s][i] over n values, in split order; four values per
+// thread (16-byte accesses when n % 4 == 0 and out is 16-byte aligned), eight
+// splits' loads in flight.
+__global__ __launch_bounds__(256) void k_rowdot_reduce(const float* __restrict__ part, int nsplit,
+                                                       int64_t n, float* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (n % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+      f32x4_t t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = *reinterpret_cast<const f32x4_t*>(part + (int64_t)(s + u) * n + i);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v += t[u];
+    }
+    for (; s < nsplit; ++s) v += *reinterpret_cast<const f32x4_t*>(part + (int64_t)s * n + i);
+    *reinterpret_cast<f32x4_t*>(out + i) = v;
+  } else {
+    for (int s = 0; s < nsplit; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i + e < n) v[e] += part[(int64_t)s * n + i + e];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (i + e < n) out[i + e] = v[e];
   }
 }
 
@@ -267,11 +467,11 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ 
     out[idx] = scaling * v;
 }
 
-template <bool GROUPED>
+template <bool GROUPED, bool VEC>
 static void rowdot_launch(int max_r, dim3 grid, hipStream_t s, const uint16_t* P, const uint16_t* Q,
                           int64_t M, int64_t C, int r, float* out, const RowdotJob* jobs, int rows) {
 #define QL_RD(RT) \
-  hipLaunchKernelGGL((k_rowdot<RT, GROUPED>), grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out, jobs, rows)
+  hipLaunchKernelGGL((k_rowdot<RT, GROUPED, VEC>), grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out, jobs, rows)
   if (max_r <= 16) QL_RD(1);
   else if (max_r <= 32) QL_RD(2);
   else if (max_r <= 64) QL_RD(4);
@@ -280,17 +480,44 @@ static void rowdot_launch(int max_r, dim3 grid, hipStream_t s, const uint16_t* P
 }
 
 hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
-                         float* out, hipStream_t s) {
+                         float* out, float* part, hipStream_t s) {
+  const bool vec = C % 8 == 0 && (reinterpret_cast<uintptr_t>(P) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(Q) & 15) == 0;
+  const int ns = rowdot_splits(M, C, r);
+  if (vec && rowdot_uses_split_path(M, r) && (ns == 1 || part)) {
+    const int64_t tiles = (M + RS_ROWS - 1) / RS_ROWS;
+    const int ch = r <= 32 ? RsGeo<2>::CH : RsGeo<4>::CH;
+    const int64_t chunks = (C + ch - 1) / ch;
+    const int per = (int)((chunks + ns - 1) / ns);
+    const dim3 grid((unsigned)tiles, (unsigned)ns);
+    if (r <= 32)
+      hipLaunchKernelGGL(k_rowdot_sk<2>, grid, dim3(512), 0, s, P, Q, M, C, r, out, part, ns, per);
+    else
+      hipLaunchKernelGGL(k_rowdot_sk<4>, grid, dim3(512), 0, s, P, Q, M, C, r, out, part, ns, per);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ns == 1) return e;
+    const int64_t n = M * r;
+    hipLaunchKernelGGL(k_rowdot_reduce, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, s, part, ns,
+                       n, out);
+    return hipGetLastError();
+  }
   // 8-row tiles when 16-row tiles would leave compute units idle
   const int rows = (M + 15) / 16 < 256 ? 8 : 16;
-  rowdot_launch<false>(r, dim3((unsigned)((M + rows - 1) / rows)), s, P, Q, M, C, r, out, nullptr, rows);
+  const dim3 grid((unsigned)((M + rows - 1) / rows));
+  // 16-byte rows: both operands start 16-byte aligned (checked by the caller
+  // for X and dY; A and the transposed B are C-element rows)
+  if (vec)
+    rowdot_launch<false, true>(r, grid, s, P, Q, M, C, r, out, nullptr, rows);
+  else
+    rowdot_launch<false, false>(r, grid, s, P, Q, M, C, r, out, nullptr, rows);
   return hipGetLastError();
 }
 
 hipError_t launch_rowdot_grouped(const RowdotJob* jobs, int njobs, int64_t M, int max_r,
                                  hipStream_t s) {
-  rowdot_launch<true>(max_r, dim3((unsigned)((M + 15) / 16), 1, (unsigned)njobs), s, nullptr, nullptr,
-                      M, int64_t(0), 0, nullptr, jobs, 16);
+  // the jobs' contraction lengths are whole 64-blocks; X and A are 16-byte aligned
+  rowdot_launch<true, true>(max_r, dim3((unsigned)((M + 15) / 16), 1, (unsigned)njobs), s, nullptr,
+                            nullptr, M, int64_t(0), 0, nullptr, jobs, 16);
   return hipGetLastError();
 }
 

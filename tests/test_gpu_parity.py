@@ -272,6 +272,34 @@ def test_backward_parity(M, N, K, r):
     assert torch.equal(dXg, dXr) and torch.equal(dAg, dAr) and torch.equal(dBg, dBr)
 
 
+@pytest.mark.parametrize("M,N,K,r", [(1000, 300, 640, 48), (513, 257, 320, 20), (600, 96, 4096, 64),
+                                     (4096, 64, 8192, 64), (700, 130, 192, 8)])
+def test_lora_rank_products_large_m(M, N, K, r):
+    """The rank projections T = X A^T and U = dY B and the adapter gradients
+    at large M (row tiles of 128 with the contraction split, ragged rows,
+    ranks and chunks), checked with W = 0 so that only the LoRA branch
+    remains: Y = s T B^T, dX = s U A, dA, dB, and T itself."""
+    B = _dev()
+    _say("lora large m", M, N, K, r)
+    s = 2.0
+    X, _, A, Bm, dY = _inputs(M, N, K, r, seed=M + 7 * N + K + r)
+    W0 = np.zeros((N, K), dtype=np.uint16)
+    q = B.qlora_quantize(_t(W0), _cb(B))
+    Xd, Ad, Bd, dYd = _t(X), _t(A), _t(Bm), _t(dY)
+    Y, T = B.qlora_linear_fwd(q, _cb(B), Xd, Ad, Bd, s)
+    dX, dA, dB = B.qlora_linear_bwd(q, _cb(B), Xd, dYd, Ad, Bd, s)      # T recomputed
+    torch.cuda.synchronize()
+    xf, dyf = onf4.bf16_to_f32(X).astype(np.float64), onf4.bf16_to_f32(dY).astype(np.float64)
+    af, bf = onf4.bf16_to_f32(A).astype(np.float64), onf4.bf16_to_f32(Bm).astype(np.float64)
+    To = xf @ af.T
+    Uo = dyf @ bf
+    assert _rel(T.cpu().numpy(), To) <= 1e-5
+    assert _rel(Y.cpu().numpy(), s * To @ bf.T) <= REL_TOL
+    assert _rel(dX.cpu().numpy(), s * Uo @ af) <= REL_TOL
+    assert _rel(dA.cpu().numpy(), s * Uo.T @ xf) <= REL_TOL
+    assert _rel(dB.cpu().numpy(), s * dyf.T @ To) <= REL_TOL
+
+
 def test_backward_lora_only_and_r0():
     B = _dev()
     M, N, K, r = 40, 320, 512, 8
