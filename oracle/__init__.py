@@ -13,6 +13,8 @@ nf4     -- the NF4 codebook, blockwise absmax NF4 encoding with double
 linear  -- the LoRA-augmented linear layer forward and backward in float64.
 affine  -- the affine (scale + zero-point) integer quantizer of the worked
            INT8 example; used only as a pinned unit.
+merge   -- folding the trained adapter into the base weight (binary32 rank-order
+           sum, bf16 rounding) before requantization.
 formats -- the alternate block formats of the base weight: asymmetric 4-bit
            min/max blocks of 64 (fp32 scale and zero-point) and Q8_0 blocks of
            32 (int8 values, fp16 scale), with their storage order.
