@@ -203,6 +203,24 @@ int qlora_quantize(const uint16_t *W, const float *codebook, const qlora_nf4 *ou
 int qlora_dequantize(const qlora_nf4 *W, const float *codebook, uint16_t *out, void *stream);
 
 /*
+ * Fold a trained adapter into the base weight (www.lqnn.cn/news/228537 §3.3:
+ * dequantize W, add the low-rank branch at high precision, quantize again;
+ * www.cf-1.com/news/5705389 §4.3 and kwkr.cn/news/627310 §4.4 on the two
+ * precision losses, the 16-bit rounding of the sum and the requantization):
+ *     merged[n][k] = bf16_rne(fp32(deq(W)[n][k] + fp32(scaling * acc))),
+ *     acc = sum_j B[n][j] A[j][k], accumulated in binary32 in rank order
+ *           (j = 0 .. r-1; each product of two bf16 values is exact).
+ * A [r x W.k], B [W.n x r] bf16 (device; A 16-byte aligned), r == 0 gives
+ * deq(W).  `merged` [W.n x W.k] bf16 (device, 16-byte aligned) receives the
+ * merged weight.  If `out` is not NULL (sizes equal to W's), the merged
+ * weight is then quantized into it, in out->format, exactly as
+ * qlora_quantize would.  The codebook is required when W or out is NF4.
+ */
+int qlora_merge(const qlora_nf4 *W, const float *codebook, const uint16_t *A, const uint16_t *B,
+                int r, float scaling, uint16_t *merged, const qlora_nf4 *out, void *stream);
+
+/*
+ * Forward of the LoRA-augmented quantized linear (www.cf-1.com/news/5705389/*
  * Forward of the LoRA-augmented quantized linear (www.cf-1.com/news/5705389
  * §2.1, §3.2; www.lqnn.cn/news/228537 §3.2-§3.3):
  *     T = X A^T            [m x r], fp32 (written to T_save if not NULL)

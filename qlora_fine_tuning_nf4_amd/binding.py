@@ -78,6 +78,8 @@ def lib():
         L.qlora_quantize.argtypes = [vp, vp, P(_Nf4Desc), vp]
         L.qlora_dequantize.restype = i32
         L.qlora_dequantize.argtypes = [P(_Nf4Desc), vp, vp, vp]
+        L.qlora_merge.restype = i32
+        L.qlora_merge.argtypes = [P(_Nf4Desc), vp, vp, vp, i32, f32, vp, P(_Nf4Desc), vp]
         L.qlora_linear_fwd.restype = i32
         L.qlora_linear_fwd.argtypes = [P(_Nf4Desc), vp, vp, i64, vp, vp, i32, f32, vp, i32, vp,
                                        vp, sz, i32, vp]
@@ -224,6 +226,24 @@ def qlora_dequantize(w: NF4Weight, codebook: torch.Tensor) -> torch.Tensor:
     _check(lib().qlora_dequantize(ctypes.byref(d), _ptr(codebook), _ptr(out), _stream()),
            "qlora_dequantize")
     return out
+
+
+def qlora_merge(w: NF4Weight, codebook, A=None, B=None, scaling: float = 0.0,
+                out: NF4Weight | None = None, merged: torch.Tensor | None = None):
+    """Fold the adapter into the base: -> (merged bf16 [n x k], out).  When
+    `out` is given the merged weight is requantized into it (its format)."""
+    r = 0 if A is None else A.shape[0]
+    if r:
+        _bf16(A, "A")
+        _bf16(B, "B")
+    M = merged if merged is not None else torch.empty((w.n, w.k), dtype=torch.bfloat16,
+                                                      device=w.codes.device)
+    d = w.desc()
+    od = out.desc() if out is not None else None
+    _check(lib().qlora_merge(ctypes.byref(d), _ptr(codebook), _ptr(A) if r else None,
+                             _ptr(B) if r else None, r, float(scaling), _ptr(M),
+                             ctypes.byref(od) if od is not None else None, _stream()), "qlora_merge")
+    return M, out
 
 
 def qlora_linear_fwd(w: NF4Weight, codebook: torch.Tensor, X: torch.Tensor, A=None, B=None,

@@ -296,6 +296,29 @@ int qlora_dequantize(const qlora_nf4* W, const float* codebook, uint16_t* out, v
   return QLORA_OK;
 }
 
+int qlora_merge(const qlora_nf4* W, const float* codebook, const uint16_t* A, const uint16_t* B,
+                int r, float scaling, uint16_t* merged, const qlora_nf4* out, void* stream) {
+  if (!merged) return QLORA_ERR_NULL;
+  if (int e = check_desc(W)) return e;
+  if (int e = check_codebook(W, codebook)) return e;
+  if (out) {
+    if (int e = check_desc(out)) return e;
+    if (int e = check_codebook(out, codebook)) return e;
+    if (out->n != W->n || out->k != W->k) return QLORA_ERR_SHAPE;
+  }
+  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
+  if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
+  if (!aligned(merged, 16) || (r > 0 && (!aligned(A, 16) || !aligned(B, 2)))) return QLORA_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (ql::launch_dequant(view(W), codebook, merged, s) != hipSuccess) return QLORA_ERR_HIP;
+  if (r > 0 && ql::launch_merge(merged, A, B, W->n, W->k, r, scaling, s) != hipSuccess)
+    return QLORA_ERR_HIP;
+  if (out && ql::launch_quantize(merged, codebook, out->codes, out->qscale, out->step, out->n,
+                                 out->k, kernel_fmt(out), s) != hipSuccess)
+    return QLORA_ERR_HIP;
+  return QLORA_OK;
+}
+
 int qlora_linear_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* X, int64_t m,
                      const uint16_t* A, const uint16_t* B, int r, float scaling, void* Y,
                      int y_dtype, float* T_save, void* ws, size_t ws_bytes, int path,

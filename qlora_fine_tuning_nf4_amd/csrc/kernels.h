@@ -35,6 +35,10 @@ hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* co
                            uint8_t* qscale, float* step, int64_t n, int64_t k, int fmt,
                            hipStream_t s);
 hipError_t launch_dequant(const Nf4View& w, const float* codebook, uint16_t* out, hipStream_t s);
+// W[n][k] <- bf16(W + s * (B A)[n][k]) in place (A [r x k], B [n x r] bf16; k % 8 == 0,
+// W and A 16-byte aligned).
+hipError_t launch_merge(uint16_t* W, const uint16_t* A, const uint16_t* B, int64_t n, int64_t k, int r,
+                        float s, hipStream_t st);
 
 // Forward base product Y = X deq(W)^T (+ LoRA term), tiled MFMA GEMM.
 // ksplit > 1 writes fp32 partials part[ksplit][M][N] and leaves the epilogue

@@ -326,6 +326,52 @@ __global__ __launch_bounds__(256) void k_dequant(Nf4View w, const float* __restr
   }
 }
 
+// Adapter merge (www.lqnn.cn/news/228537 §3.3: dequantize, add the low-rank
+// branch at high precision, quantize again), in place on the dequantized
+// weight W [N x K] bf16:
+//   merged[n][k] = bf16_rne(fp32(w + fp32(s * acc))),
+//   acc = sum_j B[n][j] A[j][k]  in binary32, in rank order (bf16 products are exact).
+// A thread owns 8 consecutive k of one row: A[j][k .. k+7] as one 16-byte load
+// per rank, B[n][j] as a scalar shared by the row's threads.  Contraction of
+// the multiply-add into an fma is switched off: the steps round as written.
+__global__ __launch_bounds__(256) void k_merge(uint16_t* __restrict__ W, const uint16_t* __restrict__ A,
+                                               const uint16_t* __restrict__ B, int64_t N, int64_t K,
+                                               int r, float s) {
+#pragma clang fp contract(off)
+  const int64_t pieces = N * (K / 8);
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= pieces) return;
+  const int64_t n = idx / (K / 8), k = (idx - n * (K / 8)) * 8;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int j = 0; j < r; ++j) {
+    const float b = __builtin_bit_cast(float, (uint32_t)B[n * r + j] << 16);
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(A + (int64_t)j * K + k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = acc[2 * e] + b * bf16_lo(a[e]);
+      acc[2 * e + 1] = acc[2 * e + 1] + b * bf16_hi(a[e]);
+    }
+  }
+  u32x4_t* wp = reinterpret_cast<u32x4_t*>(W + n * K + k);
+  const u32x4_t w = *wp;
+  u32x4_t o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float t0 = s * acc[2 * e], t1 = s * acc[2 * e + 1];
+    o[e] = pack_bf16x2(bf16_lo(w[e]) + t0, bf16_hi(w[e]) + t1);
+  }
+  *wp = o;
+}
+
+hipError_t launch_merge(uint16_t* W, const uint16_t* A, const uint16_t* B, int64_t n, int64_t k, int r,
+                        float s, hipStream_t st) {
+  const int64_t pieces = n * (k / 8);
+  hipLaunchKernelGGL(k_merge, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st, W, A, B, n, k, r, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* codes,
                            uint8_t* qscale, float* step, int64_t n, int64_t k, int fmt,
                            hipStream_t s) {

@@ -193,6 +193,30 @@ def test_bwd_argument_errors():
     assert bwd(ws=None) == 6
 
 
+def test_merge_argument_errors():
+    L = B.lib()
+    d = _desc()
+    U4 = B.QLORA_FMT_U4_ASYM
+
+    def mg(W="d", cb=FAKE, A=FAKE, Bp=FAKE, r=8, M=FAKE, out=None):
+        Wd = ctypes.byref(d) if W == "d" else W
+        return L.qlora_merge(Wd, cb, A, Bp, r, 2.0, M, out, None)
+    assert mg(W=None) == 1
+    assert mg(M=None) == 1
+    assert mg(cb=None) == 1                   # an NF4 base needs the codebook
+    assert mg(A=None) == 1
+    assert mg(Bp=None) == 1
+    assert mg(r=129) == 5
+    assert mg(r=-1) == 5
+    assert mg(M=FAKE + 8) == 3
+    assert mg(A=FAKE + 2) == 3
+    assert mg(out=ctypes.byref(_desc(n=32))) == 2
+    assert mg(out=ctypes.byref(_desc(fmt=9))) == 8
+    u = _desc(fmt=U4, qs=0)
+    assert mg(W=ctypes.byref(u), cb=None, M=FAKE + 8) == 3          # a uint4 base needs none
+    assert mg(W=ctypes.byref(u), cb=None, out=ctypes.byref(_desc())) == 1   # an NF4 target does
+
+
 def _job(n=64, k=128, X=FAKE, A=FAKE, Bp=FAKE, r=8, Y=FAKE, T=FAKE, codes=FAKE, qs=FAKE, fmt=0):
     return B._FwdJob(_desc(n, k, codes=codes, qs=qs, fmt=fmt), X, A, Bp, r, 2.0, Y, T)
 

@@ -15,6 +15,7 @@ import torch
 import synth
 from oracle import formats as F
 from oracle import linear as olin
+from oracle import merge as omerge
 from oracle import nf4 as onf4
 
 pytestmark = pytest.mark.gpu
@@ -228,3 +229,68 @@ def test_grouped_forward(name, M):
     for j, (W, X, A, Bm) in zip(jobs, ref):
         Yo, _ = olin.forward(_oracle_wd(name, W), X, A, Bm, 2.0)
         assert _rel(j["Y"].cpu().numpy(), Yo) <= REL_TOL
+
+
+# --------------------------------------------------------------------------- merge + requantize
+_LV, _MID = onf4.codebook()
+
+
+def _oracle_wd_any(name, w_bits):
+    if name == "nf4":
+        c, q, st = onf4.quantize(w_bits, _MID)
+        return onf4.dequantize(c, q, st, _LV).reshape(w_bits.shape)
+    return _oracle_wd(name, w_bits)
+
+
+def _oracle_quant_storage(name, w_bits):
+    """Expected device arrays of quantize(w) in format `name`, storage order:
+    (codes bytes, second array bytes, third array bytes)."""
+    n, k = w_bits.shape
+    if name == "nf4":
+        c, q, st = onf4.quantize(w_bits, _MID)
+        cs, qs = onf4.to_storage(c, q, n, k)
+        return cs, qs, st.view(np.uint8)
+    if name == "u4_asym":
+        c, sc, z = F.u4_quantize(w_bits)
+        cs, ps = F.u4_to_storage(c, sc, z, n, k)
+        return cs, None, ps.reshape(-1).view(np.uint8)
+    qq, d16 = F.q8_quantize(w_bits)
+    cs, ss = F.q8_to_storage(qq, d16, n, k)
+    return cs.view(np.uint8), ss.reshape(-1).view(np.uint8), None
+
+
+@pytest.mark.parametrize("src,dst,N,K,r", [("nf4", "nf4", 300, 512, 16), ("nf4", "q8_0", 257, 320, 8),
+                                          ("q8_0", "nf4", 200, 384, 64), ("u4_asym", "u4_asym", 130, 256, 4),
+                                          ("nf4", "nf4", 4096, 4096, 16)])
+def test_merge_and_requantize(src, dst, N, K, r):
+    """Merged bf16 weight bit-exact against the merge oracle, the requantized
+    arrays bit-exact against the quantizer of the target format; the forward
+    through the requantized merge is compared with the separate adapter."""
+    B = _dev()
+    _say("merge", src, dst, N, K, r)
+    s = 2.0
+    W = synth.normal_bf16((N, K), 0.02, N + K + r)
+    A = synth.normal_bf16((r, K), 0.01, N + K + r + 1)
+    Bm = synth.normal_bf16((N, r), 0.01, N + K + r + 2)
+    cb = B.device_codebook()
+    q = B.qlora_quantize(_t(W), cb if src == "nf4" else None, fmt=_fmt(B, src))
+    out = B.NF4Weight.empty(N, K, "cuda", fmt=_fmt(B, dst))
+    M, out = B.qlora_merge(q, cb, _t(A), _t(Bm), s, out=out)
+    torch.cuda.synchronize()
+    Wd = _oracle_wd_any(src, W)
+    Mo = omerge.merged_weight(Wd, A, Bm, s)
+    _same(_bits(M).astype(np.int64), Mo.astype(np.int64), ("merged", src, dst))
+    cs, a2, a3 = _oracle_quant_storage(dst, Mo)
+    assert np.array_equal(out.codes.cpu().numpy(), cs)
+    if a2 is not None:
+        assert np.array_equal(out.qscale.cpu().numpy(), a2)
+    if a3 is not None:
+        assert np.array_equal(out.step.cpu().numpy().view(np.uint8), a3)
+    # what the merge costs against keeping the adapter separate (context)
+    if N <= 512:
+        X = synth.normal_bf16((64, K), 1.0, 9)
+        Ysep, _ = olin.forward(Wd, X, A, Bm, s)
+        Ymrg, _ = olin.forward(_oracle_wd_any(dst, Mo), X)      # deq(quant(merged)), the arrays above
+        rel = _rel(Ymrg, Ysep)
+        _say(f"  forward through the requantized merge vs separate adapter: rel {rel:.4f}")
+        assert rel < 0.25
