@@ -35,6 +35,14 @@ What is computed, in the pages' order
    fp32 second-level constants stay indexed by the flat block.  ``quantize``
    returns the flat (logical) order; ``to_storage`` / ``from_storage`` convert.
 
+Other block sizes [rkmt §1.2: smaller blocks quantize more finely and cost
+more constants; zky "double quantization"]: every step above runs on blocks of
+32 or 128 consecutive weights instead of 64 (``block=``), second-level groups
+still holding 256 block scales.  Codes keep the 64-weight word layout and unit
+order; the scales are stored with ``scales_to_storage``: block 32 as the pair of
+scales of a 64-weight unit at 2p, 2p + 1 (p the unit's position), block 128 in
+the row-group order over the k/128 block columns.
+
 Without double quantization [rkmt §1.2, §2.3: one fp32 scale per 64-block,
 0.5 bit per parameter; zky "double quantization" names the saving]: steps 1-3
 only; the block keeps its fp32 absmax as the scale (``quantize_nodq``), and
@@ -109,12 +117,12 @@ def codebook() -> tuple[np.ndarray, np.ndarray]:
 # --------------------------------------------------------------------------
 # storage sizes [rkmt §1.3, §2.3]
 # --------------------------------------------------------------------------
-def nf4_bytes(n: int, k: int) -> tuple[int, int, int]:
+def nf4_bytes(n: int, k: int, block: int = BLOCK) -> tuple[int, int, int]:
     """(code bytes, u8 scale bytes, fp32 second-level bytes) of an n x k weight."""
     numel = n * k
-    if numel % BLOCK:
-        raise ValueError("numel must be a multiple of 64")
-    nblocks = numel // BLOCK
+    if numel % BLOCK or numel % block:
+        raise ValueError("numel must be a multiple of 64 and of the block")
+    nblocks = numel // block
     ngroups = -(-nblocks // GROUP)
     return numel // 2, nblocks, 4 * ngroups
 
@@ -147,11 +155,11 @@ def unpack(codes: np.ndarray) -> np.ndarray:
     return out.reshape(-1)
 
 
-def storage_positions(n: int, k: int) -> np.ndarray:
-    """Storage position of every flat block b = row * (k/64) + kb (step 6):
+def storage_positions(n: int, k: int, width: int = BLOCK) -> np.ndarray:
+    """Storage position of every flat block b = row * (k/width) + kb (step 6):
     group start g0 = 16 * (row // 16), R = min(16, n - g0) rows in the group,
-    position g0 * (k/64) + kb * R + (row - g0)."""
-    nkb = k // BLOCK
+    position g0 * (k/width) + kb * R + (row - g0)."""
+    nkb = k // width
     row = np.arange(n, dtype=np.int64)[:, None]
     kb = np.arange(nkb, dtype=np.int64)[None, :]
     g0 = (row // 16) * 16
@@ -176,18 +184,18 @@ def from_storage(codes: np.ndarray, qscale: np.ndarray, n: int, k: int):
     return cs.reshape(-1), np.asarray(qscale, dtype=np.uint8)[pos]
 
 
-def block_absmax(w_bits: np.ndarray) -> np.ndarray:
-    x = bf16_to_f32(np.asarray(w_bits).reshape(-1)).reshape(-1, BLOCK)
+def block_absmax(w_bits: np.ndarray, block: int = BLOCK) -> np.ndarray:
+    x = bf16_to_f32(np.asarray(w_bits).reshape(-1)).reshape(-1, block)
     return np.max(np.abs(x), axis=1).astype(np.float32)
 
 
-def quantize_nodq(w_bits: np.ndarray, mids: np.ndarray):
-    """Steps 1-3 only: bf16 weight bits (numel % 64 == 0) ->
-    (codes uint8[numel/2], absmax float32[numel/64]), flat order."""
+def quantize_nodq(w_bits: np.ndarray, mids: np.ndarray, block: int = BLOCK):
+    """Steps 1-3 only: bf16 weight bits (numel % 64 == 0 and % block == 0) ->
+    (codes uint8[numel/2], absmax float32[numel/block]), flat order."""
     flat = np.asarray(w_bits, dtype=np.uint16).reshape(-1)
-    if flat.size % BLOCK:
-        raise ValueError("numel must be a multiple of 64")
-    x = bf16_to_f32(flat).reshape(-1, BLOCK)
+    if flat.size % BLOCK or flat.size % block:
+        raise ValueError("numel must be a multiple of 64 and of the block")
+    x = bf16_to_f32(flat).reshape(-1, block)
     if not np.all(np.isfinite(x)):
         raise ValueError("non-finite weights are outside the contract")
     # step 1: first-level scale per 64-block
@@ -201,10 +209,10 @@ def quantize_nodq(w_bits: np.ndarray, mids: np.ndarray):
     return pack(code.reshape(-1)), absmax
 
 
-def dequantize_nodq(codes, absmax, levels) -> np.ndarray:
+def dequantize_nodq(codes, absmax, levels, block: int = BLOCK) -> np.ndarray:
     """-> bf16 bits (flat): bf16_rne(fp32(level[code] * absmax_b))."""
     code = unpack(codes)
-    s_el = np.repeat(np.asarray(absmax, dtype=np.float32), BLOCK)
+    s_el = np.repeat(np.asarray(absmax, dtype=np.float32), block)
     prod = (np.asarray(levels, dtype=np.float32)[code] * s_el).astype(np.float32)
     return f32_to_bf16_rne(prod)
 
@@ -218,10 +226,10 @@ def blocks_to_storage(per_block: np.ndarray, n: int, k: int) -> np.ndarray:
     return out
 
 
-def quantize(w_bits: np.ndarray, mids: np.ndarray):
-    """bf16 weight bits (any shape, numel % 64 == 0) ->
-    (codes uint8[numel/2], qscale uint8[numel/64], step float32[ngroups])."""
-    codes, absmax = quantize_nodq(w_bits, mids)
+def quantize(w_bits: np.ndarray, mids: np.ndarray, block: int = BLOCK):
+    """bf16 weight bits (any shape, numel % 64 == 0 and % block == 0) ->
+    (codes uint8[numel/2], qscale uint8[numel/block], step float32[ngroups])."""
+    codes, absmax = quantize_nodq(w_bits, mids, block)
     # step 4: second level over groups of 256 block scales
     nblocks = absmax.size
     ngroups = -(-nblocks // GROUP)
@@ -247,11 +255,11 @@ def block_scale(qscale: np.ndarray, step: np.ndarray) -> np.ndarray:
     return (q * np.asarray(step, dtype=np.float32)[g]).astype(np.float32)
 
 
-def dequantize(codes, qscale, step, levels) -> np.ndarray:
+def dequantize(codes, qscale, step, levels, block: int = BLOCK) -> np.ndarray:
     """-> bf16 bits (flat): bf16_rne(fp32(level[code] * s'_b))."""
     code = unpack(codes)
     s = block_scale(qscale, step)
-    s_el = np.repeat(s, BLOCK)
+    s_el = np.repeat(s, block)
     prod = (np.asarray(levels, dtype=np.float32)[code] * s_el).astype(np.float32)
     return f32_to_bf16_rne(prod)
 
@@ -260,8 +268,31 @@ def dequantize_f32(codes, qscale, step, levels) -> np.ndarray:
     return bf16_to_f32(dequantize(codes, qscale, step, levels))
 
 
+def scales_to_storage(per_block: np.ndarray, n: int, k: int, block: int = BLOCK) -> np.ndarray:
+    """Flat-order per-block scales (8-bit or fp32) of an n x k weight ->
+    storage order (step 6 for other block sizes): block 64 at the unit's
+    position; block 32 as the pair of its unit at 2p, 2p + 1; block 128 in the
+    same row-group order over the k/128 block columns."""
+    a = np.asarray(per_block)
+    if block == BLOCK:
+        return blocks_to_storage(a, n, k)
+    if block == 32:
+        return blocks_to_storage(a.reshape(-1, 2), n, k).reshape(-1)
+    pos = storage_positions(n, k, width=block)
+    out = np.empty_like(a)
+    out[pos] = a
+    return out
+
+
+def scales_from_storage(stored: np.ndarray, n: int, k: int, block: int = BLOCK) -> np.ndarray:
+    a = np.asarray(stored)
+    if block == 32:
+        return a.reshape(-1, 2)[storage_positions(n, k)].reshape(-1)
+    return a[storage_positions(n, k, width=block)]
+
+
 def dequant_error_bound(w_bits: np.ndarray, levels: np.ndarray,
-                        double_quant: bool = True) -> np.ndarray:
+                        double_quant: bool = True, block: int = BLOCK) -> np.ndarray:
     """Per-element bound on |w - deq(q(w))| (float64), derived from the steps,
     independent of how ``quantize`` is written:
 
@@ -276,7 +307,7 @@ def dequant_error_bound(w_bits: np.ndarray, levels: np.ndarray,
                                                      -> 2^-23 |w| + half a bf16 ulp of |w|
     """
     flat = np.asarray(w_bits, dtype=np.uint16).reshape(-1)
-    x = bf16_to_f32(flat).astype(np.float64).reshape(-1, BLOCK)
+    x = bf16_to_f32(flat).astype(np.float64).reshape(-1, block)
     absmax = np.max(np.abs(x), axis=1)
     nblocks = absmax.size
     ngroups = -(-nblocks // GROUP)
