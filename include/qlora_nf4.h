@@ -124,6 +124,15 @@ enum {
  *     (little-endian binary16) of the unit's elements 0-31 at bytes [4p, 4p+2)
  *     and 32-63 at [4p+2, 4p+4); step is unused (may be NULL).  Blocks with
  *     absmax above 127 * 65504 are outside the contract.
+ * NF4 at other block sizes (block = 32 or 128; news.rkmt.cn/news/4821 §1.2:
+ * smaller blocks quantize more finely and cost more constants): every step
+ * above runs on blocks of that many consecutive weights of a row; codes keep
+ * the 64-weight unit layout and order; second-level groups still hold 256
+ * block scales (flat block index b = row * (k/block) + kb).  Scale entries
+ * (qscale bytes, or single-level fp32 absmax in step): block 32 stores the
+ * unit's two scales at 2p and 2p + 1; block 128 stores one scale per pair of
+ * units, block (row, kb) at g0*(k/128) + kb*R + (row - g0).  Block 128 needs
+ * k % 128 == 0 and block 32 n*k < 2^37.  Sizes from qlora_nf4_block_bytes.
  * The codebook argument of every entry point is used by (and required for)
  * the NF4 format only.  Every entry point accepts every format; a grouped
  * forward needs one format (and for NF4 one scale level) for all its jobs.
@@ -135,6 +144,7 @@ typedef struct {
   uint8_t *qscale;
   float *step;
   int32_t format;  /* QLORA_FMT_* */
+  int32_t block;   /* NF4 block size: 0 or 64 (default), 32 or 128; 0 or 64 for other formats */
 } qlora_nf4;
 
 /*
@@ -162,6 +172,17 @@ int qlora_nf4_bytes(int64_t n, int64_t k, size_t *codes, size_t *qscale, size_t 
  * qlora_nf4_bytes.
  */
 int qlora_nf4_single_bytes(int64_t n, int64_t k, size_t *codes, size_t *absmax);
+
+/*
+ * Host.  Byte sizes of the arrays of an n x k NF4 weight with blocks of
+ * `block` weights (32, 64 or 128), with (double_quant != 0) or without double
+ * quantization: codes n*k/2; double-quantized: qscale n*k/block, step
+ * 4*ceil(n*k/block/256); single level: qscale 0, step 4*n*k/block.
+ * QLORA_ERR_ARG for another block, QLORA_ERR_SHAPE as qlora_nf4_bytes or when
+ * the block's limits above are not met.
+ */
+int qlora_nf4_block_bytes(int64_t n, int64_t k, int block, int double_quant, size_t *codes,
+                          size_t *qscale, size_t *step);
 
 /*
  * Host.  Byte sizes of the three arrays of an n x k weight in `format`

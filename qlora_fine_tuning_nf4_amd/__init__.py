@@ -9,6 +9,6 @@ from .binding import (  # noqa: F401
     FORMATS, QLORA_FMT_NF4, QLORA_FMT_Q8_0, QLORA_FMT_U4_ASYM, FwdGroup, NF4Weight, QLoRAError,
     device_codebook, lib, qlora_dequantize, qlora_group_init, qlora_group_table_bytes,
     qlora_linear_bwd, qlora_linear_fwd, qlora_linear_fwd_grouped, qlora_merge, qlora_nf4_bytes,
-    qlora_nf4_codebook, qlora_nf4_single_bytes, qlora_quantize, qlora_strerror,
+    qlora_nf4_block_bytes, qlora_nf4_codebook, qlora_nf4_single_bytes, qlora_quantize, qlora_strerror,
     qlora_weight_bytes, qlora_workspace_bytes,
 )

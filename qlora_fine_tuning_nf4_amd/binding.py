@@ -32,7 +32,8 @@ class QLoRAError(RuntimeError):
 
 class _Nf4Desc(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("codes", ctypes.c_void_p),
-                ("qscale", ctypes.c_void_p), ("step", ctypes.c_void_p), ("format", ctypes.c_int32)]
+                ("qscale", ctypes.c_void_p), ("step", ctypes.c_void_p), ("format", ctypes.c_int32),
+                ("block", ctypes.c_int32)]
 
 
 class _FwdJob(ctypes.Structure):
@@ -70,6 +71,8 @@ def lib():
         L.qlora_nf4_bytes.argtypes = [i64, i64, P(sz), P(sz), P(sz)]
         L.qlora_nf4_single_bytes.restype = i32
         L.qlora_nf4_single_bytes.argtypes = [i64, i64, P(sz), P(sz)]
+        L.qlora_nf4_block_bytes.restype = i32
+        L.qlora_nf4_block_bytes.argtypes = [i64, i64, i32, i32, P(sz), P(sz), P(sz)]
         L.qlora_weight_bytes.restype = i32
         L.qlora_weight_bytes.argtypes = [i32, i64, i64, P(sz), P(sz), P(sz)]
         L.qlora_workspace_bytes.restype = sz
@@ -135,6 +138,13 @@ def qlora_nf4_single_bytes(n: int, k: int):
     return c.value, a.value
 
 
+def qlora_nf4_block_bytes(n: int, k: int, block: int, double_quant: bool = True):
+    c, q, s = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().qlora_nf4_block_bytes(n, k, block, int(double_quant), ctypes.byref(c), ctypes.byref(q),
+                                       ctypes.byref(s)), "qlora_nf4_block_bytes")
+    return c.value, q.value, s.value
+
+
 def qlora_weight_bytes(fmt: int, n: int, k: int):
     c, q, s = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     _check(lib().qlora_weight_bytes(fmt, n, k, ctypes.byref(c), ctypes.byref(q), ctypes.byref(s)),
@@ -160,6 +170,7 @@ class NF4Weight:
     qscale: torch.Tensor | None
     step: torch.Tensor | None
     fmt: int = QLORA_FMT_NF4
+    block: int = 64                   # NF4 block size (32, 64, 128)
 
     @property
     def double_quant(self) -> bool:
@@ -168,11 +179,12 @@ class NF4Weight:
     def desc(self) -> _Nf4Desc:
         return _Nf4Desc(self.n, self.k, self.codes.data_ptr(),
                         self.qscale.data_ptr() if self.qscale is not None else None,
-                        self.step.data_ptr() if self.step is not None else None, self.fmt)
+                        self.step.data_ptr() if self.step is not None else None, self.fmt,
+                        self.block)
 
     @staticmethod
     def empty(n: int, k: int, device="cuda", double_quant: bool = True,
-              fmt: int = QLORA_FMT_NF4) -> "NF4Weight":
+              fmt: int = QLORA_FMT_NF4, block: int = 64) -> "NF4Weight":
         def u8(b):
             return torch.empty(b, dtype=torch.uint8, device=device)
 
@@ -185,11 +197,10 @@ class NF4Weight:
         if fmt == QLORA_FMT_Q8_0:
             c, q, _ = qlora_weight_bytes(fmt, n, k)
             return NF4Weight(n, k, u8(c), u8(q), None, fmt)
+        c, q, s = qlora_nf4_block_bytes(n, k, block, double_quant)
         if not double_quant:
-            c, a = qlora_nf4_single_bytes(n, k)
-            return NF4Weight(n, k, u8(c), None, f32(a), fmt)
-        c, q, s = qlora_nf4_bytes(n, k)
-        return NF4Weight(n, k, u8(c), u8(q), f32(s), fmt)
+            return NF4Weight(n, k, u8(c), None, f32(s), fmt, block)
+        return NF4Weight(n, k, u8(c), u8(q), f32(s), fmt, block)
 
     def nbytes(self) -> int:
         q = self.qscale.numel() if self.qscale is not None else 0
@@ -208,12 +219,13 @@ def _bf16(t, name):
 
 
 def qlora_quantize(W: torch.Tensor, codebook: torch.Tensor | None, out: NF4Weight | None = None,
-                   double_quant: bool = True, fmt: int = QLORA_FMT_NF4) -> NF4Weight:
+                   double_quant: bool = True, fmt: int = QLORA_FMT_NF4, block: int = 64) -> NF4Weight:
     """Quantize W; the format follows `out` when given, else `fmt` and (NF4)
-    `double_quant`.  The codebook is used by NF4 only (None otherwise)."""
+    `double_quant` and `block`.  The codebook is used by NF4 only (None
+    otherwise)."""
     _bf16(W, "W")
     n, k = W.shape
-    out = out if out is not None else NF4Weight.empty(n, k, W.device, double_quant, fmt)
+    out = out if out is not None else NF4Weight.empty(n, k, W.device, double_quant, fmt, block)
     d = out.desc()
     _check(lib().qlora_quantize(_ptr(W), _ptr(codebook), ctypes.byref(d), _stream()),
            "qlora_quantize")

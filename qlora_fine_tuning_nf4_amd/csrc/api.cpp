@@ -151,10 +151,26 @@ bool shape_ok(int64_t n, int64_t k) {
          n <= ((int64_t(1) << 38) - 1) / k;
 }
 
+// NF4 block size of a descriptor (0 means 64); 0 for an invalid one.
+int nf4_block(const qlora_nf4* W) {
+  const int b = W->block == 0 ? 64 : W->block;
+  if (W->format != QLORA_FMT_NF4) return b == 64 ? 64 : 0;
+  return (b == 32 || b == 64 || b == 128) ? b : 0;
+}
+
+// Shape limits of a block size: block 128 needs whole 128-blocks per row,
+// block 32 keeps its block count below 2^32.
+bool block_shape_ok(int64_t n, int64_t k, int block) {
+  if (block == 128 && k % 128 != 0) return false;
+  if (block == 32 && n > ((int64_t(1) << 37) - 1) / k) return false;
+  return true;
+}
+
 // The arrays each format uses (NF4: qscale NULL selects the single-level
 // scales), their alignment, the shape.
 int check_desc(const qlora_nf4* W) {
   if (!W) return QLORA_ERR_NULL;
+  if (!nf4_block(W)) return QLORA_ERR_ARG;
   switch (W->format) {
     case QLORA_FMT_NF4:
       if (!W->codes || !W->step) return QLORA_ERR_NULL;
@@ -169,7 +185,7 @@ int check_desc(const qlora_nf4* W) {
     default:
       return QLORA_ERR_ARG;
   }
-  if (!shape_ok(W->n, W->k)) return QLORA_ERR_SHAPE;
+  if (!shape_ok(W->n, W->k) || !block_shape_ok(W->n, W->k, nf4_block(W))) return QLORA_ERR_SHAPE;
   if (!aligned(W->codes, 16)) return QLORA_ERR_ALIGN;
   if (W->format == QLORA_FMT_NF4 && !aligned(W->step, 4)) return QLORA_ERR_ALIGN;
   if (W->format == QLORA_FMT_U4_ASYM && !aligned(W->step, 8)) return QLORA_ERR_ALIGN;
@@ -188,7 +204,14 @@ int kernel_fmt(const qlora_nf4* W) {
   switch (W->format) {
     case QLORA_FMT_U4_ASYM: return ql::kFmtU4;
     case QLORA_FMT_Q8_0: return ql::kFmtQ8;
-    default: return W->qscale ? ql::kFmtNf4Dq : ql::kFmtNf4;
+    default: {
+      const bool dq = W->qscale != nullptr;
+      switch (nf4_block(W)) {
+        case 32: return dq ? ql::kFmtNf4Dq32 : ql::kFmtNf4_32;
+        case 128: return dq ? ql::kFmtNf4Dq128 : ql::kFmtNf4_128;
+        default: return dq ? ql::kFmtNf4Dq : ql::kFmtNf4;
+      }
+    }
   }
 }
 
@@ -245,6 +268,17 @@ int qlora_nf4_single_bytes(int64_t n, int64_t k, size_t* codes, size_t* absmax) 
   if (!shape_ok(n, k)) return QLORA_ERR_SHAPE;
   if (codes) *codes = (size_t)(n * k / 2);
   if (absmax) *absmax = sizeof(float) * (size_t)(n * (k / kB));
+  return QLORA_OK;
+}
+
+int qlora_nf4_block_bytes(int64_t n, int64_t k, int block, int double_quant, size_t* codes,
+                          size_t* qscale, size_t* step) {
+  if (block != 32 && block != 64 && block != 128) return QLORA_ERR_ARG;
+  if (!shape_ok(n, k) || !block_shape_ok(n, k, block)) return QLORA_ERR_SHAPE;
+  const size_t nb = (size_t)(n * k / block);
+  if (codes) *codes = (size_t)(n * k / 2);
+  if (qscale) *qscale = double_quant ? nb : 0;
+  if (step) *step = double_quant ? sizeof(float) * ((nb + kG - 1) / kG) : sizeof(float) * nb;
   return QLORA_OK;
 }
 
@@ -422,10 +456,9 @@ int qlora_group_init(qlora_group* g, const qlora_fwd_job* jobs, int count, int64
 int qlora_linear_fwd_grouped(const qlora_group* g, const float* codebook, void* stream) {
   if (!g || !g->table) return QLORA_ERR_NULL;
   if (g->count < 1 || g->m < 1 || g->m > QLORA_GEMV_MAX_M || g->lora_count < 0 ||
-      g->lora_count > g->count || g->row_groups < 1 || g->variant < ql::kFmtNf4Dq ||
-      g->variant > ql::kFmtQ8)
+      g->lora_count > g->count || g->row_groups < 1 || g->variant < 0 || g->variant >= ql::kNumFmt)
     return QLORA_ERR_ARG;
-  const bool nf4 = g->variant == ql::kFmtNf4Dq || g->variant == ql::kFmtNf4;
+  const bool nf4 = g->variant != ql::kFmtU4 && g->variant != ql::kFmtQ8;
   if (nf4 && !codebook) return QLORA_ERR_NULL;
   if (nf4 && !aligned(codebook, 4)) return QLORA_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;

@@ -26,11 +26,19 @@ constexpr int kWave = 64;
 //   kFmtNf4    32 code bytes, the fp32 absmax
 //   kFmtU4     32 code bytes (uint4, NF4 packing), fp32 scale and zero-point
 //   kFmtQ8     64 int8 bytes, two fp16 scales (elements 0-31, 32-63)
+// NF4 at block 32 keeps two scales per unit (at 2p, 2p + 1), at block 128 one
+// scale per two units of a row, stored in the same row-group order over the
+// k/128 block columns.
 template <int FMT>
 struct FmtInfo {
-  static constexpr bool nf4 = FMT == kFmtNf4Dq || FMT == kFmtNf4;     // decodes through the codebook
+  static constexpr bool nf4 = FMT != kFmtU4 && FMT != kFmtQ8;        // decodes through the codebook
+  static constexpr bool dq = FMT == kFmtNf4Dq || FMT == kFmtNf4Dq32 || FMT == kFmtNf4Dq128;
+  static constexpr int block = (FMT == kFmtNf4Dq32 || FMT == kFmtNf4_32)    ? 32
+                               : (FMT == kFmtNf4Dq128 || FMT == kFmtNf4_128) ? 128
+                                                                             : 64;
   static constexpr int code_bytes = FMT == kFmtQ8 ? 64 : 32;         // per unit
-  static constexpr int param_bytes = FMT == kFmtNf4Dq ? 1 : (FMT == kFmtU4 ? 8 : 4);
+  // bytes of one scale entry: 8-bit scale, fp32 absmax, uint4 pair, Q8_0 pair
+  static constexpr int param_bytes = dq ? 1 : (FMT == kFmtU4 ? 8 : 4);
 };
 
 // D[16x16] += A[16x32] * B[32x16], bf16 operands, fp32 accumulate.
@@ -151,6 +159,28 @@ QL_DEV u32x4_t decode8(const Lut& t, uint32_t x) {
   o[2] = perm(hib, lob, 0x05010400u);
   o[3] = perm(hib, lob, 0x07030602u);
   return o;
+}
+
+// Lookup table for block-32 NF4: the two lanes of each half of a DPP quad
+// share a scale s (lanes 0, 1 the unit's first 32 weights, lanes 2, 3 the
+// rest); lane q computes entries 8 (q & 1) .. +7 (lv8[i] = level[8 (q & 1) +
+// i]) and the pair exchanges its planes with quad_perm [0,0,2,2] / [1,1,3,3].
+QL_DEV Lut make_lut_pair(const float* lv8, float s) {
+  uint32_t d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = pack_bf16x2(lv8[2 * i] * s, lv8[2 * i + 1] * s);
+  const uint32_t lo0 = perm(d[1], d[0], 0x06040200u), hi0 = perm(d[1], d[0], 0x07050301u);
+  const uint32_t lo1 = perm(d[3], d[2], 0x06040200u), hi1 = perm(d[3], d[2], 0x07050301u);
+  Lut t;
+  t.lo[0] = __builtin_amdgcn_mov_dpp(lo0, 0xA0, 0xF, 0xF, false);
+  t.lo[1] = __builtin_amdgcn_mov_dpp(lo1, 0xA0, 0xF, 0xF, false);
+  t.lo[2] = __builtin_amdgcn_mov_dpp(lo0, 0xF5, 0xF, 0xF, false);
+  t.lo[3] = __builtin_amdgcn_mov_dpp(lo1, 0xF5, 0xF, 0xF, false);
+  t.hi[0] = __builtin_amdgcn_mov_dpp(hi0, 0xA0, 0xF, 0xF, false);
+  t.hi[1] = __builtin_amdgcn_mov_dpp(hi1, 0xA0, 0xF, 0xF, false);
+  t.hi[2] = __builtin_amdgcn_mov_dpp(hi0, 0xF5, 0xF, 0xF, false);
+  t.hi[3] = __builtin_amdgcn_mov_dpp(hi1, 0xF5, 0xF, 0xF, false);
+  return t;
 }
 
 // Q8_0: four int8 values (one packed word, element order) times the block

@@ -234,25 +234,42 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
   using FI = FmtInfo<FMT>;
   constexpr uint32_t CB = FI::code_bytes, PB = FI::param_bytes;
   constexpr uint32_t kOut = 0x80000000u;
+  // NF4 scale entries: block 64 one per unit (its position), block 32 two
+  // per unit (2p + half), block 128 one per unit pair, in the row-group order
+  // over the k/128 block columns (nkb2); the second-level constant of flat
+  // block b is step[b / 256].
+  constexpr int BS = FI::block;
+  const int64_t nkb2 = nkb / 2;
+  const uint32_t hq = (uint32_t)(q >> 1);   // block 32: the lane's half of its unit
   const int64_t kb_dx = o0 / kBlock + wcb;
   const int64_t fg0 = (o0 + wr) & ~int64_t(15);
   const bool f_ok = (o0 + wr) < N;
   const uint32_t fR = f_ok ? (uint32_t)min(int64_t(16), N - fg0) : 16u;
   const uint32_t f_prel = (uint32_t)((fg0 - o0) * nkb + (o0 + wr - fg0));   // fp0 - o0 * nkb
+  const uint32_t f_prel2 = (uint32_t)((fg0 - o0) * nkb2 + (o0 + wr - fg0));
   const bool d_kok = kb_dx < nkb;
   const uint32_t d_prel = (uint32_t)((wr & ~15) * nkb + kb_dx * 16 + (wr & 15));
+  const uint32_t d_prel2 = (uint32_t)((wr & ~15) * nkb2 + (kb_dx >> 1) * 16 + (wr & 15));
+  auto sent = [&](uint32_t prel, uint32_t prel2) -> uint32_t {   // scale entry of the lane's unit
+    return BS == 64 ? prel : (BS == 32 ? 2 * prel + hq : prel2);
+  };
   const uint32_t c_vo0 =
       DX ? (d_kok ? d_prel * CB + q * (CB / 4) : kOut) : (f_ok ? f_prel * CB + q * (CB / 4) : kOut);
-  const uint32_t p_vo0 = DX ? (d_kok ? d_prel * PB : kOut) : (f_ok ? f_prel * PB : kOut);
-  const uint32_t b_lane = (uint32_t)(DX ? wr * nkb + kb_dx : (o0 + wr) * nkb);
-  const auto step_rsrc = buf_rsrc(w.step, (uint32_t)(((N * nkb + kGroup - 1) / kGroup) * 4));
+  const uint32_t p_vo0 =
+      DX ? (d_kok ? sent(d_prel, d_prel2) * PB : kOut) : (f_ok ? sent(f_prel, f_prel2) * PB : kOut);
+  const uint32_t b_lane = (uint32_t)(BS == 64    ? (DX ? wr * nkb + kb_dx : (o0 + wr) * nkb)
+                                     : BS == 32 ? 2 * (DX ? wr * nkb + kb_dx : (o0 + wr) * nkb) + hq
+                                                : (DX ? wr * nkb2 + (kb_dx >> 1) : (o0 + wr) * nkb2));
+  const auto step_rsrc = buf_rsrc(w.step, (uint32_t)(((N * K / BS + kGroup - 1) / kGroup) * 4));
   auto load_w = [&](int st, WRaw& r) {
     uint32_t cvo, pvo, bidx;
     int64_t pbase;   // storage position of the per-step (backward) or per-tile (forward) base
+    int64_t sbase;   // its scale entry
     if (DX) {
       const int64_t n0 = (int64_t)st * GBK;
       pbase = n0 * nkb;
-      bidx = b_lane + (uint32_t)(n0 * nkb);
+      sbase = BS == 64 ? pbase : (BS == 32 ? 2 * pbase : n0 * nkb2);
+      bidx = b_lane + (uint32_t)sbase;
       if (st < full_steps) {
         cvo = c_vo0;
         pvo = p_vo0;
@@ -260,14 +277,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
         const int64_t g0 = (wr & ~15), R = min(int64_t(16), N - n0 - g0);
         const bool ok = d_kok && n0 + wr < N;
         const uint32_t prel = (uint32_t)(g0 * nkb + kb_dx * R + (wr & 15));
+        const uint32_t prel2 = (uint32_t)(g0 * nkb2 + (kb_dx >> 1) * R + (wr & 15));
         cvo = ok ? prel * CB + q * (CB / 4) : kOut;
-        pvo = ok ? prel * PB : kOut;
+        pvo = ok ? sent(prel, prel2) * PB : kOut;
       }
     } else {
       pbase = o0 * nkb;
+      sbase = BS == 64 ? pbase : (BS == 32 ? 2 * pbase : o0 * nkb2);
+      const uint32_t sinc = BS == 64 ? (uint32_t)st : (BS == 32 ? 2u * st : (uint32_t)st >> 1);
       cvo = c_vo0 + (uint32_t)st * fR * CB;
-      pvo = p_vo0 + (uint32_t)st * fR * PB;
-      bidx = b_lane + (uint32_t)st;
+      pvo = p_vo0 + sinc * fR * PB;
+      bidx = b_lane + sinc;
     }
     const auto crs = buf_rsrc(w.codes + pbase * CB);
     if constexpr (FMT == kFmtQ8) {
@@ -276,12 +296,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     } else {
       const u32x2_t c = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(crs, cvo, 0, 0));
       r.codes = u32x4_t{c[0], c[1], 0u, 0u};
-      if constexpr (FMT == kFmtNf4Dq) {
-        r.qbyte = __builtin_amdgcn_raw_buffer_load_b8(buf_rsrc(w.qscale + pbase), pvo, 0, 0);
+      if constexpr (FI::nf4 && FI::dq) {
+        r.qbyte = __builtin_amdgcn_raw_buffer_load_b8(buf_rsrc(w.qscale + sbase), pvo, 0, 0);
         r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(step_rsrc, (bidx >> 8) * 4, 0, 0));
-      } else if constexpr (FMT == kFmtNf4) {
+      } else if constexpr (FI::nf4) {
         r.qbyte = 1u;   // scale = 1 * absmax, exact
-        r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(w.step + pbase), pvo, 0, 0));
+        r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(w.step + sbase), pvo, 0, 0));
       } else {
         // two dword loads (the backend merges them): a 64-bit buffer load
         // whose halves are bit-cast to float is shrunk to one dword by this
@@ -292,7 +312,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       }
     }
   };
-  float lvq[4] = {0.f, 0.f, 0.f, 0.f};   // NF4: level[4q + i] (set once the codebook is in LDS)
+  // NF4 levels of this lane's table entries (set once the codebook is in
+  // LDS): level[4q + i], or for block 32 level[8 (q & 1) + i]
+  float lvq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   // Decode this lane's 16 weights into the stage: the 4-bit formats through a
   // per-block table built by the quad (entries level[c] * s for NF4,
   // (c - zp) * scale for uint4); Q8_0 bytes times the fp16 scale of the
@@ -315,7 +337,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
         for (int i = 0; i < 4; ++i) lvr[i] = lvq[i];
         sc = (float)r.qbyte * r.step;
       }
-      const Lut t = make_lut_quad(lvr, sc);
+      // block 32: the half-quads hold different scales, so each lane pair
+      // builds its own table
+      const Lut t = BS == 32 ? make_lut_pair(lvq, sc) : make_lut_quad(lvr, sc);
       dst[0] = decode8(t, r.codes[0]);
       dst[1] = decode8(t, r.codes[1]);
     }
@@ -353,8 +377,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
 
   __syncthreads();
   if constexpr (FmtInfo<FMT>::nf4) {
+    if constexpr (FmtInfo<FMT>::block == 32) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lvq[i] = s_lv[4 * q + i];
+      for (int i = 0; i < 8; ++i) lvq[i] = s_lv[8 * (q & 1) + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lvq[i] = s_lv[4 * q + i];
+    }
   }
 
   f32x16_t acc[2][4];
@@ -660,7 +689,11 @@ static hipError_t launch_fmt(dim3 grid, hipStream_t s, const uint16_t* act, cons
     case kFmtNf4Dq: return QL_ONE(kFmtNf4Dq);
     case kFmtNf4: return QL_ONE(kFmtNf4);
     case kFmtU4: return QL_ONE(kFmtU4);
-    default: return QL_ONE(kFmtQ8);
+    case kFmtQ8: return QL_ONE(kFmtQ8);
+    case kFmtNf4Dq32: return QL_ONE(kFmtNf4Dq32);
+    case kFmtNf4_32: return QL_ONE(kFmtNf4_32);
+    case kFmtNf4Dq128: return QL_ONE(kFmtNf4Dq128);
+    default: return QL_ONE(kFmtNf4_128);
   }
 #undef QL_ONE
 }

@@ -72,7 +72,7 @@ struct GemvRaw {
   u32x4_t c[FMT == kFmtQ8 ? 4 : 2];   // the lane's unit: 32 code bytes, or 64 int8 values
   uint32_t qbyte;   // NF4 with double quantization: the 8-bit scale; Q8_0: the two fp16 scales
   float step;       // NF4: the group's fp32 constant, or the block absmax; uint4: the scale
-  float zp;         // uint4: the zero-point
+  float zp;         // uint4: the zero-point; NF4 single level at block 32: the second half's absmax
 };
 
 constexpr int GV_CHUNK_BYTES = 512;   // one row of an activation chunk: 256 bf16
@@ -160,15 +160,22 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
                                                x_vo[t], 0, 0, 0);
     }
   };
-  // block (nn, 4q + g) sits at storage position gg * nkb + 4q * R + (g * R + nn - gg)
+  // unit (nn, 4q + g) sits at storage position gg * nkb + 4q * R + (g * R + nn - gg)
   const uint32_t w_lane = (uint32_t)(g * R + (nn - gg));
-  const uint32_t b_lane = (uint32_t)(nn * nkb + g);          // flat block index at q = 0
   const int64_t nblk = N * nkb;
-  const auto step_rsrc = buf_rsrc(w.step, (uint32_t)(((nblk + kGroup - 1) / kGroup) * 4));
+  // NF4 scale entries: block 64 at the unit's position, block 32 the pair at
+  // 2p, 2p + 1, block 128 at (nn, 2q + g/2) in the row-group order over the
+  // k/128 columns (nkb2); the second-level constant of flat block b is
+  // step[b / 256]
+  constexpr int BS = FI::block;
+  const int64_t nkb2 = nkb / 2;
+  const int64_t nsc = N * K / BS;                               // scale entries
+  const uint32_t w_lane2 = (uint32_t)((g >> 1) * R + (nn - gg));
+  const uint32_t b_lane = (uint32_t)(BS == 64 ? nn * nkb + g : (BS == 32 ? 2 * (nn * nkb + g) : nn * nkb2 + (g >> 1)));
+  const auto step_rsrc = buf_rsrc(w.step, (uint32_t)(((nsc + kGroup - 1) / kGroup) * 4));
   // per-unit data at the storage position: CB code bytes, then the 8-bit
-  // scale (double quantization; the fp32 constant of flat block b at
-  // step[b / 256]), the fp32 absmax, the uint4 scale and zero-point, or the
-  // two Q8_0 scales
+  // scale(s) (double quantization), the fp32 absmax(es), the uint4 scale and
+  // zero-point, or the two Q8_0 scales
   auto load_w = [&](int q, GemvRaw<FMT>& u) {
     const int qc = min(q, nquads - 1);
     const int64_t ub = gg * nkb + (int64_t)4 * qc * R;
@@ -176,15 +183,22 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
 #pragma unroll
     for (int j = 0; j < NC; ++j)
       u.c[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, w_lane * CB + 16 * j, 0, 0));
-    if constexpr (FMT == kFmtNf4Dq) {
-      const auto rq = buf_rsrc(w.qscale + ub, rsrc_bytes(nblk - ub));
-      u.qbyte = __builtin_amdgcn_raw_buffer_load_b8(rq, w_lane, 0, 0);
+    // scale entry base (uniform) and this lane's entry offset
+    const int64_t sb = BS == 64 ? ub : (BS == 32 ? 2 * ub : gg * nkb2 + (int64_t)2 * qc * R);
+    const uint32_t so = BS == 64 ? w_lane : (BS == 32 ? 2 * w_lane : w_lane2);
+    const uint32_t bq = BS == 64 ? 4u * qc : (BS == 32 ? 8u * qc : 2u * qc);   // flat block advance
+    if constexpr (FI::nf4 && FI::dq) {
+      const auto rq = buf_rsrc(w.qscale + sb, rsrc_bytes(nsc - sb));
+      u.qbyte = BS == 32 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rq, so, 0, 0)
+                         : (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rq, so, 0, 0);
       u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                             step_rsrc, ((b_lane + 4 * (uint32_t)qc) >> 8) * 4, 0, 0));
-    } else if constexpr (FMT == kFmtNf4) {
+                                             step_rsrc, ((b_lane + bq) >> 8) * 4, 0, 0));
+    } else if constexpr (FI::nf4) {
+      const auto rs = buf_rsrc(w.step + sb, rsrc_bytes((nsc - sb) * 4));
       u.qbyte = 1u;
-      u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                             buf_rsrc(w.step + ub, rsrc_bytes((nblk - ub) * 4)), w_lane * 4, 0, 0));
+      u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, so * 4, 0, 0));
+      if constexpr (BS == 32)
+        u.zp = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, so * 4 + 4, 0, 0));
     } else if constexpr (FMT == kFmtU4) {
       // two dword loads: a 64-bit buffer load whose halves are bit-cast to
       // float is shrunk to one dword by this compiler, both halves then
@@ -236,25 +250,38 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) lvu[i] = lv[i];
-        scr = (float)u.qbyte * u.step;
+        scr = (float)(u.qbyte & 0xFFu) * u.step;
       }
       const Lut t = make_lut(lvu, ok ? scr : 0.f);
+      if constexpr (BS == 32) {
+        // words 4-7 are the second 32-weight block: its own scale and table
+        const float scr1 = FI::dq ? (float)(u.qbyte >> 8) * u.step : u.zp;
+        const Lut t1 = make_lut(lvu, ok ? scr1 : 0.f);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const u32x4_t bf = decode8(t, u.c[i >> 2][i & 3]);
+        for (int i = 0; i < 8; ++i) {
+          const u32x4_t bf = decode8(i < 4 ? t : t1, u.c[i >> 2][i & 3]);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt][i & 1] = mfma16x16x32(af[mt][i], bf, acc[mt][i & 1]);
+          for (int mt = 0; mt < MT; ++mt) acc[mt][i & 1] = mfma16x16x32(af[mt][i], bf, acc[mt][i & 1]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const u32x4_t bf = decode8(t, u.c[i >> 2][i & 3]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt][i & 1] = mfma16x16x32(af[mt][i], bf, acc[mt][i & 1]);
+        }
       }
     }
   };
 
   // wait for this wave's loads of quad q (everything but the loads issued in
   // the following iteration: NC code loads, one or two parameter loads and
-  // XPW chunk loads), then barrier.  The uint4 pair counts as one load: the
-  // backend may merge its two dword loads, and where it does not, the count
-  // only waits for one load of the next quad as well.
+  // XPW chunk loads), then barrier.  The uint4 pair and the block-32 absmax
+  // pair count as one load: the backend may merge their two dword loads, and
+  // where it does not, the count only waits for one load of the next quad as
+  // well.
   auto wait_q = [&]() {
-    QL_VMCNT(NC + (FMT == kFmtNf4Dq ? 2 : 1) + XPW);
+    QL_VMCNT(NC + (FI::dq ? 2 : 1) + XPW);
     QL_LGKMCNT0();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -333,7 +360,11 @@ static void gemv_launch(int fmt, dim3 grid, hipStream_t s, const GemvJob& job1, 
     case kFmtNf4Dq: QL_GEMV(kFmtNf4Dq); break;
     case kFmtNf4: QL_GEMV(kFmtNf4); break;
     case kFmtU4: QL_GEMV(kFmtU4); break;
-    default: QL_GEMV(kFmtQ8); break;
+    case kFmtQ8: QL_GEMV(kFmtQ8); break;
+    case kFmtNf4Dq32: QL_GEMV(kFmtNf4Dq32); break;
+    case kFmtNf4_32: QL_GEMV(kFmtNf4_32); break;
+    case kFmtNf4Dq128: QL_GEMV(kFmtNf4Dq128); break;
+    default: QL_GEMV(kFmtNf4_128); break;
   }
 #undef QL_GEMV
 }

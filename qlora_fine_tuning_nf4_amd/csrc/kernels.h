@@ -6,8 +6,14 @@
 
 namespace ql {
 
-// Weight formats as the kernels see them (a template parameter of each kernel).
-enum WFmt : int { kFmtNf4Dq = 0, kFmtNf4 = 1, kFmtU4 = 2, kFmtQ8 = 3 };
+// Weight formats as the kernels see them (a template parameter of each kernel):
+// NF4 with double-quantized (Dq) or single-level scales at block 64, 32 or
+// 128, asymmetric uint4, Q8_0.
+enum WFmt : int {
+  kFmtNf4Dq = 0, kFmtNf4 = 1, kFmtU4 = 2, kFmtQ8 = 3,
+  kFmtNf4Dq32 = 4, kFmtNf4_32 = 5, kFmtNf4Dq128 = 6, kFmtNf4_128 = 7
+};
+constexpr int kNumFmt = 8;
 
 // LoRA term added by epilogues:  out[m][c] += scaling * sum_j L[m*r + j] * R[c*rs_c + j*rs_j]
 struct LoraTerm {

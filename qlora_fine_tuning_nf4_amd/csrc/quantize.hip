@@ -66,31 +66,41 @@ QL_DEV uint32_t encode8(const float (&xin)[8], float am, const float2* tab) {
   return word;
 }
 
-// One workgroup per group of 256 blocks (16384 weights, 32 KiB of bf16) at a
-// time, walking groups with the grid as stride; the next group's loads are
-// issued before the current one is encoded.  Each wave handles 8 blocks per
-// step: lane l reads 16 bytes (8 weights) of block l/8, so one wave load is
-// 1 KiB contiguous.  The block absmax is a max over the 8 lanes of the block;
-// encoding needs only the block's own absmax, so codes are written in the
-// same pass and the group max is taken afterwards from LDS.  Without double
-// quantization (DQ false) the block absmax itself is stored, fp32, at the
-// block's storage position in `step`, and `qscale` is unused.
-template <bool DQ>
+// One workgroup per group of 256 blocks (BS weights each; 16384 weights, 32
+// KiB of bf16 at BS = 64) at a time, walking groups with the grid as stride;
+// the next group's loads are issued before the current one is encoded.  Lane
+// l reads 16 bytes (8 weights) of block l / LB (LB = BS / 8 lanes per block),
+// so one wave load is 1 KiB contiguous.  The block absmax is a max over the
+// LB lanes of the block; encoding needs only the block's own absmax, so codes
+// are written in the same pass and the group max is taken afterwards from
+// LDS.  Codes keep the 64-weight unit layout whatever the block: the lane's
+// word is word w of unit (row, u) with 64 u + 8 w its first element.  Scale
+// entries: block 64 at the unit's storage position, block 32 at 2 p + half,
+// block 128 at the row-group position over the k/128 block columns.  Without
+// double quantization (DQ false) the block absmax itself is stored, fp32, in
+// `step`, and `qscale` is unused.
+template <bool DQ, int BS>
 __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict__ W,
                                                       const float* __restrict__ codebook,
                                                       uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ qscale,
                                                       float* __restrict__ step, int64_t N,
                                                       int64_t nkb) {
+  constexpr int LB = BS / 8;                 // lanes per block
+  constexpr int BPW = 64 / LB;               // blocks per wave load
+  constexpr int BPI = 4 * BPW;               // blocks per workgroup step
+  constexpr int NIT = kGroup / BPI;          // steps per group (= LB)
   __shared__ float s_absmax[kGroup];
   __shared__ float s_red[4];
   __shared__ float2 s_tab[kEncBins];
-  // block counts fit 32 bits (n * k / 64 < 2^32 for any weight the ABI
-  // accepts), so block coordinates use 32-bit division
-  const uint32_t nblocks = (uint32_t)(N * nkb), ukb = (uint32_t)nkb;
+  // block counts fit 32 bits (the ABI keeps n * k / BS below 2^32), so block
+  // coordinates use 32-bit division
+  const uint32_t ukbB = (uint32_t)(nkb * 64 / BS);   // blocks per row
+  const uint32_t nblocks = (uint32_t)(N * ukbB);
   const uint32_t ngroups = (nblocks + kGroup - 1) / kGroup;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lb0 = wave * 8 + (lane >> 3);
+  const int lb0 = wave * BPW + lane / LB;
+  const int lw = lane % LB;                  // the lane's 8-weight piece of its block
 
   {
     float mid[15];
@@ -99,27 +109,33 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
     build_encode_table(mid, s_tab, tid, 256);
   }
 
-  // the eight 16-byte loads of this lane for group grp (a short last group
+  // the NIT 16-byte loads of this lane for group grp (a short last group
   // re-reads its last block; those lanes are not stored)
-  auto load_group = [&](uint32_t grp, u32x4_t (&r)[kGroup / 32]) {
+  auto load_group = [&](uint32_t grp, u32x4_t (&r)[NIT]) {
     const uint32_t blk0 = grp * kGroup;
     const int nb = (int)min(kGroup, nblocks - blk0);
 #pragma unroll
-    for (int it = 0; it < kGroup / 32; ++it) {
-      const int lb = min(it * 32 + lb0, nb - 1);
-      r[it] = *reinterpret_cast<const u32x4_t*>(W + ((int64_t)blk0 + lb) * kBlock + (lane & 7) * 8);
+    for (int it = 0; it < NIT; ++it) {
+      const int lb = min(it * BPI + lb0, nb - 1);
+      r[it] = *reinterpret_cast<const u32x4_t*>(W + ((int64_t)blk0 + lb) * BS + lw * 8);
     }
   };
+  // storage entry of the scale of block (row, kb)
+  auto scale_pos = [&](uint32_t row, uint32_t kb) -> int64_t {
+    if (BS == 64) return blk_pos(row, kb, N, nkb);
+    if (BS == 32) return 2 * blk_pos(row, kb >> 1, N, nkb) + (kb & 1);
+    return blk_pos(row, kb, N, nkb / 2);
+  };
 
-  auto do_group = [&](uint32_t grp, const u32x4_t (&cur)[kGroup / 32]) {
+  auto do_group = [&](uint32_t grp, const u32x4_t (&cur)[NIT]) {
     const uint32_t blk0 = grp * kGroup;
     const int nb = (int)min(kGroup, nblocks - blk0);
-    // (row, k-block) of this lane's block, advanced by 32 blocks per step
-    uint32_t row = (blk0 + lb0) / ukb;
-    uint32_t kb = (blk0 + lb0) - row * ukb;
+    // (row, block column) of this lane's block, advanced by BPI blocks per step
+    uint32_t row = (blk0 + lb0) / ukbB;
+    uint32_t kb = (blk0 + lb0) - row * ukbB;
 #pragma unroll
-    for (int it = 0; it < kGroup / 32; ++it) {
-      const int lb = it * 32 + lb0;                    // local block index
+    for (int it = 0; it < NIT; ++it) {
+      const int lb = it * BPI + lb0;                    // local block index
       float x[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -129,23 +145,23 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
       float am = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
-      am = fmaxf(am, __shfl_xor(am, 1));
-      am = fmaxf(am, __shfl_xor(am, 2));
-      am = fmaxf(am, __shfl_xor(am, 4));
+#pragma unroll
+      for (int o = 1; o < LB; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));
       const uint32_t word = encode8(x, am, s_tab);
       if (lb < nb) {
-        const int64_t p = blk_pos(row, kb, N, nkb);
-        reinterpret_cast<uint32_t*>(codes)[p * 8 + (lane & 7)] = word;
-        if ((lane & 7) == 0) {
+        const uint32_t e0 = kb * BS + lw * 8;           // first element within the row
+        const int64_t p = blk_pos(row, e0 >> 6, N, nkb);
+        reinterpret_cast<uint32_t*>(codes)[p * 8 + ((e0 & 63) >> 3)] = word;
+        if (lw == 0) {
           if (DQ)
             s_absmax[lb] = am;
           else
-            step[p] = am;
+            step[scale_pos(row, kb)] = am;
         }
       }
-      kb += 32;
-      while (kb >= ukb) {
-        kb -= ukb;
+      kb += BPI;
+      while (kb >= ukbB) {
+        kb -= ukbB;
         ++row;
       }
     }
@@ -159,8 +175,8 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
     const float st = c2 / 255.0f;
     if (tid < nb) {
       const float q = st == 0.f ? 0.f : fminf(rintf(a / st), 255.f);
-      const uint32_t b = blk0 + tid, br = b / ukb;
-      qscale[blk_pos(br, b - br * ukb, N, nkb)] = (uint8_t)q;
+      const uint32_t b = blk0 + tid, br = b / ukbB;
+      qscale[scale_pos(br, b - br * ukbB)] = (uint8_t)q;
     }
     if (tid == 0) step[grp] = st;
     __syncthreads();   // s_absmax and s_red are reused by the next group
@@ -173,7 +189,7 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
   const uint32_t per_xcd = gridDim.x / 8;
   const uint32_t lwg = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   // ping-pong between two register sets (no copies of in-flight loads)
-  u32x4_t ra[kGroup / 32], rb[kGroup / 32];
+  u32x4_t ra[NIT], rb[NIT];
   uint32_t grp = lwg;
   if (grp < ngroups) load_group(grp, ra);
   __syncthreads();   // encode table ready
@@ -303,7 +319,7 @@ __global__ __launch_bounds__(256) void k_dequant(Nf4View w, const float* __restr
     }
   } else {
     float lv[16];
-    float s;
+    float s = 0.f;
     if constexpr (FMT == kFmtU4) {
       const float2 sz = reinterpret_cast<const float2*>(w.step)[p];
       const int zp = (int)sz.y;   // c - zp is formed exactly as an integer (c == zp gives +0)
@@ -313,12 +329,34 @@ __global__ __launch_bounds__(256) void k_dequant(Nf4View w, const float* __restr
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) lv[i] = s_lv[i];
-      s = FMT == kFmtNf4Dq ? block_scale(w.qscale, w.step, b, p) : w.step[p];
     }
-    const Lut t = make_lut(lv, s);
+    // the scale of each half of the unit (the same unless the block is 32)
+    float sh[2];
+    if constexpr (FMT == kFmtU4) {
+      sh[0] = sh[1] = s;
+    } else {
+      constexpr int BS = FmtInfo<FMT>::block;
+      const int64_t row = b / nkb, kb = b - row * nkb;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int64_t e, fb;   // scale entry, flat block
+        if (BS == 64) {
+          e = p;
+          fb = b;
+        } else if (BS == 32) {
+          e = 2 * p + h;
+          fb = 2 * b + h;
+        } else {
+          e = blk_pos(row, kb >> 1, N, nkb / 2);
+          fb = row * (nkb / 2) + (kb >> 1);
+        }
+        sh[h] = FmtInfo<FMT>::dq ? (float)w.qscale[e] * w.step[fb / kGroup] : w.step[e];
+      }
+    }
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w.codes + p * 32);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      const Lut t = make_lut(lv, sh[h]);
       const u32x4_t c = src[h];
 #pragma unroll
       for (int j = 0; j < 4; ++j) dst[h * 4 + j] = decode8(t, c[j]);
@@ -375,20 +413,23 @@ hipError_t launch_merge(uint16_t* W, const uint16_t* A, const uint16_t* B, int64
 hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* codes,
                            uint8_t* qscale, float* step, int64_t n, int64_t k, int fmt,
                            hipStream_t s) {
-  const int64_t nkb = k / kBlock, nunits = n * nkb, ngroups = (nunits + kGroup - 1) / kGroup;
-  // NF4: persistent workgroups (each walks groups with a stride of the grid),
-  // a few per CU so loads of the next group overlap the current one
-  const int64_t grid = std::min<int64_t>((ngroups + 7) / 8 * 8, 256 * 8);   // multiple of 8
+  const int64_t nkb = k / kBlock, nunits = n * nkb;
   const dim3 ugrid((unsigned)((nunits + 31) / 32));                         // 32 units per workgroup
+  // NF4: persistent workgroups (each walks groups of 256 blocks of the
+  // format's block size with a stride of the grid), a few per CU so loads of
+  // the next group overlap the current one; a multiple of 8
+  const int bs = fmt == kFmtNf4Dq32 || fmt == kFmtNf4_32 ? 32 : (fmt == kFmtNf4Dq128 || fmt == kFmtNf4_128 ? 128 : 64);
+  const int64_t ngB = (n * k / bs + kGroup - 1) / kGroup;
+  const dim3 ggrid((unsigned)std::min<int64_t>((ngB + 7) / 8 * 8, 256 * 8));
+#define QL_QNF4(DQ, BS) \
+  hipLaunchKernelGGL((k_quant_nf4_dq<DQ, BS>), ggrid, dim3(256), 0, s, W, codebook, codes, qscale, step, n, nkb)
   switch (fmt) {
-    case kFmtNf4Dq:
-      hipLaunchKernelGGL(k_quant_nf4_dq<true>, dim3((unsigned)grid), dim3(256), 0, s, W, codebook,
-                         codes, qscale, step, n, nkb);
-      break;
-    case kFmtNf4:
-      hipLaunchKernelGGL(k_quant_nf4_dq<false>, dim3((unsigned)grid), dim3(256), 0, s, W, codebook,
-                         codes, qscale, step, n, nkb);
-      break;
+    case kFmtNf4Dq: QL_QNF4(true, 64); break;
+    case kFmtNf4: QL_QNF4(false, 64); break;
+    case kFmtNf4Dq32: QL_QNF4(true, 32); break;
+    case kFmtNf4_32: QL_QNF4(false, 32); break;
+    case kFmtNf4Dq128: QL_QNF4(true, 128); break;
+    case kFmtNf4_128: QL_QNF4(false, 128); break;
     case kFmtU4:
       hipLaunchKernelGGL(k_quant_u4, ugrid, dim3(256), 0, s, W, codes, step, n, nkb);
       break;
@@ -396,18 +437,25 @@ hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* co
       hipLaunchKernelGGL(k_quant_q8, ugrid, dim3(256), 0, s, W, codes, qscale, n, nkb);
       break;
   }
+#undef QL_QNF4
   return hipGetLastError();
 }
 
 hipError_t launch_dequant(const Nf4View& w, const float* codebook, uint16_t* out, hipStream_t s) {
   const int64_t nblocks = w.n * (w.k / kBlock);
   const dim3 grid((unsigned)((nblocks + 255) / 256));
+#define QL_DQ(F) hipLaunchKernelGGL(k_dequant<F>, grid, dim3(256), 0, s, w, codebook, out)
   switch (w.fmt) {
-    case kFmtNf4Dq: hipLaunchKernelGGL(k_dequant<kFmtNf4Dq>, grid, dim3(256), 0, s, w, codebook, out); break;
-    case kFmtNf4: hipLaunchKernelGGL(k_dequant<kFmtNf4>, grid, dim3(256), 0, s, w, codebook, out); break;
-    case kFmtU4: hipLaunchKernelGGL(k_dequant<kFmtU4>, grid, dim3(256), 0, s, w, codebook, out); break;
-    default: hipLaunchKernelGGL(k_dequant<kFmtQ8>, grid, dim3(256), 0, s, w, codebook, out); break;
+    case kFmtNf4Dq: QL_DQ(kFmtNf4Dq); break;
+    case kFmtNf4: QL_DQ(kFmtNf4); break;
+    case kFmtU4: QL_DQ(kFmtU4); break;
+    case kFmtQ8: QL_DQ(kFmtQ8); break;
+    case kFmtNf4Dq32: QL_DQ(kFmtNf4Dq32); break;
+    case kFmtNf4_32: QL_DQ(kFmtNf4_32); break;
+    case kFmtNf4Dq128: QL_DQ(kFmtNf4Dq128); break;
+    default: QL_DQ(kFmtNf4_128); break;
   }
+#undef QL_DQ
   return hipGetLastError();
 }
 

@@ -79,8 +79,35 @@ def test_strerror_covers_codes():
 FAKE = 0x100000   # never dereferenced: every call below fails validation first
 
 
-def _desc(n=64, k=128, codes=FAKE, qs=FAKE, st=FAKE, fmt=0):
-    return B._Nf4Desc(n, k, codes, qs, st, fmt)
+def _desc(n=64, k=128, codes=FAKE, qs=FAKE, st=FAKE, fmt=0, block=0):
+    return B._Nf4Desc(n, k, codes, qs, st, fmt, block)
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (3, 256), (4096, 11008), (257, 640)])
+@pytest.mark.parametrize("block", [32, 64, 128])
+def test_nf4_block_bytes_match_oracle(n, k, block):
+    assert B.qlora_nf4_block_bytes(n, k, block, True) == nf4.nf4_bytes(n, k, block)
+    codes, absmax = nf4.quantize_nodq(np.zeros((n, k), np.uint16), nf4.codebook()[1], block)
+    assert B.qlora_nf4_block_bytes(n, k, block, False) == (codes.nbytes, 0, absmax.nbytes)
+
+
+def test_block_argument_errors():
+    L = B.lib()
+    z = ctypes.c_size_t()
+    assert L.qlora_nf4_block_bytes(4, 128, 48, 1, ctypes.byref(z), None, None) == 8
+    assert L.qlora_nf4_block_bytes(4, 192, 128, 1, ctypes.byref(z), None, None) == 2   # k % 128
+    assert L.qlora_nf4_block_bytes(1 << 21, 1 << 16, 32, 1, ctypes.byref(z), None, None) == 2   # 2^37
+    assert L.qlora_nf4_block_bytes((1 << 21) - 1, 1 << 16, 32, 1, ctypes.byref(z), None, None) == 0
+
+    def q(d):
+        return L.qlora_quantize(FAKE + 2, FAKE, ctypes.byref(d), None)   # W misaligned: 3 if valid
+    assert q(_desc(block=48)) == 8
+    assert q(_desc(block=-64)) == 8
+    assert q(_desc(fmt=B.QLORA_FMT_U4_ASYM, qs=0, block=32)) == 8         # blocks are NF4 only
+    assert q(_desc(k=192, block=128)) == 2
+    for b in (0, 32, 64, 128):
+        assert q(_desc(k=256, block=b)) == 3
+    assert q(_desc(fmt=B.QLORA_FMT_Q8_0, st=0, block=64)) == 3
 
 
 @pytest.mark.parametrize("n,k", [(1, 64), (3, 128), (3072, 8192), (8192, 3072), (257, 320)])
@@ -269,8 +296,10 @@ def test_grouped_fwd_argument_errors():
                         variant=variant, m=m, row_groups=8, max_quads=1)
     g = grp()
     assert L.qlora_linear_fwd_grouped(ctypes.byref(g), None, None) == 1
-    bad = grp(variant=4)
+    bad = grp(variant=8)
     assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
+    g7 = grp(variant=7)                                   # NF4 block 128: the codebook is required
+    assert L.qlora_linear_fwd_grouped(ctypes.byref(g7), None, None) == 1
     bad = grp(variant=-1)
     assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
     bad = grp(count=0)
