@@ -68,14 +68,16 @@ def flops_bwd(M, N, K, r):
 
 
 # weight format: double-quantized scales (default) or one fp32 absmax per
-# block (--single-level)
+# block (--single-level); NF4 block size (--nf4-block, 64 by default)
 DQ = True
+BLOCK = 64
 
 
 def packed_bytes(N, K):
+    nb = N * K // BLOCK
     if not DQ:
-        return N * K // 2 + 4 * (N * K // 64)
-    return N * K // 2 + N * K // 64 + 4 * ((N * K // 64 + 255) // 256)
+        return N * K // 2 + 4 * nb
+    return N * K // 2 + nb + 4 * ((nb + 255) // 256)
 
 
 def step_bytes(M, N, K, r):
@@ -98,7 +100,7 @@ def traffic_from_profile(kernel, src_files):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source; else None."""
     p = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
-    if not os.path.exists(p):
+    if not os.path.exists(p) or not DQ or BLOCK != 64:   # the counters were taken on that format
         return None
     with open(p) as f:
         d = json.load(f)
@@ -157,7 +159,7 @@ def run_layer7b(args):
     layers = []
     for i, (name, N, K, r) in enumerate(PROJ):
         W = synth.device_normal_bf16((N, K), 0.02, synth.tensor_seed(2, 10 * i), device=dev)
-        q = QB.qlora_quantize(W, cb, double_quant=DQ)
+        q = QB.qlora_quantize(W, cb, double_quant=DQ, block=BLOCK)
         del W
         L = dict(name=name, N=N, K=K, r=r, q=q)
         L["X"] = synth.device_normal_bf16((M, K), 1.0, synth.tensor_seed(2, 10 * i + 1), device=dev)
@@ -247,7 +249,7 @@ def run_layer7b(args):
         "gpu_step_ms": _spread(step_ms),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.02) weights quantized to NF4+DQ, N(0,1) activations)",
-        "config": {"workload": WORKLOAD, "M": M, "r": RANK, "alpha": ALPHA, "double_quant": DQ,
+        "config": {"workload": WORKLOAD, "M": M, "r": RANK, "alpha": ALPHA, "double_quant": DQ, "nf4_block": BLOCK,
                    "projections": [[p[0], p[1], p[2], p[3]] for p in PROJ], "y_dtype": "bf16",
                    "dx_dtype": "bf16", "parallelism": "none (1 GPU)"},
         "effective_GBps": round(gbs, 1),
@@ -312,7 +314,7 @@ def run_decode(args):
         for i, (name, N, K, r) in enumerate(PROJ):
             W = synth.device_normal_bf16((N, K), 0.02, synth.tensor_seed(3, 100 * layer + 10 * i),
                                          device=dev)
-            weights.append((QB.qlora_quantize(W, cb, double_quant=DQ), N, K, r))
+            weights.append((QB.qlora_quantize(W, cb, double_quant=DQ, block=BLOCK), N, K, r))
             del W
     torch.cuda.synchronize()
     per_m = {}
@@ -360,7 +362,7 @@ def run_decode(args):
         "config": {"workload": f"decode sweep: {DECODE_LAYERS} layers x (q,k,v,o 4096x4096; gate,up "
                                "11008x4096; down 4096x11008), M=1, LoRA r=8 alpha=16 on q,k,v,o, "
                                "forward only, one grouped launch per sweep",
-                   "M": 1, "layers": DECODE_LAYERS, "double_quant": DQ, "params": sum(N * K for _, N, K, _ in weights),
+                   "M": 1, "layers": DECODE_LAYERS, "double_quant": DQ, "nf4_block": BLOCK, "params": sum(N * K for _, N, K, _ in weights),
                    "packed_bytes": sum(q.nbytes() for q, *_ in weights), "parallelism": "none (1 GPU)"},
         "per_m": per_m,
         "roofline": {"bound": "hbm", "kernel": "k_gemv_fwd", "achieved": round(achieved, 1),
@@ -424,7 +426,7 @@ def run_quantize70b(args):
     torch.cuda.set_device(dev)
     cb = QB.device_codebook(dev)
     Ws = _weights70(dev)
-    outs = [QB.NF4Weight.empty(N, K, dev, double_quant=DQ) for _, N, K in PROJ70]
+    outs = [QB.NF4Weight.empty(N, K, dev, double_quant=DQ, block=BLOCK) for _, N, K in PROJ70]
     params = sum(N * K for _, N, K in PROJ70)
     nbytes = sum(2 * N * K + packed_bytes(N, K) for _, N, K in PROJ70)
 
@@ -446,7 +448,7 @@ def run_quantize70b(args):
         "data": "synthetic (seeded N(0,0.015) bf16 weights, 0.1% outliers x20)",
         "config": {"workload": "quantize a 70B-style layer: q,k,v,o 8192x8192; gate,up 28672x8192; "
                                "down 8192x28672 (973,078,528 params)", "params": params,
-                   "double_quant": DQ,
+                   "double_quant": DQ, "nf4_block": BLOCK,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "k_quant_nf4_dq", "achieved": round(ach, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
@@ -485,7 +487,7 @@ def run_layer70b(args):
     s = alpha / r
     layers = []
     for i, (W, (name, N, K)) in enumerate(zip(_weights70(dev), PROJ70)):
-        q = QB.qlora_quantize(W, cb, double_quant=DQ)
+        q = QB.qlora_quantize(W, cb, double_quant=DQ, block=BLOCK)
         del W
         L = dict(N=N, K=K, q=q)
         L["X"] = synth.device_normal_bf16((M, K), 1.0, synth.tensor_seed(4, 10 * i + 1), device=dev)
@@ -520,7 +522,7 @@ def run_layer70b(args):
         "data": "synthetic (seeded N(0,0.015) weights with 0.1% outliers x20, NF4+DQ; N(0,1) activations)",
         "config": {"workload": "70B-style layer linears (q,k,v,o 8192x8192; gate,up 28672x8192; down "
                                "8192x28672), M=4096 tokens, LoRA r=16 alpha=32 on all seven, fwd+bwd",
-                   "M": M, "r": r, "alpha": alpha, "double_quant": DQ, "parallelism": "none (1 GPU)"},
+                   "M": M, "r": r, "alpha": alpha, "double_quant": DQ, "nf4_block": BLOCK, "parallelism": "none (1 GPU)"},
         "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
     }
     return out
@@ -599,7 +601,7 @@ def run_layer38(args):
     layers = []
     for i, (name, N, K) in enumerate(PROJ38):
         W = synth.device_normal_bf16((N, K), 0.02, synth.tensor_seed(5, 10 * i), device=dev)
-        q = QB.qlora_quantize(W, cb, double_quant=DQ, fmt=fcode)
+        q = QB.qlora_quantize(W, cb, double_quant=DQ, fmt=fcode, block=BLOCK if fmt == "nf4" else 64)
         del W
         L = dict(N=N, K=K, q=q)
         L["X"] = synth.device_normal_bf16((M, K), 1.0, synth.tensor_seed(5, 10 * i + 1), device=dev)
@@ -651,7 +653,7 @@ def run_layer38(args):
                                "3072x8192), M=4096 tokens (seq 4096), LoRA r=64 alpha=128 on all "
                                f"seven, fwd+bwd, weights {FORMAT_NAMES[fmt]}",
                    "M": M, "r": r, "alpha": alpha, "format": fmt,
-                   "double_quant": DQ if fmt == "nf4" else None,
+                   "double_quant": DQ if fmt == "nf4" else None, "nf4_block": BLOCK if fmt == "nf4" else None,
                    "packed_bytes": sum(L["q"].nbytes() for L in layers),
                    "parallelism": "none (1 GPU)"},
         "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
@@ -681,14 +683,20 @@ def main():
                     choices=["layer7b", "decode", "quantize70b", "layer70b", "layer3.8b"])
     ap.add_argument("--format", default="q8_0", choices=["q8_0", "u4_asym", "nf4"],
                     help="weight block format of the layer3.8b workload")
+    ap.add_argument("--nf4-block", type=int, default=64, choices=[32, 64, 128],
+                    help="NF4 block size; no CPU baseline unless 64 (the oracle baselines time "
+                         "block 64)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only; --gpus must be 1 "
               "(sharding over several GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
+    global DQ, BLOCK
     if args.single_level:
-        global DQ
         DQ = False
+        args.no_cpu_baseline = True
+    BLOCK = args.nf4_block
+    if BLOCK != 64:
         args.no_cpu_baseline = True
 
     run = {"layer7b": run_layer7b, "decode": run_decode, "quantize70b": run_quantize70b,
