@@ -60,6 +60,12 @@ largest fp32 not above the exact mean of levels k and k+1, so that
 ``code = #{k : v > mid[k]}`` is exactly "nearest level, ties to the lower code"
 for every fp32 v.
 
+Compute type [rkmt §3.3: the compute dtype is float16 or bfloat16; kwkr §4.3:
+fall back to fp16 where bf16 is unsupported]: the dequantized weight is
+rounded (nearest, ties to even) to the compute type instead of bf16, and a
+weight given in fp16 is read as fp16 (``dtype="f16"``); codes and scales are
+computed the same way from the exact fp32 values.
+
 Parity unpinned: the level values themselves rest on the construction rule
 (the pages print no table); the 8-bit second-level format is pinned by the
 closed-form storage sizes only.
@@ -91,6 +97,70 @@ def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
     nan = np.isnan(np.asarray(x, dtype=np.float32))
     quiet = ((u >> 16) | 0x40).astype(np.uint32)
     return np.where(nan, quiet, rounded).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# IEEE binary16 (fp16) <-> fp32, written from the definition of the format
+# [kwkr §1.1; lqnn §2.1: 1 sign bit, 5 exponent bits, 10 mantissa bits]
+# --------------------------------------------------------------------------
+def f16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """fp16 bits -> fp32 (exact: every fp16 value is an fp32 value).
+    Exponent field 0: subnormal m * 2^-24; 31: infinity or NaN; otherwise
+    (1024 + m) * 2^(e - 25)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    m = b & 0x3FF
+    mag = np.where(e == 0, np.ldexp(m.astype(np.float64), -24),
+                   np.ldexp((1024 + m).astype(np.float64), (e - 25).astype(np.int64)))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    return (sign * mag).astype(np.float32)
+
+
+def f32_to_f16_rne(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to fp16 bits, nearest with ties to even, subnormals kept,
+    magnitudes from 65520 up to infinity, NaN to a quiet NaN.  The fp32 value
+    is exact in float64; it is divided by the fp16 unit in the last place of
+    its binade (2^-24 below 2^-14), a power of two, so the quotient is exact,
+    and that quotient is rounded half to even."""
+    v = np.asarray(x, dtype=np.float32).astype(np.float64)
+    neg = np.signbit(v)
+    a = np.abs(v)
+    fin = np.isfinite(a)
+    a0 = np.where(fin & (a > 0), a, 1.0)
+    _, e = np.frexp(a0)                               # a = f * 2^e, f in [0.5, 1)
+    ef = np.clip(e - 1, -14, 15)                      # binade exponent, floor(log2 a)
+    ulp_exp = (ef - 10).astype(np.int64)
+    q = np.ldexp(np.where(fin, a, 0.0), -ulp_exp)     # exact
+    r = np.rint(q).astype(np.int64)                   # half to even
+    val = np.ldexp(r.astype(np.float64), ulp_exp)
+    bits = np.where(a < 2.0 ** -14, r, ((ef + 15).astype(np.int64) << 10) + r - 1024)
+    bits = np.where(val > 65504.0, 0x7C00, bits)
+    bits = np.where(np.isinf(a), 0x7C00, bits)
+    bits = np.where(np.isnan(v), 0x7E00, bits)
+    bits = bits | np.where(neg, 0x8000, 0)
+    return bits.astype(np.uint16)
+
+
+DTYPES = ("bf16", "f16")   # 16-bit compute types [rkmt §3.3; kwkr §4.3]
+
+
+def widen(bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """16-bit weights or activations of the compute type -> fp32 (exact)."""
+    if dtype == "bf16":
+        return bf16_to_f32(bits)
+    if dtype == "f16":
+        return f16_to_f32(bits)
+    raise ValueError(f"unknown compute dtype {dtype!r}")
+
+
+def narrow(x: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """fp32 -> 16-bit bits of the compute type, round to nearest even."""
+    if dtype == "bf16":
+        return f32_to_bf16_rne(x)
+    if dtype == "f16":
+        return f32_to_f16_rne(x)
+    raise ValueError(f"unknown compute dtype {dtype!r}")
 
 
 # --------------------------------------------------------------------------
@@ -184,18 +254,19 @@ def from_storage(codes: np.ndarray, qscale: np.ndarray, n: int, k: int):
     return cs.reshape(-1), np.asarray(qscale, dtype=np.uint8)[pos]
 
 
-def block_absmax(w_bits: np.ndarray, block: int = BLOCK) -> np.ndarray:
-    x = bf16_to_f32(np.asarray(w_bits).reshape(-1)).reshape(-1, block)
+def block_absmax(w_bits: np.ndarray, block: int = BLOCK, dtype: str = "bf16") -> np.ndarray:
+    x = widen(np.asarray(w_bits).reshape(-1), dtype).reshape(-1, block)
     return np.max(np.abs(x), axis=1).astype(np.float32)
 
 
-def quantize_nodq(w_bits: np.ndarray, mids: np.ndarray, block: int = BLOCK):
-    """Steps 1-3 only: bf16 weight bits (numel % 64 == 0 and % block == 0) ->
-    (codes uint8[numel/2], absmax float32[numel/block]), flat order."""
+def quantize_nodq(w_bits: np.ndarray, mids: np.ndarray, block: int = BLOCK, dtype: str = "bf16"):
+    """Steps 1-3 only: 16-bit weight bits of the compute type (numel % 64 == 0
+    and % block == 0) -> (codes uint8[numel/2], absmax float32[numel/block]),
+    flat order."""
     flat = np.asarray(w_bits, dtype=np.uint16).reshape(-1)
     if flat.size % BLOCK or flat.size % block:
         raise ValueError("numel must be a multiple of 64 and of the block")
-    x = bf16_to_f32(flat).reshape(-1, block)
+    x = widen(flat, dtype).reshape(-1, block)
     if not np.all(np.isfinite(x)):
         raise ValueError("non-finite weights are outside the contract")
     # step 1: first-level scale per 64-block
@@ -209,12 +280,12 @@ def quantize_nodq(w_bits: np.ndarray, mids: np.ndarray, block: int = BLOCK):
     return pack(code.reshape(-1)), absmax
 
 
-def dequantize_nodq(codes, absmax, levels, block: int = BLOCK) -> np.ndarray:
-    """-> bf16 bits (flat): bf16_rne(fp32(level[code] * absmax_b))."""
+def dequantize_nodq(codes, absmax, levels, block: int = BLOCK, dtype: str = "bf16") -> np.ndarray:
+    """-> 16-bit bits (flat): rne(fp32(level[code] * absmax_b)) in the compute type."""
     code = unpack(codes)
     s_el = np.repeat(np.asarray(absmax, dtype=np.float32), block)
     prod = (np.asarray(levels, dtype=np.float32)[code] * s_el).astype(np.float32)
-    return f32_to_bf16_rne(prod)
+    return narrow(prod, dtype)
 
 
 def blocks_to_storage(per_block: np.ndarray, n: int, k: int) -> np.ndarray:
@@ -226,10 +297,11 @@ def blocks_to_storage(per_block: np.ndarray, n: int, k: int) -> np.ndarray:
     return out
 
 
-def quantize(w_bits: np.ndarray, mids: np.ndarray, block: int = BLOCK):
-    """bf16 weight bits (any shape, numel % 64 == 0 and % block == 0) ->
-    (codes uint8[numel/2], qscale uint8[numel/block], step float32[ngroups])."""
-    codes, absmax = quantize_nodq(w_bits, mids, block)
+def quantize(w_bits: np.ndarray, mids: np.ndarray, block: int = BLOCK, dtype: str = "bf16"):
+    """16-bit weight bits of the compute type (any shape, numel % 64 == 0 and
+    % block == 0) -> (codes uint8[numel/2], qscale uint8[numel/block], step
+    float32[ngroups])."""
+    codes, absmax = quantize_nodq(w_bits, mids, block, dtype)
     # step 4: second level over groups of 256 block scales
     nblocks = absmax.size
     ngroups = -(-nblocks // GROUP)
@@ -255,13 +327,13 @@ def block_scale(qscale: np.ndarray, step: np.ndarray) -> np.ndarray:
     return (q * np.asarray(step, dtype=np.float32)[g]).astype(np.float32)
 
 
-def dequantize(codes, qscale, step, levels, block: int = BLOCK) -> np.ndarray:
-    """-> bf16 bits (flat): bf16_rne(fp32(level[code] * s'_b))."""
+def dequantize(codes, qscale, step, levels, block: int = BLOCK, dtype: str = "bf16") -> np.ndarray:
+    """-> 16-bit bits (flat): rne(fp32(level[code] * s'_b)) in the compute type."""
     code = unpack(codes)
     s = block_scale(qscale, step)
     s_el = np.repeat(s, block)
     prod = (np.asarray(levels, dtype=np.float32)[code] * s_el).astype(np.float32)
-    return f32_to_bf16_rne(prod)
+    return narrow(prod, dtype)
 
 
 def dequantize_f32(codes, qscale, step, levels) -> np.ndarray:
@@ -292,7 +364,8 @@ def scales_from_storage(stored: np.ndarray, n: int, k: int, block: int = BLOCK) 
 
 
 def dequant_error_bound(w_bits: np.ndarray, levels: np.ndarray,
-                        double_quant: bool = True, block: int = BLOCK) -> np.ndarray:
+                        double_quant: bool = True, block: int = BLOCK,
+                        dtype: str = "bf16") -> np.ndarray:
     """Per-element bound on |w - deq(q(w))| (float64), derived from the steps,
     independent of how ``quantize`` is written:
 
@@ -303,11 +376,13 @@ def dequant_error_bound(w_bits: np.ndarray, levels: np.ndarray,
       the binary32 roundings of c2/255, absmax/step and qscale*step
                                                      -> 0.5*step + 2^-15*step + 2^-22*absmax
       (multiplied by |level| <= 1)
-    * the binary32 product level*s' and the final bf16 rounding
-                                                     -> 2^-23 |w| + half a bf16 ulp of |w|
+    * the binary32 product level*s' and the final rounding to the compute
+      type                                           -> 2^-23 |w| + half an ulp of |w|
+      (bf16: 8 significant bits; fp16: 11, and never below the subnormal
+      half-ulp 2^-25)
     """
     flat = np.asarray(w_bits, dtype=np.uint16).reshape(-1)
-    x = bf16_to_f32(flat).astype(np.float64).reshape(-1, block)
+    x = widen(flat, dtype).astype(np.float64).reshape(-1, block)
     absmax = np.max(np.abs(x), axis=1)
     nblocks = absmax.size
     ngroups = -(-nblocks // GROUP)
@@ -324,8 +399,11 @@ def dequant_error_bound(w_bits: np.ndarray, levels: np.ndarray,
         dq = np.zeros_like(dq)
     wmax = np.abs(x) + enc + dq
     _, e = np.frexp(np.maximum(wmax, np.finfo(np.float64).tiny))
-    half_ulp_bf16 = np.ldexp(1.0, e - 9)
-    bound = enc + dq + 2.0 ** -23 * wmax + half_ulp_bf16
+    if dtype == "f16":
+        half_ulp = np.maximum(np.ldexp(1.0, e - 12), 2.0 ** -25)
+    else:
+        half_ulp = np.ldexp(1.0, e - 9)
+    bound = enc + dq + 2.0 ** -23 * wmax + half_ulp
     return bound.reshape(-1)
 
 
