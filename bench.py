@@ -22,6 +22,9 @@ Other workloads (--workload), each printing its own line of the same form:
               with 0.1 % of the weights scaled x20); GB/s against HBM peak.
   layer70b    the same layer, fwd + bwd at M = 4096 with LoRA r = 16,
               alpha = 32 on all seven; TFLOP/s against bf16 MFMA peak.
+--dtype f16 runs the NF4 workloads in the fp16 compute type (weights,
+activations, adapters and 16-bit outputs fp16; the fp16 MFMA peak equals the
+bf16 one).
   layer3.8b   3.8B-style layer linears (hidden 3072, intermediate 8192: q, k,
               v, o 3072x3072; gate, up 8192x3072; down 3072x8192), fwd + bwd
               at M = 4096 (seq 4096) with LoRA r = 64, alpha = 128 on all
@@ -37,6 +40,8 @@ import json
 import os
 import sys
 import time
+
+import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -71,6 +76,19 @@ def flops_bwd(M, N, K, r):
 # block (--single-level); NF4 block size (--nf4-block, 64 by default)
 DQ = True
 BLOCK = 64
+# compute type of the NF4 workloads (--dtype): bf16, or fp16 (NF4 block 64
+# with double quantization only)
+DT = torch.bfloat16
+
+
+def dt_name():
+    return "f16" if DT == torch.float16 else "bf16"
+
+
+def dnorm(*a, **k):
+    """Seeded device-side draw in the compute type."""
+    import synth
+    return synth.device_normal_bf16(*a, dtype=DT, **k)
 
 
 def packed_bytes(N, K):
@@ -100,7 +118,7 @@ def traffic_from_profile(kernel, src_files):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source; else None."""
     p = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
-    if not os.path.exists(p) or not DQ or BLOCK != 64:   # the counters were taken on that format
+    if not os.path.exists(p) or not DQ or BLOCK != 64 or DT != torch.bfloat16:   # counters: that format
         return None
     with open(p) as f:
         d = json.load(f)
@@ -158,17 +176,17 @@ def run_layer7b(args):
     s = ALPHA / RANK
     layers = []
     for i, (name, N, K, r) in enumerate(PROJ):
-        W = synth.device_normal_bf16((N, K), 0.02, synth.tensor_seed(2, 10 * i), device=dev)
+        W = dnorm((N, K), 0.02, synth.tensor_seed(2, 10 * i), device=dev)
         q = QB.qlora_quantize(W, cb, double_quant=DQ, block=BLOCK)
         del W
         L = dict(name=name, N=N, K=K, r=r, q=q)
-        L["X"] = synth.device_normal_bf16((M, K), 1.0, synth.tensor_seed(2, 10 * i + 1), device=dev)
-        L["dY"] = synth.device_normal_bf16((M, N), 1.0, synth.tensor_seed(2, 10 * i + 2), device=dev)
-        L["A"] = synth.device_normal_bf16((r, K), 0.01, synth.tensor_seed(2, 10 * i + 3), device=dev) if r else None
-        L["B"] = synth.device_normal_bf16((N, r), 0.01, synth.tensor_seed(2, 10 * i + 4), device=dev) if r else None
-        L["Y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        L["X"] = dnorm((M, K), 1.0, synth.tensor_seed(2, 10 * i + 1), device=dev)
+        L["dY"] = dnorm((M, N), 1.0, synth.tensor_seed(2, 10 * i + 2), device=dev)
+        L["A"] = dnorm((r, K), 0.01, synth.tensor_seed(2, 10 * i + 3), device=dev) if r else None
+        L["B"] = dnorm((N, r), 0.01, synth.tensor_seed(2, 10 * i + 4), device=dev) if r else None
+        L["Y"] = torch.empty((M, N), dtype=DT, device=dev)
         L["T"] = torch.empty((M, r), dtype=torch.float32, device=dev) if r else None
-        L["dX"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        L["dX"] = torch.empty((M, K), dtype=DT, device=dev)
         L["dA"] = torch.empty((r, K), dtype=torch.float32, device=dev) if r else None
         L["dB"] = torch.empty((N, r), dtype=torch.float32, device=dev) if r else None
         nws = max(QB.qlora_workspace_bytes(0, M, N, K, r), QB.qlora_workspace_bytes(1, M, N, K, r), 16)
@@ -247,11 +265,11 @@ def run_layer7b(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4),
         "gpu_step_ms": _spread(step_ms),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt_name(),
         "data": "synthetic (seeded N(0,0.02) weights quantized to NF4+DQ, N(0,1) activations)",
         "config": {"workload": WORKLOAD, "M": M, "r": RANK, "alpha": ALPHA, "double_quant": DQ, "nf4_block": BLOCK,
-                   "projections": [[p[0], p[1], p[2], p[3]] for p in PROJ], "y_dtype": "bf16",
-                   "dx_dtype": "bf16", "parallelism": "none (1 GPU)"},
+                   "projections": [[p[0], p[1], p[2], p[3]] for p in PROJ], "y_dtype": dt_name(),
+                   "dx_dtype": dt_name(), "parallelism": "none (1 GPU)"},
         "effective_GBps": round(gbs, 1),
         "frac_of_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
@@ -312,7 +330,7 @@ def run_decode(args):
     weights = []
     for layer in range(DECODE_LAYERS):
         for i, (name, N, K, r) in enumerate(PROJ):
-            W = synth.device_normal_bf16((N, K), 0.02, synth.tensor_seed(3, 100 * layer + 10 * i),
+            W = dnorm((N, K), 0.02, synth.tensor_seed(3, 100 * layer + 10 * i),
                                          device=dev)
             weights.append((QB.qlora_quantize(W, cb, double_quant=DQ, block=BLOCK), N, K, r))
             del W
@@ -323,23 +341,23 @@ def run_decode(args):
         jobs, jobs0 = [], []
         nbytes = nbytes0 = 0
         for idx, (q, N, K, r) in enumerate(weights):
-            X = synth.device_normal_bf16((M, K), 1.0, synth.tensor_seed(3, 20000 + idx), device=dev)
-            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            X = dnorm((M, K), 1.0, synth.tensor_seed(3, 20000 + idx), device=dev)
+            Y = torch.empty((M, N), dtype=DT, device=dev)
             j = dict(w=q, X=X, Y=Y)
             b0 = q.nbytes() + 2 * M * K + 2 * M * N
             nbytes0 += b0
             nbytes += b0
             if r:
-                j.update(A=synth.device_normal_bf16((r, K), 0.01, synth.tensor_seed(3, 40000 + idx),
+                j.update(A=dnorm((r, K), 0.01, synth.tensor_seed(3, 40000 + idx),
                                                     device=dev),
-                         B=synth.device_normal_bf16((N, r), 0.01, synth.tensor_seed(3, 60000 + idx),
+                         B=dnorm((N, r), 0.01, synth.tensor_seed(3, 60000 + idx),
                                                     device=dev),
                          scaling=ALPHA / RANK, T=torch.empty((M, r), dtype=torch.float32, device=dev))
                 nbytes += 2 * r * K + 2 * N * r + 4 * M * r
             jobs.append(j)
             jobs0.append(dict(w=q, X=X, Y=Y))
-        g = QB.qlora_group_init(jobs, M, y_dtype=torch.bfloat16)
-        g0 = QB.qlora_group_init(jobs0, M, y_dtype=torch.bfloat16)
+        g = QB.qlora_group_init(jobs, M, y_dtype=DT)
+        g0 = QB.qlora_group_init(jobs0, M, y_dtype=DT)
         wall, gpu, sweeps = _timed(lambda: QB.qlora_linear_fwd_grouped(g, cb), args.steps, args.warmup)
         # the streaming kernel alone: the same sweep without LoRA is one launch
         wall0, gpu0, _ = _timed(lambda: QB.qlora_linear_fwd_grouped(g0, cb), args.steps, args.warmup)
@@ -357,7 +375,7 @@ def run_decode(args):
         "metric": "QLoRA NF4 decode-sweep forward effective GB/s (% HBM roofline) on 1 MI355X",
         "value": round(nbytes / wall / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "scaling": "weak", "vs_baseline": None, "dtype": dt_name(),
         "data": "synthetic (seeded N(0,0.02) weights quantized to NF4+DQ, N(0,1) activations)",
         "config": {"workload": f"decode sweep: {DECODE_LAYERS} layers x (q,k,v,o 4096x4096; gate,up "
                                "11008x4096; down 4096x11008), M=1, LoRA r=8 alpha=16 on q,k,v,o, "
@@ -412,7 +430,7 @@ def _weights70(dev):
     import synth
     out = []
     for i, (name, N, K) in enumerate(PROJ70):
-        out.append(synth.device_normal_bf16((N, K), 0.015, synth.tensor_seed(4, 10 * i), device=dev,
+        out.append(dnorm((N, K), 0.015, synth.tensor_seed(4, 10 * i), device=dev,
                                             outlier_rate=0.001, outlier_scale=20))
     return out
 
@@ -426,7 +444,7 @@ def run_quantize70b(args):
     torch.cuda.set_device(dev)
     cb = QB.device_codebook(dev)
     Ws = _weights70(dev)
-    outs = [QB.NF4Weight.empty(N, K, dev, double_quant=DQ, block=BLOCK) for _, N, K in PROJ70]
+    outs = [QB.NF4Weight.empty(N, K, dev, double_quant=DQ, block=BLOCK, dtype=DT) for _, N, K in PROJ70]
     params = sum(N * K for _, N, K in PROJ70)
     nbytes = sum(2 * N * K + packed_bytes(N, K) for _, N, K in PROJ70)
 
@@ -444,7 +462,7 @@ def run_quantize70b(args):
         "value": round(nbytes / wall / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "gpu_step_ms": _spread(steps_ms),
         "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16->u8",
+        "scaling": "weak", "vs_baseline": None, "dtype": dt_name() + "->u8",
         "data": "synthetic (seeded N(0,0.015) bf16 weights, 0.1% outliers x20)",
         "config": {"workload": "quantize a 70B-style layer: q,k,v,o 8192x8192; gate,up 28672x8192; "
                                "down 8192x28672 (973,078,528 params)", "params": params,
@@ -490,13 +508,13 @@ def run_layer70b(args):
         q = QB.qlora_quantize(W, cb, double_quant=DQ, block=BLOCK)
         del W
         L = dict(N=N, K=K, q=q)
-        L["X"] = synth.device_normal_bf16((M, K), 1.0, synth.tensor_seed(4, 10 * i + 1), device=dev)
-        L["dY"] = synth.device_normal_bf16((M, N), 1.0, synth.tensor_seed(4, 10 * i + 2), device=dev)
-        L["A"] = synth.device_normal_bf16((r, K), 0.01, synth.tensor_seed(4, 10 * i + 3), device=dev)
-        L["B"] = synth.device_normal_bf16((N, r), 0.01, synth.tensor_seed(4, 10 * i + 4), device=dev)
-        L["Y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        L["X"] = dnorm((M, K), 1.0, synth.tensor_seed(4, 10 * i + 1), device=dev)
+        L["dY"] = dnorm((M, N), 1.0, synth.tensor_seed(4, 10 * i + 2), device=dev)
+        L["A"] = dnorm((r, K), 0.01, synth.tensor_seed(4, 10 * i + 3), device=dev)
+        L["B"] = dnorm((N, r), 0.01, synth.tensor_seed(4, 10 * i + 4), device=dev)
+        L["Y"] = torch.empty((M, N), dtype=DT, device=dev)
         L["T"] = torch.empty((M, r), dtype=torch.float32, device=dev)
-        L["dX"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        L["dX"] = torch.empty((M, K), dtype=DT, device=dev)
         L["dA"] = torch.empty((r, K), dtype=torch.float32, device=dev)
         L["dB"] = torch.empty((N, r), dtype=torch.float32, device=dev)
         nws = max(QB.qlora_workspace_bytes(0, M, N, K, r), QB.qlora_workspace_bytes(1, M, N, K, r), 16)
@@ -518,7 +536,7 @@ def run_layer70b(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4),
         "gpu_event_ms_per_step": round(gpu * 1e3, 4), "gpu_step_ms": _spread(steps_ms),
         "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16",
+        "vs_baseline": None, "dtype": dt_name(),
         "data": "synthetic (seeded N(0,0.015) weights with 0.1% outliers x20, NF4+DQ; N(0,1) activations)",
         "config": {"workload": "70B-style layer linears (q,k,v,o 8192x8192; gate,up 28672x8192; down "
                                "8192x28672), M=4096 tokens, LoRA r=16 alpha=32 on all seven, fwd+bwd",
@@ -686,12 +704,21 @@ def main():
     ap.add_argument("--nf4-block", type=int, default=64, choices=[32, 64, 128],
                     help="NF4 block size; no CPU baseline unless 64 (the oracle baselines time "
                          "block 64)")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
+                    help="compute type of the NF4 workloads (f16: block 64 with double "
+                         "quantization only; no CPU baseline)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only; --gpus must be 1 "
               "(sharding over several GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
-    global DQ, BLOCK
+    global DQ, BLOCK, DT
+    if args.dtype == "f16":
+        if args.single_level or args.nf4_block != 64 or args.workload == "layer3.8b":
+            print("--dtype f16 needs NF4 at block 64 with double quantization", file=sys.stderr)
+            sys.exit(2)
+        DT = torch.float16
+        args.no_cpu_baseline = True
     if args.single_level:
         DQ = False
         args.no_cpu_baseline = True

@@ -4,7 +4,8 @@
  * The frozen base weight W [n x k] (out_features x in_features) is stored as
  * block-wise 4-bit NF4 with double quantization of the block scales (or in
  * one of the alternate block formats below); the forward and backward of the
- * LoRA-augmented linear layer dequantize it to bf16 inside the kernels.
+ * LoRA-augmented linear layer dequantize it to bf16 (or fp16, see "Compute
+ * type") inside the kernels.
  *
  * Pages cited (address and section):
  *   news.rkmt.cn/news/4821   (QLoRA double / block-wise quantization)
@@ -17,8 +18,8 @@
  *   - Device pointers are owned by the caller; the library never allocates,
  *     frees or synchronizes.  Work is enqueued on `stream` (a hipStream_t, or
  *     NULL for the null stream) and is ordered with other work on it.
- *   - Matrices are row-major and contiguous.  bf16 tensors are passed as raw
- *     16-bit patterns (uint16_t).
+ *   - Matrices are row-major and contiguous.  bf16 and fp16 tensors are passed
+ *     as raw 16-bit patterns (uint16_t).
  *   - codes, X, Y, dY and dX must be 16-byte aligned; every other device
  *     pointer 4-byte aligned.
  *   - k % 64 == 0; m >= 1 and n >= 1 are arbitrary (ragged tails are masked);
@@ -50,15 +51,15 @@ enum {
   QLORA_ERR_NULL = 1,      /* a required pointer is NULL */
   QLORA_ERR_SHAPE = 2,     /* m, n or k <= 0, k % 64 != 0, or descriptor sizes mismatch */
   QLORA_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
-  QLORA_ERR_DTYPE = 4,     /* unknown dtype enum */
+  QLORA_ERR_DTYPE = 4,     /* unknown dtype enum, or one the weight does not allow */
   QLORA_ERR_RANK = 5,      /* LoRA rank r < 0 or r > QLORA_MAX_RANK */
   QLORA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than qlora_workspace_bytes() */
   QLORA_ERR_HIP = 7,       /* a HIP launch failed */
   QLORA_ERR_ARG = 8        /* another argument is out of range (path, op) */
 };
 
-/* output dtypes */
-enum { QLORA_F32 = 0, QLORA_BF16 = 1 };
+/* dtypes: of outputs (y_dtype, dx_dtype) and the compute type (qlora_nf4.dtype) */
+enum { QLORA_F32 = 0, QLORA_BF16 = 1, QLORA_F16 = 2 };
 
 /* path selection for qlora_linear_fwd / qlora_linear_bwd */
 enum {
@@ -136,6 +137,20 @@ enum {
  * The codebook argument of every entry point is used by (and required for)
  * the NF4 format only.  Every entry point accepts every format; a grouped
  * forward needs one format (and for NF4 one scale level) for all its jobs.
+ *
+ * Compute type (news.rkmt.cn/news/4821 §3.3: the compute dtype is float16 or
+ * bfloat16; kwkr.cn/news/627310 §4.3: fp16 where bf16 is not supported).
+ * dtype = QLORA_BF16 (or 0) is the default: every 16-bit tensor is bf16.
+ * dtype = QLORA_F16, allowed for NF4 at block 64 with double quantization
+ * only (else QLORA_ERR_DTYPE): the weight handed to qlora_quantize, X, A, B,
+ * dY, the dequantized and merged weights and every 16-bit output are IEEE
+ * fp16; the dequantized weight is w = fp16_rne(level[code] * s'), subnormals
+ * kept, and the products run on fp16 operands with fp32 accumulation.  The
+ * codes and scales are computed the same way from the exact fp32 values, so
+ * a weight exact in both types packs to the same bytes.  Values beyond the
+ * fp16 range (65504), in inputs or results, are outside the contract.
+ * A 16-bit y_dtype / dx_dtype must name the compute type (QLORA_BF16 for
+ * bf16, QLORA_F16 for fp16); QLORA_F32 is always allowed.
  */
 typedef struct {
   int64_t n;       /* out_features */
@@ -145,6 +160,7 @@ typedef struct {
   float *step;
   int32_t format;  /* QLORA_FMT_* */
   int32_t block;   /* NF4 block size: 0 or 64 (default), 32 or 128; 0 or 64 for other formats */
+  int32_t dtype;   /* compute type: 0 or QLORA_BF16 (default), or QLORA_F16 (see above) */
 } qlora_nf4;
 
 /*
@@ -200,7 +216,8 @@ int qlora_weight_bytes(int format, int64_t n, int64_t k, size_t *codes, size_t *
 size_t qlora_workspace_bytes(int op, int64_t m, int64_t n, int64_t k, int r);
 
 /*
- * Quantize a bf16 weight W [n x k] (device) into `out` (device arrays sized by
+ * Quantize a 16-bit weight W [n x k] (device; bf16, or fp16 when out->dtype is
+ * QLORA_F16) into `out` (device arrays sized by
  * qlora_nf4_bytes, out->n and out->k set).  Block-wise absmax scaling over 64
  * elements, nearest NF4 level of the binary32 quotient w / absmax (ties to the
  * lower level; an all-zero block gives level 0), then double quantization:
@@ -216,10 +233,11 @@ size_t qlora_workspace_bytes(int op, int64_t m, int64_t n, int64_t k, int r);
 int qlora_quantize(const uint16_t *W, const float *codebook, const qlora_nf4 *out, void *stream);
 
 /*
- * Dequantize `W` into a dense bf16 [n x k] device array `out`, with the same
+ * Dequantize `W` into a dense [n x k] device array `out` of its compute type
+ * (bf16, or fp16 for QLORA_F16), with the same
  * arithmetic the linear kernels use internally.  For checking and for merging
  * an adapter into the base (www.lqnn.cn/news/228537 §3.3), not for the linear
- * layer itself, which never materializes the bf16 weight.
+ * layer itself, which never materializes the 16-bit weight.
  */
 int qlora_dequantize(const qlora_nf4 *W, const float *codebook, uint16_t *out, void *stream);
 
@@ -228,27 +246,28 @@ int qlora_dequantize(const qlora_nf4 *W, const float *codebook, uint16_t *out, v
  * dequantize W, add the low-rank branch at high precision, quantize again;
  * www.cf-1.com/news/5705389 §4.3 and kwkr.cn/news/627310 §4.4 on the two
  * precision losses, the 16-bit rounding of the sum and the requantization):
- *     merged[n][k] = bf16_rne(fp32(deq(W)[n][k] + fp32(scaling * acc))),
+ *     merged[n][k] = rne16(fp32(deq(W)[n][k] + fp32(scaling * acc))),
  *     acc = sum_j B[n][j] A[j][k], accumulated in binary32 in rank order
- *           (j = 0 .. r-1; each product of two bf16 values is exact).
- * A [r x W.k], B [W.n x r] bf16 (device; A 16-byte aligned), r == 0 gives
- * deq(W).  `merged` [W.n x W.k] bf16 (device, 16-byte aligned) receives the
- * merged weight.  If `out` is not NULL (sizes equal to W's), the merged
- * weight is then quantized into it, in out->format, exactly as
- * qlora_quantize would.  The codebook is required when W or out is NF4.
+ *           (j = 0 .. r-1; each product of two 16-bit values is exact).
+ * A [r x W.k], B [W.n x r] in W's compute type (device; A 16-byte aligned),
+ * r == 0 gives deq(W).  `merged` [W.n x W.k] (device, 16-byte aligned)
+ * receives the merged weight in that type (rne16: bf16 or fp16 rounding).  If
+ * `out` is not NULL (sizes and compute type equal to W's), the merged weight
+ * is then quantized into it, in out->format, exactly as qlora_quantize would.
+ * The codebook is required when W or out is NF4.
  */
 int qlora_merge(const qlora_nf4 *W, const float *codebook, const uint16_t *A, const uint16_t *B,
                 int r, float scaling, uint16_t *merged, const qlora_nf4 *out, void *stream);
 
 /*
- * Forward of the LoRA-augmented quantized linear (www.cf-1.com/news/5705389/*
  * Forward of the LoRA-augmented quantized linear (www.cf-1.com/news/5705389
  * §2.1, §3.2; www.lqnn.cn/news/228537 §3.2-§3.3):
  *     T = X A^T            [m x r], fp32 (written to T_save if not NULL)
  *     Y = X deq(W)^T + scaling * T B^T      [m x n]
- * X [m x k] bf16, A [r x k] bf16, B [n x r] bf16, scaling = alpha / r.
- * The product runs on bf16 operands with fp32 accumulation; T stays fp32.
- * Y is fp32 (y_dtype QLORA_F32) or bf16 rounded to nearest even (QLORA_BF16).
+ * X [m x k], A [r x k], B [n x r] in W's compute type (bf16, or fp16),
+ * scaling = alpha / r.  The product runs on 16-bit operands with fp32
+ * accumulation; T stays fp32.  Y is fp32 (y_dtype QLORA_F32) or the compute
+ * type rounded to nearest even (QLORA_BF16, or QLORA_F16 for fp16 compute).
  * ws: device workspace of at least qlora_workspace_bytes(0, m, n, k, r) bytes
  * (may be NULL only if that size is 0).  path: QLORA_PATH_*.
  */
@@ -262,11 +281,11 @@ int qlora_linear_fwd(const qlora_nf4 *W, const float *codebook, const uint16_t *
  * through the quantized matrix; www.lqnn.cn/news/228537 §3.3 and zky001
  * section 5.8: the frozen base gets no gradient, only A and B):
  *     U  = dY B                          [m x r] fp32
- *     dX = dY deq(W) + scaling * U A     [m x k]  (fp32 or bf16 per dx_dtype)
+ *     dX = dY deq(W) + scaling * U A     [m x k]  (fp32, or the 16-bit compute type, per dx_dtype)
  *     dA = scaling * U^T X               [r x k]  fp32, overwritten
  *     dB = scaling * dY^T T              [n x r]  fp32, overwritten
- * T = X A^T is taken from T_saved ([m x r] fp32, as written by the forward) or
- * recomputed when T_saved is NULL.  dX may be NULL to skip the input gradient;
+ * X, dY, A and B are in W's compute type.  T = X A^T is taken from T_saved
+ * ([m x r] fp32, as written by the forward) or recomputed when T_saved is NULL.  dX may be NULL to skip the input gradient;
  * dA/dB are required when r > 0.
  */
 int qlora_linear_bwd(const qlora_nf4 *W, const float *codebook, const uint16_t *X,
@@ -288,9 +307,9 @@ int qlora_linear_bwd(const qlora_nf4 *W, const float *codebook, const uint16_t *
  */
 typedef struct {
   qlora_nf4 w;
-  const uint16_t *X; /* [m x w.k] bf16 */
-  const uint16_t *A; /* [r x w.k] bf16, NULL when r == 0 */
-  const uint16_t *B; /* [w.n x r] bf16, NULL when r == 0 */
+  const uint16_t *X; /* [m x w.k], w's compute type */
+  const uint16_t *A; /* [r x w.k], NULL when r == 0 */
+  const uint16_t *B; /* [w.n x r], NULL when r == 0 */
   int r;
   float scaling;
   void *Y;           /* [m x w.n], the group's y_dtype */
@@ -310,7 +329,7 @@ size_t qlora_group_table_bytes(int count);
 /*
  * Host, setup time.  Validates every job (QLORA_ERR_* as qlora_linear_fwd,
  * QLORA_ERR_ARG if m > QLORA_GEMV_MAX_M, count < 1 or the jobs' weights mix
- * formats or NF4 scale levels) and writes the device
+ * formats, NF4 scale levels or compute types) and writes the device
  * job table into `table` (16-byte aligned, >= qlora_group_table_bytes(count)
  * bytes) with a blocking host-to-device copy: unlike every other call this
  * one synchronizes.  The buffers named by the jobs must stay valid while the

@@ -17,7 +17,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
 
-QLORA_F32, QLORA_BF16 = 0, 1
+QLORA_F32, QLORA_BF16, QLORA_F16 = 0, 1, 2
+_DTYPE_ENUM = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16, torch.float16: QLORA_F16}
 QLORA_FMT_NF4, QLORA_FMT_U4_ASYM, QLORA_FMT_Q8_0 = 0, 1, 2
 FORMATS = {"nf4": QLORA_FMT_NF4, "u4_asym": QLORA_FMT_U4_ASYM, "q8_0": QLORA_FMT_Q8_0}
 PATHS = {"auto": 0, "gemv": 1, "gemm": 2}
@@ -33,7 +34,7 @@ class QLoRAError(RuntimeError):
 class _Nf4Desc(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("codes", ctypes.c_void_p),
                 ("qscale", ctypes.c_void_p), ("step", ctypes.c_void_p), ("format", ctypes.c_int32),
-                ("block", ctypes.c_int32)]
+                ("block", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class _FwdJob(ctypes.Structure):
@@ -163,7 +164,10 @@ class NF4Weight:
     [ceil(n*k/16384)].  NF4 single level: qscale None, step float32 [n*k/64]
     (the fp32 absmax of every block).  Asymmetric uint4: qscale None, step
     float32 [2*n*k/64] (scale, zero-point per block).  Q8_0: codes [n*k] int8
-    bytes, qscale uint8 [4*n*k/64] (two fp16 scales per 64 weights), step None."""
+    bytes, qscale uint8 [4*n*k/64] (two fp16 scales per 64 weights), step None.
+    dtype: the compute type (torch.bfloat16, or torch.float16 for NF4 at block
+    64 with double quantization): the type of the weight it was quantized
+    from, of X, A, B, dY and of 16-bit outputs."""
     n: int
     k: int
     codes: torch.Tensor               # uint8
@@ -171,6 +175,7 @@ class NF4Weight:
     step: torch.Tensor | None
     fmt: int = QLORA_FMT_NF4
     block: int = 64                   # NF4 block size (32, 64, 128)
+    dtype: torch.dtype = torch.bfloat16
 
     @property
     def double_quant(self) -> bool:
@@ -180,11 +185,11 @@ class NF4Weight:
         return _Nf4Desc(self.n, self.k, self.codes.data_ptr(),
                         self.qscale.data_ptr() if self.qscale is not None else None,
                         self.step.data_ptr() if self.step is not None else None, self.fmt,
-                        self.block)
+                        self.block, QLORA_F16 if self.dtype == torch.float16 else QLORA_BF16)
 
     @staticmethod
     def empty(n: int, k: int, device="cuda", double_quant: bool = True,
-              fmt: int = QLORA_FMT_NF4, block: int = 64) -> "NF4Weight":
+              fmt: int = QLORA_FMT_NF4, block: int = 64, dtype=torch.bfloat16) -> "NF4Weight":
         def u8(b):
             return torch.empty(b, dtype=torch.uint8, device=device)
 
@@ -199,8 +204,8 @@ class NF4Weight:
             return NF4Weight(n, k, u8(c), u8(q), None, fmt)
         c, q, s = qlora_nf4_block_bytes(n, k, block, double_quant)
         if not double_quant:
-            return NF4Weight(n, k, u8(c), None, f32(s), fmt, block)
-        return NF4Weight(n, k, u8(c), u8(q), f32(s), fmt, block)
+            return NF4Weight(n, k, u8(c), None, f32(s), fmt, block, dtype)
+        return NF4Weight(n, k, u8(c), u8(q), f32(s), fmt, block, dtype)
 
     def nbytes(self) -> int:
         q = self.qscale.numel() if self.qscale is not None else 0
@@ -212,20 +217,26 @@ def device_codebook(device="cuda") -> torch.Tensor:
     return torch.from_numpy(qlora_nf4_codebook()).to(device)
 
 
-def _bf16(t, name):
-    if t.dtype != torch.bfloat16 or not t.is_contiguous():
-        raise QLoRAError(f"{name} must be a contiguous bfloat16 tensor")
+def _t16(t, name, dtype=torch.bfloat16):
+    if t.dtype != dtype or not t.is_contiguous():
+        raise QLoRAError(f"{name} must be a contiguous {dtype} tensor")
     return t
+
+
+def _out_enum(dtype, name):
+    if dtype not in _DTYPE_ENUM:
+        raise QLoRAError(f"{name}: unsupported output dtype {dtype}")
+    return _DTYPE_ENUM[dtype]
 
 
 def qlora_quantize(W: torch.Tensor, codebook: torch.Tensor | None, out: NF4Weight | None = None,
                    double_quant: bool = True, fmt: int = QLORA_FMT_NF4, block: int = 64) -> NF4Weight:
-    """Quantize W; the format follows `out` when given, else `fmt` and (NF4)
-    `double_quant` and `block`.  The codebook is used by NF4 only (None
-    otherwise)."""
-    _bf16(W, "W")
+    """Quantize W (bf16, or fp16: the compute type of the result); the format
+    follows `out` when given, else `fmt` and (NF4) `double_quant` and `block`.
+    The codebook is used by NF4 only (None otherwise)."""
+    _t16(W, "W", out.dtype if out is not None else (W.dtype if W.dtype == torch.float16 else torch.bfloat16))
     n, k = W.shape
-    out = out if out is not None else NF4Weight.empty(n, k, W.device, double_quant, fmt, block)
+    out = out if out is not None else NF4Weight.empty(n, k, W.device, double_quant, fmt, block, W.dtype)
     d = out.desc()
     _check(lib().qlora_quantize(_ptr(W), _ptr(codebook), ctypes.byref(d), _stream()),
            "qlora_quantize")
@@ -233,7 +244,7 @@ def qlora_quantize(W: torch.Tensor, codebook: torch.Tensor | None, out: NF4Weigh
 
 
 def qlora_dequantize(w: NF4Weight, codebook: torch.Tensor) -> torch.Tensor:
-    out = torch.empty((w.n, w.k), dtype=torch.bfloat16, device=w.codes.device)
+    out = torch.empty((w.n, w.k), dtype=w.dtype, device=w.codes.device)
     d = w.desc()
     _check(lib().qlora_dequantize(ctypes.byref(d), _ptr(codebook), _ptr(out), _stream()),
            "qlora_dequantize")
@@ -242,13 +253,13 @@ def qlora_dequantize(w: NF4Weight, codebook: torch.Tensor) -> torch.Tensor:
 
 def qlora_merge(w: NF4Weight, codebook, A=None, B=None, scaling: float = 0.0,
                 out: NF4Weight | None = None, merged: torch.Tensor | None = None):
-    """Fold the adapter into the base: -> (merged bf16 [n x k], out).  When
-    `out` is given the merged weight is requantized into it (its format)."""
+    """Fold the adapter into the base: -> (merged [n x k] in w.dtype, out).
+    When `out` is given the merged weight is requantized into it (its format)."""
     r = 0 if A is None else A.shape[0]
     if r:
-        _bf16(A, "A")
-        _bf16(B, "B")
-    M = merged if merged is not None else torch.empty((w.n, w.k), dtype=torch.bfloat16,
+        _t16(A, "A", w.dtype)
+        _t16(B, "B", w.dtype)
+    M = merged if merged is not None else torch.empty((w.n, w.k), dtype=w.dtype,
                                                       device=w.codes.device)
     d = w.desc()
     od = out.desc() if out is not None else None
@@ -261,13 +272,14 @@ def qlora_merge(w: NF4Weight, codebook, A=None, B=None, scaling: float = 0.0,
 def qlora_linear_fwd(w: NF4Weight, codebook: torch.Tensor, X: torch.Tensor, A=None, B=None,
                      scaling: float = 0.0, y_dtype=torch.float32, save_T: bool = True,
                      path: str = "auto", out=None, T_out=None, workspace=None):
-    """-> (Y [m x n], T [m x r] fp32 or None)."""
-    _bf16(X, "X")
+    """-> (Y [m x n], T [m x r] fp32 or None).  X, A, B in w.dtype; y_dtype
+    float32 or w.dtype."""
+    _t16(X, "X", w.dtype)
     m = X.shape[0]
     r = 0 if A is None else A.shape[0]
     if r:
-        _bf16(A, "A")
-        _bf16(B, "B")
+        _t16(A, "A", w.dtype)
+        _t16(B, "B", w.dtype)
     dev = X.device
     Y = out if out is not None else torch.empty((m, w.n), dtype=y_dtype, device=dev)
     T = T_out if T_out is not None else (
@@ -279,7 +291,7 @@ def qlora_linear_fwd(w: NF4Weight, codebook: torch.Tensor, X: torch.Tensor, A=No
     _check(lib().qlora_linear_fwd(
         ctypes.byref(d), _ptr(codebook), _ptr(X), m, _ptr(A) if r else None,
         _ptr(B) if r else None, r, float(scaling), _ptr(Y),
-        QLORA_BF16 if Y.dtype == torch.bfloat16 else QLORA_F32, _ptr(T), _ptr(ws),
+        _out_enum(Y.dtype, "Y"), _ptr(T), _ptr(ws),
         ws.numel(), PATHS[path], _stream()), "qlora_linear_fwd")
     return Y, T
 
@@ -287,15 +299,16 @@ def qlora_linear_fwd(w: NF4Weight, codebook: torch.Tensor, X: torch.Tensor, A=No
 def qlora_linear_bwd(w: NF4Weight, codebook: torch.Tensor, X, dY, A=None, B=None,
                      scaling: float = 0.0, T=None, dx_dtype=torch.float32, need_dX: bool = True,
                      path: str = "auto", dX_out=None, dA_out=None, dB_out=None, workspace=None):
-    """-> (dX [m x k] or None, dA [r x k] fp32 or None, dB [n x r] fp32 or None)."""
-    _bf16(dY, "dY")
+    """-> (dX [m x k] or None, dA [r x k] fp32 or None, dB [n x r] fp32 or None).
+    X, dY, A, B in w.dtype; dx_dtype float32 or w.dtype."""
+    _t16(dY, "dY", w.dtype)
     m = dY.shape[0]
     r = 0 if A is None else A.shape[0]
     dev = dY.device
     if r:
-        _bf16(X, "X")
-        _bf16(A, "A")
-        _bf16(B, "B")
+        _t16(X, "X", w.dtype)
+        _t16(A, "A", w.dtype)
+        _t16(B, "B", w.dtype)
     dX = dX_out if dX_out is not None else (
         torch.empty((m, w.k), dtype=dx_dtype, device=dev) if need_dX else None)
     dA = dA_out if dA_out is not None else (
@@ -309,7 +322,7 @@ def qlora_linear_bwd(w: NF4Weight, codebook: torch.Tensor, X, dY, A=None, B=None
     _check(lib().qlora_linear_bwd(
         ctypes.byref(d), _ptr(codebook), _ptr(X) if X is not None else None, _ptr(dY), m,
         _ptr(A) if r else None, _ptr(B) if r else None, r, float(scaling), _ptr(T),
-        _ptr(dX), QLORA_BF16 if (dX is not None and dX.dtype == torch.bfloat16) else QLORA_F32,
+        _ptr(dX), _out_enum(dX.dtype, "dX") if dX is not None else QLORA_F32,
         _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), PATHS[path], _stream()), "qlora_linear_bwd")
     return dX, dA, dB
 
@@ -342,7 +355,7 @@ def qlora_group_init(jobs, m: int, y_dtype=torch.bfloat16, device="cuda") -> Fwd
     nbytes = qlora_group_table_bytes(len(jobs))
     table = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
     g = _Group()
-    yd = QLORA_BF16 if y_dtype == torch.bfloat16 else QLORA_F32
+    yd = _out_enum(y_dtype, "Y")
     _check(lib().qlora_group_init(ctypes.byref(g), arr, len(jobs), m, yd, _ptr(table), nbytes),
            "qlora_group_init")
     return FwdGroup(g, table, keep)

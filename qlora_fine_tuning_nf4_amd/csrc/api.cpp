@@ -166,11 +166,18 @@ bool block_shape_ok(int64_t n, int64_t k, int block) {
   return true;
 }
 
+// Compute type of a descriptor: fp16 (QLORA_F16) or the bf16 default.
+bool is_f16(const qlora_nf4* W) { return W->dtype == QLORA_F16; }
+
 // The arrays each format uses (NF4: qscale NULL selects the single-level
-// scales), their alignment, the shape.
+// scales), their alignment, the shape, the compute type (fp16 only for NF4
+// at block 64 with double quantization).
 int check_desc(const qlora_nf4* W) {
   if (!W) return QLORA_ERR_NULL;
   if (!nf4_block(W)) return QLORA_ERR_ARG;
+  if (W->dtype != 0 && W->dtype != QLORA_BF16 && W->dtype != QLORA_F16) return QLORA_ERR_DTYPE;
+  if (is_f16(W) && (W->format != QLORA_FMT_NF4 || nf4_block(W) != 64 || !W->qscale))
+    return QLORA_ERR_DTYPE;
   switch (W->format) {
     case QLORA_FMT_NF4:
       if (!W->codes || !W->step) return QLORA_ERR_NULL;
@@ -200,7 +207,13 @@ int check_codebook(const qlora_nf4* W, const float* codebook) {
   return aligned(codebook, 4) ? QLORA_OK : QLORA_ERR_ALIGN;
 }
 
+// 16-bit output dtype allowed for this weight: fp32 or its compute type.
+bool out_dtype_ok(const qlora_nf4* W, int dtype) {
+  return dtype == QLORA_F32 || dtype == (is_f16(W) ? QLORA_F16 : QLORA_BF16);
+}
+
 int kernel_fmt(const qlora_nf4* W) {
+  if (is_f16(W)) return ql::kFmtNf4DqF16;
   switch (W->format) {
     case QLORA_FMT_U4_ASYM: return ql::kFmtU4;
     case QLORA_FMT_Q8_0: return ql::kFmtQ8;
@@ -229,7 +242,7 @@ const char* qlora_strerror(int s) {
     case QLORA_ERR_NULL: return "a required pointer is NULL";
     case QLORA_ERR_SHAPE: return "bad shape (m, n, k must be >= 1 and k a multiple of 64)";
     case QLORA_ERR_ALIGN: return "pointer not aligned as required";
-    case QLORA_ERR_DTYPE: return "unknown dtype";
+    case QLORA_ERR_DTYPE: return "unknown dtype, or a dtype the weight or its compute type does not allow";
     case QLORA_ERR_RANK: return "LoRA rank out of range [0, 128]";
     case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
     case QLORA_ERR_HIP: return "HIP launch failed";
@@ -339,13 +352,14 @@ int qlora_merge(const qlora_nf4* W, const float* codebook, const uint16_t* A, co
     if (int e = check_desc(out)) return e;
     if (int e = check_codebook(out, codebook)) return e;
     if (out->n != W->n || out->k != W->k) return QLORA_ERR_SHAPE;
+    if (is_f16(out) != is_f16(W)) return QLORA_ERR_DTYPE;
   }
   if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
   if (!aligned(merged, 16) || (r > 0 && (!aligned(A, 16) || !aligned(B, 2)))) return QLORA_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   if (ql::launch_dequant(view(W), codebook, merged, s) != hipSuccess) return QLORA_ERR_HIP;
-  if (r > 0 && ql::launch_merge(merged, A, B, W->n, W->k, r, scaling, s) != hipSuccess)
+  if (r > 0 && ql::launch_merge(merged, A, B, W->n, W->k, r, scaling, is_f16(W), s) != hipSuccess)
     return QLORA_ERR_HIP;
   if (out && ql::launch_quantize(merged, codebook, out->codes, out->qscale, out->step, out->n,
                                  out->k, kernel_fmt(out), s) != hipSuccess)
@@ -363,7 +377,7 @@ int qlora_linear_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
   if (m < 1) return QLORA_ERR_SHAPE;
   if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
-  if (y_dtype != QLORA_F32 && y_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
+  if (!out_dtype_ok(W, y_dtype)) return QLORA_ERR_DTYPE;
   if (path < QLORA_PATH_AUTO || path > QLORA_PATH_GEMM) return QLORA_ERR_ARG;
   if (path == QLORA_PATH_GEMV && m > QLORA_GEMV_MAX_M) return QLORA_ERR_ARG;
   if (!aligned(X, 16) || !aligned(Y, 16)) return QLORA_ERR_ALIGN;
@@ -382,17 +396,17 @@ int qlora_linear_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
   if (r > 0) {
     T = T_save ? T_save : (float*)(wsb + L.t_off);
     float* rpart = ws ? (float*)(wsb + L.part_off) : nullptr;   // needed only with splits
-    if (ql::launch_rowdot(X, A, m, k, r, T, rpart, s) != hipSuccess)
+    if (ql::launch_rowdot(X, A, m, k, r, T, rpart, is_f16(W), s) != hipSuccess)
       return QLORA_ERR_HIP;
   }
   ql::LoraTerm lora{T, B, (int64_t)r, 1, r, scaling};
   float* part = p.ksplit > 1 ? (float*)(wsb + L.part_off) : nullptr;
   const ql::Nf4View v = view(W);
-  const bool bf = y_dtype == QLORA_BF16;
+  const bool bf = y_dtype != QLORA_F32;   // a 16-bit output of the compute type
   hipError_t e = p.gemv ? ql::launch_gemv_fwd(v, codebook, X, m, lora, Y, bf, part, p.ksplit, s)
                         : ql::launch_gemm_fwd(v, codebook, X, m, lora, Y, bf, part, p.ksplit, s);
   if (e != hipSuccess) return QLORA_ERR_HIP;
-  if (p.ksplit > 1 && ql::launch_reduce(part, p.ksplit, m, n, lora, Y, bf, s) != hipSuccess)
+  if (p.ksplit > 1 && ql::launch_reduce(part, p.ksplit, m, n, lora, Y, bf, is_f16(W), s) != hipSuccess)
     return QLORA_ERR_HIP;
   return QLORA_OK;
 }
@@ -407,7 +421,7 @@ int qlora_group_init(qlora_group* g, const qlora_fwd_job* jobs, int count, int64
   if (!g || !jobs || !table) return QLORA_ERR_NULL;
   if (count < 1 || m > QLORA_GEMV_MAX_M) return QLORA_ERR_ARG;
   if (m < 1) return QLORA_ERR_SHAPE;
-  if (y_dtype != QLORA_F32 && y_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
+  if (y_dtype != QLORA_F32 && y_dtype != QLORA_BF16 && y_dtype != QLORA_F16) return QLORA_ERR_DTYPE;
   if (!aligned(table, 16)) return QLORA_ERR_ALIGN;
   if (table_bytes < qlora_group_table_bytes(count)) return QLORA_ERR_WORKSPACE;
   const size_t rd_off = up16(sizeof(ql::GemvJob) * (size_t)count);
@@ -422,6 +436,7 @@ int qlora_group_init(qlora_group* g, const qlora_fwd_job* jobs, int count, int64
     if ((st = check_desc(&J.w))) break;
     if (i == 0) fmt = kernel_fmt(&J.w);
     if (kernel_fmt(&J.w) != fmt) { st = QLORA_ERR_ARG; break; }   // one format per group
+    if (!out_dtype_ok(&J.w, y_dtype)) { st = QLORA_ERR_DTYPE; break; }
     if (!J.X || !J.Y) { st = QLORA_ERR_NULL; break; }
     if (J.r < 0 || J.r > QLORA_MAX_RANK) { st = QLORA_ERR_RANK; break; }
     if (J.r > 0 && (!J.A || !J.B || !J.T)) { st = QLORA_ERR_NULL; break; }
@@ -432,7 +447,7 @@ int qlora_group_init(qlora_group* g, const qlora_fwd_job* jobs, int count, int64
     }
     const int64_t n = J.w.n, k = J.w.k;
     ql::LoraTerm lora{J.r > 0 ? J.T : nullptr, J.B, (int64_t)J.r, 1, J.r, J.scaling};
-    gj[i] = ql::GemvJob{J.X, view(&J.w), lora, J.Y, nullptr, m, y_dtype == QLORA_BF16, rgs};
+    gj[i] = ql::GemvJob{J.X, view(&J.w), lora, J.Y, nullptr, m, y_dtype != QLORA_F32, rgs};
     rgs += cdiv(n, 64);
     maxq = std::max(maxq, cdiv(k / kB, 4));
     if (J.r > 0) {
@@ -466,7 +481,7 @@ int qlora_linear_fwd_grouped(const qlora_group* g, const float* codebook, void* 
   const size_t rd_off = up16(sizeof(ql::GemvJob) * (size_t)g->count);
   if (g->lora_count > 0 &&
       ql::launch_rowdot_grouped((const ql::RowdotJob*)(tb + rd_off), g->lora_count, g->m, g->max_r,
-                                s) != hipSuccess)
+                                ql::fmt_f16(g->variant), s) != hipSuccess)
     return QLORA_ERR_HIP;
   if (ql::launch_gemv_grouped((const ql::GemvJob*)tb, g->count, g->row_groups, g->m, codebook,
                               g->max_quads, g->variant, s) != hipSuccess)
@@ -484,7 +499,7 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
   if (m < 1) return QLORA_ERR_SHAPE;
   if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
   if (r > 0 && (!A || !B || !dA || !dB || !X)) return QLORA_ERR_NULL;
-  if (dx_dtype != QLORA_F32 && dx_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
+  if (!out_dtype_ok(W, dx_dtype)) return QLORA_ERR_DTYPE;
   if (path < QLORA_PATH_AUTO || path > QLORA_PATH_GEMM) return QLORA_ERR_ARG;
   if (!aligned(dY, 16) || (dX && !aligned(dX, 16)) || (X && !aligned(X, 16)))
     return QLORA_ERR_ALIGN;
@@ -505,10 +520,10 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
     uint16_t* Bt = (uint16_t*)(wsb + L.bt_off);
     if (ql::launch_transpose_bf16(B, n, r, Bt, s) != hipSuccess) return QLORA_ERR_HIP;
     float* rpart = (float*)(wsb + L.wg_off);
-    if (ql::launch_rowdot(dY, Bt, m, n, r, U, rpart, s) != hipSuccess) return QLORA_ERR_HIP;
+    if (ql::launch_rowdot(dY, Bt, m, n, r, U, rpart, is_f16(W), s) != hipSuccess) return QLORA_ERR_HIP;
     if (!T) {
       float* Tw = (float*)(wsb + L.t_off);
-      if (ql::launch_rowdot(X, A, m, k, r, Tw, rpart, s) != hipSuccess) return QLORA_ERR_HIP;
+      if (ql::launch_rowdot(X, A, m, k, r, Tw, rpart, is_f16(W), s) != hipSuccess) return QLORA_ERR_HIP;
       T = Tw;
     }
   }
@@ -516,19 +531,19 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
     const int ns = plan_dx_split(m, n, k);
     ql::LoraTerm lora{U, A, 1, k, r, scaling};
     float* part = ns > 1 ? (float*)(wsb + L.dx_off) : nullptr;
-    const bool bf = dx_dtype == QLORA_BF16;
+    const bool bf = dx_dtype != QLORA_F32;   // a 16-bit output of the compute type
     if (ql::launch_gemm_dx(view(W), codebook, dY, m, lora, dX, bf, part, ns, s) != hipSuccess)
       return QLORA_ERR_HIP;
-    if (ns > 1 && ql::launch_reduce(part, ns, m, k, lora, dX, bf, s) != hipSuccess)
+    if (ns > 1 && ql::launch_reduce(part, ns, m, k, lora, dX, bf, is_f16(W), s) != hipSuccess)
       return QLORA_ERR_HIP;
   }
   if (r > 0) {
     float* part = (float*)(wsb + L.wg_off);
-    if (ql::launch_wgrad(X, U, m, k, r, scaling, dA, false, part, plan_wgrad_split(m, k, r), s) !=
-        hipSuccess)
+    if (ql::launch_wgrad(X, U, m, k, r, scaling, dA, false, part, plan_wgrad_split(m, k, r),
+                         is_f16(W), s) != hipSuccess)
       return QLORA_ERR_HIP;
-    if (ql::launch_wgrad(dY, T, m, n, r, scaling, dB, true, part, plan_wgrad_split(m, n, r), s) !=
-        hipSuccess)
+    if (ql::launch_wgrad(dY, T, m, n, r, scaling, dB, true, part, plan_wgrad_split(m, n, r),
+                         is_f16(W), s) != hipSuccess)
       return QLORA_ERR_HIP;
   }
   return QLORA_OK;

@@ -8,6 +8,7 @@
 #define QL_DEV __device__ __forceinline__
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -26,13 +27,16 @@ constexpr int kWave = 64;
 //   kFmtNf4    32 code bytes, the fp32 absmax
 //   kFmtU4     32 code bytes (uint4, NF4 packing), fp32 scale and zero-point
 //   kFmtQ8     64 int8 bytes, two fp16 scales (elements 0-31, 32-63)
+//   kFmtNf4DqF16  as kFmtNf4Dq; the dequantized weight is fp16
 // NF4 at block 32 keeps two scales per unit (at 2p, 2p + 1), at block 128 one
 // scale per two units of a row, stored in the same row-group order over the
 // k/128 block columns.
 template <int FMT>
 struct FmtInfo {
   static constexpr bool nf4 = FMT != kFmtU4 && FMT != kFmtQ8;        // decodes through the codebook
-  static constexpr bool dq = FMT == kFmtNf4Dq || FMT == kFmtNf4Dq32 || FMT == kFmtNf4Dq128;
+  static constexpr bool dq = FMT == kFmtNf4Dq || FMT == kFmtNf4Dq32 || FMT == kFmtNf4Dq128 ||
+                             FMT == kFmtNf4DqF16;
+  static constexpr bool f16 = FMT == kFmtNf4DqF16;                   // fp16 compute type
   static constexpr int block = (FMT == kFmtNf4Dq32 || FMT == kFmtNf4_32)    ? 32
                                : (FMT == kFmtNf4Dq128 || FMT == kFmtNf4_128) ? 128
                                                                              : 64;
@@ -41,12 +45,17 @@ struct FmtInfo {
   static constexpr int param_bytes = dq ? 1 : (FMT == kFmtU4 ? 8 : 4);
 };
 
-// D[16x16] += A[16x32] * B[32x16], bf16 operands, fp32 accumulate.
+// D[16x16] += A[16x32] * B[32x16], bf16 (F16: fp16) operands, fp32 accumulate.
 // Lane l holds A[l%16][8(l/16) .. +7], B[8(l/16) .. +7][l%16] and
-// D[4(l/16) .. +3][l%16] (layout measured on gfx950).
+// D[4(l/16) .. +3][l%16] (layout measured on gfx950; the same for both types).
+template <bool F16 = false>
 QL_DEV f32x4_t mfma16x16x32(const u32x4_t a, const u32x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
 // Global-memory view of a generic pointer.  Pointers loaded from memory
@@ -92,18 +101,50 @@ QL_DEV uint16_t to_bf16(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x
 QL_DEV float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
 QL_DEV float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xFFFF0000u); }
 
-// Per-block lookup table of the 16 dequantized bf16 values, kept as byte
+// The 16-bit compute type: bf16, or IEEE fp16 when F16.  Conversions from
+// fp32 round to nearest even (fp16 subnormals kept, overflow to infinity);
+// widening is exact.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <bool F16>
+QL_DEV uint32_t pack16x2(float lo, float hi) {
+  if constexpr (F16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
+  else
+    return pack_bf16x2(lo, hi);
+}
+template <bool F16>
+QL_DEV uint16_t to16(float x) {
+  if constexpr (F16)
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  else
+    return to_bf16(x);
+}
+template <bool F16>
+QL_DEV float w16(uint32_t bits16) {   // the low 16 bits hold the value
+  if constexpr (F16)
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+  else
+    return __builtin_bit_cast(float, bits16 << 16);
+}
+template <bool F16>
+QL_DEV float lo16(uint32_t v) { return F16 ? w16<true>(v & 0xFFFFu) : bf16_lo(v); }
+template <bool F16>
+QL_DEV float hi16(uint32_t v) { return F16 ? w16<true>(v >> 16) : bf16_hi(v); }
+
+// Per-block lookup table of the 16 dequantized 16-bit values, kept as byte
 // planes so that a 4-bit code selects its byte with v_perm_b32:
 //   lo[i] byte b = low byte of E[4i+b], hi[i] byte b = high byte of E[4i+b],
-//   E[c] = bf16_rne(level[c] * s)   (s = qscale * step of the block).
+//   E[c] = rne(level[c] * s) in bf16, or fp16 for the F16 builders
+//   (s = qscale * step of the block).
 struct Lut {
   uint32_t lo[4], hi[4];
 };
 
+template <bool F16 = false>
 QL_DEV Lut make_lut(const float* lv, float s) {
   uint32_t d[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) d[i] = pack_bf16x2(lv[2 * i] * s, lv[2 * i + 1] * s);
+  for (int i = 0; i < 8; ++i) d[i] = pack16x2<F16>(lv[2 * i] * s, lv[2 * i + 1] * s);
   Lut t;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -126,9 +167,10 @@ QL_DEV uint32_t quad_bcast(uint32_t v, int j) {
 }
 
 // lvq[i] = level[4q + i] for this lane's quad position q.
+template <bool F16 = false>
 QL_DEV Lut make_lut_quad(const float* lvq, float s) {
-  const uint32_t d0 = pack_bf16x2(lvq[0] * s, lvq[1] * s);
-  const uint32_t d1 = pack_bf16x2(lvq[2] * s, lvq[3] * s);
+  const uint32_t d0 = pack16x2<F16>(lvq[0] * s, lvq[1] * s);
+  const uint32_t d1 = pack16x2<F16>(lvq[2] * s, lvq[3] * s);
   const uint32_t lo = perm(d1, d0, 0x06040200u), hi = perm(d1, d0, 0x07050301u);
   Lut t;
 #pragma unroll

@@ -1,7 +1,8 @@
 // Fused-dequant MFMA GEMMs of the quantized linear (large-M regime):
 //   forward   Y  = X  deq(W)^T (+ LoRA term)    contraction over k
 //   backward  dX = dY deq(W)   (+ LoRA term)    contraction over n
-// The packed weight (NF4, asymmetric uint4 or Q8_0) is decoded to bf16 inside
+// The packed weight (NF4, asymmetric uint4 or Q8_0) is decoded to the 16-bit
+// compute type (bf16; fp16 for kFmtNf4DqF16, news.rkmt.cn/news/4821 §3.3) inside
 // the kernel and lives only in registers and LDS (www.cf-1.com/news/5705389
 // §2.2, §4.2: block dequant in the GEMM's outer loop, results kept in
 // registers / shared memory;
@@ -9,10 +10,11 @@
 // discard).
 //
 // gfx950 design:
-//  * 256 x 128 output tile per workgroup, 8 waves (two per SIMD, so one
-//    wave's LDS/barrier latency and decode work overlap the other's MFMAs);
-//    wave w owns the 64 x 64 sub-tile (w%4, w/4): 2 x 2 MFMA 32x32x16 bf16
-//    tiles with fp32 accumulators.
+//  * 256 x 128 output tile per workgroup, 8 waves in two groups of four (one
+//    wave of each group per SIMD): wave (g, w) accumulates rows 64w .. +63 x
+//    all 128 columns over K-slices 2g, 2g+1 of every step (MFMA 32x32x16,
+//    bf16 or fp16 operands, fp32 accumulators); the partner waves swap halves
+//    at the end, each finishing a 64 x 64 tile.
 //  * The activation operand (X or dY) goes global -> LDS with the gfx950
 //    global_load_lds b128 DMA (no registers, each wave load covers 8 whole
 //    128-byte row pieces) into a 3-stage ring, two K-steps ahead.  16-byte
@@ -22,9 +24,10 @@
 //    decoded by all 512 threads into a double-buffered LDS stage: the four
 //    lanes of a DPP quad share a unit and decode 16 weights each; for the
 //    4-bit formats they build its 16-entry table together (broadcast with
-//    quad_perm), Q8_0 bytes are scaled directly.  The decode of
-//    step s+1 is interleaved with the MFMAs of step s, one barrier per step;
-//    it is amortized over 256 output rows.
+//    quad_perm), Q8_0 bytes are scaled directly.  Ping-pong: while one
+//    group runs the MFMAs of step s the other reads its fragments and decodes
+//    its half of step s+1, a barrier between phases; the decode is amortized
+//    over 256 output rows.
 //  * Forward reads B fragments with ds_read_b128 from the [n][k] stage; the
 //    backward contracts over n and reads them with the transposing
 //    ds_read_b64_tr_b16 from a [n][k] stage.
@@ -42,9 +45,14 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // D[32x32] += A[32x16] B[16x32]; lane l holds A[l%32][8(l/32)..+7],
 // B[8(l/32)..+7][l%32], D[8(i/4) + 4(l/32) + i%4][l%32] for i = 0..15.
+template <bool F16>
 QL_DEV f32x16_t mfma32(const u32x4_t a, const u32x4_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
 constexpr int GBM = 256, GBN = 128, GBK = 64;
@@ -61,14 +69,6 @@ struct Geo {
   static constexpr int ld = DX ? cols + 32 : cols + 8;
   static constexpr int stage = rows * ld;
 };
-
-QL_DEV float lora_dot_g(const LoraTerm& L, int64_t m, int64_t c) {
-  float acc = 0.f;
-  const float* lr = L.L + m * L.r;
-  const uint16_t* rr = L.R + c * L.rs_c;
-  for (int j = 0; j < L.r; ++j) acc += lr[j] * __builtin_bit_cast(float, (uint32_t)rr[j * L.rs_j] << 16);
-  return acc;
-}
 
 QL_DEV u32x4_t load_act8(const uint16_t* row, int64_t c, int64_t C, bool vec) {
   if (vec) return *reinterpret_cast<const u32x4_t*>(row + c);
@@ -126,7 +126,7 @@ QL_DEV int a_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 template <bool DX, bool VEC, int FMT>
 __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ act, Nf4View w,
                                                  const float* __restrict__ codebook, int64_t M,
-                                                 LoraTerm lora, void* __restrict__ out, int out_bf16,
+                                                 LoraTerm lora, void* __restrict__ out, int out16,
                                                  float* __restrict__ part, int ksplit,
                                                  int steps_per_split, int64_t mtiles, int64_t otiles) {
   using G = Geo<DX>;
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       }
       // block 32: the half-quads hold different scales, so each lane pair
       // builds its own table
-      const Lut t = BS == 32 ? make_lut_pair(lvq, sc) : make_lut_quad(lvr, sc);
+      const Lut t = BS == 32 ? make_lut_pair(lvq, sc) : make_lut_quad<FI::f16>(lvr, sc);
       dst[0] = decode8(t, r.codes[0]);
       dst[1] = decode8(t, r.codes[1]);
     }
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) {
-            acc[mt][nt] = mfma32(fa[h][mt], fb[h][nt], acc[mt][nt]);
+            acc[mt][nt] = mfma32<FI::f16>(fa[h][mt], fb[h][nt], acc[mt][nt]);
             const int i = (h * 2 + mt) * 4 + nt;
             if (i % 4 == 0) {
               __builtin_amdgcn_sched_barrier(0);
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
 
   // ---- epilogue.  LoRA term (ksplit == 1): out += (scaling * L) R^T on the
   // matrix cores, 16 ranks per MFMA step; the fp32 factor scaling * L is
-  // split into bf16 hi + lo parts so the product keeps fp32 accuracy.  The
+  // split into 16-bit hi + lo parts so the product keeps fp32 accuracy.  The
   // operands of each 16-rank chunk are fetched without branches (indices
   // clamped into the matrices, values past the rank masked to zero), as
   // 16-byte loads where the layout allows, and the next chunk's fetch is
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
                       (reinterpret_cast<uintptr_t>(lora.R) & 15) == 0;
     const bool lvec = r % 8 == 0 && (reinterpret_cast<uintptr_t>(lora.L) & 15) == 0;
     struct Ops {
-      u32x4_t rb[2];      // R[o][jb .. jb+7], bf16 pairs
+      u32x4_t rb[2];      // R[o][jb .. jb+7], 16-bit pairs
       f32x4_t lv[2][2];   // L[m][jb .. jb+7]
     };
     // this lane's ranks of the chunk at j0: jb .. jb+7, jb = j0 + 8 lg
@@ -610,15 +610,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
         u32x4_t ahi, alo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          ahi[e] = pack_bf16x2(tv[2 * e], tv[2 * e + 1]);
-          lo[2 * e] = tv[2 * e] - bf16_lo(ahi[e]);
-          lo[2 * e + 1] = tv[2 * e + 1] - bf16_hi(ahi[e]);
-          alo[e] = pack_bf16x2(lo[2 * e], lo[2 * e + 1]);
+          ahi[e] = pack16x2<FI::f16>(tv[2 * e], tv[2 * e + 1]);
+          lo[2 * e] = tv[2 * e] - lo16<FI::f16>(ahi[e]);
+          lo[2 * e + 1] = tv[2 * e + 1] - hi16<FI::f16>(ahi[e]);
+          alo[e] = pack16x2<FI::f16>(lo[2 * e], lo[2 * e + 1]);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          fin[mt][j] = mfma32(ahi, rb[j], fin[mt][j]);
-          fin[mt][j] = mfma32(alo, rb[j], fin[mt][j]);
+          fin[mt][j] = mfma32<FI::f16>(ahi, rb[j], fin[mt][j]);
+          fin[mt][j] = mfma32<FI::f16>(alo, rb[j], fin[mt][j]);
         }
       }
     };
@@ -647,8 +647,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
           const float v = fin[mt][j][i];
           if (ksplit > 1)
             part[((int64_t)split * M + m) * O + o] = v;
-          else if (out_bf16)
-            reinterpret_cast<uint16_t*>(out)[m * O + o] = to_bf16(v);
+          else if (out16)
+            reinterpret_cast<uint16_t*>(out)[m * O + o] = to16<FI::f16>(v);
           else
             reinterpret_cast<float*>(out)[m * O + o] = v;
         }
@@ -663,7 +663,7 @@ static constexpr size_t smem_bytes() {
 template <bool DX, bool VEC, int FMT>
 static hipError_t launch_one(dim3 grid, hipStream_t s, const uint16_t* act, const Nf4View& w,
                              const float* codebook, int64_t M, const LoraTerm& lora, void* out,
-                             bool bf16, float* part, int ksplit, int per, int64_t mtiles,
+                             bool out16, float* part, int ksplit, int per, int64_t mtiles,
                              int64_t otiles) {
   static bool attr_set = false;   // idempotent: the same value every time
   if (!attr_set) {
@@ -674,17 +674,17 @@ static hipError_t launch_one(dim3 grid, hipStream_t s, const uint16_t* act, cons
     attr_set = true;
   }
   hipLaunchKernelGGL((k_gemm<DX, VEC, FMT>), grid, dim3(512), smem_bytes<DX>(), s, act, w, codebook,
-                     M, lora, out, (int)bf16, part, ksplit, per, mtiles, otiles);
+                     M, lora, out, (int)out16, part, ksplit, per, mtiles, otiles);
   return hipGetLastError();
 }
 
 template <bool DX, bool VEC>
 static hipError_t launch_fmt(dim3 grid, hipStream_t s, const uint16_t* act, const Nf4View& w,
                              const float* codebook, int64_t M, const LoraTerm& lora, void* out,
-                             bool bf16, float* part, int ksplit, int per, int64_t mtiles,
+                             bool out16, float* part, int ksplit, int per, int64_t mtiles,
                              int64_t otiles) {
 #define QL_ONE(F) \
-  launch_one<DX, VEC, F>(grid, s, act, w, codebook, M, lora, out, bf16, part, ksplit, per, mtiles, otiles)
+  launch_one<DX, VEC, F>(grid, s, act, w, codebook, M, lora, out, out16, part, ksplit, per, mtiles, otiles)
   switch (w.fmt) {
     case kFmtNf4Dq: return QL_ONE(kFmtNf4Dq);
     case kFmtNf4: return QL_ONE(kFmtNf4);
@@ -693,6 +693,7 @@ static hipError_t launch_fmt(dim3 grid, hipStream_t s, const uint16_t* act, cons
     case kFmtNf4Dq32: return QL_ONE(kFmtNf4Dq32);
     case kFmtNf4_32: return QL_ONE(kFmtNf4_32);
     case kFmtNf4Dq128: return QL_ONE(kFmtNf4Dq128);
+    case kFmtNf4DqF16: return QL_ONE(kFmtNf4DqF16);
     default: return QL_ONE(kFmtNf4_128);
   }
 #undef QL_ONE
@@ -700,7 +701,7 @@ static hipError_t launch_fmt(dim3 grid, hipStream_t s, const uint16_t* act, cons
 
 template <bool DX>
 static hipError_t launch(const Nf4View& w, const float* codebook, const uint16_t* act, int64_t M,
-                         const LoraTerm& lora, void* out, bool bf16, float* part, int ksplit,
+                         const LoraTerm& lora, void* out, bool out16, float* part, int ksplit,
                          hipStream_t s) {
   const int64_t C = DX ? w.n : w.k, O = DX ? w.k : w.n;
   const int nsteps = (int)((C + GBK - 1) / GBK);
@@ -711,23 +712,23 @@ static hipError_t launch(const Nf4View& w, const float* codebook, const uint16_t
   // (the forward's contraction is a whole number of 64-blocks)
   if constexpr (DX) {
     if (C % 8 != 0)
-      return launch_fmt<DX, false>(grid, s, act, w, codebook, M, lora, out, bf16, part, ksplit,
+      return launch_fmt<DX, false>(grid, s, act, w, codebook, M, lora, out, out16, part, ksplit,
                                    per, mtiles, otiles);
   }
-  return launch_fmt<DX, true>(grid, s, act, w, codebook, M, lora, out, bf16, part, ksplit, per,
+  return launch_fmt<DX, true>(grid, s, act, w, codebook, M, lora, out, out16, part, ksplit, per,
                               mtiles, otiles);
 }
 
 hipError_t launch_gemm_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,
-                           const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
+                           const LoraTerm& lora, void* Y, bool y16, float* part, int ksplit,
                            hipStream_t s) {
-  return launch<false>(w, codebook, X, M, lora, Y, y_bf16, part, ksplit, s);
+  return launch<false>(w, codebook, X, M, lora, Y, y16, part, ksplit, s);
 }
 
 hipError_t launch_gemm_dx(const Nf4View& w, const float* codebook, const uint16_t* dY, int64_t M,
-                          const LoraTerm& lora, void* dX, bool dx_bf16, float* part, int nsplit,
+                          const LoraTerm& lora, void* dX, bool dx16, float* part, int nsplit,
                           hipStream_t s) {
-  return launch<true>(w, codebook, dY, M, lora, dX, dx_bf16, part, nsplit, s);
+  return launch<true>(w, codebook, dY, M, lora, dX, dx16, part, nsplit, s);
 }
 
 }  // namespace ql

@@ -19,23 +19,27 @@
 
 namespace ql {
 
+// R and 16-bit outputs: fp16 when F16, else bf16
+template <bool F16>
 QL_DEV float lora_dot(const LoraTerm& L, int64_t m, int64_t c) {
   float acc = 0.f;
   const float* lr = L.L + m * L.r;
   const uint16_t* rr = L.R + c * L.rs_c;
-  for (int j = 0; j < L.r; ++j) acc += lr[j] * __builtin_bit_cast(float, (uint32_t)rr[j * L.rs_j] << 16);
+  for (int j = 0; j < L.r; ++j) acc += lr[j] * w16<F16>(rr[j * L.rs_j]);
   return acc;
 }
 
-QL_DEV void store_out(void* out, bool bf16, int64_t idx, float v) {
-  if (bf16)
-    gptr_w(reinterpret_cast<uint16_t*>(out))[idx] = to_bf16(v);
+template <bool F16>
+QL_DEV void store_out(void* out, bool out16, int64_t idx, float v) {
+  if (out16)
+    gptr_w(reinterpret_cast<uint16_t*>(out))[idx] = to16<F16>(v);
   else
     gptr_w(reinterpret_cast<float*>(out))[idx] = v;
 }
 
 // LoRA term of one output: scaling * sum_j L[m][j] R[c][j], with 16-byte loads
 // when the rank and the pointers allow it.
+template <bool F16>
 QL_DEV float lora_dot_v(const LoraTerm& L, int64_t m, int64_t c, bool vec) {
   const QL_GLOBAL float* lr = gptr(L.L + m * L.r);
   const QL_GLOBAL uint16_t* rr = gptr(L.R + c * L.rs_c);
@@ -46,12 +50,12 @@ QL_DEV float lora_dot_v(const LoraTerm& L, int64_t m, int64_t c, bool vec) {
       const u32x4_t bv = *reinterpret_cast<const QL_GLOBAL u32x4_t*>(rr + j);
       const f32x4_t t0 = *reinterpret_cast<const QL_GLOBAL f32x4_t*>(lr + j);
       const f32x4_t t1 = *reinterpret_cast<const QL_GLOBAL f32x4_t*>(lr + j + 4);
-      acc += t0[0] * bf16_lo(bv[0]) + t0[1] * bf16_hi(bv[0]) + t0[2] * bf16_lo(bv[1]) +
-             t0[3] * bf16_hi(bv[1]) + t1[0] * bf16_lo(bv[2]) + t1[1] * bf16_hi(bv[2]) +
-             t1[2] * bf16_lo(bv[3]) + t1[3] * bf16_hi(bv[3]);
+      acc += t0[0] * lo16<F16>(bv[0]) + t0[1] * hi16<F16>(bv[0]) + t0[2] * lo16<F16>(bv[1]) +
+             t0[3] * hi16<F16>(bv[1]) + t1[0] * lo16<F16>(bv[2]) + t1[1] * hi16<F16>(bv[2]) +
+             t1[2] * lo16<F16>(bv[3]) + t1[3] * hi16<F16>(bv[3]);
     }
   }
-  for (; j < L.r; ++j) acc += lr[j] * __builtin_bit_cast(float, (uint32_t)rr[j] << 16);
+  for (; j < L.r; ++j) acc += lr[j] * w16<F16>(rr[j]);
   return acc;
 }
 
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
         const u32x4_t& cw = u.c[i >> 1];
         const u32x4_t bf = decode_q8x8(cw[2 * (i & 1)], cw[2 * (i & 1) + 1], i < 4 ? d0 : d1);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt][i & 1] = mfma16x16x32(af[mt][i], bf, acc[mt][i & 1]);
+        for (int mt = 0; mt < MT; ++mt) acc[mt][i & 1] = mfma16x16x32<FI::f16>(af[mt][i], bf, acc[mt][i & 1]);
       }
     } else {
       float lvu[16];   // table levels: NF4 levels, or c - zp for uint4
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
         for (int i = 0; i < 16; ++i) lvu[i] = lv[i];
         scr = (float)(u.qbyte & 0xFFu) * u.step;
       }
-      const Lut t = make_lut(lvu, ok ? scr : 0.f);
+      const Lut t = make_lut<FI::f16>(lvu, ok ? scr : 0.f);
       if constexpr (BS == 32) {
         // words 4-7 are the second 32-weight block: its own scale and table
         const float scr1 = FI::dq ? (float)(u.qbyte >> 8) * u.step : u.zp;
@@ -261,14 +265,14 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
         for (int i = 0; i < 8; ++i) {
           const u32x4_t bf = decode8(i < 4 ? t : t1, u.c[i >> 2][i & 3]);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt][i & 1] = mfma16x16x32(af[mt][i], bf, acc[mt][i & 1]);
+          for (int mt = 0; mt < MT; ++mt) acc[mt][i & 1] = mfma16x16x32<FI::f16>(af[mt][i], bf, acc[mt][i & 1]);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const u32x4_t bf = decode8(t, u.c[i >> 2][i & 3]);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt][i & 1] = mfma16x16x32(af[mt][i], bf, acc[mt][i & 1]);
+          for (int mt = 0; mt < MT; ++mt) acc[mt][i & 1] = mfma16x16x32<FI::f16>(af[mt][i], bf, acc[mt][i & 1]);
         }
       }
     }
@@ -331,23 +335,24 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
         if (ksplit > 1) {
           gptr_w(J.part)[((int64_t)split * M + m) * N + n] = y;
         } else {
-          if (J.lora.r > 0) y += J.lora.scaling * lora_dot_v(J.lora, m, n, lvec);
-          store_out(J.Y, J.y_bf16, m * N + n, y);
+          if (J.lora.r > 0) y += J.lora.scaling * lora_dot_v<FI::f16>(J.lora, m, n, lvec);
+          store_out<FI::f16>(J.Y, J.y16, m * N + n, y);
         }
       }
     }
   }
 }
 
+template <bool F16>
 __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, int nsplit, int64_t M,
                                                 int64_t C, LoraTerm lora, void* __restrict__ out,
-                                                int out_bf16) {
+                                                int out16) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= M * C) return;
   float v = 0.f;
   for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * M * C + idx];
-  if (lora.r > 0) v += lora.scaling * lora_dot(lora, idx / C, idx % C);
-  store_out(out, out_bf16, idx, v);
+  if (lora.r > 0) v += lora.scaling * lora_dot<F16>(lora, idx / C, idx % C);
+  store_out<F16>(out, out16, idx, v);
 }
 
 template <int MT, int XPW, bool GROUPED>
@@ -364,6 +369,7 @@ static void gemv_launch(int fmt, dim3 grid, hipStream_t s, const GemvJob& job1, 
     case kFmtNf4Dq32: QL_GEMV(kFmtNf4Dq32); break;
     case kFmtNf4_32: QL_GEMV(kFmtNf4_32); break;
     case kFmtNf4Dq128: QL_GEMV(kFmtNf4Dq128); break;
+    case kFmtNf4DqF16: QL_GEMV(kFmtNf4DqF16); break;
     default: QL_GEMV(kFmtNf4_128); break;
   }
 #undef QL_GEMV
@@ -379,11 +385,11 @@ static void gemv_launch_m(int64_t M, int fmt, dim3 grid, hipStream_t s, const Ge
 }
 
 hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,
-                           const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
+                           const LoraTerm& lora, void* Y, bool y16, float* part, int ksplit,
                            hipStream_t s) {
   const int64_t nquads = (w.k / kBlock + 3) / 4;
   const int per = (int)((nquads + ksplit - 1) / ksplit);
-  const GemvJob job{X, w, lora, Y, part, M, (int)y_bf16, 0};
+  const GemvJob job{X, w, lora, Y, part, M, (int)y16, 0};
   const dim3 grid((unsigned)((w.n + 63) / 64), (unsigned)ksplit);
   gemv_launch_m<false>(M, w.fmt, grid, s, job, nullptr, 0, codebook, ksplit, per);
   return hipGetLastError();
@@ -398,10 +404,13 @@ hipError_t launch_gemv_grouped(const GemvJob* jobs, int njobs, int64_t row_group
 }
 
 hipError_t launch_reduce(const float* part, int nsplit, int64_t M, int64_t C, const LoraTerm& lora,
-                         void* out, bool out_bf16, hipStream_t s) {
+                         void* out, bool out16, bool f16, hipStream_t s) {
   const int64_t total = M * C;
-  hipLaunchKernelGGL(k_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, nsplit,
-                     M, C, lora, out, (int)out_bf16);
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (f16)
+    hipLaunchKernelGGL(k_reduce<true>, grid, dim3(256), 0, s, part, nsplit, M, C, lora, out, (int)out16);
+  else
+    hipLaunchKernelGGL(k_reduce<false>, grid, dim3(256), 0, s, part, nsplit, M, C, lora, out, (int)out16);
   return hipGetLastError();
 }
 

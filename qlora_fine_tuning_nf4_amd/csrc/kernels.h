@@ -8,17 +8,21 @@ namespace ql {
 
 // Weight formats as the kernels see them (a template parameter of each kernel):
 // NF4 with double-quantized (Dq) or single-level scales at block 64, 32 or
-// 128, asymmetric uint4, Q8_0.
+// 128, asymmetric uint4, Q8_0; every one computes in bf16 except
+// kFmtNf4DqF16, NF4 with double quantization at block 64 whose dequantized
+// weight, activations and adapter factors are fp16.
 enum WFmt : int {
   kFmtNf4Dq = 0, kFmtNf4 = 1, kFmtU4 = 2, kFmtQ8 = 3,
-  kFmtNf4Dq32 = 4, kFmtNf4_32 = 5, kFmtNf4Dq128 = 6, kFmtNf4_128 = 7
+  kFmtNf4Dq32 = 4, kFmtNf4_32 = 5, kFmtNf4Dq128 = 6, kFmtNf4_128 = 7,
+  kFmtNf4DqF16 = 8
 };
-constexpr int kNumFmt = 8;
+constexpr int kNumFmt = 9;
+inline bool fmt_f16(int fmt) { return fmt == kFmtNf4DqF16; }
 
 // LoRA term added by epilogues:  out[m][c] += scaling * sum_j L[m*r + j] * R[c*rs_c + j*rs_j]
 struct LoraTerm {
   const float* L;      // [M x r] fp32 (T in the forward, U in the backward), or nullptr
-  const uint16_t* R;   // bf16 (B [N x r] in the forward, A [r x K] in the backward)
+  const uint16_t* R;   // 16-bit (B [N x r] in the forward, A [r x K] in the backward)
   int64_t rs_c, rs_j;  // strides of R
   int r;
   float scaling;
@@ -37,20 +41,22 @@ struct Nf4View {
   int fmt;
 };
 
+// The 16-bit weight W is fp16 for kFmtNf4DqF16, else bf16 (likewise the
+// dequantized output).
 hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* codes,
                            uint8_t* qscale, float* step, int64_t n, int64_t k, int fmt,
                            hipStream_t s);
 hipError_t launch_dequant(const Nf4View& w, const float* codebook, uint16_t* out, hipStream_t s);
-// W[n][k] <- bf16(W + s * (B A)[n][k]) in place (A [r x k], B [n x r] bf16; k % 8 == 0,
-// W and A 16-byte aligned).
+// W[n][k] <- rne(W + s * (B A)[n][k]) in place (A [r x k], B [n x r]; all 16-bit,
+// fp16 when f16 else bf16; k % 8 == 0, W and A 16-byte aligned).
 hipError_t launch_merge(uint16_t* W, const uint16_t* A, const uint16_t* B, int64_t n, int64_t k, int r,
-                        float s, hipStream_t st);
+                        float s, bool f16, hipStream_t st);
 
 // Forward base product Y = X deq(W)^T (+ LoRA term), tiled MFMA GEMM.
 // ksplit > 1 writes fp32 partials part[ksplit][M][N] and leaves the epilogue
 // to launch_reduce.
 hipError_t launch_gemm_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,
-                           const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
+                           const LoraTerm& lora, void* Y, bool y16, float* part, int ksplit,
                            hipStream_t s);
 // One projection of the small-M forward.  rg_begin: first 64-row workgroup of
 // this job in a grouped launch (ascending over the job list).
@@ -61,13 +67,13 @@ struct GemvJob {
   void* Y;
   float* part;
   int64_t M;
-  int y_bf16;
+  int y16;
   int64_t rg_begin;
 };
 
 // Forward for small M (<= 64): streaming split-K over the packed weight.
 hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,
-                           const LoraTerm& lora, void* Y, bool y_bf16, float* part, int ksplit,
+                           const LoraTerm& lora, void* Y, bool y16, float* part, int ksplit,
                            hipStream_t s);
 // Grouped small-M forward: one launch over `njobs` device-resident jobs that
 // share M and the weight format `fmt` (a WFmt), covering `row_groups` 64-row
@@ -77,11 +83,12 @@ hipError_t launch_gemv_grouped(const GemvJob* jobs, int njobs, int64_t row_group
                                const float* codebook, int64_t max_quads, int fmt, hipStream_t s);
 // dX = dY deq(W) (+ LoRA term), contraction over n; nsplit > 1 -> partials.
 hipError_t launch_gemm_dx(const Nf4View& w, const float* codebook, const uint16_t* dY, int64_t M,
-                          const LoraTerm& lora, void* dX, bool dx_bf16, float* part, int nsplit,
+                          const LoraTerm& lora, void* dX, bool dx16, float* part, int nsplit,
                           hipStream_t s);
-// out[m][c] = sum_s part[s][m][c] + LoRA term, for C columns.
+// out[m][c] = sum_s part[s][m][c] + LoRA term, for C columns (R and a 16-bit
+// out in fp16 when f16, else bf16).
 hipError_t launch_reduce(const float* part, int nsplit, int64_t M, int64_t C,
-                         const LoraTerm& lora, void* out, bool out_bf16, hipStream_t s);
+                         const LoraTerm& lora, void* out, bool out16, bool f16, hipStream_t s);
 
 // Rank projection plan.  For M >= 512 and 16 < r <= 64 (and 16-byte rows)
 // the projection runs on 128-row tiles with the contraction split so that
@@ -100,10 +107,11 @@ inline int rowdot_splits(int64_t M, int64_t C, int r) {
   const int64_t per = (chunks + want - 1) / want;
   return (int)((chunks + per - 1) / per);
 }
-// out[m][j] = sum_c P[m][c] * Q[j][c]   (P bf16 [M x C], Q bf16 [r x C], out fp32 [M x r]);
+// out[m][j] = sum_c P[m][c] * Q[j][c]   (P [M x C], Q [r x C], both fp16 when
+// f16 else bf16; out fp32 [M x r]);
 // `part` holds rowdot_splits(M, C, r) * M * r floats when that is above 1.
 hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
-                         float* out, float* part, hipStream_t s);
+                         float* out, float* part, bool f16, hipStream_t s);
 // One product of the grouped rowdot: out[m][j] = sum_c P[m][c] Q[j][c].
 struct RowdotJob {
   const uint16_t* P;
@@ -112,16 +120,17 @@ struct RowdotJob {
   int64_t C;
   int r;
 };
-// All jobs share M; max_r is the largest r among them.
+// All jobs share M and the 16-bit type; max_r is the largest r among them.
 hipError_t launch_rowdot_grouped(const RowdotJob* jobs, int njobs, int64_t M, int max_r,
-                                 hipStream_t s);
-// Qt[j][n] = Q[n][j] for a bf16 [N x r] matrix.
+                                 bool f16, hipStream_t s);
+// Qt[j][n] = Q[n][j] for a 16-bit [N x r] matrix.
 hipError_t launch_transpose_bf16(const uint16_t* Q, int64_t N, int r, uint16_t* Qt, hipStream_t s);
 // Weight gradients of the adapter: out = scaling * sum_m Q[m][j] * P[m][c]
-// (P bf16 [M x C], Q fp32 [M x r]); written as out[j][c] (transpose_out false,
-// [r x C]) or out[c][j] (true, [C x r]).  msplit partials go through `part`.
+// (P [M x C] fp16 when f16 else bf16, Q fp32 [M x r]); written as out[j][c]
+// (transpose_out false, [r x C]) or out[c][j] (true, [C x r]).  msplit
+// partials go through `part`.
 hipError_t launch_wgrad(const uint16_t* P, const float* Q, int64_t M, int64_t C, int r,
                         float scaling, float* out, bool transpose_out, float* part, int msplit,
-                        hipStream_t s);
+                        bool f16, hipStream_t s);
 
 }  // namespace ql

@@ -1,6 +1,8 @@
 // LoRA branch pieces (www.lqnn.cn/news/228537 §3.2; www.cf-1.com/news/5705389
 // §2.1, §3.2): the rank-r projections T = X A^T and U = dY B, and the adapter
-// weight gradients dA = s U^T X and dB = s dY^T T.  T and U stay fp32.
+// weight gradients dA = s U^T X and dB = s dY^T T.  T and U stay fp32.  The
+// 16-bit operands are bf16, or fp16 in the F16 instantiations (compute type,
+// news.rkmt.cn/news/4821 §3.3).
 #include "common.h"
 #include "kernels.h"
 
@@ -25,9 +27,9 @@ QL_DEV u32x4_t load8_guard(const uint16_t* row, int64_t c, int64_t C, bool vec) 
 // past the contraction) point past the buffer and read zeros, so there are
 // no branches, and two register sets alternate: the next U slices load while
 // the current ones are multiplied.  The 8 partial tiles are summed in a
-// fixed order through LDS.  bf16 products are exact, sums fp32.
+// fixed order through LDS.  16-bit products are exact, sums fp32.
 constexpr int RD_WAVES = 8;
-template <int RT, bool GROUPED, bool VEC>
+template <int RT, bool GROUPED, bool VEC, bool F16>
 __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
                                                 const uint16_t* __restrict__ Q, int64_t M,
                                                 int64_t C, int r, float* __restrict__ out,
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int t = 0; t < RT; ++t) acc[t] = mfma16x16x32(a[u], b[u][t], acc[t]);
+        for (int t = 0; t < RT; ++t) acc[t] = mfma16x16x32<F16>(a[u], b[u][t], acc[t]);
     };
     u32x4_t a0[U], b0[U][RT], a1[U], b1[U][RT];
     int64_t c0 = wave * 32;
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int t = 0; t < RT; ++t) acc[t] = mfma16x16x32(a[u], b[u][t], acc[t]);
+        for (int t = 0; t < RT; ++t) acc[t] = mfma16x16x32<F16>(a[u], b[u][t], acc[t]);
     }
   }
   if (wave > 0) {
@@ -148,7 +150,7 @@ struct RsGeo {
   static constexpr int XS = CH / 32;                  // slices per wave and chunk
 };
 
-template <int RT>
+template <int RT, bool F16>
 __global__ __launch_bounds__(512) void k_rowdot_sk(const uint16_t* __restrict__ P,
                                                    const uint16_t* __restrict__ Q, int64_t M,
                                                    int64_t C, int r, float* __restrict__ out,
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(512) void k_rowdot_sk(const uint16_t* __restrict__ 
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const u32x4_t b = *reinterpret_cast<const u32x4_t*>(sq + (16 * t + li) * PITCH + 32 * k + 8 * g);
-        acc[t] = mfma16x16x32(x[k], b, acc[t]);
+        acc[t] = mfma16x16x32<F16>(x[k], b, acc[t]);
       }
   };
 
@@ -303,23 +305,34 @@ QL_DEV u32x2_t ds_tr16(const uint16_t* p) {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+template <bool F16>
+QL_DEV f32x16_t mfma32x32x16(const u32x4_t a, const u32x4_t b, f32x16_t c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // Weight gradient of the adapter on the matrix cores:
-//   out = scaling * sum_m Q[m][j] P[m][c]   (P bf16 [M x C], Q fp32 [M x r])
+//   out = scaling * sum_m Q[m][j] P[m][c]   (P 16-bit [M x C], Q fp32 [M x r])
 // written as out[j][c] ([r x C]) or, transposed, out[c][j] ([C x r]); with
 // msplit > 1 split s writes its unscaled sum over rows
 // [s * rows_per_split, +rows_per_split) to part[s][j][c] for k_wgrad_reduce.
 // A workgroup of 4 waves owns 32*JT ranks x 128 columns and walks its rows
-// in chunks of 64.  Each chunk of P (64 x 128 bf16) and of Q (64 x 32*JT
-// fp32, split into bf16 parts hi = bf16(q) and lo = bf16(q - hi), which
-// carry q to about 2^-16) is staged in LDS; the contraction m runs down the
-// stage rows, so wave w reads its 32 columns of P and every rank tile of Q
-// with the transposing ds_read_b64_tr_b16 and accumulates the hi and lo
-// products with MFMA 32x32x16 (bf16 products exact, sums fp32).  The next
+// in chunks of 64.  Each chunk of P (64 x 128) and of Q (64 x 32*JT fp32,
+// split into 16-bit parts of P's type, hi = rne(q) and lo = rne(q - hi),
+// which carry q to about 2^-16 for bf16, 2^-22 for fp16 above its subnormal
+// range) is staged in LDS; the contraction m runs down the stage rows, so
+// wave w reads its 32 columns of P and every rank tile of Q with the
+// transposing ds_read_b64_tr_b16 and accumulates the hi and lo products with
+// MFMA 32x32x16 (16-bit products exact, sums fp32).  The next
 // chunk's global loads are issued before the current chunk's MFMAs.  320- and
 // 192-byte stage rows keep the 4-row footprints of a transposing read on
 // disjoint banks.
 constexpr int WG_CHUNK = 64;
-template <int JT>
+template <int JT, bool F16>
 __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ P,
                                                const float* __restrict__ Q, int64_t M, int64_t C,
                                                int r, float scaling, float* __restrict__ out,
@@ -378,9 +391,9 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ P,
 #pragma unroll
     for (int i = 0; i < QPASS; ++i) {
       const f32x4_t v = qr[i];
-      const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
-      const uint32_t l01 = pack_bf16x2(v[0] - bf16_lo(h01), v[1] - bf16_hi(h01));
-      const uint32_t l23 = pack_bf16x2(v[2] - bf16_lo(h23), v[3] - bf16_hi(h23));
+      const uint32_t h01 = pack16x2<F16>(v[0], v[1]), h23 = pack16x2<F16>(v[2], v[3]);
+      const uint32_t l01 = pack16x2<F16>(v[0] - lo16<F16>(h01), v[1] - hi16<F16>(h01));
+      const uint32_t l23 = pack16x2<F16>(v[2] - lo16<F16>(h23), v[3] - hi16<F16>(h23));
       const int o = (q_row + (256 / QV) * i) * LDQ + q_j;
       *reinterpret_cast<u32x2_t*>(sQh + o) = u32x2_t{h01, h23};
       *reinterpret_cast<u32x2_t*>(sQl + o) = u32x2_t{l01, l23};
@@ -414,12 +427,8 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ P,
       const u32x4_t b = frag(sP, LDP, kk, 32 * wave);
 #pragma unroll
       for (int t = 0; t < JT; ++t) {
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, frag(sQh, LDQ, kk, 32 * t)), __builtin_bit_cast(bf16x8_t, b),
-            acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, frag(sQl, LDQ, kk, 32 * t)), __builtin_bit_cast(bf16x8_t, b),
-            acc[t], 0, 0, 0);
+        acc[t] = mfma32x32x16<F16>(frag(sQh, LDQ, kk, 32 * t), b, acc[t]);
+        acc[t] = mfma32x32x16<F16>(frag(sQl, LDQ, kk, 32 * t), b, acc[t]);
       }
     }
     __syncthreads();
@@ -467,11 +476,11 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ 
     out[idx] = scaling * v;
 }
 
-template <bool GROUPED, bool VEC>
+template <bool GROUPED, bool VEC, bool F16>
 static void rowdot_launch(int max_r, dim3 grid, hipStream_t s, const uint16_t* P, const uint16_t* Q,
                           int64_t M, int64_t C, int r, float* out, const RowdotJob* jobs, int rows) {
 #define QL_RD(RT) \
-  hipLaunchKernelGGL((k_rowdot<RT, GROUPED, VEC>), grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out, jobs, rows)
+  hipLaunchKernelGGL((k_rowdot<RT, GROUPED, VEC, F16>), grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out, jobs, rows)
   if (max_r <= 16) QL_RD(1);
   else if (max_r <= 32) QL_RD(2);
   else if (max_r <= 64) QL_RD(4);
@@ -479,8 +488,9 @@ static void rowdot_launch(int max_r, dim3 grid, hipStream_t s, const uint16_t* P
 #undef QL_RD
 }
 
-hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
-                         float* out, float* part, hipStream_t s) {
+template <bool F16>
+static hipError_t rowdot_any(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
+                             float* out, float* part, hipStream_t s) {
   const bool vec = C % 8 == 0 && (reinterpret_cast<uintptr_t>(P) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(Q) & 15) == 0;
   const int ns = rowdot_splits(M, C, r);
@@ -491,9 +501,9 @@ hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_
     const int per = (int)((chunks + ns - 1) / ns);
     const dim3 grid((unsigned)tiles, (unsigned)ns);
     if (r <= 32)
-      hipLaunchKernelGGL(k_rowdot_sk<2>, grid, dim3(512), 0, s, P, Q, M, C, r, out, part, ns, per);
+      hipLaunchKernelGGL((k_rowdot_sk<2, F16>), grid, dim3(512), 0, s, P, Q, M, C, r, out, part, ns, per);
     else
-      hipLaunchKernelGGL(k_rowdot_sk<4>, grid, dim3(512), 0, s, P, Q, M, C, r, out, part, ns, per);
+      hipLaunchKernelGGL((k_rowdot_sk<4, F16>), grid, dim3(512), 0, s, P, Q, M, C, r, out, part, ns, per);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
     const int64_t n = M * r;
@@ -507,17 +517,26 @@ hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_
   // 16-byte rows: both operands start 16-byte aligned (checked by the caller
   // for X and dY; A and the transposed B are C-element rows)
   if (vec)
-    rowdot_launch<false, true>(r, grid, s, P, Q, M, C, r, out, nullptr, rows);
+    rowdot_launch<false, true, F16>(r, grid, s, P, Q, M, C, r, out, nullptr, rows);
   else
-    rowdot_launch<false, false>(r, grid, s, P, Q, M, C, r, out, nullptr, rows);
+    rowdot_launch<false, false, F16>(r, grid, s, P, Q, M, C, r, out, nullptr, rows);
   return hipGetLastError();
 }
 
+hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
+                         float* out, float* part, bool f16, hipStream_t s) {
+  return f16 ? rowdot_any<true>(P, Q, M, C, r, out, part, s)
+             : rowdot_any<false>(P, Q, M, C, r, out, part, s);
+}
+
 hipError_t launch_rowdot_grouped(const RowdotJob* jobs, int njobs, int64_t M, int max_r,
-                                 hipStream_t s) {
+                                 bool f16, hipStream_t s) {
   // the jobs' contraction lengths are whole 64-blocks; X and A are 16-byte aligned
-  rowdot_launch<true, true>(max_r, dim3((unsigned)((M + 15) / 16), 1, (unsigned)njobs), s, nullptr,
-                            nullptr, M, int64_t(0), 0, nullptr, jobs, 16);
+  const dim3 grid((unsigned)((M + 15) / 16), 1, (unsigned)njobs);
+  if (f16)
+    rowdot_launch<true, true, true>(max_r, grid, s, nullptr, nullptr, M, int64_t(0), 0, nullptr, jobs, 16);
+  else
+    rowdot_launch<true, true, false>(max_r, grid, s, nullptr, nullptr, M, int64_t(0), 0, nullptr, jobs, 16);
   return hipGetLastError();
 }
 
@@ -534,17 +553,20 @@ int wgrad_rows_per_split(int64_t M, int msplit) {
 
 hipError_t launch_wgrad(const uint16_t* P, const float* Q, int64_t M, int64_t C, int r,
                         float scaling, float* out, bool transpose_out, float* part, int msplit,
-                        hipStream_t s) {
+                        bool f16, hipStream_t s) {
   // splits of whole 64-row chunks; a split past the rows writes a zero partial
   const int rows = wgrad_rows_per_split(M, msplit);
   const int jt = r <= 32 ? 1 : 2;
   dim3 grid((unsigned)((C + 127) / 128), (unsigned)msplit, (unsigned)((r + 32 * jt - 1) / (32 * jt)));
-  if (jt == 1)
-    hipLaunchKernelGGL(k_wgrad<1>, grid, dim3(256), 0, s, P, Q, M, C, r, scaling, out,
-                       (int)transpose_out, part, msplit, rows);
-  else
-    hipLaunchKernelGGL(k_wgrad<2>, grid, dim3(256), 0, s, P, Q, M, C, r, scaling, out,
-                       (int)transpose_out, part, msplit, rows);
+#define QL_WG(JT, H)                                                                       \
+  hipLaunchKernelGGL((k_wgrad<JT, H>), grid, dim3(256), 0, s, P, Q, M, C, r, scaling, out, \
+                     (int)transpose_out, part, msplit, rows)
+  if (jt == 1) {
+    if (f16) QL_WG(1, true); else QL_WG(1, false);
+  } else {
+    if (f16) QL_WG(2, true); else QL_WG(2, false);
+  }
+#undef QL_WG
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || msplit == 1) return e;
   const int64_t total = (int64_t)r * C;

@@ -78,8 +78,9 @@ QL_DEV uint32_t encode8(const float (&xin)[8], float am, const float2* tab) {
 // entries: block 64 at the unit's storage position, block 32 at 2 p + half,
 // block 128 at the row-group position over the k/128 block columns.  Without
 // double quantization (DQ false) the block absmax itself is stored, fp32, in
-// `step`, and `qscale` is unused.
-template <bool DQ, int BS>
+// `step`, and `qscale` is unused.  F16: the weight is fp16 instead of bf16
+// (both widen to fp32 exactly, after which the steps are the same).
+template <bool DQ, int BS, bool F16 = false>
 __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict__ W,
                                                       const float* __restrict__ codebook,
                                                       uint8_t* __restrict__ codes,
@@ -139,8 +140,8 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
       float x[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        x[2 * j] = bf16_lo(cur[it][j]);
-        x[2 * j + 1] = bf16_hi(cur[it][j]);
+        x[2 * j] = lo16<F16>(cur[it][j]);
+        x[2 * j + 1] = hi16<F16>(cur[it][j]);
       }
       float am = 0.f;
 #pragma unroll
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(256) void k_dequant(Nf4View w, const float* __restr
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w.codes + p * 32);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const Lut t = make_lut(lv, sh[h]);
+      const Lut t = make_lut<FmtInfo<FMT>::f16>(lv, sh[h]);
       const u32x4_t c = src[h];
 #pragma unroll
       for (int j = 0; j < 4; ++j) dst[h * 4 + j] = decode8(t, c[j]);
@@ -366,12 +367,13 @@ __global__ __launch_bounds__(256) void k_dequant(Nf4View w, const float* __restr
 
 // Adapter merge (www.lqnn.cn/news/228537 §3.3: dequantize, add the low-rank
 // branch at high precision, quantize again), in place on the dequantized
-// weight W [N x K] bf16:
-//   merged[n][k] = bf16_rne(fp32(w + fp32(s * acc))),
-//   acc = sum_j B[n][j] A[j][k]  in binary32, in rank order (bf16 products are exact).
+// weight W [N x K] (bf16, or fp16 when F16, as are A and B):
+//   merged[n][k] = rne16(fp32(w + fp32(s * acc))),
+//   acc = sum_j B[n][j] A[j][k]  in binary32, in rank order (16-bit products are exact).
 // A thread owns 8 consecutive k of one row: A[j][k .. k+7] as one 16-byte load
 // per rank, B[n][j] as a scalar shared by the row's threads.  Contraction of
 // the multiply-add into an fma is switched off: the steps round as written.
+template <bool F16>
 __global__ __launch_bounds__(256) void k_merge(uint16_t* __restrict__ W, const uint16_t* __restrict__ A,
                                                const uint16_t* __restrict__ B, int64_t N, int64_t K,
                                                int r, float s) {
@@ -384,12 +386,12 @@ __global__ __launch_bounds__(256) void k_merge(uint16_t* __restrict__ W, const u
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   for (int j = 0; j < r; ++j) {
-    const float b = __builtin_bit_cast(float, (uint32_t)B[n * r + j] << 16);
+    const float b = w16<F16>(B[n * r + j]);
     const u32x4_t a = *reinterpret_cast<const u32x4_t*>(A + (int64_t)j * K + k);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc[2 * e] = acc[2 * e] + b * bf16_lo(a[e]);
-      acc[2 * e + 1] = acc[2 * e + 1] + b * bf16_hi(a[e]);
+      acc[2 * e] = acc[2 * e] + b * lo16<F16>(a[e]);
+      acc[2 * e + 1] = acc[2 * e + 1] + b * hi16<F16>(a[e]);
     }
   }
   u32x4_t* wp = reinterpret_cast<u32x4_t*>(W + n * K + k);
@@ -398,15 +400,19 @@ __global__ __launch_bounds__(256) void k_merge(uint16_t* __restrict__ W, const u
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float t0 = s * acc[2 * e], t1 = s * acc[2 * e + 1];
-    o[e] = pack_bf16x2(bf16_lo(w[e]) + t0, bf16_hi(w[e]) + t1);
+    o[e] = pack16x2<F16>(lo16<F16>(w[e]) + t0, hi16<F16>(w[e]) + t1);
   }
   *wp = o;
 }
 
 hipError_t launch_merge(uint16_t* W, const uint16_t* A, const uint16_t* B, int64_t n, int64_t k, int r,
-                        float s, hipStream_t st) {
+                        float s, bool f16, hipStream_t st) {
   const int64_t pieces = n * (k / 8);
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st, W, A, B, n, k, r, s);
+  const dim3 grid((unsigned)((pieces + 255) / 256));
+  if (f16)
+    hipLaunchKernelGGL(k_merge<true>, grid, dim3(256), 0, st, W, A, B, n, k, r, s);
+  else
+    hipLaunchKernelGGL(k_merge<false>, grid, dim3(256), 0, st, W, A, B, n, k, r, s);
   return hipGetLastError();
 }
 
@@ -421,10 +427,11 @@ hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* co
   const int bs = fmt == kFmtNf4Dq32 || fmt == kFmtNf4_32 ? 32 : (fmt == kFmtNf4Dq128 || fmt == kFmtNf4_128 ? 128 : 64);
   const int64_t ngB = (n * k / bs + kGroup - 1) / kGroup;
   const dim3 ggrid((unsigned)std::min<int64_t>((ngB + 7) / 8 * 8, 256 * 8));
-#define QL_QNF4(DQ, BS) \
-  hipLaunchKernelGGL((k_quant_nf4_dq<DQ, BS>), ggrid, dim3(256), 0, s, W, codebook, codes, qscale, step, n, nkb)
+#define QL_QNF4(DQ, BS, ...) \
+  hipLaunchKernelGGL((k_quant_nf4_dq<DQ, BS, ##__VA_ARGS__>), ggrid, dim3(256), 0, s, W, codebook, codes, qscale, step, n, nkb)
   switch (fmt) {
     case kFmtNf4Dq: QL_QNF4(true, 64); break;
+    case kFmtNf4DqF16: QL_QNF4(true, 64, true); break;
     case kFmtNf4: QL_QNF4(false, 64); break;
     case kFmtNf4Dq32: QL_QNF4(true, 32); break;
     case kFmtNf4_32: QL_QNF4(false, 32); break;
@@ -453,6 +460,7 @@ hipError_t launch_dequant(const Nf4View& w, const float* codebook, uint16_t* out
     case kFmtNf4Dq32: QL_DQ(kFmtNf4Dq32); break;
     case kFmtNf4_32: QL_DQ(kFmtNf4_32); break;
     case kFmtNf4Dq128: QL_DQ(kFmtNf4Dq128); break;
+    case kFmtNf4DqF16: QL_DQ(kFmtNf4DqF16); break;
     default: QL_DQ(kFmtNf4_128); break;
   }
 #undef QL_DQ

@@ -79,8 +79,8 @@ def test_strerror_covers_codes():
 FAKE = 0x100000   # never dereferenced: every call below fails validation first
 
 
-def _desc(n=64, k=128, codes=FAKE, qs=FAKE, st=FAKE, fmt=0, block=0):
-    return B._Nf4Desc(n, k, codes, qs, st, fmt, block)
+def _desc(n=64, k=128, codes=FAKE, qs=FAKE, st=FAKE, fmt=0, block=0, dtype=0):
+    return B._Nf4Desc(n, k, codes, qs, st, fmt, block, dtype)
 
 
 @pytest.mark.parametrize("n,k", [(1, 128), (3, 256), (4096, 11008), (257, 640)])
@@ -244,6 +244,31 @@ def test_merge_argument_errors():
     assert mg(W=ctypes.byref(u), cb=None, out=ctypes.byref(_desc())) == 1   # an NF4 target does
 
 
+def test_compute_dtype_argument_errors():
+    # fp16 compute only for NF4 at block 64 with double quantization; a 16-bit
+    # output must name the compute type; unknown dtypes are refused
+    L = B.lib()
+    F16, BF16, F32 = B.QLORA_F16, B.QLORA_BF16, B.QLORA_F32
+    h = _desc(dtype=F16)
+    for bad in (_desc(dtype=F16, fmt=B.QLORA_FMT_U4_ASYM, qs=0), _desc(dtype=F16, fmt=B.QLORA_FMT_Q8_0),
+                _desc(dtype=F16, block=32), _desc(dtype=F16, block=128), _desc(dtype=F16, qs=0),
+                _desc(dtype=3), _desc(dtype=-1)):
+        assert L.qlora_quantize(FAKE, FAKE, ctypes.byref(bad), None) == 4
+        assert _fwd(L, bad) == 4
+    assert _fwd(L, h, ydt=BF16) == 4
+    assert _fwd(L, _desc(), ydt=F16) == 4
+    assert _fwd(L, _desc(dtype=BF16), ydt=F16) == 4
+    # accepted combinations get past the dtype checks (to the misaligned X)
+    for d, y in ((h, F16), (h, F32), (_desc(), BF16), (_desc(dtype=BF16), F32)):
+        assert _fwd(L, d, ydt=y, X=FAKE + 2) == 3
+    bwd = lambda d, dt: L.qlora_linear_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, 16, FAKE, FAKE, 8, 1.0,
+                                           FAKE, FAKE, dt, FAKE, FAKE, FAKE, 1 << 30, 0, None)
+    assert bwd(h, BF16) == 4 and bwd(_desc(), F16) == 4
+    # merge: the target's compute type must be the base's
+    assert L.qlora_merge(ctypes.byref(h), FAKE, FAKE, FAKE, 8, 2.0, FAKE, ctypes.byref(_desc()), None) == 4
+    assert L.qlora_merge(ctypes.byref(_desc()), FAKE, FAKE, FAKE, 8, 2.0, FAKE, ctypes.byref(h), None) == 4
+
+
 def _job(n=64, k=128, X=FAKE, A=FAKE, Bp=FAKE, r=8, Y=FAKE, T=FAKE, codes=FAKE, qs=FAKE, fmt=0):
     return B._FwdJob(_desc(n, k, codes=codes, qs=qs, fmt=fmt), X, A, Bp, r, 2.0, Y, T)
 
@@ -296,10 +321,12 @@ def test_grouped_fwd_argument_errors():
                         variant=variant, m=m, row_groups=8, max_quads=1)
     g = grp()
     assert L.qlora_linear_fwd_grouped(ctypes.byref(g), None, None) == 1
-    bad = grp(variant=8)
+    bad = grp(variant=9)
     assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
     g7 = grp(variant=7)                                   # NF4 block 128: the codebook is required
     assert L.qlora_linear_fwd_grouped(ctypes.byref(g7), None, None) == 1
+    g8 = grp(variant=8)                                   # NF4 with fp16 compute: likewise
+    assert L.qlora_linear_fwd_grouped(ctypes.byref(g8), None, None) == 1
     bad = grp(variant=-1)
     assert L.qlora_linear_fwd_grouped(ctypes.byref(bad), FAKE, None) == 8
     bad = grp(count=0)
