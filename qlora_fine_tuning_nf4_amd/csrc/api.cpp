@@ -93,12 +93,13 @@ int plan_dx_split(int64_t m, int64_t n, int64_t k) {
   return tiles >= 192 ? 1 : (int)std::min<int64_t>(cap, cdiv(256, tiles));
 }
 
-// adapter-gradient splits over the rows: enough workgroups (tiles of 128
-// columns x 32 or 64 ranks, times the splits) to fill the chip twice over,
-// each split at least one 64-row chunk
-int plan_wgrad_split(int64_t m, int64_t c, int r) {
+// adapter-gradient splits over the rows (dA over k columns and dB over n in
+// one launch): enough workgroups (tiles of 128 columns x 32 or 64 ranks, times
+// the splits) to fill the chip twice over, each split at least one 64-row
+// chunk
+int plan_wgrad_split(int64_t m, int64_t k, int64_t n, int r) {
   const int64_t jw = r <= 32 ? 32 : 64;
-  const int64_t tiles = cdiv(c, 128) * cdiv(std::max(r, 1), jw);
+  const int64_t tiles = (cdiv(k, 128) + cdiv(n, 128)) * cdiv(std::max(r, 1), jw);
   return (int)std::min<int64_t>(std::max<int64_t>(1, cdiv(512, tiles)), cdiv(m, 64));
 }
 
@@ -134,8 +135,8 @@ BwdWs bwd_ws(int64_t m, int64_t n, int64_t k, int r) {
   // those run the rank projections' split partials (U over n, T over k)
   size_t wg = 0;
   if (r > 0) {
-    const int s1 = plan_wgrad_split(m, k, r), s2 = plan_wgrad_split(m, n, r);
-    wg = sizeof(float) * std::max((size_t)s1 * r * k * (s1 > 1), (size_t)s2 * r * n * (s2 > 1));
+    const int sw = plan_wgrad_split(m, k, n, r);
+    wg = sw > 1 ? sizeof(float) * (size_t)sw * r * (k + n) : 0;
     const int ru = ql::rowdot_splits(m, n, r), rt = ql::rowdot_splits(m, k, r);
     wg = std::max(wg, sizeof(float) * (size_t)std::max(ru * (ru > 1), rt * (rt > 1)) * m * r);
   }
@@ -539,11 +540,9 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
   }
   if (r > 0) {
     float* part = (float*)(wsb + L.wg_off);
-    if (ql::launch_wgrad(X, U, m, k, r, scaling, dA, false, part, plan_wgrad_split(m, k, r),
-                         is_f16(W), s) != hipSuccess)
-      return QLORA_ERR_HIP;
-    if (ql::launch_wgrad(dY, T, m, n, r, scaling, dB, true, part, plan_wgrad_split(m, n, r),
-                         is_f16(W), s) != hipSuccess)
+    const ql::WgradJob ja{X, U, k, dA, 0}, jb{dY, T, n, dB, 1};
+    if (ql::launch_wgrad(ja, jb, m, r, scaling, part, plan_wgrad_split(m, k, n, r), is_f16(W), s) !=
+        hipSuccess)
       return QLORA_ERR_HIP;
   }
   return QLORA_OK;

@@ -125,12 +125,19 @@ hipError_t launch_rowdot_grouped(const RowdotJob* jobs, int njobs, int64_t M, in
                                  bool f16, hipStream_t s);
 // Qt[j][n] = Q[n][j] for a 16-bit [N x r] matrix.
 hipError_t launch_transpose_bf16(const uint16_t* Q, int64_t N, int r, uint16_t* Qt, hipStream_t s);
-// Weight gradients of the adapter: out = scaling * sum_m Q[m][j] * P[m][c]
+// One weight gradient of the adapter: out = scaling * sum_m Q[m][j] * P[m][c]
 // (P [M x C] fp16 when f16 else bf16, Q fp32 [M x r]); written as out[j][c]
-// (transpose_out false, [r x C]) or out[c][j] (true, [C x r]).  msplit
-// partials go through `part`.
-hipError_t launch_wgrad(const uint16_t* P, const float* Q, int64_t M, int64_t C, int r,
-                        float scaling, float* out, bool transpose_out, float* part, int msplit,
-                        bool f16, hipStream_t s);
+// (transpose_out 0, [r x C]) or out[c][j] (1, [C x r]).
+struct WgradJob {
+  const uint16_t* P;
+  const float* Q;
+  int64_t C;
+  float* out;
+  int transpose_out;
+};
+// Both gradients of a backward (a: dA, b: dB) in one launch, plus one
+// reduction launch when msplit > 1 (`part`: msplit * r * (a.C + b.C) floats).
+hipError_t launch_wgrad(const WgradJob& a, const WgradJob& b, int64_t M, int r, float scaling,
+                        float* part, int msplit, bool f16, hipStream_t s);
 
 }  // namespace ql

@@ -320,6 +320,9 @@ QL_DEV f32x16_t mfma32x32x16(const u32x4_t a, const u32x4_t b, f32x16_t c) {
 // written as out[j][c] ([r x C]) or, transposed, out[c][j] ([C x r]); with
 // msplit > 1 split s writes its unscaled sum over rows
 // [s * rows_per_split, +rows_per_split) to part[s][j][c] for k_wgrad_reduce.
+// One launch serves both products of a backward (dA: P = X, Q = U; dB: P = dY,
+// Q = T): column tiles [0, tiles_a) belong to job a, the rest to job b, whose
+// partials follow job a's (msplit * r * C_a floats).
 // A workgroup of 4 waves owns 32*JT ranks x 128 columns and walks its rows
 // in chunks of 64.  Each chunk of P (64 x 128) and of Q (64 x 32*JT fp32,
 // split into 16-bit parts of P's type, hi = rne(q) and lo = rne(q - hi),
@@ -333,11 +336,17 @@ QL_DEV f32x16_t mfma32x32x16(const u32x4_t a, const u32x4_t b, f32x16_t c) {
 // disjoint banks.
 constexpr int WG_CHUNK = 64;
 template <int JT, bool F16>
-__global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ P,
-                                               const float* __restrict__ Q, int64_t M, int64_t C,
-                                               int r, float scaling, float* __restrict__ out,
-                                               int transpose_out, float* __restrict__ part,
+__global__ __launch_bounds__(256) void k_wgrad(WgradJob ja, WgradJob jb, int tiles_a, int64_t M,
+                                               int r, float scaling, float* __restrict__ part,
                                                int msplit, int rows_per_split) {
+  const bool second = (int)blockIdx.x >= tiles_a;
+  const WgradJob& J = second ? jb : ja;
+  const uint16_t* __restrict__ P = J.P;
+  const float* __restrict__ Q = J.Q;
+  const int64_t C = J.C;
+  float* __restrict__ out = J.out;
+  const int transpose_out = J.transpose_out;
+  if (second) part += (int64_t)msplit * r * ja.C;
   constexpr int JW = 32 * JT;              // ranks per workgroup tile
   constexpr int LDP = 128 + 32;            // stage pitches (bf16 elements)
   constexpr int LDQ = JW + 32;
@@ -347,7 +356,7 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ P,
   __shared__ __attribute__((aligned(16))) uint16_t sQh[WG_CHUNK * LDQ];
   __shared__ __attribute__((aligned(16))) uint16_t sQl[WG_CHUNK * LDQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t c0 = (int64_t)blockIdx.x * 128;
+  const int64_t c0 = (int64_t)(second ? (int)blockIdx.x - tiles_a : (int)blockIdx.x) * 128;
   const int split = blockIdx.y;
   const int j0 = blockIdx.z * JW;
   const int64_t m_begin = (int64_t)split * rows_per_split;
@@ -452,11 +461,21 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t* __restrict__ P,
     }
 }
 
+// out of both jobs = scaling * (sum of the msplit partials, in split order)
 __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ part, int msplit,
-                                                      int64_t C, int r, float scaling,
-                                                      float* __restrict__ out, int transpose_out) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // = j * C + c
-  if (idx >= (int64_t)r * C) return;
+                                                      int r, float scaling, WgradJob ja,
+                                                      WgradJob jb) {
+  int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // = j * C + c within its job
+  const int64_t na = (int64_t)r * ja.C;
+  if (idx >= na + (int64_t)r * jb.C) return;
+  const bool second = idx >= na;
+  if (second) {
+    idx -= na;
+    part += (int64_t)msplit * na;
+  }
+  const int64_t C = second ? jb.C : ja.C;
+  float* __restrict__ out = second ? jb.out : ja.out;
+  const int transpose_out = second ? jb.transpose_out : ja.transpose_out;
   // partials added in split order; eight loads in flight at a time
   const int64_t stride = (int64_t)r * C;
   float v = 0.f;
@@ -551,16 +570,16 @@ int wgrad_rows_per_split(int64_t M, int msplit) {
   return (int)((per + WG_CHUNK - 1) / WG_CHUNK * WG_CHUNK);
 }
 
-hipError_t launch_wgrad(const uint16_t* P, const float* Q, int64_t M, int64_t C, int r,
-                        float scaling, float* out, bool transpose_out, float* part, int msplit,
-                        bool f16, hipStream_t s) {
+hipError_t launch_wgrad(const WgradJob& a, const WgradJob& b, int64_t M, int r, float scaling,
+                        float* part, int msplit, bool f16, hipStream_t s) {
   // splits of whole 64-row chunks; a split past the rows writes a zero partial
   const int rows = wgrad_rows_per_split(M, msplit);
   const int jt = r <= 32 ? 1 : 2;
-  dim3 grid((unsigned)((C + 127) / 128), (unsigned)msplit, (unsigned)((r + 32 * jt - 1) / (32 * jt)));
-#define QL_WG(JT, H)                                                                       \
-  hipLaunchKernelGGL((k_wgrad<JT, H>), grid, dim3(256), 0, s, P, Q, M, C, r, scaling, out, \
-                     (int)transpose_out, part, msplit, rows)
+  const int tiles_a = (int)((a.C + 127) / 128), tiles_b = (int)((b.C + 127) / 128);
+  dim3 grid((unsigned)(tiles_a + tiles_b), (unsigned)msplit, (unsigned)((r + 32 * jt - 1) / (32 * jt)));
+#define QL_WG(JT, H)                                                                           \
+  hipLaunchKernelGGL((k_wgrad<JT, H>), grid, dim3(256), 0, s, a, b, tiles_a, M, r, scaling, part, \
+                     msplit, rows)
   if (jt == 1) {
     if (f16) QL_WG(1, true); else QL_WG(1, false);
   } else {
@@ -569,9 +588,9 @@ hipError_t launch_wgrad(const uint16_t* P, const float* Q, int64_t M, int64_t C,
 #undef QL_WG
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || msplit == 1) return e;
-  const int64_t total = (int64_t)r * C;
+  const int64_t total = (int64_t)r * (a.C + b.C);
   hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part,
-                     msplit, C, r, scaling, out, (int)transpose_out);
+                     msplit, r, scaling, a, b);
   return hipGetLastError();
 }
 
