@@ -518,10 +518,16 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
   const float* T = T_saved;
   if (r > 0) {
     U = (float*)(wsb + L.u_off);
-    uint16_t* Bt = (uint16_t*)(wsb + L.bt_off);
-    if (ql::launch_transpose_bf16(B, n, r, Bt, s) != hipSuccess) return QLORA_ERR_HIP;
     float* rpart = (float*)(wsb + L.wg_off);
-    if (ql::launch_rowdot(dY, Bt, m, n, r, U, rpart, is_f16(W), s) != hipSuccess) return QLORA_ERR_HIP;
+    if (ql::rowdot_t_supported(dY, B, m, n, r)) {   // U = dY B reading B as stored
+      if (ql::launch_rowdot_t(dY, B, m, n, r, U, rpart, is_f16(W), s) != hipSuccess)
+        return QLORA_ERR_HIP;
+    } else {
+      uint16_t* Bt = (uint16_t*)(wsb + L.bt_off);
+      if (ql::launch_transpose_bf16(B, n, r, Bt, s) != hipSuccess) return QLORA_ERR_HIP;
+      if (ql::launch_rowdot(dY, Bt, m, n, r, U, rpart, is_f16(W), s) != hipSuccess)
+        return QLORA_ERR_HIP;
+    }
     if (!T) {
       float* Tw = (float*)(wsb + L.t_off);
       if (ql::launch_rowdot(X, A, m, k, r, Tw, rpart, is_f16(W), s) != hipSuccess) return QLORA_ERR_HIP;

@@ -27,9 +27,13 @@ QL_DEV u32x4_t load8_guard(const uint16_t* row, int64_t c, int64_t C, bool vec) 
 // past the contraction) point past the buffer and read zeros, so there are
 // no branches, and two register sets alternate: the next U slices load while
 // the current ones are multiplied.  The 8 partial tiles are summed in a
-// fixed order through LDS.  16-bit products are exact, sums fp32.
+// fixed order through LDS.  16-bit products are exact, sums fp32.  QT: Q is
+// given transposed, as Qs [C x r] row-major (the adapter factor B of the
+// backward, U = dY B): the VEC path gathers each fragment with 2-byte loads
+// (kept for completeness; the launcher takes QT to the split kernel only,
+// where the gathers are cheaper than a transposed copy).
 constexpr int RD_WAVES = 8;
-template <int RT, bool GROUPED, bool VEC, bool F16>
+template <int RT, bool GROUPED, bool VEC, bool F16, bool QT = false>
 __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
                                                 const uint16_t* __restrict__ Q, int64_t M,
                                                 int64_t C, int r, float* __restrict__ out,
@@ -59,7 +63,10 @@ __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
     const uint32_t pbase = li < nr ? (uint32_t)(li * C * 2) : kOut;
     uint32_t qbase[RT];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) qbase[t] = 16 * t + li < r ? (uint32_t)((16 * t + li) * C * 2) : kOut;
+    for (int t = 0; t < RT; ++t) {
+      const int j = 16 * t + li;
+      qbase[t] = j < r ? (uint32_t)(QT ? j * 2 : j * C * 2) : kOut;
+    }
     auto ld_round = [&](int64_t c0, u32x4_t (&a)[U], u32x4_t (&b)[U][RT]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -68,8 +75,20 @@ __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
         const uint32_t co = (uint32_t)(c * 2);
         a[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs, cok ? pbase + co : kOut, 0, 0));
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
-          b[u][t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(qrs, cok ? qbase[t] + co : kOut, 0, 0));
+        for (int t = 0; t < RT; ++t) {
+          if constexpr (QT) {
+            // Q[j][c + e] = Qs[c + e][j]: eight 2-byte loads, rows past C
+            // (and ranks past r) read zeros
+            uint32_t h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              h[e] = __builtin_amdgcn_raw_buffer_load_b16(
+                  qrs, c + e < C && qbase[t] != kOut ? qbase[t] + (uint32_t)((c + e) * r * 2) : kOut, 0, 0);
+            b[u][t] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+          } else {
+            b[u][t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(qrs, cok ? qbase[t] + co : kOut, 0, 0));
+          }
+        }
       }
     };
     auto mma_round = [&](const u32x4_t (&a)[U], const u32x4_t (&b)[U][RT]) {
@@ -150,7 +169,7 @@ struct RsGeo {
   static constexpr int XS = CH / 32;                  // slices per wave and chunk
 };
 
-template <int RT, bool F16>
+template <int RT, bool F16, bool QT = false>
 __global__ __launch_bounds__(512) void k_rowdot_sk(const uint16_t* __restrict__ P,
                                                    const uint16_t* __restrict__ Q, int64_t M,
                                                    int64_t C, int r, float* __restrict__ out,
@@ -176,23 +195,40 @@ __global__ __launch_bounds__(512) void k_rowdot_sk(const uint16_t* __restrict__ 
   const uint32_t pbase = prow < nr ? (uint32_t)(prow * C * 2) : kOut;
 
   // Q pieces of this thread: piece i covers chunk row q / (CH/8), 8 columns
-  // from 8 (q % (CH/8)), q = tid + 512 i
+  // from 8 (q % (CH/8)), q = tid + 512 i.  QT (Q given as Qs [C x r], r % 8
+  // == 0): piece i is ranks 8 (q % (2 RT)) .. +7 of chunk column q / (2 RT),
+  // one 16-byte load of a Qs row, stored transposed into the stage.
   auto load_q = [&](int64_t cb, u32x4_t (&v)[QL]) {
 #pragma unroll
     for (int i = 0; i < QL; ++i) {
       const int q = tid + 512 * i;
-      const int j = q / (CH / 8);
-      const int64_t c = cb + 8 * (q % (CH / 8));
-      const bool ok = j < r && c < c_end;
-      v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                            qrs, ok ? (uint32_t)((j * C + c) * 2) : kOut, 0, 0));
+      if constexpr (QT) {
+        const int j8 = 8 * (q % (2 * RT));
+        const int64_t c = cb + q / (2 * RT);
+        const bool ok = j8 < r && c < c_end;
+        v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                              qrs, ok ? (uint32_t)((c * r + j8) * 2) : kOut, 0, 0));
+      } else {
+        const int j = q / (CH / 8);
+        const int64_t c = cb + 8 * (q % (CH / 8));
+        const bool ok = j < r && c < c_end;
+        v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                              qrs, ok ? (uint32_t)((j * C + c) * 2) : kOut, 0, 0));
+      }
     }
   };
   auto store_q = [&](const u32x4_t (&v)[QL], uint16_t* sq) {
 #pragma unroll
     for (int i = 0; i < QL; ++i) {
       const int q = tid + 512 * i;
-      *reinterpret_cast<u32x4_t*>(sq + (q / (CH / 8)) * PITCH + 8 * (q % (CH / 8))) = v[i];
+      if constexpr (QT) {
+        const int j8 = 8 * (q % (2 * RT)), cl = q / (2 * RT);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sq[(j8 + e) * PITCH + cl] = (uint16_t)(e & 1 ? v[i][e >> 1] >> 16 : v[i][e >> 1] & 0xFFFFu);
+      } else {
+        *reinterpret_cast<u32x4_t*>(sq + (q / (CH / 8)) * PITCH + 8 * (q % (CH / 8))) = v[i];
+      }
     }
   };
   auto load_x = [&](int64_t cb, u32x4_t (&x)[XS]) {
@@ -495,11 +531,11 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ 
     out[idx] = scaling * v;
 }
 
-template <bool GROUPED, bool VEC, bool F16>
+template <bool GROUPED, bool VEC, bool F16, bool QT = false>
 static void rowdot_launch(int max_r, dim3 grid, hipStream_t s, const uint16_t* P, const uint16_t* Q,
                           int64_t M, int64_t C, int r, float* out, const RowdotJob* jobs, int rows) {
 #define QL_RD(RT) \
-  hipLaunchKernelGGL((k_rowdot<RT, GROUPED, VEC, F16>), grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out, jobs, rows)
+  hipLaunchKernelGGL((k_rowdot<RT, GROUPED, VEC, F16, QT>), grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out, jobs, rows)
   if (max_r <= 16) QL_RD(1);
   else if (max_r <= 32) QL_RD(2);
   else if (max_r <= 64) QL_RD(4);
@@ -507,11 +543,12 @@ static void rowdot_launch(int max_r, dim3 grid, hipStream_t s, const uint16_t* P
 #undef QL_RD
 }
 
-template <bool F16>
+template <bool F16, bool QT>
 static hipError_t rowdot_any(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
                              float* out, float* part, hipStream_t s) {
   const bool vec = C % 8 == 0 && (reinterpret_cast<uintptr_t>(P) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(Q) & 15) == 0;
+  if (QT && (!vec || r % 8 != 0)) return hipErrorInvalidValue;   // rowdot_t_supported is false
   const int ns = rowdot_splits(M, C, r);
   if (vec && rowdot_uses_split_path(M, r) && (ns == 1 || part)) {
     const int64_t tiles = (M + RS_ROWS - 1) / RS_ROWS;
@@ -520,9 +557,9 @@ static hipError_t rowdot_any(const uint16_t* P, const uint16_t* Q, int64_t M, in
     const int per = (int)((chunks + ns - 1) / ns);
     const dim3 grid((unsigned)tiles, (unsigned)ns);
     if (r <= 32)
-      hipLaunchKernelGGL((k_rowdot_sk<2, F16>), grid, dim3(512), 0, s, P, Q, M, C, r, out, part, ns, per);
+      hipLaunchKernelGGL((k_rowdot_sk<2, F16, QT>), grid, dim3(512), 0, s, P, Q, M, C, r, out, part, ns, per);
     else
-      hipLaunchKernelGGL((k_rowdot_sk<4, F16>), grid, dim3(512), 0, s, P, Q, M, C, r, out, part, ns, per);
+      hipLaunchKernelGGL((k_rowdot_sk<4, F16, QT>), grid, dim3(512), 0, s, P, Q, M, C, r, out, part, ns, per);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
     const int64_t n = M * r;
@@ -536,7 +573,7 @@ static hipError_t rowdot_any(const uint16_t* P, const uint16_t* Q, int64_t M, in
   // 16-byte rows: both operands start 16-byte aligned (checked by the caller
   // for X and dY; A and the transposed B are C-element rows)
   if (vec)
-    rowdot_launch<false, true, F16>(r, grid, s, P, Q, M, C, r, out, nullptr, rows);
+    rowdot_launch<false, true, F16, QT>(r, grid, s, P, Q, M, C, r, out, nullptr, rows);
   else
     rowdot_launch<false, false, F16>(r, grid, s, P, Q, M, C, r, out, nullptr, rows);
   return hipGetLastError();
@@ -544,8 +581,19 @@ static hipError_t rowdot_any(const uint16_t* P, const uint16_t* Q, int64_t M, in
 
 hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
                          float* out, float* part, bool f16, hipStream_t s) {
-  return f16 ? rowdot_any<true>(P, Q, M, C, r, out, part, s)
-             : rowdot_any<false>(P, Q, M, C, r, out, part, s);
+  return f16 ? rowdot_any<true, false>(P, Q, M, C, r, out, part, s)
+             : rowdot_any<false, false>(P, Q, M, C, r, out, part, s);
+}
+
+bool rowdot_t_supported(const uint16_t* P, const uint16_t* Qs, int64_t M, int64_t C, int r) {
+  return rowdot_uses_split_path(M, r) && r % 8 == 0 && C % 8 == 0 &&
+         (reinterpret_cast<uintptr_t>(P) & 15) == 0 && (reinterpret_cast<uintptr_t>(Qs) & 15) == 0;
+}
+
+hipError_t launch_rowdot_t(const uint16_t* P, const uint16_t* Qs, int64_t M, int64_t C, int r,
+                           float* out, float* part, bool f16, hipStream_t s) {
+  return f16 ? rowdot_any<true, true>(P, Qs, M, C, r, out, part, s)
+             : rowdot_any<false, true>(P, Qs, M, C, r, out, part, s);
 }
 
 hipError_t launch_rowdot_grouped(const RowdotJob* jobs, int njobs, int64_t M, int max_r,

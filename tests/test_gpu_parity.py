@@ -273,7 +273,11 @@ def test_backward_parity(M, N, K, r):
 
 
 @pytest.mark.parametrize("M,N,K,r", [(1000, 300, 640, 48), (513, 257, 320, 20), (600, 96, 4096, 64),
-                                     (4096, 64, 8192, 64), (700, 130, 192, 8)])
+                                     (4096, 64, 8192, 64), (700, 130, 192, 8),
+                                     # B read in place (r % 8 == 0, N % 8 == 0): split and
+                                     # single-pass paths, ragged chunks and rows
+                                     (1100, 2056, 512, 24), (520, 1000, 256, 40), (64, 2056, 320, 24),
+                                     (777, 4104, 256, 8)])
 def test_lora_rank_products_large_m(M, N, K, r):
     """The rank projections T = X A^T and U = dY B and the adapter gradients
     at large M (row tiles of 128 with the contraction split, ragged rows,
