@@ -31,9 +31,14 @@ QL_DEV u32x4_t load8_guard(const uint16_t* row, int64_t c, int64_t C, bool vec) 
 // given transposed, as Qs [C x r] row-major (the adapter factor B of the
 // backward, U = dY B): the VEC path gathers each fragment with 2-byte loads
 // (kept for completeness; the launcher takes QT to the split kernel only,
-// where the gathers are cheaper than a transposed copy).
+// where the gathers are cheaper than a transposed copy).  PAIR (rows == 8,
+// r <= 8, one rank tile): the idle upper halves of the 16 x 16 MFMA tile carry
+// a second contraction slice -- lanes 8-15 of each operand load rows / ranks
+// 0-7 of the next slice, the two diagonal 8 x 8 blocks of D are both valid
+// (the off-diagonal ones are cross terms and ignored) and are added at the
+// end -- so every load and MFMA does useful work on all 16 lanes.
 constexpr int RD_WAVES = 8;
-template <int RT, bool GROUPED, bool VEC, bool F16, bool QT = false>
+template <int RT, bool GROUPED, bool VEC, bool F16, bool QT = false, bool PAIR = false>
 __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
                                                 const uint16_t* __restrict__ Q, int64_t M,
                                                 int64_t C, int r, float* __restrict__ out,
@@ -60,17 +65,21 @@ __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
     const int nr = (int)min((int64_t)rows, M - m0);
     const auto prs = buf_rsrc(P + m0 * C, rsrc_bytes((int64_t)nr * C * 2));
     const auto qrs = buf_rsrc(Q, rsrc_bytes((int64_t)r * C * 2));
-    const uint32_t pbase = li < nr ? (uint32_t)(li * C * 2) : kOut;
+    const int lrow = PAIR ? (li & 7) : li;                // row / rank of this lane's operands
+    const uint32_t pbase = lrow < nr ? (uint32_t)(lrow * C * 2) : kOut;
     uint32_t qbase[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const int j = 16 * t + li;
+      const int j = 16 * t + lrow;
       qbase[t] = j < r ? (uint32_t)(QT ? j * 2 : j * C * 2) : kOut;
     }
+    // PAIR: slices u and u + 1 of a round share an MFMA (lanes 8-15 the second)
+    constexpr int SU = PAIR ? 2 : 1;
+    const int64_t half = PAIR ? (li >> 3) * stride : 0;
     auto ld_round = [&](int64_t c0, u32x4_t (&a)[U], u32x4_t (&b)[U][RT]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t c = c0 + u * stride + 8 * g;
+        const int64_t c = c0 + u * SU * stride + half + 8 * g;
         const bool cok = c < C;
         const uint32_t co = (uint32_t)(c * 2);
         a[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs, cok ? pbase + co : kOut, 0, 0));
@@ -99,11 +108,12 @@ __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
     };
     u32x4_t a0[U], b0[U][RT], a1[U], b1[U][RT];
     int64_t c0 = wave * 32;
+    constexpr int64_t RS = U * SU * stride;               // elements per round
     ld_round(c0, a0, b0);
-    for (; c0 < C; c0 += 2 * U * stride) {
-      ld_round(c0 + U * stride, a1, b1);
+    for (; c0 < C; c0 += 2 * RS) {
+      ld_round(c0 + RS, a1, b1);
       mma_round(a0, b0);
-      ld_round(c0 + 2 * U * stride, a0, b0);
+      ld_round(c0 + 2 * RS, a0, b0);
       mma_round(a1, b1);
     }
   } else {
@@ -137,13 +147,19 @@ __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
   for (int w = 0; w < RD_WAVES - 1; ++w)
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[t] += s_red[w][t][lane];
+  if constexpr (PAIR) {
+    // D[m][j] for m, j < 8 (lanes g < 2, li < 8) plus the second slice's
+    // block D[m + 8][j + 8] (lane + 40)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[0][e] += __shfl(acc[0][e], (lane + 40) & 63);
+  }
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int j = 16 * t + li;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t mm = m0 + g * 4 + e;
-      if (g * 4 + e < rows && mm < M && j < r) out[mm * r + j] = acc[t][e];
+      if (g * 4 + e < rows && mm < M && j < r && (!PAIR || li < 8)) out[mm * r + j] = acc[t][e];
     }
   }
 }
@@ -534,6 +550,13 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ 
 template <bool GROUPED, bool VEC, bool F16, bool QT = false>
 static void rowdot_launch(int max_r, dim3 grid, hipStream_t s, const uint16_t* P, const uint16_t* Q,
                           int64_t M, int64_t C, int r, float* out, const RowdotJob* jobs, int rows) {
+  if constexpr (VEC && !GROUPED) {
+    if (rows == 8 && max_r <= 8) {
+      hipLaunchKernelGGL((k_rowdot<1, false, true, F16, QT, true>), grid, dim3(64 * RD_WAVES), 0, s, P,
+                         Q, M, C, r, out, jobs, rows);
+      return;
+    }
+  }
 #define QL_RD(RT) \
   hipLaunchKernelGGL((k_rowdot<RT, GROUPED, VEC, F16, QT>), grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out, jobs, rows)
   if (max_r <= 16) QL_RD(1);
