@@ -275,7 +275,7 @@ def run_layer7b(args):
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens or M_TOKENS)
     return out
 
 
@@ -683,7 +683,7 @@ def run_layer38(args):
                      "other_gemm": {"k_gemm_fwd": round(tf_f, 1), "k_gemm_dx": round(tf_d, 1)}},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_layer38(fmt, args.cpu_sample_tokens // 6)
+        out["cpu_baseline"] = cpu_baseline_layer38(fmt, args.cpu_sample_tokens or 128)
     return out
 
 
@@ -696,7 +696,9 @@ def main():
     ap.add_argument("--single-level", action="store_true",
                     help="weights without double quantization (fp32 absmax per block); "
                          "no CPU baseline (the oracle baselines time the double-quantized format)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=768)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None,
+                    help="tokens of the oracle's CPU baseline (default: all 2048 of layer7b, "
+                         "128 of the 4096 of layer3.8b)")
     ap.add_argument("--workload", default="layer7b",
                     choices=["layer7b", "decode", "quantize70b", "layer70b", "layer3.8b"])
     ap.add_argument("--format", default="q8_0", choices=["q8_0", "u4_asym", "nf4"],
