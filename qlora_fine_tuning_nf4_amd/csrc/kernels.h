@@ -115,7 +115,8 @@ hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_
 // The same product with Q given transposed, Qs [C x r] row-major (Q[j][c] =
 // Qs[c][j]), on the split path (rowdot_t_supported: rowdot_uses_split_path,
 // r % 8 == 0, C % 8 == 0, P and Qs 16-byte aligned): each staged chunk of Qs
-// is transposed on its way into LDS, so no transposed copy is made.
+// is transposed on its way into LDS, so no transposed copy is made.  `part`
+// must be given when rowdot_splits(M, C, r) > 1.
 bool rowdot_t_supported(const uint16_t* P, const uint16_t* Qs, int64_t M, int64_t C, int r);
 hipError_t launch_rowdot_t(const uint16_t* P, const uint16_t* Qs, int64_t M, int64_t C, int r,
                            float* out, float* part, bool f16, hipStream_t s);

@@ -27,18 +27,14 @@ QL_DEV u32x4_t load8_guard(const uint16_t* row, int64_t c, int64_t C, bool vec) 
 // past the contraction) point past the buffer and read zeros, so there are
 // no branches, and two register sets alternate: the next U slices load while
 // the current ones are multiplied.  The 8 partial tiles are summed in a
-// fixed order through LDS.  16-bit products are exact, sums fp32.  QT: Q is
-// given transposed, as Qs [C x r] row-major (the adapter factor B of the
-// backward, U = dY B): the VEC path gathers each fragment with 2-byte loads
-// (kept for completeness; the launcher takes QT to the split kernel only,
-// where the gathers are cheaper than a transposed copy).  PAIR (rows == 8,
+// fixed order through LDS.  16-bit products are exact, sums fp32.  PAIR (rows == 8,
 // r <= 8, one rank tile): the idle upper halves of the 16 x 16 MFMA tile carry
 // a second contraction slice -- lanes 8-15 of each operand load rows / ranks
 // 0-7 of the next slice, the two diagonal 8 x 8 blocks of D are both valid
 // (the off-diagonal ones are cross terms and ignored) and are added at the
 // end -- so every load and MFMA does useful work on all 16 lanes.
 constexpr int RD_WAVES = 8;
-template <int RT, bool GROUPED, bool VEC, bool F16, bool QT = false, bool PAIR = false>
+template <int RT, bool GROUPED, bool VEC, bool F16, bool PAIR = false>
 __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
                                                 const uint16_t* __restrict__ Q, int64_t M,
                                                 int64_t C, int r, float* __restrict__ out,
@@ -71,7 +67,7 @@ __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int j = 16 * t + lrow;
-      qbase[t] = j < r ? (uint32_t)(QT ? j * 2 : j * C * 2) : kOut;
+      qbase[t] = j < r ? (uint32_t)(j * C * 2) : kOut;
     }
     // PAIR: slices u and u + 1 of a round share an MFMA (lanes 8-15 the second)
     constexpr int SU = PAIR ? 2 : 1;
@@ -84,20 +80,8 @@ __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
         const uint32_t co = (uint32_t)(c * 2);
         a[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(prs, cok ? pbase + co : kOut, 0, 0));
 #pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          if constexpr (QT) {
-            // Q[j][c + e] = Qs[c + e][j]: eight 2-byte loads, rows past C
-            // (and ranks past r) read zeros
-            uint32_t h[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              h[e] = __builtin_amdgcn_raw_buffer_load_b16(
-                  qrs, c + e < C && qbase[t] != kOut ? qbase[t] + (uint32_t)((c + e) * r * 2) : kOut, 0, 0);
-            b[u][t] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
-          } else {
-            b[u][t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(qrs, cok ? qbase[t] + co : kOut, 0, 0));
-          }
-        }
+        for (int t = 0; t < RT; ++t)
+          b[u][t] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(qrs, cok ? qbase[t] + co : kOut, 0, 0));
       }
     };
     auto mma_round = [&](const u32x4_t (&a)[U], const u32x4_t (&b)[U][RT]) {
@@ -547,18 +531,18 @@ __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ 
     out[idx] = scaling * v;
 }
 
-template <bool GROUPED, bool VEC, bool F16, bool QT = false>
+template <bool GROUPED, bool VEC, bool F16>
 static void rowdot_launch(int max_r, dim3 grid, hipStream_t s, const uint16_t* P, const uint16_t* Q,
                           int64_t M, int64_t C, int r, float* out, const RowdotJob* jobs, int rows) {
   if constexpr (VEC && !GROUPED) {
     if (rows == 8 && max_r <= 8) {
-      hipLaunchKernelGGL((k_rowdot<1, false, true, F16, QT, true>), grid, dim3(64 * RD_WAVES), 0, s, P,
-                         Q, M, C, r, out, jobs, rows);
+      hipLaunchKernelGGL((k_rowdot<1, false, true, F16, true>), grid, dim3(64 * RD_WAVES), 0, s, P, Q,
+                         M, C, r, out, jobs, rows);
       return;
     }
   }
 #define QL_RD(RT) \
-  hipLaunchKernelGGL((k_rowdot<RT, GROUPED, VEC, F16, QT>), grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out, jobs, rows)
+  hipLaunchKernelGGL((k_rowdot<RT, GROUPED, VEC, F16>), grid, dim3(64 * RD_WAVES), 0, s, P, Q, M, C, r, out, jobs, rows)
   if (max_r <= 16) QL_RD(1);
   else if (max_r <= 32) QL_RD(2);
   else if (max_r <= 64) QL_RD(4);
@@ -571,9 +555,11 @@ static hipError_t rowdot_any(const uint16_t* P, const uint16_t* Q, int64_t M, in
                              float* out, float* part, hipStream_t s) {
   const bool vec = C % 8 == 0 && (reinterpret_cast<uintptr_t>(P) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(Q) & 15) == 0;
-  if (QT && (!vec || r % 8 != 0)) return hipErrorInvalidValue;   // rowdot_t_supported is false
   const int ns = rowdot_splits(M, C, r);
-  if (vec && rowdot_uses_split_path(M, r) && (ns == 1 || part)) {
+  const bool split = vec && rowdot_uses_split_path(M, r) && (ns == 1 || part);
+  // transposed Q only on the split path (rowdot_t_supported, partials given)
+  if (QT && (!split || r % 8 != 0)) return hipErrorInvalidValue;
+  if (split) {
     const int64_t tiles = (M + RS_ROWS - 1) / RS_ROWS;
     const int ch = r <= 32 ? RsGeo<2>::CH : RsGeo<4>::CH;
     const int64_t chunks = (C + ch - 1) / ch;
@@ -596,7 +582,7 @@ static hipError_t rowdot_any(const uint16_t* P, const uint16_t* Q, int64_t M, in
   // 16-byte rows: both operands start 16-byte aligned (checked by the caller
   // for X and dY; A and the transposed B are C-element rows)
   if (vec)
-    rowdot_launch<false, true, F16, QT>(r, grid, s, P, Q, M, C, r, out, nullptr, rows);
+    rowdot_launch<false, true, F16>(r, grid, s, P, Q, M, C, r, out, nullptr, rows);
   else
     rowdot_launch<false, false, F16>(r, grid, s, P, Q, M, C, r, out, nullptr, rows);
   return hipGetLastError();
