@@ -250,7 +250,10 @@ def test_forward_bf16_output_within_one_ulp():
 
 
 BWD_CASES = [(1, 64, 64, 2), (16, 4096, 4096, 8), (5, 100, 192, 4), (130, 300, 512, 16), (300, 200, 256, 8),
-             (257, 513, 640, 64), (512, 1024, 1024, 8), (33, 11008, 256, 8)]
+             (257, 513, 640, 64), (512, 1024, 1024, 8), (33, 11008, 256, 8),
+             # adapter gradients over many column tiles: ragged and unaligned columns,
+             # r % 4 != 0, an odd row count split over workgroups
+             (300, 4100, 4160, 6), (2049, 4096, 4096, 16)]
 
 
 @pytest.mark.parametrize("M,N,K,r", BWD_CASES)
