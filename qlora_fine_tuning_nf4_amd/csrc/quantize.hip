@@ -40,10 +40,12 @@ QL_DEV void build_encode_table(const float* mid, float2* tab, int tid, int nthre
 // 8 weights (one 16-byte piece of a block) -> one packed word, given the
 // block absmax am.  The quotient v = fp32(w / am) is formed as
 // q0 = fp32(w * r), e = w - q0 * am (exact, fma), v = fp32(q0 + e * r) with r
-// ~ 1/am: for bf16 w and am (8-bit significands) the exact quotient is a short
-// dyadic or at least 2^-33 (relative) away from every binary32 rounding
-// boundary, while q0 + e * r is within ~2^-46 of it, so v equals the
-// correctly rounded binary32 division bit for bit.  Absmax values below 2^-100
+// ~ 1/am: for bf16 w and am (8-bit significands) the exact quotient p/q is a
+// short dyadic or at least 2^-33 (relative) away from every binary32 rounding
+// boundary (a boundary is an odd multiple of 2^-25 at that scale, so the gap
+// is at least 1/(q 2^25)); for fp16 (11-bit significands) at least 2^-36;
+// while q0 + e * r is within ~2^-46 of it, so v equals the correctly rounded
+// binary32 division bit for bit.  Absmax values below 2^-100
 // are scaled by 2^100 first (exact) so 1/am stays finite.
 QL_DEV uint32_t encode8(const float (&xin)[8], float am, const float2* tab) {
   const bool tiny = am < 0x1p-100f;

@@ -271,3 +271,37 @@ def test_same_bytes_as_bf16_on_common_values():
     torch.cuda.synchronize()
     assert torch.equal(qb.codes, qh.codes) and torch.equal(qb.qscale, qh.qscale)
     assert torch.equal(qb.step.view(torch.int32), qh.step.view(torch.int32))
+
+
+def test_quantize_quotients_near_decision_midpoints():
+    """fp16 blocks whose elements sit a few fp16 ulps around absmax * midpoint
+    for every midpoint, over absmax values across the fp16 exponent range
+    (subnormal elements included): the kernel's quotient (reciprocal and one
+    fma correction, argued exact for 11-bit significands) must round exactly as
+    binary32 division does, so the codes match the oracle bit for bit."""
+    B = _dev()
+    g = np.random.default_rng(2025)
+    nblk = 32768
+    exps = g.integers(1, 31, nblk)                  # every normal fp16 binade
+    mants = g.integers(0, 1024, nblk)
+    a_bits = ((exps << 10) | mants).astype(np.uint16)
+    a = onf4.f16_to_f32(a_bits).astype(np.float64)
+    blocks = np.empty((nblk, 64), dtype=np.uint16)
+    blocks[:, 0] = a_bits
+    for j in range(1, 64):
+        k = (j - 1) % 15
+        off = (j - 1) // 15 - 2                      # -2 .. 2 fp16 ulps around the target
+        tgt = onf4.f32_to_f16_rne((a * MID.astype(np.float64)[k]).astype(np.float32))
+        sgn = tgt & 0x8000
+        mag = np.clip((tgt & 0x7FFF).astype(np.int32) + off, 0, 0x7BFF)
+        blocks[:, j] = (sgn | mag).astype(np.uint16)
+    xf = np.abs(onf4.f16_to_f32(blocks).astype(np.float64))
+    over = xf > a[:, None]
+    blocks[over] = (blocks[over] & 0x8000) | np.repeat(a_bits[:, None], 64, axis=1)[over]
+    w = blocks.reshape(2048, 1024)
+    q = B.qlora_quantize(_t(w), B.device_codebook())
+    torch.cuda.synchronize()
+    c, qs, st, _ = _oracle(w)
+    cs, qss = onf4.to_storage(c, qs, 2048, 1024)
+    assert np.array_equal(q.codes.cpu().numpy(), cs)
+    assert np.array_equal(q.qscale.cpu().numpy(), qss)
