@@ -186,11 +186,20 @@ QL_DEV Lut make_lut_quad(const float* lvq, float s) {
 // looked up twice (entries 0-7 and 8-15, selected by the low three code
 // bits), then a third v_perm picks, per byte, the lookup that matches code
 // bit 3 (selector j or j+4).
+// d = (a & m) | c in one v_and_or_b32: a VOP3 instruction takes no literal
+// operand on this target and reads at most one scalar register, so the mask
+// comes in a scalar register and the constant in a vector register.
+QL_DEV uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(c));
+  return d;
+}
+
 QL_DEV u32x4_t decode8(const Lut& t, uint32_t x) {
   const uint32_t sa = x & 0x07070707u;                            // codes 0..3, low bits
   const uint32_t sb = (x >> 4) & 0x07070707u;                     // codes 4..7
-  const uint32_t ka = ((x >> 1) & 0x04040404u) | 0x03020100u;     // bit 3 of codes 0..3
-  const uint32_t kb = ((x >> 5) & 0x04040404u) | 0x03020100u;     // bit 3 of codes 4..7
+  const uint32_t ka = and_or(x >> 1, 0x04040404u, 0x03020100u);   // bit 3 of codes 0..3
+  const uint32_t kb = and_or(x >> 5, 0x04040404u, 0x03020100u);   // bit 3 of codes 4..7
   const uint32_t loa = perm(perm(t.lo[3], t.lo[2], sa), perm(t.lo[1], t.lo[0], sa), ka);
   const uint32_t hia = perm(perm(t.hi[3], t.hi[2], sa), perm(t.hi[1], t.hi[0], sa), ka);
   const uint32_t lob = perm(perm(t.lo[3], t.lo[2], sb), perm(t.lo[1], t.lo[0], sb), kb);
