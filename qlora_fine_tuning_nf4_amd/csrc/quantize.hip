@@ -120,7 +120,9 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int lb = min(it * BPI + lb0, nb - 1);
-      r[it] = *reinterpret_cast<const u32x4_t*>(W + ((int64_t)blk0 + lb) * BS + lw * 8);
+      // the weight is read exactly once: non-temporal loads keep it from
+      // displacing the code and scale lines that the L2 merges for writing
+      r[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(W + ((int64_t)blk0 + lb) * BS + lw * 8));
     }
   };
   // storage entry of the scale of block (row, kb)
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(256) void k_quant_u4(const uint16_t* __restrict__ W
   const int lane8 = threadIdx.x & 7;
   const uint32_t u = blockIdx.x * 32u + (threadIdx.x >> 3);
   if (u >= nunits) return;   // whole lane groups leave together
-  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + (int64_t)u * kBlock + lane8 * 8);
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(W + (int64_t)u * kBlock + lane8 * 8));
   float x[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(256) void k_quant_q8(const uint16_t* __restrict__ W
   const int lane8 = threadIdx.x & 7;
   const uint32_t u = blockIdx.x * 32u + (threadIdx.x >> 3);
   if (u >= nunits) return;
-  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + (int64_t)u * kBlock + lane8 * 8);
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(W + (int64_t)u * kBlock + lane8 * 8));
   float x[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
