@@ -648,9 +648,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
           if (ksplit > 1)
             part[((int64_t)split * M + m) * O + o] = v;
           else if (out16)
-            reinterpret_cast<uint16_t*>(out)[m * O + o] = to16<FI::f16>(v);
+            // written once: non-temporal stores leave the L2 to the operand
+            // tiles that the other workgroups reuse
+            __builtin_nontemporal_store(to16<FI::f16>(v), reinterpret_cast<uint16_t*>(out) + m * O + o);
           else
-            reinterpret_cast<float*>(out)[m * O + o] = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<float*>(out) + m * O + o);
         }
       }
 }
