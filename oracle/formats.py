@@ -15,8 +15,13 @@ block, 1 bit per weight on top of the 4-bit codes).
    represented exactly (kwkr §2.1 gives exact zero as the point of the
    zero-point; rkmt §2.1 leaves a block of one sign open).
 2. ``scale = fp32(fp32(hi - lo) / 15)`` [rkmt §2.1: (max - min) / 15].
-3. ``zp = clamp(rint_even(fp32(-lo / scale)), 0, 15)`` [rkmt §2.1:
-   round(-min / scale)], stored as an fp32 integer value.
+3. ``zp = clamp(rint_even(-lo * 15 / (hi - lo)), 0, 15)`` [rkmt §2.1:
+   round(-min / scale)], evaluated in float64 from the range, stored as an
+   fp32 integer value.  Reading: -min / scale taken with the real scale
+   (hi - lo) / 15, the same reading as the affine unit (``affine.params``),
+   which is the one that reproduces kwkr §2.1's printed zero-point 128 for
+   [-2, 2]; the quotient by the fp32-rounded scale would give 127 there, and
+   7 instead of 8 for a [-2, 2] uint4 block.
 4. ``q = clamp(rint_even(fp32(x / scale)) + zp, 0, 15)`` [kwkr §2.1 forward
    formula; the clamp is the reading of the affine unit: the pages are silent].
    A block with scale 0 (all zero) gets zp = 0 and q = 0.
@@ -79,8 +84,12 @@ def u4_quantize(w_bits: np.ndarray):
     scale = np.divide((hi - lo).astype(np.float32), np.float32(15.0), dtype=np.float32)
     live = scale > 0
     safe = np.where(live, scale, np.float32(1)).astype(np.float32)
-    # step 3: zero-point, an integer value in [0, 15] (0 for an all-zero block)
-    z = np.rint(np.divide(-lo, safe, dtype=np.float32))
+    # step 3: zero-point, an integer value in [0, 15] (0 for an all-zero
+    # block): float64 from the range (15 * lo is exact, the subtraction and
+    # the division round once each)
+    lo64, hi64 = lo.astype(np.float64), hi.astype(np.float64)
+    span = np.where(live, hi64 - lo64, 1.0)
+    z = np.rint((-lo64 * 15.0) / span)
     zp = np.where(live, np.clip(z, 0, 15), 0).astype(np.int64)
     # step 4: codes
     qv = np.rint(np.divide(x, safe[:, None], dtype=np.float32)).astype(np.int64) + zp[:, None]

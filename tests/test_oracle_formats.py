@@ -23,17 +23,19 @@ def u4_codes(codes):
 def test_u4_hand_values_symmetric_range():
     # a block spanning [-2, 2] (rkmt §2.1 with the INT8 example's range of
     # kwkr §2.1): scale = fp32(4 / 15) = 0x3E888889 = 0.26666668057, a little
-    # above 4/15, so -lo / scale = 7.4999996 (7.5 (1 - 5.2e-8)); the binary32
-    # neighbours are 7.5 and 7.49999952, the quotient rounds to the latter and
-    # the zero-point is 7
+    # above 4/15.  The zero-point comes from the range: -lo * 15 / (hi - lo) =
+    # 7.5 exactly, rint_even -> 8 (the reading that gives kwkr §2.1's printed
+    # 128 for the INT8 case).  The alternative reading, the binary32 quotient
+    # -lo / fp32(scale) = 7.49999952, would round to 7.
     x = np.zeros(64, np.float32)
     x[0], x[1], x[2], x[3] = -2.0, 2.0, 0.0, 1.0
     codes, s, z = F.u4_quantize(bf(x))
     assert s[0] == np.float32(0.2666666805744171) and s.view(np.uint32)[0] == 0x3E888889
-    assert z[0] == 7.0
+    assert z[0] == 8.0
+    assert np.rint(np.divide(np.float32(2.0), s[0], dtype=np.float32)) == 7.0   # the other reading
     q = u4_codes(codes)
-    # -2: rint(-7.4999995) = -7 -> 0;  2: 7 -> 14;  0 -> zp;  1: rint(3.7499998) = 4 -> 11
-    assert list(q[:4]) == [0, 14, 7, 11]
+    # -2: rint(-7.4999995) = -7 -> 1;  2: 7 -> 15;  0 -> zp;  1: rint(3.7499998) = 4 -> 12
+    assert list(q[:4]) == [1, 15, 8, 12]
     w = f(F.u4_dequantize(codes, s, z))
     # bf16 of -7 s = -1.8666667 is -1.8671875; of 4 s = 1.0666667 is 1.0703125;
     # zero is exact.  Both ends sit half a grid step inside the range.
