@@ -45,11 +45,18 @@ QL_DEV void build_encode_table(const float* mid, float2* tab, int tid, int nthre
 // boundary (a boundary is an odd multiple of 2^-25 at that scale, so the gap
 // is at least 1/(q 2^25)); for fp16 (11-bit significands) at least 2^-36;
 // while q0 + e * r is within ~2^-46 of it, so v equals the correctly rounded
-// binary32 division bit for bit.  Absmax values below 2^-100
-// are scaled by 2^100 first (exact) so 1/am stays finite.
+// binary32 division bit for bit.  The argument needs r and q0 to be normal
+// numbers, so the block is first scaled by a power of two (which changes no
+// quotient): absmax below 2^-100 by 2^100, so that 1/am stays finite, and
+// absmax at or above 2^64 by 2^-64, so that 1/am is not a subnormal (which
+// the reciprocal would lose or flush to zero for am >= 2^126).  Scaling down
+// is exact for every element whose quotient is at least 2^-100 or so; smaller
+// elements may round or flush, but any quotient below the first midpoints
+// around zero (|v| < 0.03) encodes as the zero level either way.
 QL_DEV uint32_t encode8(const float (&xin)[8], float am, const float2* tab) {
   const bool tiny = am < 0x1p-100f;
-  const float sc = tiny ? 0x1p100f : 1.0f;
+  const bool huge = am >= 0x1p64f;
+  const float sc = tiny ? 0x1p100f : (huge ? 0x1p-64f : 1.0f);
   const float a = am * sc;
   const float r = am > 0.f ? __builtin_amdgcn_rcpf(a) : 0.f;
   uint32_t word = 0;
@@ -213,7 +220,10 @@ __global__ __launch_bounds__(256) void k_quant_nf4_dq(const uint16_t* __restrict
 // §2.1): per 64-block, the range widened to hold 0, scale = (hi - lo) / 15,
 // zero-point = rint(-lo / scale) in [0, 15] (an fp32 integer value, never
 // -0), q = clamp(rint(x / scale) + zp, 0, 15); an all-zero block gets scale
-// 0, zp 0 and codes 0.  Every division is the correctly rounded binary32 one.
+// 0, zp 0 and codes 0.  The zero-point is taken from the range with the real
+// scale, -lo * 15 / (hi - lo) in binary64 (the reading under which kwkr §2.1's
+// INT8 example gives its printed zero-point 128); the other divisions are the
+// correctly rounded binary32 ones.
 // Eight lanes per 64-weight unit (16-byte loads, eight weights each), one
 // unit per lane group; codes packed as the NF4 codes, (scale, zp) at the
 // unit's storage position.
@@ -245,7 +255,9 @@ __global__ __launch_bounds__(256) void k_quant_u4(const uint16_t* __restrict__ W
   }
   const float sc = (hi - lo) / 15.0f;
   const bool live = sc > 0.f;
-  const int zp = live ? (int)fminf(fmaxf(rintf(-lo / sc), 0.f), 15.f) : 0;
+  // binary64: 15 * lo is exact, the subtraction and the division round once
+  const double zd = rint((-(double)lo * 15.0) / ((double)hi - (double)lo));
+  const int zp = live ? (int)fmin(fmax(zd, 0.0), 15.0) : 0;
   uint32_t word = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {

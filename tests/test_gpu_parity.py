@@ -679,3 +679,76 @@ def test_quantize_quotients_near_decision_midpoints():
     c, qs = onf4.to_storage(c, qs, 2048, 1024)
     assert np.array_equal(q.codes.cpu().numpy(), c)
     assert np.array_equal(q.qscale.cpu().numpy(), qs)
+
+
+# absmax classes of test_quantize_extreme_block_scales: (name, lowest and
+# highest bf16 bit pattern of the block absmax).  Subnormal (the smallest bf16
+# magnitude 2^-133 up to the largest subnormal), around the kernel's small-scale
+# rescale (2^-101 .. 2^-99), around its large-scale rescale (2^63 .. 2^65) and
+# the top of the range (2^125 up to the largest finite bf16, below 2^128).
+_EXTREME = [
+    ("subnormal_min", 0x0001, 0x0001), ("subnormal", 0x0002, 0x007F), ("min_normal", 0x0080, 0x00FF),
+    ("2^-101", 0x0D00, 0x0D7F), ("2^-100", 0x0D80, 0x0DFF), ("2^-99", 0x0E00, 0x0E7F),
+    ("2^63", 0x5F00, 0x5F7F), ("2^64", 0x5F80, 0x5FFF), ("2^125", 0x7E00, 0x7E7F),
+    ("2^126", 0x7E80, 0x7EFF), ("2^127", 0x7F00, 0x7F7E), ("max_finite", 0x7F7F, 0x7F7F),
+]
+
+
+def _extreme_weight(seed):
+    """16 rows x 1024 (one second-level group of 256 blocks) per absmax class:
+    element 0 of each block is +-absmax, the others sit -2 .. +2 bf16 ulps
+    around +-absmax * mid_k for every midpoint k (clipped to |x| <= absmax)."""
+    g = np.random.default_rng(seed)
+    mids = _MID.astype(np.float64)
+    rows = []
+    for _, lo, hi in _EXTREME:
+        nblk = 256
+        a_bits = g.integers(lo, hi + 1, nblk).astype(np.uint16)
+        a = onf4.bf16_to_f32(a_bits).astype(np.float64)
+        blocks = np.empty((nblk, 64), dtype=np.uint16)
+        blocks[:, 0] = a_bits | (g.integers(0, 2, nblk) << 15).astype(np.uint16)
+        for j in range(1, 64):
+            k = (j - 1) % 15
+            off = (j - 1) // 15 - 2
+            tgt = onf4.f32_to_bf16_rne((a * mids[k]).astype(np.float32))
+            mag = np.clip((tgt & 0x7FFF).astype(np.int32) + off, 0, 0x7F7F)
+            sgn = (g.integers(0, 2, nblk) << 15).astype(np.uint16)
+            blocks[:, j] = (sgn | mag).astype(np.uint16)
+        xf = np.abs(onf4.bf16_to_f32(blocks).astype(np.float64))
+        over = xf > a[:, None]
+        blocks[over] = (blocks[over] & 0x8000) | np.repeat(a_bits[:, None], 64, axis=1)[over]
+        rows.append(blocks.reshape(16, 1024))
+    return np.concatenate(rows, axis=0)
+
+
+def test_quantize_extreme_block_scales():
+    """Block absmax values at both ends of the bf16 range (subnormal through
+    the largest finite value), with elements at +-absmax and a few ulps around
+    absmax * midpoint: codes, 8-bit scales and second-level constants
+    bit-exact against the oracle, and the dense dequantization too, for every
+    absmax class (news.rkmt.cn/news/4821 §1.2, §2.1: block-wise absmax
+    scaling)."""
+    B = _dev()
+    w = _extreme_weight(515)
+    n, k = w.shape
+    _say("quantize extreme scales", n, k)
+    q = B.qlora_quantize(_t(w), _cb(B))
+    d = B.qlora_dequantize(q, _cb(B))
+    torch.cuda.synchronize()
+    c, qs, st = _oracle_q(w)
+    cs, qss = onf4.to_storage(c, qs, n, k)
+    gc, gq = onf4.from_storage(q.codes.cpu().numpy(), q.qscale.cpu().numpy(), n, k)
+    gst = q.step.cpu().numpy().view(np.uint32)
+    wd = _oracle_wd(w).reshape(n, k)
+    gd = _bits(d).reshape(n, k)
+    bad = []
+    for i, (name, _, _) in enumerate(_EXTREME):
+        rs = slice(16 * i, 16 * i + 16)
+        ok = (np.array_equal(gc[i * 8192:(i + 1) * 8192], c[i * 8192:(i + 1) * 8192])
+              and np.array_equal(gq[i * 256:(i + 1) * 256], qs[i * 256:(i + 1) * 256])
+              and gst[i] == st[i].view(np.uint32) and np.array_equal(gd[rs], wd[rs]))
+        if not ok:
+            bad.append(name)
+    assert not bad, f"absmax classes that differ from the oracle: {bad}"
+    assert np.array_equal(q.codes.cpu().numpy(), cs)
+    assert np.array_equal(q.qscale.cpu().numpy(), qss)
