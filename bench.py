@@ -127,40 +127,79 @@ def traffic_from_profile(kernel, src_files):
     return d.get("bytes_per_launch")
 
 
+def host_cpu():
+    """The host the CPU baseline runs on: logical CPUs, the CPUs this process
+    may run on, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
+def blas_threads():
+    from threadpoolctl import threadpool_info
+    return max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+
+
+def with_cpu_figures(run_sample, unit, scale, full_sample, single_sample):
+    """Time the oracle as it stands on `full_sample` with every BLAS thread,
+    then on the smaller `single_sample` with one thread; run_sample(sample)
+    returns (work, seconds, description).  value = work / seconds / scale."""
+    from threadpoolctl import threadpool_limits
+
+    work, el, desc = run_sample(full_sample)
+    out = {"value": round(work / el / scale, 4), "unit": unit, "cores": blas_threads(),
+           "kind": "oracle", "sample": f"{desc} ({el:.1f} s, all BLAS threads)", **host_cpu()}
+    with threadpool_limits(limits=1):
+        w1, e1, d1 = run_sample(single_sample)
+    out["single_thread"] = {"value": round(w1 / e1 / scale, 4), "unit": unit, "cores": 1,
+                            "sample": f"{d1} ({e1:.1f} s, one thread)"}
+    return out
+
+
 def cpu_baseline(sample_tokens: int):
     """The oracle, as it stands, on a bounded sample of the same workload: all
     seven projections with the first `sample_tokens` tokens: dequantize each
-    weight, forward, backward (float64 numpy)."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
-
+    weight, forward, backward (float64 numpy); again on 1/16 of those tokens
+    with one thread."""
     import synth
     from oracle import linear as olin
     from oracle import nf4 as onf4
 
     lv, mid = onf4.codebook()
-    M = sample_tokens
-    total_flops = 0
-    elapsed = 0.0
+    packed = {}
     for i, (name, N, K, r) in enumerate(PROJ):
         W = synth.normal_bf16((N, K), 0.02, synth.tensor_seed(2, 10 * i))
-        codes, qs, st = onf4.quantize(W, mid)          # storage, not part of the step
-        X = synth.normal_bf16((M, K), 1.0, synth.tensor_seed(2, 10 * i + 1))
-        dY = synth.normal_bf16((M, N), 1.0, synth.tensor_seed(2, 10 * i + 2))
-        A = synth.normal_bf16((r, K), 0.01, synth.tensor_seed(2, 10 * i + 3)) if r else None
-        B = synth.normal_bf16((N, r), 0.01, synth.tensor_seed(2, 10 * i + 4)) if r else None
-        t0 = time.perf_counter()
-        Wd = onf4.dequantize(codes, qs, st, lv).reshape(N, K)
-        olin.forward(Wd, X, A, B, ALPHA / RANK)
-        Wd = onf4.dequantize(codes, qs, st, lv).reshape(N, K)
-        olin.backward(Wd, X, dY, A, B, ALPHA / RANK)
-        elapsed += time.perf_counter() - t0
-        total_flops += flops_fwd(M, N, K, r) + flops_bwd(M, N, K, r)
-    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    return {"value": round(total_flops / elapsed / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"all 7 projections at M={M} of the {M_TOKENS} tokens: dequantize + fwd + bwd "
-                      f"in float64 numpy ({elapsed:.1f} s)"}
+        packed[i] = onf4.quantize(W, mid)          # storage, not part of the step
+
+    def run(M):
+        total_flops, elapsed = 0, 0.0
+        for i, (name, N, K, r) in enumerate(PROJ):
+            codes, qs, st = packed[i]
+            X = synth.normal_bf16((M, K), 1.0, synth.tensor_seed(2, 10 * i + 1))
+            dY = synth.normal_bf16((M, N), 1.0, synth.tensor_seed(2, 10 * i + 2))
+            A = synth.normal_bf16((r, K), 0.01, synth.tensor_seed(2, 10 * i + 3)) if r else None
+            B = synth.normal_bf16((N, r), 0.01, synth.tensor_seed(2, 10 * i + 4)) if r else None
+            t0 = time.perf_counter()
+            Wd = onf4.dequantize(codes, qs, st, lv).reshape(N, K)
+            olin.forward(Wd, X, A, B, ALPHA / RANK)
+            Wd = onf4.dequantize(codes, qs, st, lv).reshape(N, K)
+            olin.backward(Wd, X, dY, A, B, ALPHA / RANK)
+            elapsed += time.perf_counter() - t0
+            total_flops += flops_fwd(M, N, K, r) + flops_bwd(M, N, K, r)
+        return (total_flops, elapsed, f"all 7 projections at M={M} of the {M_TOKENS} tokens: "
+                                      "dequantize + fwd + bwd in float64 numpy")
+    return with_cpu_figures(run, "TFLOP/s", 1e12, sample_tokens, max(1, sample_tokens // 16))
 
 
 def run_layer7b(args):
@@ -397,33 +436,30 @@ def cpu_baseline_decode():
     """The oracle on a bounded sample of the decode sweep: dequantize + forward
     of the seven projections of the first CPU_DECODE_LAYERS layers at M = 1
     (float64 numpy)."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
-
     import synth
     from oracle import linear as olin
     from oracle import nf4 as onf4
 
     lv, mid = onf4.codebook()
-    nbytes, elapsed = 0, 0.0
-    for layer in range(CPU_DECODE_LAYERS):
-        for i, (name, N, K, r) in enumerate(PROJ):
-            idx = 7 * layer + i
-            W = synth.normal_bf16((N, K), 0.02, synth.tensor_seed(3, 100 * layer + 10 * i))
-            codes, qs, st = onf4.quantize(W, mid)
-            X = synth.normal_bf16((1, K), 1.0, synth.tensor_seed(3, 20000 + idx))
-            A = synth.normal_bf16((r, K), 0.01, synth.tensor_seed(3, 40000 + idx)) if r else None
-            B = synth.normal_bf16((N, r), 0.01, synth.tensor_seed(3, 60000 + idx)) if r else None
-            t0 = time.perf_counter()
-            Wd = onf4.dequantize(codes, qs, st, lv).reshape(N, K)
-            olin.forward(Wd, X, A, B, ALPHA / RANK)
-            elapsed += time.perf_counter() - t0
-            nbytes += packed_bytes(N, K) + 2 * K + 2 * N
-    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{CPU_DECODE_LAYERS} of the {DECODE_LAYERS} layers (7 projections each) at "
-                      f"M=1: dequantize + forward in float64 numpy ({elapsed:.1f} s)"}
+
+    def run(layers):
+        nbytes, elapsed = 0, 0.0
+        for layer in range(layers):
+            for i, (name, N, K, r) in enumerate(PROJ):
+                idx = 7 * layer + i
+                W = synth.normal_bf16((N, K), 0.02, synth.tensor_seed(3, 100 * layer + 10 * i))
+                codes, qs, st = onf4.quantize(W, mid)
+                X = synth.normal_bf16((1, K), 1.0, synth.tensor_seed(3, 20000 + idx))
+                A = synth.normal_bf16((r, K), 0.01, synth.tensor_seed(3, 40000 + idx)) if r else None
+                B = synth.normal_bf16((N, r), 0.01, synth.tensor_seed(3, 60000 + idx)) if r else None
+                t0 = time.perf_counter()
+                Wd = onf4.dequantize(codes, qs, st, lv).reshape(N, K)
+                olin.forward(Wd, X, A, B, ALPHA / RANK)
+                elapsed += time.perf_counter() - t0
+                nbytes += packed_bytes(N, K) + 2 * K + 2 * N
+        return (nbytes, elapsed, f"{layers} of the {DECODE_LAYERS} layers (7 projections each) at "
+                                 "M=1: dequantize + forward in float64 numpy")
+    return with_cpu_figures(run, "GB/s", 1e9, CPU_DECODE_LAYERS, 1)
 
 
 def _weights70(dev):
@@ -474,21 +510,18 @@ def run_quantize70b(args):
                      "traffic": _traffic("k_quant_nf4_dq", ["quantize.hip", "common.h"])},
     }
     if not args.no_cpu_baseline:
-        import numpy as np
-        from threadpoolctl import threadpool_info
-
         import synth
         from oracle import nf4 as onf4
         _, mid = onf4.codebook()
-        rows = 16384
-        W = synth.normal_bf16((rows, 8192), 0.015, 77, outlier_rate=0.001, outlier_scale=20)
-        t0 = time.perf_counter()
-        onf4.quantize(W, mid)
-        el = time.perf_counter() - t0
-        threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-        out["cpu_baseline"] = {"value": round((2 * rows * 8192 + packed_bytes(rows, 8192)) / el / 1e9, 4),
-                               "unit": "GB/s", "cores": threads, "kind": "oracle",
-                               "sample": f"{rows} x 8192 rows of the q projection ({el:.1f} s)"}
+
+        def run(rows):
+            W = synth.normal_bf16((rows, 8192), 0.015, 77, outlier_rate=0.001, outlier_scale=20)
+            t0 = time.perf_counter()
+            onf4.quantize(W, mid)
+            el = time.perf_counter() - t0
+            return (2 * rows * 8192 + packed_bytes(rows, 8192), el,
+                    f"{rows} x 8192 rows of the q projection")
+        out["cpu_baseline"] = with_cpu_figures(run, "GB/s", 1e9, 16384, 4096)
     return out
 
 
@@ -566,15 +599,20 @@ def cpu_baseline_layer38(fmt, sample_tokens):
     """The oracle on a bounded sample of the 3.8B-style layer: all seven
     projections at the first `sample_tokens` tokens, dequantize + forward +
     backward in float64 numpy (quantization outside the timed part)."""
-    from threadpoolctl import threadpool_info
-
     import synth
     from oracle import formats as ofmt
     from oracle import linear as olin
     from oracle import nf4 as onf4
 
     lv, mid = onf4.codebook()
-    M, r, s = sample_tokens, 64, 128 / 64
+
+    def run(M):
+        return _layer38_sample(fmt, M, lv, mid, synth, ofmt, olin, onf4)
+    return with_cpu_figures(run, "TFLOP/s", 1e12, sample_tokens, max(1, sample_tokens // 16))
+
+
+def _layer38_sample(fmt, M, lv, mid, synth, ofmt, olin, onf4):
+    r, s = 64, 128 / 64
     total_flops, elapsed = 0, 0.0
     for i, (name, N, K) in enumerate(PROJ38):
         W = synth.normal_bf16((N, K), 0.02, synth.tensor_seed(5, 10 * i))
@@ -596,11 +634,8 @@ def cpu_baseline_layer38(fmt, sample_tokens):
         olin.backward(deq(), X, dY, A, B, s)
         elapsed += time.perf_counter() - t0
         total_flops += flops_fwd(M, N, K, r) + flops_bwd(M, N, K, r)
-    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    return {"value": round(total_flops / elapsed / 1e12, 4), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"all 7 projections at M={M} of the 4096 tokens: dequantize + fwd + bwd "
-                      f"in float64 numpy ({elapsed:.1f} s)"}
+    return (total_flops, elapsed, f"all 7 projections at M={M} of the 4096 tokens: dequantize + "
+                                  "fwd + bwd in float64 numpy")
 
 
 def run_layer38(args):

@@ -23,8 +23,8 @@
  *   - codes, X, Y, dY and dX must be 16-byte aligned; every other device
  *     pointer 4-byte aligned.
  *   - k % 64 == 0; m >= 1 and n >= 1 are arbitrary (ragged tails are masked);
- *     n < 2^22, k < 2^22 and a packed weight holds fewer than 2^38 elements
- *     (n * k / 64 < 2^32 blocks).
+ *     m <= QLORA_MAX_M (2^31 - 1), n < 2^22, k < 2^22 and a packed weight
+ *     holds fewer than 2^38 elements (n * k / 64 < 2^32 blocks).
  *   - r == 0 switches the LoRA branch off: A, B, T_save, T_saved, dA and dB
  *     are then ignored and may be NULL.
  *   - All arguments are validated before any HIP call; on error nothing is
@@ -80,6 +80,7 @@ enum {
 #define QLORA_MAX_RANK 128    /* largest supported LoRA rank */
 #define QLORA_GEMV_MAX_M 32   /* largest m the streaming path accepts */
 #define QLORA_CODEBOOK_LEN 31 /* 16 NF4 levels then 15 decision midpoints */
+#define QLORA_MAX_M 2147483647LL /* largest token count m (2^31 - 1) */
 
 /*
  * Packed NF4 + double-quantized weight (device buffers owned by the caller).
@@ -111,8 +112,10 @@ enum {
  * position p.
  *   QLORA_FMT_U4_ASYM (news.rkmt.cn/news/4821 §1.3, §2.1; kwkr.cn/news/627310
  *     §2.1): per 64-block lo = min(min, 0), hi = max(max, 0),
- *     scale = fp32(fp32(hi - lo) / 15), zp = clamp(rint_even(fp32(-lo / scale)),
- *     0, 15), q = clamp(rint_even(fp32(x / scale)) + zp, 0, 15) (all 0 when
+ *     scale = fp32(fp32(hi - lo) / 15), zp = clamp(rint_even(-lo * 15 / (hi - lo)),
+ *     0, 15) evaluated in binary64 from the range (the reading that reproduces
+ *     kwkr.cn/news/627310 §2.1's printed zero-point), q = clamp(rint_even(fp32(x /
+ *     scale)) + zp, 0, 15) (all 0 when
  *     scale is 0); w = bf16_rne(fp32(scale * (q - zp))).  codes: n*k/2 bytes,
  *     q packed as the NF4 codes; step: 2*n*k/64 floats, step[2p] = scale,
  *     step[2p+1] = zp (an integer value); qscale must be NULL.  8-byte aligned
@@ -211,7 +214,9 @@ int qlora_weight_bytes(int format, int64_t n, int64_t k, size_t *codes, size_t *
 
 /*
  * Host.  Workspace bytes needed by qlora_linear_fwd (op = 0) or
- * qlora_linear_bwd (op = 1) for these sizes, for any path.  0 on bad input.
+ * qlora_linear_bwd (op = 1) for these sizes, for any path.  0 on bad input
+ * (an unknown op, m outside [1, QLORA_MAX_M], a shape qlora_nf4_bytes refuses,
+ * r outside [0, QLORA_MAX_RANK]).
  */
 size_t qlora_workspace_bytes(int op, int64_t m, int64_t n, int64_t k, int r);
 

@@ -167,6 +167,10 @@ bool block_shape_ok(int64_t n, int64_t k, int block) {
   return true;
 }
 
+// Token count: at least one row, fewer than 2^31 (with n, k < 2^22 every
+// activation, output and workspace size stays far inside 64 bits).
+bool m_ok(int64_t m) { return m >= 1 && m <= QLORA_MAX_M; }
+
 // Compute type of a descriptor: fp16 (QLORA_F16) or the bf16 default.
 bool is_f16(const qlora_nf4* W) { return W->dtype == QLORA_F16; }
 
@@ -310,7 +314,7 @@ int qlora_weight_bytes(int format, int64_t n, int64_t k, size_t* codes, size_t* 
 }
 
 size_t qlora_workspace_bytes(int op, int64_t m, int64_t n, int64_t k, int r) {
-  if (m < 1 || n < 1 || k < kB || k % kB || r < 0 || r > QLORA_MAX_RANK) return 0;
+  if (!m_ok(m) || !shape_ok(n, k) || r < 0 || r > QLORA_MAX_RANK) return 0;
   if (op == 0) {
     size_t b = 0;
     for (int path : {QLORA_PATH_AUTO, QLORA_PATH_GEMV, QLORA_PATH_GEMM}) {
@@ -375,7 +379,7 @@ int qlora_linear_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
   if (!X || !Y) return QLORA_ERR_NULL;
   if (int e = check_desc(W)) return e;
   if (int e = check_codebook(W, codebook)) return e;
-  if (m < 1) return QLORA_ERR_SHAPE;
+  if (!m_ok(m)) return QLORA_ERR_SHAPE;
   if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
   if (!out_dtype_ok(W, y_dtype)) return QLORA_ERR_DTYPE;
@@ -421,7 +425,7 @@ int qlora_group_init(qlora_group* g, const qlora_fwd_job* jobs, int count, int64
                      void* table, size_t table_bytes) {
   if (!g || !jobs || !table) return QLORA_ERR_NULL;
   if (count < 1 || m > QLORA_GEMV_MAX_M) return QLORA_ERR_ARG;
-  if (m < 1) return QLORA_ERR_SHAPE;
+  if (!m_ok(m)) return QLORA_ERR_SHAPE;
   if (y_dtype != QLORA_F32 && y_dtype != QLORA_BF16 && y_dtype != QLORA_F16) return QLORA_ERR_DTYPE;
   if (!aligned(table, 16)) return QLORA_ERR_ALIGN;
   if (table_bytes < qlora_group_table_bytes(count)) return QLORA_ERR_WORKSPACE;
@@ -497,7 +501,7 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
   if (!dY) return QLORA_ERR_NULL;
   if (int e = check_desc(W)) return e;
   if (int e = check_codebook(W, codebook)) return e;
-  if (m < 1) return QLORA_ERR_SHAPE;
+  if (!m_ok(m)) return QLORA_ERR_SHAPE;
   if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
   if (r > 0 && (!A || !B || !dA || !dB || !X)) return QLORA_ERR_NULL;
   if (!out_dtype_ok(W, dx_dtype)) return QLORA_ERR_DTYPE;

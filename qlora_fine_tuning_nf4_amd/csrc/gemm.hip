@@ -92,9 +92,6 @@ QL_DEV int64_t logical_tile(int64_t id, int64_t total) {
   return xcd * base + (xcd < rem ? xcd : rem) + slot;
 }
 
-#ifndef QL_A_DMA
-#define QL_A_DMA 1                     // activation tiles by LDS DMA (1) or through registers (0)
-#endif
 constexpr int NA = 3;                 // activation stages in the ring
 constexpr int A_STAGE = GBM * GBK;     // bf16 elements per activation stage (32 KiB)
 
@@ -667,14 +664,12 @@ static hipError_t launch_one(dim3 grid, hipStream_t s, const uint16_t* act, cons
                              const float* codebook, int64_t M, const LoraTerm& lora, void* out,
                              bool out16, float* part, int ksplit, int per, int64_t mtiles,
                              int64_t otiles) {
-  static bool attr_set = false;   // idempotent: the same value every time
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<DX, VEC, FMT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)smem_bytes<DX>());
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // the dynamic LDS limit of this instantiation, set once per process (a
+  // function-local static is initialized exactly once, thread-safely)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_gemm<DX, VEC, FMT>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)smem_bytes<DX>());
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((k_gemm<DX, VEC, FMT>), grid, dim3(512), smem_bytes<DX>(), s, act, w, codebook,
                      M, lora, out, (int)out16, part, ksplit, per, mtiles, otiles);
   return hipGetLastError();

@@ -117,7 +117,10 @@ hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_
 // r % 8 == 0, C % 8 == 0, P and Qs 16-byte aligned): each staged chunk of Qs
 // is transposed on its way into LDS, so no transposed copy is made.  `part`
 // must be given when rowdot_splits(M, C, r) > 1.
-bool rowdot_t_supported(const uint16_t* P, const uint16_t* Qs, int64_t M, int64_t C, int r);
+inline bool rowdot_t_supported(const uint16_t* P, const uint16_t* Qs, int64_t M, int64_t C, int r) {
+  return rowdot_uses_split_path(M, r) && r % 8 == 0 && C % 8 == 0 &&
+         (reinterpret_cast<uintptr_t>(P) & 15) == 0 && (reinterpret_cast<uintptr_t>(Qs) & 15) == 0;
+}
 hipError_t launch_rowdot_t(const uint16_t* P, const uint16_t* Qs, int64_t M, int64_t C, int r,
                            float* out, float* part, bool f16, hipStream_t s);
 // One product of the grouped rowdot: out[m][j] = sum_c P[m][c] Q[j][c].

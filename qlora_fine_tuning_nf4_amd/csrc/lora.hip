@@ -594,11 +594,6 @@ hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_
              : rowdot_any<false, false>(P, Q, M, C, r, out, part, s);
 }
 
-bool rowdot_t_supported(const uint16_t* P, const uint16_t* Qs, int64_t M, int64_t C, int r) {
-  return rowdot_uses_split_path(M, r) && r % 8 == 0 && C % 8 == 0 &&
-         (reinterpret_cast<uintptr_t>(P) & 15) == 0 && (reinterpret_cast<uintptr_t>(Qs) & 15) == 0;
-}
-
 hipError_t launch_rowdot_t(const uint16_t* P, const uint16_t* Qs, int64_t M, int64_t C, int r,
                            float* out, float* part, bool f16, hipStream_t s) {
   return f16 ? rowdot_any<true, true>(P, Qs, M, C, r, out, part, s)
