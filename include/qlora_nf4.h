@@ -31,8 +31,11 @@
  *     enqueued and a positive status is returned.  A failed launch returns
  *     QLORA_ERR_HIP.  Asynchronous faults surface at the caller's next
  *     synchronization.  Non-finite weights are outside the contract (no check).
- *   - The library keeps no state between calls: calls are re-entrant and
- *     thread-safe; two calls that write the same buffers race.
+ *   - The library keeps no state between calls (apart from once-per-process
+ *     kernel attributes and the per-GPU scratch of qlora_linear_fwd_noalloc):
+ *     calls are re-entrant and thread-safe; two calls that write the same
+ *     buffers race, and so do overlapping qlora_linear_fwd_noalloc calls on
+ *     one GPU.
  *   - Results are deterministic: the same inputs give the same bits.
  */
 #ifndef QLORA_NF4_H
@@ -280,6 +283,27 @@ int qlora_linear_fwd(const qlora_nf4 *W, const float *codebook, const uint16_t *
                      const uint16_t *A, const uint16_t *B, int r, float scaling,
                      void *Y, int y_dtype, float *T_save,
                      void *ws, size_t ws_bytes, int path, void *stream);
+
+/*
+ * Allocation-free variant of qlora_linear_fwd, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without `ws` and
+ * `ws_bytes`, the same kernels and results bit for bit.  Its workspace is a
+ * file-scope device array of QLORA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU,
+ * which every GPU the library is loaded on holds until the process ends; it
+ * calls no allocation routine.  Calls whose workspace would exceed that size
+ * (qlora_workspace_bytes(0, ...) counts it; with T_save given and a shape
+ * that needs no split, none is used) return QLORA_ERR_WORKSPACE before any
+ * launch.  Every call on a GPU shares that GPU's array and leaves its contents
+ * behind (nothing in it needs to start at zero): calls that overlap in time on
+ * one GPU (different streams or threads) race on it and must be serialized by
+ * the caller.
+ */
+#define QLORA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int qlora_linear_fwd_noalloc(const qlora_nf4 *W, const float *codebook, const uint16_t *X,
+                             int64_t m, const uint16_t *A, const uint16_t *B, int r,
+                             float scaling, void *Y, int y_dtype, float *T_save, int path,
+                             void *stream);
 
 /*
  * Backward of the same layer (www.cf-1.com/news/5705389 §2.1: dL/dx = dL/dy W0^T

@@ -87,6 +87,9 @@ def lib():
         L.qlora_linear_fwd.restype = i32
         L.qlora_linear_fwd.argtypes = [P(_Nf4Desc), vp, vp, i64, vp, vp, i32, f32, vp, i32, vp,
                                        vp, sz, i32, vp]
+        L.qlora_linear_fwd_noalloc.restype = i32
+        L.qlora_linear_fwd_noalloc.argtypes = [P(_Nf4Desc), vp, vp, i64, vp, vp, i32, f32, vp, i32,
+                                               vp, i32, vp]
         L.qlora_linear_bwd.restype = i32
         L.qlora_linear_bwd.argtypes = [P(_Nf4Desc), vp, vp, vp, i64, vp, vp, i32, f32, vp, vp,
                                        i32, vp, vp, vp, sz, i32, vp]
@@ -294,6 +297,29 @@ def qlora_linear_fwd(w: NF4Weight, codebook: torch.Tensor, X: torch.Tensor, A=No
         _out_enum(Y.dtype, "Y"), _ptr(T), _ptr(ws),
         ws.numel(), PATHS[path], _stream()), "qlora_linear_fwd")
     return Y, T
+
+
+def qlora_linear_fwd_noalloc(w: NF4Weight, codebook: torch.Tensor, X: torch.Tensor, A=None, B=None,
+                             scaling: float = 0.0, y_dtype=torch.float32, path: str = "auto",
+                             out=None, T_out=None):
+    """qlora_linear_fwd without a workspace argument (the library's per-GPU
+    scratch is used).  Pass `out` (and `T_out` when the LoRA branch is on) to
+    allocate nothing here either; missing ones are allocated by torch before
+    the call.  -> (Y, T or None)."""
+    _t16(X, "X", w.dtype)
+    m = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if r:
+        _t16(A, "A", w.dtype)
+        _t16(B, "B", w.dtype)
+    dev = X.device
+    Y = out if out is not None else torch.empty((m, w.n), dtype=y_dtype, device=dev)
+    d = w.desc()
+    _check(lib().qlora_linear_fwd_noalloc(
+        ctypes.byref(d), _ptr(codebook), _ptr(X), m, _ptr(A) if r else None,
+        _ptr(B) if r else None, r, float(scaling), _ptr(Y), _out_enum(Y.dtype, "Y"), _ptr(T_out),
+        PATHS[path], _stream()), "qlora_linear_fwd_noalloc")
+    return Y, T_out
 
 
 def qlora_linear_bwd(w: NF4Weight, codebook: torch.Tensor, X, dY, A=None, B=None,

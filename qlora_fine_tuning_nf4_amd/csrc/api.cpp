@@ -372,10 +372,14 @@ int qlora_merge(const qlora_nf4* W, const float* codebook, const uint16_t* A, co
   return QLORA_OK;
 }
 
-int qlora_linear_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* X, int64_t m,
-                     const uint16_t* A, const uint16_t* B, int r, float scaling, void* Y,
-                     int y_dtype, float* T_save, void* ws, size_t ws_bytes, int path,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the forward (everything but the workspace).
+int check_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* X, int64_t m,
+              const uint16_t* A, const uint16_t* B, int r, void* Y, int y_dtype, float* T_save,
+              int path) {
   if (!X || !Y) return QLORA_ERR_NULL;
   if (int e = check_desc(W)) return e;
   if (int e = check_codebook(W, codebook)) return e;
@@ -388,13 +392,23 @@ int qlora_linear_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
   if (!aligned(X, 16) || !aligned(Y, 16)) return QLORA_ERR_ALIGN;
   if (r > 0 && (!aligned(A, 16) || !aligned(B, 2) || (T_save && !aligned(T_save, 4))))
     return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+// Bytes of workspace this forward uses (0 when it needs none).
+size_t fwd_ws_needed(int64_t m, int64_t n, int64_t k, int r, bool t_saved, int path) {
+  const FwdWs L = fwd_ws(m, n, k, r, path);
+  const bool need_ws = L.total > L.part_off || (r > 0 && !t_saved);
+  return need_ws ? L.total : 0;
+}
+
+// The forward's launches, arguments already checked and the workspace
+// (ws, at least fwd_ws_needed bytes when that is not 0) in hand.
+int run_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* X, int64_t m,
+            const uint16_t* A, const uint16_t* B, int r, float scaling, void* Y, int y_dtype,
+            float* T_save, void* ws, int path, hipStream_t s) {
   const int64_t n = W->n, k = W->k;
   const FwdWs L = fwd_ws(m, n, k, r, path);
-  const bool need_ws = L.total > L.part_off || (r > 0 && !T_save);
-  if (need_ws && (!ws || ws_bytes < L.total)) return QLORA_ERR_WORKSPACE;
-  if (ws && !aligned(ws, 16)) return QLORA_ERR_ALIGN;
-
-  hipStream_t s = (hipStream_t)stream;
   const FwdPlan p = plan_fwd(m, n, k, path);
   char* wsb = (char*)ws;
   float* T = nullptr;
@@ -414,6 +428,35 @@ int qlora_linear_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
   if (p.ksplit > 1 && ql::launch_reduce(part, p.ksplit, m, n, lora, Y, bf, is_f16(W), s) != hipSuccess)
     return QLORA_ERR_HIP;
   return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlora_linear_fwd_noalloc(const qlora_nf4* W, const float* codebook, const uint16_t* X,
+                             int64_t m, const uint16_t* A, const uint16_t* B, int r,
+                             float scaling, void* Y, int y_dtype, float* T_save, int path,
+                             void* stream) {
+  if (int e = check_fwd(W, codebook, X, m, A, B, r, Y, y_dtype, T_save, path)) return e;
+  const size_t need = fwd_ws_needed(m, W->n, W->k, r, T_save != nullptr, path);
+  if (need > ql::kScratchBytes) return QLORA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && ql::device_scratch(&ws) != hipSuccess) return QLORA_ERR_HIP;
+  return run_fwd(W, codebook, X, m, A, B, r, scaling, Y, y_dtype, T_save, ws, path,
+                 (hipStream_t)stream);
+}
+
+int qlora_linear_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* X, int64_t m,
+                     const uint16_t* A, const uint16_t* B, int r, float scaling, void* Y,
+                     int y_dtype, float* T_save, void* ws, size_t ws_bytes, int path,
+                     void* stream) {
+  if (int e = check_fwd(W, codebook, X, m, A, B, r, Y, y_dtype, T_save, path)) return e;
+  const size_t need = fwd_ws_needed(m, W->n, W->k, r, T_save != nullptr, path);
+  if (need > 0 && (!ws || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
+  if (ws && !aligned(ws, 16)) return QLORA_ERR_ALIGN;
+  return run_fwd(W, codebook, X, m, A, B, r, scaling, Y, y_dtype, T_save, ws, path,
+                 (hipStream_t)stream);
 }
 
 size_t qlora_group_table_bytes(int count) {

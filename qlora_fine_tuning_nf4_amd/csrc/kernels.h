@@ -151,4 +151,10 @@ struct WgradJob {
 hipError_t launch_wgrad(const WgradJob& a, const WgradJob& b, int64_t M, int r, float scaling,
                         float* part, int msplit, bool f16, hipStream_t s);
 
+// Scratch of the allocation-free forward: a file-scope device array of
+// kScratchBytes per GPU.  device_scratch() returns its device address on the
+// current device (looked up once per device, thread-safe).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t device_scratch(void** ptr);
+
 }  // namespace ql

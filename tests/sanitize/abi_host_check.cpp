@@ -18,6 +18,10 @@
 #include "../../include/qlora_nf4.h"
 #include "../../qlora_fine_tuning_nf4_amd/csrc/kernels.h"
 
+namespace ql {
+extern void* g_scratch_base;   // the stub scratch (re-registered after each reset)
+}
+
 namespace {
 
 struct Alloc {
@@ -184,6 +188,12 @@ hipError_t launch_wgrad(const WgradJob& a, const WgradJob& b, int64_t M, int r, 
   if (msplit > 1) in_bounds(part, 4.0 * msplit * r * (a.C + b.C), "wgrad partials");
   return hipSuccess;
 }
+void* g_scratch_base = nullptr;
+hipError_t device_scratch(void** ptr) {
+  if (!g_scratch_base) g_scratch_base = fake_alloc(kScratchBytes);
+  *ptr = g_scratch_base;
+  return hipSuccess;
+}
 }  // namespace ql
 
 // hipMemcpy is the one HIP runtime call of the host code (group setup): it
@@ -231,6 +241,14 @@ void run_fwd_bwd(int64_t m, int64_t n, int64_t k, int r, int path, bool save_t, 
     }
     if (e != QLORA_OK) std::fprintf(stderr, "fwd m=%ld n=%ld k=%ld r=%d path=%d -> %d\n", (long)m, (long)n, (long)k, r, path, e);
     CHECK(e == QLORA_OK);
+    // the allocation-free forward: the same launches with the device scratch
+    {
+      ql::g_scratch_base = nullptr;
+      const int before = g_launches;
+      const int en = qlora_linear_fwd_noalloc(&w, cb, X, m, A, B, r, 2.0f, Y, dt, T, path, nullptr);
+      CHECK(wf <= ql::kScratchBytes ? en == QLORA_OK : en == QLORA_ERR_WORKSPACE);
+      CHECK(en == QLORA_OK ? g_launches > before : g_launches == before);
+    }
     const int e2 = qlora_linear_bwd(&w, cb, X, dY, m, A, B, r, 2.0f, T, dX, dt, dA, dB, wsb, wb, path,
                                     nullptr);
     if (e2 != QLORA_OK && !(path == QLORA_PATH_GEMV && e2 == QLORA_ERR_ARG))

@@ -346,3 +346,22 @@ def test_nf4_bytes_rejects_oversized_weights():
     assert L.qlora_nf4_bytes((1 << 22) - 1, 64, ctypes.byref(z), None, None) == 0
     assert L.qlora_nf4_bytes(1, 1 << 22, ctypes.byref(z), None, None) == 2         # k = 2^22
     assert L.qlora_nf4_bytes(1, (1 << 22) - 64, ctypes.byref(z), None, None) == 0
+
+
+def test_noalloc_forward_refuses_oversized_scratch_before_any_launch():
+    """qlora_linear_fwd_noalloc: a workspace need above the per-GPU scratch
+    (here T for 2^20 tokens at rank 128, 512 MiB) is refused with
+    QLORA_ERR_WORKSPACE before any HIP call; argument errors as the workspace
+    forward."""
+    L = B.lib()
+    cb, q = FAKE, FAKE
+    codes, qs, st = B.qlora_nf4_bytes(4096, 4096)
+    d = B._Nf4Desc(4096, 4096, FAKE, FAKE, FAKE, 0, 0, 0)
+    m = 1 << 20
+    st_ = L.qlora_linear_fwd_noalloc(ctypes.byref(d), cb, FAKE, m, FAKE, FAKE, 128, 1.0, FAKE, 0,
+                                     None, 0, None)
+    assert st_ == 6
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(d), cb, None, 4, None, None, 0, 1.0, FAKE, 0,
+                                      None, 0, None) == 1
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(d), cb, FAKE, 64, None, None, 0, 1.0, FAKE, 0,
+                                      None, 1, None) == 8

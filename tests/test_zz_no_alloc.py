@@ -1,0 +1,63 @@
+"""The allocation-free forward (qlora_linear_fwd_noalloc) against the
+workspace forward (qlora_linear_fwd): bit-identical outputs on two calls in
+a row on one GPU, the second with smaller inputs (the device scratch keeps the
+first call's contents), on the streaming path with split partials and the
+GEMM path with and without split partials; T recomputed into the scratch or
+written to the caller's buffer."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from qlora_fine_tuning_nf4_amd import binding
+    binding.lib()
+    return binding
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _t(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _case(B, cb, M, N, K, r, seed, path, save_t, y_dtype):
+    X = _t(synth.normal_bf16((M, K), 1.0, seed))
+    W = _t(synth.normal_bf16((N, K), 0.02, seed + 1))
+    A = _t(synth.normal_bf16((r, K), 0.01, seed + 2)) if r else None
+    Bm = _t(synth.normal_bf16((N, r), 0.01, seed + 3)) if r else None
+    q = B.qlora_quantize(W, cb)
+    Y_ref, T_ref = B.qlora_linear_fwd(q, cb, X, A, Bm, 2.0, y_dtype=y_dtype, save_T=save_t, path=path)
+    Y = torch.full((M, N), float("nan"), dtype=y_dtype, device="cuda")
+    T = torch.full((M, r), float("nan"), dtype=torch.float32, device="cuda") if (r and save_t) else None
+    B.qlora_linear_fwd_noalloc(q, cb, X, A, Bm, 2.0, path=path, out=Y, T_out=T)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16) if y_dtype != torch.float32 else Y.view(torch.int32),
+                       Y_ref.view(torch.int16) if y_dtype != torch.float32 else Y_ref.view(torch.int32))
+    if T is not None:
+        assert torch.equal(T.view(torch.int32), T_ref.view(torch.int32))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("first,second", [
+    # streaming path: split-K partials and T in the scratch, then a smaller call
+    ((16, 4096, 4096, 8, "auto", False, torch.float32), (4, 1000, 2048, 8, "auto", False, torch.bfloat16)),
+    # GEMM path with split partials (few tiles), then a smaller split call
+    ((100, 4096, 4096, 16, "gemm", False, torch.bfloat16), (40, 520, 1024, 8, "gemm", False, torch.float32)),
+    # GEMM path without splits, T to the caller's buffer (no scratch), then a split call
+    ((2048, 4096, 4096, 8, "auto", True, torch.bfloat16), (64, 256, 512, 0, "auto", True, torch.float32)),
+])
+def test_noalloc_forward_matches_workspace_forward(first, second):
+    B = _dev()
+    cb = B.device_codebook()
+    for i, (M, N, K, r, path, save_t, yd) in enumerate((first, second)):
+        _say("noalloc fwd", i, M, N, K, r, path, save_t, yd)
+        _case(B, cb, M, N, K, r, 700 + 10 * i + M, path, save_t, yd)
