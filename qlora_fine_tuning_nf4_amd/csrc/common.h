@@ -216,10 +216,11 @@ QL_DEV u32x4_t decode8(const Lut& t, uint32_t x) {
 // share a scale s (lanes 0, 1 the unit's first 32 weights, lanes 2, 3 the
 // rest); lane q computes entries 8 (q & 1) .. +7 (lv8[i] = level[8 (q & 1) +
 // i]) and the pair exchanges its planes with quad_perm [0,0,2,2] / [1,1,3,3].
+template <bool F16 = false>
 QL_DEV Lut make_lut_pair(const float* lv8, float s) {
   uint32_t d[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) d[i] = pack_bf16x2(lv8[2 * i] * s, lv8[2 * i + 1] * s);
+  for (int i = 0; i < 4; ++i) d[i] = pack16x2<F16>(lv8[2 * i] * s, lv8[2 * i + 1] * s);
   const uint32_t lo0 = perm(d[1], d[0], 0x06040200u), hi0 = perm(d[1], d[0], 0x07050301u);
   const uint32_t lo1 = perm(d[3], d[2], 0x06040200u), hi1 = perm(d[3], d[2], 0x07050301u);
   Lut t;

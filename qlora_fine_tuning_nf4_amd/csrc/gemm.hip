@@ -9,28 +9,33 @@
 // www.lqnn.cn/news/228537 §3.3: dequantize to 16 bits for the product, then
 // discard).
 //
-// gfx950 design:
-//  * 256 x 128 output tile per workgroup, 8 waves in two groups of four (one
-//    wave of each group per SIMD): wave (g, w) accumulates rows 64w .. +63 x
-//    all 128 columns over K-slices 2g, 2g+1 of every step (MFMA 32x32x16,
-//    bf16 or fp16 operands, fp32 accumulators); the partner waves swap halves
-//    at the end, each finishing a 64 x 64 tile.
-//  * The activation operand (X or dY) goes global -> LDS with the gfx950
-//    global_load_lds b128 DMA (no registers, each wave load covers 8 whole
-//    128-byte row pieces) into a 3-stage ring, two K-steps ahead.  16-byte
-//    chunks are XOR-swizzled by row so the MFMA fragment reads are free of
-//    bank conflicts.
-//  * The weight tile of each K-step (128 x 64 weights = 128 storage units) is
-//    decoded by all 512 threads into a double-buffered LDS stage: the four
-//    lanes of a DPP quad share a unit and decode 16 weights each; for the
-//    4-bit formats they build its 16-entry table together (broadcast with
-//    quad_perm), Q8_0 bytes are scaled directly.  Ping-pong: while one
-//    group runs the MFMAs of step s the other reads its fragments and decodes
-//    its half of step s+1, a barrier between phases; the decode is amortized
-//    over 256 output rows.
-//  * Forward reads B fragments with ds_read_b128 from the [n][k] stage; the
-//    backward contracts over n and reads them with the transposing
+// gfx950 design (producer / consumer):
+//  * 256 x 128 output tile per workgroup of 8 waves; wave w and wave w + 4 run
+//    on the same SIMD.  Waves 0-3 (consumers) own rows 64w .. +63 x all 128
+//    columns and issue every MFMA (32x32x16, 16-bit operands, fp32
+//    accumulators): 32 per 64-deep K-step, back to back.  Waves 4-7
+//    (producers) decode the weight tile of the next K-step into LDS.  The
+//    vector ALU work of the decode co-issues with the other wave's MFMAs on
+//    the same SIMD (measured: the MFMA rate is unchanged while a second wave
+//    runs table lookups at one per 6 cycles), so the decode is hidden as long
+//    as it takes less time than the 32 MFMAs of a step.
+//  * The activation rows of a consumer are used by no other wave: each
+//    consumer moves its own 64 rows into an LDS ring with the gfx950
+//    global_load_lds b128 DMA, two K-steps ahead, issued between its MFMAs,
+//    and needs no barrier for them.
+//  * One workgroup barrier per K-step.  Between barriers t and t+1 the
+//    consumers read weight stage t % 2 (and activation stage t % 3) and the
+//    producers write the weight of step t+1; the packed weight is loaded
+//    three steps ahead.
+//  * Each producer lane decodes half a 64-weight unit (32 weights): the two
+//    lanes of a unit build its 16-entry table together (each half of the
+//    entries, exchanged with DPP); Q8_0 bytes are scaled directly.
+//  * Forward reads weight fragments with ds_read_b128 from the [n][k] stage;
+//    the backward contracts over n and reads them with the transposing
 //    ds_read_b64_tr_b16 from a [n][k] stage.
+//  * The weight fragment is the MFMA's first operand, so each accumulator
+//    lane holds 4 consecutive output columns; the finished tile goes through
+//    LDS so that every store instruction writes whole 256-byte row pieces.
 //  * Tiles are renumbered so that the workgroups sharing one activation row
 //    tile run on the same XCD (workgroup ids are dealt to the 8 XCDs round
 //    robin), keeping that tile in the XCD's L2.
@@ -59,7 +64,7 @@ constexpr int GBM = 256, GBN = 128, GBK = 64;
 
 template <bool DX>
 struct Geo {
-  // LDS stage of one K-step of the weight, bf16, [rows][ld].  Forward:
+  // LDS stage of one K-step of the weight, 16-bit, [rows][ld].  Forward:
   // 144-byte rows put the 16 rows of a ds_read_b128 quarter-wave on 16
   // different bank groups.  Backward: 320-byte rows (16 banks apart) keep the
   // 4-row x 32-byte footprints of the two 16-lane groups of a tr16 half-wave
@@ -68,6 +73,8 @@ struct Geo {
   static constexpr int cols = DX ? GBN : GBK;    // k
   static constexpr int ld = DX ? cols + 32 : cols + 8;
   static constexpr int stage = rows * ld;
+  // element offset of (row r, column c) in a stage
+  static QL_DEV int at(int r, int c) { return r * ld + c; }
 };
 
 QL_DEV u32x4_t load_act8(const uint16_t* row, int64_t c, int64_t C, bool vec) {
@@ -93,15 +100,15 @@ QL_DEV int64_t logical_tile(int64_t id, int64_t total) {
 }
 
 constexpr int NA = 3;                 // activation stages in the ring
-constexpr int A_STAGE = GBM * GBK;     // bf16 elements per activation stage (32 KiB)
+constexpr int A_STAGE = GBM * GBK;     // 16-bit elements per activation stage (32 KiB)
 
+// Physical 16-byte chunk of logical chunk c in activation row r of a stage.
+QL_DEV int a_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-// Workgroup barrier for the K loop.  __syncthreads() would add a release
-// fence, and with LDS DMA in flight that fence waits for every outstanding
-// vector load (vmcnt 0), draining the prefetch pipeline at each step.  Here
-// the caller states the vmcnt it needs; this waits for the wave's own LDS
-// traffic and the empty asm statements keep the compiler from moving memory
-// accesses across the barrier.
+// Workgroup barrier of the K loop after this wave's LDS traffic.  (A plain
+// __syncthreads() would add a release fence that waits for every outstanding
+// vector load, draining the prefetch pipeline at each step.)  The empty asm
+// statements keep the compiler from moving memory accesses across it.
 QL_DEV void k_barrier() {
   QL_LGKMCNT0();
   asm volatile("" ::: "memory");
@@ -109,16 +116,6 @@ QL_DEV void k_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Workgroup barrier that waits for nothing: the caller has already waited for
-// what it needs.
-QL_DEV void k_barrier_issue() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Physical 16-byte chunk of logical chunk c in activation row r of a stage.
-QL_DEV int a_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 template <bool DX, bool VEC, int FMT>
 __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ act, Nf4View w,
@@ -127,15 +124,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
                                                  float* __restrict__ part, int ksplit,
                                                  int steps_per_split, int64_t mtiles, int64_t otiles) {
   using G = Geo<DX>;
+  using FI = FmtInfo<FMT>;
   extern __shared__ __attribute__((aligned(16))) uint16_t sA[];   // [NA][GBM rows][GBK], swizzled
   __shared__ __attribute__((aligned(16))) uint16_t sW[2 * G::stage];   // decoded weight stages
-  __shared__ float s_lv[16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // wave w: rows [64 (w % 4), +64) of the tile, all 128 columns, the half
-  // kk in {2g, 2g+1} of every K-step, g = w / 4 (its group)
-  const int wm = wave & 3, grp = wave >> 2;
   const int lr = lane & 31, lg = lane >> 5;
   const int64_t N = w.n, K = w.k, nkb = K / kBlock;
   const int64_t C = DX ? N : K;       // contraction length
@@ -152,48 +146,257 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
   const int nsteps = (int)((C + GBK - 1) / GBK);
   const int s_begin = split * steps_per_split;
   const int s_end = min(nsteps, s_begin + steps_per_split);
-
-  if (FmtInfo<FMT>::nf4 && tid < 16) s_lv[tid] = codebook[tid];
-
-  // Decode role: group g decodes blocks [64g, 64g+64) of each step's 128; a
-  // quad of lanes shares one block, lane q = tid & 3 decodes its elements
-  // [16q, 16q+16).
-  const int q = tid & 3;
-  const int blk = 64 * grp + ((tid & 255) >> 2);
-  const int wr = DX ? (blk >> 1) : blk;                     // stage row
-  const int wcb = DX ? (blk & 1) : 0;                       // block within the stage row (dx)
-
-  // Activation tile of step st into ring stage `stage`: wave w fills rows
-  // [32w, 32w+32) with 4 DMA loads of 8 rows; lane l lands at byte 16l of its
-  // load's 1 KiB, i.e. row l/8, physical chunk l%8.  Rows past M are clamped
-  // to row M-1 (their products are discarded).  With 16-byte rows (VEC) the
-  // loads are buffer loads from a per-step base held in scalar registers and
-  // a fixed per-lane offset, so they cost no vector ALU work; a ragged last
-  // step clamps each piece into its row instead (columns past the
-  // contraction meet zero weights).  Without 16-byte rows the loads go
-  // through registers with zero fill and complete before the stores.
-  uint32_t a_vo[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rl = wave * 32 + i * 8 + (lane >> 3);
-    a_vo[i] = (uint32_t)(((min(m0 + rl, M - 1) - m0) * C + a_chunk(rl, lane & 7) * 8) * 2);
-  }
-  const uint16_t* a_tile = act + m0 * C;
+  const int ns = max(0, s_end - s_begin);   // K-steps of this workgroup
+  const int last = s_end - 1;
   // steps whose 64 columns all lie inside the contraction (the forward's
   // contraction is a whole number of 64-blocks)
   const int full_steps = (int)(C / GBK);
-  auto fill_a_one = [&](int64_t c0, uint16_t* base, int i, auto FULLc) {
-    uint16_t* dst = base + (wave * 32 + i * 8) * GBK;
-    const int rl = wave * 32 + i * 8 + (lane >> 3);
-    const int lc = a_chunk(rl, lane & 7);
-    if (VEC) {
-      if (decltype(FULLc)::value) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(a_tile + c0), (QL_LDS void*)dst, 16,
-                                                 a_vo[i], 0, 0, 0);
+
+  if (wave >= 4) {
+    // ============================== producers ==============================
+    const int ptid = tid - 256;
+    // Weight role: the step's tile holds 128 units (64 weights: one row, 64
+    // consecutive k); lane pair pb = ptid / 2 shares unit pb, lane ph = ptid %
+    // 2 decodes its elements [32 ph, 32 ph + 32).  Forward: unit pb is weight
+    // row o0 + pb at k-block st, stage row pb.  Backward: weight row 64 st +
+    // pb / 2 at k-block o0 / 64 + pb % 2, stage row pb / 2, columns
+    // 64 (pb % 2) + 32 ph.
+    const int pb = ptid >> 1, ph = ptid & 1;
+    const int wr = DX ? (pb >> 1) : pb;                              // stage row
+    const int wc = DX ? 64 * (pb & 1) + 32 * ph : 32 * ph;          // stage column
+    struct WRaw {
+      u32x4_t c[FMT == kFmtQ8 ? 2 : 1];   // the lane's 32 weights: 16 code bytes, or 32 int8
+      uint32_t qbyte;   // NF4 with double quantization: the 8-bit scale; Q8_0: the fp16 scale
+      float step;       // NF4: the group's fp32 constant, or the block absmax; uint4: the scale
+      float zp;         // uint4: the zero-point
+    };
+    // This lane's half unit at step st.  Storage position (rows in groups of
+    // 16, k-block-major inside a group): forward fp0 + st * fR (fixed row; fR
+    // = 16 except in a partial last group), backward st * 64 * nkb plus a
+    // fixed part whenever all 64 rows of the step are present.  Positions are
+    // taken relative to a per-step base in scalar registers; units outside the
+    // weight get an offset past the buffer end, so the hardware returns zeros
+    // (scale 0, hence decoded zeros).  Per-unit data at the storage position:
+    // CB code bytes and PB parameter bytes (the 8-bit scale with double
+    // quantization, whose fp32 constant of flat block b sits at step[b / 256];
+    // the fp32 absmax; the uint4 scale and zero-point; the two Q8_0 scales).
+    constexpr uint32_t CB = FI::code_bytes, PB = FI::param_bytes;
+    constexpr uint32_t kOut = 0x80000000u;
+    // NF4 scale entries: block 64 one per unit (its position), block 32 two
+    // per unit (2p + half), block 128 one per unit pair, in the row-group order
+    // over the k/128 block columns (nkb2); the second-level constant of flat
+    // block b is step[b / 256].
+    constexpr int BS = FI::block;
+    const int64_t nkb2 = nkb / 2;
+    const uint32_t hq = (uint32_t)ph;   // block 32: the lane's half is its own block
+    const int64_t kb_dx = o0 / kBlock + (pb & 1);
+    const int64_t frow = o0 + pb;
+    const int64_t fg0 = frow & ~int64_t(15);
+    const bool f_ok = frow < N;
+    const uint32_t fR = f_ok ? (uint32_t)min(int64_t(16), N - fg0) : 16u;
+    const uint32_t f_prel = (uint32_t)((fg0 - o0) * nkb + (frow - fg0));   // fp0 - o0 * nkb
+    const uint32_t f_prel2 = (uint32_t)((fg0 - o0) * nkb2 + (frow - fg0));
+    const bool d_kok = kb_dx < nkb;
+    const uint32_t d_prel = (uint32_t)((wr & ~15) * nkb + kb_dx * 16 + (wr & 15));
+    const uint32_t d_prel2 = (uint32_t)((wr & ~15) * nkb2 + (kb_dx >> 1) * 16 + (wr & 15));
+    auto sent = [&](uint32_t prel, uint32_t prel2) -> uint32_t {   // scale entry of the lane's unit
+      return BS == 64 ? prel : (BS == 32 ? 2 * prel + hq : prel2);
+    };
+    const uint32_t c_vo0 =
+        DX ? (d_kok ? d_prel * CB + ph * (CB / 2) : kOut) : (f_ok ? f_prel * CB + ph * (CB / 2) : kOut);
+    const uint32_t p_vo0 =
+        DX ? (d_kok ? sent(d_prel, d_prel2) * PB : kOut) : (f_ok ? sent(f_prel, f_prel2) * PB : kOut);
+    const uint32_t b_lane = (uint32_t)(BS == 64    ? (DX ? wr * nkb + kb_dx : frow * nkb)
+                                       : BS == 32 ? 2 * (DX ? wr * nkb + kb_dx : frow * nkb) + hq
+                                                  : (DX ? wr * nkb2 + (kb_dx >> 1) : frow * nkb2));
+    const auto step_rsrc = buf_rsrc(w.step, (uint32_t)(((N * K / BS + kGroup - 1) / kGroup) * 4));
+    auto load_w = [&](int st, WRaw& r) {
+      uint32_t cvo, pvo, bidx;
+      int64_t pbase;   // storage position of the per-step (backward) or per-tile (forward) base
+      int64_t sbase;   // its scale entry
+      if (DX) {
+        const int64_t n0 = (int64_t)st * GBK;
+        pbase = n0 * nkb;
+        sbase = BS == 64 ? pbase : (BS == 32 ? 2 * pbase : n0 * nkb2);
+        bidx = b_lane + (uint32_t)sbase;
+        if (st < full_steps) {
+          cvo = c_vo0;
+          pvo = p_vo0;
+        } else {   // ragged last step: partial group and rows past N
+          const int64_t g0 = (wr & ~15), R = min(int64_t(16), N - n0 - g0);
+          const bool ok = d_kok && n0 + wr < N;
+          const uint32_t prel = (uint32_t)(g0 * nkb + kb_dx * R + (wr & 15));
+          const uint32_t prel2 = (uint32_t)(g0 * nkb2 + (kb_dx >> 1) * R + (wr & 15));
+          cvo = ok ? prel * CB + ph * (CB / 2) : kOut;
+          pvo = ok ? sent(prel, prel2) * PB : kOut;
+        }
       } else {
-        const int64_t row = min(m0 + rl, M - 1);
-        __builtin_amdgcn_global_load_lds(act + row * C + min(c0 + lc * 8, C - 8), (QL_LDS void*)dst,
-                                         16, 0, 0);
+        pbase = o0 * nkb;
+        sbase = BS == 64 ? pbase : (BS == 32 ? 2 * pbase : o0 * nkb2);
+        const uint32_t sinc = BS == 64 ? (uint32_t)st : (BS == 32 ? 2u * st : (uint32_t)st >> 1);
+        cvo = c_vo0 + (uint32_t)st * fR * CB;
+        pvo = p_vo0 + sinc * fR * PB;
+        bidx = b_lane + sinc;
+      }
+      const auto crs = buf_rsrc(w.codes + pbase * CB);
+      r.c[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, cvo, 0, 0));
+      if constexpr (FMT == kFmtQ8) {
+        r.c[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, cvo + 16, 0, 0));
+        // the fp16 scale of the lane's 32-element half
+        r.qbyte = __builtin_amdgcn_raw_buffer_load_b16(buf_rsrc(w.qscale + pbase * 4), pvo + 2 * ph, 0, 0);
+      } else if constexpr (FI::nf4 && FI::dq) {
+        r.qbyte = __builtin_amdgcn_raw_buffer_load_b8(buf_rsrc(w.qscale + sbase), pvo, 0, 0);
+        r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(step_rsrc, (bidx >> 8) * 4, 0, 0));
+      } else if constexpr (FI::nf4) {
+        r.qbyte = 1u;   // scale = 1 * absmax, exact
+        r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(w.step + sbase), pvo, 0, 0));
+      } else {
+        // two dword loads (the backend may merge them): a 64-bit buffer load
+        // whose halves are bit-cast to float is shrunk to one dword by this
+        // compiler, both halves then holding the scale
+        const auto prs = buf_rsrc(w.step + 2 * pbase);
+        r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, pvo, 0, 0));
+        r.zp = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, pvo + 4, 0, 0));
+      }
+    };
+    // vector-memory loads issued per load_w (codes, then the parameters: the
+    // Q8_0 scale, the NF4 8-bit scale and group constant, the NF4 absmax, the
+    // uint4 pair, counted as one load since the backend may merge its two);
+    // the wait below counts them (a count below the real one only waits
+    // longer)
+    constexpr int kWLoads = FMT == kFmtQ8 ? 3 : ((FI::nf4 && FI::dq) ? 3 : 2);
+    // NF4 levels of this lane's table entries: level[8 ph + i] (block 32: all
+    // 16, each lane its own table)
+    float lv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lv[i] = 0.f;
+    if constexpr (FI::nf4) {
+      if constexpr (BS == 32) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lv[i] = gptr(codebook)[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lv[i] = gptr(codebook)[8 * ph + i];
+      }
+    }
+    // Decode the lane's 32 weights into weight stage `stage`: the 4-bit
+    // formats through the unit's table (entries level[c] * s for NF4,
+    // (c - zp) * scale for uint4), Q8_0 bytes times the fp16 scale.
+    auto decode_to = [&](const WRaw& r, int stage) {
+      uint16_t* const sw = sW + stage * G::stage;
+      // the lane's four 8-column groups (16 bytes each)
+      auto dst = [&](int j) -> u32x4_t& {
+        return *reinterpret_cast<u32x4_t*>(sw + G::at(wr, wc + 8 * j));
+      };
+      if constexpr (FMT == kFmtQ8) {
+        const float d = half_bits_to_float(r.qbyte & 0xFFFFu);
+        dst(0) = decode_q8x8(r.c[0][0], r.c[0][1], d);
+        dst(1) = decode_q8x8(r.c[0][2], r.c[0][3], d);
+        dst(2) = decode_q8x8(r.c[1][0], r.c[1][1], d);
+        dst(3) = decode_q8x8(r.c[1][2], r.c[1][3], d);
+      } else {
+        Lut t;
+        if constexpr (FMT == kFmtU4) {
+          const int zp = (int)r.zp;   // c - zp formed as an integer: +0 at c == zp
+          float lvr[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) lvr[i] = (float)(8 * ph + i - zp);
+          t = make_lut_pair(lvr, r.step);
+        } else if constexpr (BS == 32) {
+          t = make_lut(lv, (float)r.qbyte * r.step);
+        } else {
+          t = make_lut_pair<FI::f16>(lv, (float)r.qbyte * r.step);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst(j) = decode8(t, r.c[0][j]);
+      }
+    };
+
+    if (ns > 0) {
+      // prologue: codes of the first three steps, decoded weight of the first
+      WRaw rw[3];   // codes of step s in rw[(s - s_begin) % 3]
+      load_w(s_begin, rw[0]);
+      load_w(min(s_begin + 1, last), rw[1]);
+      load_w(min(s_begin + 2, last), rw[2]);
+      QL_VMCNT(2 * kWLoads);
+      decode_to(rw[0], 0);
+      k_barrier();
+      // Iteration t (between barriers t and t+1): codes of step t+3 into the
+      // ring slot of step t (decoded in the previous iteration), then, once
+      // the codes of t+1 have landed (everything issued before this
+      // iteration), decode step t+1 into weight stage (t+1) % 2 (last read in
+      // iteration t-1).  Steps past the end re-load the last one (never read).
+      auto iter = [&](int t, auto PHc) {
+        constexpr int PH = decltype(PHc)::value;   // t % 3
+        load_w(min(s_begin + t + 3, last), rw[PH]);
+        QL_VMCNT(2 * kWLoads);   // the codes of t+1 (two iterations old) have landed
+        if (t + 1 < ns) decode_to(rw[(PH + 1) % 3], (t + 1) & 1);
+        k_barrier();
+      };
+      using P0 = std::integral_constant<int, 0>;
+      using P1 = std::integral_constant<int, 1>;
+      using P2 = std::integral_constant<int, 2>;
+      int t = 0;
+      for (; t + 2 < ns; t += 3) {
+        iter(t, P0{});
+        iter(t + 1, P1{});
+        iter(t + 2, P2{});
+      }
+      if (t < ns) iter(t, P0{});
+      if (t + 1 < ns) iter(t + 1, P1{});
+      k_barrier();   // the consumers' epilogue
+    }
+    return;
+  }
+
+  // ================================ consumers ================================
+  const int cw = wave;   // rows [64 cw, 64 cw + 64) of the tile
+  // Activation tile of step st into ring stage `stage`: each consumer moves
+  // its own rows [64 cw, 64 cw + 64) (no other wave reads them) with 8 DMA
+  // loads of 8 rows, issued between its MFMAs; lane l lands at byte 16 l of
+  // its load's 1 KiB, i.e. row l / 8, physical chunk l % 8.  With 16-byte
+  // rows (VEC) the loads are buffer loads whose resource ends at the end of
+  // the activation matrix, so rows past M read as zeros; the address is a
+  // per-step base in scalar registers, a scalar row offset and one of two
+  // per-lane offsets (the chunk swizzle repeats every two loads).  In a
+  // ragged last step (backward, n % 64 != 0) a lane whose piece lies past
+  // the contraction takes an offset past any resource (zeros), selected
+  // without a branch.  Without 16-byte rows the loads go through
+  // registers with zero fill, rows past M clamped to row M-1 (their products
+  // are discarded).  (Loading the MFMA fragments straight into
+  // registers instead was measured slower: each such load touches 32 rows.)
+  uint32_t a_vo[2], a_vo_last[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rl = cw * 64 + i * 8 + (lane >> 3);
+    const int lc = a_chunk(rl, lane & 7);
+    a_vo[i] = (uint32_t)((rl * C + lc * 8) * 2);
+    a_vo_last[i] = (int64_t)full_steps * GBK + lc * 8 < C ? a_vo[i] : 0x80000000u;
+  }
+  const uint16_t* a_tile = act + m0 * C;
+  const int64_t a_bytes = (M - m0) * C * 2;   // from the tile's first row to the matrix end
+  auto fill_a_one = [&](int st, int stage, int i) {
+    const int64_t c0 = (int64_t)st * GBK;
+    uint16_t* dst = sA + stage * A_STAGE + (cw * 64 + i * 8) * GBK;
+    const int rl = cw * 64 + i * 8 + (lane >> 3);
+    const int lc = a_chunk(rl, lane & 7);
+    const int a_so = (i >> 1) * 16 * (int)C * 2;   // rows 16 (i / 2) further
+    if (VEC) {
+      if (!DX) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(a_tile + c0, rsrc_bytes(a_bytes - c0 * 2)),
+                                                 (QL_LDS void*)dst, 16, a_vo[i & 1], a_so, 0, 0);
+      } else {
+        // The backward reads its weight fragments with ds_read_b64_tr_b16,
+        // which the compiler cannot tell apart from the DMA's LDS target: it
+        // would wait for every DMA in flight before each of those reads.  The
+        // DMA is therefore issued as inline assembly, which the compiler does
+        // not track (it sets M0, which nothing else in this loop uses); the
+        // explicit vmcnt waits of the K loop count these loads.
+        const uint32_t lds_addr = (uint32_t)(uintptr_t)(QL_LDS void*)dst;
+        const auto rs = buf_rsrc(a_tile + c0, rsrc_bytes(a_bytes - c0 * 2));
+        const uint32_t vo = st < full_steps ? a_vo[i & 1] : a_vo_last[i & 1];
+        asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+                     :: "v"(vo), "s"(lds_addr), "s"(rs), "s"(a_so) : "memory", "m0");
       }
     } else {
       const int64_t row = min(m0 + rl, M - 1);
@@ -202,159 +405,29 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       *reinterpret_cast<u32x4_t*>(dst + lane * 8) = v;
     }
   };
-  auto fill_a = [&](int st, int stage) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (!DX || st < full_steps)
-        fill_a_one((int64_t)st * GBK, sA + stage * A_STAGE, i, std::true_type{});
-      else
-        fill_a_one((int64_t)st * GBK, sA + stage * A_STAGE, i, std::false_type{});
-    }
-  };
 
-  struct WRaw {
-    u32x4_t codes;    // this lane's 16 weights: words 0-1 (4-bit formats) or 0-3 (Q8_0)
-    uint32_t qbyte;   // NF4 with double quantization: the 8-bit scale; Q8_0: the two fp16 scales
-    float step;       // NF4: the group's fp32 constant, or the block absmax; uint4: the scale
-    float zp;         // uint4: the zero-point
-  };
-  // This lane's unit at step st.  Storage position (rows in groups of 16,
-  // k-block-major inside a group): forward fp0 + st * fR (fixed row; fR = 16
-  // except in a partial last group), backward st * 64 * nkb plus a fixed part
-  // whenever all 64 rows of the step are present.  Positions are taken
-  // relative to a per-step base in scalar registers; units outside the
-  // weight get an offset past the buffer end, so the hardware returns zeros
-  // (scale 0, hence decoded zeros).  Per-unit data at the storage position:
-  // CB code bytes and PB parameter bytes (the 8-bit scale with double
-  // quantization, whose fp32 constant of flat block b sits at step[b / 256];
-  // the fp32 absmax; the uint4 scale and zero-point; the two Q8_0 scales).
-  using FI = FmtInfo<FMT>;
-  constexpr uint32_t CB = FI::code_bytes, PB = FI::param_bytes;
-  constexpr uint32_t kOut = 0x80000000u;
-  // NF4 scale entries: block 64 one per unit (its position), block 32 two
-  // per unit (2p + half), block 128 one per unit pair, in the row-group order
-  // over the k/128 block columns (nkb2); the second-level constant of flat
-  // block b is step[b / 256].
-  constexpr int BS = FI::block;
-  const int64_t nkb2 = nkb / 2;
-  const uint32_t hq = (uint32_t)(q >> 1);   // block 32: the lane's half of its unit
-  const int64_t kb_dx = o0 / kBlock + wcb;
-  const int64_t fg0 = (o0 + wr) & ~int64_t(15);
-  const bool f_ok = (o0 + wr) < N;
-  const uint32_t fR = f_ok ? (uint32_t)min(int64_t(16), N - fg0) : 16u;
-  const uint32_t f_prel = (uint32_t)((fg0 - o0) * nkb + (o0 + wr - fg0));   // fp0 - o0 * nkb
-  const uint32_t f_prel2 = (uint32_t)((fg0 - o0) * nkb2 + (o0 + wr - fg0));
-  const bool d_kok = kb_dx < nkb;
-  const uint32_t d_prel = (uint32_t)((wr & ~15) * nkb + kb_dx * 16 + (wr & 15));
-  const uint32_t d_prel2 = (uint32_t)((wr & ~15) * nkb2 + (kb_dx >> 1) * 16 + (wr & 15));
-  auto sent = [&](uint32_t prel, uint32_t prel2) -> uint32_t {   // scale entry of the lane's unit
-    return BS == 64 ? prel : (BS == 32 ? 2 * prel + hq : prel2);
-  };
-  const uint32_t c_vo0 =
-      DX ? (d_kok ? d_prel * CB + q * (CB / 4) : kOut) : (f_ok ? f_prel * CB + q * (CB / 4) : kOut);
-  const uint32_t p_vo0 =
-      DX ? (d_kok ? sent(d_prel, d_prel2) * PB : kOut) : (f_ok ? sent(f_prel, f_prel2) * PB : kOut);
-  const uint32_t b_lane = (uint32_t)(BS == 64    ? (DX ? wr * nkb + kb_dx : (o0 + wr) * nkb)
-                                     : BS == 32 ? 2 * (DX ? wr * nkb + kb_dx : (o0 + wr) * nkb) + hq
-                                                : (DX ? wr * nkb2 + (kb_dx >> 1) : (o0 + wr) * nkb2));
-  const auto step_rsrc = buf_rsrc(w.step, (uint32_t)(((N * K / BS + kGroup - 1) / kGroup) * 4));
-  auto load_w = [&](int st, WRaw& r) {
-    uint32_t cvo, pvo, bidx;
-    int64_t pbase;   // storage position of the per-step (backward) or per-tile (forward) base
-    int64_t sbase;   // its scale entry
-    if (DX) {
-      const int64_t n0 = (int64_t)st * GBK;
-      pbase = n0 * nkb;
-      sbase = BS == 64 ? pbase : (BS == 32 ? 2 * pbase : n0 * nkb2);
-      bidx = b_lane + (uint32_t)sbase;
-      if (st < full_steps) {
-        cvo = c_vo0;
-        pvo = p_vo0;
-      } else {   // ragged last step: partial group and rows past N
-        const int64_t g0 = (wr & ~15), R = min(int64_t(16), N - n0 - g0);
-        const bool ok = d_kok && n0 + wr < N;
-        const uint32_t prel = (uint32_t)(g0 * nkb + kb_dx * R + (wr & 15));
-        const uint32_t prel2 = (uint32_t)(g0 * nkb2 + (kb_dx >> 1) * R + (wr & 15));
-        cvo = ok ? prel * CB + q * (CB / 4) : kOut;
-        pvo = ok ? sent(prel, prel2) * PB : kOut;
-      }
-    } else {
-      pbase = o0 * nkb;
-      sbase = BS == 64 ? pbase : (BS == 32 ? 2 * pbase : o0 * nkb2);
-      const uint32_t sinc = BS == 64 ? (uint32_t)st : (BS == 32 ? 2u * st : (uint32_t)st >> 1);
-      cvo = c_vo0 + (uint32_t)st * fR * CB;
-      pvo = p_vo0 + sinc * fR * PB;
-      bidx = b_lane + sinc;
-    }
-    const auto crs = buf_rsrc(w.codes + pbase * CB);
-    if constexpr (FMT == kFmtQ8) {
-      r.codes = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, cvo, 0, 0));
-      r.qbyte = __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(w.qscale + pbase * 4), pvo, 0, 0);
-    } else {
-      const u32x2_t c = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(crs, cvo, 0, 0));
-      r.codes = u32x4_t{c[0], c[1], 0u, 0u};
-      if constexpr (FI::nf4 && FI::dq) {
-        r.qbyte = __builtin_amdgcn_raw_buffer_load_b8(buf_rsrc(w.qscale + sbase), pvo, 0, 0);
-        r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(step_rsrc, (bidx >> 8) * 4, 0, 0));
-      } else if constexpr (FI::nf4) {
-        r.qbyte = 1u;   // scale = 1 * absmax, exact
-        r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(w.step + sbase), pvo, 0, 0));
-      } else {
-        // two dword loads (the backend merges them): a 64-bit buffer load
-        // whose halves are bit-cast to float is shrunk to one dword by this
-        // compiler, both halves then holding the scale
-        const auto prs = buf_rsrc(w.step + 2 * pbase);
-        r.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, pvo, 0, 0));
-        r.zp = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, pvo + 4, 0, 0));
-      }
-    }
-  };
-  // NF4 levels of this lane's table entries (set once the codebook is in
-  // LDS): level[4q + i], or for block 32 level[8 (q & 1) + i]
-  float lvq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  // Decode this lane's 16 weights into the stage: the 4-bit formats through a
-  // per-block table built by the quad (entries level[c] * s for NF4,
-  // (c - zp) * scale for uint4); Q8_0 bytes times the fp16 scale of the
-  // lane's 32-element half.
-  auto decode_to = [&](const WRaw& r, u32x4_t* dst) {
-    if constexpr (FMT == kFmtQ8) {
-      const float d = half_bits_to_float(q >= 2 ? r.qbyte >> 16 : r.qbyte & 0xFFFFu);
-      dst[0] = decode_q8x8(r.codes[0], r.codes[1], d);
-      dst[1] = decode_q8x8(r.codes[2], r.codes[3], d);
-    } else {
-      float lvr[4];
-      float sc;
-      if constexpr (FMT == kFmtU4) {
-        const int zp = (int)r.zp;   // c - zp formed as an integer: +0 at c == zp
+  f32x16_t acc[4][2];    // [column tile nt][row tile mt]: D[n][m]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lvr[i] = (float)(4 * q + i - zp);
-        sc = r.step;
-      } else {
+  for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lvr[i] = lvq[i];
-        sc = (float)r.qbyte * r.step;
-      }
-      // block 32: the half-quads hold different scales, so each lane pair
-      // builds its own table
-      const Lut t = BS == 32 ? make_lut_pair(lvq, sc) : make_lut_quad<FI::f16>(lvr, sc);
-      dst[0] = decode8(t, r.codes[0]);
-      dst[1] = decode8(t, r.codes[1]);
-    }
-  };
-  auto wdst = [&](int stage) {
-    return reinterpret_cast<u32x4_t*>(sW + stage * G::stage + wr * G::ld + wcb * 64 + q * 16);
-  };
-  // MFMA fragments of this wave for one step: A rows 64 wm + 32 mt, B
-  // columns 32 nt, contraction kk = 2g + h (16 wide each)
-  auto read_frags = [&](const uint16_t* sa, const uint16_t* sw, u32x4_t (&a)[2][2],
-                        u32x4_t (&b)[2][4]) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kk = 2 * grp + h;
+      for (int i = 0; i < 16; ++i) acc[nt][mt][i] = 0.f;
+
+  if (ns > 0) {
+    // fragments of one 16-deep contraction slice, three buffers in the
+    // forward: slice kk of step t lives in slot (t + kk) % 3 (4 slices per
+    // step), read two slices before its MFMAs
+    constexpr int NS = DX ? 2 : 3;
+    u32x4_t wf[NS][4], xf[NS][2];
+    auto read = [&](int t, int kk, auto SLc) {
+      constexpr int b = decltype(SLc)::value;
+      const uint16_t* sa = sA + (t % NA) * A_STAGE;
+      const uint16_t* sw = sW + (t & 1) * G::stage;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const int r = wm * 64 + 32 * mt + lr;
-        a[h][mt] = *reinterpret_cast<const u32x4_t*>(sa + r * GBK + a_chunk(r, 2 * kk + lg) * 8);
+        const int r = cw * 64 + 32 * mt + lr;
+        xf[b][mt] = *reinterpret_cast<const u32x4_t*>(sa + r * GBK + a_chunk(r, 2 * kk + lg) * 8);
       }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
@@ -362,179 +435,113 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
           const int G16 = lane >> 4, i16 = lane & 15;
           const int row = 16 * kk + 8 * (G16 >> 1) + (i16 >> 2);
           const int col = 32 * nt + 16 * (G16 & 1) + 4 * (i16 & 3);
-          const u32x2_t lo = ds_tr16(sw + row * G::ld + col);
-          const u32x2_t hi = ds_tr16(sw + (row + 4) * G::ld + col);
-          b[h][nt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+          const u32x2_t lo = ds_tr16(sw + G::at(row, col));
+          const u32x2_t hi = ds_tr16(sw + G::at(row + 4, col));
+          wf[b][nt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         } else {
-          b[h][nt] = *reinterpret_cast<const u32x4_t*>(sw + (32 * nt + lr) * G::ld + 16 * kk + 8 * lg);
+          wf[b][nt] = *reinterpret_cast<const u32x4_t*>(sw + (32 * nt + lr) * G::ld + 16 * kk + 8 * lg);
         }
       }
-    }
-  };
-
-  __syncthreads();
-  if constexpr (FmtInfo<FMT>::nf4) {
-    if constexpr (FmtInfo<FMT>::block == 32) {
+    };
+    // 8 MFMAs of slice kk from slot b; after the 4th and the 8th, DMA loads
+    // 2 kk and 2 kk + 1 of the activation tile of step sa into ring stage
+    // `stage`
+    auto mma = [&](auto SLc, int kk, int sa, int stage) {
+      constexpr int b = decltype(SLc)::value;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) lvq[i] = s_lv[8 * (q & 1) + i];
+      for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) acc[nt][mt] = mfma32<FI::f16>(wf[b][nt], xf[b][mt], acc[nt][mt]);
+        if (nt & 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          fill_a_one(sa, stage, 2 * kk + (nt >> 1));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    // prologue: activations of the first two steps (this wave's rows)
+    for (int i = 0; i < 8; ++i) fill_a_one(s_begin, 0, i);
+    for (int i = 0; i < 8; ++i) fill_a_one(min(s_begin + 1, last), 1, i);
+    QL_VMCNT(VEC ? 8 : 0);   // step 0's rows have landed
+    k_barrier();             // weight stage 0 ready
+    read(0, 0, S0{});
+    if constexpr (!DX) read(0, 1, S1{});
+    // Iteration t (P = t % 3): slices 0-3 of step t from slots P, P+1, P+2,
+    // P, with the DMA of step t+2's activation rows (ring stage (t+2) % 3,
+    // last read in iteration t-1) spread over the MFMAs; before the barrier,
+    // this wave's rows of step t+1 (issued in iteration t-1) have landed and
+    // every read of weight stage t is done; after it the first two slices of
+    // step t+1 are read.  Steps past the end re-load the last one (never
+    // read).
+    auto iter = [&](int t, auto PHc) {
+      constexpr int P = decltype(PHc)::value;
+      using A = std::integral_constant<int, P>;
+      using B = std::integral_constant<int, (P + 1) % 3>;
+      using C2 = std::integral_constant<int, (P + 2) % 3>;
+      const int sa = min(s_begin + t + 2, last), stage = (t + 2) % NA;
+      __builtin_amdgcn_sched_barrier(0);
+      read(t, 2, C2{});
+      __builtin_amdgcn_sched_barrier(0);
+      mma(A{}, 0, sa, stage);
+      __builtin_amdgcn_sched_barrier(0);
+      read(t, 3, A{});
+      __builtin_amdgcn_sched_barrier(0);
+      mma(B{}, 1, sa, stage);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(C2{}, 2, sa, stage);
+      __builtin_amdgcn_sched_barrier(0);
+      QL_VMCNT(VEC ? 6 : 0);
+      k_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < ns) {
+        read(t + 1, 0, B{});
+        read(t + 1, 1, C2{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma(A{}, 3, sa, stage);
+    };
+    // The backward (whose transposing reads need more registers) keeps two
+    // slots: slice kk in slot kk % 2, read one slice ahead.
+    auto iter2 = [&](int t) {
+      const int sa = min(s_begin + t + 2, last), stage = (t + 2) % NA;
+      __builtin_amdgcn_sched_barrier(0);
+      read(t, 1, S1{});
+      __builtin_amdgcn_sched_barrier(0);
+      mma(S0{}, 0, sa, stage);
+      __builtin_amdgcn_sched_barrier(0);
+      read(t, 2, S0{});
+      __builtin_amdgcn_sched_barrier(0);
+      mma(S1{}, 1, sa, stage);
+      __builtin_amdgcn_sched_barrier(0);
+      read(t, 3, S1{});
+      __builtin_amdgcn_sched_barrier(0);
+      mma(S0{}, 2, sa, stage);
+      __builtin_amdgcn_sched_barrier(0);
+      QL_VMCNT(VEC ? 6 : 0);
+      k_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < ns) read(t + 1, 0, S0{});
+      __builtin_amdgcn_sched_barrier(0);
+      mma(S1{}, 3, sa, stage);
+    };
+    if constexpr (DX) {
+      for (int t = 0; t < ns; ++t) iter2(t);
     } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lvq[i] = s_lv[4 * q + i];
-    }
-  }
-
-  f32x16_t acc[2][4];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
-
-  if (s_begin < s_end) {
-    const int last = s_end - 1;
-    // prologue: decoded weight of s_begin (stage 0), activation tiles of
-    // s_begin and s_begin+1, codes of s_begin+1 and s_begin+2
-    WRaw rw[3];   // codes of step t in rw[(t - s_begin) % 3]
-    {
-      WRaw wf;
-      load_w(s_begin, wf);
-      fill_a(s_begin, 0);
-      fill_a(min(s_begin + 1, last), 1);
-      load_w(min(s_begin + 1, last), rw[1]);
-      load_w(min(s_begin + 2, last), rw[2]);
-      __builtin_amdgcn_s_waitcnt(0);       // (prologue only)
-      decode_to(wf, wdst(0));
-      __syncthreads();
-    }
-    u32x4_t fa[2][2], fb[2][4];
-
-    // Ping-pong schedule.  Every step t has a memory phase MEM(t) and a
-    // matrix phase MMA(t) per wave; group 0 runs MEM(t) while group 1 runs
-    // MMA(t-1), then group 0 runs MMA(t) while group 1 runs MEM(t), with a
-    // workgroup barrier between phases, so each SIMD (one wave of each group)
-    // alternates the matrix cores between its two waves.
-    //   MEM(t): read this wave's fragments of step t (A ring stage t%3, W
-    //   stage t&1), decode the group's half of W(t+1) into stage (t+1)&1 and
-    //   wait for its LDS traffic.
-    //   MMA(t): 16 MFMAs (2 K halves x 2 x 4 tiles) from those fragments,
-    //   with the DMA of A(t+2) and the codes of W(t+3) issued between them so
-    //   that the address and data paths stay busy under the matrix work.
-    // A(t+2) is first read by group 0 in MEM(t+2), two phases after group 1
-    // issued its rows in MMA(t): every wave waits for all its loads at the
-    // end of its next MEM phase.
-    auto mem = [&](int st, auto PHc) {
-      constexpr int PH = decltype(PHc)::value;   // (st - s_begin) % 3
-      const int rel = st - s_begin;
-      read_frags(sA + (rel % NA) * A_STAGE, sW + (rel & 1) * G::stage, fa, fb);
-      decode_to(rw[(PH + 1) % 3], wdst((rel + 1) & 1));
-      QL_LGKMCNT0();
-      QL_VMCNT(0);
-      __builtin_amdgcn_sched_barrier(0);
-      k_barrier_issue();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto mma = [&](int st, auto PHc) {
-      constexpr int PH = decltype(PHc)::value;
-      const int rel = st - s_begin;
-      const int sa = min(st + 2, last);
-      const int64_t c0 = (int64_t)sa * GBK;
-      uint16_t* abase = sA + ((rel + 2) % NA) * A_STAGE;
-      const bool full = !DX || sa < full_steps;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            acc[mt][nt] = mfma32<FI::f16>(fa[h][mt], fb[h][nt], acc[mt][nt]);
-            const int i = (h * 2 + mt) * 4 + nt;
-            if (i % 4 == 0) {
-              __builtin_amdgcn_sched_barrier(0);
-              if (full)
-                fill_a_one(c0, abase, i / 4, std::true_type{});
-              else
-                fill_a_one(c0, abase, i / 4, std::false_type{});
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            if (i == 6) {
-              load_w(min(st + 3, last), rw[PH % 3]);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-      __builtin_amdgcn_sched_barrier(0);
-      k_barrier_issue();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // group 1 starts one phase late
-    if (grp == 1) k_barrier_issue();
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
-    using P2 = std::integral_constant<int, 2>;
-    int st = s_begin;
-    for (; st + 2 < s_end; st += 3) {
-      mem(st, P0{});
-      mma(st, P0{});
-      mem(st + 1, P1{});
-      mma(st + 1, P1{});
-      mem(st + 2, P2{});
-      mma(st + 2, P2{});
-    }
-    if (st < s_end) {
-      mem(st, P0{});
-      mma(st, P0{});
-    }
-    if (st + 1 < s_end) {
-      mem(st + 1, P1{});
-      mma(st + 1, P1{});
-    }
-    // group 0 matches group 1's extra barrier
-    if (grp == 0) k_barrier_issue();
-  }
-
-  // ---- the two groups hold partial sums over complementary K halves of the
-  // same 64 x 128 tiles: group 0 finishes columns [0, 64), group 1 columns
-  // [64, 128).  Each wave hands the other group's half to its partner wave
-  // (same rows) through 16 KiB of LDS: waves 0-5 in the activation ring,
-  // waves 6-7 in the weight stages.  The clamped prefetches of the last steps
-  // may still be landing in the ring, hence the full wait first.
-  QL_VMCNT(0);
-  __syncthreads();
-  f32x16_t fin[2][2];   // this wave's finished 64 x 64 output tile
-  {
-    auto region = [&](int v) {
-      return v < 6 ? reinterpret_cast<f32x4_t*>(sA) + (size_t)v * 1024
-                   : reinterpret_cast<f32x4_t*>(sW) + (size_t)(v - 6) * 1024;
-    };
-    static_assert(2 * G::stage * sizeof(uint16_t) >= 2 * 16384, "exchange needs 32 KiB of stages");
-    static_assert(NA * A_STAGE * sizeof(uint16_t) >= 6 * 16384, "exchange needs 96 KiB of ring");
-    // (the accumulators are selected, never indexed by the group, so they
-    // stay in registers)
-    f32x4_t* mine = region(wave);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const f32x16_t v = grp == 0 ? acc[mt][2 + j] : acc[mt][j];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          mine[((mt * 2 + j) * 4 + e) * 64 + lane] = f32x4_t{v[4 * e], v[4 * e + 1], v[4 * e + 2], v[4 * e + 3]};
-        fin[mt][j] = grp == 0 ? acc[mt][j] : acc[mt][2 + j];
+      int t = 0;
+      for (; t + 2 < ns; t += 3) {
+        iter(t, S0{});
+        iter(t + 1, S1{});
+        iter(t + 2, S2{});
       }
-    __syncthreads();
-    const f32x4_t* theirs = region(wave ^ 4);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const f32x4_t v = theirs[((mt * 2 + j) * 4 + e) * 64 + lane];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) fin[mt][j][4 * e + i] += v[i];
-        }
+      if (t < ns) iter(t, S0{});
+      if (t + 1 < ns) iter(t + 1, S1{});
+    }
+    // no DMA of this wave may still be writing LDS when the epilogue reuses it
+    QL_VMCNT(0);
   }
-  const int nt0 = grp == 0 ? 0 : 2;   // this wave's output columns: nt0, nt0 + 1
 
   // ---- epilogue.  LoRA term (ksplit == 1): out += (scaling * L) R^T on the
   // matrix cores, 16 ranks per MFMA step; the fp32 factor scaling * L is
@@ -545,16 +552,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
   // issued before the current chunk's MFMAs.
   if (ksplit == 1 && lora.r > 0) {
     const int r = lora.r;
-    int64_t orow[2], mrow[2];
+    int64_t orow[4], mrow[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) orow[j] = min(o0 + 32 * (nt0 + j) + lr, O - 1);
+    for (int nt = 0; nt < 4; ++nt) orow[nt] = min(o0 + 32 * nt + lr, O - 1);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) mrow[mt] = min(m0 + wm * 64 + 32 * mt + lr, M - 1);
+    for (int mt = 0; mt < 2; ++mt) mrow[mt] = min(m0 + cw * 64 + 32 * mt + lr, M - 1);
     const bool rvec = lora.rs_j == 1 && r % 8 == 0 && (lora.rs_c % 8) == 0 &&
                       (reinterpret_cast<uintptr_t>(lora.R) & 15) == 0;
     const bool lvec = r % 8 == 0 && (reinterpret_cast<uintptr_t>(lora.L) & 15) == 0;
     struct Ops {
-      u32x4_t rb[2];      // R[o][jb .. jb+7], 16-bit pairs
+      u32x4_t rb[4];      // R[o][jb .. jb+7], 16-bit pairs
       f32x4_t lv[2][2];   // L[m][jb .. jb+7]
     };
     // this lane's ranks of the chunk at j0: jb .. jb+7, jb = j0 + 8 lg
@@ -562,15 +569,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       const int jb = j0 + 8 * lg;
       const int jc = min(jb, r - 8 > 0 ? r - 8 : 0);   // vector start kept inside the row
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int nt = 0; nt < 4; ++nt) {
         if (rvec) {
-          op.rb[j] = *reinterpret_cast<const u32x4_t*>(lora.R + orow[j] * lora.rs_c + jc);
+          op.rb[nt] = *reinterpret_cast<const u32x4_t*>(lora.R + orow[nt] * lora.rs_c + jc);
         } else {
           uint32_t h[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            h[e] = lora.R[orow[j] * lora.rs_c + (int64_t)min(jb + e, r - 1) * lora.rs_j];
-          op.rb[j] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+            h[e] = lora.R[orow[nt] * lora.rs_c + (int64_t)min(jb + e, r - 1) * lora.rs_j];
+          op.rb[nt] = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
         }
       }
 #pragma unroll
@@ -588,14 +595,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     auto apply = [&](int j0, const Ops& op) {
       const int jb = j0 + 8 * lg;
       // ranks past r read a clamped element: zero both factors' share
-      u32x4_t rb[2];
+      u32x4_t rb[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        rb[j] = op.rb[j];
+      for (int nt = 0; nt < 4; ++nt) {
+        rb[nt] = op.rb[nt];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool k0 = jb + 2 * e < r, k1 = jb + 2 * e + 1 < r;
-          rb[j][e] = (k0 ? rb[j][e] & 0xFFFFu : 0u) | (k1 ? rb[j][e] & 0xFFFF0000u : 0u);
+          rb[nt][e] = (k0 ? rb[nt][e] & 0xFFFFu : 0u) | (k1 ? rb[nt][e] & 0xFFFF0000u : 0u);
         }
       }
 #pragma unroll
@@ -613,9 +620,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
           alo[e] = pack16x2<FI::f16>(lo[2 * e], lo[2 * e + 1]);
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          fin[mt][j] = mfma32<FI::f16>(ahi, rb[j], fin[mt][j]);
-          fin[mt][j] = mfma32<FI::f16>(alo, rb[j], fin[mt][j]);
+        for (int nt = 0; nt < 4; ++nt) {
+          acc[nt][mt] = mfma32<FI::f16>(rb[nt], ahi, acc[nt][mt]);
+          acc[nt][mt] = mfma32<FI::f16>(rb[nt], alo, acc[nt][mt]);
         }
       }
     };
@@ -632,29 +639,94 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       }
     }
   }
+
+  // ---- stores.  Lane element i of acc[nt][mt] is output row m = m0 + 64 cw +
+  // 32 mt + l % 32, column o = o0 + 32 nt + 8 (i / 4) + 4 (l / 32) + i % 4.
+  // The tile goes through LDS (the activation ring, free once the producers
+  // have drained their last loads) so that each store instruction writes
+  // whole rows: 16 lanes x 16 bytes = 256 contiguous bytes per row, 16-bit
+  // output in one pass of 64 x 128, fp32 in two passes of 64 x 64 columns.
+  // Written once: non-temporal stores leave the L2 to the operand tiles the
+  // other workgroups reuse.
+  if (ns > 0) k_barrier();   // every wave is done with the stages (DMA drained)
+  const bool o8 = (O & 7) == 0;   // 8-column pieces are 16-byte aligned in 16-bit rows
+  const bool o4 = (O & 3) == 0;   // 4-column pieces are 16-byte aligned in fp32 rows
+  if (ksplit == 1 && out16) {
+    // [64 rows][136] 16-bit per consumer (row pitch 272 bytes: the 8-byte
+    // writes of a wave's 32 rows spread over the banks)
+    constexpr int LDO = 136;
+    uint16_t* st = sA + cw * 64 * LDO;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t m = m0 + wm * 64 + 32 * mt + 8 * (i >> 2) + 4 * lg + (i & 3);
-        const int64_t o = o0 + 32 * (nt0 + j) + lr;
-        if (m < M && o < O) {
-          const float v = fin[mt][j][i];
-          if (ksplit > 1)
-            part[((int64_t)split * M + m) * O + o] = v;
-          else if (out16)
-            // written once: non-temporal stores leave the L2 to the operand
-            // tiles that the other workgroups reuse
-            __builtin_nontemporal_store(to16<FI::f16>(v), reinterpret_cast<uint16_t*>(out) + m * O + o);
-          else
-            __builtin_nontemporal_store(v, reinterpret_cast<float*>(out) + m * O + o);
+        for (int q = 0; q < 4; ++q) {
+          const u32x2_t pk = {pack16x2<FI::f16>(acc[nt][mt][4 * q], acc[nt][mt][4 * q + 1]),
+                              pack16x2<FI::f16>(acc[nt][mt][4 * q + 2], acc[nt][mt][4 * q + 3])};
+          *reinterpret_cast<u32x2_t*>(st + (32 * mt + lr) * LDO + 32 * nt + 8 * q + 4 * lg) = pk;
+        }
+    QL_LGKMCNT0();
+    // lane l: row 4 j + l / 16 (j = 0..15), columns 8 (l % 16) .. + 7
+    uint16_t* outp = reinterpret_cast<uint16_t*>(out);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int rl = 4 * j + (lane >> 4), cl = 8 * (lane & 15);
+      const int64_t m = m0 + cw * 64 + rl, o = o0 + cl;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + rl * LDO + cl);
+      if (m < M) {
+        uint16_t* dst = outp + m * O + o;
+        if (o8 && o + 7 < O) {
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (o + e < O) dst[e] = (uint16_t)(e & 1 ? v[e >> 1] >> 16 : v[e >> 1] & 0xFFFFu);
         }
       }
+    }
+  } else {
+    // fp32 (output or split partials): [64 rows][68] floats per consumer and pass
+    constexpr int LDO = 68;
+    float* st = reinterpret_cast<float*>(sA) + cw * 64 * LDO;
+    float* base = ksplit > 1 ? part + (int64_t)split * M * O : reinterpret_cast<float*>(out);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass) QL_LGKMCNT0();   // (the reads of pass 0 are done before the writes of pass 1)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nt = 2 * pass + n2;
+            const f32x4_t v = {acc[nt][mt][4 * q], acc[nt][mt][4 * q + 1], acc[nt][mt][4 * q + 2],
+                               acc[nt][mt][4 * q + 3]};
+            *reinterpret_cast<f32x4_t*>(st + (32 * mt + lr) * LDO + 32 * n2 + 8 * q + 4 * lg) = v;
+          }
+      QL_LGKMCNT0();
+      // lane l: row 4 j + l / 16, columns 4 (l % 16) .. + 3 of this pass's 64
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int rl = 4 * j + (lane >> 4), cl = 4 * (lane & 15);
+        const int64_t m = m0 + cw * 64 + rl, o = o0 + 64 * pass + cl;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(st + rl * LDO + cl);
+        if (m < M) {
+          float* dst = base + m * O + o;
+          if (o4 && o + 3 < O) {
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(dst));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (o + e < O) dst[e] = v[e];
+          }
+        }
+      }
+    }
+  }
 }
 
-template <bool DX>
+
 static constexpr size_t smem_bytes() {
   return sizeof(uint16_t) * NA * A_STAGE;   // dynamic part: the activation ring
 }
@@ -668,9 +740,9 @@ static hipError_t launch_one(dim3 grid, hipStream_t s, const uint16_t* act, cons
   // function-local static is initialized exactly once, thread-safely)
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_gemm<DX, VEC, FMT>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)smem_bytes<DX>());
+      (int)smem_bytes());
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_gemm<DX, VEC, FMT>), grid, dim3(512), smem_bytes<DX>(), s, act, w, codebook,
+  hipLaunchKernelGGL((k_gemm<DX, VEC, FMT>), grid, dim3(512), smem_bytes(), s, act, w, codebook,
                      M, lora, out, (int)out16, part, ksplit, per, mtiles, otiles);
   return hipGetLastError();
 }
