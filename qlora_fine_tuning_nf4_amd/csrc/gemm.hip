@@ -66,12 +66,14 @@ template <bool DX>
 struct Geo {
   // LDS stage of one K-step of the weight, 16-bit, [rows][ld].  Forward:
   // 144-byte rows put the 16 rows of a ds_read_b128 quarter-wave on 16
-  // different bank groups.  Backward: 320-byte rows (16 banks apart) keep the
-  // 4-row x 32-byte footprints of the two 16-lane groups of a tr16 half-wave
-  // read on disjoint banks.
+  // different bank groups.  Backward: with 304-byte rows (76 dwords, 12
+  // banks apart modulo 64) the 16 rows x 4 column pieces of a producer
+  // wave's 16-byte writes start on 16 different 4-bank groups, so a write
+  // instruction takes the minimum 4 passes (320-byte rows put them all on
+  // 16 banks); the transposing reads run at the same rate either way.
   static constexpr int rows = DX ? GBK : GBN;    // n (dx: contraction) or n (fwd: output)
   static constexpr int cols = DX ? GBN : GBK;    // k
-  static constexpr int ld = DX ? cols + 32 : cols + 8;
+  static constexpr int ld = DX ? cols + 24 : cols + 8;
   static constexpr int stage = rows * ld;
   // element offset of (row r, column c) in a stage
   static QL_DEV int at(int r, int c) { return r * ld + c; }
@@ -350,9 +352,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
   }
 
   // ================================ consumers ================================
-  const int cw = wave;   // rows [64 cw, 64 cw + 64) of the tile
+  const int cw = wave;
+  // Wave tile: in the forward each consumer takes 64 rows x the 128 columns
+  // of the tile; in the backward 128 rows x 64 columns (two waves per row
+  // block), which costs 8 LDS reads per 16-deep slice (2 x 2 transposing
+  // reads + 4) instead of 10, so two slices in flight stay close to the 15
+  // LDS operations a wave can have outstanding (past that, issue stalls).
+  constexpr int WM = DX ? 128 : 64, WN = DX ? 64 : 128;
+  constexpr int MT = WM / 32, NT = WN / 32;         // 32 x 32 MFMA tiles
+  const int wr0 = DX ? 128 * (cw >> 1) : 64 * cw;   // first tile row of the wave
+  const int wc0 = DX ? 64 * (cw & 1) : 0;           // first tile column
   // Activation tile of step st into ring stage `stage`: each consumer moves
-  // its own rows [64 cw, 64 cw + 64) (no other wave reads them) with 8 DMA
+  // rows [64 cw, 64 cw + 64) (read after the step barrier, also by the other
+  // wave of its row block in the backward) with 8 DMA
   // loads of 8 rows, issued between its MFMAs; lane l lands at byte 16 l of
   // its load's 1 KiB, i.e. row l / 8, physical chunk l % 8.  With 16-byte
   // rows (VEC) the loads are buffer loads whose resource ends at the end of
@@ -406,40 +418,42 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     }
   };
 
-  f32x16_t acc[4][2];    // [column tile nt][row tile mt]: D[n][m]
+  f32x16_t acc[NT][MT];    // [column tile nt][row tile mt]: D[n][m]
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[nt][mt][i] = 0.f;
 
   if (ns > 0) {
-    // fragments of one 16-deep contraction slice, three buffers in the
-    // forward: slice kk of step t lives in slot (t + kk) % 3 (4 slices per
-    // step), read two slices before its MFMAs
-    constexpr int NS = DX ? 2 : 3;
-    u32x4_t wf[NS][4], xf[NS][2];
+    // fragments of one 16-deep contraction slice, three buffers: slice kk of
+    // step t lives in slot (t + kk) % 3 (4 slices per step), read two slices
+    // before its MFMAs.  The backward without 16-byte activation rows, whose
+    // register-path loads need more registers, keeps two.
+    constexpr bool kTwoSlots = DX && !VEC;
+    constexpr int NS = kTwoSlots ? 2 : 3;
+    u32x4_t wf[NS][NT], xf[NS][MT];
     auto read = [&](int t, int kk, auto SLc) {
       constexpr int b = decltype(SLc)::value;
       const uint16_t* sa = sA + (t % NA) * A_STAGE;
       const uint16_t* sw = sW + (t & 1) * G::stage;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int r = cw * 64 + 32 * mt + lr;
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = wr0 + 32 * mt + lr;
         xf[b][mt] = *reinterpret_cast<const u32x4_t*>(sa + r * GBK + a_chunk(r, 2 * kk + lg) * 8);
       }
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         if (DX) {
           const int G16 = lane >> 4, i16 = lane & 15;
           const int row = 16 * kk + 8 * (G16 >> 1) + (i16 >> 2);
-          const int col = 32 * nt + 16 * (G16 & 1) + 4 * (i16 & 3);
+          const int col = wc0 + 32 * nt + 16 * (G16 & 1) + 4 * (i16 & 3);
           const u32x2_t lo = ds_tr16(sw + G::at(row, col));
           const u32x2_t hi = ds_tr16(sw + G::at(row + 4, col));
           wf[b][nt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         } else {
-          wf[b][nt] = *reinterpret_cast<const u32x4_t*>(sw + (32 * nt + lr) * G::ld + 16 * kk + 8 * lg);
+          wf[b][nt] = *reinterpret_cast<const u32x4_t*>(sw + (wc0 + 32 * nt + lr) * G::ld + 16 * kk + 8 * lg);
         }
       }
     };
@@ -449,13 +463,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     auto mma = [&](auto SLc, int kk, int sa, int stage) {
       constexpr int b = decltype(SLc)::value;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[nt][mt] = mfma32<FI::f16>(wf[b][nt], xf[b][mt], acc[nt][mt]);
-        if (nt & 1) {
-          __builtin_amdgcn_sched_barrier(0);
-          fill_a_one(sa, stage, 2 * kk + (nt >> 1));
-          __builtin_amdgcn_sched_barrier(0);
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[nt][mt] = mfma32<FI::f16>(wf[b][nt], xf[b][mt], acc[nt][mt]);
+          const int q = nt * MT + mt;
+          if ((q & 3) == 3) {
+            __builtin_amdgcn_sched_barrier(0);
+            fill_a_one(sa, stage, 2 * kk + (q >> 2));
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     };
@@ -468,7 +485,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     QL_VMCNT(VEC ? 8 : 0);   // step 0's rows have landed
     k_barrier();             // weight stage 0 ready
     read(0, 0, S0{});
-    if constexpr (!DX) read(0, 1, S1{});
+    if constexpr (!kTwoSlots) read(0, 1, S1{});
     // Iteration t (P = t % 3): slices 0-3 of step t from slots P, P+1, P+2,
     // P, with the DMA of step t+2's activation rows (ring stage (t+2) % 3,
     // last read in iteration t-1) spread over the MFMAs; before the barrier,
@@ -503,8 +520,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       __builtin_amdgcn_sched_barrier(0);
       mma(A{}, 3, sa, stage);
     };
-    // The backward (whose transposing reads need more registers) keeps two
-    // slots: slice kk in slot kk % 2, read one slice ahead.
+    // Two slots: slice kk in slot kk % 2, read one slice ahead.
     auto iter2 = [&](int t) {
       const int sa = min(s_begin + t + 2, last), stage = (t + 2) % NA;
       __builtin_amdgcn_sched_barrier(0);
@@ -527,7 +543,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       __builtin_amdgcn_sched_barrier(0);
       mma(S1{}, 3, sa, stage);
     };
-    if constexpr (DX) {
+    if constexpr (kTwoSlots) {
       for (int t = 0; t < ns; ++t) iter2(t);
     } else {
       int t = 0;
@@ -552,24 +568,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
   // issued before the current chunk's MFMAs.
   if (ksplit == 1 && lora.r > 0) {
     const int r = lora.r;
-    int64_t orow[4], mrow[2];
+    int64_t orow[NT], mrow[MT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) orow[nt] = min(o0 + 32 * nt + lr, O - 1);
+    for (int nt = 0; nt < NT; ++nt) orow[nt] = min(o0 + wc0 + 32 * nt + lr, O - 1);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) mrow[mt] = min(m0 + cw * 64 + 32 * mt + lr, M - 1);
+    for (int mt = 0; mt < MT; ++mt) mrow[mt] = min(m0 + wr0 + 32 * mt + lr, M - 1);
     const bool rvec = lora.rs_j == 1 && r % 8 == 0 && (lora.rs_c % 8) == 0 &&
                       (reinterpret_cast<uintptr_t>(lora.R) & 15) == 0;
     const bool lvec = r % 8 == 0 && (reinterpret_cast<uintptr_t>(lora.L) & 15) == 0;
     struct Ops {
-      u32x4_t rb[4];      // R[o][jb .. jb+7], 16-bit pairs
-      f32x4_t lv[2][2];   // L[m][jb .. jb+7]
+      u32x4_t rb[NT];      // R[o][jb .. jb+7], 16-bit pairs
+      f32x4_t lv[MT][2];   // L[m][jb .. jb+7]
     };
     // this lane's ranks of the chunk at j0: jb .. jb+7, jb = j0 + 8 lg
     auto fetch = [&](int j0, Ops& op) {
       const int jb = j0 + 8 * lg;
       const int jc = min(jb, r - 8 > 0 ? r - 8 : 0);   // vector start kept inside the row
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         if (rvec) {
           op.rb[nt] = *reinterpret_cast<const u32x4_t*>(lora.R + orow[nt] * lora.rs_c + jc);
         } else {
@@ -581,7 +597,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
         }
       }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         const float* lp = lora.L + mrow[mt] * r;
         if (lvec) {
           op.lv[mt][0] = *reinterpret_cast<const f32x4_t*>(lp + jc);
@@ -595,9 +611,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     auto apply = [&](int j0, const Ops& op) {
       const int jb = j0 + 8 * lg;
       // ranks past r read a clamped element: zero both factors' share
-      u32x4_t rb[4];
+      u32x4_t rb[NT];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         rb[nt] = op.rb[nt];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -606,7 +622,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
         }
       }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         float tv[8], lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -620,7 +636,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
           alo[e] = pack16x2<FI::f16>(lo[2 * e], lo[2 * e + 1]);
         }
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           acc[nt][mt] = mfma32<FI::f16>(rb[nt], ahi, acc[nt][mt]);
           acc[nt][mt] = mfma32<FI::f16>(rb[nt], alo, acc[nt][mt]);
         }
@@ -640,26 +656,27 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     }
   }
 
-  // ---- stores.  Lane element i of acc[nt][mt] is output row m = m0 + 64 cw +
-  // 32 mt + l % 32, column o = o0 + 32 nt + 8 (i / 4) + 4 (l / 32) + i % 4.
-  // The tile goes through LDS (the activation ring, free once the producers
-  // have drained their last loads) so that each store instruction writes
-  // whole rows: 16 lanes x 16 bytes = 256 contiguous bytes per row, 16-bit
-  // output in one pass of 64 x 128, fp32 in two passes of 64 x 64 columns.
+  // ---- stores.  Lane element i of acc[nt][mt] is output row m = m0 + wr0 +
+  // 32 mt + l % 32, column o = o0 + wc0 + 32 nt + 8 (i / 4) + 4 (l / 32) + i % 4.
+  // The wave tile goes through LDS (the activation ring, free once the
+  // producers have drained their last loads) so that each store instruction
+  // writes whole row pieces of the wave tile (WN / 8 lanes x 16 bytes per
+  // row), 16-bit output in one pass, fp32 in two passes of 64 x 64.
   // Written once: non-temporal stores leave the L2 to the operand tiles the
   // other workgroups reuse.
   if (ns > 0) k_barrier();   // every wave is done with the stages (DMA drained)
   const bool o8 = (O & 7) == 0;   // 8-column pieces are 16-byte aligned in 16-bit rows
   const bool o4 = (O & 3) == 0;   // 4-column pieces are 16-byte aligned in fp32 rows
   if (ksplit == 1 && out16) {
-    // [64 rows][136] 16-bit per consumer (row pitch 272 bytes: the 8-byte
-    // writes of a wave's 32 rows spread over the banks)
-    constexpr int LDO = 136;
-    uint16_t* st = sA + cw * 64 * LDO;
+    // [WM rows][WN + 8] 16-bit per consumer (the row pitch, 4 banks past a
+    // multiple of 64, spreads the 8-byte writes of a wave's 32 rows over the
+    // banks)
+    constexpr int LDO = WN + 8;
+    uint16_t* st = sA + cw * WM * LDO;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const u32x2_t pk = {pack16x2<FI::f16>(acc[nt][mt][4 * q], acc[nt][mt][4 * q + 1]),
@@ -667,12 +684,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
           *reinterpret_cast<u32x2_t*>(st + (32 * mt + lr) * LDO + 32 * nt + 8 * q + 4 * lg) = pk;
         }
     QL_LGKMCNT0();
-    // lane l: row 4 j + l / 16 (j = 0..15), columns 8 (l % 16) .. + 7
+    // lane l: row RPI j + l / LPR, columns 8 (l % LPR) .. + 7
+    constexpr int LPR = WN / 8, RPI = 64 / LPR;
     uint16_t* outp = reinterpret_cast<uint16_t*>(out);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int rl = 4 * j + (lane >> 4), cl = 8 * (lane & 15);
-      const int64_t m = m0 + cw * 64 + rl, o = o0 + cl;
+    for (int j = 0; j < WM / RPI; ++j) {
+      const int rl = RPI * j + lane / LPR, cl = 8 * (lane % LPR);
+      const int64_t m = m0 + wr0 + rl, o = o0 + wc0 + cl;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + rl * LDO + cl);
       if (m < M) {
         uint16_t* dst = outp + m * O + o;
@@ -686,30 +704,34 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       }
     }
   } else {
-    // fp32 (output or split partials): [64 rows][68] floats per consumer and pass
+    // fp32 (output or split partials): [64 rows][68] floats per consumer and
+    // pass; pass p holds column tiles 2 pg, 2 pg + 1 and row tiles 2 pm,
+    // 2 pm + 1 of the wave tile (forward: pg = p, pm = 0; backward: pg = 0,
+    // pm = p)
     constexpr int LDO = 68;
     float* st = reinterpret_cast<float*>(sA) + cw * 64 * LDO;
     float* base = ksplit > 1 ? part + (int64_t)split * M * O : reinterpret_cast<float*>(out);
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
+      const int pg = NT == 4 ? pass : 0, pm = MT == 4 ? pass : 0;
       if (pass) QL_LGKMCNT0();   // (the reads of pass 0 are done before the writes of pass 1)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
         for (int n2 = 0; n2 < 2; ++n2)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int nt = 2 * pass + n2;
+            const int nt = 2 * pg + n2, mt = 2 * pm + m2;
             const f32x4_t v = {acc[nt][mt][4 * q], acc[nt][mt][4 * q + 1], acc[nt][mt][4 * q + 2],
                                acc[nt][mt][4 * q + 3]};
-            *reinterpret_cast<f32x4_t*>(st + (32 * mt + lr) * LDO + 32 * n2 + 8 * q + 4 * lg) = v;
+            *reinterpret_cast<f32x4_t*>(st + (32 * m2 + lr) * LDO + 32 * n2 + 8 * q + 4 * lg) = v;
           }
       QL_LGKMCNT0();
       // lane l: row 4 j + l / 16, columns 4 (l % 16) .. + 3 of this pass's 64
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int rl = 4 * j + (lane >> 4), cl = 4 * (lane & 15);
-        const int64_t m = m0 + cw * 64 + rl, o = o0 + 64 * pass + cl;
+        const int64_t m = m0 + wr0 + 64 * pm + rl, o = o0 + wc0 + 64 * pg + cl;
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(st + rl * LDO + cl);
         if (m < M) {
           float* dst = base + m * O + o;
