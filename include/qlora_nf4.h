@@ -67,7 +67,8 @@ enum { QLORA_F32 = 0, QLORA_BF16 = 1, QLORA_F16 = 2 };
 /* path selection for qlora_linear_fwd / qlora_linear_bwd */
 enum {
   QLORA_PATH_AUTO = 0, /* by m: split-K streaming path for small m, MFMA GEMM otherwise */
-  QLORA_PATH_GEMV = 1, /* force the small-m streaming path (m <= QLORA_GEMV_MAX_M) */
+  QLORA_PATH_GEMV = 1, /* force the small-m streaming path (m <= QLORA_GEMV_MAX_M, else
+                          QLORA_ERR_ARG); in the backward it computes dX */
   QLORA_PATH_GEMM = 2  /* force the tiled MFMA GEMM path */
 };
 
@@ -315,7 +316,13 @@ int qlora_linear_fwd_noalloc(const qlora_nf4 *W, const float *codebook, const ui
  *     dB = scaling * dY^T T              [n x r]  fp32, overwritten
  * X, dY, A and B are in W's compute type.  T = X A^T is taken from T_saved
  * ([m x r] fp32, as written by the forward) or recomputed when T_saved is NULL.  dX may be NULL to skip the input gradient;
- * dA/dB are required when r > 0.
+ * dA/dB are required when r > 0.  path selects how dX is formed: the
+ * streaming kernel (QLORA_PATH_GEMV, or QLORA_PATH_AUTO for m <=
+ * QLORA_GEMV_MAX_M: the packed weight is read once, rows split across
+ * workgroups and their partial sums added in a second pass) or the tiled
+ * MFMA GEMM (QLORA_PATH_GEMM, or AUTO above that m); QLORA_ERR_ARG for
+ * QLORA_PATH_GEMV with m > QLORA_GEMV_MAX_M.  ws: at least
+ * qlora_workspace_bytes(1, m, n, k, r) bytes, which covers every path.
  */
 int qlora_linear_bwd(const qlora_nf4 *W, const float *codebook, const uint16_t *X,
                      const uint16_t *dY, int64_t m, const uint16_t *A, const uint16_t *B,

@@ -93,6 +93,19 @@ int plan_dx_split(int64_t m, int64_t n, int64_t k) {
   return tiles >= 192 ? 1 : (int)std::min<int64_t>(cap, cdiv(256, tiles));
 }
 
+// input-gradient path: the streaming kernel for small m (or when forced),
+// else the MFMA GEMM; the number of contraction splits of either
+struct DxPlan {
+  bool gemv;
+  int nsplit;
+};
+DxPlan plan_dx(int64_t m, int64_t n, int64_t k, int path) {
+  DxPlan p;
+  p.gemv = path == QLORA_PATH_GEMV || (path == QLORA_PATH_AUTO && m <= QLORA_GEMV_MAX_M);
+  p.nsplit = p.gemv ? ql::gemv_dx_splits(n, k) : plan_dx_split(m, n, k);
+  return p;
+}
+
 // adapter-gradient splits over the rows (dA over k columns and dB over n in
 // one launch): enough workgroups (tiles of 128 columns x 32 or 64 ranks, times
 // the splits) to fill the chip twice over, each split at least one 64-row
@@ -129,8 +142,14 @@ BwdWs bwd_ws(int64_t m, int64_t n, int64_t k, int r) {
   w.t_off = w.u_off + up16(sizeof(float) * (size_t)(m * r));
   w.bt_off = w.t_off + up16(sizeof(float) * (size_t)(m * r));
   w.dx_off = w.bt_off + up16(sizeof(uint16_t) * (size_t)(r * n));
-  const int ns = plan_dx_split(m, n, k);
-  w.wg_off = w.dx_off + up16(ns > 1 ? sizeof(float) * (size_t)ns * m * k : 0);
+  // the input gradient's split partials, for whichever path runs
+  size_t dxp = 0;
+  for (int path : {QLORA_PATH_GEMV, QLORA_PATH_GEMM}) {
+    if (path == QLORA_PATH_GEMV && m > QLORA_GEMV_MAX_M) continue;
+    const DxPlan p = plan_dx(m, n, k, path);
+    if (p.nsplit > 1) dxp = std::max(dxp, sizeof(float) * (size_t)p.nsplit * m * k);
+  }
+  w.wg_off = w.dx_off + up16(dxp);
   // the last region holds the adapter-gradient split partials, and before
   // those run the rank projections' split partials (U over n, T over k)
   size_t wg = 0;
@@ -549,6 +568,7 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
   if (r > 0 && (!A || !B || !dA || !dB || !X)) return QLORA_ERR_NULL;
   if (!out_dtype_ok(W, dx_dtype)) return QLORA_ERR_DTYPE;
   if (path < QLORA_PATH_AUTO || path > QLORA_PATH_GEMM) return QLORA_ERR_ARG;
+  if (path == QLORA_PATH_GEMV && m > QLORA_GEMV_MAX_M) return QLORA_ERR_ARG;
   if (!aligned(dY, 16) || (dX && !aligned(dX, 16)) || (X && !aligned(X, 16)))
     return QLORA_ERR_ALIGN;
   if (r > 0 && (!aligned(A, 16) || !aligned(B, 2) || !aligned(dA, 4) || !aligned(dB, 4) ||
@@ -582,12 +602,14 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
     }
   }
   if (dX) {
-    const int ns = plan_dx_split(m, n, k);
+    const DxPlan p = plan_dx(m, n, k, path);
+    const int ns = p.nsplit;
     ql::LoraTerm lora{U, A, 1, k, r, scaling};
     float* part = ns > 1 ? (float*)(wsb + L.dx_off) : nullptr;
     const bool bf = dx_dtype != QLORA_F32;   // a 16-bit output of the compute type
-    if (ql::launch_gemm_dx(view(W), codebook, dY, m, lora, dX, bf, part, ns, s) != hipSuccess)
-      return QLORA_ERR_HIP;
+    const hipError_t e = p.gemv ? ql::launch_gemv_dx(view(W), codebook, dY, m, lora, dX, bf, part, ns, s)
+                                : ql::launch_gemm_dx(view(W), codebook, dY, m, lora, dX, bf, part, ns, s);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
     if (ns > 1 && ql::launch_reduce(part, ns, m, k, lora, dX, bf, is_f16(W), s) != hipSuccess)
       return QLORA_ERR_HIP;
   }

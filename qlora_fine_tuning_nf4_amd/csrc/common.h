@@ -257,6 +257,24 @@ QL_DEV u32x4_t decode_q8x8(uint32_t w0, uint32_t w1, float d) {
   return u32x4_t{a[0], a[1], b[0], b[1]};
 }
 
+// ds_read_b64_tr_b16 of an LDS address: in each 16-lane group, lane i gets
+// 4 consecutive 16-bit values of column i of the 4 x 16 block whose rows the
+// group's lanes address (lane j: row j / 4, columns 4 (j % 4) .. + 3).
+QL_DEV u32x2_t ds_tr16(const uint16_t* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((QL_LDS s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// Eight 16-bit elements row[c .. c+7] as 4 packed pairs: one 16-byte load
+// (vec: in range and 16-byte aligned), else element loads with zeros past C.
+QL_DEV u32x4_t load_act8(const uint16_t* row, int64_t c, int64_t C, bool vec) {
+  if (vec) return *reinterpret_cast<const u32x4_t*>(row + c);
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = (c + e < C) ? row[c + e] : 0u;
+  return u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+}
+
 // fp16 bits -> fp32 (exact)
 QL_DEV float half_bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);

@@ -79,20 +79,6 @@ struct Geo {
   static QL_DEV int at(int r, int c) { return r * ld + c; }
 };
 
-QL_DEV u32x4_t load_act8(const uint16_t* row, int64_t c, int64_t C, bool vec) {
-  if (vec) return *reinterpret_cast<const u32x4_t*>(row + c);
-  uint32_t h[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) h[e] = (c + e < C) ? row[c + e] : 0u;
-  return u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
-}
-
-QL_DEV u32x2_t ds_tr16(const uint16_t* p) {
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4_t*)(p));
-  return __builtin_bit_cast(u32x2_t, v);
-}
-
 // Logical tile of this workgroup: consecutive logical tiles (row-tile major)
 // go to the same XCD.
 QL_DEV int64_t logical_tile(int64_t id, int64_t total) {

@@ -15,6 +15,7 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace ql {
@@ -343,6 +344,235 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
   }
 }
 
+// Streaming input gradient, small M: dX[m][k] = sum_n dY[m][n] deq(W)[n][k]
+// (www.cf-1.com/news/5705389 §2.1: the gradient passes through the frozen
+// quantized matrix).  A workgroup of 4 waves owns one 64-wide k-block kb and
+// one split of the rows; per iteration wave w decodes rows [nb + 64 w, +64)
+// at kb, one 64-weight unit per lane (lane = row), into its own LDS tile
+// [64 n][72], and reads it back with ds_read_b64_tr_b16, which hands each
+// lane 4 consecutive rows of one column: the MFMA 16x16x32 operand
+// W^T[16 k][32 n].  The contraction over n runs inside the wave (no barrier
+// until the end); the four waves' sums are added through LDS once, and the
+// splits over n through k_reduce.  Per lane and iteration the loads are the
+// unit's code bytes, its scale entry and the dY fragments of its 64 rows
+// (dY[m][nb .. +64), 16-byte pieces, from L2): a three-deep ring keeps the
+// loads of two iterations in flight.
+constexpr int GDX_LDW = 72;   // LDS pitch of a wave tile (16-bit elements)
+
+template <int FMT, int MT>
+struct GdxRaw {
+  u32x4_t c[FMT == kFmtQ8 ? 4 : 2];
+  uint32_t qbyte;
+  float step, zp;
+  u32x4_t y[MT][2];   // dY fragments: row tile mt, row half h of the 64
+};
+
+template <int MT, int FMT>
+__global__ __launch_bounds__(256) void k_gemv_dx(const uint16_t* __restrict__ dY, Nf4View w,
+                                                 const float* __restrict__ codebook, int64_t M,
+                                                 LoraTerm lora, void* __restrict__ out, int out16,
+                                                 float* __restrict__ part, int iters) {
+  __shared__ __attribute__((aligned(16))) uint16_t sT[4 * 64 * GDX_LDW];
+  using FI = FmtInfo<FMT>;
+  constexpr int CB = FI::code_bytes, NC = CB / 16, BS = FI::block;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t N = w.n, K = w.k, nkb = K / kBlock, nkb2 = nkb / 2;
+  const int64_t kb = blockIdx.x;
+  const int split = blockIdx.y, nsplit = gridDim.y;
+  const int64_t n_begin = (int64_t)split * iters * 256;          // first row of the split
+  const int i16 = lane & 15, G16 = lane >> 4;
+  uint16_t* const sw = sT + wave * 64 * GDX_LDW;
+
+  float lv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lv[i] = FI::nf4 ? gptr(codebook)[i] : 0.f;
+
+  const int64_t nsc = N * K / BS;
+  const auto step_rsrc = buf_rsrc(w.step, (uint32_t)(((nsc + kGroup - 1) / kGroup) * 4));
+  const bool yvec = (N & 7) == 0;   // 16-byte dY pieces inside the rows
+  const auto y_rsrc = buf_rsrc(dY, (uint32_t)(M * N * 2));
+  // Unit (n, kb) sits at storage position gg * nkb + kb * R + (n - gg), gg =
+  // n & ~15, R = min(16, N - gg); positions are taken relative to the first
+  // row nb of the wave's 64 (a multiple of 16).  Rows past N get an offset
+  // past any resource: the hardware returns zeros, hence a zero scale.
+  constexpr uint32_t kOut = 0x80000000u;
+  auto load = [&](int it, GdxRaw<FMT, MT>& u) {
+    const int64_t nb = n_begin + (int64_t)min(it, iters - 1) * 256 + 64 * wave;
+    const int64_t n = nb + lane, gg = n & ~int64_t(15);
+    const bool ok = n < N;
+    const int64_t R = min(int64_t(16), N - gg);
+    const uint32_t rel = (uint32_t)((gg - nb) * nkb + kb * R + (n - gg));
+    const int64_t base = nb * nkb;   // position of (nb, 0)
+    const auto rc = buf_rsrc(w.codes + base * CB);
+    const uint32_t co = ok ? rel * CB : kOut;
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+      u.c[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, co + 16 * j, 0, 0));
+    if constexpr (FI::nf4) {
+      // scale entry: block 64 at the position, block 32 the pair at 2p, 2p+1,
+      // block 128 at (n, kb / 2) in the row-group order over k/128 columns
+      const int64_t sbase = BS == 64 ? base : (BS == 32 ? 2 * base : nb * nkb2);
+      const uint32_t srel = BS == 64 ? rel : (BS == 32 ? 2 * rel
+                                              : (uint32_t)((gg - nb) * nkb2 + (kb >> 1) * R + (n - gg)));
+      if constexpr (FI::dq) {
+        const auto rq = buf_rsrc(w.qscale + sbase);
+        u.qbyte = BS == 32 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rq, ok ? srel : kOut, 0, 0)
+                           : (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rq, ok ? srel : kOut, 0, 0);
+        // flat block index of the unit's (first) block, for its group constant
+        const int64_t b = BS == 64 ? n * nkb + kb : (BS == 32 ? 2 * (n * nkb + kb) : n * nkb2 + (kb >> 1));
+        u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               step_rsrc, ok ? (uint32_t)(b >> 8) * 4 : kOut, 0, 0));
+      } else {
+        const auto rs = buf_rsrc(w.step + sbase);
+        u.qbyte = 1u;
+        u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? srel * 4 : kOut, 0, 0));
+        if constexpr (BS == 32)
+          u.zp = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? srel * 4 + 4 : kOut, 0, 0));
+      }
+    } else if constexpr (FMT == kFmtU4) {
+      const auto prs = buf_rsrc(w.step + 2 * base);
+      u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, ok ? rel * 8 : kOut, 0, 0));
+      u.zp = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, ok ? rel * 8 + 4 : kOut, 0, 0));
+    } else {
+      u.qbyte = __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(w.qscale + 4 * base), ok ? rel * 4 : kOut, 0, 0);
+    }
+    // dY fragments: lane (i16, G16) holds dY[16 mt + i16][nb + 32 h + 8 G16 .. +7]
+    // (rows past M re-read row M-1, whose products are dropped; columns past
+    // N are zeros)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int64_t m = min((int64_t)(16 * mt + i16), M - 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t c = nb + 32 * h + 8 * G16;
+        if (yvec) {
+          u.y[mt][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       y_rsrc, c < N ? (uint32_t)((m * N + c) * 2) : kOut, 0, 0));
+        } else {
+          u.y[mt][h] = load_act8(dY + m * N, c, N, false);
+        }
+      }
+    }
+  };
+  // vector-memory loads per iteration (the uint4 pair and the block-32
+  // absmax pair counted once: the backend may merge them; a count below the
+  // real one only waits longer)
+  constexpr int kLoads = NC + (FI::dq ? 2 : 1) + 2 * MT;
+
+  f32x4_t acc[4][MT];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[kt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const GdxRaw<FMT, MT>& u) {
+    // decode the lane's unit into row `lane` of the wave tile: word i holds
+    // elements 8i .. 8i+7
+    auto put = [&](int i, const u32x4_t& v) {
+      *reinterpret_cast<u32x4_t*>(sw + lane * GDX_LDW + 8 * i) = v;
+    };
+    if constexpr (FMT == kFmtQ8) {
+      const float d0 = half_bits_to_float(u.qbyte & 0xFFFFu), d1 = half_bits_to_float(u.qbyte >> 16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const u32x4_t& cw = u.c[i >> 1];
+        put(i, decode_q8x8(cw[2 * (i & 1)], cw[2 * (i & 1) + 1], i < 4 ? d0 : d1));
+      }
+    } else {
+      float lvu[16];
+      float scr;
+      if constexpr (FMT == kFmtU4) {
+        const int zp = (int)u.zp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lvu[i] = (float)(i - zp);
+        scr = u.step;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lvu[i] = lv[i];
+        scr = (float)(u.qbyte & 0xFFu) * u.step;
+      }
+      const Lut t = make_lut<FI::f16>(lvu, scr);
+      if constexpr (BS == 32) {
+        const float scr1 = FI::dq ? (float)(u.qbyte >> 8) * u.step : u.zp;
+        const Lut t1 = make_lut(lvu, scr1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) put(i, decode8(i < 4 ? t : t1, u.c[i >> 2][i & 3]));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) put(i, decode8(t, u.c[i >> 2][i & 3]));
+      }
+    }
+    // contraction over the 64 rows: row half h, k tile kt.  (The LDS
+    // operations of a wave execute in order: these reads see the writes
+    // above, and the next iteration's writes follow these reads.)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const uint16_t* p = sw + (32 * h + 8 * G16 + (i16 >> 2)) * GDX_LDW + 16 * kt + 4 * (i16 & 3);
+        const u32x2_t lo = ds_tr16(p), hi = ds_tr16(p + 4 * GDX_LDW);
+        const u32x4_t a = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[kt][mt] = mfma16x16x32<FI::f16>(a, u.y[mt][h], acc[kt][mt]);
+      }
+    }
+  };
+
+  {
+    GdxRaw<FMT, MT> rw[3];
+    load(0, rw[0]);
+    load(1, rw[1]);
+    auto step = [&](int it, auto PHc) {
+      constexpr int PH = decltype(PHc)::value;
+      load(it + 2, rw[(PH + 2) % 3]);
+      QL_VMCNT(2 * kLoads);   // iteration it's loads have landed
+      compute(rw[PH]);
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    int it = 0;
+    for (; it + 2 < iters; it += 3) {
+      step(it, P0{});
+      step(it + 1, P1{});
+      step(it + 2, P2{});
+    }
+    if (it < iters) step(it, P0{});
+    if (it + 1 < iters) step(it + 1, P1{});
+  }
+
+  // the four waves' sums through LDS (the tiles are free once every wave is
+  // past its last reads): red[wave][kt][mt][lane][e]
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(sT);
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      *reinterpret_cast<f32x4_t*>(red + (((wave * 4 + kt) * MT + mt) * 64 + lane) * 4) = acc[kt][mt];
+  __syncthreads();
+  // thread t: outputs idx = t + 256 j over (m, k) = (idx / 64, idx % 64)
+#pragma unroll
+  for (int j = 0; j < 4 * MT; ++j) {
+    const int idx = tid + 256 * j;
+    const int m = idx >> 6, kl = idx & 63;
+    const int kt = kl >> 4, e = kl & 3, ln = 16 * ((kl & 15) >> 2) + (m & 15), mt = m >> 4;
+    float v = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) v += red[(((wv * 4 + kt) * MT + mt) * 64 + ln) * 4 + e];
+    const int64_t k = kb * kBlock + kl;
+    if (m < M) {
+      if (nsplit > 1) {
+        part[((int64_t)split * M + m) * K + k] = v;
+      } else {
+        if (lora.r > 0) v += lora.scaling * lora_dot<FI::f16>(lora, m, k);
+        store_out<FI::f16>(out, out16, m * K + k, v);
+      }
+    }
+  }
+}
+
 template <bool F16>
 __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, int nsplit, int64_t M,
                                                 int64_t C, LoraTerm lora, void* __restrict__ out,
@@ -400,6 +630,41 @@ hipError_t launch_gemv_grouped(const GemvJob* jobs, int njobs, int64_t row_group
   const dim3 grid((unsigned)row_groups, 1);
   const GemvJob none{};
   gemv_launch_m<true>(M, fmt, grid, s, none, jobs, njobs, codebook, 1, (int)max_quads);
+  return hipGetLastError();
+}
+
+template <int MT>
+static void gemv_dx_launch(int fmt, dim3 grid, hipStream_t s, const uint16_t* dY, const Nf4View& w,
+                           const float* codebook, int64_t M, const LoraTerm& lora, void* out,
+                           int out16, float* part, int iters) {
+#define QL_GDX(F)                                                                             \
+  hipLaunchKernelGGL((k_gemv_dx<MT, F>), grid, dim3(256), 0, s, dY, w, codebook, M, lora, out, \
+                     out16, part, iters)
+  switch (fmt) {
+    case kFmtNf4Dq: QL_GDX(kFmtNf4Dq); break;
+    case kFmtNf4: QL_GDX(kFmtNf4); break;
+    case kFmtU4: QL_GDX(kFmtU4); break;
+    case kFmtQ8: QL_GDX(kFmtQ8); break;
+    case kFmtNf4Dq32: QL_GDX(kFmtNf4Dq32); break;
+    case kFmtNf4_32: QL_GDX(kFmtNf4_32); break;
+    case kFmtNf4Dq128: QL_GDX(kFmtNf4Dq128); break;
+    case kFmtNf4DqF16: QL_GDX(kFmtNf4DqF16); break;
+    default: QL_GDX(kFmtNf4_128); break;
+  }
+#undef QL_GDX
+}
+
+hipError_t launch_gemv_dx(const Nf4View& w, const float* codebook, const uint16_t* dY, int64_t M,
+                          const LoraTerm& lora, void* dX, bool dx16, float* part, int nsplit,
+                          hipStream_t s) {
+  // M <= 32 and nsplit = gemv_dx_splits(M, n, k), checked by the caller
+  const int64_t niter = (w.n + 255) / 256;
+  const int iters = (int)((niter + nsplit - 1) / nsplit);
+  const dim3 grid((unsigned)(w.k / kBlock), (unsigned)nsplit);
+  if (M <= 16)
+    gemv_dx_launch<1>(w.fmt, grid, s, dY, w, codebook, M, lora, dX, (int)dx16, part, iters);
+  else
+    gemv_dx_launch<2>(w.fmt, grid, s, dY, w, codebook, M, lora, dX, (int)dx16, part, iters);
   return hipGetLastError();
 }
 

@@ -85,6 +85,23 @@ hipError_t launch_gemv_grouped(const GemvJob* jobs, int njobs, int64_t row_group
 hipError_t launch_gemm_dx(const Nf4View& w, const float* codebook, const uint16_t* dY, int64_t M,
                           const LoraTerm& lora, void* dX, bool dx16, float* part, int nsplit,
                           hipStream_t s);
+// Small-M input gradient (M <= 32): dX = dY deq(W) (+ LoRA term) with the
+// weight streamed once.  Workgroups run over the k/64 blocks x nsplit splits
+// of the rows; nsplit must be gemv_dx_splits(w.n, w.k), and when it is above
+// 1, `part` holds nsplit * M * w.k floats for launch_reduce (which then adds
+// the LoRA term).
+inline int gemv_dx_splits(int64_t N, int64_t K) {
+  // about 512 workgroups (one per k-block and split), each split a whole
+  // number of 256-row iterations and none empty
+  const int64_t nkb = K / 64, niter = (N + 255) / 256;   // 64-wide k-blocks
+  int64_t ns0 = (512 + nkb - 1) / nkb;
+  ns0 = ns0 < 1 ? 1 : (ns0 > niter ? niter : ns0);
+  const int64_t iters = (niter + ns0 - 1) / ns0;
+  return (int)((niter + iters - 1) / iters);
+}
+hipError_t launch_gemv_dx(const Nf4View& w, const float* codebook, const uint16_t* dY, int64_t M,
+                          const LoraTerm& lora, void* dX, bool dx16, float* part, int nsplit,
+                          hipStream_t s);
 // out[m][c] = sum_s part[s][m][c] + LoRA term, for C columns (R and a 16-bit
 // out in fp16 when f16, else bf16).
 hipError_t launch_reduce(const float* part, int nsplit, int64_t M, int64_t C,

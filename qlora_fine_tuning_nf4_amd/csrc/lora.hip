@@ -333,12 +333,6 @@ __global__ void k_transpose_bf16(const uint16_t* __restrict__ Q, int N, int r,
   if (n < N) Qt[(int64_t)j * N + n] = Q[(int64_t)n * r + j];
 }
 
-QL_DEV u32x2_t ds_tr16(const uint16_t* p) {
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4_t*)(p));
-  return __builtin_bit_cast(u32x2_t, v);
-}
-
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 template <bool F16>

@@ -137,6 +137,19 @@ hipError_t launch_gemm_dx(const Nf4View& w, const float*, const uint16_t* dY, in
   check_lora(lora, M, w.k);
   return hipSuccess;
 }
+hipError_t launch_gemv_dx(const Nf4View& w, const float*, const uint16_t* dY, int64_t M,
+                          const LoraTerm& lora, void* dX, bool dx16, float* part, int nsplit,
+                          hipStream_t) {
+  ++g_launches;
+  check_view(w);
+  CHECK(M >= 1 && M <= 32);
+  CHECK(nsplit == gemv_dx_splits(w.n, w.k));
+  in_bounds(dY, 2.0 * M * w.n, "dY");
+  if (nsplit > 1) in_bounds(part, 4.0 * nsplit * M * w.k, "gemv dx partials");
+  else in_bounds(dX, (dx16 ? 2.0 : 4.0) * M * w.k, "dX");
+  check_lora(lora, M, w.k);
+  return hipSuccess;
+}
 hipError_t launch_reduce(const float* part, int nsplit, int64_t M, int64_t C, const LoraTerm& lora,
                          void* out, bool out16, bool, hipStream_t) {
   ++g_launches;
@@ -251,11 +264,12 @@ void run_fwd_bwd(int64_t m, int64_t n, int64_t k, int r, int path, bool save_t, 
     }
     const int e2 = qlora_linear_bwd(&w, cb, X, dY, m, A, B, r, 2.0f, T, dX, dt, dA, dB, wsb, wb, path,
                                     nullptr);
-    if (e2 != QLORA_OK && !(path == QLORA_PATH_GEMV && e2 == QLORA_ERR_ARG))
+    const bool bwd_refused = path == QLORA_PATH_GEMV && m > QLORA_GEMV_MAX_M;
+    if (e2 != (bwd_refused ? QLORA_ERR_ARG : QLORA_OK))
       std::fprintf(stderr, "bwd m=%ld n=%ld k=%ld r=%d path=%d -> %d\n", (long)m, (long)n, (long)k, r, path, e2);
-    CHECK(e2 == QLORA_OK || (path == QLORA_PATH_GEMV && e2 == QLORA_ERR_ARG));
+    CHECK(e2 == (bwd_refused ? QLORA_ERR_ARG : QLORA_OK));
     // a workspace one byte short is refused before any launch
-    if (wb > 0) {
+    if (wb > 0 && !bwd_refused) {
       const int before = g_launches;
       CHECK(qlora_linear_bwd(&w, cb, X, dY, m, A, B, r, 2.0f, T, dX, dt, dA, dB, wsb, wb - 1, path,
                              nullptr) == QLORA_ERR_WORKSPACE);
