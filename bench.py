@@ -13,6 +13,11 @@ backward 2MNK + 2Mr(2K+2N) flops; bytes = packed weight once per pass plus
 every activation, gradient and adapter tensor at its dtype.
 
 Other workloads (--workload), each printing its own line of the same form:
+  single      one 4096x4096 linear at M = 16 tokens with LoRA r = 8, alpha =
+              16, fwd + bwd on the small-m streaming paths, from a cold cache
+              (2 GiB written before each step, the launches queued behind it);
+              effective GB/s against HBM peak, the streaming input gradient
+              as the roofline kernel.
   decode      the seven projections stacked for 32 layers (6.48e9 NF4 params,
               3.35 GB packed), forward only at M = 1 (also 4 and 16 in
               "per_m"), LoRA r = 8, alpha = 16 on q, k, v, o; one grouped
@@ -317,6 +322,150 @@ def run_layer7b(args):
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens or M_TOKENS)
     return out
 
+
+
+SINGLE_M = 16
+SINGLE_WORKLOAD = ("single linear 4096x4096 (N(0,0.02) weight, NF4 block 64 + double quant), "
+                   "M=16 tokens, LoRA r=8 alpha=16, fwd (Y, T) + bwd (dX, dA, dB), "
+                   "cold cache (2 GiB written between steps)")
+
+
+def run_single(args):
+    """Single 4096x4096 linear at M = 16 with LoRA r = 8, forward + backward,
+    each step starting from a cold cache: a 2 GiB fill runs before each step
+    and the step's launches (the forward and the backward, on the small-m
+    streaming paths) are enqueued behind it, so the timed interval holds the
+    step's kernels back to back and no host overhead."""
+    import torch
+
+    import synth
+    from qlora_fine_tuning_nf4_amd import binding as QB
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cb = QB.device_codebook(dev)
+    M, N, K, r = SINGLE_M, 4096, 4096, RANK
+    s = ALPHA / RANK
+    W = dnorm((N, K), 0.02, synth.tensor_seed(1, 0), device=dev)
+    q = QB.qlora_quantize(W, cb, double_quant=DQ, block=BLOCK)
+    del W
+    X = dnorm((M, K), 1.0, synth.tensor_seed(1, 1), device=dev)
+    A = dnorm((r, K), 0.01, synth.tensor_seed(1, 2), device=dev)
+    Bm = dnorm((N, r), 0.01, synth.tensor_seed(1, 3), device=dev)
+    dY = dnorm((M, N), 1.0, synth.tensor_seed(1, 4), device=dev)
+    Y = torch.empty((M, N), dtype=DT, device=dev)
+    T = torch.empty((M, r), dtype=torch.float32, device=dev)
+    dX = torch.empty((M, K), dtype=DT, device=dev)
+    dA = torch.empty((r, K), dtype=torch.float32, device=dev)
+    dB = torch.empty((N, r), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(QB.qlora_workspace_bytes(0, M, N, K, r), QB.qlora_workspace_bytes(1, M, N, K, r), 16),
+                     dtype=torch.uint8, device=dev)
+    dX0 = torch.empty((M, K), dtype=DT, device=dev)
+    ws0 = torch.empty(max(QB.qlora_workspace_bytes(1, M, N, K, 0), 16), dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+
+    def step():
+        QB.qlora_linear_fwd(q, cb, X, A, Bm, s, y_dtype=DT, out=Y, T_out=T, workspace=ws)
+        QB.qlora_linear_bwd(q, cb, X, dY, A, Bm, s, T=T, dx_dtype=DT, dX_out=dX, dA_out=dA, dB_out=dB,
+                            workspace=ws)
+
+    def dx_only():   # the streaming input gradient alone (r = 0): its kernel and split reduce
+        QB.qlora_linear_bwd(q, cb, None, dY, dx_dtype=DT, dX_out=dX0, workspace=ws0)
+
+    def cold_times(fn, n, warmup):
+        """GPU time of fn after a 2 GiB fill: the host enqueues the events and
+        fn's launches while the fill runs (host_us says how long that took),
+        so the interval holds fn's kernels back to back."""
+        out, host = [], []
+        for i in range(warmup + n):
+            flush.fill_(i & 255)
+            e0, e1 = _events()
+            h0 = time.perf_counter()
+            e0.record()
+            fn()
+            e1.record()
+            h1 = time.perf_counter()
+            torch.cuda.synchronize()
+            if i >= warmup:
+                out.append(e0.elapsed_time(e1))
+                host.append((h1 - h0) * 1e6)
+        return out, statistics.median(host)
+
+    step(); dx_only()
+    torch.cuda.synchronize()
+    flush.fill_(2)
+    f0, f1 = _events()
+    f0.record()
+    flush.fill_(1)
+    f1.record()
+    torch.cuda.synchronize()
+    fill_us = f0.elapsed_time(f1) * 1e3
+    t0 = time.perf_counter()
+    step_ms, host_step = cold_times(step, args.steps, args.warmup)
+    wall_s = time.perf_counter() - t0
+    dx_ms, host_dx = cold_times(dx_only, args.steps, args.warmup)
+    ms = statistics.median(step_ms)
+    flops = flops_fwd(M, N, K, r) + flops_bwd(M, N, K, r)
+    nbytes = step_bytes(M, N, K, r)
+    dx_bytes = packed_bytes(N, K) + 2 * M * N + 2 * M * K
+    dx_us = statistics.median(dx_ms) * 1e3
+    achieved = dx_bytes / (dx_us * 1e-6) / 1e9
+    out = {
+        "metric": METRIC, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "us_per_step": round(ms * 1e3, 2), "tflops": round(flops / (ms * 1e-3) / 1e12, 4),
+        "wall_ms_per_step_incl_flush": round(wall_s * 1e3 / (args.steps + args.warmup), 4),
+        "host_enqueue_us": {"step": round(host_step, 1), "dx": round(host_dx, 1),
+                            "fill_us": round(fill_us, 1),
+                            "covered_by_fill": bool(max(host_step, host_dx) < fill_us)},
+        "gpu_step_ms": _spread(step_ms),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt_name(),
+        "data": "synthetic (seeded N(0,0.02) weight quantized to NF4+DQ, N(0,1) X and dY, N(0,0.01) A, B)",
+        "config": {"workload": SINGLE_WORKLOAD, "M": M, "N": N, "K": K, "r": r, "alpha": ALPHA,
+                   "double_quant": DQ, "nf4_block": BLOCK, "path": "auto (small-m streaming)",
+                   "parallelism": "none (1 GPU)"},
+        "algorithmic_bytes_per_step": nbytes,
+        "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "k_gemv_dx", "interval": "k_gemv_dx + k_reduce (its split sum)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "avg_launch_us": round(dx_us, 2),
+                     "bytes_per_launch": dx_bytes, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_single()
+    return out
+
+
+def cpu_baseline_single():
+    """The oracle as it stands on the same single-linear step (dequantize,
+    forward, dequantize, backward in float64 numpy), repeated for about 10 s;
+    then with one thread."""
+    import synth
+    from oracle import linear as olin
+    from oracle import nf4 as onf4
+
+    lv, mid = onf4.codebook()
+    M, N, K, r = SINGLE_M, 4096, 4096, RANK
+    W = synth.normal_bf16((N, K), 0.02, synth.tensor_seed(1, 0))
+    codes, qs, st = onf4.quantize(W, mid)
+    X = synth.normal_bf16((M, K), 1.0, synth.tensor_seed(1, 1))
+    A = synth.normal_bf16((r, K), 0.01, synth.tensor_seed(1, 2))
+    B = synth.normal_bf16((N, r), 0.01, synth.tensor_seed(1, 3))
+    dY = synth.normal_bf16((M, N), 1.0, synth.tensor_seed(1, 4))
+    nbytes = step_bytes(M, N, K, r)
+
+    def run(budget_s):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            Wd = onf4.dequantize(codes, qs, st, lv).reshape(N, K)
+            olin.forward(Wd, X, A, B, ALPHA / RANK)
+            Wd = onf4.dequantize(codes, qs, st, lv).reshape(N, K)
+            olin.backward(Wd, X, dY, A, B, ALPHA / RANK)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                return n * nbytes, el, f"{n} steps of the same workload"
+    return with_cpu_figures(run, "GB/s", 1e9, 10.0, 5.0)
 
 
 def _events():
@@ -735,7 +884,7 @@ def main():
                     help="tokens of the oracle's CPU baseline (default: all 2048 of layer7b, "
                          "128 of the 4096 of layer3.8b)")
     ap.add_argument("--workload", default="layer7b",
-                    choices=["layer7b", "decode", "quantize70b", "layer70b", "layer3.8b"])
+                    choices=["layer7b", "single", "decode", "quantize70b", "layer70b", "layer3.8b"])
     ap.add_argument("--format", default="q8_0", choices=["q8_0", "u4_asym", "nf4"],
                     help="weight block format of the layer3.8b workload")
     ap.add_argument("--nf4-block", type=int, default=64, choices=[32, 64, 128],
@@ -763,7 +912,7 @@ def main():
     if BLOCK != 64:
         args.no_cpu_baseline = True
 
-    run = {"layer7b": run_layer7b, "decode": run_decode, "quantize70b": run_quantize70b,
+    run = {"layer7b": run_layer7b, "single": run_single, "decode": run_decode, "quantize70b": run_quantize70b,
            "layer70b": run_layer70b, "layer3.8b": run_layer38}[args.workload]
     out = run(args)
     print(json.dumps(out), flush=True)
