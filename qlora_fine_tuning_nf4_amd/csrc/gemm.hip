@@ -104,6 +104,16 @@ QL_DEV void k_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The same barrier with this wave's last 4 LDS operations still allowed in
+// flight (LDS operations complete in order, and the producer loop issues no
+// other operation counted by lgkmcnt).
+QL_DEV void k_barrier_lgkm4() {
+  __builtin_amdgcn_s_waitcnt(0xC47F);   // lgkmcnt(4), vmcnt and expcnt not waited
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 
 template <bool DX, bool VEC, int FMT>
 __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ act, Nf4View w,
@@ -114,7 +124,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
   using G = Geo<DX>;
   using FI = FmtInfo<FMT>;
   extern __shared__ __attribute__((aligned(16))) uint16_t sA[];   // [NA][GBM rows][GBK], swizzled
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2 * G::stage];   // decoded weight stages
+  __shared__ __attribute__((aligned(16))) uint16_t sW[3 * G::stage];   // decoded weight stages
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -301,37 +311,61 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     };
 
     if (ns > 0) {
-      // prologue: codes of the first three steps, decoded weight of the first
-      WRaw rw[3];   // codes of step s in rw[(s - s_begin) % 3]
-      load_w(s_begin, rw[0]);
-      load_w(min(s_begin + 1, last), rw[1]);
-      load_w(min(s_begin + 2, last), rw[2]);
-      QL_VMCNT(2 * kWLoads);
+      // Weight stages: step s in stage s % 3, decoded two steps ahead, so
+      // that a step's LDS writes have a whole iteration to complete (they
+      // queue behind the consumers' fragment reads) before the barrier that
+      // hands the step over.  Codes ring of kRing steps: the codes of step s
+      // in rw[(s - s_begin) % kRing], loaded kRing - 2 iterations before
+      // their decode (under full load the loads take more than two steps to
+      // return).
+      constexpr int kRing = 6;
+      WRaw rw[kRing];
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) load_w(min(s_begin + j, last), rw[j]);
+      QL_VMCNT((kRing - 1) * kWLoads);
       decode_to(rw[0], 0);
+      QL_VMCNT((kRing - 2) * kWLoads);
+      if (ns > 1) decode_to(rw[1], 1);
       k_barrier();
-      // Iteration t (between barriers t and t+1): codes of step t+3 into the
-      // ring slot of step t (decoded in the previous iteration), then, once
-      // the codes of t+1 have landed (everything issued before this
-      // iteration), decode step t+1 into weight stage (t+1) % 2 (last read in
-      // iteration t-1).  Steps past the end re-load the last one (never read).
+      // Iteration t (between barriers t and t+1): codes of step t+kRing into
+      // the ring slot of step t (decoded two iterations ago), then, once the
+      // codes of step t+2 have landed, decode it into stage (t+2) % 3 (the
+      // stage of step t-1, whose reads finished before barrier t); at the
+      // barrier only this iteration's 4 writes may still be in flight (step
+      // t+2 is read after barrier t+2).  Steps past the end re-load the last
+      // one (never decoded).  (Fenced: left free, the scheduler pulls the
+      // next iterations' scale arithmetic into this decode, which then waits
+      // for their loads.)
       auto iter = [&](int t, auto PHc) {
-        constexpr int PH = decltype(PHc)::value;   // t % 3
-        load_w(min(s_begin + t + 3, last), rw[PH]);
-        QL_VMCNT(2 * kWLoads);   // the codes of t+1 (two iterations old) have landed
-        if (t + 1 < ns) decode_to(rw[(PH + 1) % 3], (t + 1) & 1);
-        k_barrier();
+        constexpr int PH = decltype(PHc)::value;   // t % kRing
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(min(s_begin + t + kRing, last), rw[PH]);
+        __builtin_amdgcn_sched_barrier(0);
+        QL_VMCNT((kRing - 2) * kWLoads);
+        if (t + 2 < ns) decode_to(rw[(PH + 2) % kRing], (t + 2) % 3);
+        __builtin_amdgcn_sched_barrier(0);
+        k_barrier_lgkm4();
       };
       using P0 = std::integral_constant<int, 0>;
       using P1 = std::integral_constant<int, 1>;
       using P2 = std::integral_constant<int, 2>;
+      using P3 = std::integral_constant<int, 3>;
+      using P4 = std::integral_constant<int, 4>;
+      using P5 = std::integral_constant<int, 5>;
       int t = 0;
-      for (; t + 2 < ns; t += 3) {
+      for (; t + kRing - 1 < ns; t += kRing) {
         iter(t, P0{});
         iter(t + 1, P1{});
         iter(t + 2, P2{});
+        iter(t + 3, P3{});
+        iter(t + 4, P4{});
+        iter(t + 5, P5{});
       }
       if (t < ns) iter(t, P0{});
       if (t + 1 < ns) iter(t + 1, P1{});
+      if (t + 2 < ns) iter(t + 2, P2{});
+      if (t + 3 < ns) iter(t + 3, P3{});
+      if (t + 4 < ns) iter(t + 4, P4{});
       k_barrier();   // the consumers' epilogue
     }
     return;
@@ -420,17 +454,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     constexpr bool kTwoSlots = DX && !VEC;
     constexpr int NS = kTwoSlots ? 2 : 3;
     u32x4_t wf[NS][NT], xf[NS][MT];
-    auto read = [&](int t, int kk, auto SLc) {
+    // fragment f of slice kk of step t into slot b: f < MT the activation
+    // rows of row tile f, else the weight fragment of column tile f - MT
+    auto read_one = [&](int t, int kk, auto SLc, int f) {
       constexpr int b = decltype(SLc)::value;
-      const uint16_t* sa = sA + (t % NA) * A_STAGE;
-      const uint16_t* sw = sW + (t & 1) * G::stage;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int r = wr0 + 32 * mt + lr;
-        xf[b][mt] = *reinterpret_cast<const u32x4_t*>(sa + r * GBK + a_chunk(r, 2 * kk + lg) * 8);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+      if (f < MT) {
+        const uint16_t* sa = sA + (t % NA) * A_STAGE;
+        const int r = wr0 + 32 * f + lr;
+        xf[b][f] = *reinterpret_cast<const u32x4_t*>(sa + r * GBK + a_chunk(r, 2 * kk + lg) * 8);
+      } else {
+        const int nt = f - MT;
+        const uint16_t* sw = sW + (t % 3) * G::stage;
         if (DX) {
           const int G16 = lane >> 4, i16 = lane & 15;
           const int row = 16 * kk + 8 * (G16 >> 1) + (i16 >> 2);
@@ -442,6 +476,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
           wf[b][nt] = *reinterpret_cast<const u32x4_t*>(sw + (wc0 + 32 * nt + lr) * G::ld + 16 * kk + 8 * lg);
         }
       }
+    };
+    auto read = [&](int t, int kk, auto SLc) {
+#pragma unroll
+      for (int f = 0; f < MT + NT; ++f) read_one(t, kk, SLc, f);
     };
     // 8 MFMAs of slice kk from slot b; after the 4th and the 8th, DMA loads
     // 2 kk and 2 kk + 1 of the activation tile of step sa into ring stage
@@ -462,6 +500,26 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
         }
       }
     };
+    // The same 8 MFMAs in a fixed order with one fragment read of slice rkk
+    // of step rt (into slot rs) after each of the first MT + NT: the reads
+    // then leave one by one between the MFMAs instead of as a burst that can
+    // fill the LDS queue and hold up the MFMAs behind it (a wave issues in
+    // order).
+    auto slice = [&](auto SLc, int kk, int sa, int stage, int rt, int rkk, auto RSc) {
+      constexpr int b = decltype(SLc)::value;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int nt = q / MT, mt = q % MT;
+        acc[nt][mt] = mfma32<FI::f16>(wf[b][nt], xf[b][mt], acc[nt][mt]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (q < MT + NT) read_one(rt, rkk, RSc, q);
+        __builtin_amdgcn_sched_barrier(0);
+        if ((q & 3) == 3) {
+          fill_a_one(sa, stage, 2 * kk + (q >> 2));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
@@ -474,11 +532,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
     if constexpr (!kTwoSlots) read(0, 1, S1{});
     // Iteration t (P = t % 3): slices 0-3 of step t from slots P, P+1, P+2,
     // P, with the DMA of step t+2's activation rows (ring stage (t+2) % 3,
-    // last read in iteration t-1) spread over the MFMAs; before the barrier,
-    // this wave's rows of step t+1 (issued in iteration t-1) have landed and
-    // every read of weight stage t is done; after it the first two slices of
-    // step t+1 are read.  Steps past the end re-load the last one (never
-    // read).
+    // last read before the previous barrier) spread over the MFMAs.  Slices
+    // 0 and 1 read slices 2 and 3 of step t; the barrier follows (every read
+    // of weight stage t and of step t's rows has been issued, and this
+    // wave's rows of step t+1, issued in iteration t-1, have landed: only
+    // the 4 DMAs of this iteration may still be in flight); slices 2 and 3
+    // then read slices 0 and 1 of step t+1.  Past the last step the reads
+    // take stale stages and the DMAs re-load the last step (never used).
     auto iter = [&](int t, auto PHc) {
       constexpr int P = decltype(PHc)::value;
       using A = std::integral_constant<int, P>;
@@ -486,25 +546,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       using C2 = std::integral_constant<int, (P + 2) % 3>;
       const int sa = min(s_begin + t + 2, last), stage = (t + 2) % NA;
       __builtin_amdgcn_sched_barrier(0);
-      read(t, 2, C2{});
-      __builtin_amdgcn_sched_barrier(0);
-      mma(A{}, 0, sa, stage);
-      __builtin_amdgcn_sched_barrier(0);
-      read(t, 3, A{});
-      __builtin_amdgcn_sched_barrier(0);
-      mma(B{}, 1, sa, stage);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(C2{}, 2, sa, stage);
-      __builtin_amdgcn_sched_barrier(0);
-      QL_VMCNT(VEC ? 6 : 0);
+      slice(A{}, 0, sa, stage, t, 2, C2{});
+      slice(B{}, 1, sa, stage, t, 3, A{});
+      QL_VMCNT(VEC ? 4 : 0);
       k_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      if (t + 1 < ns) {
-        read(t + 1, 0, B{});
-        read(t + 1, 1, C2{});
-      }
+      slice(C2{}, 2, sa, stage, t + 1, 0, B{});
+      slice(A{}, 3, sa, stage, t + 1, 1, C2{});
       __builtin_amdgcn_sched_barrier(0);
-      mma(A{}, 3, sa, stage);
     };
     // Two slots: slice kk in slot kk % 2, read one slice ahead.
     auto iter2 = [&](int t) {
