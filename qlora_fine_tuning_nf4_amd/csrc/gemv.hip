@@ -129,9 +129,13 @@ __global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* _
 
   using FI = FmtInfo<FMT>;
   constexpr int CB = FI::code_bytes, NC = CB / 16;   // code bytes per unit, 16-byte loads
+  // the 16 levels are the same in every lane: scalar registers
   float lv[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) lv[i] = FI::nf4 ? gptr(codebook)[i] : 0.f;
+  for (int i = 0; i < 16; ++i)
+    lv[i] = FI::nf4 ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                   __builtin_bit_cast(int, gptr(codebook)[i])))
+                    : 0.f;
 
   // DMA of an activation chunk: instruction j covers chunk rows 2j, 2j+1;
   // instruction j is issued by wave j % 4.  Lane l writes LDS bytes
@@ -384,9 +388,12 @@ __global__ __launch_bounds__(256) void k_gemv_dx(const uint16_t* __restrict__ dY
   const int i16 = lane & 15, G16 = lane >> 4;
   uint16_t* const sw = sT + wave * 64 * GDX_LDW;
 
-  float lv[16];
+  float lv[16];   // the same in every lane: scalar registers
 #pragma unroll
-  for (int i = 0; i < 16; ++i) lv[i] = FI::nf4 ? gptr(codebook)[i] : 0.f;
+  for (int i = 0; i < 16; ++i)
+    lv[i] = FI::nf4 ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                   __builtin_bit_cast(int, gptr(codebook)[i])))
+                    : 0.f;
 
   const int64_t nsc = N * K / BS;
   const auto step_rsrc = buf_rsrc(w.step, (uint32_t)(((nsc + kGroup - 1) / kGroup) * 4));
