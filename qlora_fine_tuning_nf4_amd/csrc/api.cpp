@@ -156,7 +156,9 @@ BwdWs bwd_ws(int64_t m, int64_t n, int64_t k, int r) {
   if (r > 0) {
     const int sw = plan_wgrad_split(m, k, n, r);
     wg = sw > 1 ? sizeof(float) * (size_t)sw * r * (k + n) : 0;
-    const int ru = ql::rowdot_splits(m, n, r), rt = ql::rowdot_splits(m, k, r);
+    // U reads B in place when it can (its own split count), else a transposed copy
+    const int ru = std::max(ql::rowdot_splits(m, n, r), ql::rowdot_splits(m, n, r, true));
+    const int rt = ql::rowdot_splits(m, k, r);
     wg = std::max(wg, sizeof(float) * (size_t)std::max(ru * (ru > 1), rt * (rt > 1)) * m * r);
   }
   w.total = w.wg_off + up16(wg);

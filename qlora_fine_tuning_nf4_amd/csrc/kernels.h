@@ -112,10 +112,14 @@ hipError_t launch_reduce(const float* part, int nsplit, int64_t M, int64_t C,
 // about 256 workgroups run; rowdot_splits() is the number of splits (each
 // needing M * r floats of partials when > 1; the launcher and the workspace
 // sizing both use it).  At r <= 16 the rank factor is small enough that the
-// single-pass kernel, which needs no partials, is faster.
-inline bool rowdot_uses_split_path(int64_t M, int r) { return M >= 512 && r > 16 && r <= 64; }
-inline int rowdot_splits(int64_t M, int64_t C, int r) {
-  if (!rowdot_uses_split_path(M, r)) return 1;
+// single-pass kernel, which needs no partials, is faster -- unless the rank
+// factor is given transposed (qt: read in place on the split path instead
+// of being transposed by a launch of its own).
+inline bool rowdot_uses_split_path(int64_t M, int r, bool qt = false) {
+  return M >= 512 && (r > 16 || qt) && r <= 64;
+}
+inline int rowdot_splits(int64_t M, int64_t C, int r, bool qt = false) {
+  if (!rowdot_uses_split_path(M, r, qt)) return 1;
   const int64_t ch = r <= 32 ? 256 : 128;
   const int64_t tiles = (M + 127) / 128, chunks = (C + ch - 1) / ch;
   int64_t want = (256 + tiles - 1) / tiles;
@@ -130,12 +134,12 @@ inline int rowdot_splits(int64_t M, int64_t C, int r) {
 hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r,
                          float* out, float* part, bool f16, hipStream_t s);
 // The same product with Q given transposed, Qs [C x r] row-major (Q[j][c] =
-// Qs[c][j]), on the split path (rowdot_t_supported: rowdot_uses_split_path,
-// r % 8 == 0, C % 8 == 0, P and Qs 16-byte aligned): each staged chunk of Qs
-// is transposed on its way into LDS, so no transposed copy is made.  `part`
-// must be given when rowdot_splits(M, C, r) > 1.
+// Qs[c][j]), on the split path (rowdot_t_supported: rowdot_uses_split_path
+// with qt, r % 8 == 0, C % 8 == 0, P and Qs 16-byte aligned): each staged
+// chunk of Qs is transposed on its way into LDS, so no transposed copy is
+// made.  `part` must be given when rowdot_splits(M, C, r, true) > 1.
 inline bool rowdot_t_supported(const uint16_t* P, const uint16_t* Qs, int64_t M, int64_t C, int r) {
-  return rowdot_uses_split_path(M, r) && r % 8 == 0 && C % 8 == 0 &&
+  return rowdot_uses_split_path(M, r, true) && r % 8 == 0 && C % 8 == 0 &&
          (reinterpret_cast<uintptr_t>(P) & 15) == 0 && (reinterpret_cast<uintptr_t>(Qs) & 15) == 0;
 }
 hipError_t launch_rowdot_t(const uint16_t* P, const uint16_t* Qs, int64_t M, int64_t C, int r,

@@ -149,7 +149,8 @@ __global__ __launch_bounds__(512) void k_rowdot(const uint16_t* __restrict__ P,
 }
 
 // Large-M rank projection, out[m][j] = sum_c P[m][c] Q[j][c], for 16-byte
-// rows (C % 8 == 0, aligned bases) and 16 < r <= 64.  Every row tile reads all of
+// rows (C % 8 == 0, aligned bases) and 16 < r <= 64, or r <= 64 with Q read
+// in place from its transpose.  Every row tile reads all of
 // Q, so Q is shared through LDS: a workgroup of 8 waves owns 128 rows (wave
 // w: rows 16w .. 16w+15) and the contraction range of its split, walked in
 // chunks of CH columns.  Each chunk of Q (16 RT ranks x CH bf16, rows padded
@@ -549,8 +550,8 @@ static hipError_t rowdot_any(const uint16_t* P, const uint16_t* Q, int64_t M, in
                              float* out, float* part, hipStream_t s) {
   const bool vec = C % 8 == 0 && (reinterpret_cast<uintptr_t>(P) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(Q) & 15) == 0;
-  const int ns = rowdot_splits(M, C, r);
-  const bool split = vec && rowdot_uses_split_path(M, r) && (ns == 1 || part);
+  const int ns = rowdot_splits(M, C, r, QT);
+  const bool split = vec && rowdot_uses_split_path(M, r, QT) && (ns == 1 || part);
   // transposed Q only on the split path (rowdot_t_supported, partials given)
   if (QT && (!split || r % 8 != 0)) return hipErrorInvalidValue;
   if (split) {
@@ -559,7 +560,9 @@ static hipError_t rowdot_any(const uint16_t* P, const uint16_t* Q, int64_t M, in
     const int64_t chunks = (C + ch - 1) / ch;
     const int per = (int)((chunks + ns - 1) / ns);
     const dim3 grid((unsigned)tiles, (unsigned)ns);
-    if (r <= 32)
+    if (r <= 16)
+      hipLaunchKernelGGL((k_rowdot_sk<1, F16, QT>), grid, dim3(512), 0, s, P, Q, M, C, r, out, part, ns, per);
+    else if (r <= 32)
       hipLaunchKernelGGL((k_rowdot_sk<2, F16, QT>), grid, dim3(512), 0, s, P, Q, M, C, r, out, part, ns, per);
     else
       hipLaunchKernelGGL((k_rowdot_sk<4, F16, QT>), grid, dim3(512), 0, s, P, Q, M, C, r, out, part, ns, per);

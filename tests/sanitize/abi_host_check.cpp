@@ -175,7 +175,7 @@ hipError_t launch_rowdot_t(const uint16_t* P, const uint16_t* Qs, int64_t M, int
   in_bounds(P, 2.0 * M * C, "rowdot_t P");
   in_bounds(Qs, 2.0 * C * r, "rowdot_t Qs");
   in_bounds(out, 4.0 * M * r, "rowdot_t out");
-  const int ns = rowdot_splits(M, C, r);
+  const int ns = rowdot_splits(M, C, r, true);
   if (ns > 1) in_bounds(part, 4.0 * ns * M * r, "rowdot_t partials");
   return hipSuccess;
 }
