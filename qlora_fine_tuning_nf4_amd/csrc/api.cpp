@@ -603,25 +603,34 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
       T = Tw;
     }
   }
+  // Adapter gradients.  When the input gradient runs as one tiled GEMM, the
+  // gradients' split partials go first and that GEMM adds them up (its
+  // producer waves are idle once their last decode is done), which saves the
+  // reduction launch; otherwise they come last with their own reduction.
+  const DxPlan p = plan_dx(m, n, k, path);
+  const int msplit = r > 0 ? plan_wgrad_split(m, k, n, r) : 1;
+  const bool fold = r > 0 && dX && !p.gemv && p.nsplit == 1 && msplit > 1;
+  const ql::WgradJob ja{X, U, k, dA, 0}, jb{dY, T, n, dB, 1};
+  float* wpart = (float*)(wsb + L.wg_off);
+  if (fold && ql::launch_wgrad(ja, jb, m, r, scaling, wpart, msplit, is_f16(W), s, false) != hipSuccess)
+    return QLORA_ERR_HIP;
   if (dX) {
-    const DxPlan p = plan_dx(m, n, k, path);
     const int ns = p.nsplit;
     ql::LoraTerm lora{U, A, 1, k, r, scaling};
     float* part = ns > 1 ? (float*)(wsb + L.dx_off) : nullptr;
     const bool bf = dx_dtype != QLORA_F32;   // a 16-bit output of the compute type
+    ql::WgradFold wf;
+    if (fold) wf = ql::WgradFold{wpart, msplit, r, scaling, k, n, dA, dB, 0, 1};
     const hipError_t e = p.gemv ? ql::launch_gemv_dx(view(W), codebook, dY, m, lora, dX, bf, part, ns, s)
-                                : ql::launch_gemm_dx(view(W), codebook, dY, m, lora, dX, bf, part, ns, s);
+                                : ql::launch_gemm_dx(view(W), codebook, dY, m, lora, dX, bf, part, ns, s,
+                                                     fold ? &wf : nullptr);
     if (e != hipSuccess) return QLORA_ERR_HIP;
     if (ns > 1 && ql::launch_reduce(part, ns, m, k, lora, dX, bf, is_f16(W), s) != hipSuccess)
       return QLORA_ERR_HIP;
   }
-  if (r > 0) {
-    float* part = (float*)(wsb + L.wg_off);
-    const ql::WgradJob ja{X, U, k, dA, 0}, jb{dY, T, n, dB, 1};
-    if (ql::launch_wgrad(ja, jb, m, r, scaling, part, plan_wgrad_split(m, k, n, r), is_f16(W), s) !=
-        hipSuccess)
-      return QLORA_ERR_HIP;
-  }
+  if (r > 0 && !fold &&
+      ql::launch_wgrad(ja, jb, m, r, scaling, wpart, msplit, is_f16(W), s) != hipSuccess)
+    return QLORA_ERR_HIP;
   return QLORA_OK;
 }
 

@@ -123,12 +123,43 @@ QL_DEV void k_barrier_lgkm4() {
 }
 
 
+// Adapter-gradient partials of launch_wgrad into their outputs: elements
+// t0, t0 + stride, ... of the concatenated outputs (job a's r x ca, then job
+// b's r x cb; element j * C + c), each the scaled sum of its msplit partials
+// in split order, eight loads in flight.
+QL_DEV void fold_wgrad(const WgradFold& f, int64_t t0, int64_t stride) {
+  const int64_t na = (int64_t)f.r * f.ca, total = na + (int64_t)f.r * f.cb;
+  for (int64_t idx = t0; idx < total; idx += stride) {
+    const bool second = idx >= na;
+    const int64_t i = second ? idx - na : idx;
+    const int64_t C = second ? f.cb : f.ca;
+    const int64_t pstride = (int64_t)f.r * C;
+    const float* p = f.part + (second ? (int64_t)f.msplit * na : 0) + i;
+    float v = 0.f;
+    int s = 0;
+    for (; s + 8 <= f.msplit; s += 8) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = p[(int64_t)(s + u) * pstride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v += t[u];
+    }
+    for (; s < f.msplit; ++s) v += p[(int64_t)s * pstride];
+    const int64_t j = i / C, c = i - j * C;
+    if (second ? f.tb : f.ta)
+      (second ? f.out_b : f.out_a)[c * f.r + j] = f.scaling * v;
+    else
+      (second ? f.out_b : f.out_a)[i] = f.scaling * v;
+  }
+}
+
 template <bool DX, bool VEC, int FMT>
 __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ act, Nf4View w,
                                                  const float* __restrict__ codebook, int64_t M,
                                                  LoraTerm lora, void* __restrict__ out, int out16,
                                                  float* __restrict__ part, int ksplit,
-                                                 int steps_per_split, int64_t mtiles, int64_t otiles) {
+                                                 int steps_per_split, int64_t mtiles, int64_t otiles,
+                                                 WgradFold fold) {
   using G = Geo<DX>;
   using FI = FmtInfo<FMT>;
   extern __shared__ __attribute__((aligned(16))) uint16_t sA[];   // [NA][GBM rows][GBK], swizzled
@@ -380,6 +411,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm(const uint16_t* __restrict__ ac
       if (t + 3 < ns) iter(t + 3, P3{});
       if (t + 4 < ns) iter(t + 4, P4{});
       k_barrier();   // the consumers' epilogue
+    }
+    // backward: the adapter-gradient reduction handed to this launch, in
+    // global memory only (the consumers are storing the output meanwhile)
+    if constexpr (DX) {
+      if (fold.msplit > 1) fold_wgrad(fold, (int64_t)blockIdx.x * 256 + ptid, (int64_t)gridDim.x * 256);
     }
     return;
   }
@@ -805,7 +841,7 @@ template <bool DX, bool VEC, int FMT>
 static hipError_t launch_one(dim3 grid, hipStream_t s, const uint16_t* act, const Nf4View& w,
                              const float* codebook, int64_t M, const LoraTerm& lora, void* out,
                              bool out16, float* part, int ksplit, int per, int64_t mtiles,
-                             int64_t otiles) {
+                             int64_t otiles, const WgradFold& fold) {
   // the dynamic LDS limit of this instantiation, set once per process (a
   // function-local static is initialized exactly once, thread-safely)
   static const hipError_t attr = hipFuncSetAttribute(
@@ -813,7 +849,7 @@ static hipError_t launch_one(dim3 grid, hipStream_t s, const uint16_t* act, cons
       (int)smem_bytes());
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((k_gemm<DX, VEC, FMT>), grid, dim3(512), smem_bytes(), s, act, w, codebook,
-                     M, lora, out, (int)out16, part, ksplit, per, mtiles, otiles);
+                     M, lora, out, (int)out16, part, ksplit, per, mtiles, otiles, fold);
   return hipGetLastError();
 }
 
@@ -821,9 +857,10 @@ template <bool DX, bool VEC>
 static hipError_t launch_fmt(dim3 grid, hipStream_t s, const uint16_t* act, const Nf4View& w,
                              const float* codebook, int64_t M, const LoraTerm& lora, void* out,
                              bool out16, float* part, int ksplit, int per, int64_t mtiles,
-                             int64_t otiles) {
+                             int64_t otiles, const WgradFold& fold) {
 #define QL_ONE(F) \
-  launch_one<DX, VEC, F>(grid, s, act, w, codebook, M, lora, out, out16, part, ksplit, per, mtiles, otiles)
+  launch_one<DX, VEC, F>(grid, s, act, w, codebook, M, lora, out, out16, part, ksplit, per, mtiles, \
+                         otiles, fold)
   switch (w.fmt) {
     case kFmtNf4Dq: return QL_ONE(kFmtNf4Dq);
     case kFmtNf4: return QL_ONE(kFmtNf4);
@@ -841,7 +878,7 @@ static hipError_t launch_fmt(dim3 grid, hipStream_t s, const uint16_t* act, cons
 template <bool DX>
 static hipError_t launch(const Nf4View& w, const float* codebook, const uint16_t* act, int64_t M,
                          const LoraTerm& lora, void* out, bool out16, float* part, int ksplit,
-                         hipStream_t s) {
+                         hipStream_t s, const WgradFold& fold) {
   const int64_t C = DX ? w.n : w.k, O = DX ? w.k : w.n;
   const int nsteps = (int)((C + GBK - 1) / GBK);
   const int per = (nsteps + ksplit - 1) / ksplit;
@@ -852,22 +889,23 @@ static hipError_t launch(const Nf4View& w, const float* codebook, const uint16_t
   if constexpr (DX) {
     if (C % 8 != 0)
       return launch_fmt<DX, false>(grid, s, act, w, codebook, M, lora, out, out16, part, ksplit,
-                                   per, mtiles, otiles);
+                                   per, mtiles, otiles, fold);
   }
   return launch_fmt<DX, true>(grid, s, act, w, codebook, M, lora, out, out16, part, ksplit, per,
-                              mtiles, otiles);
+                              mtiles, otiles, fold);
 }
 
 hipError_t launch_gemm_fwd(const Nf4View& w, const float* codebook, const uint16_t* X, int64_t M,
                            const LoraTerm& lora, void* Y, bool y16, float* part, int ksplit,
                            hipStream_t s) {
-  return launch<false>(w, codebook, X, M, lora, Y, y16, part, ksplit, s);
+  return launch<false>(w, codebook, X, M, lora, Y, y16, part, ksplit, s, WgradFold{});
 }
 
 hipError_t launch_gemm_dx(const Nf4View& w, const float* codebook, const uint16_t* dY, int64_t M,
                           const LoraTerm& lora, void* dX, bool dx16, float* part, int nsplit,
-                          hipStream_t s) {
-  return launch<true>(w, codebook, dY, M, lora, dX, dx16, part, nsplit, s);
+                          hipStream_t s, const WgradFold* fold) {
+  if (fold && fold->msplit > 1 && nsplit != 1) return hipErrorInvalidValue;
+  return launch<true>(w, codebook, dY, M, lora, dX, dx16, part, nsplit, s, fold ? *fold : WgradFold{});
 }
 
 }  // namespace ql

@@ -81,10 +81,26 @@ hipError_t launch_gemv_fwd(const Nf4View& w, const float* codebook, const uint16
 // k/256 (rounded up) over the jobs.
 hipError_t launch_gemv_grouped(const GemvJob* jobs, int njobs, int64_t row_groups, int64_t M,
                                const float* codebook, int64_t max_quads, int fmt, hipStream_t s);
+// The reduction of the adapter-gradient partials of launch_wgrad (msplit >
+// 1, launched with reduce = false), carried out by another kernel: out of
+// job a / b = scaling * (sum of the msplit partials, in split order), the
+// partials laid out as launch_wgrad writes them.
+struct WgradFold {
+  const float* part = nullptr;
+  int msplit = 0;   // 0: nothing to add
+  int r = 0;
+  float scaling = 0.f;
+  int64_t ca = 0, cb = 0;   // columns of job a and of job b
+  float* out_a = nullptr;
+  float* out_b = nullptr;
+  int ta = 0, tb = 0;       // their transpose_out
+};
 // dX = dY deq(W) (+ LoRA term), contraction over n; nsplit > 1 -> partials.
+// With a fold (nsplit == 1 only) the producer waves of the workgroups also
+// carry out that reduction once their K loop is over.
 hipError_t launch_gemm_dx(const Nf4View& w, const float* codebook, const uint16_t* dY, int64_t M,
                           const LoraTerm& lora, void* dX, bool dx16, float* part, int nsplit,
-                          hipStream_t s);
+                          hipStream_t s, const WgradFold* fold = nullptr);
 // Small-M input gradient (M <= 32): dX = dY deq(W) (+ LoRA term) with the
 // weight streamed once.  Workgroups run over the k/64 blocks x nsplit splits
 // of the rows; nsplit must be gemv_dx_splits(w.n, w.k), and when it is above
@@ -168,9 +184,10 @@ struct WgradJob {
   int transpose_out;
 };
 // Both gradients of a backward (a: dA, b: dB) in one launch, plus one
-// reduction launch when msplit > 1 (`part`: msplit * r * (a.C + b.C) floats).
+// reduction launch when msplit > 1 (`part`: msplit * r * (a.C + b.C) floats)
+// unless reduce is false (a WgradFold then adds the partials).
 hipError_t launch_wgrad(const WgradJob& a, const WgradJob& b, int64_t M, int r, float scaling,
-                        float* part, int msplit, bool f16, hipStream_t s);
+                        float* part, int msplit, bool f16, hipStream_t s, bool reduce = true);
 
 // Scratch of the allocation-free forward: a file-scope device array of
 // kScratchBytes per GPU.  device_scratch() returns its device address on the

@@ -620,7 +620,7 @@ int wgrad_rows_per_split(int64_t M, int msplit) {
 }
 
 hipError_t launch_wgrad(const WgradJob& a, const WgradJob& b, int64_t M, int r, float scaling,
-                        float* part, int msplit, bool f16, hipStream_t s) {
+                        float* part, int msplit, bool f16, hipStream_t s, bool reduce) {
   // splits of whole 64-row chunks; a split past the rows writes a zero partial
   const int rows = wgrad_rows_per_split(M, msplit);
   const int jt = r <= 32 ? 1 : 2;
@@ -636,7 +636,7 @@ hipError_t launch_wgrad(const WgradJob& a, const WgradJob& b, int64_t M, int r, 
   }
 #undef QL_WG
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || msplit == 1) return e;
+  if (e != hipSuccess || msplit == 1 || !reduce) return e;
   const int64_t total = (int64_t)r * (a.C + b.C);
   hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part,
                      msplit, r, scaling, a, b);

@@ -32,6 +32,8 @@ std::vector<Alloc> g_allocs;
 uintptr_t g_next = 0x100000000000ull;
 int g_fail = 0;
 int g_launches = 0;
+int g_folds = 0;       // dX GEMMs that add the adapter-gradient partials
+int g_unreduced = 0;   // adapter-gradient launches that leave their partials to a fold
 
 void* fake_alloc(size_t bytes) {
   const uintptr_t b = g_next;
@@ -128,13 +130,21 @@ hipError_t launch_gemv_grouped(const GemvJob*, int, int64_t, int64_t M, const fl
 }
 hipError_t launch_gemm_dx(const Nf4View& w, const float*, const uint16_t* dY, int64_t M,
                           const LoraTerm& lora, void* dX, bool dx16, float* part, int nsplit,
-                          hipStream_t) {
+                          hipStream_t, const WgradFold* fold) {
   ++g_launches;
   check_view(w);
   in_bounds(dY, 2.0 * M * w.n, "dY");
   if (nsplit > 1) in_bounds(part, 4.0 * nsplit * M * w.k, "dx partials");
   else in_bounds(dX, (dx16 ? 2.0 : 4.0) * M * w.k, "dX");
   check_lora(lora, M, w.k);
+  if (fold && fold->msplit > 1) {
+    ++g_folds;
+    CHECK(nsplit == 1);
+    CHECK(fold->r == lora.r && fold->ca == w.k && fold->cb == w.n);
+    in_bounds(fold->part, 4.0 * fold->msplit * fold->r * (fold->ca + fold->cb), "folded wgrad partials");
+    in_bounds(fold->out_a, 4.0 * fold->r * fold->ca, "folded dA");
+    in_bounds(fold->out_b, 4.0 * fold->r * fold->cb, "folded dB");
+  }
   return hipSuccess;
 }
 hipError_t launch_gemv_dx(const Nf4View& w, const float*, const uint16_t* dY, int64_t M,
@@ -190,8 +200,9 @@ hipError_t launch_transpose_bf16(const uint16_t* Q, int64_t N, int r, uint16_t* 
   return hipSuccess;
 }
 hipError_t launch_wgrad(const WgradJob& a, const WgradJob& b, int64_t M, int r, float, float* part,
-                        int msplit, bool, hipStream_t) {
+                        int msplit, bool, hipStream_t, bool reduce) {
   ++g_launches;
+  if (!reduce) ++g_unreduced;
   in_bounds(a.P, 2.0 * M * a.C, "wgrad a.P");
   in_bounds(a.Q, 4.0 * M * r, "wgrad a.Q");
   in_bounds(a.out, 4.0 * r * a.C, "wgrad a.out");
@@ -262,8 +273,11 @@ void run_fwd_bwd(int64_t m, int64_t n, int64_t k, int r, int path, bool save_t, 
       CHECK(wf <= ql::kScratchBytes ? en == QLORA_OK : en == QLORA_ERR_WORKSPACE);
       CHECK(en == QLORA_OK ? g_launches > before : g_launches == before);
     }
+    const int f0 = g_folds, u0 = g_unreduced;
     const int e2 = qlora_linear_bwd(&w, cb, X, dY, m, A, B, r, 2.0f, T, dX, dt, dA, dB, wsb, wb, path,
                                     nullptr);
+    // a wgrad launch without its reduction is always paired with a fold
+    CHECK(g_folds - f0 == g_unreduced - u0 && g_folds - f0 <= 1);
     const bool bwd_refused = path == QLORA_PATH_GEMV && m > QLORA_GEMV_MAX_M;
     if (e2 != (bwd_refused ? QLORA_ERR_ARG : QLORA_OK))
       std::fprintf(stderr, "bwd m=%ld n=%ld k=%ld r=%d path=%d -> %d\n", (long)m, (long)n, (long)k, r, path, e2);
@@ -346,6 +360,7 @@ int main() {
     run_fwd_bwd(100, 200, 384, 8, QLORA_PATH_AUTO, true, fmt, 0);
   run_fwd_bwd(16, 256, 512, 8, QLORA_PATH_AUTO, false, QLORA_FMT_NF4, 32);
   run_fwd_bwd(600, 256, 512, 32, QLORA_PATH_AUTO, false, QLORA_FMT_NF4, 128);
-  std::printf("abi host check: %d launches, %d failures\n", g_launches, g_fail);
+  CHECK(g_folds > 0);   // the folded reduction was exercised
+  std::printf("abi host check: %d launches, %d folds, %d failures\n", g_launches, g_folds, g_fail);
   return g_fail == 0 ? 0 : 1;
 }
