@@ -318,10 +318,64 @@ def run_layer7b(args):
         "frac_of_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
     }
+    if not args.no_library_baseline:
+        out["library_baseline"] = library_gemm_baseline(layers, M, cb)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens or M_TOKENS)
     return out
 
+
+def library_gemm_baseline(layers, M, cb, iters=10):
+    """The base products of the layer (Y = X deq(W)^T and dX = dY deq(W) for
+    the seven projections, no LoRA) three ways, GPU time per step: the fused
+    GEMMs of this library (r = 0 calls, one launch each); the library bf16 GEMM
+    (torch.matmul, hipBLASLt) on weights dequantized beforehand, which keeps a
+    16-bit copy of every weight resident; and dequantize-then-matmul, the
+    weight expanded once for the forward and once for the backward."""
+    import torch
+
+    from qlora_fine_tuning_nf4_amd import binding as QB
+
+    stream = torch.cuda.current_stream()
+    wd = [QB.qlora_dequantize(L["q"], cb) for L in layers]
+
+    def gpu_ms(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    def fused():
+        for L in layers:
+            QB.qlora_linear_fwd(L["q"], cb, L["X"], out=L["Y"], workspace=L["ws"], path="gemm")
+            QB.qlora_linear_bwd(L["q"], cb, None, L["dY"], dX_out=L["dX"], workspace=L["ws"], path="gemm")
+
+    def matmul():
+        for L, W in zip(layers, wd):
+            torch.matmul(L["X"], W.t(), out=L["Y"])
+            torch.matmul(L["dY"], W, out=L["dX"])
+
+    def deq_matmul():
+        for L, W in zip(layers, wd):
+            QB.qlora_dequantize(L["q"], cb, out=W)
+            torch.matmul(L["X"], W.t(), out=L["Y"])
+            QB.qlora_dequantize(L["q"], cb, out=W)
+            torch.matmul(L["dY"], W, out=L["dX"])
+
+    t_f, t_m, t_dm = gpu_ms(fused), gpu_ms(matmul), gpu_ms(deq_matmul)
+    flops = sum(4.0 * M * L["N"] * L["K"] for L in layers)
+    del wd
+    return {"kind": "base products of the layer (fwd + dX, 7 projections, no LoRA) on the GPU",
+            "fused_gemm_ms": round(t_f, 4), "fused_tflops": round(flops / t_f / 1e9, 1),
+            "hipblaslt_bf16_resident_ms": round(t_m, 4), "hipblaslt_bf16_tflops": round(flops / t_m / 1e9, 1),
+            "dequant_then_hipblaslt_ms": round(t_dm, 4),
+            "fused_speedup_vs_dequant_then_hipblaslt": round(t_dm / t_f, 3)}
 
 
 SINGLE_M = 16
@@ -877,6 +931,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-library-baseline", action="store_true",
+                    help="layer7b: skip the hipBLASLt comparison of the base products")
     ap.add_argument("--single-level", action="store_true",
                     help="weights without double quantization (fp32 absmax per block); "
                          "no CPU baseline (the oracle baselines time the double-quantized format)")

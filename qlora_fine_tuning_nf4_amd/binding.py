@@ -246,8 +246,11 @@ def qlora_quantize(W: torch.Tensor, codebook: torch.Tensor | None, out: NF4Weigh
     return out
 
 
-def qlora_dequantize(w: NF4Weight, codebook: torch.Tensor) -> torch.Tensor:
-    out = torch.empty((w.n, w.k), dtype=w.dtype, device=w.codes.device)
+def qlora_dequantize(w: NF4Weight, codebook: torch.Tensor, out=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((w.n, w.k), dtype=w.dtype, device=w.codes.device)
+    elif out.shape != (w.n, w.k) or out.dtype != w.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [n x k] tensor of the weight's 16-bit type")
     d = w.desc()
     _check(lib().qlora_dequantize(ctypes.byref(d), _ptr(codebook), _ptr(out), _stream()),
            "qlora_dequantize")
