@@ -251,6 +251,34 @@ int qlora_quantize(const uint16_t *W, const float *codebook, const qlora_nf4 *ou
 int qlora_dequantize(const qlora_nf4 *W, const float *codebook, uint16_t *out, void *stream);
 
 /*
+ * Plain layout of a packed weight, for exchange with code that knows only the
+ * pages' description (news.rkmt.cn/news/4821 §4.2: the 4-bit codes live two
+ * per uint8 byte; §1.2, §2.2: one constant per block of the flat row-major
+ * weight and one per group of 256 block constants).  The same arrays with
+ * the same sizes as the layout above, every byte in flat row-major order:
+ *   codes, 4-bit formats: byte j = code(2j) | code(2j+1) << 4 over the
+ *     row-major elements (the even element in the low nibble);
+ *   codes, Q8_0: byte e = the int8 value of element e;
+ *   block constants indexed by the flat block b = row * (k/block) + kb:
+ *     NF4 double-quantized: qscale[b], and step[g] per group of 256 flat
+ *     blocks (already flat above); NF4 single level: step[b] the fp32 absmax;
+ *     uint4: step[2b], step[2b+1] = scale, zero-point of 64-block b; Q8_0:
+ *     qscale bytes [2b, 2b+2) the little-endian fp16 scale of 32-block b.
+ * qlora_to_plain copies `src` (library layout) into `dst` (plain layout);
+ * qlora_from_plain copies `src` (plain layout) into `dst` (library layout),
+ * which the other entry points then accept.  A descriptor whose arrays hold
+ * the plain layout must not be passed anywhere else.  Both descriptors
+ * describe the same weight: equal n, k, format, block and compute type, and
+ * qscale NULL in both or in neither (QLORA_ERR_SHAPE, QLORA_ERR_ARG,
+ * QLORA_ERR_DTYPE otherwise); each must pass the checks of a weight
+ * descriptor (sizes, alignment); no array of dst may overlap an array of src
+ * (QLORA_ERR_ARG).  Device buffers owned by the caller; one launch on
+ * `stream`, no allocation, nothing enqueued on error.
+ */
+int qlora_to_plain(const qlora_nf4 *src, const qlora_nf4 *dst, void *stream);
+int qlora_from_plain(const qlora_nf4 *src, const qlora_nf4 *dst, void *stream);
+
+/*
  * Fold a trained adapter into the base weight (www.lqnn.cn/news/228537 §3.3:
  * dequantize W, add the low-rank branch at high precision, quantize again;
  * www.cf-1.com/news/5705389 §4.3 and kwkr.cn/news/627310 §4.4 on the two

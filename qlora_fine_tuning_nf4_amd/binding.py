@@ -82,6 +82,10 @@ def lib():
         L.qlora_quantize.argtypes = [vp, vp, P(_Nf4Desc), vp]
         L.qlora_dequantize.restype = i32
         L.qlora_dequantize.argtypes = [P(_Nf4Desc), vp, vp, vp]
+        L.qlora_to_plain.restype = i32
+        L.qlora_to_plain.argtypes = [P(_Nf4Desc), P(_Nf4Desc), vp]
+        L.qlora_from_plain.restype = i32
+        L.qlora_from_plain.argtypes = [P(_Nf4Desc), P(_Nf4Desc), vp]
         L.qlora_merge.restype = i32
         L.qlora_merge.argtypes = [P(_Nf4Desc), vp, vp, vp, i32, f32, vp, P(_Nf4Desc), vp]
         L.qlora_linear_fwd.restype = i32
@@ -254,6 +258,32 @@ def qlora_dequantize(w: NF4Weight, codebook: torch.Tensor, out=None) -> torch.Te
     d = w.desc()
     _check(lib().qlora_dequantize(ctypes.byref(d), _ptr(codebook), _ptr(out), _stream()),
            "qlora_dequantize")
+    return out
+
+
+def _like(w: NF4Weight) -> NF4Weight:
+    """Empty arrays of the same sizes, format, block and compute type."""
+    def e(t):
+        return torch.empty_like(t) if t is not None else None
+    return NF4Weight(w.n, w.k, e(w.codes), e(w.qscale), e(w.step), w.fmt, w.block, w.dtype)
+
+
+def qlora_to_plain(w: NF4Weight, out: NF4Weight | None = None) -> NF4Weight:
+    """The weight's arrays in the plain flat layout (same shapes; see the C
+    header).  The result is a container for exchange only: it must not be
+    passed to the compute entry points."""
+    out = out if out is not None else _like(w)
+    a, b = w.desc(), out.desc()
+    _check(lib().qlora_to_plain(ctypes.byref(a), ctypes.byref(b), _stream()), "qlora_to_plain")
+    return out
+
+
+def qlora_from_plain(plain: NF4Weight, out: NF4Weight | None = None) -> NF4Weight:
+    """Arrays in the plain flat layout (held in an NF4Weight of the weight's
+    shape, format, block and compute type) -> the library layout."""
+    out = out if out is not None else _like(plain)
+    a, b = plain.desc(), out.desc()
+    _check(lib().qlora_from_plain(ctypes.byref(a), ctypes.byref(b), _stream()), "qlora_from_plain")
     return out
 
 

@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libqlora_nf4.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "gemv.hip", "lora.hip", "scratch.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "gemv.hip", "lora.hip", "scratch.hip",
+           "relayout.hip"]
 
 ARCH = os.environ.get("QLORA_OFFLOAD_ARCH", "gfx950")
 FLAGS = [

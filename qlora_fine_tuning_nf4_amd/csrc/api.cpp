@@ -258,6 +258,37 @@ ql::Nf4View view(const qlora_nf4* W) {
   return ql::Nf4View{W->codes, W->qscale, W->step, W->n, W->k, kernel_fmt(W)};
 }
 
+// Byte sizes of the three arrays of a valid descriptor (0 for an unused one).
+void desc_bytes(const qlora_nf4* W, size_t sz[3]) {
+  if (W->format == QLORA_FMT_NF4)
+    qlora_nf4_block_bytes(W->n, W->k, nf4_block(W), W->qscale != nullptr, &sz[0], &sz[1], &sz[2]);
+  else
+    qlora_weight_bytes(W->format, W->n, W->k, &sz[0], &sz[1], &sz[2]);
+}
+
+// Two descriptors of the same weight in the two layouts: both valid, the
+// same shape, format, block size, compute type and scale level, and no array
+// of one overlapping an array of the other.
+int check_relayout(const qlora_nf4* src, const qlora_nf4* dst) {
+  if (!src || !dst) return QLORA_ERR_NULL;
+  if (int e = check_desc(src)) return e;
+  if (int e = check_desc(dst)) return e;
+  if (src->n != dst->n || src->k != dst->k) return QLORA_ERR_SHAPE;
+  if (src->format != dst->format || nf4_block(src) != nf4_block(dst) ||
+      (src->qscale == nullptr) != (dst->qscale == nullptr))
+    return QLORA_ERR_ARG;
+  if (is_f16(src) != is_f16(dst)) return QLORA_ERR_DTYPE;
+  size_t a[3], b[3];
+  desc_bytes(src, a);
+  desc_bytes(dst, b);
+  const uintptr_t pa[3] = {(uintptr_t)src->codes, (uintptr_t)src->qscale, (uintptr_t)src->step};
+  const uintptr_t pb[3] = {(uintptr_t)dst->codes, (uintptr_t)dst->qscale, (uintptr_t)dst->step};
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 3; ++j)
+      if (a[i] && b[j] && pa[i] < pb[j] + b[j] && pb[j] < pa[i] + a[i]) return QLORA_ERR_ARG;
+  return QLORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -365,6 +396,22 @@ int qlora_dequantize(const qlora_nf4* W, const float* codebook, uint16_t* out, v
   if (int e = check_codebook(W, codebook)) return e;
   if (!aligned(out, 16)) return QLORA_ERR_ALIGN;
   if (ql::launch_dequant(view(W), codebook, out, (hipStream_t)stream) != hipSuccess)
+    return QLORA_ERR_HIP;
+  return QLORA_OK;
+}
+
+int qlora_to_plain(const qlora_nf4* src, const qlora_nf4* dst, void* stream) {
+  if (int e = check_relayout(src, dst)) return e;
+  if (ql::launch_relayout(src->codes, src->qscale, src->step, dst->codes, dst->qscale, dst->step, src->n,
+                          src->k, kernel_fmt(src), true, (hipStream_t)stream) != hipSuccess)
+    return QLORA_ERR_HIP;
+  return QLORA_OK;
+}
+
+int qlora_from_plain(const qlora_nf4* src, const qlora_nf4* dst, void* stream) {
+  if (int e = check_relayout(src, dst)) return e;
+  if (ql::launch_relayout(src->codes, src->qscale, src->step, dst->codes, dst->qscale, dst->step, src->n,
+                          src->k, kernel_fmt(src), false, (hipStream_t)stream) != hipSuccess)
     return QLORA_ERR_HIP;
   return QLORA_OK;
 }

@@ -47,6 +47,12 @@ hipError_t launch_quantize(const uint16_t* W, const float* codebook, uint8_t* co
                            uint8_t* qscale, float* step, int64_t n, int64_t k, int fmt,
                            hipStream_t s);
 hipError_t launch_dequant(const Nf4View& w, const float* codebook, uint16_t* out, hipStream_t s);
+// Copy of a packed weight from the library layout to the plain flat layout
+// (to_plain) or back: source arrays sc / sq / ss, destination dc / dq / ds (the
+// arrays the format uses; same sizes in both layouts, disjoint buffers).
+hipError_t launch_relayout(const uint8_t* sc, const uint8_t* sq, const float* ss, uint8_t* dc,
+                           uint8_t* dq, float* ds, int64_t n, int64_t k, int fmt, bool to_plain,
+                           hipStream_t s);
 // W[n][k] <- rne(W + s * (B A)[n][k]) in place (A [r x k], B [n x r]; all 16-bit,
 // fp16 when f16 else bf16; k % 8 == 0, W and A 16-byte aligned).
 hipError_t launch_merge(uint16_t* W, const uint16_t* A, const uint16_t* B, int64_t n, int64_t k, int r,

@@ -10,6 +10,7 @@
 // wrong workspace offset or size shows up as a failure here.  Any sanitizer
 // report aborts the run (built with -fno-sanitize-recover).
 #include <cstdint>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -32,6 +33,7 @@ std::vector<Alloc> g_allocs;
 uintptr_t g_next = 0x100000000000ull;
 int g_fail = 0;
 int g_launches = 0;
+int g_relayouts = 0;   // plain-layout conversions launched
 int g_folds = 0;       // dX GEMMs that add the adapter-gradient partials
 int g_unreduced = 0;   // adapter-gradient launches that leave their partials to a fold
 
@@ -89,6 +91,33 @@ hipError_t launch_dequant(const Nf4View& w, const float*, uint16_t* out, hipStre
   ++g_launches;
   check_view(w);
   in_bounds(out, 2.0 * w.n * w.k, "dequant out");
+  return hipSuccess;
+}
+hipError_t launch_relayout(const uint8_t* sc, const uint8_t* sq, const float* ss, uint8_t* dc,
+                           uint8_t* dq, float* ds, int64_t n, int64_t k, int fmt, bool, hipStream_t) {
+  ++g_launches;
+  ++g_relayouts;
+  const double units = (double)n * (k / 64);
+  const double cb = fmt == kFmtQ8 ? 64.0 : 32.0;
+  in_bounds(sc, cb * units, "relayout src codes");
+  in_bounds(dc, cb * units, "relayout dst codes");
+  // the per-unit constants each format keeps, in bytes (qscale / step)
+  double qb = 0, sb = 0, groups = 0;
+  switch (fmt) {
+    case kFmtNf4Dq: case kFmtNf4DqF16: qb = units; groups = n * k / 64; break;
+    case kFmtNf4Dq32: qb = 2 * units; groups = n * k / 32; break;
+    case kFmtNf4Dq128: qb = units / 2; groups = n * k / 128; break;
+    case kFmtNf4: sb = 4 * units; break;
+    case kFmtNf4_32: case kFmtU4: sb = 8 * units; break;
+    case kFmtNf4_128: sb = 2 * units; break;
+    case kFmtQ8: qb = 4 * units; break;
+    default: CHECK(false);
+  }
+  if (groups > 0) sb = 4.0 * std::ceil(groups / 256.0);
+  CHECK((qb > 0) == (sq != nullptr) && (qb > 0) == (dq != nullptr));
+  CHECK((sb > 0) == (ss != nullptr) && (sb > 0) == (ds != nullptr));
+  if (qb > 0) { in_bounds(sq, qb, "relayout src qscale"); in_bounds(dq, qb, "relayout dst qscale"); }
+  if (sb > 0) { in_bounds(ss, sb, "relayout src step"); in_bounds(ds, sb, "relayout dst step"); }
   return hipSuccess;
 }
 hipError_t launch_merge(uint16_t* W, const uint16_t* A, const uint16_t* B, int64_t n, int64_t k, int r,
@@ -292,6 +321,33 @@ void run_fwd_bwd(int64_t m, int64_t n, int64_t k, int r, int path, bool save_t, 
   }
 }
 
+// Both conversions for every format, block size and scale level, on shapes
+// with a partial last row group; overlapping buffers are refused first.
+void plain_layout() {
+  struct F { int fmt, block; bool dq; };
+  const F fs[] = {{QLORA_FMT_NF4, 0, true},   {QLORA_FMT_NF4, 32, true}, {QLORA_FMT_NF4, 128, true},
+                  {QLORA_FMT_NF4, 0, false},  {QLORA_FMT_NF4, 32, false}, {QLORA_FMT_NF4, 128, false},
+                  {QLORA_FMT_U4_ASYM, 0, false}, {QLORA_FMT_Q8_0, 0, false}};
+  const int64_t nks[][2] = {{1, 128}, {17, 256}, {300, 384}, {4096, 11008}};
+  for (const F& f : fs)
+    for (const auto& nk : nks) {
+      if (f.block == 128 && nk[1] % 128) continue;
+      reset_allocs();
+      qlora_nf4 a = make_weight(nk[0], nk[1], f.fmt, f.block, f.dq);
+      qlora_nf4 b = make_weight(nk[0], nk[1], f.fmt, f.block, f.dq);
+      if (f.fmt == QLORA_FMT_NF4 && !f.dq) a.qscale = b.qscale = nullptr;
+      const int before = g_relayouts;
+      CHECK(qlora_to_plain(&a, &b, nullptr) == QLORA_OK);
+      CHECK(qlora_from_plain(&b, &a, nullptr) == QLORA_OK);
+      CHECK(g_relayouts == before + 2);
+      qlora_nf4 c = b;
+      c.codes = a.codes;   // the destination's codes on the source's
+      CHECK(qlora_to_plain(&a, &c, nullptr) == QLORA_ERR_ARG);
+      CHECK(qlora_to_plain(&a, &a, nullptr) == QLORA_ERR_ARG);
+      CHECK(g_relayouts == before + 2);
+    }
+}
+
 void error_paths() {
   reset_allocs();
   const qlora_nf4 w = make_weight(64, 128, QLORA_FMT_NF4, 0, true);
@@ -348,6 +404,7 @@ void error_paths() {
 
 int main() {
   error_paths();
+  plain_layout();
   const int64_t ms[] = {1, 5, 16, 32, 33, 100, 256, 513, 2048};
   const int64_t nks[][2] = {{64, 64}, {200, 384}, {4096, 4096}, {11008, 4096}, {4096, 11008}, {3072, 8192}};
   const int rs[] = {0, 1, 8, 16, 24, 64, 128};
@@ -361,6 +418,8 @@ int main() {
   run_fwd_bwd(16, 256, 512, 8, QLORA_PATH_AUTO, false, QLORA_FMT_NF4, 32);
   run_fwd_bwd(600, 256, 512, 32, QLORA_PATH_AUTO, false, QLORA_FMT_NF4, 128);
   CHECK(g_folds > 0);   // the folded reduction was exercised
-  std::printf("abi host check: %d launches, %d folds, %d failures\n", g_launches, g_folds, g_fail);
+  CHECK(g_relayouts > 0);
+  std::printf("abi host check: %d launches, %d folds, %d relayouts, %d failures\n", g_launches, g_folds,
+              g_relayouts, g_fail);
   return g_fail == 0 ? 0 : 1;
 }

@@ -365,3 +365,32 @@ def test_noalloc_forward_refuses_oversized_scratch_before_any_launch():
                                       None, 0, None) == 1
     assert L.qlora_linear_fwd_noalloc(ctypes.byref(d), cb, FAKE, 64, None, None, 0, 1.0, FAKE, 0,
                                       None, 1, None) == 8
+
+
+def test_plain_layout_argument_errors():
+    # both descriptors must describe the same weight and must not overlap;
+    # every refusal comes before any HIP call
+    L = B.lib()
+    src = _desc(codes=FAKE, qs=FAKE + 0x10000, st=FAKE + 0x20000)
+
+    def both(a, b):
+        r1 = L.qlora_to_plain(ctypes.byref(a) if a is not None else None,
+                              ctypes.byref(b) if b is not None else None, None)
+        r2 = L.qlora_from_plain(ctypes.byref(a) if a is not None else None,
+                                ctypes.byref(b) if b is not None else None, None)
+        assert r1 == r2
+        return r1
+
+    dst = dict(codes=FAKE + 0x30000, qs=FAKE + 0x40000, st=FAKE + 0x50000)
+    assert both(None, _desc(**dst)) == 1
+    assert both(src, None) == 1
+    assert both(src, _desc(n=32, **dst)) == 2                                 # shape
+    assert both(src, _desc(fmt=B.QLORA_FMT_Q8_0, codes=dst["codes"], qs=dst["qs"], st=0)) == 8
+    assert both(src, _desc(codes=dst["codes"], qs=0, st=dst["st"])) == 8      # scale levels differ
+    assert both(src, _desc(block=32, **dst)) == 8                             # block sizes differ
+    assert both(src, _desc(dtype=B.QLORA_F16, **dst)) == 4                   # compute types differ
+    assert both(src, _desc(codes=FAKE + 0x800, qs=dst["qs"], st=dst["st"])) == 8   # codes overlap
+    assert both(src, _desc(codes=dst["codes"], qs=FAKE + 0x10000, st=dst["st"])) == 8
+    assert both(src, _desc(codes=dst["codes"], qs=dst["qs"], st=FAKE + 0x800)) == 8   # step inside src codes
+    assert both(src, _desc(codes=FAKE + 0x30008, qs=dst["qs"], st=dst["st"])) == 3    # alignment
+    assert both(src, _desc(codes=0, qs=dst["qs"], st=dst["st"])) == 1
