@@ -320,6 +320,10 @@ def run_layer7b(args):
     }
     if not args.no_library_baseline:
         out["library_baseline"] = library_gemm_baseline(layers, M, cb)
+    if not args.no_measured_peaks:
+        mp = measured_peaks()
+        roofline["measured_peak"] = {"value": mp["mfma_bf16_loop_TFLOPs"], "unit": "TFLOP/s",
+                                     "frac": round(achieved / mp["mfma_bf16_loop_TFLOPs"], 4), "all": mp}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens or M_TOKENS)
     return out
@@ -630,6 +634,10 @@ def run_decode(args):
                      "avg_launch_us": round(gpu0 * 1e6, 1),
                      "traffic": _traffic("k_gemv_fwd", ["gemv.hip", "common.h"])},
     }
+    if not args.no_measured_peaks:
+        mp = measured_peaks()
+        out["roofline"]["measured_peak"] = {"value": mp["stream_read_GBps"], "unit": "GB/s",
+                                            "frac": round(achieved / mp["stream_read_GBps"], 4), "all": mp}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode()
     return out
@@ -925,6 +933,68 @@ def run_layer38(args):
     return out
 
 
+def measured_peaks(read_bytes=1 << 30, mfma_iters=1024, reps=10):
+    """The part's measured ceilings on this machine (``libqlora_peaks.so``): a
+    streaming read of `read_bytes` in two orders, a device copy of half that,
+    and a bf16 MFMA 32x32x16 loop, each the median over `reps` launches timed
+    with HIP events on the launching stream."""
+    import torch
+
+    from qlora_fine_tuning_nf4_amd import peaks
+
+    dev = torch.device("cuda:0")
+    buf = torch.ones(read_bytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(read_bytes // 2, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def med_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return sorted(t)[len(t) // 2]
+
+    t_rr = med_ms(lambda: peaks.read(buf, True, sink))
+    t_rs = med_ms(lambda: peaks.read(buf, False, sink))
+    half = buf[: read_bytes // 2]
+    t_cp = med_ms(lambda: peaks.copy(half, dst))
+    t_mf = med_ms(lambda: peaks.mfma(mfma_iters, sink))
+    flops = peaks.mfma_flops(mfma_iters)
+    del buf, dst
+    return {"stream_read_GBps": round(read_bytes / t_rr / 1e6, 1),
+            "stream_read_grid_stride_GBps": round(read_bytes / t_rs / 1e6, 1),
+            "copy_GBps": round(2 * (read_bytes // 2) / t_cp / 1e6, 1),
+            "mfma_bf16_loop_TFLOPs": round(flops / t_mf / 1e9, 1),
+            "how": f"median of {reps} launches each (HIP events): a {read_bytes >> 20} MiB read "
+                   "(4096 workgroups on contiguous ranges; and grid-stride), a copy of half of it "
+                   "(read + write bytes), 1024 workgroups x 4 waves x "
+                   f"{mfma_iters} iterations of 4 independent bf16 MFMA 32x32x16 chains"}
+
+
+def run_peaks(args):
+    """The measured ceilings alone, as one JSON line."""
+    m = measured_peaks()
+    return {"metric": "MI355X measured ceilings: streaming read, device copy, bf16 MFMA loop",
+            "value": m["stream_read_GBps"], "unit": "GB/s", "n_gpus": 1, "steps": 10, "warmup": 1,
+            "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "u8 (read), bf16 (MFMA)", "data": "synthetic (a device buffer of ones)",
+            "config": {"workload": "measured ceilings of one MI355X"},
+            "measured": m,
+            "roofline": {"bound": "hbm", "kernel": "k_read_ranges", "achieved": m["stream_read_GBps"],
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(m["stream_read_GBps"] / PEAK_HBM_GBS, 4), "traffic": None,
+                         "mfma": {"achieved": m["mfma_bf16_loop_TFLOPs"], "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s",
+                                  "frac": round(m["mfma_bf16_loop_TFLOPs"] / PEAK_BF16_TFLOPS, 4)}}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -933,6 +1003,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-library-baseline", action="store_true",
                     help="layer7b: skip the hipBLASLt comparison of the base products")
+    ap.add_argument("--no-measured-peaks", action="store_true",
+                    help="layer7b, decode: skip measuring the part's ceilings beside the data-sheet peaks")
     ap.add_argument("--single-level", action="store_true",
                     help="weights without double quantization (fp32 absmax per block); "
                          "no CPU baseline (the oracle baselines time the double-quantized format)")
@@ -940,7 +1012,8 @@ def main():
                     help="tokens of the oracle's CPU baseline (default: all 2048 of layer7b, "
                          "128 of the 4096 of layer3.8b)")
     ap.add_argument("--workload", default="layer7b",
-                    choices=["layer7b", "single", "decode", "quantize70b", "layer70b", "layer3.8b"])
+                    choices=["layer7b", "single", "decode", "quantize70b", "layer70b", "layer3.8b",
+                             "peaks"])
     ap.add_argument("--format", default="q8_0", choices=["q8_0", "u4_asym", "nf4"],
                     help="weight block format of the layer3.8b workload")
     ap.add_argument("--nf4-block", type=int, default=64, choices=[32, 64, 128],
@@ -969,7 +1042,7 @@ def main():
         args.no_cpu_baseline = True
 
     run = {"layer7b": run_layer7b, "single": run_single, "decode": run_decode, "quantize70b": run_quantize70b,
-           "layer70b": run_layer70b, "layer3.8b": run_layer38}[args.workload]
+           "layer70b": run_layer70b, "layer3.8b": run_layer38, "peaks": run_peaks}[args.workload]
     out = run(args)
     print(json.dumps(out), flush=True)
 

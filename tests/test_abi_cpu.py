@@ -394,3 +394,23 @@ def test_plain_layout_argument_errors():
     assert both(src, _desc(codes=dst["codes"], qs=dst["qs"], st=FAKE + 0x800)) == 8   # step inside src codes
     assert both(src, _desc(codes=FAKE + 0x30008, qs=dst["qs"], st=dst["st"])) == 3    # alignment
     assert both(src, _desc(codes=0, qs=dst["qs"], st=dst["st"])) == 1
+
+
+def test_peaks_library_exports_and_refusals():
+    # the measured-ceiling probes: every declared entry point exported, and
+    # bad arguments refused before any launch
+    from qlora_fine_tuning_nf4_amd import peaks
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "qlora_peaks.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(qlora_\w+)\s*\(", src)))
+    assert {"qlora_peak_read", "qlora_peak_copy", "qlora_peak_mfma", "qlora_peak_mfma_flops"} <= set(names)
+    L = peaks.lib()
+    for name in names:
+        assert hasattr(L, name), name
+    assert L.qlora_peak_read(None, 16, 0, FAKE, None) == 1
+    assert L.qlora_peak_read(FAKE, 24, 0, FAKE, None) == 2
+    assert L.qlora_peak_read(FAKE + 8, 16, 1, FAKE, None) == 2
+    assert L.qlora_peak_copy(FAKE, FAKE + 64, 128, None) == 2          # overlapping
+    assert L.qlora_peak_copy(FAKE, None, 128, None) == 1
+    assert L.qlora_peak_mfma(0, FAKE, None) == 2
+    assert L.qlora_peak_mfma(1, None, None) == 1
+    assert L.qlora_peak_mfma_flops(1) == 1024 * 4 * 4 * 2.0 * 32 * 32 * 16
