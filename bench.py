@@ -933,7 +933,7 @@ def run_layer38(args):
     return out
 
 
-def measured_peaks(read_bytes=1 << 30, mfma_iters=1024, reps=10):
+def measured_peaks(read_bytes=1 << 30, mfma_iters=4096, reps=10):
     """The part's measured ceilings on this machine (``libqlora_peaks.so``): a
     streaming read of `read_bytes` in two orders, a device copy of half that,
     and a bf16 MFMA 32x32x16 loop, each the median over `reps` launches timed
@@ -975,7 +975,7 @@ def measured_peaks(read_bytes=1 << 30, mfma_iters=1024, reps=10):
             "how": f"median of {reps} launches each (HIP events): a {read_bytes >> 20} MiB read "
                    "(4096 workgroups on contiguous ranges; and grid-stride), a copy of half of it "
                    "(read + write bytes), 1024 workgroups x 4 waves x "
-                   f"{mfma_iters} iterations of 4 independent bf16 MFMA 32x32x16 chains"}
+                   f"{mfma_iters} iterations of 8 independent bf16 MFMA 32x32x16 chains"}
 
 
 def run_peaks(args):

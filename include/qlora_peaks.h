@@ -30,7 +30,7 @@ int qlora_peak_read(const void *buf, size_t bytes, int contiguous, float *sink, 
 int qlora_peak_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 /*
- * 1024 workgroups of four waves, each wave `iters` iterations of four
+ * 1024 workgroups of four waves, each wave `iters` iterations of eight
  * independent bf16 MFMA 32x32x16 accumulation chains on register operands;
  * qlora_peak_mfma_flops(iters) is the launch's floating-point operation count.
  */

@@ -413,4 +413,4 @@ def test_peaks_library_exports_and_refusals():
     assert L.qlora_peak_copy(FAKE, None, 128, None) == 1
     assert L.qlora_peak_mfma(0, FAKE, None) == 2
     assert L.qlora_peak_mfma(1, None, None) == 1
-    assert L.qlora_peak_mfma_flops(1) == 1024 * 4 * 4 * 2.0 * 32 * 32 * 16
+    assert L.qlora_peak_mfma_flops(1) == 1024 * 4 * 8 * 2.0 * 32 * 32 * 16
