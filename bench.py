@@ -775,6 +775,22 @@ def run_layer70b(args):
     wall, gpu, steps_ms = _timed(step, args.steps, args.warmup)
     flops = sum(flops_fwd(M, L["N"], L["K"], r) + flops_bwd(M, L["N"], L["K"], r) for L in layers)
     tf = flops / wall / 1e12
+
+    # the fused-dequant GEMMs alone (LoRA off: one launch per call), timed with
+    # HIP events on the stream they run on
+    def gemm_only(dx):
+        def f():
+            for L in layers:
+                if dx:
+                    QB.qlora_linear_bwd(L["q"], cb, None, L["dY"], dX_out=L["dX"], workspace=L["ws"])
+                else:
+                    QB.qlora_linear_fwd(L["q"], cb, L["X"], out=L["Y"], workspace=L["ws"])
+        return f
+    kf = 2 * M * sum(L["N"] * L["K"] for L in layers)
+    _, gf, _ = _timed(gemm_only(False), args.steps, args.warmup)
+    _, gd, _ = _timed(gemm_only(True), args.steps, args.warmup)
+    tf_f, tf_d = kf / gf / 1e12, kf / gd / 1e12
+    kname, ach, t_k = ("k_gemm_dx", tf_d, gd) if gd >= gf else ("k_gemm_fwd", tf_f, gf)
     out = {
         "metric": METRIC, "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4),
@@ -786,8 +802,45 @@ def run_layer70b(args):
                                "8192x28672), M=4096 tokens, LoRA r=16 alpha=32 on all seven, fwd+bwd",
                    "M": M, "r": r, "alpha": alpha, "double_quant": DQ, "nf4_block": BLOCK, "parallelism": "none (1 GPU)"},
         "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(ach, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "avg_launch_us": round(t_k / len(layers) * 1e6, 2),
+                     "traffic": None,
+                     "other_gemm": {"k_gemm_fwd": round(tf_f, 1), "k_gemm_dx": round(tf_d, 1)}},
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_layer70(args.cpu_sample_tokens or 4096)
     return out
+
+
+def cpu_baseline_layer70(sample_tokens):
+    """The oracle on a bounded sample of the 70B-style layer: the q
+    projection (8192 x 8192, its N(0, 0.015) weight with outliers) at the
+    first `sample_tokens` tokens, dequantize + forward + backward with LoRA
+    r = 16 in float64 numpy (quantization outside the timed part)."""
+    import synth
+    from oracle import linear as olin
+    from oracle import nf4 as onf4
+
+    lv, mid = onf4.codebook()
+    N, K, r, s = 8192, 8192, 16, 32 / 16
+    W = synth.normal_bf16((N, K), 0.015, synth.tensor_seed(6, 0), outlier_rate=0.001, outlier_scale=20)
+    c, qs, st = onf4.quantize(W, mid)
+
+    def run(M):
+        X = synth.normal_bf16((M, K), 1.0, synth.tensor_seed(6, 1))
+        dY = synth.normal_bf16((M, N), 1.0, synth.tensor_seed(6, 2))
+        A = synth.normal_bf16((r, K), 0.01, synth.tensor_seed(6, 3))
+        B = synth.normal_bf16((N, r), 0.01, synth.tensor_seed(6, 4))
+        t0 = time.perf_counter()
+        olin.forward(onf4.dequantize(c, qs, st, lv).reshape(N, K), X, A, B, s)
+        olin.backward(onf4.dequantize(c, qs, st, lv).reshape(N, K), X, dY, A, B, s)
+        el = time.perf_counter() - t0
+        return (flops_fwd(M, N, K, r) + flops_bwd(M, N, K, r), el,
+                f"q projection (8192 x 8192) at M={M} of the 4096 tokens: "
+                "dequantize + fwd + bwd in float64 numpy")
+    return with_cpu_figures(run, "TFLOP/s", 1e12, sample_tokens, max(1, sample_tokens // 16))
 
 
 PROJ38 = [("q", 3072, 3072), ("k", 3072, 3072), ("v", 3072, 3072), ("o", 3072, 3072),
