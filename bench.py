@@ -1031,6 +1031,90 @@ def measured_peaks(read_bytes=1 << 30, mfma_iters=4096, reps=10):
                    f"{mfma_iters} iterations of 8 independent bf16 MFMA 32x32x16 chains"}
 
 
+REGIME_SHAPES = [(4096, 4096), (11008, 4096), (4096, 11008)]
+REGIME_M = [1, 4, 16, 32, 48, 64, 96, 128]
+
+
+def run_regime(args):
+    """The small-token regime split: forward and input-gradient GPU time of
+    the streaming kernels (m <= 32) and of the tiled GEMMs at each m, for the
+    7B projection shapes (no LoRA), warm (20 calls enqueued behind a 2 GiB
+    fill, HIP events around them) and cold (2 GiB written before each call)."""
+    import torch
+
+    import synth
+    from qlora_fine_tuning_nf4_amd import binding as QB
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cb = QB.device_codebook(dev)
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+
+    def warm_us(fn, n=20):
+        # enqueued behind a 2 GiB fill, so the calls run back to back on the
+        # GPU whatever the host's per-call cost
+        fn()
+        torch.cuda.synchronize()
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    def cold_us(fn, n=10):
+        ts = []
+        for _ in range(n):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return sorted(ts)[len(ts) // 2]
+
+    rows, cross = [], {}
+    for N, K in REGIME_SHAPES:
+        q = QB.qlora_quantize(dnorm((N, K), 0.02, synth.tensor_seed(7, N + K), device=dev), cb)
+        ws = torch.empty(max(QB.qlora_workspace_bytes(0, 128, N, K, 0),
+                             QB.qlora_workspace_bytes(1, 128, N, K, 0), 16), dtype=torch.uint8, device=dev)
+        Y = torch.empty((128, N), dtype=DT, device=dev)
+        dXo = torch.empty((128, K), dtype=DT, device=dev)
+        for M in REGIME_M:
+            X = dnorm((M, K), 1.0, synth.tensor_seed(7, M), device=dev)
+            dY = dnorm((M, N), 1.0, synth.tensor_seed(7, M + 1), device=dev)
+            rec = {"N": N, "K": K, "M": M}
+            for path in ("gemv", "gemm"):
+                if path == "gemv" and M > 32:
+                    continue
+                f = lambda: QB.qlora_linear_fwd(q, cb, X, out=Y[:M], workspace=ws, path=path)   # noqa: E731
+                b = lambda: QB.qlora_linear_bwd(q, cb, None, dY, dX_out=dXo[:M], workspace=ws, path=path)   # noqa: E731
+                rec[f"fwd_{path}_warm_us"] = round(warm_us(f), 2)
+                rec[f"dx_{path}_warm_us"] = round(warm_us(b), 2)
+                rec[f"fwd_{path}_cold_us"] = round(cold_us(f), 2)
+                rec[f"dx_{path}_cold_us"] = round(cold_us(b), 2)
+            rows.append(rec)
+        # largest m at which the streaming kernels are faster (warm, forward and dX)
+        wins = [r["M"] for r in rows if r["N"] == N and r["K"] == K and "fwd_gemv_warm_us" in r
+                and r["fwd_gemv_warm_us"] < r["fwd_gemm_warm_us"] and r["dx_gemv_warm_us"] < r["dx_gemm_warm_us"]]
+        cross[f"{N}x{K}"] = max(wins) if wins else 0
+        del q, ws
+    del flush
+    return {"metric": "small-token regime split: streaming vs tiled GEMM time per call (7B projection shapes)",
+            "value": min(cross.values()), "unit": "largest m where the streaming path wins (all shapes)",
+            "n_gpus": 1, "steps": 20, "warmup": 1, "ms_per_step": None, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dt_name(),
+            "data": "synthetic (seeded N(0,0.02) weights, NF4+DQ; N(0,1) activations and gradients)",
+            "config": {"workload": "regime split sweep, m in " + str(REGIME_M) + ", no LoRA",
+                       "shapes": REGIME_SHAPES, "auto_switch_m": 32,
+                       "streaming_limit_m": 32},
+            "streaming_wins_up_to_m": cross, "sweep": rows}
+
+
 def run_peaks(args):
     """The measured ceilings alone, as one JSON line."""
     m = measured_peaks()
@@ -1066,7 +1150,7 @@ def main():
                          "128 of the 4096 of layer3.8b)")
     ap.add_argument("--workload", default="layer7b",
                     choices=["layer7b", "single", "decode", "quantize70b", "layer70b", "layer3.8b",
-                             "peaks"])
+                             "peaks", "regime"])
     ap.add_argument("--format", default="q8_0", choices=["q8_0", "u4_asym", "nf4"],
                     help="weight block format of the layer3.8b workload")
     ap.add_argument("--nf4-block", type=int, default=64, choices=[32, 64, 128],
@@ -1095,7 +1179,8 @@ def main():
         args.no_cpu_baseline = True
 
     run = {"layer7b": run_layer7b, "single": run_single, "decode": run_decode, "quantize70b": run_quantize70b,
-           "layer70b": run_layer70b, "layer3.8b": run_layer38, "peaks": run_peaks}[args.workload]
+           "layer70b": run_layer70b, "layer3.8b": run_layer38, "peaks": run_peaks,
+           "regime": run_regime}[args.workload]
     out = run(args)
     print(json.dumps(out), flush=True)
 
