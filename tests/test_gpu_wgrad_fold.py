@@ -6,7 +6,7 @@ Both routes add the same partials in the same split order, so dA and dB from
 a backward that computes dX on the tiled GEMM path (folded) equal those of
 the same backward without dX (own reduction launch) bit for bit.  Shapes:
 ragged m and n, r = 12 (not a multiple of 8: U through a transposed copy),
-r = 64 (two 32-rank tiles), a grid with fewer producer threads than outputs
+r = 64 (one 64-rank tile) and r = 128 (two), a grid with fewer producer threads than outputs
 (the fold loops), fp16 compute, 7B projections at m = 2048 and 4096, and B
 not 16-byte aligned (U through a transposed copy).  Agreement with the
 oracle is covered by the backward parity tests, which run the folded route
@@ -40,7 +40,8 @@ def _t(bits, f16=False):
 # GEMM at one split
 CASES = [(600, 100, 384, 16, False, 0), (600, 120, 320, 24, False, 0), (600, 100, 384, 12, False, 0), (600, 100, 384, 64, False, 0),
          (600, 100, 384, 16, True, 0), (1500, 4096, 4096, 8, False, 0), (2048, 11008, 4096, 64, False, 0),
-         (2048, 4096, 4096, 8, False, 0), (2048, 4096, 4096, 8, False, 1), (4096, 4096, 4096, 8, False, 0)]
+         (2048, 4096, 4096, 8, False, 0), (2048, 4096, 4096, 8, False, 1), (4096, 4096, 4096, 8, False, 0),
+         (600, 100, 384, 128, False, 0), (2048, 4096, 4096, 128, False, 0)]
 
 
 @pytest.mark.parametrize("m,n,k,r,f16,boff", CASES)
