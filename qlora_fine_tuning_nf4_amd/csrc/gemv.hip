@@ -84,8 +84,14 @@ constexpr int GV_CHUNK_BYTES = 512;   // one row of an activation chunk: 256 bf1
 
 // XPW: activation-chunk DMA instructions per wave and quad (8 * XPW chunk
 // rows: XPW = 1 for M <= 8, 2 for M <= 16, 4 for M <= 32).
+// Waves per SIMD the small-M forward is held to: four for one 16-row tile (its
+// registers fit 128 without spilling, where the unconstrained build takes 132
+// and runs three), except for the formats that would spill (Q8_0, block 32).
+template <int MT, int FMT>
+constexpr int gv_waves() { return MT == 1 && FMT != kFmtQ8 && FMT != kFmtNf4Dq32 && FMT != kFmtNf4_32 ? 4 : 1; }
+
 template <int MT, int XPW, bool GROUPED, int FMT>
-__global__ __launch_bounds__(256) void k_gemv_fwd(GemvJob job1, const GemvJob* __restrict__ jobs,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gv_waves<MT, FMT>()))) void k_gemv_fwd(GemvJob job1, const GemvJob* __restrict__ jobs,
                                                   int njobs, const float* __restrict__ codebook,
                                                   int ksplit, int quads_per_split) {
   constexpr int XROWS = 8 * XPW;                           // rows of a chunk stage
