@@ -68,17 +68,23 @@ template <bool DX>
 struct Geo {
   // LDS stage of one K-step of the weight, 16-bit, [rows][ld].  Forward:
   // 144-byte rows put the 16 rows of a ds_read_b128 quarter-wave on 16
-  // different bank groups.  Backward: with 304-byte rows (76 dwords, 12
-  // banks apart modulo 64) the 16 rows x 4 column pieces of a producer
-  // wave's 16-byte writes start on 16 different 4-bank groups, so a write
-  // instruction takes the minimum 4 passes (320-byte rows put them all on
-  // 16 banks); the transposing reads run at the same rate either way.
+  // different bank groups.  Backward: unpadded 256-byte rows whose dword
+  // index is XORed with (row % 4) in bits 4-5 and in bits 2-3 (element
+  // column XOR 40 (row % 4)).  A 32-lane pass of the transposing reads covers
+  // four consecutive rows of one aligned 16-dword block, which the bits 4-5
+  // term puts on four different 16-bank groups; a 16-lane pass of a producer
+  // wave's 16-byte writes covers four consecutive rows x the four 16-dword
+  // blocks at one 4-dword offset, which the bits 2-3 term moves to four
+  // different offsets.  Both then hit every one of the 64 banks once per
+  // pass.  (A row pitch alone cannot do both: the reads need a pitch of
+  // 16 mod 64 dwords, the writes 4 or 12 mod 16; the former 76-dword pitch
+  // kept the writes conflict-free and made every read take two passes.)
   static constexpr int rows = DX ? GBK : GBN;    // n (dx: contraction) or n (fwd: output)
   static constexpr int cols = DX ? GBN : GBK;    // k
-  static constexpr int ld = DX ? cols + 24 : cols + 8;
+  static constexpr int ld = DX ? cols : cols + 8;
   static constexpr int stage = rows * ld;
-  // element offset of (row r, column c) in a stage
-  static QL_DEV int at(int r, int c) { return r * ld + c; }
+  // element offset of (row r, column c) in a stage; c even
+  static QL_DEV int at(int r, int c) { return DX ? r * ld + (c ^ ((r & 3) * 40)) : r * ld + c; }
 };
 
 // Logical tile of this workgroup: consecutive logical tiles (row-tile major)
