@@ -87,6 +87,13 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int path) {
   return p;
 }
 
+// The split streaming forward forms T = X A^T inside its reduce.
+bool t_in_reduce_ok(const FwdPlan& p, int64_t m, int64_t n, int64_t k, int r, const void* X,
+                    const void* A) {
+  (void)m;
+  return p.gemv && p.ksplit > 1 && ql::rank_row_ok(r, k, X, A, n);
+}
+
 int plan_dx_split(int64_t m, int64_t n, int64_t k) {
   const int64_t tiles = cdiv(m, 256) * cdiv(k, 128), nsteps = cdiv(n, 64);
   const int64_t cap = std::max<int64_t>(1, nsteps / 4);
@@ -479,8 +486,11 @@ int run_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* X, int64_
   const FwdWs L = fwd_ws(m, n, k, r, path);
   const FwdPlan p = plan_fwd(m, n, k, path);
   char* wsb = (char*)ws;
+  // split streaming forward: T is formed by the split reduce, which needs it
+  // (no rank-projection launch)
+  const bool t_in_reduce = t_in_reduce_ok(p, m, n, k, r, X, A);
   float* T = nullptr;
-  if (r > 0) {
+  if (r > 0 && !t_in_reduce) {
     T = T_save ? T_save : (float*)(wsb + L.t_off);
     float* rpart = ws ? (float*)(wsb + L.part_off) : nullptr;   // needed only with splits
     if (ql::launch_rowdot(X, A, m, k, r, T, rpart, is_f16(W), s) != hipSuccess)
@@ -493,8 +503,13 @@ int run_fwd(const qlora_nf4* W, const float* codebook, const uint16_t* X, int64_
   hipError_t e = p.gemv ? ql::launch_gemv_fwd(v, codebook, X, m, lora, Y, bf, part, p.ksplit, s)
                         : ql::launch_gemm_fwd(v, codebook, X, m, lora, Y, bf, part, p.ksplit, s);
   if (e != hipSuccess) return QLORA_ERR_HIP;
-  if (p.ksplit > 1 && ql::launch_reduce(part, p.ksplit, m, n, lora, Y, bf, is_f16(W), s) != hipSuccess)
-    return QLORA_ERR_HIP;
+  if (p.ksplit > 1) {
+    const hipError_t er =
+        t_in_reduce ? ql::launch_reduce_rows(part, p.ksplit, m, n, lora, Y, bf, is_f16(W), s,
+                                             ql::RankRow{X, A, k, 1, r, k, T_save})
+                    : ql::launch_reduce(part, p.ksplit, m, n, lora, Y, bf, is_f16(W), s);
+    if (er != hipSuccess) return QLORA_ERR_HIP;
+  }
   return QLORA_OK;
 }
 
@@ -630,12 +645,19 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
 
   hipStream_t s = (hipStream_t)stream;
   char* wsb = (char*)ws;
+  const DxPlan p = plan_dx(m, n, k, path);
+  // split streaming input gradient: U = dY B is formed by its split reduce,
+  // which writes it for the adapter gradients that follow (no rank-projection
+  // or transpose launch)
+  const bool u_in_reduce = dX && p.gemv && p.nsplit > 1 && ql::rank_row_ok(r, n, dY, B, k);
   float* U = nullptr;
   const float* T = T_saved;
   if (r > 0) {
     U = (float*)(wsb + L.u_off);
     float* rpart = (float*)(wsb + L.wg_off);
-    if (ql::rowdot_t_supported(dY, B, m, n, r)) {   // U = dY B reading B as stored
+    if (u_in_reduce) {
+      // formed by the input gradient's reduce below
+    } else if (ql::rowdot_t_supported(dY, B, m, n, r)) {   // U = dY B reading B as stored
       if (ql::launch_rowdot_t(dY, B, m, n, r, U, rpart, is_f16(W), s) != hipSuccess)
         return QLORA_ERR_HIP;
     } else {
@@ -645,8 +667,14 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
         return QLORA_ERR_HIP;
     }
     if (!T) {
+      // recomputed bit for bit as the forward's AUTO path forms it
       float* Tw = (float*)(wsb + L.t_off);
-      if (ql::launch_rowdot(X, A, m, k, r, Tw, rpart, is_f16(W), s) != hipSuccess) return QLORA_ERR_HIP;
+      if (t_in_reduce_ok(plan_fwd(m, n, k, QLORA_PATH_AUTO), m, n, k, r, X, A)) {
+        if (ql::launch_rank_rows(ql::RankRow{X, A, k, 1, r, k, Tw}, m, is_f16(W), s) != hipSuccess)
+          return QLORA_ERR_HIP;
+      } else if (ql::launch_rowdot(X, A, m, k, r, Tw, rpart, is_f16(W), s) != hipSuccess) {
+        return QLORA_ERR_HIP;
+      }
       T = Tw;
     }
   }
@@ -654,7 +682,6 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
   // gradients' split partials go first and that GEMM adds them up (its
   // producer waves are idle once their last decode is done), which saves the
   // reduction launch; otherwise they come last with their own reduction.
-  const DxPlan p = plan_dx(m, n, k, path);
   const int msplit = r > 0 ? plan_wgrad_split(m, k, n, r) : 1;
   const bool fold = r > 0 && dX && !p.gemv && p.nsplit == 1 && msplit > 1;
   const ql::WgradJob ja{X, U, k, dA, 0}, jb{dY, T, n, dB, 1};
@@ -672,8 +699,13 @@ int qlora_linear_bwd(const qlora_nf4* W, const float* codebook, const uint16_t* 
                                 : ql::launch_gemm_dx(view(W), codebook, dY, m, lora, dX, bf, part, ns, s,
                                                      fold ? &wf : nullptr);
     if (e != hipSuccess) return QLORA_ERR_HIP;
-    if (ns > 1 && ql::launch_reduce(part, ns, m, k, lora, dX, bf, is_f16(W), s) != hipSuccess)
-      return QLORA_ERR_HIP;
+    if (ns > 1) {
+      const hipError_t er =
+          u_in_reduce ? ql::launch_reduce_rows(part, ns, m, k, lora, dX, bf, is_f16(W), s,
+                                               ql::RankRow{dY, B, 1, r, r, n, U})
+                      : ql::launch_reduce(part, ns, m, k, lora, dX, bf, is_f16(W), s);
+      if (er != hipSuccess) return QLORA_ERR_HIP;
+    }
   }
   if (r > 0 && !fold &&
       ql::launch_wgrad(ja, jb, m, r, scaling, wpart, msplit, is_f16(W), s) != hipSuccess)

@@ -124,10 +124,37 @@ inline int gemv_dx_splits(int64_t N, int64_t K) {
 hipError_t launch_gemv_dx(const Nf4View& w, const float* codebook, const uint16_t* dY, int64_t M,
                           const LoraTerm& lora, void* dX, bool dx16, float* part, int nsplit,
                           hipStream_t s);
+// A rank projection formed where it is used: row m of L = P Q^T,
+// L[m][j] = sum_{c < C} P[m][c] Q[j qs_j + c qs_c] (T = X A^T: Q = A, qs_j =
+// C, qs_c = 1; U = dY B: Q = B, qs_j = 1, qs_c = r).  Used when rank_row_ok.
+struct RankRow {
+  const uint16_t* P = nullptr;   // [M x C]
+  const uint16_t* Q = nullptr;
+  int64_t qs_j = 0, qs_c = 0;
+  int r = 0;
+  int64_t C = 0;                 // contraction length
+  float* out = nullptr;          // [M x r], written when given
+};
+// Ranks in whole 16-byte pieces up to 64; 16-byte aligned P and Q with C % 8
+// == 0; at least 256 output columns (a reduce workgroup then spans at most two
+// rows).
+inline bool rank_row_ok(int r, int64_t C, const void* P, const void* Q, int64_t out_cols) {
+  return r > 0 && r % 8 == 0 && r <= 64 && C % 8 == 0 && out_cols >= 256 &&
+         (reinterpret_cast<uintptr_t>(P) & 15) == 0 && (reinterpret_cast<uintptr_t>(Q) & 15) == 0;
+}
 // out[m][c] = sum_s part[s][m][c] + LoRA term, for C columns (R and a 16-bit
 // out in fp16 when f16, else bf16).
 hipError_t launch_reduce(const float* part, int nsplit, int64_t M, int64_t C,
                          const LoraTerm& lora, void* out, bool out16, bool f16, hipStream_t s);
+// The same with the LoRA factor rows formed in the kernel from `rank`
+// (lora.L unused; rank_row_ok must hold with C output columns) and written to
+// rank.out when given.
+hipError_t launch_reduce_rows(const float* part, int nsplit, int64_t M, int64_t C,
+                              const LoraTerm& lora, void* out, bool out16, bool f16, hipStream_t s,
+                              const RankRow& rank);
+// rank->out = P Q^T for all M rows, each row formed exactly as launch_reduce
+// forms it (one workgroup per row).
+hipError_t launch_rank_rows(const RankRow& rank, int64_t M, bool f16, hipStream_t s);
 
 // Rank projection plan.  For M >= 512 and 16 < r <= 64 (and 16-byte rows)
 // the projection runs on 128-row tiles with the contraction split so that

@@ -643,4 +643,142 @@ hipError_t launch_wgrad(const WgradJob& a, const WgradJob& b, int64_t M, int r, 
   return hipGetLastError();
 }
 
+// Row m of a rank projection, L[m][j] = sum_c P[m][c] Q_j(c), formed by a
+// whole workgroup of 256 threads into lrow[0 .. r) (LDS; www.lqnn.cn/news/
+// 228537 §3.2: the low-rank branch).  Thread t takes the 8-column pieces
+// 8 t + 2048 i, two pieces' loads issued before their products (16-byte loads;
+// rank-major Q: the piece of each rank's row; contraction-major Q: the eight
+// 16-byte rows of the piece's columns, eight ranks each), eight ranks at a
+// time; products of 16-bit values are exact in fp32; a thread adds its pieces
+// in order, a wave's 64 sums are added by a butterfly and the four waves'
+// sums in wave order, so the value depends only on the row, Q and C.  red:
+// LDS scratch of 32 floats.  Ends with the workgroup synchronized.
+template <bool F16>
+QL_DEV void rank_row(const RankRow& f, int64_t m, float* lrow, float* red) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const bool rank_major = f.qs_c == 1;
+  const QL_GLOBAL uint16_t* prow = gptr(f.P + m * f.C);
+  for (int jb = 0; jb < f.r; jb += 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto piece = [&](int64_t c, u32x4_t (&qv)[8]) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        qv[i] = *reinterpret_cast<const QL_GLOBAL u32x4_t*>(
+            gptr(rank_major ? f.Q + (jb + i) * f.qs_j + c : f.Q + (c + i) * f.qs_c + jb));
+      return *reinterpret_cast<const QL_GLOBAL u32x4_t*>(prow + c);
+    };
+    auto products = [&](const u32x4_t& pv, const u32x4_t (&qv)[8]) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[2 * e] = lo16<F16>(pv[e]);
+        p[2 * e + 1] = hi16<F16>(pv[e]);
+      }
+      if (rank_major) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[jj] += p[2 * e] * lo16<F16>(qv[jj][e]) + p[2 * e + 1] * hi16<F16>(qv[jj][e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += p[e] * lo16<F16>(qv[e][q]);
+            acc[2 * q + 1] += p[e] * hi16<F16>(qv[e][q]);
+          }
+      }
+    };
+    for (int64_t c = 8 * t; c < f.C; c += 4096) {
+      u32x4_t q0[8], q1[8];
+      const bool two = c + 2048 < f.C;
+      const u32x4_t p0 = piece(c, q0);
+      u32x4_t p1 = p0;
+      if (two) p1 = piece(c + 2048, q1);
+      products(p0, q0);
+      if (two) products(p1, q1);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      float v = acc[jj];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+      acc[jj] = v;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) red[wave * 8 + jj] = acc[jj];
+    }
+    __syncthreads();
+    if (t < 8) lrow[jb + t] = ((red[t] + red[8 + t]) + red[16 + t]) + red[24 + t];
+    __syncthreads();
+  }
+}
+
+// The split reduce of the small-m streaming paths when the LoRA factor is a
+// rank projection formed here: out[m][c] = sum_s part[s][m][c] (split order)
+// + scaling sum_j L[m][j] R[c][j], with L = P Q^T.  With C >= 256 a
+// workgroup's 256 outputs lie in at most two rows, whose factor rows it forms
+// first (rank_row); the workgroup holding column 0 of a row writes that row
+// to rank.out when given (T saved by the forward, U for the adapter
+// gradients).  16-bit R and out in fp16 when F16, else bf16.
+template <bool F16>
+__global__ __launch_bounds__(256) void k_reduce_rows(const float* __restrict__ part, int nsplit,
+                                                     int64_t M, int64_t C, LoraTerm lora,
+                                                     void* __restrict__ out, int out16, RankRow rank) {
+  __shared__ float s_l[2 * 64];
+  __shared__ float s_red[32];
+  const int64_t idx0 = (int64_t)blockIdx.x * 256, idx = idx0 + threadIdx.x;
+  const int r = lora.r;
+  const int64_t m_first = idx0 / C, m_last = min(M - 1, (idx0 + 255) / C);
+  for (int64_t m = m_first; m <= m_last; ++m) {
+    float* lrow = s_l + (m - m_first) * r;
+    rank_row<F16>(rank, m, lrow, s_red);
+    if (rank.out && m * C >= idx0 && threadIdx.x < r) rank.out[m * r + threadIdx.x] = lrow[threadIdx.x];
+  }
+  if (idx >= M * C) return;
+  float v = 0.f;
+  for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * M * C + idx];
+  const int64_t m = idx / C, c = idx % C;
+  const float* lrow = s_l + (m - m_first) * r;
+  float acc = 0.f;
+  for (int j = 0; j < r; ++j) acc += lrow[j] * w16<F16>(lora.R[c * lora.rs_c + j * lora.rs_j]);
+  v += lora.scaling * acc;
+  if (out16)
+    gptr_w(reinterpret_cast<uint16_t*>(out))[idx] = to16<F16>(v);
+  else
+    gptr_w(reinterpret_cast<float*>(out))[idx] = v;
+}
+
+// rank.out = P Q^T, row blockIdx.x formed by rank_row as the reduce forms it.
+template <bool F16>
+__global__ __launch_bounds__(256) void k_rank_rows(RankRow rank) {
+  __shared__ float s_l[64];
+  __shared__ float s_red[32];
+  const int64_t m = blockIdx.x;
+  rank_row<F16>(rank, m, s_l, s_red);
+  if (threadIdx.x < rank.r) rank.out[m * rank.r + threadIdx.x] = s_l[threadIdx.x];
+}
+
+hipError_t launch_reduce_rows(const float* part, int nsplit, int64_t M, int64_t C, const LoraTerm& lora,
+                              void* out, bool out16, bool f16, hipStream_t s, const RankRow& rank) {
+  const dim3 grid((unsigned)((M * C + 255) / 256));
+  if (f16)
+    hipLaunchKernelGGL(k_reduce_rows<true>, grid, dim3(256), 0, s, part, nsplit, M, C, lora, out,
+                       (int)out16, rank);
+  else
+    hipLaunchKernelGGL(k_reduce_rows<false>, grid, dim3(256), 0, s, part, nsplit, M, C, lora, out,
+                       (int)out16, rank);
+  return hipGetLastError();
+}
+
+hipError_t launch_rank_rows(const RankRow& rank, int64_t M, bool f16, hipStream_t s) {
+  if (f16)
+    hipLaunchKernelGGL(k_rank_rows<true>, dim3((unsigned)M), dim3(256), 0, s, rank);
+  else
+    hipLaunchKernelGGL(k_rank_rows<false>, dim3((unsigned)M), dim3(256), 0, s, rank);
+  return hipGetLastError();
+}
+
 }  // namespace ql

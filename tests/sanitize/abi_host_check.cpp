@@ -35,6 +35,7 @@ int g_fail = 0;
 int g_launches = 0;
 int g_relayouts = 0;   // plain-layout conversions launched
 int g_folds = 0;       // dX GEMMs that add the adapter-gradient partials
+int g_rank_rows = 0;   // split reduces that form the LoRA factor rows themselves
 int g_unreduced = 0;   // adapter-gradient launches that leave their partials to a fold
 
 void* fake_alloc(size_t bytes) {
@@ -69,9 +70,9 @@ size_t code_bytes(const ql::Nf4View& w) {
 void check_view(const ql::Nf4View& w) {
   in_bounds(w.codes, (double)code_bytes(w), "codes");
 }
-void check_lora(const ql::LoraTerm& l, int64_t M, int64_t C) {
+void check_lora(const ql::LoraTerm& l, int64_t M, int64_t C, bool l_needed = true) {
   if (l.r == 0) return;
-  in_bounds(l.L, 4.0 * M * l.r, "lora.L");
+  if (l_needed) in_bounds(l.L, 4.0 * M * l.r, "lora.L");
   // R is [C x r] (stride rs_c) or [r x C] (stride rs_j)
   in_bounds(l.R, 2.0 * ((C - 1) * l.rs_c + (l.r - 1) * l.rs_j + 1), "lora.R");
 }
@@ -148,7 +149,8 @@ hipError_t launch_gemv_fwd(const Nf4View& w, const float*, const uint16_t* X, in
   in_bounds(X, 2.0 * M * w.k, "X");
   if (ksplit > 1) in_bounds(part, 4.0 * ksplit * M * w.n, "gemv partials");
   else in_bounds(Y, (y16 ? 2.0 : 4.0) * M * w.n, "Y");
-  check_lora(lora, M, w.n);
+  // a split launch leaves the LoRA term (and its factor) to the reduce
+  check_lora(lora, M, w.n, ksplit == 1);
   return hipSuccess;
 }
 hipError_t launch_gemv_grouped(const GemvJob*, int, int64_t, int64_t M, const float*, int64_t, int,
@@ -189,12 +191,37 @@ hipError_t launch_gemv_dx(const Nf4View& w, const float*, const uint16_t* dY, in
   check_lora(lora, M, w.k);
   return hipSuccess;
 }
+// A rank projection formed in a kernel: P [M x C], Q rank-major [r x C]
+// (qs_c == 1) or contraction-major [C x r]; out [M x r] when given.
+void check_rank_row(const ql::RankRow& f, int64_t M) {
+  CHECK(f.qs_c == 1 ? f.qs_j == f.C : (f.qs_j == 1 && f.qs_c == f.r));
+  in_bounds(f.P, 2.0 * M * f.C, "rank row P");
+  in_bounds(f.Q, 2.0 * f.r * f.C, "rank row Q");
+  if (f.out) in_bounds(f.out, 4.0 * M * f.r, "rank row out");
+}
 hipError_t launch_reduce(const float* part, int nsplit, int64_t M, int64_t C, const LoraTerm& lora,
                          void* out, bool out16, bool, hipStream_t) {
   ++g_launches;
   in_bounds(part, 4.0 * nsplit * M * C, "reduce partials");
   in_bounds(out, (out16 ? 2.0 : 4.0) * M * C, "reduce out");
   check_lora(lora, M, C);
+  return hipSuccess;
+}
+hipError_t launch_reduce_rows(const float* part, int nsplit, int64_t M, int64_t C, const LoraTerm& lora,
+                              void* out, bool out16, bool, hipStream_t, const RankRow& rank) {
+  ++g_launches;
+  ++g_rank_rows;
+  in_bounds(part, 4.0 * nsplit * M * C, "reduce partials");
+  in_bounds(out, (out16 ? 2.0 : 4.0) * M * C, "reduce out");
+  check_lora(lora, M, C, false);
+  CHECK(lora.r == rank.r && ql::rank_row_ok(rank.r, rank.C, rank.P, rank.Q, C));
+  check_rank_row(rank, M);
+  return hipSuccess;
+}
+hipError_t launch_rank_rows(const RankRow& rank, int64_t M, bool, hipStream_t) {
+  ++g_launches;
+  CHECK(rank.out != nullptr && rank.qs_c == 1);
+  check_rank_row(rank, M);
   return hipSuccess;
 }
 hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int64_t C, int r, float* out,
@@ -418,6 +445,7 @@ int main() {
   run_fwd_bwd(16, 256, 512, 8, QLORA_PATH_AUTO, false, QLORA_FMT_NF4, 32);
   run_fwd_bwd(600, 256, 512, 32, QLORA_PATH_AUTO, false, QLORA_FMT_NF4, 128);
   CHECK(g_folds > 0);   // the folded reduction was exercised
+  CHECK(g_rank_rows > 0);   // and the factor rows formed by split reduces
   CHECK(g_relayouts > 0);
   std::printf("abi host check: %d launches, %d folds, %d relayouts, %d failures\n", g_launches, g_folds,
               g_relayouts, g_fail);
