@@ -306,7 +306,9 @@ int qlora_merge(const qlora_nf4 *W, const float *codebook, const uint16_t *A, co
  * accumulation; T stays fp32.  Y is fp32 (y_dtype QLORA_F32) or the compute
  * type rounded to nearest even (QLORA_BF16, or QLORA_F16 for fp16 compute).
  * ws: device workspace of at least qlora_workspace_bytes(0, m, n, k, r) bytes
- * (may be NULL only if that size is 0).  path: QLORA_PATH_*.
+ * (may be NULL only if that size is 0).  path: QLORA_PATH_*.  The T written
+ * here is the T that qlora_linear_bwd recomputes, bit for bit, when given
+ * none (path AUTO).
  */
 int qlora_linear_fwd(const qlora_nf4 *W, const float *codebook, const uint16_t *X, int64_t m,
                      const uint16_t *A, const uint16_t *B, int r, float scaling,
@@ -363,7 +365,9 @@ int qlora_linear_bwd(const qlora_nf4 *W, const float *codebook, const uint16_t *
  * of many independent projections, so that each projection does not pay a
  * kernel launch of its own.  Same arithmetic as qlora_linear_fwd on the
  * streaming path, except that the contraction is never split (the per-row
- * sums run in one pass).
+ * sums run in one pass) and T comes from one rank-projection launch for all
+ * jobs (a split single-projection forward forms T in its split reduce; the
+ * two T agree to fp32 rounding, not bit for bit).
  *
  * One job per projection (host struct; the buffers it points to are device
  * memory owned by the caller, with the sizes and alignments of
