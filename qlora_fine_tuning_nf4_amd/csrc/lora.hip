@@ -732,14 +732,27 @@ __global__ __launch_bounds__(256) void k_reduce_rows(const float* __restrict__ p
   const int64_t idx0 = (int64_t)blockIdx.x * 256, idx = idx0 + threadIdx.x;
   const int r = lora.r;
   const int64_t m_first = idx0 / C, m_last = min(M - 1, (idx0 + 255) / C);
+  // this output's first eight split partials are loaded before the factor
+  // rows are formed (their latency overlaps those loads), then added in
+  // split order
+  const bool live = idx < M * C;
+  const float* pp = part + (live ? idx : 0);
+  const int64_t ps = M * C;
+  const int n8 = min(nsplit, 8);
+  float t[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) t[u] = u < n8 ? pp[u * ps] : 0.f;
   for (int64_t m = m_first; m <= m_last; ++m) {
     float* lrow = s_l + (m - m_first) * r;
     rank_row<F16>(rank, m, lrow, s_red);
     if (rank.out && m * C >= idx0 && threadIdx.x < r) rank.out[m * r + threadIdx.x] = lrow[threadIdx.x];
   }
-  if (idx >= M * C) return;
+  if (!live) return;
   float v = 0.f;
-  for (int s = 0; s < nsplit; ++s) v += part[(int64_t)s * M * C + idx];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (u < n8) v += t[u];
+  for (int sp = 8; sp < nsplit; ++sp) v += pp[sp * ps];
   const int64_t m = idx / C, c = idx % C;
   const float* lrow = s_l + (m - m_first) * r;
   float acc = 0.f;
