@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <vector>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -576,14 +577,27 @@ int qlora_group_init(qlora_group* g, const qlora_fwd_job* jobs, int count, int64
       st = QLORA_ERR_ALIGN;
       break;
     }
-    const int64_t n = J.w.n, k = J.w.k;
-    ql::LoraTerm lora{J.r > 0 ? J.T : nullptr, J.B, (int64_t)J.r, 1, J.r, J.scaling};
-    gj[i] = ql::GemvJob{J.X, view(&J.w), lora, J.Y, nullptr, m, y_dtype != QLORA_F32, rgs};
-    rgs += cdiv(n, 64);
+    const int64_t k = J.w.k;
     maxq = std::max(maxq, cdiv(k / kB, 4));
     if (J.r > 0) {
       rj[nl++] = ql::RowdotJob{J.X, J.A, J.T, k, J.r};
       max_r = std::max(max_r, J.r);
+    }
+  }
+  if (st == QLORA_OK) {
+    // The launch's workgroup ranges go to the jobs longest contraction first
+    // (stable): workgroups are dispatched in range order, so the launch ends
+    // on the shortest ones instead of on a few long ones running alone.  The
+    // table is in range order, as the kernel's search needs.
+    std::vector<int> order(count);
+    for (int i = 0; i < count; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int a, int b) { return jobs[a].w.k > jobs[b].w.k; });
+    for (int p = 0; p < count; ++p) {
+      const qlora_fwd_job& J = jobs[order[p]];
+      ql::LoraTerm lora{J.r > 0 ? J.T : nullptr, J.B, (int64_t)J.r, 1, J.r, J.scaling};
+      gj[p] = ql::GemvJob{J.X, view(&J.w), lora, J.Y, nullptr, m, y_dtype != QLORA_F32, rgs};
+      rgs += cdiv(J.w.n, 64);
     }
   }
   if (st == QLORA_OK) {
