@@ -201,3 +201,49 @@ def test_stream_dx_deterministic():
     outs = [B.qlora_linear_bwd(q, cb, None, dY, path="gemv")[0] for _ in range(3)]
     torch.cuda.synchronize()
     assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+# (m, n, k, r): several 8-rank blocks (24, 64), a ragged last 16-row group, n
+# not a multiple of 8 (U falls back to its own launch, T still formed in the
+# forward's reduce), the 11008-wide contraction
+RANK_ROW_CASES = [(32, 2048, 4096, 64), (5, 1024, 8192, 24), (16, 4104, 2048, 16),
+                  (8, 1002, 4096, 8), (3, 4096, 11008, 8)]
+
+
+@pytest.mark.parametrize("M,N,K,r", RANK_ROW_CASES)
+def test_small_m_rank_rows_in_split_reduce(M, N, K, r):
+    """Small-m forward and backward whose split reduces form the T and U rows
+    themselves (www.lqnn.cn/news/228537 §3.2): Y, the saved T, dX, dA, dB
+    against the oracle; a backward that recomputes T gives the same bytes as
+    one given the forward's T; bf16 outputs within one bf16 ulp of fp32."""
+    B = _dev()
+    _say("rank rows", M, N, K, r)
+    s = 2.0
+    seed = 11 * M + N + 5 * K + r
+    X = synth.normal_bf16((M, K), 1.0, seed)
+    W = synth.normal_bf16((N, K), 0.02, seed + 1)
+    A = synth.normal_bf16((r, K), 0.01, seed + 2)
+    Bm = synth.normal_bf16((N, r), 0.01, seed + 3)
+    dY = synth.normal_bf16((M, N), 1.0, seed + 4)
+    cb = B.device_codebook()
+    q = B.qlora_quantize(_t(W), cb)
+    Xd, Ad, Bd, dYd = _t(X), _t(A), _t(Bm), _t(dY)
+    Y, T = B.qlora_linear_fwd(q, cb, Xd, Ad, Bd, s)
+    Yh, _ = B.qlora_linear_fwd(q, cb, Xd, Ad, Bd, s, y_dtype=torch.bfloat16)
+    dX, dA, dB = B.qlora_linear_bwd(q, cb, Xd, dYd, Ad, Bd, s, T=T)
+    dXr, dAr, dBr = B.qlora_linear_bwd(q, cb, Xd, dYd, Ad, Bd, s)   # T recomputed
+    torch.cuda.synchronize()
+    c, qs, st = onf4.quantize(W, MID)
+    Wd = onf4.dequantize(c, qs, st, LV).reshape(W.shape)
+    Yo, To = olin.forward(Wd, X, A, Bm, s)
+    dXo, dAo, dBo = olin.backward(Wd, X, dY, A, Bm, s)
+    errs = {"Y": _rel(Y.cpu().numpy(), Yo), "T": _rel(T.cpu().numpy(), To),
+            "dX": _rel(dX.cpu().numpy(), dXo), "dA": _rel(dA.cpu().numpy(), dAo),
+            "dB": _rel(dB.cpu().numpy(), dBo)}
+    _say("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert max(errs.values()) <= REL_TOL, errs
+    assert torch.equal(dX, dXr) and torch.equal(dA, dAr) and torch.equal(dB, dBr)
+    hv = Yh.float().cpu().numpy().astype(np.float64)
+    fv = Y.cpu().numpy().astype(np.float64)
+    ulp = np.spacing(np.abs(fv).astype(np.float32)).astype(np.float64) * 65536.0
+    assert np.all(np.abs(hv - fv) <= ulp)
