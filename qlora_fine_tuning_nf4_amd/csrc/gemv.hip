@@ -60,6 +60,22 @@ QL_DEV float lora_dot_v(const LoraTerm& L, int64_t m, int64_t c, bool vec) {
   return acc;
 }
 
+// rsrc_bytes for a wave-uniform, non-negative count, on the scalar unit:
+// this part has no scalar 64-bit ordered compare, and in C the clamp becomes
+// a vector-ALU 64-bit compare once per quad (any bit at or above bit 31 means
+// the count exceeds the clamp).
+QL_DEV uint32_t rsrc_bytes_u(int64_t b) {
+  uint32_t r;
+  uint64_t t;
+  asm("s_lshr_b64 %1, %2, 31\n\t"
+      "s_cmp_lg_u64 %1, 0\n\t"
+      "s_cselect_b32 %0, 0x7fffffff, %3"
+      : "=s"(r), "=&s"(t)
+      : "s"(b), "s"((uint32_t)b)
+      : "scc");
+  return r;
+}
+
 // Streaming forward, small M.  A workgroup of 4 waves owns 64 weight rows
 // (wave w: the 16-row group 4 * blockIdx.x + w) and walks the quads (4
 // blocks = 256 k) of its split in step.  Per quad, lane l (n = l % 16,
@@ -194,7 +210,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gv_waves<MT
   auto load_w = [&](int q, GemvRaw<FMT>& u) {
     const int qc = min(q, nquads - 1);
     const int64_t ub = gg * nkb + (int64_t)4 * qc * R;
-    const auto rc = buf_rsrc(w.codes + ub * CB, rsrc_bytes((nblk - ub) * CB));
+    const auto rc = buf_rsrc(w.codes + ub * CB, rsrc_bytes_u((nblk - ub) * CB));
 #pragma unroll
     for (int j = 0; j < NC; ++j)
       u.c[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, w_lane * CB + 16 * j, 0, 0));
@@ -203,13 +219,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gv_waves<MT
     const uint32_t so = BS == 64 ? w_lane : (BS == 32 ? 2 * w_lane : w_lane2);
     const uint32_t bq = BS == 64 ? 4u * qc : (BS == 32 ? 8u * qc : 2u * qc);   // flat block advance
     if constexpr (FI::nf4 && FI::dq) {
-      const auto rq = buf_rsrc(w.qscale + sb, rsrc_bytes(nsc - sb));
+      const auto rq = buf_rsrc(w.qscale + sb, rsrc_bytes_u(nsc - sb));
       u.qbyte = BS == 32 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rq, so, 0, 0)
                          : (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rq, so, 0, 0);
       u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                              step_rsrc, ((b_lane + bq) >> 8) * 4, 0, 0));
     } else if constexpr (FI::nf4) {
-      const auto rs = buf_rsrc(w.step + sb, rsrc_bytes((nsc - sb) * 4));
+      const auto rs = buf_rsrc(w.step + sb, rsrc_bytes_u((nsc - sb) * 4));
       u.qbyte = 1u;
       u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, so * 4, 0, 0));
       if constexpr (BS == 32)
@@ -218,11 +234,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gv_waves<MT
       // two dword loads: a 64-bit buffer load whose halves are bit-cast to
       // float is shrunk to one dword by this compiler, both halves then
       // holding the scale
-      const auto prs = buf_rsrc(w.step + 2 * ub, rsrc_bytes((nblk - ub) * 8));
+      const auto prs = buf_rsrc(w.step + 2 * ub, rsrc_bytes_u((nblk - ub) * 8));
       u.step = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, w_lane * 8, 0, 0));
       u.zp = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, w_lane * 8 + 4, 0, 0));
     } else {
-      u.qbyte = __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(w.qscale + 4 * ub, rsrc_bytes((nblk - ub) * 4)),
+      u.qbyte = __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(w.qscale + 4 * ub, rsrc_bytes_u((nblk - ub) * 4)),
                                                      w_lane * 4, 0, 0);
     }
   };
@@ -232,7 +248,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(gv_waves<MT
   for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int q, int stage, const GemvRaw<FMT>& u) {
-    const bool ok = nok && 4 * q + g < nkb;
+    // Blocks past the row end exist only in a ragged last quad (k % 256 !=
+    // 0): their scale is forced to zero there.  Rows past N read the last
+    // row (finite values) and their outputs are never stored.
+    const bool ok = (nkb & 3) == 0 || q < nquads - 1 || 4 * q + g < nkb;
     const uint16_t* sx = stage_ptr(stage);
     u32x4_t af[MT][8];
 #pragma unroll
