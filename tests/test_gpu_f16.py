@@ -171,6 +171,32 @@ def test_linear_parity(M, N, K, r, path):
         assert _rel(dB.cpu().numpy(), dBo) <= REL_TOL
 
 
+@pytest.mark.parametrize("M,N,K,r", [(16, 4096, 4096, 8), (5, 1024, 8192, 24), (32, 2048, 4096, 64)])
+def test_small_m_recomputed_t_bit_identical(M, N, K, r):
+    """fp16 operands on the small-m streaming path (path AUTO), where T and U
+    are formed inside the split reduces.  A backward given no T forms T again,
+    one row per workgroup in the same summation order, so its dX, dA and dB
+    equal, byte for byte, those of the backward given the saved T; both
+    against the oracle in fp32."""
+    B = _dev()
+    _say("f16 recomputed T", M, N, K, r)
+    s = 2.0
+    cb = B.device_codebook()
+    X, W, A, Bm, dY = _inputs(M, N, K, r, seed=7 * M + N + K + r)
+    q = B.qlora_quantize(_t(W), cb)
+    Xd, Ad, Bd, dYd = _t(X), _t(A), _t(Bm), _t(dY)
+    Y, T = B.qlora_linear_fwd(q, cb, Xd, Ad, Bd, s)
+    dX, dA, dB = B.qlora_linear_bwd(q, cb, Xd, dYd, Ad, Bd, s, T=T)
+    dXr, dAr, dBr = B.qlora_linear_bwd(q, cb, Xd, dYd, Ad, Bd, s)
+    torch.cuda.synchronize()
+    assert torch.equal(dX, dXr) and torch.equal(dA, dAr) and torch.equal(dB, dBr)
+    Wd = _oracle(W)[3]
+    Yo, To = olin.forward(Wd, X, A, Bm, s, dtype=F16)
+    dXo, dAo, dBo = olin.backward(Wd, X, dY, A, Bm, s, dtype=F16)
+    for got, ref in [(Y, Yo), (T, To), (dX, dXo), (dA, dAo), (dB, dBo)]:
+        assert _rel(got.cpu().numpy(), ref) <= REL_TOL
+
+
 @pytest.mark.parametrize("M,path", [(16, "gemv"), (200, "gemm")])
 def test_lora_only(M, path):
     """W = 0 isolates the adapter terms of Y and dX."""
