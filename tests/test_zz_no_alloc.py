@@ -54,6 +54,8 @@ def _case(B, cb, M, N, K, r, seed, path, save_t, y_dtype):
     ((100, 4096, 4096, 16, "gemm", False, torch.bfloat16), (40, 520, 1024, 8, "gemm", False, torch.float32)),
     # GEMM path without splits, T to the caller's buffer (no scratch), then a split call
     ((2048, 4096, 4096, 8, "auto", True, torch.bfloat16), (64, 256, 512, 0, "auto", True, torch.float32)),
+    # streaming path with T saved (formed inside the split reduce), then a smaller call
+    ((16, 4096, 4096, 16, "auto", True, torch.bfloat16), (3, 1024, 2048, 8, "auto", True, torch.float32)),
 ])
 def test_noalloc_forward_matches_workspace_forward(first, second):
     B = _dev()
